@@ -1,0 +1,154 @@
+/*
+ * C ABI of the MI355X (gfx950) Mamba-2 SSD library: the SSD core forward and
+ * analytic backward, plus the block-shell ops around it (causal depthwise
+ * conv1d + SiLU, RMSNorm-gated output).
+ *
+ * The operations are those of the burn_dragon_kernel 0.5.0 page
+ * "src/sequence/mamba2/backward.rs":
+ *   ssd_fwd   the recurrence of ssd_forward_state_history_reference
+ *             h_t = exp(dt_t A_h) h_{t-1} + dt_t x_t (outer) B_t, A_h = -exp(A_log_h),
+ *             and the readout y_t = C_t . h_t + D_h x_t of the block backward
+ *             (the y_grouped expression); head h reads group h / (nheads/ngroups).
+ *   ssd_bwd   the gradients of ssd_backward_reference (grad_x, grad_b, grad_c,
+ *             grad_dt, grad_a_log, grad_d_skip) plus the gradient of the initial
+ *             state, for the loss sum(dy * y).  The optional saved state history
+ *             and the "recompute" mode mirror the fused backward's optional
+ *             ssd_state_history argument (its two parity tests).
+ *   mamba2_conv1d_silu_*      depthwise_conv_preact_with_history + silu, and the
+ *                             block backward's conv / SiLU tap loop.
+ *   mamba2_rmsnorm_gated_*    rmsnorm_gated_{forward,backward}_from_inv_rms with
+ *                             inv_rms = 1/sqrt(mean(y^2) + eps).
+ *
+ * Conventions (all entry points):
+ *  - Every tensor pointer is a DEVICE pointer owned by the caller; the library
+ *    never allocates, frees or keeps them.  Scratch memory is the caller's
+ *    `workspace` (size from the matching *_workspace_bytes call).
+ *  - Layouts are row-major and contiguous.  bf16 tensors hold raw bfloat16 bits.
+ *  - Every output is overwritten (never accumulated into).
+ *  - `stream` is a hipStream_t (0 = the null stream).  Work is enqueued
+ *    asynchronously; the call returns once it is enqueued.
+ *  - Arguments are checked before anything is enqueued; on failure nothing is
+ *    enqueued and the call returns a negative ssd_status, with a description in
+ *    ssd_last_error() (thread-local, valid until the next call on that thread).
+ *    A launch failure returns SSD_ERR_HIP naming the kernel.
+ *  - Tensor pointers must be 16-byte aligned (SSD_ERR_ALIGN otherwise).
+ *  - Results are deterministic: every reduction runs in a fixed order.
+ *  - Calls that share a workspace must be ordered on one stream.
+ */
+#ifndef SSD_MI355X_H
+#define SSD_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SSD_OK = 0,
+  SSD_ERR_INVALID_ARG = -1, /* null required pointer, non-positive size */
+  SSD_ERR_SHAPE = -2,       /* unsupported or inconsistent dimensions */
+  SSD_ERR_DTYPE = -3,       /* unknown dtype code */
+  SSD_ERR_WORKSPACE = -4,   /* workspace missing or smaller than required */
+  SSD_ERR_HIP = -5,         /* a HIP launch failed */
+  SSD_ERR_ALIGN = -6        /* a tensor pointer is not 16-byte aligned */
+} ssd_status;
+
+typedef enum { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype;
+
+/* The statement of one SSD problem (the page's batch, time, nheads, headdim,
+ * d_state, ngroups, plus the chunk length of the chunked algorithm).
+ * Limits: 1 <= headdim <= 64, 1 <= dstate <= 128, 1 <= chunk <= 256,
+ * seqlen % chunk == 0, nheads % ngroups == 0, nheads <= 65535,
+ * batch <= 65535.  batch == 0 or seqlen == 0 is an empty problem. */
+typedef struct {
+  int64_t batch, seqlen, nheads, headdim, dstate, ngroups, chunk;
+  int32_t act_dtype; /* dtype of x, dt, B, C and y (ssd_dtype) */
+  int32_t dy_dtype;  /* dtype of dy (ssd_dtype) */
+} ssd_problem;
+
+/* Bytes of workspace ssd_fwd (for_backward = 0) or ssd_bwd (for_backward = 1)
+ * needs.  has_chunk_states tells whether the caller passes chunk_states (fwd:
+ * as an output, bwd: as the saved history); without them the library keeps
+ * the chunk states in the workspace.  Returns 0 for an invalid problem. */
+size_t ssd_workspace_bytes(const ssd_problem* prob, int for_backward, int has_chunk_states);
+
+/* Forward.
+ *   x [b,T,H,P], dt [b,T,H] (dt after softplus, > 0), B, C [b,T,G,N]: act_dtype
+ *   A_log, D [H]: f32
+ *   init_state [b,H,P,N] f32, nullable (zeros)
+ *   y [b,T,H,P] act_dtype (output)
+ *   final_state [b,H,P,N] f32, nullable (output): state after the last step
+ *   chunk_states [b,T/chunk,H,P,N] f32, nullable (output): the state entering
+ *     each chunk (chunk 0: init_state) = the page's per-step state history
+ *     sampled at the last step of the previous chunk.  Pass it to ssd_bwd to
+ *     skip the recomputation. */
+int ssd_fwd(const ssd_problem* prob, const void* x, const void* dt, const float* A_log,
+            const void* B, const void* C, const float* D, const float* init_state, void* y,
+            float* final_state, float* chunk_states, void* workspace, size_t workspace_bytes,
+            void* stream);
+
+/* Backward of L = sum(dy * y).
+ *   inputs as in ssd_fwd; dy [b,T,H,P] in dy_dtype
+ *   chunk_states: nullable; when given it must be what ssd_fwd wrote for the
+ *     same inputs (not checked); when null the states are recomputed
+ *   outputs (f32, all required except d_init_state):
+ *     dx [b,T,H,P], ddt [b,T,H], dA_log [H], dB, dC [b,T,G,N], dD [H]
+ *     d_init_state [b,H,P,N] nullable: gradient of the initial state (written
+ *     also when init_state is null: the gradient at a zero initial state). */
+int ssd_bwd(const ssd_problem* prob, const void* x, const void* dt, const float* A_log,
+            const void* B, const void* C, const float* D, const float* init_state,
+            const float* chunk_states, const void* dy, float* dx, float* ddt, float* dA_log,
+            float* dB, float* dC, float* dD, float* d_init_state, void* workspace,
+            size_t workspace_bytes, void* stream);
+
+/* Causal depthwise conv1d (zero initial state) followed by SiLU, split into
+ * the SSD inputs.  xbc [b,T,conv_dim] with conv_dim = d_inner + 2*ngroups*dstate
+ * (channel order: x, then B, then C); w [conv_dim, d_conv] f32, tap d_conv-1
+ * multiplies the current step; bias [conv_dim] f32.  Outputs in `dtype`:
+ * x_out [b,T,d_inner], B_out, C_out [b,T,ngroups,dstate].  1 <= d_conv <= 8. */
+int mamba2_conv1d_silu_fwd(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t ngroups,
+                           int64_t dstate, int64_t d_conv, int32_t dtype, const void* xbc,
+                           const float* w, const float* bias, void* x_out, void* B_out,
+                           void* C_out, void* stream);
+
+size_t mamba2_conv1d_silu_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t d_inner,
+                                              int64_t ngroups, int64_t dstate, int64_t d_conv);
+
+/* Backward of mamba2_conv1d_silu_fwd.  dx [b,T,d_inner], dB, dC [b,T,G,N] are
+ * the f32 gradients of its three outputs.  Outputs f32: dxbc [b,T,conv_dim],
+ * dw [conv_dim,d_conv], dbias [conv_dim]. */
+int mamba2_conv1d_silu_bwd(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t ngroups,
+                           int64_t dstate, int64_t d_conv, int32_t dtype, const void* xbc,
+                           const float* w, const float* bias, const float* dx, const float* dB,
+                           const float* dC, float* dxbc, float* dw, float* dbias, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+/* RMSNorm-gated forward over rows of `width`: inv_rms = 1/sqrt(mean(y^2)+eps),
+ * out = y * inv_rms * w * silu(z).  y, z, out in `dtype`; w [width] f32;
+ * inv_rms [rows] f32 (output, saved for the backward). */
+int mamba2_rmsnorm_gated_fwd(int64_t rows, int64_t width, float eps, int32_t dtype, const void* y,
+                             const void* z, const float* w, void* out, float* inv_rms,
+                             void* stream);
+
+size_t mamba2_rmsnorm_gated_bwd_workspace_bytes(int64_t rows, int64_t width);
+
+/* RMSNorm-gated backward with the saved inv_rms.  g [rows,width] is the
+ * gradient of `out` in `g_dtype`.  Outputs f32: dy, dz [rows,width], dw [width]. */
+int mamba2_rmsnorm_gated_bwd(int64_t rows, int64_t width, int32_t dtype, int32_t g_dtype,
+                             const void* y, const void* z, const float* w, const float* inv_rms,
+                             const void* g, float* dy, float* dz, float* dw, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/* Description of the last failure on the calling thread ("" after success). */
+const char* ssd_last_error(void);
+
+/* Library version string. */
+const char* ssd_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSD_MI355X_H */

@@ -1,0 +1,23 @@
+"""MI355X (gfx950) Mamba-2 SSD core: forward and analytic backward, plus the
+conv1d+SiLU and RMSNorm-gated block-shell ops.
+
+Thin Python binding over the C ABI in include/ssd.h (libssd_mi355x.so, built
+by ``selective_state_space_mamba_amd.build``).  The binding only marshals
+arguments: it checks devices, dtypes, shapes and contiguity, allocates outputs
+and the workspace with PyTorch, and passes raw pointers plus the current HIP
+stream.  Every step of the computation runs in the library's HIP kernels; if
+the library is missing the calls raise.
+"""
+from ._binding import (  # noqa: F401
+    SSDError,
+    conv1d_silu_bwd,
+    conv1d_silu_fwd,
+    library_path,
+    load_library,
+    rmsnorm_gated_bwd,
+    rmsnorm_gated_fwd,
+    ssd_bwd,
+    ssd_fwd,
+    ssd_workspace_bytes,
+    version,
+)

@@ -1,0 +1,282 @@
+"""ctypes binding of libssd_mi355x.so (argument marshalling only)."""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, Optional, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_NAME = "libssd_mi355x.so"
+_lib = None
+
+SSD_F32, SSD_BF16 = 0, 1
+_STATUS = {0: "SSD_OK", -1: "SSD_ERR_INVALID_ARG", -2: "SSD_ERR_SHAPE", -3: "SSD_ERR_DTYPE",
+           -4: "SSD_ERR_WORKSPACE", -5: "SSD_ERR_HIP", -6: "SSD_ERR_ALIGN"}
+
+
+class SSDError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("nheads", ctypes.c_int64),
+                ("headdim", ctypes.c_int64), ("dstate", ctypes.c_int64), ("ngroups", ctypes.c_int64),
+                ("chunk", ctypes.c_int64), ("act_dtype", ctypes.c_int32), ("dy_dtype", ctypes.c_int32)]
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, _LIB_NAME)
+
+
+def load_library():
+    """Load the HIP library; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python -m selective_state_space_mamba_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, sz, i64, i32, f32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int64, ctypes.c_int32, ctypes.c_float
+    pp = ctypes.POINTER(Problem)
+    lib.ssd_workspace_bytes.argtypes = [pp, ctypes.c_int, ctypes.c_int]
+    lib.ssd_workspace_bytes.restype = sz
+    lib.ssd_fwd.argtypes = [pp] + [vp] * 10 + [vp, sz, vp]
+    lib.ssd_fwd.restype = ctypes.c_int
+    lib.ssd_bwd.argtypes = [pp] + [vp] * 16 + [vp, sz, vp]
+    lib.ssd_bwd.restype = ctypes.c_int
+    lib.mamba2_conv1d_silu_fwd.argtypes = [i64] * 6 + [i32] + [vp] * 6 + [vp]
+    lib.mamba2_conv1d_silu_fwd.restype = ctypes.c_int
+    lib.mamba2_conv1d_silu_bwd_workspace_bytes.argtypes = [i64] * 6
+    lib.mamba2_conv1d_silu_bwd_workspace_bytes.restype = sz
+    lib.mamba2_conv1d_silu_bwd.argtypes = [i64] * 6 + [i32] + [vp] * 9 + [vp, sz, vp]
+    lib.mamba2_conv1d_silu_bwd.restype = ctypes.c_int
+    lib.mamba2_rmsnorm_gated_fwd.argtypes = [i64, i64, f32, i32] + [vp] * 5 + [vp]
+    lib.mamba2_rmsnorm_gated_fwd.restype = ctypes.c_int
+    lib.mamba2_rmsnorm_gated_bwd_workspace_bytes.argtypes = [i64, i64]
+    lib.mamba2_rmsnorm_gated_bwd_workspace_bytes.restype = sz
+    lib.mamba2_rmsnorm_gated_bwd.argtypes = [i64, i64, i32, i32] + [vp] * 8 + [vp, sz, vp]
+    lib.mamba2_rmsnorm_gated_bwd.restype = ctypes.c_int
+    lib.ssd_last_error.argtypes = []
+    lib.ssd_last_error.restype = ctypes.c_char_p
+    lib.ssd_version.argtypes = []
+    lib.ssd_version.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def version() -> str:
+    return load_library().ssd_version().decode()
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise SSDError(rc, load_library().ssd_last_error().decode())
+
+
+def _code(dtype: torch.dtype) -> int:
+    if dtype == torch.float32:
+        return SSD_F32
+    if dtype == torch.bfloat16:
+        return SSD_BF16
+    raise TypeError(f"unsupported dtype {dtype}: use float32 or bfloat16")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _need(t: torch.Tensor, name: str, shape, dtype=None, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def make_problem(x: torch.Tensor, B: torch.Tensor, chunk: int, dy_dtype: Optional[torch.dtype] = None) -> Problem:
+    b, T, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    act = _code(x.dtype)
+    return Problem(b, T, H, P, N, G, chunk, act, _code(dy_dtype) if dy_dtype is not None else act)
+
+
+def ssd_workspace_bytes(prob: Problem, for_backward: bool, has_chunk_states: bool) -> int:
+    return int(load_library().ssd_workspace_bytes(ctypes.byref(prob), int(for_backward), int(has_chunk_states)))
+
+
+def _check_inputs(x, dt, A_log, B, C, D, init_state):
+    b, T, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    dev = x.device
+    _need(x, "x", (b, T, H, P), device=dev)
+    _need(dt, "dt", (b, T, H), x.dtype, dev)
+    _need(B, "B", (b, T, G, N), x.dtype, dev)
+    _need(C, "C", (b, T, G, N), x.dtype, dev)
+    _need(A_log, "A_log", (H,), torch.float32, dev)
+    _need(D, "D", (H,), torch.float32, dev)
+    if init_state is not None:
+        _need(init_state, "init_state", (b, H, P, N), torch.float32, dev)
+    return b, T, H, P, N, G
+
+
+def ssd_fwd(x, dt, A_log, B, C, D, init_state=None, chunk: int = 256, want_chunk_states: bool = True,
+            want_final_state: bool = True, out: Optional[Dict[str, torch.Tensor]] = None,
+            workspace: Optional[torch.Tensor] = None, stream=None
+            ) -> Tuple[torch.Tensor, Optional[torch.Tensor], Optional[torch.Tensor]]:
+    """SSD forward.  Returns (y, final_state, chunk_states); the last two are
+    None when not requested.  `out` may hold preallocated y / final_state /
+    chunk_states; `workspace` a preallocated uint8 device buffer."""
+    lib = load_library()
+    b, T, H, P, N, G = _check_inputs(x, dt, A_log, B, C, D, init_state)
+    prob = make_problem(x, B, chunk)
+    out = out or {}
+    nc = T // chunk if chunk > 0 else 0
+    y = out.get("y")
+    if y is None:
+        y = torch.empty((b, T, H, P), dtype=x.dtype, device=x.device)
+    fin = out.get("final_state")
+    if fin is None and want_final_state:
+        fin = torch.empty((b, H, P, N), dtype=torch.float32, device=x.device)
+    cs = out.get("chunk_states")
+    if cs is None and want_chunk_states:
+        cs = torch.empty((b, nc, H, P, N), dtype=torch.float32, device=x.device)
+    need = lib.ssd_workspace_bytes(ctypes.byref(prob), 0, int(cs is not None))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    wsz = 0 if workspace is None else workspace.numel()
+    _check(lib.ssd_fwd(ctypes.byref(prob), _ptr(x), _ptr(dt), _ptr(A_log), _ptr(B), _ptr(C), _ptr(D),
+                       _ptr(init_state), _ptr(y), _ptr(fin), _ptr(cs), _ptr(workspace), wsz, _stream(stream)))
+    return y, fin, cs
+
+
+def ssd_bwd(x, dt, A_log, B, C, D, dy, init_state=None, chunk_states=None, chunk: int = 256,
+            want_d_init_state: bool = True, out: Optional[Dict[str, torch.Tensor]] = None,
+            workspace: Optional[torch.Tensor] = None, stream=None) -> Dict[str, torch.Tensor]:
+    """SSD backward of sum(dy * y).  Returns dx, ddt, dA_log, dB, dC, dD (f32)
+    and d_init_state (f32, or None when not requested)."""
+    lib = load_library()
+    b, T, H, P, N, G = _check_inputs(x, dt, A_log, B, C, D, init_state)
+    if dy.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("dy must be float32 or bfloat16")
+    _need(dy, "dy", (b, T, H, P), device=x.device)
+    if chunk_states is not None:
+        _need(chunk_states, "chunk_states", (b, T // chunk, H, P, N), torch.float32, x.device)
+    prob = make_problem(x, B, chunk, dy.dtype)
+    out = dict(out or {})
+    f32 = dict(dtype=torch.float32, device=x.device)
+    shapes = dict(dx=(b, T, H, P), ddt=(b, T, H), dA_log=(H,), dB=(b, T, G, N), dC=(b, T, G, N), dD=(H,))
+    for k, s in shapes.items():
+        if out.get(k) is None:
+            out[k] = torch.empty(s, **f32)
+    if want_d_init_state and out.get("d_init_state") is None:
+        out["d_init_state"] = torch.empty((b, H, P, N), **f32)
+    dinit = out.get("d_init_state")
+    need = lib.ssd_workspace_bytes(ctypes.byref(prob), 1, int(chunk_states is not None))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    wsz = 0 if workspace is None else workspace.numel()
+    _check(lib.ssd_bwd(ctypes.byref(prob), _ptr(x), _ptr(dt), _ptr(A_log), _ptr(B), _ptr(C), _ptr(D),
+                       _ptr(init_state), _ptr(chunk_states), _ptr(dy), _ptr(out["dx"]), _ptr(out["ddt"]),
+                       _ptr(out["dA_log"]), _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out["dD"]), _ptr(dinit),
+                       _ptr(workspace), wsz, _stream(stream)))
+    out["d_init_state"] = dinit
+    return out
+
+
+def conv1d_silu_fwd(xbc, w, bias, d_inner: int, ngroups: int, dstate: int, stream=None):
+    """Causal depthwise conv1d + SiLU on xbc [b,T,conv_dim]; returns
+    (x [b,T,d_inner], B [b,T,G,N], C [b,T,G,N]) in xbc's dtype."""
+    lib = load_library()
+    b, T, cd = xbc.shape
+    K = w.shape[1]
+    _need(xbc, "xbc", (b, T, d_inner + 2 * ngroups * dstate), device=xbc.device)
+    _need(w, "w", (cd, K), torch.float32, xbc.device)
+    if bias is not None:
+        _need(bias, "bias", (cd,), torch.float32, xbc.device)
+    xo = torch.empty((b, T, d_inner), dtype=xbc.dtype, device=xbc.device)
+    Bo = torch.empty((b, T, ngroups, dstate), dtype=xbc.dtype, device=xbc.device)
+    Co = torch.empty_like(Bo)
+    _check(lib.mamba2_conv1d_silu_fwd(b, T, d_inner, ngroups, dstate, K, _code(xbc.dtype), _ptr(xbc), _ptr(w),
+                                      _ptr(bias), _ptr(xo), _ptr(Bo), _ptr(Co), _stream(stream)))
+    return xo, Bo, Co
+
+
+def conv1d_silu_bwd(xbc, w, bias, dx, dB, dC, d_inner: int, ngroups: int, dstate: int, workspace=None,
+                    stream=None):
+    """Backward of conv1d_silu_fwd given f32 gradients of its outputs; returns
+    (dxbc [b,T,conv_dim], dw [conv_dim,d_conv], dbias [conv_dim]) in f32."""
+    lib = load_library()
+    b, T, cd = xbc.shape
+    K = w.shape[1]
+    _need(dx, "dx", (b, T, d_inner), torch.float32, xbc.device)
+    _need(dB, "dB", (b, T, ngroups, dstate), torch.float32, xbc.device)
+    _need(dC, "dC", (b, T, ngroups, dstate), torch.float32, xbc.device)
+    f32 = dict(dtype=torch.float32, device=xbc.device)
+    dxbc = torch.empty((b, T, cd), **f32)
+    dw = torch.empty((cd, K), **f32)
+    db = torch.empty((cd,), **f32)
+    need = lib.mamba2_conv1d_silu_bwd_workspace_bytes(b, T, d_inner, ngroups, dstate, K)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=xbc.device)
+    wsz = 0 if workspace is None else workspace.numel()
+    _check(lib.mamba2_conv1d_silu_bwd(b, T, d_inner, ngroups, dstate, K, _code(xbc.dtype), _ptr(xbc), _ptr(w),
+                                      _ptr(bias), _ptr(dx), _ptr(dB), _ptr(dC), _ptr(dxbc), _ptr(dw), _ptr(db),
+                                      _ptr(workspace), wsz, _stream(stream)))
+    return dxbc, dw, db
+
+
+def rmsnorm_gated_fwd(y, z, w, eps: float = 1e-5, stream=None):
+    """RMSNorm over the last axis of y, times w * silu(z).  Returns
+    (out in y's dtype, inv_rms f32 over the leading axes)."""
+    lib = load_library()
+    width = y.shape[-1]
+    rows = y.numel() // width if width else 0
+    _need(z, "z", tuple(y.shape), y.dtype, y.device)
+    _need(w, "w", (width,), torch.float32, y.device)
+    if not y.is_contiguous():
+        raise ValueError("y must be contiguous")
+    out = torch.empty_like(y)
+    inv = torch.empty(tuple(y.shape[:-1]), dtype=torch.float32, device=y.device)
+    _check(lib.mamba2_rmsnorm_gated_fwd(rows, width, float(eps), _code(y.dtype), _ptr(y), _ptr(z), _ptr(w),
+                                        _ptr(out), _ptr(inv), _stream(stream)))
+    return out, inv
+
+
+def rmsnorm_gated_bwd(y, z, w, inv_rms, g, workspace=None, stream=None):
+    """Backward of rmsnorm_gated_fwd with the saved inv_rms; returns
+    (dy, dz, dw) in f32."""
+    lib = load_library()
+    width = y.shape[-1]
+    rows = y.numel() // width if width else 0
+    _need(z, "z", tuple(y.shape), y.dtype, y.device)
+    _need(w, "w", (width,), torch.float32, y.device)
+    _need(inv_rms, "inv_rms", tuple(y.shape[:-1]), torch.float32, y.device)
+    _need(g, "g", tuple(y.shape), None, y.device)
+    f32 = dict(dtype=torch.float32, device=y.device)
+    dy = torch.empty(tuple(y.shape), **f32)
+    dz = torch.empty(tuple(y.shape), **f32)
+    dw = torch.empty((width,), **f32)
+    need = lib.mamba2_rmsnorm_gated_bwd_workspace_bytes(rows, width)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=y.device)
+    wsz = 0 if workspace is None else workspace.numel()
+    _check(lib.mamba2_rmsnorm_gated_bwd(rows, width, _code(y.dtype), _code(g.dtype), _ptr(y), _ptr(z), _ptr(w),
+                                        _ptr(inv_rms), _ptr(g), _ptr(dy), _ptr(dz), _ptr(dw), _ptr(workspace), wsz,
+                                        _stream(stream)))
+    return dy, dz, dw

@@ -1,0 +1,407 @@
+// C ABI of the SSD library: argument checks, workspace plan and the launch
+// sequence of every entry point declared in include/ssd.h.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <string>
+
+#include "../../include/ssd.h"
+#include "ssd_common.hpp"
+#include "shell_launch.hpp"
+#include "ssd_launch.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int ok() {
+  g_last_error.clear();
+  return SSD_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool valid_dtype(int32_t t) { return t == SSD_F32 || t == SSD_BF16; }
+
+// Checks the problem statement; fills `d` on success.
+int check_problem(const ssd_problem* p, ssd::Dims* d) {
+  if (!p) return fail(SSD_ERR_INVALID_ARG, "problem is null");
+  if (!valid_dtype(p->act_dtype)) return fail(SSD_ERR_DTYPE, "act_dtype %d is not SSD_F32 or SSD_BF16", p->act_dtype);
+  if (!valid_dtype(p->dy_dtype)) return fail(SSD_ERR_DTYPE, "dy_dtype %d is not SSD_F32 or SSD_BF16", p->dy_dtype);
+  if (p->batch < 0 || p->seqlen < 0)
+    return fail(SSD_ERR_INVALID_ARG, "batch (%lld) and seqlen (%lld) must be >= 0", (long long)p->batch,
+                (long long)p->seqlen);
+  if (p->nheads <= 0 || p->headdim <= 0 || p->dstate <= 0 || p->ngroups <= 0 || p->chunk <= 0)
+    return fail(SSD_ERR_INVALID_ARG, "nheads, headdim, dstate, ngroups and chunk must be > 0");
+  if (p->headdim > ssd::PMAX)
+    return fail(SSD_ERR_SHAPE, "headdim %lld exceeds the supported maximum %d", (long long)p->headdim, ssd::PMAX);
+  if (p->dstate > ssd::NMAX)
+    return fail(SSD_ERR_SHAPE, "dstate %lld exceeds the supported maximum %d", (long long)p->dstate, ssd::NMAX);
+  if (p->chunk > ssd::QMAX)
+    return fail(SSD_ERR_SHAPE, "chunk %lld exceeds the supported maximum %d", (long long)p->chunk, ssd::QMAX);
+  if (p->nheads % p->ngroups)
+    return fail(SSD_ERR_SHAPE, "nheads %lld is not a multiple of ngroups %lld", (long long)p->nheads,
+                (long long)p->ngroups);
+  if (p->seqlen % p->chunk)
+    return fail(SSD_ERR_SHAPE, "seqlen %lld is not a multiple of chunk %lld", (long long)p->seqlen,
+                (long long)p->chunk);
+  if (p->nheads > 65535 || p->batch > 65535)
+    return fail(SSD_ERR_SHAPE, "nheads and batch must be <= 65535");
+  const int64_t elems = p->batch * p->seqlen * p->nheads * p->headdim;
+  if (p->seqlen > (int64_t(1) << 30) || elems > (int64_t(1) << 40))
+    return fail(SSD_ERR_SHAPE, "problem too large");
+  d->b = static_cast<int>(p->batch);
+  d->T = static_cast<int>(p->seqlen);
+  d->H = static_cast<int>(p->nheads);
+  d->P = static_cast<int>(p->headdim);
+  d->N = static_cast<int>(p->dstate);
+  d->G = static_cast<int>(p->ngroups);
+  d->Q = static_cast<int>(p->chunk);
+  return SSD_OK;
+}
+
+// Heads of a group are split over this many workgroups so that one launch has
+// at least `target` workgroups (never more splits than heads per group).
+int choose_nsplit(const ssd::Dims& d, int64_t target) {
+  const int64_t base = static_cast<int64_t>(d.b) * d.nc() * d.G * d.nb();
+  const int hpg = d.hpg();
+  for (int s = 1; s <= hpg; ++s)
+    if (hpg % s == 0 && base * s >= target) return s;
+  return hpg;
+}
+constexpr int64_t kFwdTarget = 512;
+constexpr int64_t kBwdTarget = 256;
+
+struct FwdPlan {
+  size_t states = 0, total = 0;
+};
+struct BwdPlan {
+  size_t states = 0, gamma = 0, gh = 0, rowM = 0, colE = 0, diagE = 0, Rp = 0, dsoff = 0, dA = 0, dD = 0, dB = 0,
+         dC = 0, total = 0;
+  int nsplit = 1;
+};
+
+size_t state_bytes(const ssd::Dims& d) {
+  return sizeof(float) * static_cast<size_t>(d.b) * d.nc() * d.H * d.P * d.N;
+}
+
+FwdPlan plan_fwd(const ssd::Dims& d, bool has_states) {
+  FwdPlan p;
+  size_t off = 0;
+  if (!has_states) {
+    p.states = off;
+    off += align_up(state_bytes(d));
+  }
+  p.total = off;
+  return p;
+}
+
+BwdPlan plan_bwd(const ssd::Dims& d, bool has_states) {
+  BwdPlan p;
+  p.nsplit = choose_nsplit(d, kBwdTarget);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += align_up(bytes);
+    return o;
+  };
+  const size_t bht = sizeof(float) * static_cast<size_t>(d.b) * d.H * d.T;
+  if (!has_states) p.states = take(state_bytes(d));
+  p.gamma = take(state_bytes(d));
+  p.gh = take(sizeof(float) * static_cast<size_t>(d.b) * d.nc() * d.H * ssd::state_npb(d));
+  p.rowM = take(bht);
+  p.colE = take(bht);
+  p.diagE = take(bht);
+  p.Rp = take(bht);
+  p.dsoff = take(bht);
+  p.dA = take(sizeof(float) * static_cast<size_t>(d.b) * d.nc() * d.H);
+  p.dD = take(sizeof(float) * static_cast<size_t>(d.b) * d.nc() * d.nb() * d.H);
+  if (p.nsplit > 1) {
+    const size_t part = sizeof(float) * static_cast<size_t>(p.nsplit) * d.b * d.T * d.G * d.N;
+    p.dB = take(part);
+    p.dC = take(part);
+  }
+  p.total = off;
+  return p;
+}
+
+template <typename T>
+T* at(void* base, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(base) + off);
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(SSD_ERR_HIP, "%s launch failed: %s", what, hipGetErrorString(e));
+}
+
+#define SSD_LAUNCH(expr, what)                 \
+  do {                                         \
+    hipError_t e_ = (expr);                    \
+    if (e_ != hipSuccess) return hip_fail(e_, what); \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+const char* ssd_last_error(void) { return g_last_error.c_str(); }
+
+const char* ssd_version(void) { return "ssd-mi355x 0.1 (gfx950)"; }
+
+size_t ssd_workspace_bytes(const ssd_problem* prob, int for_backward, int has_chunk_states) {
+  ssd::Dims d;
+  if (check_problem(prob, &d) != SSD_OK) return 0;
+  if (d.b == 0 || d.T == 0) return 0;
+  return for_backward ? plan_bwd(d, has_chunk_states != 0).total : plan_fwd(d, has_chunk_states != 0).total;
+}
+
+int ssd_fwd(const ssd_problem* prob, const void* x, const void* dt, const float* A_log, const void* B,
+            const void* C, const float* D, const float* init_state, void* y, float* final_state,
+            float* chunk_states, void* workspace, size_t workspace_bytes, void* stream) {
+  ssd::Dims d;
+  int rc = check_problem(prob, &d);
+  if (rc != SSD_OK) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const ssd::DType act = static_cast<ssd::DType>(prob->act_dtype);
+  if (!A_log || !D) return fail(SSD_ERR_INVALID_ARG, "ssd_fwd: A_log and D are required");
+  const bool empty = d.b == 0 || d.T == 0;
+  if (!empty && (!x || !dt || !B || !C || !y))
+    return fail(SSD_ERR_INVALID_ARG, "ssd_fwd: x, dt, B, C and y are required");
+  const void* ptrs[] = {x, dt, A_log, B, C, D, init_state, y, final_state, chunk_states};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return fail(SSD_ERR_ALIGN, "ssd_fwd: a tensor pointer is not 16-byte aligned");
+  const int64_t state_elems = static_cast<int64_t>(d.b) * d.H * d.P * d.N;
+  if (empty) {
+    if (final_state) {
+      if (init_state)
+        SSD_LAUNCH(ssd::launch_copy(final_state, init_state, state_elems, st), "copy");
+      else
+        SSD_LAUNCH(ssd::launch_fill(final_state, state_elems, 0.f, st), "fill");
+    }
+    return ok();
+  }
+  const FwdPlan plan = plan_fwd(d, chunk_states != nullptr);
+  if (plan.total > 0 && !workspace) return fail(SSD_ERR_WORKSPACE, "ssd_fwd: workspace is null (%zu bytes needed)", plan.total);
+  if (workspace_bytes < plan.total)
+    return fail(SSD_ERR_WORKSPACE, "ssd_fwd: workspace of %zu bytes is smaller than the %zu needed", workspace_bytes,
+                plan.total);
+  if (workspace && !aligned16(workspace)) return fail(SSD_ERR_ALIGN, "ssd_fwd: workspace is not 16-byte aligned");
+  float* states = chunk_states ? chunk_states : at<float>(workspace, plan.states);
+  SSD_LAUNCH(ssd::launch_chunk_state_fwd(d, act, x, B, dt, A_log, init_state, states, final_state, st),
+             "chunk_state_fwd");
+  SSD_LAUNCH(ssd::launch_chunk_out_fwd(d, act, choose_nsplit(d, kFwdTarget), x, B, C, dt, A_log, D, states, y, st),
+             "chunk_out_fwd");
+  return ok();
+}
+
+int ssd_bwd(const ssd_problem* prob, const void* x, const void* dt, const float* A_log, const void* B,
+            const void* C, const float* D, const float* init_state, const float* chunk_states, const void* dy,
+            float* dx, float* ddt, float* dA_log, float* dB, float* dC, float* dD, float* d_init_state,
+            void* workspace, size_t workspace_bytes, void* stream) {
+  ssd::Dims d;
+  int rc = check_problem(prob, &d);
+  if (rc != SSD_OK) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const ssd::DType act = static_cast<ssd::DType>(prob->act_dtype);
+  const ssd::DType dyt = static_cast<ssd::DType>(prob->dy_dtype);
+  if (!A_log || !D || !dA_log || !dD) return fail(SSD_ERR_INVALID_ARG, "ssd_bwd: A_log, D, dA_log and dD are required");
+  const bool empty = d.b == 0 || d.T == 0;
+  if (!empty && (!x || !dt || !B || !C || !dy || !dx || !ddt || !dB || !dC))
+    return fail(SSD_ERR_INVALID_ARG, "ssd_bwd: x, dt, B, C, dy, dx, ddt, dB and dC are required");
+  const void* ptrs[] = {x, dt, A_log, B, C, D, init_state, chunk_states, dy, dx, ddt, dA_log, dB, dC, dD, d_init_state};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return fail(SSD_ERR_ALIGN, "ssd_bwd: a tensor pointer is not 16-byte aligned");
+  if (empty) {
+    SSD_LAUNCH(ssd::launch_fill(dA_log, d.H, 0.f, st), "fill");
+    SSD_LAUNCH(ssd::launch_fill(dD, d.H, 0.f, st), "fill");
+    if (d_init_state)
+      SSD_LAUNCH(ssd::launch_fill(d_init_state, static_cast<int64_t>(d.b) * d.H * d.P * d.N, 0.f, st), "fill");
+    return ok();
+  }
+  const BwdPlan plan = plan_bwd(d, chunk_states != nullptr);
+  if (!workspace) return fail(SSD_ERR_WORKSPACE, "ssd_bwd: workspace is null (%zu bytes needed)", plan.total);
+  if (workspace_bytes < plan.total)
+    return fail(SSD_ERR_WORKSPACE, "ssd_bwd: workspace of %zu bytes is smaller than the %zu needed", workspace_bytes,
+                plan.total);
+  if (!aligned16(workspace)) return fail(SSD_ERR_ALIGN, "ssd_bwd: workspace is not 16-byte aligned");
+
+  ssd::BwdScratch s;
+  s.rowM = at<float>(workspace, plan.rowM);
+  s.colE = at<float>(workspace, plan.colE);
+  s.diagE = at<float>(workspace, plan.diagE);
+  s.Rp = at<float>(workspace, plan.Rp);
+  s.dsoff = at<float>(workspace, plan.dsoff);
+  s.gh_part = at<float>(workspace, plan.gh);
+  s.dA_part = at<float>(workspace, plan.dA);
+  s.dD_part = at<float>(workspace, plan.dD);
+  s.dB_part = plan.nsplit > 1 ? at<float>(workspace, plan.dB) : nullptr;
+  s.dC_part = plan.nsplit > 1 ? at<float>(workspace, plan.dC) : nullptr;
+  float* gamma = at<float>(workspace, plan.gamma);
+
+  const float* states = chunk_states;
+  if (!states) {
+    float* rec = at<float>(workspace, plan.states);
+    SSD_LAUNCH(ssd::launch_chunk_state_fwd(d, act, x, B, dt, A_log, init_state, rec, nullptr, st),
+               "chunk_state_fwd (recompute)");
+    states = rec;
+  }
+  SSD_LAUNCH(ssd::launch_chunk_state_bwd(d, act, dyt, dy, C, dt, A_log, states, gamma, d_init_state, s.gh_part, st),
+             "chunk_state_bwd");
+  SSD_LAUNCH(ssd::launch_chunk_bwd_col(d, act, dyt, plan.nsplit, x, B, C, dt, dy, A_log, D, gamma, dx,
+                                       plan.nsplit > 1 ? s.dB_part : dB, s, st),
+             "chunk_bwd_col");
+  SSD_LAUNCH(ssd::launch_chunk_bwd_row(d, act, dyt, plan.nsplit, x, B, C, dt, dy, A_log, states,
+                                       plan.nsplit > 1 ? s.dC_part : dC, s, st),
+             "chunk_bwd_row");
+  SSD_LAUNCH(ssd::launch_bwd_dt(d, act, dt, A_log, ddt, s, st), "bwd_dt");
+  SSD_LAUNCH(ssd::launch_bwd_reduce(d, plan.nsplit, A_log, dA_log, dD, dB, dC, s, st), "bwd_reduce");
+  return ok();
+}
+
+// ------------------------------------------------------------------ shell
+
+static int check_conv(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t ngroups, int64_t dstate,
+                      int64_t d_conv, int32_t dtype) {
+  if (!valid_dtype(dtype)) return fail(SSD_ERR_DTYPE, "conv1d: dtype %d is not SSD_F32 or SSD_BF16", dtype);
+  if (batch < 0 || seqlen < 0 || d_inner <= 0 || ngroups <= 0 || dstate <= 0 || d_conv <= 0)
+    return fail(SSD_ERR_INVALID_ARG, "conv1d: sizes must be positive (batch, seqlen >= 0)");
+  if (d_conv > ssd::conv_max_k()) return fail(SSD_ERR_SHAPE, "conv1d: d_conv %lld exceeds %d", (long long)d_conv, ssd::conv_max_k());
+  if (batch > 65535 || seqlen > (int64_t(1) << 30) || d_inner + 2 * ngroups * dstate > (int64_t(1) << 24))
+    return fail(SSD_ERR_SHAPE, "conv1d: problem too large");
+  return SSD_OK;
+}
+
+size_t mamba2_conv1d_silu_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t ngroups,
+                                              int64_t dstate, int64_t d_conv) {
+  if (check_conv(batch, seqlen, d_inner, ngroups, dstate, d_conv, SSD_F32) != SSD_OK) return 0;
+  if (batch == 0 || seqlen == 0) return 0;
+  const int64_t cd = d_inner + 2 * ngroups * dstate;
+  return align_up(sizeof(float) * static_cast<size_t>(batch) * ssd::conv_nruns(static_cast<int>(seqlen)) * cd *
+                  (d_conv + 1));
+}
+
+int mamba2_conv1d_silu_fwd(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t ngroups, int64_t dstate,
+                           int64_t d_conv, int32_t dtype, const void* xbc, const float* w, const float* bias,
+                           void* x_out, void* B_out, void* C_out, void* stream) {
+  int rc = check_conv(batch, seqlen, d_inner, ngroups, dstate, d_conv, dtype);
+  if (rc != SSD_OK) return rc;
+  if (batch == 0 || seqlen == 0) return ok();
+  if (!xbc || !w || !x_out || !B_out || !C_out)
+    return fail(SSD_ERR_INVALID_ARG, "conv1d_silu_fwd: xbc, w, x_out, B_out and C_out are required");
+  const void* ptrs[] = {xbc, w, bias, x_out, B_out, C_out};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return fail(SSD_ERR_ALIGN, "conv1d_silu_fwd: a tensor pointer is not 16-byte aligned");
+  SSD_LAUNCH(ssd::launch_conv_fwd(static_cast<int>(batch), static_cast<int>(seqlen), static_cast<int>(d_inner),
+                                  static_cast<int>(ngroups * dstate), static_cast<int>(d_conv),
+                                  static_cast<ssd::DType>(dtype), xbc, w, bias, x_out, B_out, C_out,
+                                  static_cast<hipStream_t>(stream)),
+             "conv1d_silu_fwd");
+  return ok();
+}
+
+int mamba2_conv1d_silu_bwd(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t ngroups, int64_t dstate,
+                           int64_t d_conv, int32_t dtype, const void* xbc, const float* w, const float* bias,
+                           const float* dx, const float* dB, const float* dC, float* dxbc, float* dw, float* dbias,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_conv(batch, seqlen, d_inner, ngroups, dstate, d_conv, dtype);
+  if (rc != SSD_OK) return rc;
+  if (!dw || !dbias) return fail(SSD_ERR_INVALID_ARG, "conv1d_silu_bwd: dw and dbias are required");
+  const int64_t cd = d_inner + 2 * ngroups * dstate;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (batch == 0 || seqlen == 0) {
+    SSD_LAUNCH(ssd::launch_fill(dw, cd * d_conv, 0.f, st), "fill");
+    SSD_LAUNCH(ssd::launch_fill(dbias, cd, 0.f, st), "fill");
+    return ok();
+  }
+  if (!xbc || !w || !dx || !dB || !dC || !dxbc)
+    return fail(SSD_ERR_INVALID_ARG, "conv1d_silu_bwd: xbc, w, dx, dB, dC and dxbc are required");
+  const void* ptrs[] = {xbc, w, bias, dx, dB, dC, dxbc, dw, dbias, workspace};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return fail(SSD_ERR_ALIGN, "conv1d_silu_bwd: a pointer is not 16-byte aligned");
+  const size_t need = mamba2_conv1d_silu_bwd_workspace_bytes(batch, seqlen, d_inner, ngroups, dstate, d_conv);
+  if (!workspace || workspace_bytes < need)
+    return fail(SSD_ERR_WORKSPACE, "conv1d_silu_bwd: workspace of %zu bytes is smaller than the %zu needed",
+                workspace ? workspace_bytes : 0, need);
+  SSD_LAUNCH(ssd::launch_conv_bwd(static_cast<int>(batch), static_cast<int>(seqlen), static_cast<int>(d_inner),
+                                  static_cast<int>(ngroups * dstate), static_cast<int>(d_conv),
+                                  static_cast<ssd::DType>(dtype), xbc, w, bias, dx, dB, dC, dxbc, dw, dbias,
+                                  static_cast<float*>(workspace), st),
+             "conv1d_silu_bwd");
+  return ok();
+}
+
+static int check_rms(int64_t rows, int64_t width, int32_t dtype) {
+  if (!valid_dtype(dtype)) return fail(SSD_ERR_DTYPE, "rmsnorm_gated: dtype %d is not SSD_F32 or SSD_BF16", dtype);
+  if (rows < 0 || width <= 0) return fail(SSD_ERR_INVALID_ARG, "rmsnorm_gated: rows >= 0 and width > 0 required");
+  if (width > ssd::rms_max_width())
+    return fail(SSD_ERR_SHAPE, "rmsnorm_gated: width %lld exceeds %d", (long long)width, ssd::rms_max_width());
+  if (rows > (int64_t(1) << 31) - 1) return fail(SSD_ERR_SHAPE, "rmsnorm_gated: too many rows");
+  return SSD_OK;
+}
+
+size_t mamba2_rmsnorm_gated_bwd_workspace_bytes(int64_t rows, int64_t width) {
+  if (check_rms(rows, width, SSD_F32) != SSD_OK || rows == 0) return 0;
+  return align_up(sizeof(float) * static_cast<size_t>(ssd::rms_nparts(rows)) * width);
+}
+
+int mamba2_rmsnorm_gated_fwd(int64_t rows, int64_t width, float eps, int32_t dtype, const void* y, const void* z,
+                             const float* w, void* out, float* inv_rms, void* stream) {
+  int rc = check_rms(rows, width, dtype);
+  if (rc != SSD_OK) return rc;
+  if (rows == 0) return ok();
+  if (!y || !z || !w || !out || !inv_rms)
+    return fail(SSD_ERR_INVALID_ARG, "rmsnorm_gated_fwd: y, z, w, out and inv_rms are required");
+  if (!(eps >= 0.f)) return fail(SSD_ERR_INVALID_ARG, "rmsnorm_gated_fwd: eps must be >= 0");
+  const void* ptrs[] = {y, z, w, out, inv_rms};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return fail(SSD_ERR_ALIGN, "rmsnorm_gated_fwd: a tensor pointer is not 16-byte aligned");
+  SSD_LAUNCH(ssd::launch_rms_fwd(rows, static_cast<int>(width), eps, static_cast<ssd::DType>(dtype), y, z, w, out,
+                                 inv_rms, static_cast<hipStream_t>(stream)),
+             "rmsnorm_gated_fwd");
+  return ok();
+}
+
+int mamba2_rmsnorm_gated_bwd(int64_t rows, int64_t width, int32_t dtype, int32_t g_dtype, const void* y,
+                             const void* z, const float* w, const float* inv_rms, const void* g, float* dy,
+                             float* dz, float* dw, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_rms(rows, width, dtype);
+  if (rc != SSD_OK) return rc;
+  if (!valid_dtype(g_dtype)) return fail(SSD_ERR_DTYPE, "rmsnorm_gated_bwd: g_dtype %d is not SSD_F32 or SSD_BF16", g_dtype);
+  if (!dw) return fail(SSD_ERR_INVALID_ARG, "rmsnorm_gated_bwd: dw is required");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (rows == 0) {
+    SSD_LAUNCH(ssd::launch_fill(dw, width, 0.f, st), "fill");
+    return ok();
+  }
+  if (!y || !z || !w || !inv_rms || !g || !dy || !dz)
+    return fail(SSD_ERR_INVALID_ARG, "rmsnorm_gated_bwd: y, z, w, inv_rms, g, dy and dz are required");
+  const void* ptrs[] = {y, z, w, inv_rms, g, dy, dz, dw, workspace};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return fail(SSD_ERR_ALIGN, "rmsnorm_gated_bwd: a pointer is not 16-byte aligned");
+  const size_t need = mamba2_rmsnorm_gated_bwd_workspace_bytes(rows, width);
+  if (!workspace || workspace_bytes < need)
+    return fail(SSD_ERR_WORKSPACE, "rmsnorm_gated_bwd: workspace of %zu bytes is smaller than the %zu needed",
+                workspace ? workspace_bytes : 0, need);
+  SSD_LAUNCH(ssd::launch_rms_bwd(rows, static_cast<int>(width), static_cast<ssd::DType>(dtype),
+                                 static_cast<ssd::DType>(g_dtype), y, z, w, inv_rms, g, dy, dz, dw,
+                                 static_cast<float*>(workspace), st),
+             "rmsnorm_gated_bwd");
+  return ok();
+}
+
+}  // extern "C"

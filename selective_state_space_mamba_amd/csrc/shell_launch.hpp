@@ -1,0 +1,29 @@
+// Host-side launchers of the block-shell kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ssd_launch.hpp"
+
+namespace ssd {
+
+int conv_nruns(int T);
+int rms_nparts(int64_t rows);
+int rms_max_width();
+int conv_max_k();
+
+hipError_t launch_conv_fwd(int b, int T, int d_inner, int gn, int K, DType dt, const void* xbc, const float* w,
+                           const float* bias, void* x_out, void* B_out, void* C_out, hipStream_t st);
+// part: [b * conv_nruns(T), conv_dim, K + 1] floats of scratch
+hipError_t launch_conv_bwd(int b, int T, int d_inner, int gn, int K, DType dt, const void* xbc, const float* w,
+                           const float* bias, const float* dx, const float* dB, const float* dC, float* dxbc,
+                           float* dw, float* dbias, float* part, hipStream_t st);
+hipError_t launch_rms_fwd(int64_t rows, int width, float eps, DType dt, const void* y, const void* z, const float* w,
+                          void* out, float* inv_rms, hipStream_t st);
+// part: [rms_nparts(rows), width] floats of scratch
+hipError_t launch_rms_bwd(int64_t rows, int width, DType dt, DType gt, const void* y, const void* z, const float* w,
+                          const float* inv_rms, const void* g, float* dy, float* dz, float* dw, float* part,
+                          hipStream_t st);
+
+}  // namespace ssd

@@ -1,0 +1,186 @@
+// Device building blocks shared by the SSD kernels (gfx950, wave64).
+//
+// MFMA tiles are 16x16 (v_mfma_f32_16x16x4_f32 for f32 operands,
+// v_mfma_f32_16x16x32_bf16 for bf16 operands), both accumulating in f32.
+// Lane l of a wave holds r = l % 16, q = l / 16; operand fragments are
+//   f32 : A[r][k0+q],          B[k0+q][r]
+//   bf16: A[r][k0+8q .. +7],   B[k0+8q .. +7][r]
+// and the 16x16 f32 result element i (0..3) of lane l is C[4q+i][r].
+//
+// Operands are staged in LDS.  A "view" of an LDS matrix gives the element
+// (row, k) at p[row*sr + k*sk]; when sk == 1 (k contiguous) a bf16 fragment is
+// one 16-byte LDS read, otherwise eight 2-byte reads.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssd {
+
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int WAVE = 64;
+constexpr int NTHREADS = 256;  // 4 waves per workgroup
+constexpr int BQ = 64;         // rows per block of a chunk
+constexpr int PMAX = 64;       // largest headdim the kernels take
+constexpr int NMAX = 128;      // largest d_state the kernels take
+constexpr int QMAX = 256;      // largest chunk the kernels take
+constexpr int NBMAX = QMAX / BQ;
+
+// ---------------------------------------------------------------- scalars
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t v) {
+  return __uint_as_float(static_cast<uint32_t>(v) << 16);
+}
+
+// f32 -> bf16 bits, round to nearest even (inputs are finite).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+__device__ __forceinline__ float load_f(const float* p, int64_t i) { return p[i]; }
+__device__ __forceinline__ float load_f(const uint16_t* p, int64_t i) { return bf16_bits_to_f32(p[i]); }
+
+__device__ __forceinline__ void store_f(float* p, int64_t i, float v) { p[i] = v; }
+__device__ __forceinline__ void store_f(uint16_t* p, int64_t i, float v) { p[i] = f32_to_bf16_bits(v); }
+
+// ------------------------------------------------------------- MFMA types
+
+template <bool BF> struct Op;
+template <> struct Op<false> {
+  typedef float T;  // LDS element
+  typedef float V;  // fragment
+  static constexpr int KS = 4;
+  static __device__ __forceinline__ T cvt(float v) { return v; }
+  static __device__ __forceinline__ float back(T v) { return v; }
+};
+template <> struct Op<true> {
+  typedef uint16_t T;
+  typedef bf16x8 V;
+  static constexpr int KS = 32;
+  static __device__ __forceinline__ T cvt(float v) { return f32_to_bf16_bits(v); }
+  static __device__ __forceinline__ float back(T v) { return bf16_bits_to_f32(v); }
+};
+
+__device__ __forceinline__ f4 mfma(float a, float b, f4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f4 mfma(bf16x8 a, bf16x8 b, f4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (WAVE - 1); }
+__device__ __forceinline__ int wave_id() { return threadIdx.x / WAVE; }
+
+// Fragment of rows r0..r0+15 and k-slice starting at k0 of an LDS view.
+template <bool BF, bool KC>
+__device__ __forceinline__ typename Op<BF>::V fetch(const typename Op<BF>::T* p, int sr, int sk,
+                                                    int r0, int k0) {
+  const int l = lane_id(), r = l & 15, q = l >> 4;
+  if constexpr (!BF) {
+    return p[(r0 + r) * sr + (k0 + q) * sk];
+  } else if constexpr (KC) {
+    return *reinterpret_cast<const bf16x8*>(p + (r0 + r) * sr + k0 + 8 * q);
+  } else {
+    bf16x8 v;
+    const uint16_t* b = p + (r0 + r) * sr + (k0 + 8 * q) * sk;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = __builtin_bit_cast(__bf16, b[e * sk]);
+    return v;
+  }
+}
+
+// acc[t] (16 x 16, columns 16t..16t+15) += A(16 x K) * B(K x 16*NT), where
+// A is the view (row = output row, k) and B the view (row = output column, k).
+// K must be a multiple of Op<BF>::KS; the LDS operands are zero beyond the
+// logical extent.
+template <bool BF, bool AKC, bool BKC, int NT>
+__device__ __forceinline__ void wave_gemm(f4 (&acc)[NT], const typename Op<BF>::T* A, int asr,
+                                          int ask, const typename Op<BF>::T* B, int bsr, int bsk,
+                                          int K) {
+  for (int k0 = 0; k0 < K; k0 += Op<BF>::KS) {
+    const typename Op<BF>::V a = fetch<BF, AKC>(A, asr, ask, 0, k0);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[t] = mfma(a, fetch<BF, BKC>(B, bsr, bsk, 16 * t, k0), acc[t]);
+  }
+}
+
+template <int NT>
+__device__ __forceinline__ void zero(f4 (&acc)[NT]) {
+#pragma unroll
+  for (int t = 0; t < NT; ++t) acc[t] = f4{0.f, 0.f, 0.f, 0.f};
+}
+
+__device__ __forceinline__ int round_up(int v, int m) { return (v + m - 1) / m * m; }
+
+// Sum over the 16 lanes that share q (one output row of an MFMA tile).
+__device__ __forceinline__ float sum16(float v) {
+  v += __shfl_xor(v, 1);
+  v += __shfl_xor(v, 2);
+  v += __shfl_xor(v, 4);
+  v += __shfl_xor(v, 8);
+  return v;
+}
+
+// Sum over the 4 lanes that share r (one output column across the q groups).
+__device__ __forceinline__ float sum_q(float v) {
+  v += __shfl_xor(v, 16);
+  v += __shfl_xor(v, 32);
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// Inclusive prefix sum over the 256 threads of the workgroup.  `tmp` holds 4
+// floats of LDS.  Every thread of the workgroup must call it.
+__device__ __forceinline__ float block_inclusive_scan(float v, float* tmp) {
+  const int l = lane_id(), w = wave_id();
+#pragma unroll
+  for (int o = 1; o < WAVE; o <<= 1) {
+    const float t = __shfl_up(v, o);
+    if (l >= o) v += t;
+  }
+  if (l == WAVE - 1) tmp[w] = v;
+  __syncthreads();
+  float off = 0.f;
+  for (int i = 0; i < w; ++i) off += tmp[i];
+  __syncthreads();
+  return v + off;
+}
+
+// Copy a rows x cols tile from global memory (row r at src + r*ld_src, columns
+// contiguous) into LDS, converting to the operand type.  Elements with
+// r >= rows_valid or c >= cols_valid are written as zero.  Transposed (TR)
+// writes put element (r, c) at dst[c*ld_dst + r], else dst[r*ld_dst + c].
+// Optional per-row scale.
+template <typename TS, typename TD, bool TR>
+__device__ __forceinline__ void stage_tile(TD* dst, int ld_dst, const TS* src, int64_t ld_src,
+                                           int rows, int cols, int rows_valid, int cols_valid,
+                                           const float* row_scale = nullptr) {
+  for (int idx = threadIdx.x; idx < rows * cols; idx += NTHREADS) {
+    const int r = idx / cols, c = idx % cols;
+    float v = 0.f;
+    if (r < rows_valid && c < cols_valid) {
+      v = load_f(src, r * ld_src + c);
+      if (row_scale) v *= row_scale[r];
+    }
+    TD o;
+    if constexpr (sizeof(TD) == 4)
+      o = v;
+    else
+      o = f32_to_bf16_bits(v);
+    if constexpr (TR)
+      dst[c * ld_dst + r] = o;
+    else
+      dst[r * ld_dst + c] = o;
+  }
+}
+
+}  // namespace ssd

@@ -1,0 +1,74 @@
+// Host-side launchers of the SSD kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssd {
+
+enum DType : int { F32 = 0, BF16 = 1 };
+
+struct Dims {
+  int b, T, H, P, N, G, Q;
+  int nc() const { return T / Q; }
+  int nb() const { return (Q + 63) / 64; }
+  int hpg() const { return H / G; }
+};
+
+// Number of headdim rows one chunk-state workgroup owns.
+constexpr int STATE_PB = 16;
+inline int state_npb(const Dims& d) { return (d.P + STATE_PB - 1) / STATE_PB; }
+
+// Forward state passing: states[b,c,h] = state entering chunk c, final = state
+// after the last chunk.  `init` may be null (zero initial state), `final_state`
+// may be null.
+hipError_t launch_chunk_state_fwd(const Dims& d, DType act, const void* x, const void* B,
+                                  const void* dt, const float* A_log, const float* init,
+                                  float* states, float* final_state, hipStream_t st);
+
+// Reverse state-gradient pass: gamma[b,c,h] = gradient reaching the state that
+// leaves chunk c; dinit = gradient of the initial state (nullable);
+// gh_part[b,c,h,pb] = partial <gamma[b,c,h], states[b,c,h]> over headdim block pb.
+hipError_t launch_chunk_state_bwd(const Dims& d, DType act, DType dyt, const void* dy,
+                                  const void* C, const void* dt, const float* A_log,
+                                  const float* states, float* gamma, float* dinit, float* gh_part,
+                                  hipStream_t st);
+
+hipError_t launch_chunk_out_fwd(const Dims& d, DType act, int nsplit, const void* x, const void* B,
+                                const void* C, const void* dt, const float* A_log, const float* D,
+                                const float* states, void* y, hipStream_t st);
+
+struct BwdScratch {
+  float* rowM;   // [b,H,T] strictly-lower row sums of the decay-gradient matrix
+  float* colE;   // [b,H,T] column sums (diagonal included) without the dt factor
+  float* diagE;  // [b,H,T] diagonal entries
+  float* Rp;     // [b,H,T] state-term of the dt gradient without the dt factor
+  float* dsoff;  // [b,H,T] decay gradient from the incoming-state readout
+  float* gh_part;  // [b,nc,H,npb]
+  float* dA_part;  // [b,nc,H]
+  float* dD_part;  // [b,nc,nb,H]
+  float* dB_part;  // [nsplit,b,T,G,N] or null when nsplit == 1
+  float* dC_part;
+};
+
+hipError_t launch_chunk_bwd_col(const Dims& d, DType act, DType dyt, int nsplit, const void* x,
+                                const void* B, const void* C, const void* dt, const void* dy,
+                                const float* A_log, const float* D, const float* gamma, float* dx,
+                                float* dB_out, const BwdScratch& s, hipStream_t st);
+
+hipError_t launch_chunk_bwd_row(const Dims& d, DType act, DType dyt, int nsplit, const void* x,
+                                const void* B, const void* C, const void* dt, const void* dy,
+                                const float* A_log, const float* states, float* dC_out,
+                                const BwdScratch& s, hipStream_t st);
+
+hipError_t launch_bwd_dt(const Dims& d, DType act, const void* dt, const float* A_log, float* ddt,
+                         const BwdScratch& s, hipStream_t st);
+
+hipError_t launch_bwd_reduce(const Dims& d, int nsplit, const float* A_log, float* dA_log,
+                             float* dD, float* dB, float* dC, const BwdScratch& s, hipStream_t st);
+
+// Writes `value` into n floats (used for empty problems).
+hipError_t launch_fill(float* p, int64_t n, float value, hipStream_t st);
+hipError_t launch_copy(float* dst, const float* src, int64_t n, hipStream_t st);
+
+}  // namespace ssd

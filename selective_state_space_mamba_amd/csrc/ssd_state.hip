@@ -1,0 +1,169 @@
+// Inter-chunk state passing (forward) and the reverse-time state-gradient pass
+// (backward) of the chunked SSD.
+//
+// The recurrence h_t = exp(dt_t A) h_{t-1} + dt_t x_t (outer) B_t of the page-1
+// reference (burn_dragon_kernel mamba2/backward.rs,
+// ssd_forward_state_history_reference), unrolled over one chunk of Q steps with
+// s_i = sum_{r<=i} dt_r A (within the chunk), gives
+//
+//   H_{c+1} = exp(s_end) H_c + sum_j exp(s_end - s_j) dt_j x_j (outer) B_j.
+//
+// The reverse-time loop of ssd_backward_reference carries
+// G_t = dy_t (outer) C_t + exp(dt_{t+1} A) G_{t+1}; unrolled over a chunk,
+//
+//   Gamma_c = exp(s_end) Gamma_{c+1} + sum_i exp(s_i) dy_i (outer) C_i,
+//
+// with Gamma_nc = 0 and d(initial state) = Gamma_0.
+//
+// Both are one kernel: a workgroup owns 16 headdim rows of one (batch, head)
+// and walks the chunks in order (forward) or in reverse (backward), keeping its
+// 16 x N slice of the state in registers.  Per chunk the weighted sum is one
+// MFMA contraction over the chunk's time steps (K = Q), the operands staged in
+// LDS in 64-step slabs.  Rows of the state are independent, so the headdim
+// split needs no communication.  All decay factors are exp of non-positive
+// numbers (dt > 0, A < 0).
+#include "ssd_common.hpp"
+#include "ssd_launch.hpp"
+
+namespace ssd {
+
+template <typename TX, typename TB, typename TDT, bool BF, bool REV>
+__global__ __launch_bounds__(NTHREADS) void chunk_state_kernel(
+    const TX* __restrict__ X,          // fwd: x; bwd: dy            [b,T,H,P]
+    const TB* __restrict__ Bm,         // fwd: B; bwd: C             [b,T,G,N]
+    const TDT* __restrict__ dt,        // [b,T,H]
+    const float* __restrict__ A_log,   // [H]
+    const float* __restrict__ init,    // fwd: initial state (nullable); bwd: unused
+    float* __restrict__ states_out,    // fwd: H_c; bwd: Gamma_{c+1}    [b,nc,H,P,N]
+    float* __restrict__ last_out,      // fwd: final state; bwd: d(initial state) (nullable)
+    const float* __restrict__ hstates, // bwd: H_c, for <Gamma_{c+1}, H_c>
+    float* __restrict__ gh_part,       // bwd: [b,nc,H,npb]
+    int T, int H, int P, int N, int G, int Q) {
+  typedef typename Op<BF>::T OT;
+  constexpr int PB = STATE_PB;
+  constexpr int LDX = BQ + (BF ? 8 : 4);  // [p][j] and [n][j]: time contiguous
+  __shared__ __attribute__((aligned(16))) OT sX[PB * LDX];
+  __shared__ __attribute__((aligned(16))) OT sB[NMAX * LDX];
+  __shared__ float sS[QMAX];
+  __shared__ float sW[QMAX];
+  __shared__ float sTmp[8];
+
+  const int pb = blockIdx.x, h = blockIdx.y, bi = blockIdx.z;
+  const int npb = gridDim.x;
+  const int p0 = pb * PB;
+  const int g = h / (H / G);
+  const int nc = T / Q, nb = (Q + BQ - 1) / BQ;
+  const float A = -__expf(A_log[h]);
+  const int tid = threadIdx.x, w = wave_id(), l = lane_id(), r = l & 15, q = l >> 4;
+  const int64_t HP = static_cast<int64_t>(H) * P;
+  const int64_t PN = static_cast<int64_t>(P) * N;
+
+  // wave w holds state columns n = 32w .. 32w+31 (two 16-wide tiles) of rows p0..p0+15
+  f4 st[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int p = p0 + 4 * q + i, n = 32 * w + 16 * t + r;
+      st[t][i] = (!REV && init && p < P && n < N) ? init[(static_cast<int64_t>(bi) * H + h) * PN + p * N + n] : 0.f;
+    }
+
+  for (int it = 0; it < nc; ++it) {
+    const int c = REV ? nc - 1 - it : it;
+    const int64_t t0 = static_cast<int64_t>(c) * Q;
+    const float dtv = (tid < Q) ? load_f(dt, (static_cast<int64_t>(bi) * T + t0 + tid) * H + h) : 0.f;
+    const float s = block_inclusive_scan(dtv * A, sTmp);
+    if (tid < Q) sS[tid] = s;
+    __syncthreads();
+    const float s_end = sS[Q - 1];
+    if (tid < Q) sW[tid] = REV ? __expf(s) : __expf(s_end - s) * dtv;
+
+    f4 acc[2];
+    zero(acc);
+    for (int jb = 0; jb < nb; ++jb) {
+      const int j0 = jb * BQ, vr = min(BQ, Q - j0);
+      __syncthreads();
+      stage_tile<TX, OT, true>(sX, LDX, X + ((static_cast<int64_t>(bi) * T + t0 + j0) * H + h) * P + p0,
+                               HP, BQ, PB, vr, P - p0, sW + j0);
+      stage_tile<TB, OT, true>(sB, LDX, Bm + ((static_cast<int64_t>(bi) * T + t0 + j0) * G + g) * N,
+                               static_cast<int64_t>(G) * N, BQ, NMAX, vr, N);
+      __syncthreads();
+      wave_gemm<BF, true, true, 2>(acc, sX, LDX, 1, sB + 32 * w * LDX, LDX, 1, BQ);
+    }
+
+    const float decay = __expf(s_end);
+    const int64_t sbase = ((static_cast<int64_t>(bi) * nc + c) * H + h) * PN;
+    float gh = 0.f;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int p = p0 + 4 * q + i, n = 32 * w + 16 * t + r;
+        if (p < P && n < N) {
+          if (states_out) states_out[sbase + p * N + n] = st[t][i];
+          if (REV) gh += st[t][i] * hstates[sbase + p * N + n];
+        }
+        st[t][i] = decay * st[t][i] + acc[t][i];
+      }
+    if (REV) {
+      gh = wave_sum(gh);
+      __syncthreads();
+      if (l == 0) sTmp[4 + w] = gh;
+      __syncthreads();
+      if (tid == 0)
+        gh_part[((static_cast<int64_t>(bi) * nc + c) * H + h) * npb + pb] =
+            sTmp[4] + sTmp[5] + sTmp[6] + sTmp[7];
+    }
+  }
+
+  if (last_out) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int p = p0 + 4 * q + i, n = 32 * w + 16 * t + r;
+        if (p < P && n < N) last_out[(static_cast<int64_t>(bi) * H + h) * PN + p * N + n] = st[t][i];
+      }
+  }
+}
+
+template <typename TX, typename TB, bool BF, bool REV>
+static hipError_t launch_state(const Dims& d, const void* X, const void* Bm, const void* dt,
+                               const float* A_log, const float* init, float* states, float* last,
+                               const float* hstates, float* gh_part, hipStream_t st) {
+  dim3 grid(state_npb(d), d.H, d.b);
+  hipLaunchKernelGGL((chunk_state_kernel<TX, TB, TB, BF, REV>), grid, dim3(NTHREADS), 0, st,
+                     static_cast<const TX*>(X), static_cast<const TB*>(Bm), static_cast<const TB*>(dt),
+                     A_log, init, states, last, hstates, gh_part, d.T, d.H, d.P, d.N, d.G, d.Q);
+  return hipGetLastError();
+}
+
+hipError_t launch_chunk_state_fwd(const Dims& d, DType act, const void* x, const void* B,
+                                  const void* dt, const float* A_log, const float* init,
+                                  float* states, float* final_state, hipStream_t st) {
+  if (act == BF16)
+    return launch_state<uint16_t, uint16_t, true, false>(d, x, B, dt, A_log, init, states, final_state,
+                                                         nullptr, nullptr, st);
+  return launch_state<float, float, false, false>(d, x, B, dt, A_log, init, states, final_state, nullptr,
+                                                  nullptr, st);
+}
+
+hipError_t launch_chunk_state_bwd(const Dims& d, DType act, DType dyt, const void* dy,
+                                  const void* C, const void* dt, const float* A_log,
+                                  const float* states, float* gamma, float* dinit, float* gh_part,
+                                  hipStream_t st) {
+  if (act == BF16) {
+    if (dyt == BF16)
+      return launch_state<uint16_t, uint16_t, true, true>(d, dy, C, dt, A_log, nullptr, gamma, dinit,
+                                                          states, gh_part, st);
+    return launch_state<float, uint16_t, true, true>(d, dy, C, dt, A_log, nullptr, gamma, dinit, states,
+                                                     gh_part, st);
+  }
+  if (dyt == BF16)
+    return launch_state<uint16_t, float, false, true>(d, dy, C, dt, A_log, nullptr, gamma, dinit, states,
+                                                      gh_part, st);
+  return launch_state<float, float, false, true>(d, dy, C, dt, A_log, nullptr, gamma, dinit, states,
+                                                 gh_part, st);
+}
+
+}  // namespace ssd

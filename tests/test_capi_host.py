@@ -1,0 +1,157 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/ssd.h declares, and rejects bad arguments with the documented status
+before enqueuing anything (these paths make no HIP call)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from selective_state_space_mamba_amd import _binding as bd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ssd.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(bd.library_path()):
+        from selective_state_space_mamba_amd.build import build
+        build()
+    return bd.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", text, flags=re.M)
+    return sorted(set(n for n in names if n not in ("if", "sizeof")))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("ssd_fwd", "ssd_bwd", "ssd_workspace_bytes", "ssd_last_error", "mamba2_conv1d_silu_fwd",
+              "mamba2_conv1d_silu_bwd", "mamba2_rmsnorm_gated_fwd", "mamba2_rmsnorm_gated_bwd"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+    assert "gfx950" in lib.ssd_version().decode()
+
+
+def prob(**kw):
+    base = dict(batch=2, seqlen=512, nheads=8, headdim=64, dstate=128, ngroups=2, chunk=256, act_dtype=0, dy_dtype=0)
+    base.update(kw)
+    return bd.Problem(**base)
+
+
+FAKE = 1 << 20  # a 16-byte aligned non-null address that is never dereferenced
+
+
+def call_fwd(lib, p, ws_bytes=1 << 30, misalign=None, null=None):
+    ptrs = {k: ctypes.c_void_p(FAKE) for k in ("x", "dt", "A_log", "B", "C", "D", "y", "ws")}
+    if misalign:
+        ptrs[misalign] = ctypes.c_void_p(FAKE + 2)
+    if null:
+        ptrs[null] = None
+    return lib.ssd_fwd(ctypes.byref(p), ptrs["x"], ptrs["dt"], ptrs["A_log"], ptrs["B"], ptrs["C"], ptrs["D"],
+                       None, ptrs["y"], None, None, ptrs["ws"], ws_bytes, None)
+
+
+def call_bwd(lib, p, ws_bytes=1 << 30, misalign=None, null=None):
+    names = ("x", "dt", "A_log", "B", "C", "D", "dy", "dx", "ddt", "dA_log", "dB", "dC", "dD", "ws")
+    ptrs = {k: ctypes.c_void_p(FAKE) for k in names}
+    if misalign:
+        ptrs[misalign] = ctypes.c_void_p(FAKE + 4)
+    if null:
+        ptrs[null] = None
+    return lib.ssd_bwd(ctypes.byref(p), ptrs["x"], ptrs["dt"], ptrs["A_log"], ptrs["B"], ptrs["C"], ptrs["D"],
+                       None, None, ptrs["dy"], ptrs["dx"], ptrs["ddt"], ptrs["dA_log"], ptrs["dB"], ptrs["dC"],
+                       ptrs["dD"], None, ptrs["ws"], ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status,text", [
+    (dict(act_dtype=7), -3, "act_dtype"),
+    (dict(dy_dtype=-1), -3, "dy_dtype"),
+    (dict(headdim=65), -2, "headdim"),
+    (dict(dstate=129), -2, "dstate"),
+    (dict(chunk=512, seqlen=1024), -2, "chunk"),
+    (dict(seqlen=500), -2, "multiple of chunk"),
+    (dict(nheads=6, ngroups=4), -2, "multiple of ngroups"),
+    (dict(nheads=0), -1, "must be > 0"),
+    (dict(batch=-1), -1, ">= 0"),
+])
+def test_invalid_problem_statements(lib, kw, status, text):
+    p = prob(**kw)
+    for f in (call_fwd, call_bwd):
+        assert f(lib, p) == status
+        assert text in lib.ssd_last_error().decode()
+    assert lib.ssd_workspace_bytes(ctypes.byref(p), 1, 0) == 0
+
+
+def test_null_problem(lib):
+    assert lib.ssd_fwd(None, *([None] * 10), None, 0, None) == -1
+    assert "null" in lib.ssd_last_error().decode()
+
+
+@pytest.mark.parametrize("which", ["x", "dt", "B", "C", "y", "A_log", "D"])
+def test_fwd_null_required_pointer(lib, which):
+    assert call_fwd(lib, prob(), null=which) == -1
+
+
+@pytest.mark.parametrize("which", ["dy", "dx", "ddt", "dB", "dC", "dA_log", "dD"])
+def test_bwd_null_required_pointer(lib, which):
+    assert call_bwd(lib, prob(), null=which) == -1
+
+
+def test_misaligned_pointer(lib):
+    assert call_fwd(lib, prob(), misalign="B") == -6
+    assert call_bwd(lib, prob(), misalign="dy") == -6
+
+
+def test_workspace_too_small(lib):
+    p = prob()
+    need_f = lib.ssd_workspace_bytes(ctypes.byref(p), 0, 0)
+    need_b = lib.ssd_workspace_bytes(ctypes.byref(p), 1, 0)
+    assert need_f > 0 and need_b > need_f
+    assert call_fwd(lib, p, ws_bytes=need_f - 1) == -4
+    assert call_bwd(lib, p, ws_bytes=need_b - 1) == -4
+    assert call_bwd(lib, p, null="ws") == -4
+    assert "workspace" in lib.ssd_last_error().decode()
+
+
+def test_workspace_sizes_follow_the_plan(lib):
+    # forward: the chunk states, unless the caller passes them
+    p = prob()
+    nc = 512 // 256
+    states = 4 * 2 * nc * 8 * 64 * 128
+    assert lib.ssd_workspace_bytes(ctypes.byref(p), 0, 0) == states
+    assert lib.ssd_workspace_bytes(ctypes.byref(p), 0, 1) == 0
+    # backward needs at least the state gradients, plus the states in recompute mode
+    wb1 = lib.ssd_workspace_bytes(ctypes.byref(p), 1, 1)
+    wb0 = lib.ssd_workspace_bytes(ctypes.byref(p), 1, 0)
+    assert wb1 >= states and wb0 == wb1 + states
+
+
+def test_shell_argument_checks(lib):
+    f = ctypes.c_void_p(FAKE)
+    assert lib.mamba2_conv1d_silu_fwd(1, 8, 64, 1, 16, 9, 0, f, f, f, f, f, f, None) == -2  # d_conv > 8
+    assert lib.mamba2_conv1d_silu_fwd(1, 8, 64, 1, 16, 4, 5, f, f, f, f, f, f, None) == -3
+    assert lib.mamba2_conv1d_silu_fwd(1, 8, 64, 1, 16, 4, 0, None, f, f, f, f, f, None) == -1
+    assert lib.mamba2_rmsnorm_gated_fwd(4, 5000, 1e-5, 0, f, f, f, f, f, None) == -2
+    assert lib.mamba2_rmsnorm_gated_fwd(4, 64, 1e-5, 0, f, None, f, f, f, None) == -1
+    need = lib.mamba2_rmsnorm_gated_bwd_workspace_bytes(100, 64)
+    assert need > 0
+    assert lib.mamba2_rmsnorm_gated_bwd(100, 64, 0, 0, f, f, f, f, f, f, f, f, f, need - 1, None) == -4
+    assert lib.mamba2_conv1d_silu_bwd_workspace_bytes(2, 300, 64, 1, 16, 4) > 0
+
+
+def test_product_path_does_not_import_the_oracle():
+    pkg = os.path.join(ROOT, "selective_state_space_mamba_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for fn in files:
+            if fn.endswith((".py", ".cpp", ".hip", ".hpp", ".h")):
+                text = open(os.path.join(dirpath, fn)).read()
+                assert "oracle" not in text.lower(), fn
