@@ -1,0 +1,251 @@
+#!/usr/bin/env python3
+"""SSD fwd+bwd throughput on one MI355X.
+
+One step = ssd_fwd (saving the chunk states) + ssd_bwd (reading them) over one
+batch of synthetic input already resident in HBM; for the block-slice workload
+the step also runs conv1d+SiLU and RMSNorm-gated forward and backward.
+Prints ONE JSON line on stdout (progress goes to stderr).
+
+The default workload is the grouped bf16 configuration (b=4, T=2048, H=32,
+P=64, N=128, G=8, chunk 256), the one the performance target is quoted on.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "SSD fwd+bwd tokens/sec on 1 MI355X; achieved HBM GB/s and MFMA % of peak"
+HBM_PEAK_GBS = 8000.0
+KERNELS_FWD = ["chunk_state_fwd", "chunk_out_fwd"]
+KERNELS_BWD = ["chunk_state_bwd", "chunk_bwd_col", "chunk_bwd_row", "bwd_dt", "bwd_reduce"]
+KERNELS_SHELL = ["conv1d_silu_fwd", "rmsnorm_gated_fwd", "rmsnorm_gated_bwd", "conv1d_silu_bwd"]
+KERNEL_SOURCES = {
+    "chunk_state_fwd": ["ssd_state.hip", "ssd_common.hpp"],
+    "chunk_state_bwd": ["ssd_state.hip", "ssd_common.hpp"],
+    "chunk_out_fwd": ["ssd_chunk_fwd.hip", "ssd_common.hpp"],
+    "chunk_bwd_col": ["ssd_chunk_bwd.hip", "ssd_common.hpp"],
+    "chunk_bwd_row": ["ssd_chunk_bwd.hip", "ssd_common.hpp"],
+    "bwd_dt": ["ssd_chunk_bwd.hip", "ssd_common.hpp"],
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(cfg, kernel: str) -> float:
+    """Bytes one launch must move at minimum: each input it needs read once and
+    each output written once, at the storage dtypes (the per-token figures are
+    listed in the design doc)."""
+    s_a = 2 if cfg.dtype == "bf16" else 4
+    s_y = s_a
+    tok = cfg.batch * cfg.seqlen
+    HP, GN, H = cfg.nheads * cfg.headdim, cfg.ngroups * cfg.dstate, cfg.nheads
+    st = H * cfg.headdim * cfg.dstate * 4 / cfg.chunk  # chunk states per token (f32)
+    per_token = {
+        "chunk_state_fwd": HP * s_a + GN * s_a + H * s_a + st,
+        "chunk_out_fwd": HP * s_a + 2 * GN * s_a + H * s_a + st + HP * s_a,
+        "chunk_state_bwd": HP * s_y + GN * s_a + H * s_a + 2 * st,
+        "chunk_bwd_col": HP * s_a + 2 * GN * s_a + H * s_a + HP * s_y + st + HP * 4 + GN * 4 + 3 * H * 4,
+        "chunk_bwd_row": HP * s_a + 2 * GN * s_a + H * s_a + HP * s_y + st + GN * 4 + 2 * H * 4,
+        "bwd_dt": H * s_a + 5 * H * 4 + H * 4,
+    }
+    return per_token[kernel] * tok
+
+
+def algorithmic_flops(cfg, kernel: str) -> float:
+    """Useful MFMA flops of one launch (causal halves counted once)."""
+    Q, P, N, H, G = cfg.chunk, cfg.headdim, cfg.dstate, cfg.nheads, cfg.ngroups
+    tok = cfg.batch * cfg.seqlen
+    per_token = {
+        "chunk_state_fwd": 2 * H * P * N,
+        "chunk_out_fwd": 2 * (0.5 * G * Q * N + 0.5 * H * Q * P + H * P * N),
+        "chunk_state_bwd": 2 * H * P * N,
+        "chunk_bwd_col": 2 * (0.5 * G * Q * N + 0.5 * G * Q * N + H * Q * P + 2 * H * P * N),
+        "chunk_bwd_row": 2 * (0.5 * G * Q * N + 0.5 * G * Q * N + 0.5 * H * Q * P + H * P * N),
+        "bwd_dt": 0.0,
+    }
+    return per_token[kernel] * tok
+
+
+def source_digest(kernel: str) -> str:
+    h = hashlib.sha256()
+    for fn in KERNEL_SOURCES.get(kernel, []):
+        with open(os.path.join(ROOT, "selective_state_space_mamba_amd", "csrc", fn), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when there is none or the kernel's sources changed since."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_hbm_counters.txt")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_src = re.search(r"^source_digest:\s*(\S+)", text, re.M)
+    m_b = re.search(r"^hbm_bytes_per_launch:\s*([0-9.eE+]+)", text, re.M)
+    if not m_src or not m_b or m_src.group(1) != source_digest(kernel):
+        return None
+    return float(m_b.group(1))
+
+
+def to_dev(a):
+    import numpy as np
+    import torch
+    from ssd_inputs import Stored
+    if a is None:
+        return None
+    if isinstance(a, Stored):
+        if a.dtype == "bf16":
+            return torch.from_numpy(a.raw.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(np.ascontiguousarray(a.raw)).cuda()
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+
+
+def make_step(cfg, d):
+    import torch
+    import selective_state_space_mamba_amd as ssd
+    x, dt, B, C = to_dev(d["x"]), to_dev(d["dt"]), to_dev(d["B"]), to_dev(d["C"])
+    A_log, D, h0 = to_dev(d["A_log"]), to_dev(d["D"]), to_dev(d.get("h0"))
+    dy = to_dev(d["dy"])
+    f32 = dict(dtype=torch.float32, device="cuda")
+    b, T, H, P, N, G, Q = cfg.batch, cfg.seqlen, cfg.nheads, cfg.headdim, cfg.dstate, cfg.ngroups, cfg.chunk
+    fo = {"y": torch.empty_like(x), "final_state": torch.empty((b, H, P, N), **f32),
+          "chunk_states": torch.empty((b, T // Q, H, P, N), **f32)}
+    go = {"dx": torch.empty((b, T, H, P), **f32), "ddt": torch.empty((b, T, H), **f32),
+          "dA_log": torch.empty(H, **f32), "dB": torch.empty((b, T, G, N), **f32),
+          "dC": torch.empty((b, T, G, N), **f32), "dD": torch.empty(H, **f32),
+          "d_init_state": torch.empty((b, H, P, N), **f32)}
+    if not cfg.shell:
+        prob = ssd._binding.make_problem(x, B, Q, dy.dtype)
+        wsf = torch.empty(max(1, ssd.ssd_workspace_bytes(prob, False, True)), dtype=torch.uint8, device="cuda")
+        wsb = torch.empty(max(1, ssd.ssd_workspace_bytes(prob, True, True)), dtype=torch.uint8, device="cuda")
+
+        def step():
+            ssd.ssd_fwd(x, dt, A_log, B, C, D, h0, chunk=Q, out=fo, workspace=wsf)
+            ssd.ssd_bwd(x, dt, A_log, B, C, D, dy, h0, chunk_states=fo["chunk_states"], chunk=Q, out=go,
+                        workspace=wsb)
+        return step
+
+    xbc, z, gout = to_dev(d["xBC"]), to_dev(d["z"]), to_dev(d["gout"])
+    conv_w, conv_b, norm_w = to_dev(d["conv_w"]), to_dev(d["conv_b"]), to_dev(d["norm_w"])
+    di = cfg.d_inner
+
+    def step():
+        xs, Bs, Cs = ssd.conv1d_silu_fwd(xbc, conv_w, conv_b, di, G, N)
+        xs = xs.view(b, T, H, P)
+        y, _, cs = ssd.ssd_fwd(xs, dt, A_log, Bs, Cs, D, h0, chunk=Q, out=fo)
+        out, inv = ssd.rmsnorm_gated_fwd(y.view(b, T, di), z, norm_w, cfg.norm_eps)
+        gy, gz, gw = ssd.rmsnorm_gated_bwd(y.view(b, T, di), z, norm_w, inv, gout)
+        g = ssd.ssd_bwd(xs, dt, A_log, Bs, Cs, D, gy.view(b, T, H, P), h0, chunk_states=cs, chunk=Q, out=go)
+        ssd.conv1d_silu_bwd(xbc, conv_w, conv_b, g["dx"].view(b, T, di), g["dB"], g["dC"], di, G, N)
+    return step
+
+
+def cpu_baseline(cfg, d, batches: int):
+    import numpy as np
+    import oracle
+    nb = min(cfg.batch, max(1, batches))
+    sl = slice(0, nb)
+    args = (d["x"].values[sl], d["dt"].values[sl], d["A_log"], d["B"].values[sl], d["C"].values[sl], d["D"])
+    h0 = None if d.get("h0") is None else d["h0"][sl]
+    threads = oracle.default_threads()
+    t0 = time.perf_counter()
+    oracle.ssd_fwd(*args, h0, chunk=cfg.chunk, nthreads=threads)
+    oracle.ssd_bwd(*args, d["dy"].values[sl], h0, nthreads=threads)
+    el = time.perf_counter() - t0
+    del np
+    return {"value": nb * cfg.seqlen / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": (f"sequential f64 oracle, SSD fwd+bwd on batch rows 0..{nb - 1} of {cfg.batch} "
+                       f"({nb * cfg.seqlen} tokens, {el:.1f} s wall on {threads} threads); tokens/s of that sample")}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="grouped", choices=["tiny", "m130", "grouped", "long", "block"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-batches", type=int, default=0, help="batch rows in the oracle sample (0: workload default)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): this build has no multi-GPU path; "
+              "see DESIGN.md for how the SSD would shard.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import selective_state_space_mamba_amd as ssd
+    from ssd_inputs import CONFIGS, make_inputs
+
+    cfg = CONFIGS[args.workload]
+    log(f"[bench] workload {cfg}")
+    d = make_inputs(cfg)
+    step = make_step(cfg, d)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"[bench] warmup {args.warmup} done; timing {args.steps} steps")
+
+    ssd.profile_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    kernels = KERNELS_FWD + KERNELS_BWD + (KERNELS_SHELL if cfg.shell else [])
+    kms = {}
+    for k in kernels:
+        ms, n = ssd.profile_kernel_ms(k)
+        if n:
+            kms[k] = ms / n
+    ssd.profile_enable(False)
+    ms_step = elapsed * 1e3 / args.steps
+    value = cfg.tokens * args.steps / elapsed
+    log(f"[bench] {ms_step:.3f} ms/step, {value:.4g} tokens/s; per-kernel ms: "
+        + " ".join(f"{k}={v:.4f}" for k, v in kms.items()))
+
+    core = {k: v for k, v in kms.items() if k in KERNEL_SOURCES}
+    dom = max(core, key=core.get)
+    t_dom = core[dom] * 1e-3
+    alg = algorithmic_bytes(cfg, dom)
+    achieved = alg / t_dom / 1e9
+    traffic = measured_traffic(dom, cfg.name)
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "kernel": dom, "kernel_ms": round(core[dom], 4), "algorithmic_bytes": alg,
+                "mfma_tflops": round(algorithmic_flops(cfg, dom) / t_dom / 1e12, 2)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the oracle on the host")
+        cpu = cpu_baseline(cfg, d, args.cpu_batches or (1 if cfg.shell else cfg.batch))
+
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16" if cfg.dtype == "bf16" else "f32", "data": "synthetic",
+        "config": {"workload": (f"{cfg.name}: b={cfg.batch} T={cfg.seqlen} H={cfg.nheads} P={cfg.headdim} "
+                                f"N={cfg.dstate} G={cfg.ngroups} chunk={cfg.chunk} {cfg.dtype}"
+                                + (" + conv1d/SiLU + RMSNorm-gated" if cfg.shell else "")),
+                   "global_batch": cfg.batch, "seq_len": cfg.seqlen, "parallelism": "single-gpu"},
+        "kernel_ms": {k: round(v, 4) for k, v in kms.items()},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -147,6 +147,18 @@ const char* ssd_last_error(void);
 /* Library version string. */
 const char* ssd_version(void);
 
+/* Opt-in per-kernel timing (a tracing aid, off by default).  ssd_profile_enable
+ * clears earlier records and turns recording on (on != 0) or off.  While on,
+ * every kernel an entry point launches is bracketed by two HIP events on the
+ * caller's stream.  ssd_profile_kernel_ms waits for the recorded events and
+ * returns the summed milliseconds and the number of launches of one kernel:
+ * "chunk_state_fwd", "chunk_out_fwd", "chunk_state_fwd (recompute)",
+ * "chunk_state_bwd", "chunk_bwd_col", "chunk_bwd_row", "bwd_dt", "bwd_reduce",
+ * "conv1d_silu_fwd", "conv1d_silu_bwd", "rmsnorm_gated_fwd",
+ * "rmsnorm_gated_bwd".  Not for use while other threads call the library. */
+int ssd_profile_enable(int on);
+int ssd_profile_kernel_ms(const char* kernel, double* total_ms, int64_t* launches);
+
 #ifdef __cplusplus
 }
 #endif

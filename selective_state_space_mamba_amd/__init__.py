@@ -14,6 +14,8 @@ from ._binding import (  # noqa: F401
     conv1d_silu_fwd,
     library_path,
     load_library,
+    profile_enable,
+    profile_kernel_ms,
     rmsnorm_gated_bwd,
     rmsnorm_gated_fwd,
     ssd_bwd,

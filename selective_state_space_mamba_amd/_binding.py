@@ -65,12 +65,29 @@ def load_library():
     lib.ssd_last_error.restype = ctypes.c_char_p
     lib.ssd_version.argtypes = []
     lib.ssd_version.restype = ctypes.c_char_p
+    lib.ssd_profile_enable.argtypes = [ctypes.c_int]
+    lib.ssd_profile_enable.restype = ctypes.c_int
+    lib.ssd_profile_kernel_ms.argtypes = [ctypes.c_char_p, ctypes.POINTER(ctypes.c_double),
+                                          ctypes.POINTER(ctypes.c_int64)]
+    lib.ssd_profile_kernel_ms.restype = ctypes.c_int
     _lib = lib
     return lib
 
 
 def version() -> str:
     return load_library().ssd_version().decode()
+
+
+def profile_enable(on: bool = True) -> None:
+    """Clear earlier per-kernel timing records and turn recording on or off."""
+    _check(load_library().ssd_profile_enable(int(on)))
+
+
+def profile_kernel_ms(kernel: str) -> Tuple[float, int]:
+    """(summed milliseconds, launches) of one kernel since profile_enable."""
+    ms, n = ctypes.c_double(0.0), ctypes.c_int64(0)
+    _check(load_library().ssd_profile_kernel_ms(kernel.encode(), ctypes.byref(ms), ctypes.byref(n)))
+    return ms.value, n.value
 
 
 def _check(rc: int):

@@ -5,7 +5,10 @@
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <cstring>
+#include <mutex>
 #include <string>
+#include <vector>
 
 #include "../../include/ssd.h"
 #include "ssd_common.hpp"
@@ -149,10 +152,49 @@ int hip_fail(hipError_t e, const char* what) {
   return fail(SSD_ERR_HIP, "%s launch failed: %s", what, hipGetErrorString(e));
 }
 
-#define SSD_LAUNCH(expr, what)                 \
-  do {                                         \
-    hipError_t e_ = (expr);                    \
-    if (e_ != hipSuccess) return hip_fail(e_, what); \
+// Opt-in per-kernel timing: when enabled, every launch made by an entry point
+// is bracketed by two HIP events recorded on the caller's stream.
+struct ProfRecord {
+  const char* name;
+  hipEvent_t start, stop;
+};
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+std::vector<ProfRecord> g_prof_records;
+std::vector<hipEvent_t> g_prof_pool;
+
+hipEvent_t prof_event() {
+  if (!g_prof_pool.empty()) {
+    hipEvent_t e = g_prof_pool.back();
+    g_prof_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+hipEvent_t prof_begin(hipStream_t st) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  if (!g_prof_on) return nullptr;
+  hipEvent_t e = prof_event();
+  if (e && hipEventRecord(e, st) != hipSuccess) return nullptr;
+  return e;
+}
+
+void prof_end(hipEvent_t start, const char* name, hipStream_t st) {
+  if (!start) return;
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  hipEvent_t e = prof_event();
+  if (e && hipEventRecord(e, st) == hipSuccess) g_prof_records.push_back({name, start, e});
+}
+
+#define SSD_LAUNCH(expr, what)                                \
+  do {                                                        \
+    hipEvent_t p_ = prof_begin(st);                           \
+    hipError_t e_ = (expr);                                   \
+    if (e_ != hipSuccess) return hip_fail(e_, what);          \
+    prof_end(p_, what, st);                                   \
   } while (0)
 
 }  // namespace
@@ -162,6 +204,36 @@ extern "C" {
 const char* ssd_last_error(void) { return g_last_error.c_str(); }
 
 const char* ssd_version(void) { return "ssd-mi355x 0.1 (gfx950)"; }
+
+int ssd_profile_enable(int on) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  for (const ProfRecord& r : g_prof_records) {
+    g_prof_pool.push_back(r.start);
+    g_prof_pool.push_back(r.stop);
+  }
+  g_prof_records.clear();
+  g_prof_on = on != 0;
+  return ok();
+}
+
+int ssd_profile_kernel_ms(const char* kernel, double* total_ms, int64_t* launches) {
+  if (!kernel || !total_ms || !launches) return fail(SSD_ERR_INVALID_ARG, "ssd_profile_kernel_ms: null argument");
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  double tot = 0.0;
+  int64_t n = 0;
+  for (const ProfRecord& r : g_prof_records) {
+    if (std::strcmp(r.name, kernel) != 0) continue;
+    hipError_t e = hipEventSynchronize(r.stop);
+    float ms = 0.f;
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, r.start, r.stop);
+    if (e != hipSuccess) return hip_fail(e, "profile event");
+    tot += ms;
+    ++n;
+  }
+  *total_ms = tot;
+  *launches = n;
+  return ok();
+}
 
 size_t ssd_workspace_bytes(const ssd_problem* prob, int for_backward, int has_chunk_states) {
   ssd::Dims d;
@@ -300,6 +372,7 @@ int mamba2_conv1d_silu_fwd(int64_t batch, int64_t seqlen, int64_t d_inner, int64
                            void* x_out, void* B_out, void* C_out, void* stream) {
   int rc = check_conv(batch, seqlen, d_inner, ngroups, dstate, d_conv, dtype);
   if (rc != SSD_OK) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
   if (batch == 0 || seqlen == 0) return ok();
   if (!xbc || !w || !x_out || !B_out || !C_out)
     return fail(SSD_ERR_INVALID_ARG, "conv1d_silu_fwd: xbc, w, x_out, B_out and C_out are required");
@@ -308,8 +381,7 @@ int mamba2_conv1d_silu_fwd(int64_t batch, int64_t seqlen, int64_t d_inner, int64
     if (p && !aligned16(p)) return fail(SSD_ERR_ALIGN, "conv1d_silu_fwd: a tensor pointer is not 16-byte aligned");
   SSD_LAUNCH(ssd::launch_conv_fwd(static_cast<int>(batch), static_cast<int>(seqlen), static_cast<int>(d_inner),
                                   static_cast<int>(ngroups * dstate), static_cast<int>(d_conv),
-                                  static_cast<ssd::DType>(dtype), xbc, w, bias, x_out, B_out, C_out,
-                                  static_cast<hipStream_t>(stream)),
+                                  static_cast<ssd::DType>(dtype), xbc, w, bias, x_out, B_out, C_out, st),
              "conv1d_silu_fwd");
   return ok();
 }
@@ -363,6 +435,7 @@ int mamba2_rmsnorm_gated_fwd(int64_t rows, int64_t width, float eps, int32_t dty
                              const float* w, void* out, float* inv_rms, void* stream) {
   int rc = check_rms(rows, width, dtype);
   if (rc != SSD_OK) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
   if (rows == 0) return ok();
   if (!y || !z || !w || !out || !inv_rms)
     return fail(SSD_ERR_INVALID_ARG, "rmsnorm_gated_fwd: y, z, w, out and inv_rms are required");
@@ -371,7 +444,7 @@ int mamba2_rmsnorm_gated_fwd(int64_t rows, int64_t width, float eps, int32_t dty
   for (const void* p : ptrs)
     if (!aligned16(p)) return fail(SSD_ERR_ALIGN, "rmsnorm_gated_fwd: a tensor pointer is not 16-byte aligned");
   SSD_LAUNCH(ssd::launch_rms_fwd(rows, static_cast<int>(width), eps, static_cast<ssd::DType>(dtype), y, z, w, out,
-                                 inv_rms, static_cast<hipStream_t>(stream)),
+                                 inv_rms, st),
              "rmsnorm_gated_fwd");
   return ok();
 }

@@ -1,0 +1,111 @@
+"""GPU parity of the block-shell ops (conv1d+SiLU, RMSNorm-gated) and of the
+whole block-core slice (conv -> SSD -> RMSNorm-gated, and back) against the
+oracle on the same seeded inputs."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import selective_state_space_mamba_amd as ssd
+from ssd_inputs import CONFIGS, Stored, make_inputs
+from tests.gpu_util import TOL, dev, host, relerr
+
+pytestmark = pytest.mark.gpu
+
+
+def conv_case(seed, b, T, d_inner, G, N, K, dtype):
+    rng = np.random.default_rng(seed)
+    cd = d_inner + 2 * G * N
+    xbc = Stored(rng.standard_normal((b, T, cd)).astype(np.float32), dtype)
+    w = (0.5 * rng.standard_normal((cd, K))).astype(np.float32)
+    bias = (0.1 * rng.standard_normal(cd)).astype(np.float32)
+    gact = rng.standard_normal((b, T, cd)).astype(np.float32)
+    return xbc, w, bias, gact
+
+
+@pytest.mark.parametrize("b,T,d_inner,G,N,K,dtype", [
+    (2, 300, 64, 1, 16, 4, "f32"),   # T not a multiple of the 128-step run
+    (2, 300, 64, 2, 16, 4, "bf16"),
+    (1, 2, 32, 1, 8, 4, "f32"),      # fewer steps than taps
+    (3, 129, 48, 1, 8, 1, "f32"),
+    (3, 129, 48, 1, 8, 3, "f32"),
+    (1, 64, 40, 1, 8, 8, "f32"),
+    (8, 2048, 3072, 1, 128, 4, "bf16"),  # the block-slice shape
+])
+def test_conv1d_silu(b, T, d_inner, G, N, K, dtype):
+    xbc, w, bias, gact = conv_case(11, b, T, d_inner, G, N, K, dtype)
+    xo, Bo, Co = ssd.conv1d_silu_fwd(dev(xbc), dev(w), dev(bias), d_inner, G, N)
+    gx = gact[..., :d_inner]
+    gB = gact[..., d_inner:d_inner + G * N].reshape(b, T, G, N)
+    gC = gact[..., d_inner + G * N:].reshape(b, T, G, N)
+    dxbc, dw, db = ssd.conv1d_silu_bwd(dev(xbc), dev(w), dev(bias), dev(gx), dev(gB), dev(gC), d_inner, G, N)
+    torch.cuda.synchronize()
+    _, act = oracle.conv_fwd(xbc.values, w, bias)
+    rdx, rdw, rdb = oracle.conv_bwd(xbc.values, w, bias, gact)
+    got_act = np.concatenate([host(xo), host(Bo).reshape(b, T, -1), host(Co).reshape(b, T, -1)], axis=-1)
+    tol = TOL[dtype]
+    errs = {"act": relerr(got_act, act), "dxbc": relerr(host(dxbc), rdx), "dw": relerr(host(dw), rdw),
+            "dbias": relerr(host(db), rdb)}
+    print("[parity conv]", errs, flush=True)
+    assert all(v <= tol for v in errs.values()), errs
+
+
+@pytest.mark.parametrize("rows,width,dtype,gdtype", [
+    ((3, 5), 64, "f32", "f32"),
+    ((2, 37), 200, "bf16", "f32"),
+    ((1, 1), 4096, "f32", "bf16"),
+    ((8, 2048), 3072, "bf16", "bf16"),  # the block-slice shape
+])
+def test_rmsnorm_gated(rows, width, dtype, gdtype):
+    rng = np.random.default_rng(12)
+    y = Stored(rng.standard_normal(rows + (width,)).astype(np.float32), dtype)
+    z = Stored(rng.standard_normal(rows + (width,)).astype(np.float32), dtype)
+    w = (1.0 + 0.1 * rng.standard_normal(width)).astype(np.float32)
+    g = Stored(rng.standard_normal(rows + (width,)).astype(np.float32), gdtype)
+    out, inv = ssd.rmsnorm_gated_fwd(dev(y), dev(z), dev(w), 1e-5)
+    dy, dz, dw = ssd.rmsnorm_gated_bwd(dev(y), dev(z), dev(w), inv, dev(g))
+    torch.cuda.synchronize()
+    rout, rinv = oracle.rmsnorm_fwd(y.values, z.values, w, 1e-5)
+    rdy, rdz, rdw = oracle.rmsnorm_bwd(y.values, z.values, w, rinv, g.values)
+    tol = TOL["bf16" if "bf16" in (dtype, gdtype) else "f32"]
+    errs = {"out": relerr(host(out), rout), "inv_rms": relerr(host(inv), rinv), "dy": relerr(host(dy), rdy),
+            "dz": relerr(host(dz), rdz), "dw": relerr(host(dw), rdw)}
+    print("[parity rmsnorm]", errs, flush=True)
+    assert all(v <= tol for v in errs.values()), errs
+
+
+def test_block_slice_end_to_end():
+    """conv1d+SiLU -> SSD -> RMSNorm-gated forward and the backward through all
+    three at the block-slice size, against the oracle chain run in f64 from the
+    same generated inputs (the HIP chain stores its intermediates in bf16)."""
+    cfg = CONFIGS["block"]
+    d = make_inputs(cfg)
+    b, T, H, P, N, G, Q, di = cfg.batch, cfg.seqlen, cfg.nheads, cfg.headdim, cfg.dstate, cfg.ngroups, cfg.chunk, cfg.d_inner
+    xbc, z, gout = dev(d["xBC"]), dev(d["z"]), dev(d["gout"])
+    cw, cb, nw = dev(d["conv_w"]), dev(d["conv_b"]), dev(d["norm_w"])
+    dt, A_log, D = dev(d["dt"]), dev(d["A_log"]), dev(d["D"])
+    xs, Bs, Cs = ssd.conv1d_silu_fwd(xbc, cw, cb, di, G, N)
+    y, _, cs = ssd.ssd_fwd(xs.view(b, T, H, P), dt, A_log, Bs, Cs, D, chunk=Q)
+    out, inv = ssd.rmsnorm_gated_fwd(y.view(b, T, di), z, nw, cfg.norm_eps)
+    gy, gz, gw = ssd.rmsnorm_gated_bwd(y.view(b, T, di), z, nw, inv, gout)
+    g = ssd.ssd_bwd(xs.view(b, T, H, P), dt, A_log, Bs, Cs, D, gy.view(b, T, H, P), chunk_states=cs, chunk=Q)
+    dxbc, dcw, dcb = ssd.conv1d_silu_bwd(xbc, cw, cb, g["dx"].view(b, T, di), g["dB"], g["dC"], di, G, N)
+    torch.cuda.synchronize()
+
+    _, act = oracle.conv_fwd(d["xBC"].values, d["conv_w"], d["conv_b"])
+    rx = act[..., :di].reshape(b, T, H, P)
+    rB = act[..., di:di + G * N].reshape(b, T, G, N)
+    rC = act[..., di + G * N:].reshape(b, T, G, N)
+    sargs = (rx, d["dt"].values, d["A_log"], rB, rC, d["D"])
+    ry = oracle.ssd_fwd(*sargs)["y"].reshape(b, T, di)
+    rout, rinv = oracle.rmsnorm_fwd(ry, d["z"].values, d["norm_w"], cfg.norm_eps)
+    rgy, rgz, rgw = oracle.rmsnorm_bwd(ry, d["z"].values, d["norm_w"], rinv, d["gout"].values)
+    rg = oracle.ssd_bwd(*sargs, rgy.reshape(b, T, H, P))
+    gact = np.concatenate([rg["dx"].reshape(b, T, di), rg["dB"].reshape(b, T, -1), rg["dC"].reshape(b, T, -1)], -1)
+    rdxbc, rdcw, rdcb = oracle.conv_bwd(d["xBC"].values, d["conv_w"], d["conv_b"], gact)
+    errs = {"out": relerr(host(out), rout), "dz": relerr(host(gz), rgz), "dnorm_w": relerr(host(gw), rgw),
+            "ddt": relerr(host(g["ddt"]), rg["ddt"]), "dA_log": relerr(host(g["dA_log"]), rg["dA_log"]),
+            "dD": relerr(host(g["dD"]), rg["dD"]), "dxbc": relerr(host(dxbc), rdxbc),
+            "dconv_w": relerr(host(dcw), rdcw), "dconv_b": relerr(host(dcb), rdcb)}
+    print("[parity block chain]", {k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
+    assert all(v <= TOL["bf16"] for v in errs.values()), errs
