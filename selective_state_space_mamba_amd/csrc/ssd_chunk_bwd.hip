@@ -44,6 +44,12 @@ __device__ __forceinline__ float block_sum(float v, float* tmp) {
   return tmp[0] + tmp[1] + tmp[2] + tmp[3];
 }
 
+// Chunk rows (or columns) staged per slab: the whole chunk for bf16 operands,
+// 64 at a time for f32.
+template <bool BF> struct BwdSlab { static constexpr int W = BF ? QMAX : BQ; };
+
+constexpr int cmax(int a, int b) { return a > b ? a : b; }
+
 // ------------------------------------------------------------ column kernel
 
 template <typename TI, typename TY, bool BF>
@@ -55,20 +61,27 @@ __global__ __launch_bounds__(NTHREADS) void chunk_bwd_col_kernel(
     float* __restrict__ Rp, int T, int H, int P, int N, int G, int Q, int nsplit) {
   typedef typename Op<BF>::T OT;
   constexpr int PAD = BF ? 8 : 4;
-  constexpr int LDN = NMAX + PAD;
-  constexpr int LDP = PMAX + PAD;
-  constexpr int LDQ = BQ + PAD;
-  constexpr int U_SZ = BF ? (PMAX * LDN + NMAX * LDP) : (BQ * LDN);
-  __shared__ __attribute__((aligned(16))) OT sB[BQ * LDN];    // B_jb [j][n]
-  __shared__ __attribute__((aligned(16))) OT sX[BQ * LDP];    // x_jb [j][p]
-  __shared__ __attribute__((aligned(16))) OT sDy[BQ * LDP];   // dy_ib [i][p]
-  __shared__ __attribute__((aligned(16))) OT sDyT[BF ? PMAX * LDQ : 8];  // dy_ib [p][i]
-  __shared__ __attribute__((aligned(16))) OT sGt[BQ * LDQ];   // [j][i]
-  __shared__ __attribute__((aligned(16))) OT sU[U_SZ];        // C_ib | Gamma (+Gamma^T) | C_ib^T
+  constexpr int IW = BwdSlab<BF>::W;
+  constexpr int LDN = NMAX + PAD, LDP = PMAX + PAD, LDI = IW + PAD;
+  constexpr int R_PH1 = IW * LDN;                                       // C rows [i][n]
+  constexpr int R_DIAG = IW * LDP + (BF ? PMAX * LDI : 0) + BQ * LDI;   // dy [i][p], dy^T [p][i], G1^T [j][i]
+  constexpr int R_STATE = PMAX * LDN + (BF ? NMAX * LDP : 0);           // Gamma [p][n], Gamma^T [n][p]
+  constexpr int R_FIN = BQ * LDI + (BF ? NMAX * LDI : IW * LDN);        // W^T [j][i], C^T [n][i] or C [i][n]
+  constexpr int RSZ = cmax(cmax(R_PH1, R_DIAG), cmax(R_STATE, R_FIN));
+  __shared__ __attribute__((aligned(16))) OT sB[BQ * LDN];  // B_jb [j][n]
+  __shared__ __attribute__((aligned(16))) OT sX[BQ * LDP];  // x_jb [j][p]
+  __shared__ __attribute__((aligned(16))) OT sR[RSZ];
   __shared__ float sS[QMAX];
   __shared__ float sDt[QMAX];
   __shared__ float sTmp[8];
   __shared__ float sRed[4][BQ][2];
+  OT* const sDy = sR;
+  OT* const sDyT = sR + IW * LDP;
+  OT* const sGt = sR + IW * LDP + (BF ? PMAX * LDI : 0);
+  OT* const sGam = sR;
+  OT* const sGamT = sR + PMAX * LDN;
+  OT* const sWt = sR;
+  OT* const sCf = sR + BQ * LDI;
 
   const int nc = T / Q, nb = (Q + BQ - 1) / BQ;
   const int hpg = H / G, hps = hpg / nsplit;
@@ -83,24 +96,34 @@ __global__ __launch_bounds__(NTHREADS) void chunk_bwd_col_kernel(
   const int bi = idx / nc;
 
   const int tid = threadIdx.x, w = wave_id(), l = lane_id(), r = l & 15, q = l >> 4;
-  const int64_t t0 = static_cast<int64_t>(c) * Q;
+  const int64_t row0 = static_cast<int64_t>(bi) * T + static_cast<int64_t>(c) * Q;
   const int j0 = jb * BQ, vj = min(BQ, Q - j0);
+  const int i_lo = j0;                          // rows i >= j0 feed this column block
+  const int nsl = (Q - i_lo + IW - 1) / IW;     // slabs of i-rows
   const int Kn = round_up(N, Op<BF>::KS), Kp = round_up(P, Op<BF>::KS);
   const int64_t GN = static_cast<int64_t>(G) * N, HP = static_cast<int64_t>(H) * P;
   const int64_t PN = static_cast<int64_t>(P) * N;
 
-  stage_tile<TI, OT, false>(sB, LDN, Bm + ((static_cast<int64_t>(bi) * T + t0 + j0) * G + g) * N, GN, BQ, NMAX,
-                            vj, N);
+  {
+    RowTile<TI, BQ, NMAX> tb;
+    tb.load(Bm + (row0 + j0) * GN + static_cast<int64_t>(g) * N, GN, vj, N);
+    tb.store(sB, LDN);
+  }
   f4 cb[NBMAX][4];
 #pragma unroll
-  for (int ib = 0; ib < NBMAX; ++ib) {
-    zero(cb[ib]);
-    if (ib >= jb && ib < nb) {
-      __syncthreads();
-      stage_tile<TI, OT, false>(sU, LDN, Cm + ((static_cast<int64_t>(bi) * T + t0 + ib * BQ) * G + g) * N, GN, BQ,
-                                NMAX, min(BQ, Q - ib * BQ), N);
-      __syncthreads();
-      wave_gemm<BF, true, true, 4>(cb[ib], sU + 16 * w * LDN, LDN, 1, sB, LDN, 1, Kn);
+  for (int ib = 0; ib < NBMAX; ++ib) zero(cb[ib]);
+  for (int sl = 0; sl < nsl; ++sl) {
+    const int s0 = i_lo + sl * IW;
+    RowTile<TI, IW, NMAX> tc;
+    tc.load(Cm + (row0 + s0) * GN + static_cast<int64_t>(g) * N, GN, min(IW, Q - s0), N);
+    __syncthreads();
+    tc.store(sR, LDN);
+    __syncthreads();
+#pragma unroll
+    for (int ib = 0; ib < NBMAX; ++ib) {
+      const int il = ib * BQ - s0;
+      if (ib >= jb && ib < nb && il >= 0 && il < IW)
+        wave_gemm<BF, true, true, 4>(cb[ib], sR + (il + 16 * w) * LDN, LDN, 1, sB, LDN, 1, Kn);
     }
   }
   f4 ws[NBMAX][4];
@@ -109,58 +132,75 @@ __global__ __launch_bounds__(NTHREADS) void chunk_bwd_col_kernel(
   f4 dbs[8];
   zero(dbs);
 
+  RowTile<TI, BQ, PMAX> tX;          // x_jb
+  TransTile<TY, IW, PMAX> tDy;        // dy rows of one slab
+  TransTile<float, PMAX, NMAX> tG;    // Gamma_{c+1}
+  float dt_next = 0.f;
+  auto load_head = [&](int hh) {
+    const int h = g * hpg + sp * hps + hh;
+    tX.load(x + (row0 + j0) * HP + static_cast<int64_t>(h) * P, HP, vj, P);
+    tDy.load(dy + (row0 + i_lo) * HP + static_cast<int64_t>(h) * P, HP, min(IW, Q - i_lo), P);
+    dt_next = (tid < Q) ? load_f(dt, (row0 + tid) * H + h) : 0.f;
+  };
+  load_head(0);
+
   for (int hh = 0; hh < hps; ++hh) {
     const int h = g * hpg + sp * hps + hh;
     const float A = -__expf(A_log[h]);
     const float Dh = D[h];
-    __syncthreads();
-    const float dtv = (tid < Q) ? load_f(dt, (static_cast<int64_t>(bi) * T + t0 + tid) * H + h) : 0.f;
+    const float dtv = dt_next;
+    __syncthreads();  // previous head done with every tile
     const float s = block_inclusive_scan(dtv * A, sTmp);
     if (tid < Q) {
       sS[tid] = s;
       sDt[tid] = dtv;
     }
-    stage_tile<TI, OT, false>(sX, LDP, x + ((static_cast<int64_t>(bi) * T + t0 + j0) * H + h) * P, HP, BQ, PMAX,
-                              vj, P);
+    tX.store(sX, LDP);
 
     f4 dxa[4];
     zero(dxa);
     float csum[4] = {0.f, 0.f, 0.f, 0.f}, dsum[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int sl = 0; sl < nsl; ++sl) {
+      const int s0 = i_lo + sl * IW;
+      if (sl > 0) __syncthreads();
+      tDy.store_rows(sDy, LDP);
+      if constexpr (BF) tDy.store(sDyT, LDI);
+      if (sl + 1 < nsl)
+        tDy.load(dy + (row0 + s0 + IW) * HP + static_cast<int64_t>(h) * P, HP, min(IW, Q - s0 - IW), P);
+      else
+        tG.load(gamma + ((static_cast<int64_t>(bi) * nc + c) * H + h) * PN, N, P, N);
+      __syncthreads();
 #pragma unroll
-    for (int ib = 0; ib < NBMAX; ++ib) {
-      if (ib >= jb && ib < nb) {
-        const int i0 = ib * BQ, vi = min(BQ, Q - i0);
-        __syncthreads();
-        const TY* dysrc = dy + ((static_cast<int64_t>(bi) * T + t0 + i0) * H + h) * P;
-        stage_tile<TY, OT, false>(sDy, LDP, dysrc, HP, BQ, PMAX, vi, P);
-        if constexpr (BF) stage_tile<TY, OT, true>(sDyT, LDQ, dysrc, HP, BQ, PMAX, vi, P);
-        __syncthreads();
-        f4 yx[4];
-        zero(yx);
-        wave_gemm<BF, true, true, 4>(yx, sDy + 16 * w * LDP, LDP, 1, sX, LDP, 1, Kp);
+      for (int ib = 0; ib < NBMAX; ++ib) {
+        const int il = ib * BQ - s0;
+        if (ib >= jb && ib < nb && il >= 0 && il < IW) {
+          f4 yx[4];
+          zero(yx);
+          wave_gemm<BF, true, true, 4>(yx, sDy + (il + 16 * w) * LDP, LDP, 1, sX, LDP, 1, Kp);
 #pragma unroll
-        for (int ct = 0; ct < 4; ++ct)
+          for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int il = 16 * w + 4 * q + i, jl = 16 * ct + r;
-            const int iq = i0 + il, jq = j0 + jl;
-            const bool valid = iq < Q && jq <= iq;
-            const float Lv = valid ? __expf(sS[iq] - sS[jq]) : 0.f;
-            const float g1 = Lv * cb[ib][ct][i];
-            const float e = g1 * yx[ct][i];
-            csum[ct] += e;
-            if (iq == jq) dsum[ct] += e;
-            ws[ib][ct][i] += valid ? Lv * yx[ct][i] * sDt[jq] : 0.f;
-            sGt[jl * LDQ + il] = Op<BF>::cvt(g1);
-          }
-        __syncthreads();
-        if constexpr (BF)
-          wave_gemm<BF, true, true, 4>(dxa, sGt + 16 * w * LDQ, LDQ, 1, sDyT, LDQ, 1, BQ);
-        else
-          wave_gemm<BF, true, false, 4>(dxa, sGt + 16 * w * LDQ, LDQ, 1, sDy, 1, LDP, BQ);
+            for (int i = 0; i < 4; ++i) {
+              const int ir = il + 16 * w + 4 * q + i;  // row inside the slab
+              const int iq = s0 + ir, jl = 16 * ct + r, jq = j0 + jl;
+              const bool valid = iq < Q && jq <= iq;
+              const float Lv = valid ? __expf(sS[iq] - sS[jq]) : 0.f;
+              const float g1 = Lv * cb[ib][ct][i];
+              const float e = g1 * yx[ct][i];
+              csum[ct] += e;
+              if (iq == jq) dsum[ct] += e;
+              ws[ib][ct][i] += valid ? Lv * yx[ct][i] * sDt[jq] : 0.f;
+              sGt[jl * LDI + ir] = Op<BF>::cvt(g1);
+            }
+        }
       }
+      __syncthreads();
+      const int kw = round_up(min(IW, Q - s0), Op<BF>::KS);
+      if constexpr (BF)
+        wave_gemm<BF, true, true, 4>(dxa, sGt + 16 * w * LDI, LDI, 1, sDyT, LDI, 1, kw);
+      else
+        wave_gemm<BF, true, false, 4>(dxa, sGt + 16 * w * LDI, LDI, 1, sDy, 1, LDP, kw);
     }
-    // column statistics: reduce over the q groups, then over waves through LDS
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) {
       const float cs = sum_q(csum[ct]), ds = sum_q(dsum[ct]);
@@ -172,24 +212,24 @@ __global__ __launch_bounds__(NTHREADS) void chunk_bwd_col_kernel(
 
     // state terms with Gamma_{c+1}
     __syncthreads();
-    const float* gsrc = gamma + ((static_cast<int64_t>(bi) * nc + c) * H + h) * PN;
-    stage_tile<float, OT, false>(sU, LDN, gsrc, N, PMAX, NMAX, P, N);
-    if constexpr (BF) stage_tile<float, OT, true>(sU + PMAX * LDN, LDP, gsrc, N, PMAX, NMAX, P, N);
+    tG.store_rows(sGam, LDN);
+    if constexpr (BF) tG.store(sGamT, LDP);
+    if (hh + 1 < hps) load_head(hh + 1);
     __syncthreads();
     if (tid < BQ && j0 + tid < Q) {
-      const int64_t o = (static_cast<int64_t>(bi) * H + h) * T + t0 + j0 + tid;
+      const int64_t o = (static_cast<int64_t>(bi) * H + h) * T + static_cast<int64_t>(c) * Q + j0 + tid;
       colE[o] = sRed[0][tid][0] + sRed[1][tid][0] + sRed[2][tid][0] + sRed[3][tid][0];
       diagE[o] = sRed[0][tid][1] + sRed[1][tid][1] + sRed[2][tid][1] + sRed[3][tid][1];
     }
     f4 bg[4];
     zero(bg);
-    wave_gemm<BF, true, true, 4>(bg, sB + 16 * w * LDN, LDN, 1, sU, LDN, 1, Kn);
+    wave_gemm<BF, true, true, 4>(bg, sB + 16 * w * LDN, LDN, 1, sGam, LDN, 1, Kn);
     f4 v[8];
     zero(v);
     if constexpr (BF)
-      wave_gemm<BF, true, true, 8>(v, sX + 16 * w * LDP, LDP, 1, sU + PMAX * LDN, LDP, 1, Kp);
+      wave_gemm<BF, true, true, 8>(v, sX + 16 * w * LDP, LDP, 1, sGamT, LDP, 1, Kp);
     else
-      wave_gemm<BF, true, false, 8>(v, sX + 16 * w * LDP, LDP, 1, sU, 1, LDN, Kp);
+      wave_gemm<BF, true, false, 8>(v, sX + 16 * w * LDP, LDP, 1, sGam, 1, LDN, Kp);
     const float s_end = sS[Q - 1];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -204,12 +244,12 @@ __global__ __launch_bounds__(NTHREADS) void chunk_bwd_col_kernel(
         dbs[t][i] += dtj * wj * v[t][i];
       }
       part = sum16(part);
-      if (valid && r == 0) Rp[(static_cast<int64_t>(bi) * H + h) * T + t0 + jq] = wj * part;
+      if (valid && r == 0) Rp[(static_cast<int64_t>(bi) * H + h) * T + static_cast<int64_t>(c) * Q + jq] = wj * part;
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const int p = 16 * t + r;
         if (valid && p < P) {
-          const int64_t o = ((static_cast<int64_t>(bi) * T + t0 + jq) * H + h) * P + p;
+          const int64_t o = (row0 + jq) * HP + static_cast<int64_t>(h) * P + p;
           dx[o] = dtj * (dxa[t][i] + wj * bg[t][i]) + Dh * load_f(dy, o);
         }
       }
@@ -217,25 +257,37 @@ __global__ __launch_bounds__(NTHREADS) void chunk_bwd_col_kernel(
   }
 
   // dB_j += sum_i W^T[j][i] C_i with W = sum over heads of L yx dt
+  for (int sl = 0; sl < nsl; ++sl) {
+    const int s0 = i_lo + sl * IW;
+    __syncthreads();
 #pragma unroll
-  for (int ib = 0; ib < NBMAX; ++ib) {
-    if (ib >= jb && ib < nb) {
-      __syncthreads();
+    for (int ib = 0; ib < NBMAX; ++ib) {
+      const int il = ib * BQ - s0;
+      if (ib >= jb && ib < nb && il >= 0 && il < IW) {
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct)
+        for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sGt[(16 * ct + r) * LDQ + 16 * w + 4 * q + i] = Op<BF>::cvt(ws[ib][ct][i]);
-      const TI* csrc = Cm + ((static_cast<int64_t>(bi) * T + t0 + ib * BQ) * G + g) * N;
-      if constexpr (BF)
-        stage_tile<TI, OT, true>(sU, LDQ, csrc, GN, BQ, NMAX, min(BQ, Q - ib * BQ), N);
-      else
-        stage_tile<TI, OT, false>(sU, LDN, csrc, GN, BQ, NMAX, min(BQ, Q - ib * BQ), N);
-      __syncthreads();
-      if constexpr (BF)
-        wave_gemm<BF, true, true, 8>(dbs, sGt + 16 * w * LDQ, LDQ, 1, sU, LDQ, 1, BQ);
-      else
-        wave_gemm<BF, true, false, 8>(dbs, sGt + 16 * w * LDQ, LDQ, 1, sU, 1, LDN, BQ);
+          for (int i = 0; i < 4; ++i)
+            sWt[(16 * ct + r) * LDI + il + 16 * w + 4 * q + i] = Op<BF>::cvt(ws[ib][ct][i]);
+      }
     }
+    const int vi = min(IW, Q - s0);
+    const TI* csrc = Cm + (row0 + s0) * GN + static_cast<int64_t>(g) * N;
+    if constexpr (BF) {
+      TransTile<TI, IW, NMAX> tc;
+      tc.load(csrc, GN, vi, N);
+      tc.store(sCf, LDI);
+    } else {
+      RowTile<TI, IW, NMAX> tc;
+      tc.load(csrc, GN, vi, N);
+      tc.store(sCf, LDN);
+    }
+    __syncthreads();
+    const int kw = round_up(vi, Op<BF>::KS);
+    if constexpr (BF)
+      wave_gemm<BF, true, true, 8>(dbs, sWt + 16 * w * LDI, LDI, 1, sCf, LDI, 1, kw);
+    else
+      wave_gemm<BF, true, false, 8>(dbs, sWt + 16 * w * LDI, LDI, 1, sCf, 1, LDN, kw);
   }
   const int64_t batch = gridDim.x / (nb * nsplit * G * nc);
   float* dBo = dB_out + static_cast<int64_t>(sp) * batch * T * GN;
@@ -244,7 +296,7 @@ __global__ __launch_bounds__(NTHREADS) void chunk_bwd_col_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int jq = j0 + 16 * w + 4 * q + i, n = 16 * t + r;
-      if (jq < Q && n < N) dBo[((static_cast<int64_t>(bi) * T + t0 + jq) * G + g) * N + n] = dbs[t][i];
+      if (jq < Q && n < N) dBo[(row0 + jq) * GN + static_cast<int64_t>(g) * N + n] = dbs[t][i];
     }
 }
 
@@ -259,24 +311,27 @@ __global__ __launch_bounds__(NTHREADS) void chunk_bwd_row_kernel(
     int nsplit) {
   typedef typename Op<BF>::T OT;
   constexpr int PAD = BF ? 8 : 4;
-  constexpr int LDN = NMAX + PAD;
-  constexpr int LDP = PMAX + PAD;
-  constexpr int LDQ = BQ + PAD;
-  constexpr int U_A = BQ * LDN, U_B = NMAX * LDP, U_C = NMAX * LDQ;
-  constexpr int U_SZ = BF ? (U_A > U_B ? (U_A > U_C ? U_A : U_C) : (U_B > U_C ? U_B : U_C)) : U_A;
-  __shared__ __attribute__((aligned(16))) OT sC[BQ * LDN];    // C_ib [i][n]
-  __shared__ __attribute__((aligned(16))) OT sDy[BQ * LDP];   // dy_ib [i][p]
-  __shared__ __attribute__((aligned(16))) OT sX[BQ * LDP];    // x_jb [j][p]
-  __shared__ __attribute__((aligned(16))) OT sW[BQ * LDQ];    // [i][j]
-  __shared__ __attribute__((aligned(16))) OT sU[U_SZ];        // B_jb | H_c | B_jb^T
+  constexpr int JW = BwdSlab<BF>::W;
+  constexpr int LDN = NMAX + PAD, LDP = PMAX + PAD, LDJ = JW + PAD;
+  constexpr int R_PH1 = JW * LDN;                                        // B rows [j][n]
+  constexpr int R_HEAD = (BF ? NMAX * LDP : PMAX * LDN) + JW * LDP;      // H^T [n][p] or H [p][n]; x rows [j][p]
+  constexpr int R_FIN = BQ * LDJ + (BF ? NMAX * LDJ : JW * LDN);         // W [i][j]; B^T [n][j] or B [j][n]
+  constexpr int RSZ = cmax(R_PH1, cmax(R_HEAD, R_FIN));
+  __shared__ __attribute__((aligned(16))) OT sC[BQ * LDN];   // C_ib [i][n]
+  __shared__ __attribute__((aligned(16))) OT sDy[BQ * LDP];  // dy_ib [i][p]
+  __shared__ __attribute__((aligned(16))) OT sR[RSZ];
   __shared__ float sS[QMAX];
   __shared__ float sDt[QMAX];
   __shared__ float sTmp[8];
+  OT* const sH = sR;
+  OT* const sXr = sR + (BF ? NMAX * LDP : PMAX * LDN);
+  OT* const sW = sR;
+  OT* const sBf = sR + BQ * LDJ;
 
   const int nc = T / Q, nb = (Q + BQ - 1) / BQ;
   const int hpg = H / G, hps = hpg / nsplit;
   int idx = blockIdx.x;
-  const int ib = idx % nb;
+  const int ib = nb - 1 - idx % nb;  // heavier row blocks first
   idx /= nb;
   const int sp = idx % nsplit;
   idx /= nsplit;
@@ -286,24 +341,34 @@ __global__ __launch_bounds__(NTHREADS) void chunk_bwd_row_kernel(
   const int bi = idx / nc;
 
   const int tid = threadIdx.x, w = wave_id(), l = lane_id(), r = l & 15, q = l >> 4;
-  const int64_t t0 = static_cast<int64_t>(c) * Q;
+  const int64_t row0 = static_cast<int64_t>(bi) * T + static_cast<int64_t>(c) * Q;
   const int i0 = ib * BQ, vi = min(BQ, Q - i0);
+  const int jend = min(Q, i0 + BQ);
+  const int nsl = (jend + JW - 1) / JW;
   const int Kn = round_up(N, Op<BF>::KS), Kp = round_up(P, Op<BF>::KS);
   const int64_t GN = static_cast<int64_t>(G) * N, HP = static_cast<int64_t>(H) * P;
   const int64_t PN = static_cast<int64_t>(P) * N;
 
-  stage_tile<TI, OT, false>(sC, LDN, Cm + ((static_cast<int64_t>(bi) * T + t0 + i0) * G + g) * N, GN, BQ, NMAX,
-                            vi, N);
+  {
+    RowTile<TI, BQ, NMAX> tc;
+    tc.load(Cm + (row0 + i0) * GN + static_cast<int64_t>(g) * N, GN, vi, N);
+    tc.store(sC, LDN);
+  }
   f4 cb[NBMAX][4];
 #pragma unroll
-  for (int jb = 0; jb < NBMAX; ++jb) {
-    zero(cb[jb]);
-    if (jb <= ib) {
-      __syncthreads();
-      stage_tile<TI, OT, false>(sU, LDN, Bm + ((static_cast<int64_t>(bi) * T + t0 + jb * BQ) * G + g) * N, GN, BQ,
-                                NMAX, min(BQ, Q - jb * BQ), N);
-      __syncthreads();
-      wave_gemm<BF, true, true, 4>(cb[jb], sC + 16 * w * LDN, LDN, 1, sU, LDN, 1, Kn);
+  for (int jb = 0; jb < NBMAX; ++jb) zero(cb[jb]);
+  for (int sl = 0; sl < nsl; ++sl) {
+    const int s0 = sl * JW;
+    RowTile<TI, JW, NMAX> tb;
+    tb.load(Bm + (row0 + s0) * GN + static_cast<int64_t>(g) * N, GN, min(JW, jend - s0), N);
+    __syncthreads();
+    tb.store(sR, LDN);
+    __syncthreads();
+#pragma unroll
+    for (int jb = 0; jb < NBMAX; ++jb) {
+      const int jl = jb * BQ - s0;
+      if (jb <= ib && jl >= 0 && jl < JW)
+        wave_gemm<BF, true, true, 4>(cb[jb], sC + 16 * w * LDN, LDN, 1, sR + jl * LDN, LDN, 1, Kn);
     }
   }
   f4 ws[NBMAX][4];
@@ -312,32 +377,43 @@ __global__ __launch_bounds__(NTHREADS) void chunk_bwd_row_kernel(
   f4 dca[8];
   zero(dca);
 
+  RowTile<TY, BQ, PMAX> tDy;        // dy_ib
+  TransTile<float, PMAX, NMAX> tH;  // H_c rows p, columns n
+  RowTile<TI, JW, PMAX> tXs;        // x rows of one slab
+  float dt_next = 0.f;
+  auto load_head = [&](int hh) {
+    const int h = g * hpg + sp * hps + hh;
+    tDy.load(dy + (row0 + i0) * HP + static_cast<int64_t>(h) * P, HP, vi, P);
+    tH.load(hstates + ((static_cast<int64_t>(bi) * nc + c) * H + h) * PN, N, P, N);
+    tXs.load(x + row0 * HP + static_cast<int64_t>(h) * P, HP, min(JW, jend), P);
+    dt_next = (tid < Q) ? load_f(dt, (row0 + tid) * H + h) : 0.f;
+  };
+  load_head(0);
+
   for (int hh = 0; hh < hps; ++hh) {
     const int h = g * hpg + sp * hps + hh;
     const float A = -__expf(A_log[h]);
+    const float dtv = dt_next;
     __syncthreads();
-    const float dtv = (tid < Q) ? load_f(dt, (static_cast<int64_t>(bi) * T + t0 + tid) * H + h) : 0.f;
     const float s = block_inclusive_scan(dtv * A, sTmp);
     if (tid < Q) {
       sS[tid] = s;
       sDt[tid] = dtv;
     }
-    const TY* dysrc = dy + ((static_cast<int64_t>(bi) * T + t0 + i0) * H + h) * P;
-    stage_tile<TY, OT, false>(sDy, LDP, dysrc, HP, BQ, PMAX, vi, P);
-    const float* hsrc = hstates + ((static_cast<int64_t>(bi) * nc + c) * H + h) * PN;
+    tDy.store(sDy, LDP);
     if constexpr (BF)
-      stage_tile<float, OT, true>(sU, LDP, hsrc, N, PMAX, NMAX, P, N);
+      tH.store(sH, LDP);
     else
-      stage_tile<float, OT, false>(sU, LDN, hsrc, N, PMAX, NMAX, P, N);
+      tH.store_rows(sH, LDN);
     __syncthreads();
 
     // U_i = dy_i H_c (rows i, d_state columns)
     f4 u[8];
     zero(u);
     if constexpr (BF)
-      wave_gemm<BF, true, true, 8>(u, sDy + 16 * w * LDP, LDP, 1, sU, LDP, 1, Kp);
+      wave_gemm<BF, true, true, 8>(u, sDy + 16 * w * LDP, LDP, 1, sH, LDP, 1, Kp);
     else
-      wave_gemm<BF, true, false, 8>(u, sDy + 16 * w * LDP, LDP, 1, sU, 1, LDN, Kp);
+      wave_gemm<BF, true, false, 8>(u, sDy + 16 * w * LDP, LDP, 1, sH, 1, LDN, Kp);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int il = 16 * w + 4 * q + i, iq = i0 + il;
@@ -349,43 +425,50 @@ __global__ __launch_bounds__(NTHREADS) void chunk_bwd_row_kernel(
         dca[t][i] += e * u[t][i];
       }
       part = sum16(part);
-      if (iq < Q && r == 0) dsoff[(static_cast<int64_t>(bi) * H + h) * T + t0 + iq] = e * part;
+      if (iq < Q && r == 0) dsoff[(static_cast<int64_t>(bi) * H + h) * T + static_cast<int64_t>(c) * Q + iq] = e * part;
     }
 
     float racc[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int sl = 0; sl < nsl; ++sl) {
+      const int s0 = sl * JW;
+      __syncthreads();  // previous slab's reads of sXr done (and U's reads of sH)
+      tXs.store(sXr, LDP);
+      if (sl + 1 < nsl)
+        tXs.load(x + (row0 + s0 + JW) * HP + static_cast<int64_t>(h) * P, HP, min(JW, jend - s0 - JW), P);
+      else if (hh + 1 < hps)
+        load_head(hh + 1);
+      __syncthreads();
 #pragma unroll
-    for (int jb = 0; jb < NBMAX; ++jb) {
-      if (jb <= ib) {
-        __syncthreads();
-        stage_tile<TI, OT, false>(sX, LDP, x + ((static_cast<int64_t>(bi) * T + t0 + jb * BQ) * H + h) * P, HP, BQ,
-                                  PMAX, min(BQ, Q - jb * BQ), P);
-        __syncthreads();
-        f4 yx[4];
-        zero(yx);
-        wave_gemm<BF, true, true, 4>(yx, sDy + 16 * w * LDP, LDP, 1, sX, LDP, 1, Kp);
+      for (int jb = 0; jb < NBMAX; ++jb) {
+        const int jl = jb * BQ - s0;
+        if (jb <= ib && jl >= 0 && jl < JW) {
+          f4 yx[4];
+          zero(yx);
+          wave_gemm<BF, true, true, 4>(yx, sDy + 16 * w * LDP, LDP, 1, sXr + jl * LDP, LDP, 1, Kp);
 #pragma unroll
-        for (int ct = 0; ct < 4; ++ct)
+          for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int iq = i0 + 16 * w + 4 * q + i, jq = jb * BQ + 16 * ct + r;
-            const bool valid = iq < Q && jq <= iq;
-            const float ly = valid ? __expf(sS[iq] - sS[jq]) * yx[ct][i] * sDt[jq] : 0.f;
-            ws[jb][ct][i] += ly;
-            if (jq < iq) racc[i] += ly * cb[jb][ct][i];
-          }
+            for (int i = 0; i < 4; ++i) {
+              const int iq = i0 + 16 * w + 4 * q + i, jq = jb * BQ + 16 * ct + r;
+              const bool valid = iq < Q && jq <= iq;
+              const float ly = valid ? __expf(sS[iq] - sS[jq]) * yx[ct][i] * sDt[jq] : 0.f;
+              ws[jb][ct][i] += ly;
+              if (jq < iq) racc[i] += ly * cb[jb][ct][i];
+            }
+        }
       }
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const float rr = sum16(racc[i]);
       const int iq = i0 + 16 * w + 4 * q + i;
-      if (iq < Q && r == 0) rowM[(static_cast<int64_t>(bi) * H + h) * T + t0 + iq] = rr;
+      if (iq < Q && r == 0) rowM[(static_cast<int64_t>(bi) * H + h) * T + static_cast<int64_t>(c) * Q + iq] = rr;
     }
     // dD partial over this block's rows
     float dd = 0.f;
     for (int e = tid; e < vi * P; e += NTHREADS) {
       const int il = e / P, p = e % P;
-      const int64_t o = ((static_cast<int64_t>(bi) * T + t0 + i0 + il) * H + h) * P + p;
+      const int64_t o = (row0 + i0 + il) * HP + static_cast<int64_t>(h) * P + p;
       dd += load_f(dy, o) * load_f(x, o);
     }
     dd = wave_sum(dd);
@@ -395,25 +478,37 @@ __global__ __launch_bounds__(NTHREADS) void chunk_bwd_row_kernel(
   }
 
   // dC_i += sum_j W[i][j] B_j with W = sum over heads of L yx dt
+  for (int sl = 0; sl < nsl; ++sl) {
+    const int s0 = sl * JW;
+    __syncthreads();
 #pragma unroll
-  for (int jb = 0; jb < NBMAX; ++jb) {
-    if (jb <= ib) {
-      __syncthreads();
+    for (int jb = 0; jb < NBMAX; ++jb) {
+      const int jl = jb * BQ - s0;
+      if (jb <= ib && jl >= 0 && jl < JW) {
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct)
+        for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sW[(16 * w + 4 * q + i) * LDQ + 16 * ct + r] = Op<BF>::cvt(ws[jb][ct][i]);
-      const TI* bsrc = Bm + ((static_cast<int64_t>(bi) * T + t0 + jb * BQ) * G + g) * N;
-      if constexpr (BF)
-        stage_tile<TI, OT, true>(sU, LDQ, bsrc, GN, BQ, NMAX, min(BQ, Q - jb * BQ), N);
-      else
-        stage_tile<TI, OT, false>(sU, LDN, bsrc, GN, BQ, NMAX, min(BQ, Q - jb * BQ), N);
-      __syncthreads();
-      if constexpr (BF)
-        wave_gemm<BF, true, true, 8>(dca, sW + 16 * w * LDQ, LDQ, 1, sU, LDQ, 1, BQ);
-      else
-        wave_gemm<BF, true, false, 8>(dca, sW + 16 * w * LDQ, LDQ, 1, sU, 1, LDN, BQ);
+          for (int i = 0; i < 4; ++i)
+            sW[(16 * w + 4 * q + i) * LDJ + jl + 16 * ct + r] = Op<BF>::cvt(ws[jb][ct][i]);
+      }
     }
+    const int vj = min(JW, jend - s0);
+    const TI* bsrc = Bm + (row0 + s0) * GN + static_cast<int64_t>(g) * N;
+    if constexpr (BF) {
+      TransTile<TI, JW, NMAX> tb;
+      tb.load(bsrc, GN, vj, N);
+      tb.store(sBf, LDJ);
+    } else {
+      RowTile<TI, JW, NMAX> tb;
+      tb.load(bsrc, GN, vj, N);
+      tb.store(sBf, LDN);
+    }
+    __syncthreads();
+    const int kw = round_up(vj, Op<BF>::KS);
+    if constexpr (BF)
+      wave_gemm<BF, true, true, 8>(dca, sW + 16 * w * LDJ, LDJ, 1, sBf, LDJ, 1, kw);
+    else
+      wave_gemm<BF, true, false, 8>(dca, sW + 16 * w * LDJ, LDJ, 1, sBf, 1, LDN, kw);
   }
   const int64_t batch = gridDim.x / (nb * nsplit * G * nc);
   float* dCo = dC_out + static_cast<int64_t>(sp) * batch * T * GN;
@@ -422,7 +517,7 @@ __global__ __launch_bounds__(NTHREADS) void chunk_bwd_row_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int iq = i0 + 16 * w + 4 * q + i, n = 16 * t + r;
-      if (iq < Q && n < N) dCo[((static_cast<int64_t>(bi) * T + t0 + iq) * G + g) * N + n] = dca[t][i];
+      if (iq < Q && n < N) dCo[(row0 + iq) * GN + static_cast<int64_t>(g) * N + n] = dca[t][i];
     }
 }
 

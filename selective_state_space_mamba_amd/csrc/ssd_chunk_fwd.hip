@@ -13,11 +13,16 @@
 // group.  It computes the group's C.B^T tiles (ib, jb <= ib) once with MFMA
 // (K = d_state) and keeps them in registers, then per head applies the decay
 // mask L_ij = exp(s_i - s_j) (i >= j; exponents are <= 0) and dt_j, and runs
-// the two remaining contractions (K = chunk block, K = d_state) on MFMA.
+// the two remaining contractions (K = chunk columns, K = d_state) on MFMA.
+// Operands are staged with 16-byte loads; the next head's x and H_c are loaded
+// into registers while the current head computes.  bf16 operands stage the
+// whole chunk width at once (one slab); f32 operands go 64 columns at a time.
 #include "ssd_common.hpp"
 #include "ssd_launch.hpp"
 
 namespace ssd {
+
+template <bool BF> struct OutSlab { static constexpr int JW = BF ? QMAX : BQ; };
 
 template <typename TI, bool BF>
 __global__ __launch_bounds__(NTHREADS) void chunk_out_fwd_kernel(
@@ -27,20 +32,25 @@ __global__ __launch_bounds__(NTHREADS) void chunk_out_fwd_kernel(
     int nsplit) {
   typedef typename Op<BF>::T OT;
   constexpr int PAD = BF ? 8 : 4;
-  constexpr int LDN = NMAX + PAD;  // [row][n]
-  constexpr int LDQ = BQ + PAD;    // [row][j] and [p][j]
+  constexpr int JW = OutSlab<BF>::JW;  // chunk columns staged per slab
+  constexpr int LDN = NMAX + PAD;      // [row][n]
+  constexpr int LDJ = JW + PAD;        // [row][j]
+  constexpr int PH1 = JW * LDN;                     // phase 1: B rows
+  constexpr int PH2 = PMAX * LDN + PMAX * LDJ + BQ * LDJ;  // phase 2: H, x^T, G
   __shared__ __attribute__((aligned(16))) OT sC[BQ * LDN];
-  __shared__ __attribute__((aligned(16))) OT sBH[BQ * LDN];  // B block, then H_c as [p][n]
-  __shared__ __attribute__((aligned(16))) OT sXt[PMAX * LDQ];
-  __shared__ __attribute__((aligned(16))) OT sG[BQ * LDQ];
+  __shared__ __attribute__((aligned(16))) OT sU[PH1 > PH2 ? PH1 : PH2];
   __shared__ float sS[QMAX];
   __shared__ float sDt[QMAX];
   __shared__ float sTmp[8];
+  OT* const sB = sU;
+  OT* const sH = sU;
+  OT* const sXt = sU + PMAX * LDN;
+  OT* const sG = sXt + PMAX * LDJ;
 
   const int nc = T / Q, nb = (Q + BQ - 1) / BQ;
   const int hpg = H / G, hps = hpg / nsplit;
   int idx = blockIdx.x;
-  const int ib = idx % nb;
+  const int ib = nb - 1 - idx % nb;  // heavier row blocks first
   idx /= nb;
   const int sp = idx % nsplit;
   idx /= nsplit;
@@ -50,48 +60,72 @@ __global__ __launch_bounds__(NTHREADS) void chunk_out_fwd_kernel(
   const int bi = idx / nc;
 
   const int tid = threadIdx.x, w = wave_id(), l = lane_id(), r = l & 15, q = l >> 4;
-  const int64_t t0 = static_cast<int64_t>(c) * Q;
+  const int64_t row0 = static_cast<int64_t>(bi) * T + static_cast<int64_t>(c) * Q;
   const int i0 = ib * BQ;
   const int vi = min(BQ, Q - i0);
+  const int jend = min(Q, i0 + BQ);  // columns j < jend are needed
+  const int nslab = (jend + JW - 1) / JW;
   const int Kn = round_up(N, Op<BF>::KS);
   const int64_t GN = static_cast<int64_t>(G) * N, HP = static_cast<int64_t>(H) * P;
+  const int64_t PN = static_cast<int64_t>(P) * N;
 
   // ---- group-level C.B^T tiles for (ib, jb <= ib)
-  stage_tile<TI, OT, false>(sC, LDN, Cm + ((static_cast<int64_t>(bi) * T + t0 + i0) * G + g) * N, GN, BQ,
-                            NMAX, vi, N);
+  {
+    RowTile<TI, BQ, NMAX> tc;
+    tc.load(Cm + (row0 + i0) * GN + static_cast<int64_t>(g) * N, GN, vi, N);
+    tc.store(sC, LDN);
+  }
   f4 cb[NBMAX][4];
 #pragma unroll
-  for (int jb = 0; jb < NBMAX; ++jb) {
-    zero(cb[jb]);
-    if (jb <= ib) {
-      __syncthreads();
-      stage_tile<TI, OT, false>(sBH, LDN, Bm + ((static_cast<int64_t>(bi) * T + t0 + jb * BQ) * G + g) * N,
-                                GN, BQ, NMAX, min(BQ, Q - jb * BQ), N);
-      __syncthreads();
-      wave_gemm<BF, true, true, 4>(cb[jb], sC + 16 * w * LDN, LDN, 1, sBH, LDN, 1, Kn);
+  for (int jb = 0; jb < NBMAX; ++jb) zero(cb[jb]);
+  for (int sl = 0; sl < nslab; ++sl) {
+    const int j0 = sl * JW;
+    RowTile<TI, JW, NMAX> tb;
+    tb.load(Bm + (row0 + j0) * GN + static_cast<int64_t>(g) * N, GN, min(JW, jend - j0), N);
+    __syncthreads();
+    tb.store(sB, LDN);
+    __syncthreads();
+#pragma unroll
+    for (int jb = 0; jb < NBMAX; ++jb) {
+      const int jl = jb * BQ - j0;  // block start inside the slab
+      if (jb <= ib && jl >= 0 && jl < JW)
+        wave_gemm<BF, true, true, 4>(cb[jb], sC + 16 * w * LDN, LDN, 1, sB + jl * LDN, LDN, 1, Kn);
     }
   }
+
+  // ---- per head
+  RowTile<float, PMAX, NMAX> th;  // H_c as [p][n]
+  TransTile<TI, JW, PMAX> tx;     // x rows j -> [p][j]
+  float dt_next = 0.f;
+  auto prefetch = [&](int hh, int sl) {
+    const int h = g * hpg + sp * hps + hh;
+    if (sl == 0) {
+      th.load(hstates + ((static_cast<int64_t>(bi) * nc + c) * H + h) * PN, N, P, N);
+      dt_next = (tid < Q) ? load_f(dt, (row0 + tid) * H + h) : 0.f;
+    }
+    const int j0 = sl * JW;
+    tx.load(x + (row0 + j0) * HP + static_cast<int64_t>(h) * P, HP, min(JW, jend - j0), P);
+  };
+  prefetch(0, 0);
 
   for (int hh = 0; hh < hps; ++hh) {
     const int h = g * hpg + sp * hps + hh;
     const float A = -__expf(A_log[h]);
     const float Dh = D[h];
-    __syncthreads();
-    const float dtv = (tid < Q) ? load_f(dt, (static_cast<int64_t>(bi) * T + t0 + tid) * H + h) : 0.f;
+    const float dtv = dt_next;
+    __syncthreads();  // the previous head is done with sS, sDt and the tiles
     const float s = block_inclusive_scan(dtv * A, sTmp);
     if (tid < Q) {
       sS[tid] = s;
       sDt[tid] = dtv;
     }
-    stage_tile<float, OT, false>(sBH, LDN,
-                                 hstates + ((static_cast<int64_t>(bi) * nc + c) * H + h) * static_cast<int64_t>(P) * N,
-                                 N, PMAX, NMAX, P, N);
+    th.store(sH, LDN);
     __syncthreads();
 
     // incoming-state readout: exp(s_i) * C_i . H_c^T
     f4 acc[4];
     zero(acc);
-    wave_gemm<BF, true, true, 4>(acc, sC + 16 * w * LDN, LDN, 1, sBH, LDN, 1, Kn);
+    wave_gemm<BF, true, true, 4>(acc, sC + 16 * w * LDN, LDN, 1, sH, LDN, 1, Kn);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int iq = i0 + 16 * w + 4 * q + i;
@@ -100,26 +134,35 @@ __global__ __launch_bounds__(NTHREADS) void chunk_out_fwd_kernel(
       for (int t = 0; t < 4; ++t) acc[t][i] *= e;
     }
 
-    // intra-chunk part, one 64-column block of the chunk at a time
+    // intra-chunk part, one slab of chunk columns at a time
+    for (int sl = 0; sl < nslab; ++sl) {
+      const int j0 = sl * JW;
+      if (sl > 0) __syncthreads();  // previous slab's MFMA reads done
+      tx.store(sXt, LDJ);
 #pragma unroll
-    for (int jb = 0; jb < NBMAX; ++jb) {
-      if (jb <= ib) {
-        __syncthreads();
+      for (int jb = 0; jb < NBMAX; ++jb) {
+        const int jl = jb * BQ - j0;
+        if (jb <= ib && jl >= 0 && jl < JW) {
 #pragma unroll
-        for (int ct = 0; ct < 4; ++ct)
+          for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int il = 16 * w + 4 * q + i;
-            const int iq = i0 + il, jq = jb * BQ + 16 * ct + r;
-            float v = 0.f;
-            if (iq < Q && jq <= iq) v = cb[jb][ct][i] * __expf(sS[iq] - sS[jq]) * sDt[jq];
-            sG[il * LDQ + 16 * ct + r] = Op<BF>::cvt(v);
-          }
-        stage_tile<TI, OT, true>(sXt, LDQ, x + ((static_cast<int64_t>(bi) * T + t0 + jb * BQ) * H + h) * P, HP,
-                                 BQ, PMAX, min(BQ, Q - jb * BQ), P);
-        __syncthreads();
-        wave_gemm<BF, true, true, 4>(acc, sG + 16 * w * LDQ, LDQ, 1, sXt, LDQ, 1, BQ);
+            for (int i = 0; i < 4; ++i) {
+              const int il = 16 * w + 4 * q + i;
+              const int iq = i0 + il, jq = jb * BQ + 16 * ct + r;
+              float v = 0.f;
+              if (iq < Q && jq <= iq) v = cb[jb][ct][i] * __expf(sS[iq] - sS[jq]) * sDt[jq];
+              sG[il * LDJ + jl + 16 * ct + r] = Op<BF>::cvt(v);
+            }
+        }
       }
+      // next x slab (or the next head's first slab) loads while this one computes
+      if (sl + 1 < nslab)
+        prefetch(hh, sl + 1);
+      else if (hh + 1 < hps)
+        prefetch(hh + 1, 0);
+      __syncthreads();
+      const int kw = round_up(min(JW, jend - j0), Op<BF>::KS);
+      wave_gemm<BF, true, true, 4>(acc, sG + 16 * w * LDJ, LDJ, 1, sXt, LDJ, 1, kw);
     }
 
     // skip term and store
@@ -129,7 +172,7 @@ __global__ __launch_bounds__(NTHREADS) void chunk_out_fwd_kernel(
       for (int i = 0; i < 4; ++i) {
         const int iq = i0 + 16 * w + 4 * q + i, p = 16 * t + r;
         if (iq < Q && p < P) {
-          const int64_t o = ((static_cast<int64_t>(bi) * T + t0 + iq) * H + h) * P + p;
+          const int64_t o = (row0 + iq) * HP + static_cast<int64_t>(h) * P + p;
           store_f(y, o, acc[t][i] + Dh * load_f(x, o));
         }
       }

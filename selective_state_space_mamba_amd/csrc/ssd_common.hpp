@@ -183,4 +183,188 @@ __device__ __forceinline__ void stage_tile(TD* dst, int ld_dst, const TS* src, i
   }
 }
 
+// ------------------------------------------------------------- staging
+
+// Raw 16-byte global loads.
+__device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+
+__device__ __forceinline__ bool vec16_ok(const void* base, int64_t ld_elems, int elem_bytes) {
+  return (reinterpret_cast<uintptr_t>(base) & 15u) == 0 && ((ld_elems * elem_bytes) & 15) == 0;
+}
+
+// Eight consecutive source elements held in registers.
+template <typename TS> struct Vec8;
+template <> struct Vec8<uint16_t> {
+  uint4 v;  // 8 bf16
+  __device__ __forceinline__ float get(int e) const {
+    const uint32_t w = (&v.x)[e >> 1];
+    return __uint_as_float((e & 1) ? (w & 0xFFFF0000u) : (w << 16));
+  }
+  __device__ __forceinline__ void load(const uint16_t* p) { v = ld16(p); }
+  __device__ __forceinline__ void load_guarded(const uint16_t* p, int n) {
+    uint16_t t[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) t[e] = e < n ? p[e] : uint16_t(0);
+    v.x = t[0] | (uint32_t(t[1]) << 16);
+    v.y = t[2] | (uint32_t(t[3]) << 16);
+    v.z = t[4] | (uint32_t(t[5]) << 16);
+    v.w = t[6] | (uint32_t(t[7]) << 16);
+  }
+  __device__ __forceinline__ void zero() { v = make_uint4(0, 0, 0, 0); }
+};
+template <> struct Vec8<float> {
+  uint4 a, b;  // 8 f32
+  __device__ __forceinline__ float get(int e) const {
+    return __uint_as_float(e < 4 ? (&a.x)[e] : (&b.x)[e - 4]);
+  }
+  __device__ __forceinline__ void load(const float* p) {
+    a = ld16(p);
+    b = ld16(p + 4);
+  }
+  __device__ __forceinline__ void load_guarded(const float* p, int n) {
+    float t[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) t[e] = e < n ? p[e] : 0.f;
+    a = make_uint4(__float_as_uint(t[0]), __float_as_uint(t[1]), __float_as_uint(t[2]), __float_as_uint(t[3]));
+    b = make_uint4(__float_as_uint(t[4]), __float_as_uint(t[5]), __float_as_uint(t[6]), __float_as_uint(t[7]));
+  }
+  __device__ __forceinline__ void zero() { a = b = make_uint4(0, 0, 0, 0); }
+};
+
+// Store eight floats (converted to the operand type) at an LDS address that is
+// 16-byte aligned for bf16 (one 16-byte write) or f32 (two).
+__device__ __forceinline__ void st8(uint16_t* d, const float (&f)[8]) {
+  uint4 o;
+  o.x = f32_to_bf16_bits(f[0]) | (uint32_t(f32_to_bf16_bits(f[1])) << 16);
+  o.y = f32_to_bf16_bits(f[2]) | (uint32_t(f32_to_bf16_bits(f[3])) << 16);
+  o.z = f32_to_bf16_bits(f[4]) | (uint32_t(f32_to_bf16_bits(f[5])) << 16);
+  o.w = f32_to_bf16_bits(f[6]) | (uint32_t(f32_to_bf16_bits(f[7])) << 16);
+  *reinterpret_cast<uint4*>(d) = o;
+}
+__device__ __forceinline__ void st8(float* d, const float (&f)[8]) {
+  *reinterpret_cast<float4*>(d) = make_float4(f[0], f[1], f[2], f[3]);
+  *reinterpret_cast<float4*>(d + 4) = make_float4(f[4], f[5], f[6], f[7]);
+}
+
+// Global -> LDS staging of a ROWS x COLS tile whose source rows are contiguous:
+// source element (r, c) at src[r*ld + c], destination dst[r*ld_dst + c]
+// (ld_dst a multiple of 8).  Elements outside rows_valid x cols_valid are zero.
+// load() issues every global load of the tile into registers; store() converts
+// (optionally scaling by row) and writes LDS.  Splitting the two lets a kernel
+// overlap the loads of the next tile with work on the current one.
+template <typename TS, int ROWS, int COLS>
+struct RowTile {
+  static_assert(COLS % 8 == 0, "tile width must be a multiple of 8");
+  static constexpr int ITEMS = ROWS * COLS / 8;
+  static constexpr int PER = (ITEMS + NTHREADS - 1) / NTHREADS;
+  Vec8<TS> v[PER];
+  int nrows;
+  __device__ __forceinline__ void load(const TS* src, int64_t ld, int rows_valid, int cols_valid) {
+    nrows = rows_valid;
+    const bool vec = vec16_ok(src, ld, sizeof(TS));
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int it = threadIdx.x + i * NTHREADS;
+      const int r = it / (COLS / 8), c0 = (it % (COLS / 8)) * 8;
+      if (it < ITEMS && r < rows_valid && c0 < cols_valid) {
+        const TS* p = src + r * ld + c0;
+        if (vec && c0 + 8 <= cols_valid)
+          v[i].load(p);
+        else
+          v[i].load_guarded(p, cols_valid - c0);
+      } else {
+        v[i].zero();
+      }
+    }
+  }
+  template <typename TD>
+  __device__ __forceinline__ void store(TD* dst, int ld_dst, const float* row_scale = nullptr) const {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int it = threadIdx.x + i * NTHREADS;
+      if (it < ITEMS) {
+        const int r = it / (COLS / 8), c0 = (it % (COLS / 8)) * 8;
+        const float sc = (row_scale && r < nrows) ? row_scale[r] : 1.f;
+        float f[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) f[e] = v[i].get(e) * sc;
+        st8(dst + r * ld_dst + c0, f);
+      }
+    }
+  }
+};
+
+// Global -> LDS staging with a transpose: source element (r, c) at
+// src[r*ld + c] (ROWS x COLS), destination dst[c*ld_dst + r], i.e. the LDS tile
+// has COLS rows of ROWS contiguous elements.  Each thread moves 8x8 blocks
+// through registers.  Optional scale by source row (a time step, say).
+template <typename TS, int ROWS, int COLS>
+struct TransTile {
+  static_assert(COLS % 8 == 0 && ROWS % 8 == 0, "tile sides must be multiples of 8");
+  static constexpr int ITEMS = (ROWS / 8) * (COLS / 8);
+  static constexpr int PER = (ITEMS + NTHREADS - 1) / NTHREADS;
+  Vec8<TS> v[PER][8];
+  int nrows;
+  __device__ __forceinline__ void load(const TS* src, int64_t ld, int rows_valid, int cols_valid) {
+    nrows = rows_valid;
+    const bool vec = vec16_ok(src, ld, sizeof(TS));
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int it = threadIdx.x + i * NTHREADS;
+      const int c0 = (it % (COLS / 8)) * 8, r0 = (it / (COLS / 8)) * 8;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int r = r0 + e;
+        if (it < ITEMS && r < rows_valid && c0 < cols_valid) {
+          const TS* p = src + r * ld + c0;
+          if (vec && c0 + 8 <= cols_valid)
+            v[i][e].load(p);
+          else
+            v[i][e].load_guarded(p, cols_valid - c0);
+        } else {
+          v[i][e].zero();
+        }
+      }
+    }
+  }
+  template <typename TD>
+  __device__ __forceinline__ void store(TD* dst, int ld_dst, const float* row_scale = nullptr) const {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int it = threadIdx.x + i * NTHREADS;
+      if (it < ITEMS) {
+        const int c0 = (it % (COLS / 8)) * 8, r0 = (it / (COLS / 8)) * 8;
+        float sc[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sc[e] = (row_scale && r0 + e < nrows) ? row_scale[r0 + e] : 1.f;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          float f[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) f[e] = v[i][e].get(c) * sc[e];
+          st8(dst + (c0 + c) * ld_dst + r0, f);
+        }
+      }
+    }
+  }
+  // The same registers written untransposed: dst[r*ld_dst + c].
+  template <typename TD>
+  __device__ __forceinline__ void store_rows(TD* dst, int ld_dst) const {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int it = threadIdx.x + i * NTHREADS;
+      if (it < ITEMS) {
+        const int c0 = (it % (COLS / 8)) * 8, r0 = (it / (COLS / 8)) * 8;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          float f[8];
+#pragma unroll
+          for (int c = 0; c < 8; ++c) f[c] = v[i][e].get(c);
+          st8(dst + (r0 + e) * ld_dst + c0, f);
+        }
+      }
+    }
+  }
+};
+
 }  // namespace ssd

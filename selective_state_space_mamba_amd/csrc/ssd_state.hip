@@ -27,8 +27,12 @@
 
 namespace ssd {
 
+// Time steps staged per slab: a whole chunk of up to 256 steps for bf16
+// operands (64 KB of B), 128 for f32.
+template <bool BF> struct StateSlab { static constexpr int SJ = BF ? 256 : 128; };
+
 template <typename TX, typename TB, typename TDT, bool BF, bool REV>
-__global__ __launch_bounds__(NTHREADS) void chunk_state_kernel(
+__global__ __launch_bounds__(NTHREADS, 2) void chunk_state_kernel(
     const TX* __restrict__ X,          // fwd: x; bwd: dy            [b,T,H,P]
     const TB* __restrict__ Bm,         // fwd: B; bwd: C             [b,T,G,N]
     const TDT* __restrict__ dt,        // [b,T,H]
@@ -41,7 +45,8 @@ __global__ __launch_bounds__(NTHREADS) void chunk_state_kernel(
     int T, int H, int P, int N, int G, int Q) {
   typedef typename Op<BF>::T OT;
   constexpr int PB = STATE_PB;
-  constexpr int LDX = BQ + (BF ? 8 : 4);  // [p][j] and [n][j]: time contiguous
+  constexpr int SJ = StateSlab<BF>::SJ;
+  constexpr int LDX = SJ + (BF ? 8 : 4);  // [p][j] and [n][j]: time contiguous
   __shared__ __attribute__((aligned(16))) OT sX[PB * LDX];
   __shared__ __attribute__((aligned(16))) OT sB[NMAX * LDX];
   __shared__ float sS[QMAX];
@@ -52,10 +57,11 @@ __global__ __launch_bounds__(NTHREADS) void chunk_state_kernel(
   const int npb = gridDim.x;
   const int p0 = pb * PB;
   const int g = h / (H / G);
-  const int nc = T / Q, nb = (Q + BQ - 1) / BQ;
+  const int nc = T / Q;
+  const int nslab = (Q + SJ - 1) / SJ;
   const float A = -__expf(A_log[h]);
   const int tid = threadIdx.x, w = wave_id(), l = lane_id(), r = l & 15, q = l >> 4;
-  const int64_t HP = static_cast<int64_t>(H) * P;
+  const int64_t HP = static_cast<int64_t>(H) * P, GN = static_cast<int64_t>(G) * N;
   const int64_t PN = static_cast<int64_t>(P) * N;
 
   // wave w holds state columns n = 32w .. 32w+31 (two 16-wide tiles) of rows p0..p0+15
@@ -68,30 +74,44 @@ __global__ __launch_bounds__(NTHREADS) void chunk_state_kernel(
       st[t][i] = (!REV && init && p < P && n < N) ? init[(static_cast<int64_t>(bi) * H + h) * PN + p * N + n] : 0.f;
     }
 
-  for (int it = 0; it < nc; ++it) {
-    const int c = REV ? nc - 1 - it : it;
-    const int64_t t0 = static_cast<int64_t>(c) * Q;
-    const float dtv = (tid < Q) ? load_f(dt, (static_cast<int64_t>(bi) * T + t0 + tid) * H + h) : 0.f;
-    const float s = block_inclusive_scan(dtv * A, sTmp);
-    if (tid < Q) sS[tid] = s;
-    __syncthreads();
-    const float s_end = sS[Q - 1];
-    if (tid < Q) sW[tid] = REV ? __expf(s) : __expf(s_end - s) * dtv;
+  TransTile<TX, SJ, PB> tx;    // x (or dy) rows j, columns p0..p0+15 -> [p][j]
+  TransTile<TB, SJ, NMAX> tb;  // B (or C) rows j -> [n][j]
+  const int total = nc * nslab;
+  auto chunk_of = [&](int step) { const int it = step / nslab; return REV ? nc - 1 - it : it; };
+  auto prefetch = [&](int step, float& dtn) {
+    const int c = chunk_of(step), sl = step % nslab;
+    const int64_t row0 = static_cast<int64_t>(bi) * T + static_cast<int64_t>(c) * Q + sl * SJ;
+    const int vr = min(SJ, Q - sl * SJ);
+    tx.load(X + row0 * HP + static_cast<int64_t>(h) * P + p0, HP, vr, P - p0);
+    tb.load(Bm + row0 * GN + static_cast<int64_t>(g) * N, GN, vr, N);
+    if (sl == 0)
+      dtn = (tid < Q) ? load_f(dt, (static_cast<int64_t>(bi) * T + static_cast<int64_t>(c) * Q + tid) * H + h) : 0.f;
+  };
+  float dt_next = 0.f;
+  prefetch(0, dt_next);
 
-    f4 acc[2];
-    zero(acc);
-    for (int jb = 0; jb < nb; ++jb) {
-      const int j0 = jb * BQ, vr = min(BQ, Q - j0);
+  f4 acc[2];
+  zero(acc);
+  for (int step = 0; step < total; ++step) {
+    const int c = chunk_of(step), sl = step % nslab;
+    if (sl == 0) {
+      const float dtv = dt_next;
+      const float s = block_inclusive_scan(dtv * A, sTmp);
+      if (tid < Q) sS[tid] = s;
       __syncthreads();
-      stage_tile<TX, OT, true>(sX, LDX, X + ((static_cast<int64_t>(bi) * T + t0 + j0) * H + h) * P + p0,
-                               HP, BQ, PB, vr, P - p0, sW + j0);
-      stage_tile<TB, OT, true>(sB, LDX, Bm + ((static_cast<int64_t>(bi) * T + t0 + j0) * G + g) * N,
-                               static_cast<int64_t>(G) * N, BQ, NMAX, vr, N);
-      __syncthreads();
-      wave_gemm<BF, true, true, 2>(acc, sX, LDX, 1, sB + 32 * w * LDX, LDX, 1, BQ);
+      const float s_end = sS[Q - 1];
+      if (tid < Q) sW[tid] = REV ? __expf(s) : __expf(s_end - s) * dtv;
+      zero(acc);
     }
+    __syncthreads();  // sW visible; previous slab's MFMA reads of sX / sB done
+    tx.store(sX, LDX, sW + sl * SJ);
+    tb.store(sB, LDX);
+    if (step + 1 < total) prefetch(step + 1, dt_next);
+    __syncthreads();
+    wave_gemm<BF, true, true, 2>(acc, sX, LDX, 1, sB + 32 * w * LDX, LDX, 1, round_up(min(SJ, Q - sl * SJ), Op<BF>::KS));
+    if (sl != nslab - 1) continue;
 
-    const float decay = __expf(s_end);
+    const float decay = __expf(sS[Q - 1]);
     const int64_t sbase = ((static_cast<int64_t>(bi) * nc + c) * H + h) * PN;
     float gh = 0.f;
 #pragma unroll
@@ -107,12 +127,10 @@ __global__ __launch_bounds__(NTHREADS) void chunk_state_kernel(
       }
     if (REV) {
       gh = wave_sum(gh);
-      __syncthreads();
       if (l == 0) sTmp[4 + w] = gh;
       __syncthreads();
       if (tid == 0)
-        gh_part[((static_cast<int64_t>(bi) * nc + c) * H + h) * npb + pb] =
-            sTmp[4] + sTmp[5] + sTmp[6] + sTmp[7];
+        gh_part[((static_cast<int64_t>(bi) * nc + c) * H + h) * npb + pb] = sTmp[4] + sTmp[5] + sTmp[6] + sTmp[7];
     }
   }
 
