@@ -323,7 +323,7 @@ int ssd_bwd(const ssd_problem* prob, const void* x, const void* dt, const float*
   s.dD_part = at<float>(workspace, plan.dD);
   s.dB_part = plan.nsplit > 1 ? at<float>(workspace, plan.dB) : nullptr;
   s.dC_part = plan.nsplit > 1 ? at<float>(workspace, plan.dC) : nullptr;
-  float* gamma = at<float>(workspace, plan.gamma);
+  void* gamma = at<float>(workspace, plan.gamma);
 
   const float* states = chunk_states;
   if (!states) {

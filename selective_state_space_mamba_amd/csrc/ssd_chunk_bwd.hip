@@ -30,6 +30,8 @@
 // L yx dt over heads before the single contraction with C (or B) that dB (dC)
 // needs.  Every cross-workgroup sum goes through fixed-order partial buffers
 // (no atomics), so results are bitwise reproducible.
+#include <type_traits>
+
 #include "ssd_common.hpp"
 #include "ssd_launch.hpp"
 
@@ -56,7 +58,7 @@ template <typename TI, typename TY, bool BF>
 __global__ __launch_bounds__(NTHREADS) void chunk_bwd_col_kernel(
     const TI* __restrict__ x, const TI* __restrict__ Bm, const TI* __restrict__ Cm,
     const TI* __restrict__ dt, const TY* __restrict__ dy, const float* __restrict__ A_log,
-    const float* __restrict__ D, const float* __restrict__ gamma, float* __restrict__ dx,
+    const float* __restrict__ D, const typename Op<BF>::T* __restrict__ gamma, float* __restrict__ dx,
     float* __restrict__ dB_out, float* __restrict__ colE, float* __restrict__ diagE,
     float* __restrict__ Rp, int T, int H, int P, int N, int G, int Q, int nsplit) {
   typedef typename Op<BF>::T OT;
@@ -85,7 +87,7 @@ __global__ __launch_bounds__(NTHREADS) void chunk_bwd_col_kernel(
 
   const int nc = T / Q, nb = (Q + BQ - 1) / BQ;
   const int hpg = H / G, hps = hpg / nsplit;
-  int idx = blockIdx.x;
+  int idx = xcd_logical_block(blockIdx.x, gridDim.x);
   const int jb = idx % nb;
   idx /= nb;
   const int sp = idx % nsplit;
@@ -133,8 +135,10 @@ __global__ __launch_bounds__(NTHREADS) void chunk_bwd_col_kernel(
   zero(dbs);
 
   RowTile<TI, BQ, PMAX> tX;          // x_jb
-  TransTile<TY, IW, PMAX> tDy;        // dy rows of one slab
-  TransTile<float, PMAX, NMAX> tG;    // Gamma_{c+1}
+  // bf16 operands need dy and Gamma also transposed; f32 operands read the
+  // transposed views with strided fetches, so rows suffice.
+  typename std::conditional<BF, TransTile<TY, IW, PMAX>, RowTile<TY, IW, PMAX>>::type tDy;  // dy rows of a slab
+  typename std::conditional<BF, TransTile<OT, PMAX, NMAX>, RowTile<OT, PMAX, NMAX>>::type tG;  // Gamma_{c+1}
   float dt_next = 0.f;
   auto load_head = [&](int hh) {
     const int h = g * hpg + sp * hps + hh;
@@ -156,10 +160,23 @@ __global__ __launch_bounds__(NTHREADS) void chunk_bwd_col_kernel(
       sDt[tid] = dtv;
     }
     tX.store(sX, LDP);
+    // skip term D dy_j of this wave's output rows, loaded now, used at the end
+    float dsk[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int jq = j0 + 16 * w + 4 * q + i;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int p = 16 * t + r;
+        dsk[i][t] = (jq < Q && p < P) ? load_f(dy, (row0 + jq) * HP + static_cast<int64_t>(h) * P + p) : 0.f;
+      }
+    }
 
     f4 dxa[4];
     zero(dxa);
     float csum[4] = {0.f, 0.f, 0.f, 0.f}, dsum[4] = {0.f, 0.f, 0.f, 0.f};
+    bool sj_loaded = false;
+    float sj[4], dtj4[4];
     for (int sl = 0; sl < nsl; ++sl) {
       const int s0 = i_lo + sl * IW;
       if (sl > 0) __syncthreads();
@@ -177,21 +194,41 @@ __global__ __launch_bounds__(NTHREADS) void chunk_bwd_col_kernel(
           f4 yx[4];
           zero(yx);
           wave_gemm<BF, true, true, 4>(yx, sDy + (il + 16 * w) * LDP, LDP, 1, sX, LDP, 1, Kp);
+          if (!sj_loaded) {
 #pragma unroll
-          for (int ct = 0; ct < 4; ++ct)
+            for (int ct = 0; ct < 4; ++ct) {
+              const int jq = min(j0 + 16 * ct + r, Q - 1);
+              sj[ct] = sS[jq];
+              dtj4[ct] = sDt[jq];
+            }
+            sj_loaded = true;
+          }
+          const int ir0 = il + 16 * w + 4 * q;  // the lane's four rows inside the slab
+          float si[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) si[i] = sS[min(s0 + ir0 + i, Q - 1)];
+#pragma unroll
+          for (int ct = 0; ct < 4; ++ct) {
+            const int jl = 16 * ct + r, jq = j0 + jl;
+            float g4[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              const int ir = il + 16 * w + 4 * q + i;  // row inside the slab
-              const int iq = s0 + ir, jl = 16 * ct + r, jq = j0 + jl;
+              const int iq = s0 + ir0 + i;
               const bool valid = iq < Q && jq <= iq;
-              const float Lv = valid ? __expf(sS[iq] - sS[jq]) : 0.f;
+              const float Lv = valid ? __expf(si[i] - sj[ct]) : 0.f;
               const float g1 = Lv * cb[ib][ct][i];
               const float e = g1 * yx[ct][i];
               csum[ct] += e;
               if (iq == jq) dsum[ct] += e;
-              ws[ib][ct][i] += valid ? Lv * yx[ct][i] * sDt[jq] : 0.f;
-              sGt[jl * LDI + ir] = Op<BF>::cvt(g1);
+              ws[ib][ct][i] += Lv * yx[ct][i] * dtj4[ct];
+              g4[i] = g1;
             }
+            OT* gp = sGt + jl * LDI + ir0;
+            if constexpr (BF)
+              *reinterpret_cast<uint2*>(gp) = make_uint2(pack_bf16(g4[0], g4[1]), pack_bf16(g4[2], g4[3]));
+            else
+              *reinterpret_cast<float4*>(gp) = make_float4(g4[0], g4[1], g4[2], g4[3]);
+          }
         }
       }
       __syncthreads();
@@ -250,7 +287,7 @@ __global__ __launch_bounds__(NTHREADS) void chunk_bwd_col_kernel(
         const int p = 16 * t + r;
         if (valid && p < P) {
           const int64_t o = (row0 + jq) * HP + static_cast<int64_t>(h) * P + p;
-          dx[o] = dtj * (dxa[t][i] + wj * bg[t][i]) + Dh * load_f(dy, o);
+          dx[o] = dtj * (dxa[t][i] + wj * bg[t][i]) + Dh * dsk[i][t];
         }
       }
     }
@@ -265,10 +302,14 @@ __global__ __launch_bounds__(NTHREADS) void chunk_bwd_col_kernel(
       const int il = ib * BQ - s0;
       if (ib >= jb && ib < nb && il >= 0 && il < IW) {
 #pragma unroll
-        for (int ct = 0; ct < 4; ++ct)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            sWt[(16 * ct + r) * LDI + il + 16 * w + 4 * q + i] = Op<BF>::cvt(ws[ib][ct][i]);
+        for (int ct = 0; ct < 4; ++ct) {
+          OT* wp = sWt + (16 * ct + r) * LDI + il + 16 * w + 4 * q;
+          if constexpr (BF)
+            *reinterpret_cast<uint2*>(wp) = make_uint2(pack_bf16(ws[ib][ct][0], ws[ib][ct][1]),
+                                                        pack_bf16(ws[ib][ct][2], ws[ib][ct][3]));
+          else
+            *reinterpret_cast<float4*>(wp) = make_float4(ws[ib][ct][0], ws[ib][ct][1], ws[ib][ct][2], ws[ib][ct][3]);
+        }
       }
     }
     const int vi = min(IW, Q - s0);
@@ -330,7 +371,7 @@ __global__ __launch_bounds__(NTHREADS) void chunk_bwd_row_kernel(
 
   const int nc = T / Q, nb = (Q + BQ - 1) / BQ;
   const int hpg = H / G, hps = hpg / nsplit;
-  int idx = blockIdx.x;
+  int idx = xcd_logical_block(blockIdx.x, gridDim.x);
   const int ib = nb - 1 - idx % nb;  // heavier row blocks first
   idx /= nb;
   const int sp = idx % nsplit;
@@ -378,7 +419,7 @@ __global__ __launch_bounds__(NTHREADS) void chunk_bwd_row_kernel(
   zero(dca);
 
   RowTile<TY, BQ, PMAX> tDy;        // dy_ib
-  TransTile<float, PMAX, NMAX> tH;  // H_c rows p, columns n
+  TransTile<float, PMAX, NMAX, 4> tH;  // H_c rows p, columns n
   RowTile<TI, JW, PMAX> tXs;        // x rows of one slab
   float dt_next = 0.f;
   auto load_head = [&](int hh) {
@@ -445,13 +486,22 @@ __global__ __launch_bounds__(NTHREADS) void chunk_bwd_row_kernel(
           f4 yx[4];
           zero(yx);
           wave_gemm<BF, true, true, 4>(yx, sDy + 16 * w * LDP, LDP, 1, sXr + jl * LDP, LDP, 1, Kp);
+          float si[4], sjv[4], dtjv[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) si[i] = sS[min(i0 + 16 * w + 4 * q + i, Q - 1)];
+#pragma unroll
+          for (int ct = 0; ct < 4; ++ct) {
+            const int jq = min(jb * BQ + 16 * ct + r, Q - 1);
+            sjv[ct] = sS[jq];
+            dtjv[ct] = sDt[jq];
+          }
 #pragma unroll
           for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
               const int iq = i0 + 16 * w + 4 * q + i, jq = jb * BQ + 16 * ct + r;
               const bool valid = iq < Q && jq <= iq;
-              const float ly = valid ? __expf(sS[iq] - sS[jq]) * yx[ct][i] * sDt[jq] : 0.f;
+              const float ly = valid ? __expf(si[i] - sjv[ct]) * yx[ct][i] * dtjv[ct] : 0.f;
               ws[jb][ct][i] += ly;
               if (jq < iq) racc[i] += ly * cb[jb][ct][i];
             }
@@ -609,17 +659,18 @@ static int64_t nblocks_chunk(const Dims& d, int nsplit) {
 
 template <typename TI, typename TY, bool BF>
 static void col_launch(const Dims& d, int nsplit, const void* x, const void* B, const void* C, const void* dt,
-                       const void* dy, const float* A_log, const float* D, const float* gamma, float* dx,
+                       const void* dy, const float* A_log, const float* D, const void* gamma, float* dx,
                        float* dB_out, const BwdScratch& s, hipStream_t st) {
   hipLaunchKernelGGL((chunk_bwd_col_kernel<TI, TY, BF>), dim3(nblocks_chunk(d, nsplit)), dim3(NTHREADS), 0, st,
                      static_cast<const TI*>(x), static_cast<const TI*>(B), static_cast<const TI*>(C),
-                     static_cast<const TI*>(dt), static_cast<const TY*>(dy), A_log, D, gamma, dx, dB_out, s.colE,
+                     static_cast<const TI*>(dt), static_cast<const TY*>(dy), A_log, D,
+                     static_cast<const typename Op<BF>::T*>(gamma), dx, dB_out, s.colE,
                      s.diagE, s.Rp, d.T, d.H, d.P, d.N, d.G, d.Q, nsplit);
 }
 
 hipError_t launch_chunk_bwd_col(const Dims& d, DType act, DType dyt, int nsplit, const void* x,
                                 const void* B, const void* C, const void* dt, const void* dy,
-                                const float* A_log, const float* D, const float* gamma, float* dx,
+                                const float* A_log, const float* D, const void* gamma, float* dx,
                                 float* dB_out, const BwdScratch& s, hipStream_t st) {
   if (act == BF16) {
     if (dyt == BF16)

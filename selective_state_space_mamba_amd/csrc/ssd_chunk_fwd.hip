@@ -10,8 +10,9 @@
 //       + D x_i.
 //
 // A workgroup owns one 64-row block ib of chunk c for a run of heads of one
-// group.  It computes the group's C.B^T tiles (ib, jb <= ib) once with MFMA
-// (K = d_state) and keeps them in registers, then per head applies the decay
+// group.  It computes the group's (C.B^T)^T = B.C^T tiles (jb <= ib, ib) once
+// with MFMA (K = d_state) and keeps them in registers (transposed, so that each
+// lane's four values of the masked matrix are adjacent in LDS), then per head applies the decay
 // mask L_ij = exp(s_i - s_j) (i >= j; exponents are <= 0) and dt_j, and runs
 // the two remaining contractions (K = chunk columns, K = d_state) on MFMA.
 // Operands are staged with 16-byte loads; the next head's x and H_c are loaded
@@ -49,7 +50,7 @@ __global__ __launch_bounds__(NTHREADS) void chunk_out_fwd_kernel(
 
   const int nc = T / Q, nb = (Q + BQ - 1) / BQ;
   const int hpg = H / G, hps = hpg / nsplit;
-  int idx = blockIdx.x;
+  int idx = xcd_logical_block(blockIdx.x, gridDim.x);
   const int ib = nb - 1 - idx % nb;  // heavier row blocks first
   idx /= nb;
   const int sp = idx % nsplit;
@@ -88,8 +89,8 @@ __global__ __launch_bounds__(NTHREADS) void chunk_out_fwd_kernel(
 #pragma unroll
     for (int jb = 0; jb < NBMAX; ++jb) {
       const int jl = jb * BQ - j0;  // block start inside the slab
-      if (jb <= ib && jl >= 0 && jl < JW)
-        wave_gemm<BF, true, true, 4>(cb[jb], sC + 16 * w * LDN, LDN, 1, sB + jl * LDN, LDN, 1, Kn);
+      if (jb <= ib && jl >= 0 && jl < JW)  // rows j of block jb (this wave's 16), columns i
+        wave_gemm<BF, true, true, 4>(cb[jb], sB + (jl + 16 * w) * LDN, LDN, 1, sC, LDN, 1, Kn);
     }
   }
 
@@ -120,6 +121,17 @@ __global__ __launch_bounds__(NTHREADS) void chunk_out_fwd_kernel(
       sDt[tid] = dtv;
     }
     th.store(sH, LDN);
+    // skip term D x_i of this wave's output rows, loaded now, used at the end
+    float xsk[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int iq = i0 + 16 * w + 4 * q + i;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int p = 16 * t + r;
+        xsk[i][t] = (iq < Q && p < P) ? load_f(x, (row0 + iq) * HP + static_cast<int64_t>(h) * P + p) : 0.f;
+      }
+    }
     __syncthreads();
 
     // incoming-state readout: exp(s_i) * C_i . H_c^T
@@ -144,15 +156,24 @@ __global__ __launch_bounds__(NTHREADS) void chunk_out_fwd_kernel(
         const int jl = jb * BQ - j0;
         if (jb <= ib && jl >= 0 && jl < JW) {
 #pragma unroll
-          for (int ct = 0; ct < 4; ++ct)
+          for (int t = 0; t < 4; ++t) {
+            // lane holds B.C^T rows j = jb*64 + 16w + 4q + e (e = 0..3), column i = i0 + 16t + r
+            const int il = 16 * t + r, iq = i0 + il;
+            const int jw = 16 * w + 4 * q;  // first of the lane's four j inside block jb
+            const float si = sS[min(iq, Q - 1)];
+            float v4[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int il = 16 * w + 4 * q + i;
-              const int iq = i0 + il, jq = jb * BQ + 16 * ct + r;
-              float v = 0.f;
-              if (iq < Q && jq <= iq) v = cb[jb][ct][i] * __expf(sS[iq] - sS[jq]) * sDt[jq];
-              sG[il * LDJ + jl + 16 * ct + r] = Op<BF>::cvt(v);
+            for (int e = 0; e < 4; ++e) {
+              const int jq = jb * BQ + jw + e;
+              const int jc = min(jq, Q - 1);
+              v4[e] = (iq < Q && jq <= iq) ? cb[jb][t][e] * __expf(si - sS[jc]) * sDt[jc] : 0.f;
             }
+            OT* gp = sG + il * LDJ + jl + jw;
+            if constexpr (BF)
+              *reinterpret_cast<uint2*>(gp) = make_uint2(pack_bf16(v4[0], v4[1]), pack_bf16(v4[2], v4[3]));
+            else
+              *reinterpret_cast<float4*>(gp) = make_float4(v4[0], v4[1], v4[2], v4[3]);
+          }
         }
       }
       // next x slab (or the next head's first slab) loads while this one computes
@@ -173,7 +194,7 @@ __global__ __launch_bounds__(NTHREADS) void chunk_out_fwd_kernel(
         const int iq = i0 + 16 * w + 4 * q + i, p = 16 * t + r;
         if (iq < Q && p < P) {
           const int64_t o = (row0 + iq) * HP + static_cast<int64_t>(h) * P + p;
-          store_f(y, o, acc[t][i] + Dh * load_f(x, o));
+          store_f(y, o, acc[t][i] + Dh * xsk[i][t]);
         }
       }
   }

@@ -101,10 +101,16 @@ template <bool BF, bool AKC, bool BKC, int NT>
 __device__ __forceinline__ void wave_gemm(f4 (&acc)[NT], const typename Op<BF>::T* A, int asr,
                                           int ask, const typename Op<BF>::T* B, int bsr, int bsk,
                                           int K) {
-  for (int k0 = 0; k0 < K; k0 += Op<BF>::KS) {
-    const typename Op<BF>::V a = fetch<BF, AKC>(A, asr, ask, 0, k0);
+  typedef typename Op<BF>::V V;
+  constexpr int KS = Op<BF>::KS;
+  if (K <= 0) return;
+  // the next k-step's A fragment is read from LDS while the current MFMAs run
+  V a = fetch<BF, AKC>(A, asr, ask, 0, 0);
+  for (int k0 = 0; k0 < K; k0 += KS) {
+    const V an = (k0 + KS < K) ? fetch<BF, AKC>(A, asr, ask, 0, k0 + KS) : a;
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[t] = mfma(a, fetch<BF, BKC>(B, bsr, bsk, 16 * t, k0), acc[t]);
+    a = an;
   }
 }
 
@@ -231,19 +237,29 @@ template <> struct Vec8<float> {
   __device__ __forceinline__ void zero() { a = b = make_uint4(0, 0, 0, 0); }
 };
 
+// Two floats -> two bf16 (round to nearest even) in one 32-bit word, low
+// half first (one v_cvt_pk_bf16_f32 on gfx950).
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  const bf16x2 v = {static_cast<__bf16>(a), static_cast<__bf16>(b)};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
 // Store eight floats (converted to the operand type) at an LDS address that is
 // 16-byte aligned for bf16 (one 16-byte write) or f32 (two).
 __device__ __forceinline__ void st8(uint16_t* d, const float (&f)[8]) {
-  uint4 o;
-  o.x = f32_to_bf16_bits(f[0]) | (uint32_t(f32_to_bf16_bits(f[1])) << 16);
-  o.y = f32_to_bf16_bits(f[2]) | (uint32_t(f32_to_bf16_bits(f[3])) << 16);
-  o.z = f32_to_bf16_bits(f[4]) | (uint32_t(f32_to_bf16_bits(f[5])) << 16);
-  o.w = f32_to_bf16_bits(f[6]) | (uint32_t(f32_to_bf16_bits(f[7])) << 16);
-  *reinterpret_cast<uint4*>(d) = o;
+  *reinterpret_cast<uint4*>(d) =
+      make_uint4(pack_bf16(f[0], f[1]), pack_bf16(f[2], f[3]), pack_bf16(f[4], f[5]), pack_bf16(f[6], f[7]));
 }
 __device__ __forceinline__ void st8(float* d, const float (&f)[8]) {
   *reinterpret_cast<float4*>(d) = make_float4(f[0], f[1], f[2], f[3]);
   *reinterpret_cast<float4*>(d + 4) = make_float4(f[4], f[5], f[6], f[7]);
+}
+
+// 16-bit element c (0..7) of rows a and b packed as (a_c | b_c << 16).
+__device__ __forceinline__ uint32_t pair16(const uint4& a, const uint4& b, int c) {
+  const uint32_t wa = (&a.x)[c >> 1], wb = (&b.x)[c >> 1];
+  return (c & 1) ? ((wa >> 16) | (wb & 0xFFFF0000u)) : ((wa & 0xFFFFu) | (wb << 16));
 }
 
 // Global -> LDS staging of a ROWS x COLS tile whose source rows are contiguous:
@@ -284,6 +300,12 @@ struct RowTile {
       const int it = threadIdx.x + i * NTHREADS;
       if (it < ITEMS) {
         const int r = it / (COLS / 8), c0 = (it % (COLS / 8)) * 8;
+        if constexpr (sizeof(TS) == 2 && sizeof(TD) == 2) {
+          if (!row_scale) {
+            *reinterpret_cast<uint4*>(dst + r * ld_dst + c0) = v[i].v;
+            continue;
+          }
+        }
         const float sc = (row_scale && r < nrows) ? row_scale[r] : 1.f;
         float f[8];
 #pragma unroll
@@ -292,18 +314,24 @@ struct RowTile {
       }
     }
   }
+  // Same as store() without a scale (interface shared with TransTile).
+  template <typename TD>
+  __device__ __forceinline__ void store_rows(TD* dst, int ld_dst) const { store(dst, ld_dst); }
 };
 
 // Global -> LDS staging with a transpose: source element (r, c) at
 // src[r*ld + c] (ROWS x COLS), destination dst[c*ld_dst + r], i.e. the LDS tile
-// has COLS rows of ROWS contiguous elements.  Each thread moves 8x8 blocks
-// through registers.  Optional scale by source row (a time step, say).
-template <typename TS, int ROWS, int COLS>
+// has COLS rows of ROWS contiguous elements.  Each thread moves RB x 8 blocks
+// (RB = 8 or 4 source rows) through registers: 16-bit blocks are transposed
+// with byte permutes, f32 blocks converted in pairs.  Optional scale by source
+// row (a time step, say).  RB = 4 halves the registers a thread holds.
+template <typename TS, int ROWS, int COLS, int RB = 8>
 struct TransTile {
-  static_assert(COLS % 8 == 0 && ROWS % 8 == 0, "tile sides must be multiples of 8");
-  static constexpr int ITEMS = (ROWS / 8) * (COLS / 8);
+  static_assert(RB == 8 || RB == 4, "blocks of 8 or 4 rows");
+  static_assert(COLS % 8 == 0 && ROWS % RB == 0, "tile sides must be multiples of the block");
+  static constexpr int ITEMS = (ROWS / RB) * (COLS / 8);
   static constexpr int PER = (ITEMS + NTHREADS - 1) / NTHREADS;
-  Vec8<TS> v[PER][8];
+  Vec8<TS> v[PER][RB];
   int nrows;
   __device__ __forceinline__ void load(const TS* src, int64_t ld, int rows_valid, int cols_valid) {
     nrows = rows_valid;
@@ -311,9 +339,9 @@ struct TransTile {
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int it = threadIdx.x + i * NTHREADS;
-      const int c0 = (it % (COLS / 8)) * 8, r0 = (it / (COLS / 8)) * 8;
+      const int c0 = (it % (COLS / 8)) * 8, r0 = (it / (COLS / 8)) * RB;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
+      for (int e = 0; e < RB; ++e) {
         const int r = r0 + e;
         if (it < ITEMS && r < rows_valid && c0 < cols_valid) {
           const TS* p = src + r * ld + c0;
@@ -333,16 +361,38 @@ struct TransTile {
     for (int i = 0; i < PER; ++i) {
       const int it = threadIdx.x + i * NTHREADS;
       if (it < ITEMS) {
-        const int c0 = (it % (COLS / 8)) * 8, r0 = (it / (COLS / 8)) * 8;
-        float sc[8];
+        const int c0 = (it % (COLS / 8)) * 8, r0 = (it / (COLS / 8)) * RB;
+        if constexpr (sizeof(TS) == 2 && sizeof(TD) == 2) {
+          if (!row_scale) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) sc[e] = (row_scale && r0 + e < nrows) ? row_scale[r0 + e] : 1.f;
+            for (int c = 0; c < 8; ++c) {
+              TD* d = dst + (c0 + c) * ld_dst + r0;
+              if constexpr (RB == 8)
+                *reinterpret_cast<uint4*>(d) =
+                    make_uint4(pair16(v[i][0].v, v[i][1].v, c), pair16(v[i][2].v, v[i][3].v, c),
+                               pair16(v[i][4].v, v[i][5].v, c), pair16(v[i][6].v, v[i][7].v, c));
+              else
+                *reinterpret_cast<uint2*>(d) = make_uint2(pair16(v[i][0].v, v[i][1].v, c), pair16(v[i][2].v, v[i][3].v, c));
+            }
+            continue;
+          }
+        }
+        float sc[RB];
+#pragma unroll
+        for (int e = 0; e < RB; ++e) sc[e] = (row_scale && r0 + e < nrows) ? row_scale[r0 + e] : 1.f;
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
-          float f[8];
+          float f[RB];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) f[e] = v[i][e].get(c) * sc[e];
-          st8(dst + (c0 + c) * ld_dst + r0, f);
+          for (int e = 0; e < RB; ++e) f[e] = v[i][e].get(c) * sc[e];
+          TD* d = dst + (c0 + c) * ld_dst + r0;
+          if constexpr (RB == 8) {
+            st8(d, f);
+          } else if constexpr (sizeof(TD) == 2) {
+            *reinterpret_cast<uint2*>(d) = make_uint2(pack_bf16(f[0], f[1]), pack_bf16(f[2], f[3]));
+          } else {
+            *reinterpret_cast<float4*>(d) = make_float4(f[0], f[1], f[2], f[3]);
+          }
         }
       }
     }
@@ -354,17 +404,32 @@ struct TransTile {
     for (int i = 0; i < PER; ++i) {
       const int it = threadIdx.x + i * NTHREADS;
       if (it < ITEMS) {
-        const int c0 = (it % (COLS / 8)) * 8, r0 = (it / (COLS / 8)) * 8;
+        const int c0 = (it % (COLS / 8)) * 8, r0 = (it / (COLS / 8)) * RB;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          float f[8];
+        for (int e = 0; e < RB; ++e) {
+          if constexpr (sizeof(TS) == 2 && sizeof(TD) == 2) {
+            *reinterpret_cast<uint4*>(dst + (r0 + e) * ld_dst + c0) = v[i][e].v;
+          } else {
+            float f[8];
 #pragma unroll
-          for (int c = 0; c < 8; ++c) f[c] = v[i][e].get(c);
-          st8(dst + (r0 + e) * ld_dst + c0, f);
+            for (int c = 0; c < 8; ++c) f[c] = v[i][e].get(c);
+            st8(dst + (r0 + e) * ld_dst + c0, f);
+          }
         }
       }
     }
   }
 };
+
+// Workgroups are handed to the 8 XCDs of the chip round-robin in launch order,
+// so consecutive block indices land on different XCDs (different L2 caches).
+// This maps the launch index to a logical index such that consecutive logical
+// indices run on one XCD: workgroups that share operands then share its L2.
+constexpr int NXCD = 8;
+__device__ __forceinline__ int xcd_logical_block(int bid, int nblk) {
+  const int per = nblk / NXCD, rem = nblk % NXCD;
+  const int xcd = bid % NXCD, slot = bid / NXCD;
+  return (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + slot;
+}
 
 }  // namespace ssd

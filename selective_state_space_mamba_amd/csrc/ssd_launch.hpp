@@ -27,11 +27,12 @@ hipError_t launch_chunk_state_fwd(const Dims& d, DType act, const void* x, const
                                   float* states, float* final_state, hipStream_t st);
 
 // Reverse state-gradient pass: gamma[b,c,h] = gradient reaching the state that
-// leaves chunk c; dinit = gradient of the initial state (nullable);
+// leaves chunk c, stored in the MFMA operand type (bf16 when act is BF16, else
+// f32); dinit = gradient of the initial state (nullable);
 // gh_part[b,c,h,pb] = partial <gamma[b,c,h], states[b,c,h]> over headdim block pb.
 hipError_t launch_chunk_state_bwd(const Dims& d, DType act, DType dyt, const void* dy,
                                   const void* C, const void* dt, const float* A_log,
-                                  const float* states, float* gamma, float* dinit, float* gh_part,
+                                  const float* states, void* gamma, float* dinit, float* gh_part,
                                   hipStream_t st);
 
 hipError_t launch_chunk_out_fwd(const Dims& d, DType act, int nsplit, const void* x, const void* B,
@@ -53,7 +54,7 @@ struct BwdScratch {
 
 hipError_t launch_chunk_bwd_col(const Dims& d, DType act, DType dyt, int nsplit, const void* x,
                                 const void* B, const void* C, const void* dt, const void* dy,
-                                const float* A_log, const float* D, const float* gamma, float* dx,
+                                const float* A_log, const float* D, const void* gamma, float* dx,
                                 float* dB_out, const BwdScratch& s, hipStream_t st);
 
 hipError_t launch_chunk_bwd_row(const Dims& d, DType act, DType dyt, int nsplit, const void* x,

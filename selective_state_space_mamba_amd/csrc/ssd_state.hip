@@ -22,6 +22,8 @@
 // LDS in 64-step slabs.  Rows of the state are independent, so the headdim
 // split needs no communication.  All decay factors are exp of non-positive
 // numbers (dt > 0, A < 0).
+#include <type_traits>
+
 #include "ssd_common.hpp"
 #include "ssd_launch.hpp"
 
@@ -38,12 +40,16 @@ __global__ __launch_bounds__(NTHREADS, 2) void chunk_state_kernel(
     const TDT* __restrict__ dt,        // [b,T,H]
     const float* __restrict__ A_log,   // [H]
     const float* __restrict__ init,    // fwd: initial state (nullable); bwd: unused
-    float* __restrict__ states_out,    // fwd: H_c; bwd: Gamma_{c+1}    [b,nc,H,P,N]
+    void* __restrict__ states_out_v,   // fwd: H_c (f32); bwd: Gamma_{c+1} (operand type) [b,nc,H,P,N]
     float* __restrict__ last_out,      // fwd: final state; bwd: d(initial state) (nullable)
     const float* __restrict__ hstates, // bwd: H_c, for <Gamma_{c+1}, H_c>
     float* __restrict__ gh_part,       // bwd: [b,nc,H,npb]
     int T, int H, int P, int N, int G, int Q) {
   typedef typename Op<BF>::T OT;
+  // The forward writes the f32 chunk states; the backward writes Gamma in the
+  // operand type of the kernels that read it (its only use is as an MFMA operand).
+  typedef typename std::conditional<REV, OT, float>::type TSO;
+  TSO* const states_out = static_cast<TSO*>(states_out_v);
   constexpr int PB = STATE_PB;
   constexpr int SJ = StateSlab<BF>::SJ;
   constexpr int LDX = SJ + (BF ? 8 : 4);  // [p][j] and [n][j]: time contiguous
@@ -120,7 +126,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void chunk_state_kernel(
       for (int i = 0; i < 4; ++i) {
         const int p = p0 + 4 * q + i, n = 32 * w + 16 * t + r;
         if (p < P && n < N) {
-          if (states_out) states_out[sbase + p * N + n] = st[t][i];
+          if (states_out) store_f(states_out, sbase + p * N + n, st[t][i]);
           if (REV) gh += st[t][i] * hstates[sbase + p * N + n];
         }
         st[t][i] = decay * st[t][i] + acc[t][i];
@@ -147,7 +153,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void chunk_state_kernel(
 
 template <typename TX, typename TB, bool BF, bool REV>
 static hipError_t launch_state(const Dims& d, const void* X, const void* Bm, const void* dt,
-                               const float* A_log, const float* init, float* states, float* last,
+                               const float* A_log, const float* init, void* states, float* last,
                                const float* hstates, float* gh_part, hipStream_t st) {
   dim3 grid(state_npb(d), d.H, d.b);
   hipLaunchKernelGGL((chunk_state_kernel<TX, TB, TB, BF, REV>), grid, dim3(NTHREADS), 0, st,
@@ -168,7 +174,7 @@ hipError_t launch_chunk_state_fwd(const Dims& d, DType act, const void* x, const
 
 hipError_t launch_chunk_state_bwd(const Dims& d, DType act, DType dyt, const void* dy,
                                   const void* C, const void* dt, const float* A_log,
-                                  const float* states, float* gamma, float* dinit, float* gh_part,
+                                  const float* states, void* gamma, float* dinit, float* gh_part,
                                   hipStream_t st) {
   if (act == BF16) {
     if (dyt == BF16)
