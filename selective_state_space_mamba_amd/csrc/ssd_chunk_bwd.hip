@@ -46,16 +46,22 @@ __device__ __forceinline__ float block_sum(float v, float* tmp) {
   return tmp[0] + tmp[1] + tmp[2] + tmp[3];
 }
 
-// Chunk rows (or columns) staged per slab: the whole chunk for bf16 operands,
-// 64 at a time for f32.
-template <bool BF> struct BwdSlab { static constexpr int W = BF ? QMAX : BQ; };
+// Chunk rows (or columns) staged per slab: 128 at a time for bf16 operands, 64
+// for f32.
+template <bool BF> struct BwdSlab { static constexpr int W = BF ? 2 * BQ : BQ; };
 
 constexpr int cmax(int a, int b) { return a > b ? a : b; }
 
 // ------------------------------------------------------------ column kernel
+//
+// 8 waves; wave w = (rw, cw) with rw = w % 4, cw = w / 4 owns rows 16*rw..+15
+// and columns 32*cw..+31 of every 64 x 64 tile it computes (two 16-wide MFMA
+// tiles), so two waves share each SIMD.
+
+constexpr int NT8 = 512;
 
 template <typename TI, typename TY, bool BF>
-__global__ __launch_bounds__(NTHREADS) void chunk_bwd_col_kernel(
+__global__ __launch_bounds__(NT8) void chunk_bwd_col_kernel(
     const TI* __restrict__ x, const TI* __restrict__ Bm, const TI* __restrict__ Cm,
     const TI* __restrict__ dt, const TY* __restrict__ dy, const float* __restrict__ A_log,
     const float* __restrict__ D, const typename Op<BF>::T* __restrict__ gamma, float* __restrict__ dx,
@@ -75,8 +81,15 @@ __global__ __launch_bounds__(NTHREADS) void chunk_bwd_col_kernel(
   __shared__ __attribute__((aligned(16))) OT sR[RSZ];
   __shared__ float sS[QMAX];
   __shared__ float sDt[QMAX];
-  __shared__ float sTmp[8];
+  __shared__ float sTmp[16];
   __shared__ float sRed[4][BQ][2];
+  __shared__ float sRp[2][BQ];
+  // bf16 mode keeps the sum over heads of L yx dt for every tile in LDS (f32,
+  // each lane owning the 8 values of its two 16x16 fragments, so no two lanes
+  // touch a slot) to stay within two waves' registers; f32 mode keeps it in
+  // registers (its tiles leave no LDS for it).
+  __shared__ __attribute__((aligned(16))) float sWs[BF ? NBMAX * NT8 * 8 : 4];
+  f4 wsr[NBMAX][2];
   OT* const sDy = sR;
   OT* const sDyT = sR + IW * LDP;
   OT* const sGt = sR + IW * LDP + (BF ? PMAX * LDI : 0);
@@ -98,6 +111,7 @@ __global__ __launch_bounds__(NTHREADS) void chunk_bwd_col_kernel(
   const int bi = idx / nc;
 
   const int tid = threadIdx.x, w = wave_id(), l = lane_id(), r = l & 15, q = l >> 4;
+  const int rw = w & 3, cw = w >> 2;
   const int64_t row0 = static_cast<int64_t>(bi) * T + static_cast<int64_t>(c) * Q;
   const int j0 = jb * BQ, vj = min(BQ, Q - j0);
   const int i_lo = j0;                          // rows i >= j0 feed this column block
@@ -107,16 +121,17 @@ __global__ __launch_bounds__(NTHREADS) void chunk_bwd_col_kernel(
   const int64_t PN = static_cast<int64_t>(P) * N;
 
   {
-    RowTile<TI, BQ, NMAX> tb;
+    RowTile<TI, BQ, NMAX, NT8> tb;
     tb.load(Bm + (row0 + j0) * GN + static_cast<int64_t>(g) * N, GN, vj, N);
     tb.store(sB, LDN);
   }
-  f4 cb[NBMAX][4];
+  // C.B^T tiles (ib, jb): rows i (this wave's 16), columns j (this wave's 32)
+  f4 cb[NBMAX][2];
 #pragma unroll
   for (int ib = 0; ib < NBMAX; ++ib) zero(cb[ib]);
   for (int sl = 0; sl < nsl; ++sl) {
     const int s0 = i_lo + sl * IW;
-    RowTile<TI, IW, NMAX> tc;
+    RowTile<TI, IW, NMAX, NT8> tc;
     tc.load(Cm + (row0 + s0) * GN + static_cast<int64_t>(g) * N, GN, min(IW, Q - s0), N);
     __syncthreads();
     tc.store(sR, LDN);
@@ -125,20 +140,25 @@ __global__ __launch_bounds__(NTHREADS) void chunk_bwd_col_kernel(
     for (int ib = 0; ib < NBMAX; ++ib) {
       const int il = ib * BQ - s0;
       if (ib >= jb && ib < nb && il >= 0 && il < IW)
-        wave_gemm<BF, true, true, 4>(cb[ib], sR + (il + 16 * w) * LDN, LDN, 1, sB, LDN, 1, Kn);
+        wave_gemm<BF, true, true, 2>(cb[ib], sR + (il + 16 * rw) * LDN, LDN, 1, sB + 32 * cw * LDN, LDN, 1, Kn);
     }
   }
-  f4 ws[NBMAX][4];
 #pragma unroll
-  for (int ib = 0; ib < NBMAX; ++ib) zero(ws[ib]);
-  f4 dbs[8];
+  for (int ib = 0; ib < NBMAX; ++ib) {
+    zero(wsr[ib]);
+    if constexpr (BF) {
+      float4* wsp = reinterpret_cast<float4*>(sWs + (ib * NT8 + tid) * 8);
+      wsp[0] = make_float4(0.f, 0.f, 0.f, 0.f);
+      wsp[1] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  }
+  f4 dbs[4];        // dB rows j (16 rw), columns n 64*cw..+63
   zero(dbs);
 
-  RowTile<TI, BQ, PMAX> tX;          // x_jb
   // bf16 operands need dy and Gamma also transposed; f32 operands read the
   // transposed views with strided fetches, so rows suffice.
-  typename std::conditional<BF, TransTile<TY, IW, PMAX>, RowTile<TY, IW, PMAX>>::type tDy;  // dy rows of a slab
-  typename std::conditional<BF, TransTile<OT, PMAX, NMAX>, RowTile<OT, PMAX, NMAX>>::type tG;  // Gamma_{c+1}
+  RowTile<TI, BQ, PMAX, NT8> tX;
+  typename std::conditional<BF, TransTile<TY, IW, PMAX, 4, NT8>, RowTile<TY, IW, PMAX, NT8>>::type tDy;
   float dt_next = 0.f;
   auto load_head = [&](int hh) {
     const int h = g * hpg + sp * hps + hh;
@@ -160,23 +180,10 @@ __global__ __launch_bounds__(NTHREADS) void chunk_bwd_col_kernel(
       sDt[tid] = dtv;
     }
     tX.store(sX, LDP);
-    // skip term D dy_j of this wave's output rows, loaded now, used at the end
-    float dsk[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int jq = j0 + 16 * w + 4 * q + i;
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int p = 16 * t + r;
-        dsk[i][t] = (jq < Q && p < P) ? load_f(dy, (row0 + jq) * HP + static_cast<int64_t>(h) * P + p) : 0.f;
-      }
-    }
-
-    f4 dxa[4];
+    f4 dxa[2];
     zero(dxa);
-    float csum[4] = {0.f, 0.f, 0.f, 0.f}, dsum[4] = {0.f, 0.f, 0.f, 0.f};
-    bool sj_loaded = false;
-    float sj[4], dtj4[4];
+    float csum[2] = {0.f, 0.f}, dsum[2] = {0.f, 0.f};
+    float sj[2], dtj2[2];
     for (int sl = 0; sl < nsl; ++sl) {
       const int s0 = i_lo + sl * IW;
       if (sl > 0) __syncthreads();
@@ -184,44 +191,52 @@ __global__ __launch_bounds__(NTHREADS) void chunk_bwd_col_kernel(
       if constexpr (BF) tDy.store(sDyT, LDI);
       if (sl + 1 < nsl)
         tDy.load(dy + (row0 + s0 + IW) * HP + static_cast<int64_t>(h) * P, HP, min(IW, Q - s0 - IW), P);
-      else
-        tG.load(gamma + ((static_cast<int64_t>(bi) * nc + c) * H + h) * PN, N, P, N);
       __syncthreads();
+      if (sl == 0) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const int jq = min(j0 + 32 * cw + 16 * t + r, Q - 1);
+          sj[t] = sS[jq];
+          dtj2[t] = sDt[jq];
+        }
+      }
 #pragma unroll
       for (int ib = 0; ib < NBMAX; ++ib) {
         const int il = ib * BQ - s0;
         if (ib >= jb && ib < nb && il >= 0 && il < IW) {
-          f4 yx[4];
+          f4 yx[2];
           zero(yx);
-          wave_gemm<BF, true, true, 4>(yx, sDy + (il + 16 * w) * LDP, LDP, 1, sX, LDP, 1, Kp);
-          if (!sj_loaded) {
+          wave_gemm<BF, true, true, 2>(yx, sDy + (il + 16 * rw) * LDP, LDP, 1, sX + 32 * cw * LDP, LDP, 1, Kp);
+          float4* wsp = reinterpret_cast<float4*>(sWs + (ib * NT8 + tid) * 8);
+          f4 ws[2];
 #pragma unroll
-            for (int ct = 0; ct < 4; ++ct) {
-              const int jq = min(j0 + 16 * ct + r, Q - 1);
-              sj[ct] = sS[jq];
-              dtj4[ct] = sDt[jq];
+          for (int t = 0; t < 2; ++t) {
+            if constexpr (BF) {
+              const float4 v4 = wsp[t];
+              ws[t] = f4{v4.x, v4.y, v4.z, v4.w};
+            } else {
+              ws[t] = wsr[ib][t];
             }
-            sj_loaded = true;
           }
-          const int ir0 = il + 16 * w + 4 * q;  // the lane's four rows inside the slab
+          const int ir0 = il + 16 * rw + 4 * q;  // the lane's four rows inside the slab
           float si[4];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) si[i] = sS[min(s0 + ir0 + i, Q - 1)];
+          for (int e = 0; e < 4; ++e) si[e] = sS[min(s0 + ir0 + e, Q - 1)];
 #pragma unroll
-          for (int ct = 0; ct < 4; ++ct) {
-            const int jl = 16 * ct + r, jq = j0 + jl;
+          for (int t = 0; t < 2; ++t) {
+            const int jl = 32 * cw + 16 * t + r, jq = j0 + jl;
             float g4[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int iq = s0 + ir0 + i;
+            for (int e = 0; e < 4; ++e) {
+              const int iq = s0 + ir0 + e;
               const bool valid = iq < Q && jq <= iq;
-              const float Lv = valid ? __expf(si[i] - sj[ct]) : 0.f;
-              const float g1 = Lv * cb[ib][ct][i];
-              const float e = g1 * yx[ct][i];
-              csum[ct] += e;
-              if (iq == jq) dsum[ct] += e;
-              ws[ib][ct][i] += Lv * yx[ct][i] * dtj4[ct];
-              g4[i] = g1;
+              const float Lv = valid ? __expf(si[e] - sj[t]) : 0.f;
+              const float g1 = Lv * cb[ib][t][e];
+              const float E = g1 * yx[t][e];
+              csum[t] += E;
+              if (iq == jq) dsum[t] += E;
+              ws[t][e] += Lv * yx[t][e] * dtj2[t];
+              g4[e] = g1;
             }
             OT* gp = sGt + jl * LDI + ir0;
             if constexpr (BF)
@@ -229,68 +244,96 @@ __global__ __launch_bounds__(NTHREADS) void chunk_bwd_col_kernel(
             else
               *reinterpret_cast<float4*>(gp) = make_float4(g4[0], g4[1], g4[2], g4[3]);
           }
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            if constexpr (BF)
+              wsp[t] = make_float4(ws[t][0], ws[t][1], ws[t][2], ws[t][3]);
+            else
+              wsr[ib][t] = ws[t];
+          }
         }
       }
       __syncthreads();
       const int kw = round_up(min(IW, Q - s0), Op<BF>::KS);
       if constexpr (BF)
-        wave_gemm<BF, true, true, 4>(dxa, sGt + 16 * w * LDI, LDI, 1, sDyT, LDI, 1, kw);
+        wave_gemm<BF, true, true, 2>(dxa, sGt + 16 * rw * LDI, LDI, 1, sDyT + 32 * cw * LDI, LDI, 1, kw);
       else
-        wave_gemm<BF, true, false, 4>(dxa, sGt + 16 * w * LDI, LDI, 1, sDy, 1, LDP, kw);
+        wave_gemm<BF, true, false, 2>(dxa, sGt + 16 * rw * LDI, LDI, 1, sDy + 32 * cw, 1, LDP, kw);
     }
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {
-      const float cs = sum_q(csum[ct]), ds = sum_q(dsum[ct]);
+    for (int t = 0; t < 2; ++t) {
+      const float cs = sum_q(csum[t]), ds = sum_q(dsum[t]);
       if (q == 0) {
-        sRed[w][16 * ct + r][0] = cs;
-        sRed[w][16 * ct + r][1] = ds;
+        sRed[rw][32 * cw + 16 * t + r][0] = cs;
+        sRed[rw][32 * cw + 16 * t + r][1] = ds;
       }
     }
 
     // state terms with Gamma_{c+1}
-    __syncthreads();
-    tG.store_rows(sGam, LDN);
-    if constexpr (BF) tG.store(sGamT, LDP);
+    {
+      typename std::conditional<BF, TransTile<OT, PMAX, NMAX, 4, NT8>, RowTile<OT, PMAX, NMAX, NT8>>::type tG;
+      tG.load(gamma + ((static_cast<int64_t>(bi) * nc + c) * H + h) * PN, N, P, N);
+      __syncthreads();
+      tG.store_rows(sGam, LDN);
+      if constexpr (BF) tG.store(sGamT, LDP);
+    }
     if (hh + 1 < hps) load_head(hh + 1);
     __syncthreads();
+    // skip term D dy_j (loaded here, while the MFMAs below run) for this wave's output rows j, columns p
+    float dsk[4][2];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int jq = j0 + 16 * rw + 4 * q + e;
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int p = 32 * cw + 16 * t + r;
+        dsk[e][t] = (jq < Q && p < P) ? load_f(dy, (row0 + jq) * HP + static_cast<int64_t>(h) * P + p) : 0.f;
+      }
+    }
+
     if (tid < BQ && j0 + tid < Q) {
       const int64_t o = (static_cast<int64_t>(bi) * H + h) * T + static_cast<int64_t>(c) * Q + j0 + tid;
       colE[o] = sRed[0][tid][0] + sRed[1][tid][0] + sRed[2][tid][0] + sRed[3][tid][0];
       diagE[o] = sRed[0][tid][1] + sRed[1][tid][1] + sRed[2][tid][1] + sRed[3][tid][1];
     }
-    f4 bg[4];
+    // bg = B Gamma^T (rows j, columns p), v = x Gamma (rows j, columns n)
+    f4 bg[2];
     zero(bg);
-    wave_gemm<BF, true, true, 4>(bg, sB + 16 * w * LDN, LDN, 1, sGam, LDN, 1, Kn);
-    f4 v[8];
+    wave_gemm<BF, true, true, 2>(bg, sB + 16 * rw * LDN, LDN, 1, sGam + 32 * cw * LDN, LDN, 1, Kn);
+    f4 v[4];
     zero(v);
     if constexpr (BF)
-      wave_gemm<BF, true, true, 8>(v, sX + 16 * w * LDP, LDP, 1, sGamT, LDP, 1, Kp);
+      wave_gemm<BF, true, true, 4>(v, sX + 16 * rw * LDP, LDP, 1, sGamT + 64 * cw * LDP, LDP, 1, Kp);
     else
-      wave_gemm<BF, true, false, 8>(v, sX + 16 * w * LDP, LDP, 1, sGam, 1, LDN, Kp);
+      wave_gemm<BF, true, false, 4>(v, sX + 16 * rw * LDP, LDP, 1, sGam + 64 * cw, 1, LDN, Kp);
     const float s_end = sS[Q - 1];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int jl = 16 * w + 4 * q + i, jq = j0 + jl;
+    for (int e = 0; e < 4; ++e) {
+      const int jl = 16 * rw + 4 * q + e, jq = j0 + jl;
       const bool valid = jq < Q;
       const float wj = valid ? __expf(s_end - sS[jq]) : 0.f;
       const float dtj = valid ? sDt[jq] : 0.f;
+      // R'_j / w_j = x_j . (B_j Gamma^T): partial over this wave's columns p
       float part = 0.f;
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        part += v[t][i] * Op<BF>::back(sB[jl * LDN + 16 * t + r]);
-        dbs[t][i] += dtj * wj * v[t][i];
-      }
+      for (int t = 0; t < 2; ++t) part += bg[t][e] * Op<BF>::back(sX[jl * LDP + 32 * cw + 16 * t + r]);
       part = sum16(part);
-      if (valid && r == 0) Rp[(static_cast<int64_t>(bi) * H + h) * T + static_cast<int64_t>(c) * Q + jq] = wj * part;
+      if (r == 0) sRp[cw][jl] = part;
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int p = 16 * t + r;
+      for (int t = 0; t < 4; ++t) dbs[t][e] += dtj * wj * v[t][e];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int p = 32 * cw + 16 * t + r;
         if (valid && p < P) {
           const int64_t o = (row0 + jq) * HP + static_cast<int64_t>(h) * P + p;
-          dx[o] = dtj * (dxa[t][i] + wj * bg[t][i]) + Dh * dsk[i][t];
+          dx[o] = dtj * (dxa[t][e] + wj * bg[t][e]) + Dh * dsk[e][t];
         }
       }
     }
+    __syncthreads();
+    if (tid < BQ && j0 + tid < Q)
+      Rp[(static_cast<int64_t>(bi) * H + h) * T + static_cast<int64_t>(c) * Q + j0 + tid] =
+          __expf(s_end - sS[j0 + tid]) * (sRp[0][tid] + sRp[1][tid]);
   }
 
   // dB_j += sum_i W^T[j][i] C_i with W = sum over heads of L yx dt
@@ -301,50 +344,61 @@ __global__ __launch_bounds__(NTHREADS) void chunk_bwd_col_kernel(
     for (int ib = 0; ib < NBMAX; ++ib) {
       const int il = ib * BQ - s0;
       if (ib >= jb && ib < nb && il >= 0 && il < IW) {
+        const float4* wsp = reinterpret_cast<const float4*>(sWs + (ib * NT8 + tid) * 8);
 #pragma unroll
-        for (int ct = 0; ct < 4; ++ct) {
-          OT* wp = sWt + (16 * ct + r) * LDI + il + 16 * w + 4 * q;
+        for (int t = 0; t < 2; ++t) {
+          float4 v4;
           if constexpr (BF)
-            *reinterpret_cast<uint2*>(wp) = make_uint2(pack_bf16(ws[ib][ct][0], ws[ib][ct][1]),
-                                                        pack_bf16(ws[ib][ct][2], ws[ib][ct][3]));
+            v4 = wsp[t];
           else
-            *reinterpret_cast<float4*>(wp) = make_float4(ws[ib][ct][0], ws[ib][ct][1], ws[ib][ct][2], ws[ib][ct][3]);
+            v4 = make_float4(wsr[ib][t][0], wsr[ib][t][1], wsr[ib][t][2], wsr[ib][t][3]);
+          OT* wp = sWt + (32 * cw + 16 * t + r) * LDI + il + 16 * rw + 4 * q;
+          if constexpr (BF)
+            *reinterpret_cast<uint2*>(wp) = make_uint2(pack_bf16(v4.x, v4.y), pack_bf16(v4.z, v4.w));
+          else
+            *reinterpret_cast<float4*>(wp) = v4;
         }
       }
     }
     const int vi = min(IW, Q - s0);
     const TI* csrc = Cm + (row0 + s0) * GN + static_cast<int64_t>(g) * N;
     if constexpr (BF) {
-      TransTile<TI, IW, NMAX> tc;
+      TransTile<TI, IW, NMAX, 4, NT8> tc;
       tc.load(csrc, GN, vi, N);
       tc.store(sCf, LDI);
     } else {
-      RowTile<TI, IW, NMAX> tc;
+      RowTile<TI, IW, NMAX, NT8> tc;
       tc.load(csrc, GN, vi, N);
       tc.store(sCf, LDN);
     }
     __syncthreads();
     const int kw = round_up(vi, Op<BF>::KS);
     if constexpr (BF)
-      wave_gemm<BF, true, true, 8>(dbs, sWt + 16 * w * LDI, LDI, 1, sCf, LDI, 1, kw);
+      wave_gemm<BF, true, true, 4>(dbs, sWt + 16 * rw * LDI, LDI, 1, sCf + 64 * cw * LDI, LDI, 1, kw);
     else
-      wave_gemm<BF, true, false, 8>(dbs, sWt + 16 * w * LDI, LDI, 1, sCf, 1, LDN, kw);
+      wave_gemm<BF, true, false, 4>(dbs, sWt + 16 * rw * LDI, LDI, 1, sCf + 64 * cw, 1, LDN, kw);
   }
   const int64_t batch = gridDim.x / (nb * nsplit * G * nc);
   float* dBo = dB_out + static_cast<int64_t>(sp) * batch * T * GN;
 #pragma unroll
-  for (int t = 0; t < 8; ++t)
+  for (int t = 0; t < 4; ++t)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int jq = j0 + 16 * w + 4 * q + i, n = 16 * t + r;
-      if (jq < Q && n < N) dBo[(row0 + jq) * GN + static_cast<int64_t>(g) * N + n] = dbs[t][i];
+    for (int e = 0; e < 4; ++e) {
+      const int jq = j0 + 16 * rw + 4 * q + e, n = 64 * cw + 16 * t + r;
+      if (jq < Q && n < N) dBo[(row0 + jq) * GN + static_cast<int64_t>(g) * N + n] = dbs[t][e];
     }
 }
 
 // --------------------------------------------------------------- row kernel
+//
+// 8 waves.  The causal tiles are computed transposed (rows j, columns i):
+// wave (rw, cw) owns rows j 16*rw..+15 and columns i 32*cw..+31 of each tile,
+// so the head-summed W[i][j] is written to LDS with packed 8-byte stores.  The
+// incoming-state term U = dy H_c (rows i, d_state columns) uses rows i 16*rw,
+// columns n 64*cw..+63, as does dC.
 
 template <typename TI, typename TY, bool BF>
-__global__ __launch_bounds__(NTHREADS) void chunk_bwd_row_kernel(
+__global__ __launch_bounds__(NT8) void chunk_bwd_row_kernel(
     const TI* __restrict__ x, const TI* __restrict__ Bm, const TI* __restrict__ Cm,
     const TI* __restrict__ dt, const TY* __restrict__ dy, const float* __restrict__ A_log,
     const float* __restrict__ hstates, float* __restrict__ dC_out, float* __restrict__ rowM,
@@ -363,7 +417,12 @@ __global__ __launch_bounds__(NTHREADS) void chunk_bwd_row_kernel(
   __shared__ __attribute__((aligned(16))) OT sR[RSZ];
   __shared__ float sS[QMAX];
   __shared__ float sDt[QMAX];
-  __shared__ float sTmp[8];
+  __shared__ float sTmp[16];
+  __shared__ float sRow[4][BQ];  // row sums of M by row group of j
+  __shared__ float sDso[2][BQ];  // U_i . C_i by column half of n
+  // bf16 mode keeps the head sum of L yx dt in LDS (each lane owns its slots);
+  // f32 mode in registers.
+  __shared__ __attribute__((aligned(16))) float sWs[BF ? NBMAX * NT8 * 8 : 4];
   OT* const sH = sR;
   OT* const sXr = sR + (BF ? NMAX * LDP : PMAX * LDN);
   OT* const sW = sR;
@@ -382,6 +441,7 @@ __global__ __launch_bounds__(NTHREADS) void chunk_bwd_row_kernel(
   const int bi = idx / nc;
 
   const int tid = threadIdx.x, w = wave_id(), l = lane_id(), r = l & 15, q = l >> 4;
+  const int rw = w & 3, cw = w >> 2;
   const int64_t row0 = static_cast<int64_t>(bi) * T + static_cast<int64_t>(c) * Q;
   const int i0 = ib * BQ, vi = min(BQ, Q - i0);
   const int jend = min(Q, i0 + BQ);
@@ -391,16 +451,17 @@ __global__ __launch_bounds__(NTHREADS) void chunk_bwd_row_kernel(
   const int64_t PN = static_cast<int64_t>(P) * N;
 
   {
-    RowTile<TI, BQ, NMAX> tc;
+    RowTile<TI, BQ, NMAX, NT8> tc;
     tc.load(Cm + (row0 + i0) * GN + static_cast<int64_t>(g) * N, GN, vi, N);
     tc.store(sC, LDN);
   }
-  f4 cb[NBMAX][4];
+  // (C.B^T)^T tiles (jb, ib): rows j (this wave's 16), columns i (this wave's 32)
+  f4 cb[NBMAX][2];
 #pragma unroll
   for (int jb = 0; jb < NBMAX; ++jb) zero(cb[jb]);
   for (int sl = 0; sl < nsl; ++sl) {
     const int s0 = sl * JW;
-    RowTile<TI, JW, NMAX> tb;
+    RowTile<TI, JW, NMAX, NT8> tb;
     tb.load(Bm + (row0 + s0) * GN + static_cast<int64_t>(g) * N, GN, min(JW, jend - s0), N);
     __syncthreads();
     tb.store(sR, LDN);
@@ -409,23 +470,28 @@ __global__ __launch_bounds__(NTHREADS) void chunk_bwd_row_kernel(
     for (int jb = 0; jb < NBMAX; ++jb) {
       const int jl = jb * BQ - s0;
       if (jb <= ib && jl >= 0 && jl < JW)
-        wave_gemm<BF, true, true, 4>(cb[jb], sC + 16 * w * LDN, LDN, 1, sR + jl * LDN, LDN, 1, Kn);
+        wave_gemm<BF, true, true, 2>(cb[jb], sR + (jl + 16 * rw) * LDN, LDN, 1, sC + 32 * cw * LDN, LDN, 1, Kn);
     }
   }
-  f4 ws[NBMAX][4];
+  f4 wsr[NBMAX][2];  // sum over heads of L yx dt, transposed like cb (f32 mode)
 #pragma unroll
-  for (int jb = 0; jb < NBMAX; ++jb) zero(ws[jb]);
-  f4 dca[8];
+  for (int jb = 0; jb < NBMAX; ++jb) {
+    zero(wsr[jb]);
+    if constexpr (BF) {
+      float4* wsp = reinterpret_cast<float4*>(sWs + (jb * NT8 + tid) * 8);
+      wsp[0] = make_float4(0.f, 0.f, 0.f, 0.f);
+      wsp[1] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  }
+  f4 dca[4];        // dC rows i (16 rw), columns n 64*cw..+63
   zero(dca);
 
-  RowTile<TY, BQ, PMAX> tDy;        // dy_ib
-  TransTile<float, PMAX, NMAX, 4> tH;  // H_c rows p, columns n
-  RowTile<TI, JW, PMAX> tXs;        // x rows of one slab
+  RowTile<TY, BQ, PMAX, NT8> tDy;  // dy_ib
+  RowTile<TI, JW, PMAX, NT8> tXs;  // x rows of one slab
   float dt_next = 0.f;
   auto load_head = [&](int hh) {
     const int h = g * hpg + sp * hps + hh;
     tDy.load(dy + (row0 + i0) * HP + static_cast<int64_t>(h) * P, HP, vi, P);
-    tH.load(hstates + ((static_cast<int64_t>(bi) * nc + c) * H + h) * PN, N, P, N);
     tXs.load(x + row0 * HP + static_cast<int64_t>(h) * P, HP, min(JW, jend), P);
     dt_next = (tid < Q) ? load_f(dt, (row0 + tid) * H + h) : 0.f;
   };
@@ -442,34 +508,40 @@ __global__ __launch_bounds__(NTHREADS) void chunk_bwd_row_kernel(
       sDt[tid] = dtv;
     }
     tDy.store(sDy, LDP);
-    if constexpr (BF)
-      tH.store(sH, LDP);
-    else
-      tH.store_rows(sH, LDN);
+    {
+      typename std::conditional<BF, TransTile<float, PMAX, NMAX, 4, NT8>, RowTile<float, PMAX, NMAX, NT8>>::type tH;
+      tH.load(hstates + ((static_cast<int64_t>(bi) * nc + c) * H + h) * PN, N, P, N);
+      if constexpr (BF)
+        tH.store(sH, LDP);
+      else
+        tH.store_rows(sH, LDN);
+    }
     __syncthreads();
 
-    // U_i = dy_i H_c (rows i, d_state columns)
-    f4 u[8];
-    zero(u);
-    if constexpr (BF)
-      wave_gemm<BF, true, true, 8>(u, sDy + 16 * w * LDP, LDP, 1, sH, LDP, 1, Kp);
-    else
-      wave_gemm<BF, true, false, 8>(u, sDy + 16 * w * LDP, LDP, 1, sH, 1, LDN, Kp);
+    // U_i = dy_i H_c: rows i (16 rw), columns n (64 cw)
+    {
+      f4 u[4];
+      zero(u);
+      if constexpr (BF)
+        wave_gemm<BF, true, true, 4>(u, sDy + 16 * rw * LDP, LDP, 1, sH + 64 * cw * LDP, LDP, 1, Kp);
+      else
+        wave_gemm<BF, true, false, 4>(u, sDy + 16 * rw * LDP, LDP, 1, sH + 64 * cw, 1, LDN, Kp);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int il = 16 * w + 4 * q + i, iq = i0 + il;
-      const float e = (iq < Q) ? __expf(sS[iq]) : 0.f;
-      float part = 0.f;
+      for (int e = 0; e < 4; ++e) {
+        const int il = 16 * rw + 4 * q + e, iq = i0 + il;
+        const float ex = (iq < Q) ? __expf(sS[iq]) : 0.f;
+        float part = 0.f;
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        part += u[t][i] * Op<BF>::back(sC[il * LDN + 16 * t + r]);
-        dca[t][i] += e * u[t][i];
+        for (int t = 0; t < 4; ++t) {
+          part += u[t][e] * Op<BF>::back(sC[il * LDN + 64 * cw + 16 * t + r]);
+          dca[t][e] += ex * u[t][e];
+        }
+        part = sum16(part);
+        if (r == 0) sDso[cw][il] = part;
       }
-      part = sum16(part);
-      if (iq < Q && r == 0) dsoff[(static_cast<int64_t>(bi) * H + h) * T + static_cast<int64_t>(c) * Q + iq] = e * part;
     }
 
-    float racc[4] = {0.f, 0.f, 0.f, 0.f};
+    float racc[2] = {0.f, 0.f};  // row sums for the lane's columns i
     for (int sl = 0; sl < nsl; ++sl) {
       const int s0 = sl * JW;
       __syncthreads();  // previous slab's reads of sXr done (and U's reads of sH)
@@ -479,52 +551,80 @@ __global__ __launch_bounds__(NTHREADS) void chunk_bwd_row_kernel(
       else if (hh + 1 < hps)
         load_head(hh + 1);
       __syncthreads();
+      float si[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) si[t] = sS[min(i0 + 32 * cw + 16 * t + r, Q - 1)];
 #pragma unroll
       for (int jb = 0; jb < NBMAX; ++jb) {
         const int jl = jb * BQ - s0;
         if (jb <= ib && jl >= 0 && jl < JW) {
-          f4 yx[4];
+          // yx^T = x_j . dy_i: rows j, columns i
+          f4 yx[2];
           zero(yx);
-          wave_gemm<BF, true, true, 4>(yx, sDy + 16 * w * LDP, LDP, 1, sXr + jl * LDP, LDP, 1, Kp);
-          float si[4], sjv[4], dtjv[4];
+          wave_gemm<BF, true, true, 2>(yx, sXr + (jl + 16 * rw) * LDP, LDP, 1, sDy + 32 * cw * LDP, LDP, 1, Kp);
+          float4* wsp = reinterpret_cast<float4*>(sWs + (jb * NT8 + tid) * 8);
+          f4 ws[2];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) si[i] = sS[min(i0 + 16 * w + 4 * q + i, Q - 1)];
+          for (int t = 0; t < 2; ++t) {
+            if constexpr (BF) {
+              const float4 v4 = wsp[t];
+              ws[t] = f4{v4.x, v4.y, v4.z, v4.w};
+            } else {
+              ws[t] = wsr[jb][t];
+            }
+          }
+          float sjv[4], dtjv[4];
 #pragma unroll
-          for (int ct = 0; ct < 4; ++ct) {
-            const int jq = min(jb * BQ + 16 * ct + r, Q - 1);
-            sjv[ct] = sS[jq];
-            dtjv[ct] = sDt[jq];
+          for (int e = 0; e < 4; ++e) {
+            const int jq = min(jb * BQ + 16 * rw + 4 * q + e, Q - 1);
+            sjv[e] = sS[jq];
+            dtjv[e] = sDt[jq];
           }
 #pragma unroll
-          for (int ct = 0; ct < 4; ++ct)
+          for (int t = 0; t < 2; ++t)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int iq = i0 + 16 * w + 4 * q + i, jq = jb * BQ + 16 * ct + r;
+            for (int e = 0; e < 4; ++e) {
+              const int iq = i0 + 32 * cw + 16 * t + r, jq = jb * BQ + 16 * rw + 4 * q + e;
               const bool valid = iq < Q && jq <= iq;
-              const float ly = valid ? __expf(si[i] - sjv[ct]) * yx[ct][i] * dtjv[ct] : 0.f;
-              ws[jb][ct][i] += ly;
-              if (jq < iq) racc[i] += ly * cb[jb][ct][i];
+              const float ly = valid ? __expf(si[t] - sjv[e]) * yx[t][e] * dtjv[e] : 0.f;
+              ws[t][e] += ly;
+              if (jq < iq) racc[t] += ly * cb[jb][t][e];
             }
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            if constexpr (BF)
+              wsp[t] = make_float4(ws[t][0], ws[t][1], ws[t][2], ws[t][3]);
+            else
+              wsr[jb][t] = ws[t];
+          }
         }
       }
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float rr = sum16(racc[i]);
-      const int iq = i0 + 16 * w + 4 * q + i;
-      if (iq < Q && r == 0) rowM[(static_cast<int64_t>(bi) * H + h) * T + static_cast<int64_t>(c) * Q + iq] = rr;
+    for (int t = 0; t < 2; ++t) {
+      const float rr = sum_q(racc[t]);
+      if (q == 0) sRow[rw][32 * cw + 16 * t + r] = rr;
     }
     // dD partial over this block's rows
     float dd = 0.f;
-    for (int e = tid; e < vi * P; e += NTHREADS) {
+    for (int e = tid; e < vi * P; e += NT8) {
       const int il = e / P, p = e % P;
       const int64_t o = (row0 + i0 + il) * HP + static_cast<int64_t>(h) * P + p;
       dd += load_f(dy, o) * load_f(x, o);
     }
     dd = wave_sum(dd);
-    if (l == 0) sTmp[4 + w] = dd;
+    if (l == 0) sTmp[8 + w] = dd;
     __syncthreads();
-    if (tid == 0) dD_part[((static_cast<int64_t>(bi) * nc + c) * nb + ib) * H + h] = sTmp[4] + sTmp[5] + sTmp[6] + sTmp[7];
+    if (tid < BQ && i0 + tid < Q) {
+      const int64_t o = (static_cast<int64_t>(bi) * H + h) * T + static_cast<int64_t>(c) * Q + i0 + tid;
+      rowM[o] = sRow[0][tid] + sRow[1][tid] + sRow[2][tid] + sRow[3][tid];
+      dsoff[o] = __expf(sS[i0 + tid]) * (sDso[0][tid] + sDso[1][tid]);
+    }
+    if (tid == 0) {
+      float tot = 0.f;
+      for (int k = 0; k < NT8 / WAVE; ++k) tot += sTmp[8 + k];
+      dD_part[((static_cast<int64_t>(bi) * nc + c) * nb + ib) * H + h] = tot;
+    }
   }
 
   // dC_i += sum_j W[i][j] B_j with W = sum over heads of L yx dt
@@ -535,39 +635,48 @@ __global__ __launch_bounds__(NTHREADS) void chunk_bwd_row_kernel(
     for (int jb = 0; jb < NBMAX; ++jb) {
       const int jl = jb * BQ - s0;
       if (jb <= ib && jl >= 0 && jl < JW) {
+        const float4* wsp = reinterpret_cast<const float4*>(sWs + (jb * NT8 + tid) * 8);
 #pragma unroll
-        for (int ct = 0; ct < 4; ++ct)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            sW[(16 * w + 4 * q + i) * LDJ + jl + 16 * ct + r] = Op<BF>::cvt(ws[jb][ct][i]);
+        for (int t = 0; t < 2; ++t) {
+          float4 v4;
+          if constexpr (BF)
+            v4 = wsp[t];
+          else
+            v4 = make_float4(wsr[jb][t][0], wsr[jb][t][1], wsr[jb][t][2], wsr[jb][t][3]);
+          OT* wp = sW + (32 * cw + 16 * t + r) * LDJ + jl + 16 * rw + 4 * q;
+          if constexpr (BF)
+            *reinterpret_cast<uint2*>(wp) = make_uint2(pack_bf16(v4.x, v4.y), pack_bf16(v4.z, v4.w));
+          else
+            *reinterpret_cast<float4*>(wp) = v4;
+        }
       }
     }
     const int vj = min(JW, jend - s0);
     const TI* bsrc = Bm + (row0 + s0) * GN + static_cast<int64_t>(g) * N;
     if constexpr (BF) {
-      TransTile<TI, JW, NMAX> tb;
+      TransTile<TI, JW, NMAX, 4, NT8> tb;
       tb.load(bsrc, GN, vj, N);
       tb.store(sBf, LDJ);
     } else {
-      RowTile<TI, JW, NMAX> tb;
+      RowTile<TI, JW, NMAX, NT8> tb;
       tb.load(bsrc, GN, vj, N);
       tb.store(sBf, LDN);
     }
     __syncthreads();
     const int kw = round_up(vj, Op<BF>::KS);
     if constexpr (BF)
-      wave_gemm<BF, true, true, 8>(dca, sW + 16 * w * LDJ, LDJ, 1, sBf, LDJ, 1, kw);
+      wave_gemm<BF, true, true, 4>(dca, sW + 16 * rw * LDJ, LDJ, 1, sBf + 64 * cw * LDJ, LDJ, 1, kw);
     else
-      wave_gemm<BF, true, false, 8>(dca, sW + 16 * w * LDJ, LDJ, 1, sBf, 1, LDN, kw);
+      wave_gemm<BF, true, false, 4>(dca, sW + 16 * rw * LDJ, LDJ, 1, sBf + 64 * cw, 1, LDN, kw);
   }
   const int64_t batch = gridDim.x / (nb * nsplit * G * nc);
   float* dCo = dC_out + static_cast<int64_t>(sp) * batch * T * GN;
 #pragma unroll
-  for (int t = 0; t < 8; ++t)
+  for (int t = 0; t < 4; ++t)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int iq = i0 + 16 * w + 4 * q + i, n = 16 * t + r;
-      if (iq < Q && n < N) dCo[(row0 + iq) * GN + static_cast<int64_t>(g) * N + n] = dca[t][i];
+    for (int e = 0; e < 4; ++e) {
+      const int iq = i0 + 16 * rw + 4 * q + e, n = 64 * cw + 16 * t + r;
+      if (iq < Q && n < N) dCo[(row0 + iq) * GN + static_cast<int64_t>(g) * N + n] = dca[t][e];
     }
 }
 
@@ -661,7 +770,7 @@ template <typename TI, typename TY, bool BF>
 static void col_launch(const Dims& d, int nsplit, const void* x, const void* B, const void* C, const void* dt,
                        const void* dy, const float* A_log, const float* D, const void* gamma, float* dx,
                        float* dB_out, const BwdScratch& s, hipStream_t st) {
-  hipLaunchKernelGGL((chunk_bwd_col_kernel<TI, TY, BF>), dim3(nblocks_chunk(d, nsplit)), dim3(NTHREADS), 0, st,
+  hipLaunchKernelGGL((chunk_bwd_col_kernel<TI, TY, BF>), dim3(nblocks_chunk(d, nsplit)), dim3(NT8), 0, st,
                      static_cast<const TI*>(x), static_cast<const TI*>(B), static_cast<const TI*>(C),
                      static_cast<const TI*>(dt), static_cast<const TY*>(dy), A_log, D,
                      static_cast<const typename Op<BF>::T*>(gamma), dx, dB_out, s.colE,
@@ -690,7 +799,7 @@ template <typename TI, typename TY, bool BF>
 static void row_launch(const Dims& d, int nsplit, const void* x, const void* B, const void* C, const void* dt,
                        const void* dy, const float* A_log, const float* states, float* dC_out, const BwdScratch& s,
                        hipStream_t st) {
-  hipLaunchKernelGGL((chunk_bwd_row_kernel<TI, TY, BF>), dim3(nblocks_chunk(d, nsplit)), dim3(NTHREADS), 0, st,
+  hipLaunchKernelGGL((chunk_bwd_row_kernel<TI, TY, BF>), dim3(nblocks_chunk(d, nsplit)), dim3(NT8), 0, st,
                      static_cast<const TI*>(x), static_cast<const TI*>(B), static_cast<const TI*>(C),
                      static_cast<const TI*>(dt), static_cast<const TY*>(dy), A_log, states, dC_out, s.rowM, s.dsoff,
                      s.dD_part, d.T, d.H, d.P, d.N, d.G, d.Q, nsplit);

@@ -18,6 +18,8 @@
 // Operands are staged with 16-byte loads; the next head's x and H_c are loaded
 // into registers while the current head computes.  bf16 operands stage the
 // whole chunk width at once (one slab); f32 operands go 64 columns at a time.
+// 8 waves: wave (rw, cw) = (w % 4, w / 4) owns rows 16*rw..+15 and columns
+// 32*cw..+31 of every 64 x 64 tile, so two waves share each SIMD.
 #include "ssd_common.hpp"
 #include "ssd_launch.hpp"
 
@@ -25,8 +27,10 @@ namespace ssd {
 
 template <bool BF> struct OutSlab { static constexpr int JW = BF ? QMAX : BQ; };
 
+constexpr int NT8 = 512;
+
 template <typename TI, bool BF>
-__global__ __launch_bounds__(NTHREADS) void chunk_out_fwd_kernel(
+__global__ __launch_bounds__(NT8) void chunk_out_fwd_kernel(
     const TI* __restrict__ x, const TI* __restrict__ Bm, const TI* __restrict__ Cm,
     const TI* __restrict__ dt, const float* __restrict__ A_log, const float* __restrict__ D,
     const float* __restrict__ hstates, TI* __restrict__ y, int T, int H, int P, int N, int G, int Q,
@@ -42,7 +46,7 @@ __global__ __launch_bounds__(NTHREADS) void chunk_out_fwd_kernel(
   __shared__ __attribute__((aligned(16))) OT sU[PH1 > PH2 ? PH1 : PH2];
   __shared__ float sS[QMAX];
   __shared__ float sDt[QMAX];
-  __shared__ float sTmp[8];
+  __shared__ float sTmp[16];
   OT* const sB = sU;
   OT* const sH = sU;
   OT* const sXt = sU + PMAX * LDN;
@@ -61,6 +65,8 @@ __global__ __launch_bounds__(NTHREADS) void chunk_out_fwd_kernel(
   const int bi = idx / nc;
 
   const int tid = threadIdx.x, w = wave_id(), l = lane_id(), r = l & 15, q = l >> 4;
+  const int rw = w & 3, cw = w >> 2;
+  (void)l;
   const int64_t row0 = static_cast<int64_t>(bi) * T + static_cast<int64_t>(c) * Q;
   const int i0 = ib * BQ;
   const int vi = min(BQ, Q - i0);
@@ -72,16 +78,16 @@ __global__ __launch_bounds__(NTHREADS) void chunk_out_fwd_kernel(
 
   // ---- group-level C.B^T tiles for (ib, jb <= ib)
   {
-    RowTile<TI, BQ, NMAX> tc;
+    RowTile<TI, BQ, NMAX, NT8> tc;
     tc.load(Cm + (row0 + i0) * GN + static_cast<int64_t>(g) * N, GN, vi, N);
     tc.store(sC, LDN);
   }
-  f4 cb[NBMAX][4];
+  f4 cb[NBMAX][2];
 #pragma unroll
   for (int jb = 0; jb < NBMAX; ++jb) zero(cb[jb]);
   for (int sl = 0; sl < nslab; ++sl) {
     const int j0 = sl * JW;
-    RowTile<TI, JW, NMAX> tb;
+    RowTile<TI, JW, NMAX, NT8> tb;
     tb.load(Bm + (row0 + j0) * GN + static_cast<int64_t>(g) * N, GN, min(JW, jend - j0), N);
     __syncthreads();
     tb.store(sB, LDN);
@@ -89,14 +95,14 @@ __global__ __launch_bounds__(NTHREADS) void chunk_out_fwd_kernel(
 #pragma unroll
     for (int jb = 0; jb < NBMAX; ++jb) {
       const int jl = jb * BQ - j0;  // block start inside the slab
-      if (jb <= ib && jl >= 0 && jl < JW)  // rows j of block jb (this wave's 16), columns i
-        wave_gemm<BF, true, true, 4>(cb[jb], sB + (jl + 16 * w) * LDN, LDN, 1, sC, LDN, 1, Kn);
+      if (jb <= ib && jl >= 0 && jl < JW)  // rows j of block jb (this wave's 16), columns i (its 32)
+        wave_gemm<BF, true, true, 2>(cb[jb], sB + (jl + 16 * rw) * LDN, LDN, 1, sC + 32 * cw * LDN, LDN, 1, Kn);
     }
   }
 
   // ---- per head
-  RowTile<float, PMAX, NMAX> th;  // H_c as [p][n]
-  TransTile<TI, JW, PMAX> tx;     // x rows j -> [p][j]
+  RowTile<float, PMAX, NMAX, NT8> th;      // H_c as [p][n]
+  TransTile<TI, JW, PMAX, 4, NT8> tx;      // x rows j -> [p][j]
   float dt_next = 0.f;
   auto prefetch = [&](int hh, int sl) {
     const int h = g * hpg + sp * hps + hh;
@@ -122,28 +128,28 @@ __global__ __launch_bounds__(NTHREADS) void chunk_out_fwd_kernel(
     }
     th.store(sH, LDN);
     // skip term D x_i of this wave's output rows, loaded now, used at the end
-    float xsk[4][4];
+    float xsk[4][2];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int iq = i0 + 16 * w + 4 * q + i;
+      const int iq = i0 + 16 * rw + 4 * q + i;
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int p = 16 * t + r;
+      for (int t = 0; t < 2; ++t) {
+        const int p = 32 * cw + 16 * t + r;
         xsk[i][t] = (iq < Q && p < P) ? load_f(x, (row0 + iq) * HP + static_cast<int64_t>(h) * P + p) : 0.f;
       }
     }
     __syncthreads();
 
     // incoming-state readout: exp(s_i) * C_i . H_c^T
-    f4 acc[4];
+    f4 acc[2];
     zero(acc);
-    wave_gemm<BF, true, true, 4>(acc, sC + 16 * w * LDN, LDN, 1, sH, LDN, 1, Kn);
+    wave_gemm<BF, true, true, 2>(acc, sC + 16 * rw * LDN, LDN, 1, sH + 32 * cw * LDN, LDN, 1, Kn);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int iq = i0 + 16 * w + 4 * q + i;
+      const int iq = i0 + 16 * rw + 4 * q + i;
       const float e = (iq < Q) ? __expf(sS[iq]) : 0.f;
 #pragma unroll
-      for (int t = 0; t < 4; ++t) acc[t][i] *= e;
+      for (int t = 0; t < 2; ++t) acc[t][i] *= e;
     }
 
     // intra-chunk part, one slab of chunk columns at a time
@@ -156,10 +162,10 @@ __global__ __launch_bounds__(NTHREADS) void chunk_out_fwd_kernel(
         const int jl = jb * BQ - j0;
         if (jb <= ib && jl >= 0 && jl < JW) {
 #pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            // lane holds B.C^T rows j = jb*64 + 16w + 4q + e (e = 0..3), column i = i0 + 16t + r
-            const int il = 16 * t + r, iq = i0 + il;
-            const int jw = 16 * w + 4 * q;  // first of the lane's four j inside block jb
+          for (int t = 0; t < 2; ++t) {
+            // lane holds B.C^T rows j = jb*64 + 16rw + 4q + e (e = 0..3), column i = i0 + 32cw + 16t + r
+            const int il = 32 * cw + 16 * t + r, iq = i0 + il;
+            const int jw = 16 * rw + 4 * q;  // first of the lane's four j inside block jb
             const float si = sS[min(iq, Q - 1)];
             float v4[4];
 #pragma unroll
@@ -183,15 +189,15 @@ __global__ __launch_bounds__(NTHREADS) void chunk_out_fwd_kernel(
         prefetch(hh + 1, 0);
       __syncthreads();
       const int kw = round_up(min(JW, jend - j0), Op<BF>::KS);
-      wave_gemm<BF, true, true, 4>(acc, sG + 16 * w * LDJ, LDJ, 1, sXt, LDJ, 1, kw);
+      wave_gemm<BF, true, true, 2>(acc, sG + 16 * rw * LDJ, LDJ, 1, sXt + 32 * cw * LDJ, LDJ, 1, kw);
     }
 
     // skip term and store
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int iq = i0 + 16 * w + 4 * q + i, p = 16 * t + r;
+        const int iq = i0 + 16 * rw + 4 * q + i, p = 32 * cw + 16 * t + r;
         if (iq < Q && p < P) {
           const int64_t o = (row0 + iq) * HP + static_cast<int64_t>(h) * P + p;
           store_f(y, o, acc[t][i] + Dh * xsk[i][t]);
@@ -205,12 +211,12 @@ hipError_t launch_chunk_out_fwd(const Dims& d, DType act, int nsplit, const void
                                 const float* states, void* y, hipStream_t st) {
   const int64_t nblk = static_cast<int64_t>(d.b) * d.nc() * d.G * nsplit * d.nb();
   if (act == BF16) {
-    hipLaunchKernelGGL((chunk_out_fwd_kernel<uint16_t, true>), dim3(nblk), dim3(NTHREADS), 0, st,
+    hipLaunchKernelGGL((chunk_out_fwd_kernel<uint16_t, true>), dim3(nblk), dim3(NT8), 0, st,
                        static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(B),
                        static_cast<const uint16_t*>(C), static_cast<const uint16_t*>(dt), A_log, D, states,
                        static_cast<uint16_t*>(y), d.T, d.H, d.P, d.N, d.G, d.Q, nsplit);
   } else {
-    hipLaunchKernelGGL((chunk_out_fwd_kernel<float, false>), dim3(nblk), dim3(NTHREADS), 0, st,
+    hipLaunchKernelGGL((chunk_out_fwd_kernel<float, false>), dim3(nblk), dim3(NT8), 0, st,
                        static_cast<const float*>(x), static_cast<const float*>(B),
                        static_cast<const float*>(C), static_cast<const float*>(dt), A_log, D, states,
                        static_cast<float*>(y), d.T, d.H, d.P, d.N, d.G, d.Q, nsplit);

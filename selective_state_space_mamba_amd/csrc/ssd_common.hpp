@@ -144,8 +144,8 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-// Inclusive prefix sum over the 256 threads of the workgroup.  `tmp` holds 4
-// floats of LDS.  Every thread of the workgroup must call it.
+// Inclusive prefix sum over the threads of the workgroup.  `tmp` holds one
+// float of LDS per wave.  Every thread of the workgroup must call it.
 __device__ __forceinline__ float block_inclusive_scan(float v, float* tmp) {
   const int l = lane_id(), w = wave_id();
 #pragma unroll
@@ -268,11 +268,11 @@ __device__ __forceinline__ uint32_t pair16(const uint4& a, const uint4& b, int c
 // load() issues every global load of the tile into registers; store() converts
 // (optionally scaling by row) and writes LDS.  Splitting the two lets a kernel
 // overlap the loads of the next tile with work on the current one.
-template <typename TS, int ROWS, int COLS>
+template <typename TS, int ROWS, int COLS, int NT = NTHREADS>
 struct RowTile {
   static_assert(COLS % 8 == 0, "tile width must be a multiple of 8");
   static constexpr int ITEMS = ROWS * COLS / 8;
-  static constexpr int PER = (ITEMS + NTHREADS - 1) / NTHREADS;
+  static constexpr int PER = (ITEMS + NT - 1) / NT;
   Vec8<TS> v[PER];
   int nrows;
   __device__ __forceinline__ void load(const TS* src, int64_t ld, int rows_valid, int cols_valid) {
@@ -280,7 +280,7 @@ struct RowTile {
     const bool vec = vec16_ok(src, ld, sizeof(TS));
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      const int it = threadIdx.x + i * NTHREADS;
+      const int it = threadIdx.x + i * NT;
       const int r = it / (COLS / 8), c0 = (it % (COLS / 8)) * 8;
       if (it < ITEMS && r < rows_valid && c0 < cols_valid) {
         const TS* p = src + r * ld + c0;
@@ -297,7 +297,7 @@ struct RowTile {
   __device__ __forceinline__ void store(TD* dst, int ld_dst, const float* row_scale = nullptr) const {
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      const int it = threadIdx.x + i * NTHREADS;
+      const int it = threadIdx.x + i * NT;
       if (it < ITEMS) {
         const int r = it / (COLS / 8), c0 = (it % (COLS / 8)) * 8;
         if constexpr (sizeof(TS) == 2 && sizeof(TD) == 2) {
@@ -325,12 +325,12 @@ struct RowTile {
 // (RB = 8 or 4 source rows) through registers: 16-bit blocks are transposed
 // with byte permutes, f32 blocks converted in pairs.  Optional scale by source
 // row (a time step, say).  RB = 4 halves the registers a thread holds.
-template <typename TS, int ROWS, int COLS, int RB = 8>
+template <typename TS, int ROWS, int COLS, int RB = 8, int NT = NTHREADS>
 struct TransTile {
   static_assert(RB == 8 || RB == 4, "blocks of 8 or 4 rows");
   static_assert(COLS % 8 == 0 && ROWS % RB == 0, "tile sides must be multiples of the block");
   static constexpr int ITEMS = (ROWS / RB) * (COLS / 8);
-  static constexpr int PER = (ITEMS + NTHREADS - 1) / NTHREADS;
+  static constexpr int PER = (ITEMS + NT - 1) / NT;
   Vec8<TS> v[PER][RB];
   int nrows;
   __device__ __forceinline__ void load(const TS* src, int64_t ld, int rows_valid, int cols_valid) {
@@ -338,7 +338,7 @@ struct TransTile {
     const bool vec = vec16_ok(src, ld, sizeof(TS));
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      const int it = threadIdx.x + i * NTHREADS;
+      const int it = threadIdx.x + i * NT;
       const int c0 = (it % (COLS / 8)) * 8, r0 = (it / (COLS / 8)) * RB;
 #pragma unroll
       for (int e = 0; e < RB; ++e) {
@@ -359,7 +359,7 @@ struct TransTile {
   __device__ __forceinline__ void store(TD* dst, int ld_dst, const float* row_scale = nullptr) const {
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      const int it = threadIdx.x + i * NTHREADS;
+      const int it = threadIdx.x + i * NT;
       if (it < ITEMS) {
         const int c0 = (it % (COLS / 8)) * 8, r0 = (it / (COLS / 8)) * RB;
         if constexpr (sizeof(TS) == 2 && sizeof(TD) == 2) {
@@ -402,7 +402,7 @@ struct TransTile {
   __device__ __forceinline__ void store_rows(TD* dst, int ld_dst) const {
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      const int it = threadIdx.x + i * NTHREADS;
+      const int it = threadIdx.x + i * NT;
       if (it < ITEMS) {
         const int c0 = (it % (COLS / 8)) * 8, r0 = (it / (COLS / 8)) * RB;
 #pragma unroll

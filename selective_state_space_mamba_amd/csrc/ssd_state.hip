@@ -59,8 +59,11 @@ __global__ __launch_bounds__(NTHREADS, 2) void chunk_state_kernel(
   __shared__ float sW[QMAX];
   __shared__ float sTmp[8];
 
-  const int pb = blockIdx.x, h = blockIdx.y, bi = blockIdx.z;
-  const int npb = gridDim.x;
+  // p-blocks of a head, then the heads of a group, are consecutive logical
+  // blocks: they read the same B (or C) slab, so they share an XCD's L2.
+  const int npb = (P + PB - 1) / PB;
+  const int lb = xcd_logical_block(blockIdx.x, gridDim.x);
+  const int pb = lb % npb, h = (lb / npb) % H, bi = lb / (npb * H);
   const int p0 = pb * PB;
   const int g = h / (H / G);
   const int nc = T / Q;
@@ -155,7 +158,7 @@ template <typename TX, typename TB, bool BF, bool REV>
 static hipError_t launch_state(const Dims& d, const void* X, const void* Bm, const void* dt,
                                const float* A_log, const float* init, void* states, float* last,
                                const float* hstates, float* gh_part, hipStream_t st) {
-  dim3 grid(state_npb(d), d.H, d.b);
+  dim3 grid(state_npb(d) * d.H * d.b);
   hipLaunchKernelGGL((chunk_state_kernel<TX, TB, TB, BF, REV>), grid, dim3(NTHREADS), 0, st,
                      static_cast<const TX*>(X), static_cast<const TB*>(Bm), static_cast<const TB*>(dt),
                      A_log, init, states, last, hstates, gh_part, d.T, d.H, d.P, d.N, d.G, d.Q);
