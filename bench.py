@@ -99,6 +99,62 @@ def measured_traffic(kernel: str, workload: str):
     return float(m_b.group(1))
 
 
+def _counter_rows(d: str):
+    import csv
+    import glob
+    rows = []
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        rows.extend(csv.DictReader(open(f)))
+    return rows
+
+
+def write_counter_summary(fetch_dir: str, write_dir: str, kernel: str, workload: str, copy_mb: int) -> None:
+    """HBM bytes per launch of `kernel` from rocprofv3 FETCH_SIZE / WRITE_SIZE
+    runs (KiB per dispatch), each scaled by what the same counter reads for the
+    plain copy of `copy_mb` MiB that --calibrate-copy-mb ran in those runs."""
+    if copy_mb <= 0:
+        raise SystemExit("--counter-summary needs --calibrate-copy-mb (the calibration copy size)")
+    known = float(copy_mb << 20)
+    out = {}
+    for label, d, counter in (("fetch", fetch_dir, "FETCH_SIZE"), ("write", write_dir, "WRITE_SIZE")):
+        rows = [r for r in _counter_rows(d) if r["Counter_Name"] == counter]
+        kv = [float(r["Counter_Value"]) for r in rows if kernel + "_kernel" in r["Kernel_Name"]]
+        copies = sorted(float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"])
+        if not kv or not copies:
+            raise SystemExit(f"no {counter} rows for {kernel} or for the calibration copy in {d}")
+        cal = copies[-3:]  # the calibration copies are the largest ones
+        factor = known / (sum(cal) / len(cal) * 1024.0)
+        out[label] = (sum(kv) / len(kv), len(kv), sum(cal) / len(cal), factor)
+    fetch_b = out["fetch"][0] * 1024.0 * out["fetch"][3]
+    write_b = out["write"][0] * 1024.0 * out["write"][3]
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_hbm_counters.txt")
+    lines = [
+        f"HBM traffic of {kernel} on the {workload} workload (rocprofv3 counters, per launch)",
+        "",
+        "Commands (repository root, one MI355X, TMPDIR=/tmp):",
+        f"  rocprofv3 --pmc FETCH_SIZE -f csv -d <FETCH_DIR> -o run -- python3 bench.py --workload {workload} "
+        f"--steps 2 --warmup 1 --no-cpu-baseline --calibrate-copy-mb {copy_mb}",
+        f"  rocprofv3 --pmc WRITE_SIZE -f csv -d <WRITE_DIR> -o run -- python3 bench.py --workload {workload} "
+        f"--steps 2 --warmup 1 --no-cpu-baseline --calibrate-copy-mb {copy_mb}",
+        f"  python3 bench.py --workload {workload} --kernel {kernel} --calibrate-copy-mb {copy_mb} "
+        "--counter-summary <FETCH_DIR> <WRITE_DIR>",
+        "",
+        f"FETCH_SIZE: {out['fetch'][0]:.1f} KiB per launch (mean of {out['fetch'][1]} launches); "
+        f"the {copy_mb} MiB copy reads {out['fetch'][2]:.1f} KiB -> scale {out['fetch'][3]:.4f}",
+        f"WRITE_SIZE: {out['write'][0]:.1f} KiB per launch (mean of {out['write'][1]} launches); "
+        f"the {copy_mb} MiB copy writes {out['write'][2]:.1f} KiB -> scale {out['write'][3]:.4f}",
+        f"fetch_bytes_per_launch: {fetch_b:.0f}",
+        f"write_bytes_per_launch: {write_b:.0f}",
+        f"hbm_bytes_per_launch: {fetch_b + write_b:.0f}",
+        f"source_digest: {source_digest(kernel)}",
+        "",
+        "The digest covers the kernel's source files; bench.py reports this traffic only while it matches.",
+    ]
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(path)
+
+
 def to_dev(a):
     import numpy as np
     import torch
@@ -178,7 +234,16 @@ def main():
     ap.add_argument("--workload", default="grouped", choices=["tiny", "m130", "grouped", "long", "block"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-batches", type=int, default=0, help="batch rows in the oracle sample (0: workload default)")
+    ap.add_argument("--calibrate-copy-mb", type=int, default=0,
+                    help="after timing, run a plain device copy of this many MiB (3 times) for counter calibration")
+    ap.add_argument("--counter-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write the HBM-traffic summary from two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) and exit")
+    ap.add_argument("--kernel", default="chunk_bwd_col", help="kernel for --counter-summary")
     args = ap.parse_args()
+    if args.counter_summary:
+        write_counter_summary(args.counter_summary[0], args.counter_summary[1], args.kernel, args.workload,
+                              args.calibrate_copy_mb)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): this build has no multi-GPU path; "
               "see DESIGN.md for how the SSD would shard.", file=sys.stderr)
@@ -226,6 +291,15 @@ def main():
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "kernel": dom, "kernel_ms": round(core[dom], 4), "algorithmic_bytes": alg,
                 "mfma_tflops": round(algorithmic_flops(cfg, dom) / t_dom / 1e12, 2)}
+
+    if args.calibrate_copy_mb > 0:
+        nbytes = args.calibrate_copy_mb << 20
+        src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     cpu = None
     if not args.no_cpu_baseline:
