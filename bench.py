@@ -51,15 +51,24 @@ def algorithmic_bytes(cfg, kernel: str) -> float:
     tok = cfg.batch * cfg.seqlen
     HP, GN, H = cfg.nheads * cfg.headdim, cfg.ngroups * cfg.dstate, cfg.nheads
     st = H * cfg.headdim * cfg.dstate * 4 / cfg.chunk  # chunk states per token (f32)
+    sg = H * cfg.headdim * cfg.dstate * s_a / cfg.chunk  # state gradients per token (operand dtype)
     per_token = {
         "chunk_state_fwd": HP * s_a + GN * s_a + H * s_a + st,
         "chunk_out_fwd": HP * s_a + 2 * GN * s_a + H * s_a + st + HP * s_a,
-        "chunk_state_bwd": HP * s_y + GN * s_a + H * s_a + 2 * st,
-        "chunk_bwd_col": HP * s_a + 2 * GN * s_a + H * s_a + HP * s_y + st + HP * 4 + GN * 4 + 3 * H * 4,
+        "chunk_state_bwd": HP * s_y + GN * s_a + H * s_a + st + sg,
+        "chunk_bwd_col": HP * s_a + 2 * GN * s_a + H * s_a + HP * s_y + sg + HP * 4 + GN * 4 + 3 * H * 4,
         "chunk_bwd_row": HP * s_a + 2 * GN * s_a + H * s_a + HP * s_y + st + GN * 4 + 2 * H * 4,
         "bwd_dt": H * s_a + 5 * H * 4 + H * 4,
     }
     return per_token[kernel] * tok
+
+
+def backward_algorithmic_bytes(cfg) -> float:
+    """Bytes the whole backward must move: x, dt, B, C, dy read once, dx, ddt,
+    dB, dC written once (f32); saved chunk states excluded."""
+    s_a = 2 if cfg.dtype == "bf16" else 4
+    HP, GN, H = cfg.nheads * cfg.headdim, cfg.ngroups * cfg.dstate, cfg.nheads
+    return (2 * HP * s_a + 2 * GN * s_a + H * s_a + HP * 4 + 2 * GN * 4 + H * 4) * cfg.batch * cfg.seqlen
 
 
 def algorithmic_flops(cfg, kernel: str) -> float:
@@ -291,6 +300,11 @@ def main():
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "kernel": dom, "kernel_ms": round(core[dom], 4), "algorithmic_bytes": alg,
                 "mfma_tflops": round(algorithmic_flops(cfg, dom) / t_dom / 1e12, 2)}
+    t_bwd = sum(v for k, v in kms.items() if k in KERNELS_BWD) * 1e-3
+    bwd_alg = backward_algorithmic_bytes(cfg)
+    ssd_bwd = {"ms": round(t_bwd * 1e3, 4), "algorithmic_bytes": bwd_alg,
+               "achieved": round(bwd_alg / t_bwd / 1e9, 1), "unit": "GB/s",
+               "frac": round(bwd_alg / t_bwd / 1e9 / HBM_PEAK_GBS, 4)}
 
     if args.calibrate_copy_mb > 0:
         nbytes = args.calibrate_copy_mb << 20
@@ -316,6 +330,7 @@ def main():
                    "global_batch": cfg.batch, "seq_len": cfg.seqlen, "parallelism": "single-gpu"},
         "kernel_ms": {k: round(v, 4) for k, v in kms.items()},
         "roofline": roofline,
+        "ssd_bwd": ssd_bwd,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
