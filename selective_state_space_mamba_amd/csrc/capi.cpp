@@ -334,9 +334,14 @@ int ssd_bwd(const ssd_problem* prob, const void* x, const void* dt, const float*
   }
   SSD_LAUNCH(ssd::launch_chunk_state_bwd(d, act, dyt, dy, C, dt, A_log, states, gamma, d_init_state, s.gh_part, st),
              "chunk_state_bwd");
-  SSD_LAUNCH(ssd::launch_chunk_bwd_col(d, act, dyt, plan.nsplit, x, B, C, dt, dy, A_log, D, gamma, dx,
-                                       plan.nsplit > 1 ? s.dB_part : dB, s, st),
-             "chunk_bwd_col");
+  if (act == ssd::BF16 && dyt == ssd::BF16 && ssd::bwd_bf16_supported(d))
+    SSD_LAUNCH(ssd::launch_bwd_col_bf16(d, plan.nsplit, x, B, C, dt, dy, A_log, D, gamma, dx,
+                                        plan.nsplit > 1 ? s.dB_part : dB, s, st),
+               "chunk_bwd_col");
+  else
+    SSD_LAUNCH(ssd::launch_chunk_bwd_col(d, act, dyt, plan.nsplit, x, B, C, dt, dy, A_log, D, gamma, dx,
+                                         plan.nsplit > 1 ? s.dB_part : dB, s, st),
+               "chunk_bwd_col");
   SSD_LAUNCH(ssd::launch_chunk_bwd_row(d, act, dyt, plan.nsplit, x, B, C, dt, dy, A_log, states,
                                        plan.nsplit > 1 ? s.dC_part : dC, s, st),
              "chunk_bwd_row");

@@ -1,0 +1,184 @@
+// Asynchronous LDS staging and MFMA fragment reads for bf16 operands (gfx950).
+//
+// Tiles are copied from global memory straight into LDS with
+// buffer_load_dwordx4 ... lds: each lane moves 16 bytes and the wave writes
+// 1 KB of consecutive LDS (from M0), so no VGPRs hold staged data and the copy
+// proceeds while the wave computes.  Loads outside a tile's valid rows or
+// 16-byte chunks use an offset past the buffer descriptor's range, which the
+// hardware returns as zeros, so ragged edges arrive zero-filled.  The copy is
+// issued from inline assembly: the compiler then does not know of it and
+// inserts none of its own vmcnt waits before later LDS reads (it cannot always
+// tell that a copy in flight targets another buffer); completion is the
+// caller's business, with wait_vm() before the barrier that publishes a tile.
+//
+// A tile row of CPR 16-byte chunks (CPR * 8 bf16) is stored unpadded with the
+// chunk index XOR-swizzled by a function of the row.  The swizzle keeps both
+// fragment reads below free of bank conflicts, for 32 or 64 LDS banks:
+//  * rows(): lane (r, q) reads row m0 + r, chunk kc + q (one 16-byte read):
+//    the MFMA fragment whose k index runs along the row;
+//  * cols(): ds_read_b64_tr_b16 pairs that deliver, to lane (r, q), the 8
+//    elements of column m0 + r in rows k0 + 8q .. k0 + 8q + 7: the MFMA
+//    fragment whose k index runs down the rows.  Within each group of 16
+//    lanes the instruction returns to lane i, element e, the (i % 4)-th value
+//    read by lane 4e + i / 4, so lane j of the group reads the 4 elements at
+//    row k0 + 8q + (j / 4) (+4 for the second read), column m0 + 4 (j % 4).
+#pragma once
+
+#include "ssd_common.hpp"
+
+namespace ssd {
+
+typedef __attribute__((address_space(3))) char lds_char;
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef short short8_t __attribute__((ext_vector_type(8)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Byte offsets at or beyond this value are out of every descriptor's range.
+constexpr uint32_t OOB_OFFSET = 0x80000000u;
+
+// Raw buffer descriptor over the 2 GiB that start at `base` (byte offsets,
+// stride 0; loads at OOB_OFFSET or beyond return zeros).
+__device__ __forceinline__ i32x4 make_rsrc(const void* base) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return i32x4{static_cast<int>(a), static_cast<int>((a >> 32) & 0xFFFFu), 0x7FFFFFF0, 0x00020000};
+}
+
+// One wave's 16-byte-per-lane copy into LDS at dst + 16 * lane (dst uniform).
+__device__ __forceinline__ void dma16(const i32x4& rs, lds_char* dst, uint32_t voff) {
+#if defined(__HIP_DEVICE_COMPILE__)  // gfx950 assembly: device pass only
+  // dst is uniform across the wave but derived from the wave index, so make
+  // that explicit for the scalar operand
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(dst)));
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(m0v), "v"(voff), "s"(rs)
+               : "memory", "m0");
+#endif
+}
+
+// The same descriptor in the type the buffer-load builtins take.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc_ptr(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0x7FFFFFF0, 0x00020000);
+}
+
+__device__ __forceinline__ lds_char* lds_ptr(void* p) { return (lds_char*)p; }
+
+// vmcnt(n) with the other counters left alone.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0070 | 0x0F00);
+}
+
+// Workgroup barrier for LDS data written with ds_write only: waits for this
+// wave's LDS operations (lgkmcnt) but not for vector-memory operations, so
+// asynchronous tile copies stay in flight across it (__syncthreads' fence
+// would wait for them too).  The empty asm statements keep the compiler from
+// moving memory accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt at their maximum
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
+}
+
+template <int CPR>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (CPR <= 2) {
+    return 0;
+  } else {
+    const int b = ((r & 3) << 1) | ((r >> 2) & 1);
+    return b ^ (((r >> 3) & 1) * (CPR == 16 ? 8 : 2));
+  }
+}
+
+template <int CPR>
+__device__ __forceinline__ int tile_off(int row, int chunk) {
+  return row * (CPR * 16) + ((chunk ^ swz<CPR>(row)) << 4);
+}
+
+// Copy rows 0..ROWS-1 of a bf16 matrix into an LDS tile of ROWS x CPR chunks:
+// row r starts at byte base + r * ldb of the descriptor; rows >= row_ok and
+// chunks >= chunk_ok are zero.  The NW waves of the workgroup share the copy.
+template <int ROWS, int CPR, int NW>
+__device__ __forceinline__ void tile_async(lds_char* dst, const i32x4& rs, uint32_t base,
+                                           uint32_t ldb, int row_ok, int chunk_ok) {
+  constexpr int LPI = 64 / CPR;  // rows per wave instruction
+  constexpr int NI = ROWS / LPI;
+  static_assert(ROWS % LPI == 0, "tile rows");
+  const int l = lane_id(), w = wave_id();
+  const int rl = l / CPR, pc = l % CPR;
+#pragma unroll
+  for (int it = 0; it < (NI + NW - 1) / NW; ++it) {
+    const int ins = it * NW + w;
+    if ((NI % NW) == 0 || ins < NI) {
+      const int r = ins * LPI + rl;
+      const int c = pc ^ swz<CPR>(r);
+      const uint32_t off = (r < row_ok && c < chunk_ok) ? base + static_cast<uint32_t>(r) * ldb + (c << 4) : OOB_OFFSET;
+      dma16(rs, dst + ins * 1024, off);
+    }
+  }
+}
+
+// Fragment with k along the row: lane (r, q) gets row m0 + r, elements
+// 8 (kc + q) .. +7.
+template <int CPR>
+__device__ __forceinline__ bf16x8 frag_rows(const lds_char* t, int m0, int kc) {
+  const int l = lane_id(), r = l & 15, q = l >> 4;
+  const int row = m0 + r;
+  return *(const __attribute__((address_space(3))) bf16x8*)(t + tile_off<CPR>(row, kc + q));
+}
+
+// Fragment with k down the rows: lane (r, q) gets column m0 + r, rows
+// k0 + 8q .. k0 + 8q + 7 (m0 a multiple of 16, k0 of 8).
+template <int CPR>
+__device__ __forceinline__ bf16x8 frag_cols(const lds_char* t, int k0, int m0) {
+  const int l = lane_id(), i = l & 15, q = l >> 4;
+  const int c = (m0 >> 3) + ((i >> 1) & 1), half = (i & 1) << 3;
+  const int r0 = k0 + 8 * q + (i >> 2), r1 = r0 + 4;
+  const short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) short4_t*)(t + tile_off<CPR>(r0, c) + half));
+  const short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) short4_t*)(t + tile_off<CPR>(r1, c) + half));
+  const short8_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// One element (row, col) of a swizzled tile, as f32.
+template <int CPR>
+__device__ __forceinline__ float tile_elem(const lds_char* t, int row, int col) {
+  const uint16_t v =
+      *(const __attribute__((address_space(3))) uint16_t*)(t + tile_off<CPR>(row, col >> 3) + ((col & 7) << 1));
+  return bf16_bits_to_f32(v);
+}
+
+// Sum over each row of 16 lanes (lanes sharing q), complete in lane r = 15
+// (DPP row shifts, zero-filled at the row start).
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float v) {
+  return v + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float row_sum16(float v) {
+  v = dpp_add<0x111>(v);  // row_shr:1
+  v = dpp_add<0x112>(v);  // row_shr:2
+  v = dpp_add<0x114>(v);  // row_shr:4
+  return dpp_add<0x118>(v);  // row_shr:8
+}
+
+// Inclusive scan over the 64 lanes of a wave: shifts within rows of 16, then
+// row_bcast15 / row_bcast31 carry each row's total into the following rows
+// (DPP; zero where a lane has no source).
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_add_rows(float v) {
+  return v + __builtin_bit_cast(float,
+                                __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROW_MASK, 0xF, true));
+}
+__device__ __forceinline__ float wave_scan(float v) {
+  v = dpp_add<0x111>(v);
+  v = dpp_add<0x112>(v);
+  v = dpp_add<0x114>(v);
+  v = dpp_add<0x118>(v);
+  v = dpp_add_rows<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+  return dpp_add_rows<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
+}
+
+}  // namespace ssd

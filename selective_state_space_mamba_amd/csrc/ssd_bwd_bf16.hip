@@ -1,0 +1,433 @@
+// Intra-chunk backward of the SSD for bf16 operands, with asynchronous LDS
+// staging (ssd_async.hpp).  Same outputs and formulas as the column and row
+// kernels of ssd_chunk_bwd.hip (derived there from the reverse-time loop of the
+// page-1 reference, burn_dragon_kernel mamba2/backward.rs,
+// ssd_backward_reference), organised so that each wave's chain of
+// contractions stays inside the wave.
+//
+// Column kernel: a workgroup owns the 64 columns j of block jb of one chunk
+// for the heads of one group (or a run of them).  Its 8 waves form two teams;
+// wave (team, wt) owns columns j0 + 16 wt .. +15 and, in every 64-row block
+// ib >= jb, the rows i0 + 32 team .. +31.  C.B^T for those tiles is formed
+// once (MFMA) and kept in LDS.  One step handles one head and one block ib;
+// in it the wave
+//   * forms yx^T = x_j . dy_i for its 16 x 32 tile with MFMA,
+//   * applies the decay: G = L CB (to a wave-private LDS strip, bf16),
+//     E = G yx (column and diagonal sums) and W = L yx dt_j (summed over heads
+//     in registers),
+//   * after a barrier, accumulates dx_j += sum_i G_ij dy_i for half of the
+//     headdim columns over all 64 rows of the block (its own strip and its
+//     partner wave's), reading G and dy down their rows with the LDS transpose
+//     read.
+// After the blocks of a head the teams add their column-sum halves through
+// LDS and the state terms B_j Gamma^T and x_j Gamma follow.  At the end,
+// dB_j = sum_i W_ij C_i + state terms, each team finishing half of the
+// d_state columns.  The other workgroup barrier ends a step, where the next
+// step's tiles (loaded by all waves while this step computed) become visible.
+// Every ring slot that an asynchronous copy targets is its own LDS variable,
+// selected by a compile-time step index, so the compiler can tell that the
+// (The copies are issued from inline assembly, so the compiler adds no waits
+// of its own for them; the barriers inside a step wait for LDS operations
+// only.)
+//
+// Off the diagonal block every i exceeds every j, so with s non-increasing
+// L_ij = exp(s_i - s_i0) exp(s_i0 - s_j) (i0 the block's first row): factors
+// <= 1 per row and per column instead of one exponential per element.
+#include "ssd_async.hpp"
+#include "ssd_common.hpp"
+#include "ssd_launch.hpp"
+
+namespace ssd {
+
+namespace {
+constexpr int BW = 8;               // waves per workgroup
+constexpr int BT = BW * WAVE;       // threads per workgroup
+constexpr int TILE_N = 64 * 256;    // bytes of a 64 x 128 bf16 tile
+constexpr int TILE_P = 64 * 128;    // bytes of a 64 x 64 bf16 tile
+constexpr int STRIP = 32 * 32;      // bytes of a 32 x 16 bf16 strip
+}  // namespace
+
+// s (within-chunk inclusive cumsum of dt A) and dt for t < Q, from the dt bits
+// of t = 4l .. 4l+3 held by lane l; every wave computes the whole scan and
+// waves 0..3 each write a quarter.
+__device__ __forceinline__ void scan_store(const uint32_t (&dtb)[4], float A, float* s_out, float* dt_out) {
+  const int l = lane_id(), w = wave_id();
+  float d[4], a[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) d[e] = bf16_bits_to_f32(static_cast<uint16_t>(dtb[e]));
+  a[0] = d[0] * A;
+#pragma unroll
+  for (int e = 1; e < 4; ++e) a[e] = a[e - 1] + d[e] * A;
+  const float incl = wave_scan(a[3]);
+  const float ex = incl - a[3];
+  if ((l >> 4) == w) {
+    *reinterpret_cast<float4*>(s_out + 4 * l) = make_float4(ex + a[0], ex + a[1], ex + a[2], ex + a[3]);
+    *reinterpret_cast<float4*>(dt_out + 4 * l) = make_float4(d[0], d[1], d[2], d[3]);
+  }
+}
+
+// Write two MFMA tiles (lane element e at row j = 4q + e, column i = 16 tt + r)
+// into a wave strip as bf16 [i][j] (32 rows i of 16 columns j).
+__device__ __forceinline__ void put_strip(lds_char* strip, const f4 (&v)[2]) {
+  const int l = lane_id(), r = l & 15, q = l >> 4;
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt)
+    *(__attribute__((address_space(3))) u32x2*)(strip + (16 * tt + r) * 32 + 8 * q) =
+        u32x2{pack_bf16(v[tt][0], v[tt][1]), pack_bf16(v[tt][2], v[tt][3])};
+}
+
+__global__ __launch_bounds__(BT) void bwd_col_bf16_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ Bm, const uint16_t* __restrict__ Cm,
+    const uint16_t* __restrict__ dt, const uint16_t* __restrict__ dy, const float* __restrict__ A_log,
+    const float* __restrict__ D, const uint16_t* __restrict__ gamma, float* __restrict__ dx,
+    float* __restrict__ dB_out, float* __restrict__ colE, float* __restrict__ diagE, float* __restrict__ Rp,
+    int T, int H, int P, int N, int G, int Q, int nsplit) {
+  __shared__ __attribute__((aligned(1024))) char sB_[TILE_N];          // B rows j of block jb
+  __shared__ __attribute__((aligned(1024))) char sX_[2 * TILE_P];      // x rows j, two heads; C tile slot
+  __shared__ __attribute__((aligned(1024))) char sDy0_[TILE_P];        // dy rows i, even steps
+  __shared__ __attribute__((aligned(1024))) char sDy1_[TILE_P];        // dy rows i, odd steps
+  __shared__ __attribute__((aligned(1024))) char sGam_[TILE_N];        // Gamma [p][n]; C tile slot
+  __shared__ __attribute__((aligned(1024))) char sG_[BW * STRIP];      // per-wave strips [i][j]
+  __shared__ f4 sCB[NBMAX][2][BW][WAVE];                               // C.B^T, lane-linear
+  __shared__ float sRed[2][BQ][3];                                     // column sums, diagonal, R' halves
+  __shared__ __attribute__((aligned(16))) float sS[2][QMAX];
+  __shared__ __attribute__((aligned(16))) float sDt[2][QMAX];
+  lds_char* const sB = lds_ptr(sB_);
+  lds_char* const sX = lds_ptr(sX_);
+  lds_char* const sDy[2] = {lds_ptr(sDy0_), lds_ptr(sDy1_)};
+  lds_char* const sGam = lds_ptr(sGam_);
+  lds_char* const sG = lds_ptr(sG_);
+
+  const int nc = T / Q, nb = (Q + BQ - 1) / BQ;
+  const int hpg = H / G, hps = hpg / nsplit;
+  int idx = xcd_logical_block(blockIdx.x, gridDim.x);
+  const int jb = idx % nb;  // block 0 (the most rows i) first
+  idx /= nb;
+  const int sp = idx % nsplit;
+  idx /= nsplit;
+  const int g = idx % G;
+  idx /= G;
+  const int c = idx % nc;
+  const int bi = idx / nc;
+
+  const int l = lane_id(), w = wave_id(), r = l & 15, q = l >> 4;
+  const int team = w >> 2, wt = w & 3;
+  const int ti = 32 * team;  // this team's rows inside every 64-row block
+  const int64_t row0 = static_cast<int64_t>(bi) * T + static_cast<int64_t>(c) * Q;
+  const int j0 = jb * BQ, vj = min(BQ, Q - j0);
+  const int nib = nb - jb;
+  const int64_t HP = static_cast<int64_t>(H) * P, GN = static_cast<int64_t>(G) * N;
+  const uint32_t HPb = static_cast<uint32_t>(HP) * 2, GNb = static_cast<uint32_t>(GN) * 2;
+  const uint32_t goff = static_cast<uint32_t>(g) * N * 2;
+  const int pch = P >> 3, nch = N >> 3;
+  const int kp = (P + 31) >> 5, kn = (N + 31) >> 5;
+  const i32x4 rx = make_rsrc(x + row0 * HP);
+  const i32x4 rdy = make_rsrc(dy + row0 * HP);
+  const i32x4 rb = make_rsrc(Bm + row0 * GN);
+  const i32x4 rc = make_rsrc(Cm + row0 * GN);
+  const i32x4 rg = make_rsrc(gamma + (static_cast<int64_t>(bi) * nc + c) * HP * N);
+  const __amdgpu_buffer_rsrc_t rdt = make_rsrc_ptr(dt + row0 * H);
+  auto head = [&](int hh) { return g * hpg + sp * hps + hh; };
+
+  uint32_t dtb[4];  // dt bits of t = 4l .. 4l+3 for the next scan, converted when used
+  auto load_dt = [&](int hh) {
+    const int h = head(hh);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int t = 4 * l + e;
+      const uint32_t off = (t < Q) ? static_cast<uint32_t>(t) * H * 2 : OOB_OFFSET;
+      dtb[e] = __builtin_amdgcn_raw_buffer_load_b16(rdt, off, h * 2, 0);
+    }
+  };
+  auto load_x = [&](int hh) {
+    tile_async<64, 8, BW>(sX + (hh & 1) * TILE_P, rx, j0 * HPb + head(hh) * P * 2, HPb, vj, pch);
+  };
+  auto load_dy = [&](int hh, int u, lds_char* dst) {
+    const int i0 = (jb + u) * BQ;
+    tile_async<64, 8, BW>(dst, rdy, i0 * HPb + head(hh) * P * 2, HPb, min(BQ, Q - i0), pch);
+  };
+  auto load_c = [&](int u, lds_char* dst) {
+    const int i0 = (jb + u) * BQ;
+    tile_async<64, 16, BW>(dst, rc, i0 * GNb + goff, GNb, min(BQ, Q - i0), nch);
+  };
+
+  // ---- B rows of block jb, then C.B^T for every block ib >= jb (C tiles two at a time)
+  tile_async<64, 16, BW>(sB, rb, j0 * GNb + goff, GNb, vj, nch);
+  load_dt(0);
+#pragma unroll
+  for (int u0 = 0; u0 < NBMAX; u0 += 2) {
+    if (u0 < nib) {
+      load_c(u0, sX);
+      if (u0 + 1 < nib) load_c(u0 + 1, sGam);
+      wait_vm<0>();
+      __syncthreads();
+#pragma unroll
+      for (int d = 0; d < 2; ++d) {
+        const int u = u0 + d;
+        if (u < nib) {
+          const lds_char* ct = d ? sGam : sX;
+          f4 cb[2];
+          zero(cb);
+          for (int ks = 0; ks < kn; ++ks) {
+            const bf16x8 a = frag_rows<16>(sB, 16 * wt, 4 * ks);
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) cb[tt] = mfma(a, frag_rows<16>(ct, ti + 16 * tt, 4 * ks), cb[tt]);
+          }
+          sCB[u][0][w][l] = cb[0];
+          sCB[u][1][w][l] = cb[1];
+        }
+      }
+      __syncthreads();
+    }
+  }
+  load_x(0);
+  load_dy(0, 0, sDy[0]);
+  wait_vm<0>();
+  scan_store(dtb, -__expf(A_log[head(0)]), sS[0], sDt[0]);
+  __syncthreads();
+
+  f4 ws[NBMAX][2];  // sum over heads of L yx dt: rows j, columns i as in sCB
+  f4 dbs[4];        // state part of dB: rows j, columns n = 16 (4 team + k) + r
+#pragma unroll
+  for (int u = 0; u < NBMAX; ++u) zero(ws[u]);
+  zero(dbs);
+
+  for (int hh = 0; hh < hps; ++hh) {
+    const int h = head(hh), hb = hh & 1;
+    const lds_char* xt = sX + hb * TILE_P;
+    const float* sSh = sS[hb];
+    const float* sDh = sDt[hb];
+    float sj[4], dtj[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int jq = j0 + 16 * wt + 4 * q + e;
+      sj[e] = sSh[min(jq, Q - 1)];
+      dtj[e] = (jq < Q) ? sDh[jq] : 0.f;
+    }
+    f4 dxa[2];  // sum over rows i of G_ij dy_i: rows j, columns p = 16 (2 team + k) + r
+    zero(dxa);
+    float csum[4] = {0.f, 0.f, 0.f, 0.f}, dsum[4] = {0.f, 0.f, 0.f, 0.f};
+    uint32_t dsk[4];  // dy_j at columns p = ti + r and ti + 16 + r (bf16 pair)
+
+#pragma unroll
+    for (int u = 0; u < NBMAX; ++u) {
+      if (u < nib) {
+        const int i0 = (jb + u) * BQ;
+        const lds_char* dyt = sDy[u & 1];
+        // tiles of later steps start loading now
+        if (u + 1 < nib) load_dy(hh, u + 1, sDy[(u + 1) & 1]);
+        if (u == 0) {
+          tile_async<64, 16, BW>(sGam, rg, h * P * N * 2, N * 2, P, nch);
+          if (hh + 1 < hps) load_dt(hh + 1);
+        }
+
+        // yx^T: rows j (this wave's 16), columns i = i0 + ti + 16 tt + r
+        f4 yx[2];
+        zero(yx);
+        for (int ks = 0; ks < kp; ++ks) {
+          const bf16x8 a = frag_rows<8>(xt, 16 * wt, 4 * ks);
+#pragma unroll
+          for (int tt = 0; tt < 2; ++tt) yx[tt] = mfma(a, frag_rows<8>(dyt, ti + 16 * tt, 4 * ks), yx[tt]);
+        }
+        const f4 cbt[2] = {sCB[u][0][w][l], sCB[u][1][w][l]};
+        f4 gv[2];
+        if (u == 0) {
+#pragma unroll
+          for (int tt = 0; tt < 2; ++tt) {
+            const int iq = i0 + ti + 16 * tt + r;
+            const float si = sSh[min(iq, Q - 1)];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int jq = j0 + 16 * wt + 4 * q + e;
+              const float L = (iq < Q && iq >= jq) ? __expf(si - sj[e]) : 0.f;
+              const float G1 = L * cbt[tt][e];
+              const float E = G1 * yx[tt][e];
+              csum[e] += E;
+              if (iq == jq) dsum[e] += E;
+              ws[u][tt][e] += L * dtj[e] * yx[tt][e];
+              gv[tt][e] = G1;
+            }
+          }
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int jl = 16 * wt + 4 * q + e;
+            dsk[e] = pack_bf16(tile_elem<8>(dyt, jl, ti + r), tile_elem<8>(dyt, jl, ti + 16 + r));
+          }
+        } else {
+          const float sref = sSh[i0];
+          float cf[4], cfd[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            cf[e] = __expf(sref - sj[e]);
+            cfd[e] = cf[e] * dtj[e];
+          }
+#pragma unroll
+          for (int tt = 0; tt < 2; ++tt) {
+            const int iq = i0 + ti + 16 * tt + r;
+            const float rf = (iq < Q) ? __expf(sSh[min(iq, Q - 1)] - sref) : 0.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float G1 = rf * cf[e] * cbt[tt][e];
+              const float E = G1 * yx[tt][e];
+              csum[e] += E;
+              ws[u][tt][e] += rf * cfd[e] * yx[tt][e];
+              gv[tt][e] = G1;
+            }
+          }
+        }
+        put_strip(sG + w * STRIP, gv);
+        lds_barrier();
+        // dx_j += sum_i G_ij dy_i over the block's 64 rows i: k-step ks reads
+        // the strip of team ks
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const bf16x8 a = frag_cols<2>(sG + (4 * ks + wt) * STRIP, 0, 0);
+#pragma unroll
+          for (int k = 0; k < 2; ++k) dxa[k] = mfma(a, frag_cols<8>(dyt, 32 * ks, 16 * (2 * team + k)), dxa[k]);
+        }
+        wait_vm<0>();
+        __syncthreads();
+      }
+    }
+
+    // ---- state terms of head hh; the next head's first tiles start loading
+    if (hh + 1 < hps) {
+      load_x(hh + 1);
+      load_dy(hh + 1, 0, sDy[0]);
+    }
+    f4 bg[2];  // B_j Gamma^T: rows j, columns p = 16 (2 team + k) + r
+    zero(bg);
+    for (int ks = 0; ks < kn; ++ks) {
+      const bf16x8 a = frag_rows<16>(sB, 16 * wt, 4 * ks);
+#pragma unroll
+      for (int k = 0; k < 2; ++k) bg[k] = mfma(a, frag_rows<16>(sGam, 16 * (2 * team + k), 4 * ks), bg[k]);
+    }
+    const float s_end = sSh[Q - 1];
+    float wj[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int jl = 16 * wt + 4 * q + e;
+      wj[e] = (j0 + jl < Q) ? __expf(s_end - sj[e]) : 0.f;
+      float part = 0.f;
+#pragma unroll
+      for (int k = 0; k < 2; ++k) part += bg[k][e] * tile_elem<8>(xt, jl, 16 * (2 * team + k) + r);
+      part = row_sum16(part);
+      const float cs = row_sum16(csum[e]), ds = row_sum16(dsum[e]);
+      if (r == 15) {
+        sRed[team][jl][0] = cs;
+        sRed[team][jl][1] = ds;
+        sRed[team][jl][2] = part;
+      }
+    }
+    lds_barrier();
+    const float Dh = D[h];
+    const int64_t tb = (static_cast<int64_t>(bi) * H + h) * T + static_cast<int64_t>(c) * Q;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int jq = j0 + 16 * wt + 4 * q + e, p = 16 * (2 * team + k) + r;
+        const uint32_t pk = dsk[e];
+        const float dyv = __uint_as_float(k ? (pk & 0xFFFF0000u) : (pk << 16));
+        if (jq < Q && p < P)
+          dx[(row0 + jq) * HP + static_cast<int64_t>(h) * P + p] =
+              dtj[e] * (dxa[k][e] + wj[e] * bg[k][e]) + Dh * dyv;
+      }
+    }
+    if (team == 0 && r == 15) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int jl = 16 * wt + 4 * q + e, jq = j0 + jl;
+        if (jq < Q) {
+          colE[tb + jq] = sRed[0][jl][0] + sRed[1][jl][0];
+          diagE[tb + jq] = sRed[0][jl][1] + sRed[1][jl][1];
+          Rp[tb + jq] = wj[e] * (sRed[0][jl][2] + sRed[1][jl][2]);
+        }
+      }
+    }
+    // x_j Gamma for this team's d_state columns, into the state part of dB
+    {
+      f4 v[4];
+      zero(v);
+      for (int ks = 0; ks < kp; ++ks) {
+        const bf16x8 a = frag_rows<8>(xt, 16 * wt, 4 * ks);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) v[k] = mfma(a, frag_cols<16>(sGam, 32 * ks, 16 * (4 * team + k)), v[k]);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float f = dtj[e] * wj[e];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) dbs[k][e] += f * v[k][e];
+      }
+    }
+    if (hh + 1 < hps) scan_store(dtb, -__expf(A_log[head(hh + 1)]), sS[hb ^ 1], sDt[hb ^ 1]);
+    wait_vm<0>();
+    __syncthreads();
+  }
+
+  // ---- dB_j = sum_i W_ij C_i + state terms, for this team's d_state columns
+  // over all rows i (own and partner strips); two blocks at a time, their C
+  // tiles in the x and Gamma regions and their W strips in sG and a dy slot
+  f4 dbp[4];
+  zero(dbp);
+  lds_char* const wset[2] = {sG, sDy[0]};
+#pragma unroll
+  for (int u0 = 0; u0 < NBMAX; u0 += 2) {
+    if (u0 < nib) {
+      load_c(u0, sX);
+      if (u0 + 1 < nib) load_c(u0 + 1, sGam);
+#pragma unroll
+      for (int d = 0; d < 2; ++d)
+        if (u0 + d < nib) put_strip(wset[d] + w * STRIP, ws[u0 + d]);
+      wait_vm<0>();
+      __syncthreads();
+#pragma unroll
+      for (int d = 0; d < 2; ++d) {
+        if (u0 + d < nib) {
+          const lds_char* ct = d ? sGam : sX;
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) {
+            const bf16x8 a = frag_cols<2>(wset[d] + (4 * ks + wt) * STRIP, 0, 0);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) dbp[k] = mfma(a, frag_cols<16>(ct, 32 * ks, 16 * (4 * team + k)), dbp[k]);
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  const int64_t batch = gridDim.x / (nb * nsplit * G * nc);
+  float* dBo = dB_out + static_cast<int64_t>(sp) * batch * T * GN;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int n = 16 * (4 * team + k) + r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int jq = j0 + 16 * wt + 4 * q + e;
+      if (jq < Q && n < N) dBo[(row0 + jq) * GN + static_cast<int64_t>(g) * N + n] = dbp[k][e] + dbs[k][e];
+    }
+  }
+}
+
+bool bwd_bf16_supported(const Dims& d) {
+  const int64_t HPb = int64_t(d.H) * d.P * 2, GNb = int64_t(d.G) * d.N * 2;
+  return d.P % 8 == 0 && d.N % 8 == 0 && int64_t(QMAX) * HPb < (int64_t(1) << 30) &&
+         int64_t(QMAX) * GNb < (int64_t(1) << 30) && HPb * d.N < (int64_t(1) << 30) &&
+         int64_t(QMAX) * d.H * 2 < (int64_t(1) << 30);
+}
+
+hipError_t launch_bwd_col_bf16(const Dims& d, int nsplit, const void* x, const void* B, const void* C,
+                               const void* dt, const void* dy, const float* A_log, const float* D,
+                               const void* gamma, float* dx, float* dB_out, const BwdScratch& s,
+                               hipStream_t st) {
+  const int64_t nblk = static_cast<int64_t>(d.b) * d.nc() * d.G * nsplit * d.nb();
+  hipLaunchKernelGGL(bwd_col_bf16_kernel, dim3(nblk), dim3(BT), 0, st, static_cast<const uint16_t*>(x),
+                     static_cast<const uint16_t*>(B), static_cast<const uint16_t*>(C),
+                     static_cast<const uint16_t*>(dt), static_cast<const uint16_t*>(dy), A_log, D,
+                     static_cast<const uint16_t*>(gamma), dx, dB_out, s.colE, s.diagE, s.Rp, d.T, d.H, d.P,
+                     d.N, d.G, d.Q, nsplit);
+  return hipGetLastError();
+}
+
+}  // namespace ssd

@@ -62,6 +62,14 @@ hipError_t launch_chunk_bwd_row(const Dims& d, DType act, DType dyt, int nsplit,
                                 const float* A_log, const float* states, float* dC_out,
                                 const BwdScratch& s, hipStream_t st);
 
+// bf16 operands (activations and dy) with asynchronous LDS staging: headdim
+// and d_state multiples of 8 and tile offsets within 1 GiB.
+bool bwd_bf16_supported(const Dims& d);
+hipError_t launch_bwd_col_bf16(const Dims& d, int nsplit, const void* x, const void* B, const void* C,
+                               const void* dt, const void* dy, const float* A_log, const float* D,
+                               const void* gamma, float* dx, float* dB_out, const BwdScratch& s,
+                               hipStream_t st);
+
 hipError_t launch_bwd_dt(const Dims& d, DType act, const void* dt, const float* A_log, float* ddt,
                          const BwdScratch& s, hipStream_t st);
 
