@@ -33,7 +33,7 @@ KERNEL_SOURCES = {
     "chunk_state_bwd": ["ssd_state.hip", "ssd_common.hpp"],
     "chunk_out_fwd": ["ssd_chunk_fwd.hip", "ssd_common.hpp"],
     "chunk_bwd_col": ["ssd_chunk_bwd.hip", "ssd_bwd_bf16.hip", "ssd_async.hpp", "ssd_common.hpp"],
-    "chunk_bwd_row": ["ssd_chunk_bwd.hip", "ssd_common.hpp"],
+    "chunk_bwd_row": ["ssd_chunk_bwd.hip", "ssd_bwd_bf16.hip", "ssd_async.hpp", "ssd_common.hpp"],
     "bwd_dt": ["ssd_chunk_bwd.hip", "ssd_common.hpp"],
 }
 

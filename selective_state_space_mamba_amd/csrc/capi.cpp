@@ -94,9 +94,10 @@ struct FwdPlan {
   size_t states = 0, total = 0;
 };
 struct BwdPlan {
-  size_t states = 0, gamma = 0, gh = 0, rowM = 0, colE = 0, diagE = 0, Rp = 0, dsoff = 0, dA = 0, dD = 0, dB = 0,
-         dC = 0, total = 0;
+  size_t states = 0, gamma = 0, hbf = 0, gh = 0, rowM = 0, colE = 0, diagE = 0, Rp = 0, dsoff = 0, dA = 0, dD = 0,
+         dB = 0, dC = 0, total = 0;
   int nsplit = 1;
+  bool bf16 = false;  // bf16 kernels with asynchronous staging (they also need a bf16 copy of the states)
 };
 
 size_t state_bytes(const ssd::Dims& d) {
@@ -114,9 +115,14 @@ FwdPlan plan_fwd(const ssd::Dims& d, bool has_states) {
   return p;
 }
 
-BwdPlan plan_bwd(const ssd::Dims& d, bool has_states) {
+bool use_bf16_kernels(const ssd::Dims& d, int act, int dyt) {
+  return act == SSD_BF16 && dyt == SSD_BF16 && ssd::bwd_bf16_supported(d);
+}
+
+BwdPlan plan_bwd(const ssd::Dims& d, bool has_states, bool bf16) {
   BwdPlan p;
   p.nsplit = choose_nsplit(d, kBwdTarget);
+  p.bf16 = bf16;
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t o = off;
@@ -126,6 +132,7 @@ BwdPlan plan_bwd(const ssd::Dims& d, bool has_states) {
   const size_t bht = sizeof(float) * static_cast<size_t>(d.b) * d.H * d.T;
   if (!has_states) p.states = take(state_bytes(d));
   p.gamma = take(state_bytes(d));
+  if (bf16) p.hbf = take(state_bytes(d) / 2);
   p.gh = take(sizeof(float) * static_cast<size_t>(d.b) * d.nc() * d.H * ssd::state_npb(d));
   p.rowM = take(bht);
   p.colE = take(bht);
@@ -239,7 +246,8 @@ size_t ssd_workspace_bytes(const ssd_problem* prob, int for_backward, int has_ch
   ssd::Dims d;
   if (check_problem(prob, &d) != SSD_OK) return 0;
   if (d.b == 0 || d.T == 0) return 0;
-  return for_backward ? plan_bwd(d, has_chunk_states != 0).total : plan_fwd(d, has_chunk_states != 0).total;
+  return for_backward ? plan_bwd(d, has_chunk_states != 0, use_bf16_kernels(d, prob->act_dtype, prob->dy_dtype)).total
+                      : plan_fwd(d, has_chunk_states != 0).total;
 }
 
 int ssd_fwd(const ssd_problem* prob, const void* x, const void* dt, const float* A_log, const void* B,
@@ -305,7 +313,7 @@ int ssd_bwd(const ssd_problem* prob, const void* x, const void* dt, const float*
       SSD_LAUNCH(ssd::launch_fill(d_init_state, static_cast<int64_t>(d.b) * d.H * d.P * d.N, 0.f, st), "fill");
     return ok();
   }
-  const BwdPlan plan = plan_bwd(d, chunk_states != nullptr);
+  const BwdPlan plan = plan_bwd(d, chunk_states != nullptr, use_bf16_kernels(d, prob->act_dtype, prob->dy_dtype));
   if (!workspace) return fail(SSD_ERR_WORKSPACE, "ssd_bwd: workspace is null (%zu bytes needed)", plan.total);
   if (workspace_bytes < plan.total)
     return fail(SSD_ERR_WORKSPACE, "ssd_bwd: workspace of %zu bytes is smaller than the %zu needed", workspace_bytes,
@@ -324,6 +332,7 @@ int ssd_bwd(const ssd_problem* prob, const void* x, const void* dt, const float*
   s.dB_part = plan.nsplit > 1 ? at<float>(workspace, plan.dB) : nullptr;
   s.dC_part = plan.nsplit > 1 ? at<float>(workspace, plan.dC) : nullptr;
   void* gamma = at<float>(workspace, plan.gamma);
+  void* hbf = plan.bf16 ? at<float>(workspace, plan.hbf) : nullptr;
 
   const float* states = chunk_states;
   if (!states) {
@@ -332,19 +341,24 @@ int ssd_bwd(const ssd_problem* prob, const void* x, const void* dt, const float*
                "chunk_state_fwd (recompute)");
     states = rec;
   }
-  SSD_LAUNCH(ssd::launch_chunk_state_bwd(d, act, dyt, dy, C, dt, A_log, states, gamma, d_init_state, s.gh_part, st),
-             "chunk_state_bwd");
-  if (act == ssd::BF16 && dyt == ssd::BF16 && ssd::bwd_bf16_supported(d))
+  SSD_LAUNCH(
+      ssd::launch_chunk_state_bwd(d, act, dyt, dy, C, dt, A_log, states, gamma, d_init_state, s.gh_part, hbf, st),
+      "chunk_state_bwd");
+  if (plan.bf16) {
     SSD_LAUNCH(ssd::launch_bwd_col_bf16(d, plan.nsplit, x, B, C, dt, dy, A_log, D, gamma, dx,
                                         plan.nsplit > 1 ? s.dB_part : dB, s, st),
                "chunk_bwd_col");
-  else
+    SSD_LAUNCH(ssd::launch_bwd_row_bf16(d, plan.nsplit, x, B, C, dt, dy, A_log, hbf,
+                                        plan.nsplit > 1 ? s.dC_part : dC, s, st),
+               "chunk_bwd_row");
+  } else {
     SSD_LAUNCH(ssd::launch_chunk_bwd_col(d, act, dyt, plan.nsplit, x, B, C, dt, dy, A_log, D, gamma, dx,
                                          plan.nsplit > 1 ? s.dB_part : dB, s, st),
                "chunk_bwd_col");
-  SSD_LAUNCH(ssd::launch_chunk_bwd_row(d, act, dyt, plan.nsplit, x, B, C, dt, dy, A_log, states,
-                                       plan.nsplit > 1 ? s.dC_part : dC, s, st),
-             "chunk_bwd_row");
+    SSD_LAUNCH(ssd::launch_chunk_bwd_row(d, act, dyt, plan.nsplit, x, B, C, dt, dy, A_log, states,
+                                         plan.nsplit > 1 ? s.dC_part : dC, s, st),
+               "chunk_bwd_row");
+  }
   SSD_LAUNCH(ssd::launch_bwd_dt(d, act, dt, A_log, ddt, s, st), "bwd_dt");
   SSD_LAUNCH(ssd::launch_bwd_reduce(d, plan.nsplit, A_log, dA_log, dD, dB, dC, s, st), "bwd_reduce");
   return ok();

@@ -410,11 +410,318 @@ __global__ __launch_bounds__(BT) void bwd_col_bf16_kernel(
   }
 }
 
+// Row kernel: a workgroup owns the 64 rows i of block ib of one chunk for the
+// heads of one group (or a run of them); wave (team, wt) owns rows
+// i0 + 16 wt .. +15 and, in every block jb <= ib, the columns j0 + 32 team
+// .. +31.  C_i.B_j for those tiles is formed once and kept in LDS.  A step
+// (one head, one block jb) forms yx = dy_i . x_j with MFMA and applies the
+// decay: W = L yx dt_j (summed over heads in registers) and the strictly-lower
+// row sums of M = W CB.  Once per head: U_i = dy_i H_c with MFMA (H_c as bf16,
+// read down its rows with the LDS transpose read), the readout term
+// exp(s_i) U_i . C_i, and the head sum of exp(s_i) U_i; dD is the diagonal of
+// yx.  At the end dC_i = sum_j W_ij B_j + sum_h exp(s_i) U_i, each team
+// finishing half of the d_state columns.
+__global__ __launch_bounds__(BT) void bwd_row_bf16_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ Bm, const uint16_t* __restrict__ Cm,
+    const uint16_t* __restrict__ dt, const uint16_t* __restrict__ dy, const float* __restrict__ A_log,
+    const uint16_t* __restrict__ hbf, float* __restrict__ dC_out, float* __restrict__ rowM,
+    float* __restrict__ dsoff, float* __restrict__ dD_part, int T, int H, int P, int N, int G, int Q,
+    int nsplit) {
+  __shared__ __attribute__((aligned(1024))) char sC_[TILE_N];          // C rows i of block ib
+  __shared__ __attribute__((aligned(1024))) char sDy_[2 * TILE_P];     // dy rows i, two heads; B tile slot
+  __shared__ __attribute__((aligned(1024))) char sX0_[TILE_P];         // x rows j, even steps
+  __shared__ __attribute__((aligned(1024))) char sX1_[TILE_P];         // x rows j, odd steps
+  __shared__ __attribute__((aligned(1024))) char sH_[TILE_N];          // H_c [p][n] (bf16); B tile slot
+  __shared__ __attribute__((aligned(1024))) char sG_[BW * STRIP];      // per-wave W strips [j][i]
+  __shared__ f4 sCB[NBMAX][2][BW][WAVE];                               // C.B^T, lane-linear
+  __shared__ float sRed[2][BQ][2];                                     // row-sum and readout halves
+  __shared__ float sDD[BW][4];                                         // dD partials
+  __shared__ __attribute__((aligned(16))) float sS[2][QMAX];
+  __shared__ __attribute__((aligned(16))) float sDt[2][QMAX];
+  lds_char* const sC = lds_ptr(sC_);
+  lds_char* const sDy = lds_ptr(sDy_);
+  lds_char* const sX[2] = {lds_ptr(sX0_), lds_ptr(sX1_)};
+  lds_char* const sH = lds_ptr(sH_);
+  lds_char* const sG = lds_ptr(sG_);
+
+  const int nc = T / Q, nb = (Q + BQ - 1) / BQ;
+  const int hpg = H / G, hps = hpg / nsplit;
+  int idx = xcd_logical_block(blockIdx.x, gridDim.x);
+  const int ib = nb - 1 - idx % nb;  // the block with the most columns j first
+  idx /= nb;
+  const int sp = idx % nsplit;
+  idx /= nsplit;
+  const int g = idx % G;
+  idx /= G;
+  const int c = idx % nc;
+  const int bi = idx / nc;
+
+  const int l = lane_id(), w = wave_id(), r = l & 15, q = l >> 4;
+  const int team = w >> 2, wt = w & 3;
+  const int tj = 32 * team;  // this team's columns inside every 64-column block
+  const int64_t row0 = static_cast<int64_t>(bi) * T + static_cast<int64_t>(c) * Q;
+  const int i0 = ib * BQ, vi = min(BQ, Q - i0);
+  const int nj = ib + 1;
+  const int64_t HP = static_cast<int64_t>(H) * P, GN = static_cast<int64_t>(G) * N;
+  const uint32_t HPb = static_cast<uint32_t>(HP) * 2, GNb = static_cast<uint32_t>(GN) * 2;
+  const uint32_t goff = static_cast<uint32_t>(g) * N * 2;
+  const int pch = P >> 3, nch = N >> 3;
+  const int kp = (P + 31) >> 5, kn = (N + 31) >> 5;
+  const i32x4 rx = make_rsrc(x + row0 * HP);
+  const i32x4 rdy = make_rsrc(dy + row0 * HP);
+  const i32x4 rb = make_rsrc(Bm + row0 * GN);
+  const i32x4 rc = make_rsrc(Cm + row0 * GN);
+  const i32x4 rh = make_rsrc(hbf + (static_cast<int64_t>(bi) * nc + c) * HP * N);
+  const __amdgpu_buffer_rsrc_t rdt = make_rsrc_ptr(dt + row0 * H);
+  auto head = [&](int hh) { return g * hpg + sp * hps + hh; };
+
+  uint32_t dtb[4];
+  auto load_dt = [&](int hh) {
+    const int h = head(hh);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int t = 4 * l + e;
+      const uint32_t off = (t < Q) ? static_cast<uint32_t>(t) * H * 2 : OOB_OFFSET;
+      dtb[e] = __builtin_amdgcn_raw_buffer_load_b16(rdt, off, h * 2, 0);
+    }
+  };
+  auto load_x = [&](int hh, int jb, lds_char* dst) {
+    const int j0 = jb * BQ;
+    tile_async<64, 8, BW>(dst, rx, j0 * HPb + head(hh) * P * 2, HPb, min(BQ, Q - j0), pch);
+  };
+  auto load_dy = [&](int hh) {
+    tile_async<64, 8, BW>(sDy + (hh & 1) * TILE_P, rdy, i0 * HPb + head(hh) * P * 2, HPb, vi, pch);
+  };
+  auto load_b = [&](int jb, lds_char* dst) {
+    const int j0 = jb * BQ;
+    tile_async<64, 16, BW>(dst, rb, j0 * GNb + goff, GNb, min(BQ, Q - j0), nch);
+  };
+
+  // ---- C rows of block ib, then C.B^T for every block jb <= ib (B tiles two at a time)
+  tile_async<64, 16, BW>(sC, rc, i0 * GNb + goff, GNb, vi, nch);
+  load_dt(0);
+#pragma unroll
+  for (int jb0 = 0; jb0 < NBMAX; jb0 += 2) {
+    if (jb0 < nj) {
+      load_b(jb0, sDy);
+      if (jb0 + 1 < nj) load_b(jb0 + 1, sH);
+      wait_vm<0>();
+      __syncthreads();
+#pragma unroll
+      for (int d = 0; d < 2; ++d) {
+        const int jb = jb0 + d;
+        if (jb < nj) {
+          const lds_char* bt = d ? sH : sDy;
+          f4 cb[2];
+          zero(cb);
+          for (int ks = 0; ks < kn; ++ks) {
+            const bf16x8 a = frag_rows<16>(sC, 16 * wt, 4 * ks);
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) cb[tt] = mfma(a, frag_rows<16>(bt, tj + 16 * tt, 4 * ks), cb[tt]);
+          }
+          sCB[jb][0][w][l] = cb[0];
+          sCB[jb][1][w][l] = cb[1];
+        }
+      }
+      __syncthreads();
+    }
+  }
+  load_dy(0);
+  load_x(0, 0, sX[0]);
+  wait_vm<0>();
+  scan_store(dtb, -__expf(A_log[head(0)]), sS[0], sDt[0]);
+  __syncthreads();
+
+  f4 ws[NBMAX][2];  // sum over heads of L yx dt: rows i, columns j = jb * 64 + tj + 16 tt + r
+  f4 ua[4];         // sum over heads of exp(s_i) U_i: rows i, columns n = 16 (4 team + k) + r
+#pragma unroll
+  for (int jb = 0; jb < NBMAX; ++jb) zero(ws[jb]);
+  zero(ua);
+
+  for (int hh = 0; hh < hps; ++hh) {
+    const int h = head(hh), hb = hh & 1;
+    const lds_char* dyt = sDy + hb * TILE_P;
+    const float* sSh = sS[hb];
+    const float* sDh = sDt[hb];
+    float si[4], rf[4];
+    const float sref = sSh[i0];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int iq = i0 + 16 * wt + 4 * q + e;
+      si[e] = sSh[min(iq, Q - 1)];
+      rf[e] = (iq < Q) ? __expf(si[e] - sref) : 0.f;
+    }
+    float rm[4] = {0.f, 0.f, 0.f, 0.f};  // strictly-lower row sums of M over this team's columns
+    float ddv = 0.f;                     // diagonal of yx
+
+#pragma unroll
+    for (int jb = 0; jb < NBMAX; ++jb) {
+      if (jb < nj) {
+        const int j0 = jb * BQ;
+        const lds_char* xt = sX[jb & 1];
+        if (jb + 1 < nj) load_x(hh, jb + 1, sX[(jb + 1) & 1]);
+        if (jb == 0) {
+          tile_async<64, 16, BW>(sH, rh, h * P * N * 2, N * 2, P, nch);
+          if (hh + 1 < hps) load_dt(hh + 1);
+        }
+        // yx: rows i (this wave's 16), columns j = j0 + tj + 16 tt + r
+        f4 yx[2];
+        zero(yx);
+        for (int ks = 0; ks < kp; ++ks) {
+          const bf16x8 a = frag_rows<8>(dyt, 16 * wt, 4 * ks);
+#pragma unroll
+          for (int tt = 0; tt < 2; ++tt) yx[tt] = mfma(a, frag_rows<8>(xt, tj + 16 * tt, 4 * ks), yx[tt]);
+        }
+        const f4 cbt[2] = {sCB[jb][0][w][l], sCB[jb][1][w][l]};
+        if (jb == ib) {
+#pragma unroll
+          for (int tt = 0; tt < 2; ++tt) {
+            const int jq = j0 + tj + 16 * tt + r;
+            const float sj = sSh[min(jq, Q - 1)];
+            const float dtj = (jq < Q) ? sDh[jq] : 0.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int iq = i0 + 16 * wt + 4 * q + e;
+              const float L = (iq < Q && jq <= iq) ? __expf(si[e] - sj) : 0.f;
+              const float ly = L * yx[tt][e] * dtj;
+              ws[jb][tt][e] += ly;
+              if (jq < iq) rm[e] += ly * cbt[tt][e];
+              if (jq == iq) ddv += yx[tt][e];
+            }
+          }
+        } else {
+#pragma unroll
+          for (int tt = 0; tt < 2; ++tt) {
+            const int jq = j0 + tj + 16 * tt + r;
+            const float cfd = __expf(sref - sSh[jq]) * sDh[jq];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float ly = rf[e] * cfd * yx[tt][e];
+              ws[jb][tt][e] += ly;
+              rm[e] += ly * cbt[tt][e];
+            }
+          }
+        }
+        wait_vm<0>();
+        __syncthreads();
+      }
+    }
+
+    // ---- per-head terms; the next head's first tiles start loading
+    if (hh + 1 < hps) {
+      load_dy(hh + 1);
+      load_x(hh + 1, 0, sX[0]);
+    }
+    f4 u[4];  // U_i = dy_i H_c: rows i, columns n = 16 (4 team + k) + r
+    zero(u);
+    for (int ks = 0; ks < kp; ++ks) {
+      const bf16x8 a = frag_rows<8>(dyt, 16 * wt, 4 * ks);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) u[k] = mfma(a, frag_cols<16>(sH, 32 * ks, 16 * (4 * team + k)), u[k]);
+    }
+    float ex[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int il = 16 * wt + 4 * q + e;
+      ex[e] = (i0 + il < Q) ? __expf(si[e]) : 0.f;
+      float part = 0.f;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        part += u[k][e] * tile_elem<16>(sC, il, 16 * (4 * team + k) + r);
+        ua[k][e] += ex[e] * u[k][e];
+      }
+      part = row_sum16(part);
+      const float rs = row_sum16(rm[e]);
+      if (r == 15) {
+        sRed[team][il][0] = rs;
+        sRed[team][il][1] = part;
+      }
+    }
+    {
+      const float dd = row_sum16(ddv);
+      if (r == 15) sDD[w][q] = dd;
+    }
+    lds_barrier();
+    const int64_t tb = (static_cast<int64_t>(bi) * H + h) * T + static_cast<int64_t>(c) * Q;
+    if (team == 0 && r == 15) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int il = 16 * wt + 4 * q + e, iq = i0 + il;
+        if (iq < Q) {
+          rowM[tb + iq] = sRed[0][il][0] + sRed[1][il][0];
+          dsoff[tb + iq] = ex[e] * (sRed[0][il][1] + sRed[1][il][1]);
+        }
+      }
+    }
+    if (threadIdx.x == 0) {
+      float tot = 0.f;
+#pragma unroll
+      for (int k = 0; k < BW; ++k) tot += sDD[k][0] + sDD[k][1] + sDD[k][2] + sDD[k][3];
+      dD_part[((static_cast<int64_t>(bi) * nc + c) * nb + ib) * H + h] = tot;
+    }
+    if (hh + 1 < hps) scan_store(dtb, -__expf(A_log[head(hh + 1)]), sS[hb ^ 1], sDt[hb ^ 1]);
+    wait_vm<0>();
+    __syncthreads();
+  }
+
+  // ---- dC_i = sum_j W_ij B_j + sum_h exp(s_i) U_i for this team's d_state
+  // columns over all columns j (own and partner strips); B tiles two at a time
+  lds_char* const wset[2] = {sG, sX[0]};
+#pragma unroll
+  for (int jb0 = 0; jb0 < NBMAX; jb0 += 2) {
+    if (jb0 < nj) {
+      load_b(jb0, sDy);
+      if (jb0 + 1 < nj) load_b(jb0 + 1, sH);
+#pragma unroll
+      for (int d = 0; d < 2; ++d)
+        if (jb0 + d < nj) put_strip(wset[d] + w * STRIP, ws[jb0 + d]);
+      wait_vm<0>();
+      __syncthreads();
+#pragma unroll
+      for (int d = 0; d < 2; ++d) {
+        if (jb0 + d < nj) {
+          const lds_char* bt = d ? sH : sDy;
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) {
+            const bf16x8 a = frag_cols<2>(wset[d] + (4 * ks + wt) * STRIP, 0, 0);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) ua[k] = mfma(a, frag_cols<16>(bt, 32 * ks, 16 * (4 * team + k)), ua[k]);
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  const int64_t batch = gridDim.x / (nb * nsplit * G * nc);
+  float* dCo = dC_out + static_cast<int64_t>(sp) * batch * T * GN;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int n = 16 * (4 * team + k) + r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int iq = i0 + 16 * wt + 4 * q + e;
+      if (iq < Q && n < N) dCo[(row0 + iq) * GN + static_cast<int64_t>(g) * N + n] = ua[k][e];
+    }
+  }
+}
+
 bool bwd_bf16_supported(const Dims& d) {
   const int64_t HPb = int64_t(d.H) * d.P * 2, GNb = int64_t(d.G) * d.N * 2;
   return d.P % 8 == 0 && d.N % 8 == 0 && int64_t(QMAX) * HPb < (int64_t(1) << 30) &&
          int64_t(QMAX) * GNb < (int64_t(1) << 30) && HPb * d.N < (int64_t(1) << 30) &&
          int64_t(QMAX) * d.H * 2 < (int64_t(1) << 30);
+}
+
+hipError_t launch_bwd_row_bf16(const Dims& d, int nsplit, const void* x, const void* B, const void* C,
+                               const void* dt, const void* dy, const float* A_log, const void* hbf,
+                               float* dC_out, const BwdScratch& s, hipStream_t st) {
+  const int64_t nblk = static_cast<int64_t>(d.b) * d.nc() * d.G * nsplit * d.nb();
+  hipLaunchKernelGGL(bwd_row_bf16_kernel, dim3(nblk), dim3(BT), 0, st, static_cast<const uint16_t*>(x),
+                     static_cast<const uint16_t*>(B), static_cast<const uint16_t*>(C),
+                     static_cast<const uint16_t*>(dt), static_cast<const uint16_t*>(dy), A_log,
+                     static_cast<const uint16_t*>(hbf), dC_out, s.rowM, s.dsoff, s.dD_part, d.T, d.H, d.P, d.N,
+                     d.G, d.Q, nsplit);
+  return hipGetLastError();
 }
 
 hipError_t launch_bwd_col_bf16(const Dims& d, int nsplit, const void* x, const void* B, const void* C,

@@ -38,12 +38,16 @@
 namespace ssd {
 
 // Sum over the workgroup; result valid in every thread.  `tmp`: 4 floats.
+// Ends with a barrier, so the next user of `tmp` (a scan writes it before its
+// first barrier) cannot overwrite the partial sums while a wave still reads them.
 __device__ __forceinline__ float block_sum(float v, float* tmp) {
   v = wave_sum(v);
   __syncthreads();
   if (lane_id() == 0) tmp[wave_id()] = v;
   __syncthreads();
-  return tmp[0] + tmp[1] + tmp[2] + tmp[3];
+  const float total = tmp[0] + tmp[1] + tmp[2] + tmp[3];
+  __syncthreads();
+  return total;
 }
 
 // Chunk rows (or columns) staged per slab: 128 at a time for bf16 operands, 64

@@ -29,11 +29,12 @@ hipError_t launch_chunk_state_fwd(const Dims& d, DType act, const void* x, const
 // Reverse state-gradient pass: gamma[b,c,h] = gradient reaching the state that
 // leaves chunk c, stored in the MFMA operand type (bf16 when act is BF16, else
 // f32); dinit = gradient of the initial state (nullable);
-// gh_part[b,c,h,pb] = partial <gamma[b,c,h], states[b,c,h]> over headdim block pb.
+// gh_part[b,c,h,pb] = partial <gamma[b,c,h], states[b,c,h]> over headdim block pb;
+// hbf (nullable) = the states rounded to bf16, same layout.
 hipError_t launch_chunk_state_bwd(const Dims& d, DType act, DType dyt, const void* dy,
                                   const void* C, const void* dt, const float* A_log,
                                   const float* states, void* gamma, float* dinit, float* gh_part,
-                                  hipStream_t st);
+                                  void* hbf, hipStream_t st);
 
 hipError_t launch_chunk_out_fwd(const Dims& d, DType act, int nsplit, const void* x, const void* B,
                                 const void* C, const void* dt, const float* A_log, const float* D,
@@ -65,6 +66,9 @@ hipError_t launch_chunk_bwd_row(const Dims& d, DType act, DType dyt, int nsplit,
 // bf16 operands (activations and dy) with asynchronous LDS staging: headdim
 // and d_state multiples of 8 and tile offsets within 1 GiB.
 bool bwd_bf16_supported(const Dims& d);
+hipError_t launch_bwd_row_bf16(const Dims& d, int nsplit, const void* x, const void* B, const void* C,
+                               const void* dt, const void* dy, const float* A_log, const void* hbf,
+                               float* dC_out, const BwdScratch& s, hipStream_t st);
 hipError_t launch_bwd_col_bf16(const Dims& d, int nsplit, const void* x, const void* B, const void* C,
                                const void* dt, const void* dy, const float* A_log, const float* D,
                                const void* gamma, float* dx, float* dB_out, const BwdScratch& s,

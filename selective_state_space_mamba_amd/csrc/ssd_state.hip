@@ -44,6 +44,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void chunk_state_kernel(
     float* __restrict__ last_out,      // fwd: final state; bwd: d(initial state) (nullable)
     const float* __restrict__ hstates, // bwd: H_c, for <Gamma_{c+1}, H_c>
     float* __restrict__ gh_part,       // bwd: [b,nc,H,npb]
+    uint16_t* __restrict__ hbf,        // bwd: H_c rounded to bf16 (nullable)
     int T, int H, int P, int N, int G, int Q) {
   typedef typename Op<BF>::T OT;
   // The forward writes the f32 chunk states; the backward writes Gamma in the
@@ -130,7 +131,11 @@ __global__ __launch_bounds__(NTHREADS, 2) void chunk_state_kernel(
         const int p = p0 + 4 * q + i, n = 32 * w + 16 * t + r;
         if (p < P && n < N) {
           if (states_out) store_f(states_out, sbase + p * N + n, st[t][i]);
-          if (REV) gh += st[t][i] * hstates[sbase + p * N + n];
+          if (REV) {
+            const float hv = hstates[sbase + p * N + n];
+            gh += st[t][i] * hv;
+            if (hbf) hbf[sbase + p * N + n] = f32_to_bf16_bits(hv);
+          }
         }
         st[t][i] = decay * st[t][i] + acc[t][i];
       }
@@ -157,11 +162,12 @@ __global__ __launch_bounds__(NTHREADS, 2) void chunk_state_kernel(
 template <typename TX, typename TB, bool BF, bool REV>
 static hipError_t launch_state(const Dims& d, const void* X, const void* Bm, const void* dt,
                                const float* A_log, const float* init, void* states, float* last,
-                               const float* hstates, float* gh_part, hipStream_t st) {
+                               const float* hstates, float* gh_part, hipStream_t st, void* hbf = nullptr) {
   dim3 grid(state_npb(d) * d.H * d.b);
   hipLaunchKernelGGL((chunk_state_kernel<TX, TB, TB, BF, REV>), grid, dim3(NTHREADS), 0, st,
                      static_cast<const TX*>(X), static_cast<const TB*>(Bm), static_cast<const TB*>(dt),
-                     A_log, init, states, last, hstates, gh_part, d.T, d.H, d.P, d.N, d.G, d.Q);
+                     A_log, init, states, last, hstates, gh_part, static_cast<uint16_t*>(hbf), d.T, d.H, d.P,
+                     d.N, d.G, d.Q);
   return hipGetLastError();
 }
 
@@ -178,13 +184,13 @@ hipError_t launch_chunk_state_fwd(const Dims& d, DType act, const void* x, const
 hipError_t launch_chunk_state_bwd(const Dims& d, DType act, DType dyt, const void* dy,
                                   const void* C, const void* dt, const float* A_log,
                                   const float* states, void* gamma, float* dinit, float* gh_part,
-                                  hipStream_t st) {
+                                  void* hbf, hipStream_t st) {
   if (act == BF16) {
     if (dyt == BF16)
       return launch_state<uint16_t, uint16_t, true, true>(d, dy, C, dt, A_log, nullptr, gamma, dinit,
-                                                          states, gh_part, st);
+                                                          states, gh_part, st, hbf);
     return launch_state<float, uint16_t, true, true>(d, dy, C, dt, A_log, nullptr, gamma, dinit, states,
-                                                     gh_part, st);
+                                                     gh_part, st, hbf);
   }
   if (dyt == BF16)
     return launch_state<uint16_t, float, false, true>(d, dy, C, dt, A_log, nullptr, gamma, dinit, states,

@@ -122,3 +122,26 @@ def test_errors_are_raised_not_hidden():
     A_log = torch.zeros(4, device="cuda:0")
     with pytest.raises(ssd.SSDError, match="multiple of chunk"):
         ssd.ssd_fwd(x, dt, A_log, B, B, A_log, chunk=64)
+
+
+@pytest.mark.parametrize("dy_f32", [True, False])
+def test_repeated_backward_bitwise(dy_f32):
+    # 48 heads per group: long per-workgroup head loops and many workgroup-wide
+    # sums in the decay-gradient pass; every repeat must give the same bits
+    # (a data race in a block reduction showed up here as run-to-run dA_log
+    # differences).
+    cfg = CONFIGS["block"].with_(batch=2)
+    d = make_inputs(cfg)
+    x, dt, B, C = dev(d["x"]), dev(d["dt"]), dev(d["B"]), dev(d["C"])
+    A_log, D = dev(d["A_log"]), dev(d["D"])
+    dy = dev(d["dy"]).float() if dy_f32 else dev(d["dy"])
+    import selective_state_space_mamba_amd as ssd
+    y, fin, cs = ssd.ssd_fwd(x, dt, A_log, B, C, D, chunk=cfg.chunk)
+    first = None
+    for _ in range(6):
+        g = ssd.ssd_bwd(x, dt, A_log, B, C, D, dy, chunk_states=cs, chunk=cfg.chunk)
+        got = {k: host(g[k]) for k in ("dA_log", "ddt", "dD")}
+        if first is None:
+            first = got
+        for k in got:
+            assert np.array_equal(got[k], first[k]), k
