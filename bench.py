@@ -29,9 +29,9 @@ KERNELS_FWD = ["chunk_state_fwd", "chunk_out_fwd"]
 KERNELS_BWD = ["chunk_state_bwd", "chunk_bwd_col", "chunk_bwd_row", "bwd_dt", "bwd_reduce"]
 KERNELS_SHELL = ["conv1d_silu_fwd", "rmsnorm_gated_fwd", "rmsnorm_gated_bwd", "conv1d_silu_bwd"]
 KERNEL_SOURCES = {
-    "chunk_state_fwd": ["ssd_state.hip", "ssd_common.hpp"],
-    "chunk_state_bwd": ["ssd_state.hip", "ssd_common.hpp"],
-    "chunk_out_fwd": ["ssd_chunk_fwd.hip", "ssd_common.hpp"],
+    "chunk_state_fwd": ["ssd_state.hip", "ssd_state_bf16.hip", "ssd_async.hpp", "ssd_common.hpp"],
+    "chunk_state_bwd": ["ssd_state.hip", "ssd_state_bf16.hip", "ssd_async.hpp", "ssd_common.hpp"],
+    "chunk_out_fwd": ["ssd_chunk_fwd.hip", "ssd_fwd_bf16.hip", "ssd_async.hpp", "ssd_common.hpp"],
     "chunk_bwd_col": ["ssd_chunk_bwd.hip", "ssd_bwd_bf16.hip", "ssd_async.hpp", "ssd_common.hpp"],
     "chunk_bwd_row": ["ssd_chunk_bwd.hip", "ssd_bwd_bf16.hip", "ssd_async.hpp", "ssd_common.hpp"],
     "bwd_dt": ["ssd_chunk_bwd.hip", "ssd_common.hpp"],

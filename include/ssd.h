@@ -71,7 +71,10 @@ typedef struct {
 /* Bytes of workspace ssd_fwd (for_backward = 0) or ssd_bwd (for_backward = 1)
  * needs.  has_chunk_states tells whether the caller passes chunk_states (fwd:
  * as an output, bwd: as the saved history); without them the library keeps
- * the chunk states in the workspace.  Returns 0 for an invalid problem. */
+ * the chunk states in the workspace.  bf16 problems (headdim and dstate
+ * multiples of 8) also keep a bf16 copy of the chunk states there, so they
+ * need a workspace even when chunk_states is given.  Returns 0 for an
+ * invalid problem. */
 size_t ssd_workspace_bytes(const ssd_problem* prob, int for_backward, int has_chunk_states);
 
 /* Forward.

@@ -91,7 +91,8 @@ constexpr int64_t kFwdTarget = 512;
 constexpr int64_t kBwdTarget = 256;
 
 struct FwdPlan {
-  size_t states = 0, total = 0;
+  size_t states = 0, hbf = 0, total = 0;
+  bool bf16 = false;  // bf16 output kernel with asynchronous staging (reads a bf16 copy of the states)
 };
 struct BwdPlan {
   size_t states = 0, gamma = 0, hbf = 0, gh = 0, rowM = 0, colE = 0, diagE = 0, Rp = 0, dsoff = 0, dA = 0, dD = 0,
@@ -104,19 +105,24 @@ size_t state_bytes(const ssd::Dims& d) {
   return sizeof(float) * static_cast<size_t>(d.b) * d.nc() * d.H * d.P * d.N;
 }
 
-FwdPlan plan_fwd(const ssd::Dims& d, bool has_states) {
+bool use_bf16_kernels(const ssd::Dims& d, int act, int dyt) {
+  return act == SSD_BF16 && dyt == SSD_BF16 && ssd::bwd_bf16_supported(d);
+}
+
+FwdPlan plan_fwd(const ssd::Dims& d, bool has_states, bool bf16) {
   FwdPlan p;
+  p.bf16 = bf16;
   size_t off = 0;
   if (!has_states) {
     p.states = off;
     off += align_up(state_bytes(d));
   }
+  if (bf16) {
+    p.hbf = off;
+    off += align_up(state_bytes(d) / 2);
+  }
   p.total = off;
   return p;
-}
-
-bool use_bf16_kernels(const ssd::Dims& d, int act, int dyt) {
-  return act == SSD_BF16 && dyt == SSD_BF16 && ssd::bwd_bf16_supported(d);
 }
 
 BwdPlan plan_bwd(const ssd::Dims& d, bool has_states, bool bf16) {
@@ -247,7 +253,7 @@ size_t ssd_workspace_bytes(const ssd_problem* prob, int for_backward, int has_ch
   if (check_problem(prob, &d) != SSD_OK) return 0;
   if (d.b == 0 || d.T == 0) return 0;
   return for_backward ? plan_bwd(d, has_chunk_states != 0, use_bf16_kernels(d, prob->act_dtype, prob->dy_dtype)).total
-                      : plan_fwd(d, has_chunk_states != 0).total;
+                      : plan_fwd(d, has_chunk_states != 0, use_bf16_kernels(d, prob->act_dtype, prob->act_dtype)).total;
 }
 
 int ssd_fwd(const ssd_problem* prob, const void* x, const void* dt, const float* A_log, const void* B,
@@ -275,17 +281,26 @@ int ssd_fwd(const ssd_problem* prob, const void* x, const void* dt, const float*
     }
     return ok();
   }
-  const FwdPlan plan = plan_fwd(d, chunk_states != nullptr);
+  const FwdPlan plan = plan_fwd(d, chunk_states != nullptr, use_bf16_kernels(d, prob->act_dtype, prob->act_dtype));
   if (plan.total > 0 && !workspace) return fail(SSD_ERR_WORKSPACE, "ssd_fwd: workspace is null (%zu bytes needed)", plan.total);
   if (workspace_bytes < plan.total)
     return fail(SSD_ERR_WORKSPACE, "ssd_fwd: workspace of %zu bytes is smaller than the %zu needed", workspace_bytes,
                 plan.total);
   if (workspace && !aligned16(workspace)) return fail(SSD_ERR_ALIGN, "ssd_fwd: workspace is not 16-byte aligned");
   float* states = chunk_states ? chunk_states : at<float>(workspace, plan.states);
-  SSD_LAUNCH(ssd::launch_chunk_state_fwd(d, act, x, B, dt, A_log, init_state, states, final_state, st),
-             "chunk_state_fwd");
-  SSD_LAUNCH(ssd::launch_chunk_out_fwd(d, act, choose_nsplit(d, kFwdTarget), x, B, C, dt, A_log, D, states, y, st),
-             "chunk_out_fwd");
+  void* hbf = plan.bf16 ? at<float>(workspace, plan.hbf) : nullptr;
+  if (plan.bf16)
+    SSD_LAUNCH(ssd::launch_chunk_state_fwd_bf16(d, x, B, dt, A_log, init_state, states, final_state, hbf, st),
+               "chunk_state_fwd");
+  else
+    SSD_LAUNCH(ssd::launch_chunk_state_fwd(d, act, x, B, dt, A_log, init_state, states, final_state, nullptr, st),
+               "chunk_state_fwd");
+  if (plan.bf16)
+    SSD_LAUNCH(ssd::launch_out_fwd_bf16(d, choose_nsplit(d, kFwdTarget), x, B, C, dt, A_log, D, hbf, y, st),
+               "chunk_out_fwd");
+  else
+    SSD_LAUNCH(ssd::launch_chunk_out_fwd(d, act, choose_nsplit(d, kFwdTarget), x, B, C, dt, A_log, D, states, y, st),
+               "chunk_out_fwd");
   return ok();
 }
 
@@ -337,13 +352,22 @@ int ssd_bwd(const ssd_problem* prob, const void* x, const void* dt, const float*
   const float* states = chunk_states;
   if (!states) {
     float* rec = at<float>(workspace, plan.states);
-    SSD_LAUNCH(ssd::launch_chunk_state_fwd(d, act, x, B, dt, A_log, init_state, rec, nullptr, st),
-               "chunk_state_fwd (recompute)");
+    // the same kernel as ssd_fwd picks, so recomputed states match saved ones bitwise
+    if (use_bf16_kernels(d, prob->act_dtype, prob->act_dtype))
+      SSD_LAUNCH(ssd::launch_chunk_state_fwd_bf16(d, x, B, dt, A_log, init_state, rec, nullptr, nullptr, st),
+                 "chunk_state_fwd (recompute)");
+    else
+      SSD_LAUNCH(ssd::launch_chunk_state_fwd(d, act, x, B, dt, A_log, init_state, rec, nullptr, nullptr, st),
+                 "chunk_state_fwd (recompute)");
     states = rec;
   }
-  SSD_LAUNCH(
-      ssd::launch_chunk_state_bwd(d, act, dyt, dy, C, dt, A_log, states, gamma, d_init_state, s.gh_part, hbf, st),
-      "chunk_state_bwd");
+  if (plan.bf16)
+    SSD_LAUNCH(ssd::launch_chunk_state_bwd_bf16(d, dy, C, dt, A_log, states, gamma, d_init_state, s.gh_part, hbf, st),
+               "chunk_state_bwd");
+  else
+    SSD_LAUNCH(
+        ssd::launch_chunk_state_bwd(d, act, dyt, dy, C, dt, A_log, states, gamma, d_init_state, s.gh_part, nullptr, st),
+        "chunk_state_bwd");
   if (plan.bf16) {
     SSD_LAUNCH(ssd::launch_bwd_col_bf16(d, plan.nsplit, x, B, C, dt, dy, A_log, D, gamma, dx,
                                         plan.nsplit > 1 ? s.dB_part : dB, s, st),

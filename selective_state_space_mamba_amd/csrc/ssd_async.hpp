@@ -13,7 +13,8 @@
 //
 // A tile row of CPR 16-byte chunks (CPR * 8 bf16) is stored unpadded with the
 // chunk index XOR-swizzled by a function of the row.  The swizzle keeps both
-// fragment reads below free of bank conflicts, for 32 or 64 LDS banks:
+// fragment reads below free of bank conflicts, for 32 or 64 LDS banks (for
+// CPR = 4, only the transpose read):
 //  * rows(): lane (r, q) reads row m0 + r, chunk kc + q (one 16-byte read):
 //    the MFMA fragment whose k index runs along the row;
 //  * cols(): ds_read_b64_tr_b16 pairs that deliver, to lane (r, q), the 8
@@ -83,8 +84,12 @@ __device__ __forceinline__ void lds_barrier() {
 
 template <int CPR>
 __device__ __forceinline__ int swz(int r) {
-  if constexpr (CPR <= 2) {
+  if constexpr (CPR <= 2 || CPR >= 32) {
     return 0;
+  } else if constexpr (CPR == 4) {
+    // 64-byte rows (read with the transpose read only): rows r and r + 2 of a
+    // group of four share banks, so they take opposite chunk pairs
+    return ((r >> 1) & 1) << 1;
   } else {
     const int b = ((r & 3) << 1) | ((r >> 2) & 1);
     return b ^ (((r >> 3) & 1) * (CPR == 16 ? 8 : 2));

@@ -1,0 +1,285 @@
+// Chunk output of the SSD forward for bf16 operands, with asynchronous LDS
+// staging (ssd_async.hpp).  Same result as chunk_out_fwd_kernel
+// (ssd_chunk_fwd.hip): for the state H_c entering chunk c and s the
+// within-chunk cumsum of dt A (the recurrence of the page-1 reference,
+// burn_dragon_kernel mamba2/backward.rs, ssd_forward_state_history_reference,
+// with the y readout of the block backward),
+//
+//   y_i = sum_{j<=i} exp(s_i - s_j) (C_i . B_j) dt_j x_j + exp(s_i) C_i . H_c^T + D x_i.
+//
+// A workgroup owns the 64 rows i of block ib of one chunk for the heads of one
+// group (or a run of them).  Its 8 waves form two teams; wave (team, wt) owns
+// rows i0 + 16 wt .. +15 and, in every block jb <= ib, the columns
+// j0 + 32 team .. +31.  C_i.B_j for those tiles is formed once (MFMA) and
+// kept in LDS.  A step (one head, one block jb) applies the decay and dt_j,
+// puts the bf16 result in a wave-private LDS strip and accumulates
+// sum_j G_ij x_j over the wave's 32 columns j with MFMA (G and x read down
+// their rows with the LDS transpose read).  Once per head the teams swap the
+// halves of their sums through LDS; each team finishes half of the headdim
+// columns with the incoming-state term (C_i against H_c in bf16) and the skip
+// term.  Workgroup barriers end steps, where the next step's tiles (loaded
+// by all waves while this step computed) become visible.
+//
+// Off the diagonal block every j is below every i, so with s non-increasing
+// L_ij = exp(s_i - s_i0) exp(s_i0 - s_j) (i0 the block's first row): factors
+// <= 1 per row and per column instead of one exponential per element.
+#include "ssd_async.hpp"
+#include "ssd_common.hpp"
+#include "ssd_launch.hpp"
+
+namespace ssd {
+
+namespace {
+constexpr int FW = 8;               // waves per workgroup
+constexpr int FT = FW * WAVE;       // threads per workgroup
+constexpr int FTILE_N = 64 * 256;   // bytes of a 64 x 128 bf16 tile
+constexpr int FTILE_P = 64 * 128;   // bytes of a 64 x 64 bf16 tile
+constexpr int FSTRIP = 32 * 32;     // bytes of a 32 x 16 bf16 strip
+
+// s and dt for t < Q from the dt bits of t = 4l .. 4l+3 (see the backward kernels).
+__device__ __forceinline__ void fwd_scan_store(const uint32_t (&dtb)[4], float A, float* s_out, float* dt_out) {
+  const int l = lane_id(), w = wave_id();
+  float d[4], a[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) d[e] = bf16_bits_to_f32(static_cast<uint16_t>(dtb[e]));
+  a[0] = d[0] * A;
+#pragma unroll
+  for (int e = 1; e < 4; ++e) a[e] = a[e - 1] + d[e] * A;
+  const float incl = wave_scan(a[3]);
+  const float ex = incl - a[3];
+  if ((l >> 4) == w) {
+    *reinterpret_cast<float4*>(s_out + 4 * l) = make_float4(ex + a[0], ex + a[1], ex + a[2], ex + a[3]);
+    *reinterpret_cast<float4*>(dt_out + 4 * l) = make_float4(d[0], d[1], d[2], d[3]);
+  }
+}
+
+// Two MFMA tiles (lane element e at row 4q + e, column 16 tt + r) into a wave
+// strip as bf16 [column][row] (32 x 16).
+__device__ __forceinline__ void fwd_put_strip(lds_char* strip, const f4 (&v)[2]) {
+  const int l = lane_id(), r = l & 15, q = l >> 4;
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt)
+    *(__attribute__((address_space(3))) u32x2*)(strip + (16 * tt + r) * 32 + 8 * q) =
+        u32x2{pack_bf16(v[tt][0], v[tt][1]), pack_bf16(v[tt][2], v[tt][3])};
+}
+}  // namespace
+
+__global__ __launch_bounds__(FT) void out_fwd_bf16_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ Bm, const uint16_t* __restrict__ Cm,
+    const uint16_t* __restrict__ dt, const float* __restrict__ A_log, const float* __restrict__ D,
+    const uint16_t* __restrict__ hbf, uint16_t* __restrict__ y, int T, int H, int P, int N, int G, int Q,
+    int nsplit) {
+  __shared__ __attribute__((aligned(1024))) char sC_[FTILE_N];          // C rows i of block ib
+  __shared__ __attribute__((aligned(1024))) char sX0_[FTILE_P];         // x rows j, even steps
+  __shared__ __attribute__((aligned(1024))) char sX1_[FTILE_P];         // x rows j, odd steps
+  __shared__ __attribute__((aligned(1024))) char sH_[FTILE_N];          // H_c [p][n] (bf16); B tile slot
+  __shared__ __attribute__((aligned(1024))) char sXch_[FTILE_N];        // y halves; B tile slot
+  __shared__ __attribute__((aligned(1024))) char sG_[FW * FSTRIP];      // per-wave G strips [j][i]
+  __shared__ f4 sCB[NBMAX][2][FW][WAVE];                                // C.B^T, lane-linear
+  __shared__ __attribute__((aligned(16))) float sS[2][QMAX];
+  __shared__ __attribute__((aligned(16))) float sDt[2][QMAX];
+  lds_char* const sC = lds_ptr(sC_);
+  lds_char* const sX[2] = {lds_ptr(sX0_), lds_ptr(sX1_)};
+  lds_char* const sH = lds_ptr(sH_);
+  lds_char* const sXch = lds_ptr(sXch_);
+  lds_char* const sG = lds_ptr(sG_);
+
+  const int nc = T / Q, nb = (Q + BQ - 1) / BQ;
+  const int hpg = H / G, hps = hpg / nsplit;
+  int idx = xcd_logical_block(blockIdx.x, gridDim.x);
+  const int ib = nb - 1 - idx % nb;  // the block with the most columns j first
+  idx /= nb;
+  const int sp = idx % nsplit;
+  idx /= nsplit;
+  const int g = idx % G;
+  idx /= G;
+  const int c = idx % nc;
+  const int bi = idx / nc;
+
+  const int l = lane_id(), w = wave_id(), r = l & 15, q = l >> 4;
+  const int team = w >> 2, wt = w & 3;
+  const int tj = 32 * team;
+  const int64_t row0 = static_cast<int64_t>(bi) * T + static_cast<int64_t>(c) * Q;
+  const int i0 = ib * BQ, vi = min(BQ, Q - i0);
+  const int nj = ib + 1;
+  const int64_t HP = static_cast<int64_t>(H) * P, GN = static_cast<int64_t>(G) * N;
+  const uint32_t HPb = static_cast<uint32_t>(HP) * 2, GNb = static_cast<uint32_t>(GN) * 2;
+  const uint32_t goff = static_cast<uint32_t>(g) * N * 2;
+  const int pch = P >> 3, nch = N >> 3;
+  const int kn = (N + 31) >> 5;
+  const i32x4 rx = make_rsrc(x + row0 * HP);
+  const i32x4 rb = make_rsrc(Bm + row0 * GN);
+  const i32x4 rc = make_rsrc(Cm + row0 * GN);
+  const i32x4 rh = make_rsrc(hbf + (static_cast<int64_t>(bi) * nc + c) * HP * N);
+  const __amdgpu_buffer_rsrc_t rdt = make_rsrc_ptr(dt + row0 * H);
+  auto head = [&](int hh) { return g * hpg + sp * hps + hh; };
+
+  uint32_t dtb[4];
+  auto load_dt = [&](int hh) {
+    const int h = head(hh);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int t = 4 * l + e;
+      const uint32_t off = (t < Q) ? static_cast<uint32_t>(t) * H * 2 : OOB_OFFSET;
+      dtb[e] = __builtin_amdgcn_raw_buffer_load_b16(rdt, off, h * 2, 0);
+    }
+  };
+  auto load_x = [&](int hh, int jb, lds_char* dst) {
+    const int j0 = jb * BQ;
+    tile_async<64, 8, FW>(dst, rx, j0 * HPb + head(hh) * P * 2, HPb, min(BQ, Q - j0), pch);
+  };
+  auto load_b = [&](int jb, lds_char* dst) {
+    const int j0 = jb * BQ;
+    tile_async<64, 16, FW>(dst, rb, j0 * GNb + goff, GNb, min(BQ, Q - j0), nch);
+  };
+
+  // ---- C rows of block ib, then C.B^T for every block jb <= ib (B tiles two at a time)
+  tile_async<64, 16, FW>(sC, rc, i0 * GNb + goff, GNb, vi, nch);
+  load_dt(0);
+#pragma unroll
+  for (int jb0 = 0; jb0 < NBMAX; jb0 += 2) {
+    if (jb0 < nj) {
+      load_b(jb0, sXch);
+      if (jb0 + 1 < nj) load_b(jb0 + 1, sH);
+      wait_vm<0>();
+      __syncthreads();
+#pragma unroll
+      for (int d = 0; d < 2; ++d) {
+        const int jb = jb0 + d;
+        if (jb < nj) {
+          const lds_char* bt = d ? sH : sXch;
+          f4 cb[2];
+          zero(cb);
+          for (int ks = 0; ks < kn; ++ks) {
+            const bf16x8 a = frag_rows<16>(sC, 16 * wt, 4 * ks);
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) cb[tt] = mfma(a, frag_rows<16>(bt, tj + 16 * tt, 4 * ks), cb[tt]);
+          }
+          sCB[jb][0][w][l] = cb[0];
+          sCB[jb][1][w][l] = cb[1];
+        }
+      }
+      __syncthreads();
+    }
+  }
+  load_x(0, 0, sX[0]);
+  wait_vm<0>();
+  fwd_scan_store(dtb, -__expf(A_log[head(0)]), sS[0], sDt[0]);
+  __syncthreads();
+
+  for (int hh = 0; hh < hps; ++hh) {
+    const int h = head(hh), hb = hh & 1;
+    const float* sSh = sS[hb];
+    const float* sDh = sDt[hb];
+    float si[4], rf[4];
+    const float sref = sSh[i0];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int iq = i0 + 16 * wt + 4 * q + e;
+      si[e] = sSh[min(iq, Q - 1)];
+      rf[e] = (iq < Q) ? __expf(si[e] - sref) : 0.f;
+    }
+    f4 ya[4];  // sum over this team's columns j of G_ij x_j: rows i, columns p = 16 pt + r
+    zero(ya);
+    uint32_t xsk[4];  // x_i at columns p = 32 team + r and 32 team + 16 + r (bf16 pair)
+
+#pragma unroll
+    for (int jb = 0; jb < NBMAX; ++jb) {
+      if (jb < nj) {
+        const int j0 = jb * BQ;
+        const lds_char* xt = sX[jb & 1];
+        if (jb + 1 < nj) load_x(hh, jb + 1, sX[(jb + 1) & 1]);
+        if (jb == 0) {
+          tile_async<64, 16, FW>(sH, rh, h * P * N * 2, N * 2, P, nch);
+          if (hh + 1 < hps) load_dt(hh + 1);
+        }
+        const f4 cbt[2] = {sCB[jb][0][w][l], sCB[jb][1][w][l]};
+        f4 gv[2];
+        if (jb == ib) {
+#pragma unroll
+          for (int tt = 0; tt < 2; ++tt) {
+            const int jq = j0 + tj + 16 * tt + r;
+            const float sj = sSh[min(jq, Q - 1)];
+            const float dtj = (jq < Q) ? sDh[jq] : 0.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int iq = i0 + 16 * wt + 4 * q + e;
+              const float L = (iq < Q && jq <= iq) ? __expf(si[e] - sj) : 0.f;
+              gv[tt][e] = L * dtj * cbt[tt][e];
+            }
+          }
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int il = 16 * wt + 4 * q + e;
+            xsk[e] = pack_bf16(tile_elem<8>(xt, il, 32 * team + r), tile_elem<8>(xt, il, 32 * team + 16 + r));
+          }
+        } else {
+#pragma unroll
+          for (int tt = 0; tt < 2; ++tt) {
+            const int jq = j0 + tj + 16 * tt + r;
+            const float cfd = __expf(sref - sSh[jq]) * sDh[jq];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) gv[tt][e] = rf[e] * cfd * cbt[tt][e];
+          }
+        }
+        fwd_put_strip(sG + w * FSTRIP, gv);
+        {
+          const bf16x8 a = frag_cols<2>(sG + w * FSTRIP, 0, 0);
+#pragma unroll
+          for (int pt = 0; pt < 4; ++pt) ya[pt] = mfma(a, frag_cols<8>(xt, tj, 16 * pt), ya[pt]);
+        }
+        wait_vm<0>();
+        __syncthreads();
+      }
+    }
+
+    // ---- finish head hh; the next head's first x tile starts loading
+    if (hh + 1 < hps) load_x(hh + 1, 0, sX[0]);
+    // hand the other team's headdim columns to it
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int pt = 2 * (1 - team) + k;
+      *(__attribute__((address_space(3))) f4*)(sXch + ((wt * 4 + pt) * WAVE + l) * 16) = ya[pt];
+    }
+    f4 yo[2];  // C_i . H_c^T: rows i, columns p = 16 (2 team + k) + r
+    zero(yo);
+    for (int ks = 0; ks < kn; ++ks) {
+      const bf16x8 a = frag_rows<16>(sC, 16 * wt, 4 * ks);
+#pragma unroll
+      for (int k = 0; k < 2; ++k) yo[k] = mfma(a, frag_rows<16>(sH, 16 * (2 * team + k), 4 * ks), yo[k]);
+    }
+    lds_barrier();
+    const float Dh = D[h];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int pt = 2 * team + k;
+      const f4 other = *(const __attribute__((address_space(3))) f4*)(sXch + ((wt * 4 + pt) * WAVE + l) * 16);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int iq = i0 + 16 * wt + 4 * q + e, p = 16 * pt + r;
+        const uint32_t pk = xsk[e];
+        const float xv = __uint_as_float(k ? (pk & 0xFFFF0000u) : (pk << 16));
+        const float ex = __expf(si[e]);
+        if (iq < Q && p < P)
+          y[(row0 + iq) * HP + static_cast<int64_t>(h) * P + p] =
+              f32_to_bf16_bits(ya[pt][e] + other[e] + ex * yo[k][e] + Dh * xv);
+      }
+    }
+    if (hh + 1 < hps) fwd_scan_store(dtb, -__expf(A_log[head(hh + 1)]), sS[hb ^ 1], sDt[hb ^ 1]);
+    wait_vm<0>();
+    __syncthreads();
+  }
+}
+
+hipError_t launch_out_fwd_bf16(const Dims& d, int nsplit, const void* x, const void* B, const void* C,
+                               const void* dt, const float* A_log, const float* D, const void* hbf, void* y,
+                               hipStream_t st) {
+  const int64_t nblk = static_cast<int64_t>(d.b) * d.nc() * d.G * nsplit * d.nb();
+  hipLaunchKernelGGL(out_fwd_bf16_kernel, dim3(nblk), dim3(FT), 0, st, static_cast<const uint16_t*>(x),
+                     static_cast<const uint16_t*>(B), static_cast<const uint16_t*>(C),
+                     static_cast<const uint16_t*>(dt), A_log, D, static_cast<const uint16_t*>(hbf),
+                     static_cast<uint16_t*>(y), d.T, d.H, d.P, d.N, d.G, d.Q, nsplit);
+  return hipGetLastError();
+}
+
+}  // namespace ssd

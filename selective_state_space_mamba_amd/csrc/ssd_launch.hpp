@@ -21,10 +21,10 @@ inline int state_npb(const Dims& d) { return (d.P + STATE_PB - 1) / STATE_PB; }
 
 // Forward state passing: states[b,c,h] = state entering chunk c, final = state
 // after the last chunk.  `init` may be null (zero initial state), `final_state`
-// may be null.
+// may be null; hbf (nullable) receives the states rounded to bf16.
 hipError_t launch_chunk_state_fwd(const Dims& d, DType act, const void* x, const void* B,
                                   const void* dt, const float* A_log, const float* init,
-                                  float* states, float* final_state, hipStream_t st);
+                                  float* states, float* final_state, void* hbf, hipStream_t st);
 
 // Reverse state-gradient pass: gamma[b,c,h] = gradient reaching the state that
 // leaves chunk c, stored in the MFMA operand type (bf16 when act is BF16, else
@@ -35,6 +35,19 @@ hipError_t launch_chunk_state_bwd(const Dims& d, DType act, DType dyt, const voi
                                   const void* C, const void* dt, const float* A_log,
                                   const float* states, void* gamma, float* dinit, float* gh_part,
                                   void* hbf, hipStream_t st);
+
+// bf16 operands with asynchronous LDS staging (bwd_bf16_supported shapes):
+// the chunk-state passes (same outputs as launch_chunk_state_fwd/_bwd) and the
+// chunk output, which reads the bf16 copy of the states.
+hipError_t launch_chunk_state_fwd_bf16(const Dims& d, const void* x, const void* B, const void* dt,
+                                       const float* A_log, const float* init, float* states, float* final_state,
+                                       void* hbf, hipStream_t st);
+hipError_t launch_chunk_state_bwd_bf16(const Dims& d, const void* dy, const void* C, const void* dt,
+                                       const float* A_log, const float* states, void* gamma, float* dinit,
+                                       float* gh_part, void* hbf, hipStream_t st);
+hipError_t launch_out_fwd_bf16(const Dims& d, int nsplit, const void* x, const void* B, const void* C,
+                               const void* dt, const float* A_log, const float* D, const void* hbf, void* y,
+                               hipStream_t st);
 
 hipError_t launch_chunk_out_fwd(const Dims& d, DType act, int nsplit, const void* x, const void* B,
                                 const void* C, const void* dt, const float* A_log, const float* D,

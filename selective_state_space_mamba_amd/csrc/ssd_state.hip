@@ -131,6 +131,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void chunk_state_kernel(
         const int p = p0 + 4 * q + i, n = 32 * w + 16 * t + r;
         if (p < P && n < N) {
           if (states_out) store_f(states_out, sbase + p * N + n, st[t][i]);
+          if (!REV && hbf) hbf[sbase + p * N + n] = f32_to_bf16_bits(st[t][i]);
           if (REV) {
             const float hv = hstates[sbase + p * N + n];
             gh += st[t][i] * hv;
@@ -173,10 +174,10 @@ static hipError_t launch_state(const Dims& d, const void* X, const void* Bm, con
 
 hipError_t launch_chunk_state_fwd(const Dims& d, DType act, const void* x, const void* B,
                                   const void* dt, const float* A_log, const float* init,
-                                  float* states, float* final_state, hipStream_t st) {
+                                  float* states, float* final_state, void* hbf, hipStream_t st) {
   if (act == BF16)
     return launch_state<uint16_t, uint16_t, true, false>(d, x, B, dt, A_log, init, states, final_state,
-                                                         nullptr, nullptr, st);
+                                                         nullptr, nullptr, st, hbf);
   return launch_state<float, float, false, false>(d, x, B, dt, A_log, init, states, final_state, nullptr,
                                                   nullptr, st);
 }

@@ -1,0 +1,256 @@
+// Inter-chunk state passing (forward) and the reverse-time state-gradient pass
+// (backward) for bf16 operands, with asynchronous LDS staging (ssd_async.hpp).
+// Same recurrences and outputs as chunk_state_kernel (ssd_state.hip):
+//
+//   H_{c+1}   = exp(s_end) H_c + sum_j exp(s_end - s_j) dt_j x_j (outer) B_j
+//   Gamma_c   = exp(s_end) Gamma_{c+1} + sum_i exp(s_i) dy_i (outer) C_i
+//
+// (page-1 reference, burn_dragon_kernel mamba2/backward.rs: the recurrence of
+// ssd_forward_state_history_reference and the carry of ssd_backward_reference,
+// unrolled over one chunk).
+//
+// A workgroup owns 32 headdim rows of one (batch, head); wave w holds rows
+// p0 + 16 (w % 2) .. +15 and d_state columns 32 (w / 2) .. +31 of the state
+// in registers and walks the chunks in order (or in reverse).  Per chunk the
+// weighted sum is one MFMA contraction over time: the x (or dy) tile arrives
+// with time along its rows and is read down them with the LDS transpose read,
+// each fragment scaled by the per-step weights before the MFMA; the B (or C)
+// tile likewise.  Tiles come in 128-step slabs, double-buffered and copied
+// asynchronously while the previous slab computes, together with (backward)
+// the f32 state tile H_c; the chunk's dt values are prefetched into registers.
+// Every wave computes the within-chunk scan itself (DPP) into its own weight
+// row.
+#include "ssd_async.hpp"
+#include "ssd_common.hpp"
+#include "ssd_launch.hpp"
+
+namespace ssd {
+
+namespace {
+constexpr int SW = 8;              // waves per workgroup
+constexpr int ST = SW * WAVE;      // threads
+constexpr int SSJ = 128;           // time steps per slab
+constexpr int SPB = 32;            // headdim rows per workgroup
+constexpr int XSLAB = SSJ * 64;    // bytes of a 128 x 32 bf16 slab
+constexpr int BSLAB = SSJ * 256;   // bytes of a 128 x 128 bf16 slab
+constexpr int HTILE = SPB * 512;   // bytes of a 32 x 128 f32 state tile
+
+__device__ __forceinline__ bf16x8 scale_frag(bf16x8 a, const float* w) {
+  const float4 w0 = *reinterpret_cast<const float4*>(w);
+  const float4 w1 = *reinterpret_cast<const float4*>(w + 4);
+  const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+  bf16x8 o;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] = static_cast<__bf16>(static_cast<float>(a[e]) * wv[e]);
+  return o;
+}
+
+// Sum over all 64 lanes of the wave (the row sums end in lanes 15, 31, 47, 63).
+__device__ __forceinline__ float wave_total(float v) {
+  const int b = __builtin_bit_cast(int, row_sum16(v));
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 15)) +
+         __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 31)) +
+         __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 47)) +
+         __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 63));
+}
+}  // namespace
+
+template <bool REV>
+__global__ __launch_bounds__(ST) void chunk_state_bf16_kernel(
+    const uint16_t* __restrict__ X,     // fwd: x; bwd: dy       [b,T,H,P]
+    const uint16_t* __restrict__ Bm,    // fwd: B; bwd: C        [b,T,G,N]
+    const uint16_t* __restrict__ dt,    // [b,T,H]
+    const float* __restrict__ A_log,    // [H]
+    const float* __restrict__ init,     // fwd: initial state (nullable)
+    float* __restrict__ states_f32,     // fwd: H_c [b,nc,H,P,N]
+    uint16_t* __restrict__ states_bf,   // fwd: H_c in bf16 (nullable); bwd: Gamma_{c+1} in bf16
+    float* __restrict__ last_out,       // fwd: final state; bwd: d(initial state) (nullable)
+    const float* __restrict__ hstates,  // bwd: H_c
+    float* __restrict__ gh_part,        // bwd: [b,nc,H,ceil(P/16)] partial <Gamma_{c+1}, H_c>
+    uint16_t* __restrict__ hbf_out,     // bwd: H_c in bf16 (nullable)
+    int T, int H, int P, int N, int G, int Q) {
+  __shared__ __attribute__((aligned(1024))) char sX_[2 * XSLAB];
+  __shared__ __attribute__((aligned(1024))) char sB_[2 * BSLAB];
+  __shared__ __attribute__((aligned(1024))) char sH_[REV ? 2 * HTILE : 16];  // bwd: H_c (f32), two chunks
+  __shared__ __attribute__((aligned(16))) float sWt[SW][QMAX];                // per-wave step weights
+  __shared__ float sGh[2][SW];
+  lds_char* const sX = lds_ptr(sX_);
+  lds_char* const sB = lds_ptr(sB_);
+  lds_char* const sH = lds_ptr(sH_);
+
+  const int npb = (P + SPB - 1) / SPB, npb16 = (P + 15) / 16;
+  const int lb = xcd_logical_block(blockIdx.x, gridDim.x);
+  const int pb = lb % npb, h = (lb / npb) % H, bi = lb / (npb * H);
+  const int p0 = pb * SPB;
+  const int g = h / (H / G);
+  const int nc = T / Q;
+  const int nsl = (Q + SSJ - 1) / SSJ;
+  const float A = -__expf(A_log[h]);
+  const int l = lane_id(), w = wave_id(), r = l & 15, q = l >> 4;
+  const int pw = w & 1, nw = w >> 1;
+  const int64_t HP = static_cast<int64_t>(H) * P, GN = static_cast<int64_t>(G) * N;
+  const int64_t PN = static_cast<int64_t>(P) * N;
+  const uint32_t HPb = static_cast<uint32_t>(HP) * 2, GNb = static_cast<uint32_t>(GN) * 2;
+  const int pch = min(4, (P - p0) >> 3), nch = N >> 3;
+  const __amdgpu_buffer_rsrc_t rdt = make_rsrc_ptr(dt + static_cast<int64_t>(bi) * T * H);
+  float* const wts = sWt[w];
+
+  f4 st[2];  // rows p = p0 + 16 pw + 4q + e, columns n = 32 nw + 16 t + r
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int p = p0 + 16 * pw + 4 * q + e, n = 32 * nw + 16 * t + r;
+      st[t][e] = (!REV && init && p < P && n < N) ? init[(static_cast<int64_t>(bi) * H + h) * PN + p * N + n] : 0.f;
+    }
+
+  auto chunk_of = [&](int it) { return REV ? nc - 1 - it : it; };
+  uint32_t dtb[4];  // dt bits of t = 4l .. 4l+3 of the next chunk to scan
+  // slab sl of chunk it; with the first slab also the chunk's dt and (bwd) H_c
+  auto load_slab = [&](int it, int sl) {
+    const int c = chunk_of(it);
+    const int64_t row0 = static_cast<int64_t>(bi) * T + static_cast<int64_t>(c) * Q + sl * SSJ;
+    const int vr = min(SSJ, Q - sl * SSJ);
+    const int buf = (it * nsl + sl) & 1;
+    tile_async<SSJ, 4, SW>(sX + buf * XSLAB, make_rsrc(X + row0 * HP), h * P * 2 + p0 * 2, HPb, vr, pch);
+    tile_async<SSJ, 16, SW>(sB + buf * BSLAB, make_rsrc(Bm + row0 * GN), g * N * 2, GNb, vr, nch);
+    if (sl == 0) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = 4 * l + e;
+        const uint32_t off = (t < Q) ? static_cast<uint32_t>((c * Q + t) * H) * 2 : OOB_OFFSET;
+        dtb[e] = __builtin_amdgcn_raw_buffer_load_b16(rdt, off, h * 2, 0);
+      }
+      if constexpr (REV) {
+        const int64_t sbase = ((static_cast<int64_t>(bi) * nc + c) * H + h) * PN + static_cast<int64_t>(p0) * N;
+        tile_async<SPB, 32, SW>(sH + (it & 1) * HTILE, make_rsrc(hstates + sbase), 0, N * 4, P - p0, N >> 2);
+      }
+    }
+  };
+
+  load_slab(0, 0);
+  for (int it = 0; it < nc; ++it) {
+    const int c = chunk_of(it);
+    f4 acc[2];
+    zero(acc);
+    float s_end = 0.f;
+    for (int sl = 0; sl < nsl; ++sl) {
+      wait_vm<0>();
+      __syncthreads();  // slab (it, sl) visible; the other buffer is free
+      if (sl == 0) {
+        // this chunk's step weights (every wave computes the scan itself)
+        float d[4], a[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) d[e] = bf16_bits_to_f32(static_cast<uint16_t>(dtb[e]));
+        a[0] = d[0] * A;
+#pragma unroll
+        for (int e = 1; e < 4; ++e) a[e] = a[e - 1] + d[e] * A;
+        const float incl = wave_scan(a[3]);
+        const float ex = incl - a[3];
+        const int last = Q - 1;
+        s_end = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ex + a[last & 3]), last >> 2));
+        float wv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float s = ex + a[e];
+          wv[e] = (4 * l + e < Q) ? (REV ? __expf(s) : __expf(s_end - s) * d[e]) : 0.f;
+        }
+        *reinterpret_cast<float4*>(wts + 4 * l) = make_float4(wv[0], wv[1], wv[2], wv[3]);
+      }
+      // the next slab (or the next chunk's first, with its dt) starts loading
+      if (sl + 1 < nsl)
+        load_slab(it, sl + 1);
+      else if (it + 1 < nc)
+        load_slab(it + 1, 0);
+      const int buf = (it * nsl + sl) & 1;
+      const lds_char* xs = sX + buf * XSLAB;
+      const lds_char* bs = sB + buf * BSLAB;
+      const int kw = min(SSJ, Q - sl * SSJ);
+      for (int k0 = 0; k0 < kw; k0 += 32) {
+        const bf16x8 ax = scale_frag(frag_cols<4>(xs, k0, 16 * pw), wts + sl * SSJ + k0 + 8 * q);
+#pragma unroll
+        for (int t = 0; t < 2; ++t) acc[t] = mfma(ax, frag_cols<16>(bs, k0, 32 * nw + 16 * t), acc[t]);
+      }
+    }
+
+    // chunk end
+    const float decay = __expf(s_end);
+    const int64_t sbase = ((static_cast<int64_t>(bi) * nc + c) * H + h) * PN;
+    const float* ht = reinterpret_cast<const float*>(sH_ + (it & 1) * HTILE);
+    float gh = 0.f;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int pl = 16 * pw + 4 * q + e, p = p0 + pl, n = 32 * nw + 16 * t + r;
+        if (p < P && n < N) {
+          const int64_t o = sbase + p * N + n;
+          if constexpr (!REV) {
+            states_f32[o] = st[t][e];
+            if (states_bf) states_bf[o] = f32_to_bf16_bits(st[t][e]);
+          } else {
+            const float hv = ht[pl * NMAX + n];  // tile rows are 128 floats
+            states_bf[o] = f32_to_bf16_bits(st[t][e]);
+            gh += st[t][e] * hv;
+            if (hbf_out) hbf_out[o] = f32_to_bf16_bits(hv);
+          }
+        }
+        st[t][e] = decay * st[t][e] + acc[t][e];
+      }
+    if constexpr (REV) {
+      // per 16-row headdim block (waves with the same pw), summed after the next barrier
+      gh = wave_total(gh);
+      if (l == 0) sGh[it & 1][w] = gh;
+      if (it > 0 && threadIdx.x < 2) {
+        const int cp = chunk_of(it - 1), pbi = 2 * pb + threadIdx.x;
+        const float* v = sGh[(it - 1) & 1];
+        if (pbi < npb16)
+          gh_part[((static_cast<int64_t>(bi) * nc + cp) * H + h) * npb16 + pbi] =
+              v[threadIdx.x] + v[threadIdx.x + 2] + v[threadIdx.x + 4] + v[threadIdx.x + 6];
+      }
+    }
+  }
+  if constexpr (REV) {
+    __syncthreads();
+    if (threadIdx.x < 2) {
+      const int cp = chunk_of(nc - 1), pbi = 2 * pb + threadIdx.x;
+      const float* v = sGh[(nc - 1) & 1];
+      if (pbi < npb16)
+        gh_part[((static_cast<int64_t>(bi) * nc + cp) * H + h) * npb16 + pbi] =
+            v[threadIdx.x] + v[threadIdx.x + 2] + v[threadIdx.x + 4] + v[threadIdx.x + 6];
+    }
+  }
+  if (last_out) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int p = p0 + 16 * pw + 4 * q + e, n = 32 * nw + 16 * t + r;
+        if (p < P && n < N) last_out[(static_cast<int64_t>(bi) * H + h) * PN + p * N + n] = st[t][e];
+      }
+  }
+}
+
+hipError_t launch_chunk_state_fwd_bf16(const Dims& d, const void* x, const void* B, const void* dt,
+                                       const float* A_log, const float* init, float* states, float* final_state,
+                                       void* hbf, hipStream_t st) {
+  const int64_t nblk = static_cast<int64_t>(d.b) * d.H * ((d.P + SPB - 1) / SPB);
+  hipLaunchKernelGGL(chunk_state_bf16_kernel<false>, dim3(nblk), dim3(ST), 0, st, static_cast<const uint16_t*>(x),
+                     static_cast<const uint16_t*>(B), static_cast<const uint16_t*>(dt), A_log, init, states,
+                     static_cast<uint16_t*>(hbf), final_state, nullptr, nullptr, nullptr, d.T, d.H, d.P, d.N, d.G,
+                     d.Q);
+  return hipGetLastError();
+}
+
+hipError_t launch_chunk_state_bwd_bf16(const Dims& d, const void* dy, const void* C, const void* dt,
+                                       const float* A_log, const float* states, void* gamma, float* dinit,
+                                       float* gh_part, void* hbf, hipStream_t st) {
+  const int64_t nblk = static_cast<int64_t>(d.b) * d.H * ((d.P + SPB - 1) / SPB);
+  hipLaunchKernelGGL(chunk_state_bf16_kernel<true>, dim3(nblk), dim3(ST), 0, st, static_cast<const uint16_t*>(dy),
+                     static_cast<const uint16_t*>(C), static_cast<const uint16_t*>(dt), A_log, nullptr, nullptr,
+                     static_cast<uint16_t*>(gamma), dinit, states, gh_part, static_cast<uint16_t*>(hbf), d.T, d.H,
+                     d.P, d.N, d.G, d.Q);
+  return hipGetLastError();
+}
+
+}  // namespace ssd
