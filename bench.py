@@ -38,6 +38,16 @@ KERNEL_SOURCES = {
 }
 
 
+# Device kernels behind each profiled launch (bf16 variant first).
+DEVICE_KERNELS = {
+    "chunk_state_fwd": ("chunk_state_bf16_kernel", "chunk_state_kernel"),
+    "chunk_state_bwd": ("chunk_state_bf16_kernel", "chunk_state_kernel"),
+    "chunk_out_fwd": ("out_fwd_bf16_kernel", "chunk_out_fwd_kernel"),
+    "chunk_bwd_col": ("bwd_col_bf16_kernel", "chunk_bwd_col_kernel"),
+    "chunk_bwd_row": ("bwd_row_bf16_kernel", "chunk_bwd_row_kernel"),
+}
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -127,7 +137,9 @@ def write_counter_summary(fetch_dir: str, write_dir: str, kernel: str, workload:
     out = {}
     for label, d, counter in (("fetch", fetch_dir, "FETCH_SIZE"), ("write", write_dir, "WRITE_SIZE")):
         rows = [r for r in _counter_rows(d) if r["Counter_Name"] == counter]
-        kv = [float(r["Counter_Value"]) for r in rows if kernel + "_kernel" in r["Kernel_Name"]]
+        names = DEVICE_KERNELS.get(kernel, (kernel + "_kernel",))
+        kv = [float(r["Counter_Value"]) for r in rows if any(n + "(" in r["Kernel_Name"] or n + "<" in r["Kernel_Name"]
+                                                             for n in names)]
         copies = sorted(float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"])
         if not kv or not copies:
             raise SystemExit(f"no {counter} rows for {kernel} or for the calibration copy in {d}")
