@@ -79,9 +79,11 @@ int check_problem(const ssd_problem* p, ssd::Dims* d) {
 }
 
 // Heads of a group are split over this many workgroups so that one launch has
-// at least `target` workgroups (never more splits than heads per group).
-int choose_nsplit(const ssd::Dims& d, int64_t target) {
-  const int64_t base = static_cast<int64_t>(d.b) * d.nc() * d.G * d.nb();
+// at least `target` workgroups (never more splits than heads per group).  The
+// bf16 kernels give one workgroup two 64-row blocks of a chunk (paired so that
+// every workgroup has the same work), the general ones one block.
+int choose_nsplit(const ssd::Dims& d, int64_t target, bool paired) {
+  const int64_t base = static_cast<int64_t>(d.b) * d.nc() * d.G * (paired ? (d.nb() + 1) / 2 : d.nb());
   const int hpg = d.hpg();
   for (int s = 1; s <= hpg; ++s)
     if (hpg % s == 0 && base * s >= target) return s;
@@ -127,7 +129,7 @@ FwdPlan plan_fwd(const ssd::Dims& d, bool has_states, bool bf16) {
 
 BwdPlan plan_bwd(const ssd::Dims& d, bool has_states, bool bf16) {
   BwdPlan p;
-  p.nsplit = choose_nsplit(d, kBwdTarget);
+  p.nsplit = choose_nsplit(d, kBwdTarget, bf16);
   p.bf16 = bf16;
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -296,10 +298,10 @@ int ssd_fwd(const ssd_problem* prob, const void* x, const void* dt, const float*
     SSD_LAUNCH(ssd::launch_chunk_state_fwd(d, act, x, B, dt, A_log, init_state, states, final_state, nullptr, st),
                "chunk_state_fwd");
   if (plan.bf16)
-    SSD_LAUNCH(ssd::launch_out_fwd_bf16(d, choose_nsplit(d, kFwdTarget), x, B, C, dt, A_log, D, hbf, y, st),
+    SSD_LAUNCH(ssd::launch_out_fwd_bf16(d, choose_nsplit(d, kFwdTarget, true), x, B, C, dt, A_log, D, hbf, y, st),
                "chunk_out_fwd");
   else
-    SSD_LAUNCH(ssd::launch_chunk_out_fwd(d, act, choose_nsplit(d, kFwdTarget), x, B, C, dt, A_log, D, states, y, st),
+    SSD_LAUNCH(ssd::launch_chunk_out_fwd(d, act, choose_nsplit(d, kFwdTarget, false), x, B, C, dt, A_log, D, states, y, st),
                "chunk_out_fwd");
   return ok();
 }

@@ -100,15 +100,23 @@ __global__ __launch_bounds__(BT) void bwd_col_bf16_kernel(
 
   const int nc = T / Q, nb = (Q + BQ - 1) / BQ;
   const int hpg = H / G, hps = hpg / nsplit;
+  // blocks k and nb - 1 - k share a workgroup, one after the other, so that
+  // every workgroup has the same number of (row block, column block) pairs
+  const int npair = (nb + 1) >> 1;
   int idx = xcd_logical_block(blockIdx.x, gridDim.x);
-  const int jb = idx % nb;  // block 0 (the most rows i) first
-  idx /= nb;
+  const int kpair = idx % npair;
+  idx /= npair;
   const int sp = idx % nsplit;
   idx /= nsplit;
   const int g = idx % G;
   idx /= G;
   const int c = idx % nc;
   const int bi = idx / nc;
+
+  for (int pass = 0; pass < 2; ++pass) {
+  const int jb = pass ? nb - 1 - kpair : kpair;  // the block with the most rows i first
+  if (pass && jb == kpair) break;
+  if (pass) __syncthreads();
 
   const int l = lane_id(), w = wave_id(), r = l & 15, q = l >> 4;
   const int team = w >> 2, wt = w & 3;
@@ -397,7 +405,7 @@ __global__ __launch_bounds__(BT) void bwd_col_bf16_kernel(
       __syncthreads();
     }
   }
-  const int64_t batch = gridDim.x / (nb * nsplit * G * nc);
+  const int64_t batch = gridDim.x / (npair * nsplit * G * nc);
   float* dBo = dB_out + static_cast<int64_t>(sp) * batch * T * GN;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
@@ -408,6 +416,7 @@ __global__ __launch_bounds__(BT) void bwd_col_bf16_kernel(
       if (jq < Q && n < N) dBo[(row0 + jq) * GN + static_cast<int64_t>(g) * N + n] = dbp[k][e] + dbs[k][e];
     }
   }
+  }  // pass
 }
 
 // Row kernel: a workgroup owns the 64 rows i of block ib of one chunk for the
@@ -446,15 +455,22 @@ __global__ __launch_bounds__(BT) void bwd_row_bf16_kernel(
 
   const int nc = T / Q, nb = (Q + BQ - 1) / BQ;
   const int hpg = H / G, hps = hpg / nsplit;
+  // blocks nb - 1 - k and k share a workgroup, one after the other
+  const int npair = (nb + 1) >> 1;
   int idx = xcd_logical_block(blockIdx.x, gridDim.x);
-  const int ib = nb - 1 - idx % nb;  // the block with the most columns j first
-  idx /= nb;
+  const int kpair = idx % npair;
+  idx /= npair;
   const int sp = idx % nsplit;
   idx /= nsplit;
   const int g = idx % G;
   idx /= G;
   const int c = idx % nc;
   const int bi = idx / nc;
+
+  for (int pass = 0; pass < 2; ++pass) {
+  const int ib = pass ? kpair : nb - 1 - kpair;  // the block with the most columns j first
+  if (pass && ib == nb - 1 - kpair) break;
+  if (pass) __syncthreads();
 
   const int l = lane_id(), w = wave_id(), r = l & 15, q = l >> 4;
   const int team = w >> 2, wt = w & 3;
@@ -692,7 +708,7 @@ __global__ __launch_bounds__(BT) void bwd_row_bf16_kernel(
       __syncthreads();
     }
   }
-  const int64_t batch = gridDim.x / (nb * nsplit * G * nc);
+  const int64_t batch = gridDim.x / (npair * nsplit * G * nc);
   float* dCo = dC_out + static_cast<int64_t>(sp) * batch * T * GN;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
@@ -703,6 +719,7 @@ __global__ __launch_bounds__(BT) void bwd_row_bf16_kernel(
       if (iq < Q && n < N) dCo[(row0 + iq) * GN + static_cast<int64_t>(g) * N + n] = ua[k][e];
     }
   }
+  }  // pass
 }
 
 bool bwd_bf16_supported(const Dims& d) {
@@ -715,7 +732,7 @@ bool bwd_bf16_supported(const Dims& d) {
 hipError_t launch_bwd_row_bf16(const Dims& d, int nsplit, const void* x, const void* B, const void* C,
                                const void* dt, const void* dy, const float* A_log, const void* hbf,
                                float* dC_out, const BwdScratch& s, hipStream_t st) {
-  const int64_t nblk = static_cast<int64_t>(d.b) * d.nc() * d.G * nsplit * d.nb();
+  const int64_t nblk = static_cast<int64_t>(d.b) * d.nc() * d.G * nsplit * ((d.nb() + 1) / 2);
   hipLaunchKernelGGL(bwd_row_bf16_kernel, dim3(nblk), dim3(BT), 0, st, static_cast<const uint16_t*>(x),
                      static_cast<const uint16_t*>(B), static_cast<const uint16_t*>(C),
                      static_cast<const uint16_t*>(dt), static_cast<const uint16_t*>(dy), A_log,
@@ -728,7 +745,7 @@ hipError_t launch_bwd_col_bf16(const Dims& d, int nsplit, const void* x, const v
                                const void* dt, const void* dy, const float* A_log, const float* D,
                                const void* gamma, float* dx, float* dB_out, const BwdScratch& s,
                                hipStream_t st) {
-  const int64_t nblk = static_cast<int64_t>(d.b) * d.nc() * d.G * nsplit * d.nb();
+  const int64_t nblk = static_cast<int64_t>(d.b) * d.nc() * d.G * nsplit * ((d.nb() + 1) / 2);
   hipLaunchKernelGGL(bwd_col_bf16_kernel, dim3(nblk), dim3(BT), 0, st, static_cast<const uint16_t*>(x),
                      static_cast<const uint16_t*>(B), static_cast<const uint16_t*>(C),
                      static_cast<const uint16_t*>(dt), static_cast<const uint16_t*>(dy), A_log, D,

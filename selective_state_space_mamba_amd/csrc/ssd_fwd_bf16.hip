@@ -86,15 +86,23 @@ __global__ __launch_bounds__(FT) void out_fwd_bf16_kernel(
 
   const int nc = T / Q, nb = (Q + BQ - 1) / BQ;
   const int hpg = H / G, hps = hpg / nsplit;
+  // blocks nb - 1 - k and k share a workgroup, one after the other, so that
+  // every workgroup has the same number of (row block, column block) pairs
+  const int npair = (nb + 1) >> 1;
   int idx = xcd_logical_block(blockIdx.x, gridDim.x);
-  const int ib = nb - 1 - idx % nb;  // the block with the most columns j first
-  idx /= nb;
+  const int kpair = idx % npair;
+  idx /= npair;
   const int sp = idx % nsplit;
   idx /= nsplit;
   const int g = idx % G;
   idx /= G;
   const int c = idx % nc;
   const int bi = idx / nc;
+
+  for (int pass = 0; pass < 2; ++pass) {
+  const int ib = pass ? kpair : nb - 1 - kpair;  // the block with the most columns j first
+  if (pass && ib == nb - 1 - kpair) break;
+  if (pass) __syncthreads();
 
   const int l = lane_id(), w = wave_id(), r = l & 15, q = l >> 4;
   const int team = w >> 2, wt = w & 3;
@@ -269,12 +277,13 @@ __global__ __launch_bounds__(FT) void out_fwd_bf16_kernel(
     wait_vm<0>();
     __syncthreads();
   }
+  }  // pass
 }
 
 hipError_t launch_out_fwd_bf16(const Dims& d, int nsplit, const void* x, const void* B, const void* C,
                                const void* dt, const float* A_log, const float* D, const void* hbf, void* y,
                                hipStream_t st) {
-  const int64_t nblk = static_cast<int64_t>(d.b) * d.nc() * d.G * nsplit * d.nb();
+  const int64_t nblk = static_cast<int64_t>(d.b) * d.nc() * d.G * nsplit * ((d.nb() + 1) / 2);
   hipLaunchKernelGGL(out_fwd_bf16_kernel, dim3(nblk), dim3(FT), 0, st, static_cast<const uint16_t*>(x),
                      static_cast<const uint16_t*>(B), static_cast<const uint16_t*>(C),
                      static_cast<const uint16_t*>(dt), A_log, D, static_cast<const uint16_t*>(hbf),
