@@ -148,12 +148,80 @@ __device__ __forceinline__ bf16x8 frag_cols(const lds_char* t, int k0, int m0) {
   return __builtin_bit_cast(bf16x8, v);
 }
 
+// The same reads from per-lane base offsets.  The swizzle only permutes the
+// 16-byte chunks inside a row, so for m0 and k0 multiples of 16 and kc a
+// multiple of 4 every address of a read is the lane's offset at
+// m0 = k0 = kc = 0, XORed with the chunk offset of kc (rows) or m0 (columns),
+// plus the row offset of m0 (rows) or k0 (columns): one VALU operation per
+// read.  The bases are computed once; a loop body passes them through
+// opaque() so that the compiler recomputes the few XORs per iteration
+// instead of keeping one register per distinct address alive across the loop.
+template <int CPR>
+struct RowsAt {
+  int b;
+};
+template <int CPR>
+struct ColsAt {
+  int b;  // the first transpose read (rows k0 + 8q + i/4); the second reads 4 rows further
+};
+template <int CPR>
+__device__ __forceinline__ RowsAt<CPR> rows_at() {
+  const int l = lane_id(), r = l & 15, q = l >> 4;
+  return {r * (CPR * 16) + ((q ^ swz<CPR>(r)) << 4)};
+}
+template <int CPR>
+__device__ __forceinline__ ColsAt<CPR> cols_at() {
+  const int l = lane_id(), i = l & 15, q = l >> 4;
+  const int half = (i & 1) << 3, ra = 8 * q + (i >> 2);
+  return {ra * (CPR * 16) + ((((i >> 1) & 1) ^ swz<CPR>(ra)) << 4) + half};
+}
+template <int CPR>
+__device__ __forceinline__ RowsAt<CPR> opaque(RowsAt<CPR> a) {
+  asm volatile("" : "+v"(a.b));
+  return a;
+}
+template <int CPR>
+__device__ __forceinline__ ColsAt<CPR> opaque(ColsAt<CPR> a) {
+  asm volatile("" : "+v"(a.b));
+  return a;
+}
+template <int CPR>
+__device__ __forceinline__ bf16x8 frag_rows(const lds_char* t, int m0, int kc, RowsAt<CPR> a) {
+  return *(const __attribute__((address_space(3))) bf16x8*)(t + ((a.b ^ (kc << 4)) + m0 * (CPR * 16)));
+}
+template <int CPR>
+__device__ __forceinline__ bf16x8 frag_cols(const lds_char* t, int k0, int m0, ColsAt<CPR> a) {
+  // rows r and r + 4 (r % 8 < 4) differ in the low bit of the swizzle of 8-
+  // and 16-chunk rows, and not at all for the others
+  constexpr int flip = (CPR == 8 || CPR == 16) ? 16 : 0;
+  const int x = (m0 >> 3) << 4, o = k0 * (CPR * 16);
+  const short4_t lo =
+      __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) short4_t*)(t + ((a.b ^ x) + o)));
+  const short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) short4_t*)(t + ((a.b ^ (x ^ flip)) + o + 4 * CPR * 16)));
+  const short8_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
 // One element (row, col) of a swizzled tile, as f32.
 template <int CPR>
 __device__ __forceinline__ float tile_elem(const lds_char* t, int row, int col) {
   const uint16_t v =
       *(const __attribute__((address_space(3))) uint16_t*)(t + tile_off<CPR>(row, col >> 3) + ((col & 7) << 1));
   return bf16_bits_to_f32(v);
+}
+
+// Scheduling groups (AMDGPU sched_group_barrier): the next N LDS reads, or N
+// MFMAs, of the enclosing scheduling region are placed here, in program
+// order of the groups.  Used to issue all of a phase's fragment reads before
+// its MFMAs, so that their latencies overlap.
+template <int N>
+__device__ __forceinline__ void sched_ds_reads() {
+  __builtin_amdgcn_sched_group_barrier(0x100, N, 0);
+}
+template <int N>
+__device__ __forceinline__ void sched_mfmas() {
+  __builtin_amdgcn_sched_group_barrier(0x008, N, 0);
 }
 
 // Sum over each row of 16 lanes (lanes sharing q), complete in lane r = 15

@@ -45,6 +45,10 @@ constexpr int BT = BW * WAVE;       // threads per workgroup
 constexpr int TILE_N = 64 * 256;    // bytes of a 64 x 128 bf16 tile
 constexpr int TILE_P = 64 * 128;    // bytes of a 64 x 64 bf16 tile
 constexpr int STRIP = 32 * 32;      // bytes of a 32 x 16 bf16 strip
+// k-steps of 32 over the largest headdim and d_state: tiles are zero past the
+// problem's P and N, so the contractions always run over the full tiles
+constexpr int KP = PMAX / 32;
+constexpr int KN = NMAX / 32;
 }  // namespace
 
 // s (within-chunk inclusive cumsum of dt A) and dt for t < Q, from the dt bits
@@ -120,7 +124,13 @@ __global__ __launch_bounds__(BT) void bwd_col_bf16_kernel(
 
   const int l = lane_id(), w = wave_id(), r = l & 15, q = l >> 4;
   const int team = w >> 2, wt = w & 3;
-  const int ti = 32 * team;  // this team's rows inside every 64-row block
+  const int ti = 32 * team;
+  // per-lane fragment offsets (tiles of 2, 8 and 16 chunks per row)
+  const RowsAt<8> r8_ = rows_at<8>();
+  const RowsAt<16> r16_ = rows_at<16>();
+  const ColsAt<2> c2_ = cols_at<2>();
+  const ColsAt<8> c8_ = cols_at<8>();
+  const ColsAt<16> c16_ = cols_at<16>();  // this team's rows inside every 64-row block
   const int64_t row0 = static_cast<int64_t>(bi) * T + static_cast<int64_t>(c) * Q;
   const int j0 = jb * BQ, vj = min(BQ, Q - j0);
   const int nib = nb - jb;
@@ -128,7 +138,6 @@ __global__ __launch_bounds__(BT) void bwd_col_bf16_kernel(
   const uint32_t HPb = static_cast<uint32_t>(HP) * 2, GNb = static_cast<uint32_t>(GN) * 2;
   const uint32_t goff = static_cast<uint32_t>(g) * N * 2;
   const int pch = P >> 3, nch = N >> 3;
-  const int kp = (P + 31) >> 5, kn = (N + 31) >> 5;
   const i32x4 rx = make_rsrc(x + row0 * HP);
   const i32x4 rdy = make_rsrc(dy + row0 * HP);
   const i32x4 rb = make_rsrc(Bm + row0 * GN);
@@ -174,13 +183,22 @@ __global__ __launch_bounds__(BT) void bwd_col_bf16_kernel(
         const int u = u0 + d;
         if (u < nib) {
           const lds_char* ct = d ? sGam : sX;
+          const RowsAt<16> ar16 = opaque(r16_);
           f4 cb[2];
           zero(cb);
-          for (int ks = 0; ks < kn; ++ks) {
-            const bf16x8 a = frag_rows<16>(sB, 16 * wt, 4 * ks);
+          bf16x8 fa[KN], fb[KN][2];
 #pragma unroll
-            for (int tt = 0; tt < 2; ++tt) cb[tt] = mfma(a, frag_rows<16>(ct, ti + 16 * tt, 4 * ks), cb[tt]);
+          for (int ks = 0; ks < KN; ++ks) {
+            fa[ks] = frag_rows(sB, 16 * wt, 4 * ks, ar16);
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) fb[ks][tt] = frag_rows(ct, ti + 16 * tt, 4 * ks, ar16);
           }
+          sched_ds_reads<3 * KN>();
+#pragma unroll
+          for (int ks = 0; ks < KN; ++ks)
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) cb[tt] = mfma(fa[ks], fb[ks][tt], cb[tt]);
+          sched_mfmas<2 * KN>();
           sCB[u][0][w][l] = cb[0];
           sCB[u][1][w][l] = cb[1];
         }
@@ -220,6 +238,9 @@ __global__ __launch_bounds__(BT) void bwd_col_bf16_kernel(
 #pragma unroll
     for (int u = 0; u < NBMAX; ++u) {
       if (u < nib) {
+        const RowsAt<8> ar8 = opaque(r8_);
+        const ColsAt<2> ac2 = opaque(c2_);
+        const ColsAt<8> ac8 = opaque(c8_);
         const int i0 = (jb + u) * BQ;
         const lds_char* dyt = sDy[u & 1];
         // tiles of later steps start loading now
@@ -229,25 +250,44 @@ __global__ __launch_bounds__(BT) void bwd_col_bf16_kernel(
           if (hh + 1 < hps) load_dt(hh + 1);
         }
 
-        // yx^T: rows j (this wave's 16), columns i = i0 + ti + 16 tt + r
+        // yx^T: rows j (this wave's 16), columns i = i0 + ti + 16 tt + r; the
+        // C.B^T tiles and the s values of the step are read with the fragments
         f4 yx[2];
         zero(yx);
-        for (int ks = 0; ks < kp; ++ks) {
-          const bf16x8 a = frag_rows<8>(xt, 16 * wt, 4 * ks);
+        f4 cbt[2];
+        float sv[2];  // s at rows i = i0 + ti + 16 tt + r (clamped)
+        float sref;   // s at the block's first row
+        {
+          bf16x8 fa[KP], fb[KP][2];
 #pragma unroll
-          for (int tt = 0; tt < 2; ++tt) yx[tt] = mfma(a, frag_rows<8>(dyt, ti + 16 * tt, 4 * ks), yx[tt]);
+          for (int ks = 0; ks < KP; ++ks) {
+            fa[ks] = frag_rows(xt, 16 * wt, 4 * ks, ar8);
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) fb[ks][tt] = frag_rows(dyt, ti + 16 * tt, 4 * ks, ar8);
+          }
+          cbt[0] = sCB[u][0][w][l];
+          cbt[1] = sCB[u][1][w][l];
+#pragma unroll
+          for (int tt = 0; tt < 2; ++tt) sv[tt] = sSh[min(i0 + ti + 16 * tt + r, Q - 1)];
+          sref = sSh[i0];
+          sched_ds_reads<3 * KP + 5>();
+#pragma unroll
+          for (int ks = 0; ks < KP; ++ks)
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) yx[tt] = mfma(fa[ks], fb[ks][tt], yx[tt]);
+          sched_mfmas<2 * KP>();
         }
-        const f4 cbt[2] = {sCB[u][0][w][l], sCB[u][1][w][l]};
         f4 gv[2];
         if (u == 0) {
 #pragma unroll
           for (int tt = 0; tt < 2; ++tt) {
             const int iq = i0 + ti + 16 * tt + r;
-            const float si = sSh[min(iq, Q - 1)];
+            const float si = sv[tt];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               const int jq = j0 + 16 * wt + 4 * q + e;
-              const float L = (iq < Q && iq >= jq) ? __expf(si - sj[e]) : 0.f;
+              const float ex = __expf(si - sj[e]);
+              const float L = (iq < Q && iq >= jq) ? ex : 0.f;
               const float G1 = L * cbt[tt][e];
               const float E = G1 * yx[tt][e];
               csum[e] += E;
@@ -262,7 +302,6 @@ __global__ __launch_bounds__(BT) void bwd_col_bf16_kernel(
             dsk[e] = pack_bf16(tile_elem<8>(dyt, jl, ti + r), tile_elem<8>(dyt, jl, ti + 16 + r));
           }
         } else {
-          const float sref = sSh[i0];
           float cf[4], cfd[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
@@ -272,7 +311,8 @@ __global__ __launch_bounds__(BT) void bwd_col_bf16_kernel(
 #pragma unroll
           for (int tt = 0; tt < 2; ++tt) {
             const int iq = i0 + ti + 16 * tt + r;
-            const float rf = (iq < Q) ? __expf(sSh[min(iq, Q - 1)] - sref) : 0.f;
+            const float rx = __expf(sv[tt] - sref);
+            const float rf = (iq < Q) ? rx : 0.f;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               const float G1 = rf * cf[e] * cbt[tt][e];
@@ -287,11 +327,20 @@ __global__ __launch_bounds__(BT) void bwd_col_bf16_kernel(
         lds_barrier();
         // dx_j += sum_i G_ij dy_i over the block's 64 rows i: k-step ks reads
         // the strip of team ks
+        {
+          bf16x8 ga[2], gb[2][2];
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const bf16x8 a = frag_cols<2>(sG + (4 * ks + wt) * STRIP, 0, 0);
+          for (int ks = 0; ks < 2; ++ks) {
+            ga[ks] = frag_cols(sG + (4 * ks + wt) * STRIP, 0, 0, ac2);
 #pragma unroll
-          for (int k = 0; k < 2; ++k) dxa[k] = mfma(a, frag_cols<8>(dyt, 32 * ks, 16 * (2 * team + k)), dxa[k]);
+            for (int k = 0; k < 2; ++k) gb[ks][k] = frag_cols(dyt, 32 * ks, 16 * (2 * team + k), ac8);
+          }
+          sched_ds_reads<12>();
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int k = 0; k < 2; ++k) dxa[k] = mfma(ga[ks], gb[ks][k], dxa[k]);
+          sched_mfmas<4>();
         }
         wait_vm<0>();
         __syncthreads();
@@ -299,16 +348,44 @@ __global__ __launch_bounds__(BT) void bwd_col_bf16_kernel(
     }
 
     // ---- state terms of head hh; the next head's first tiles start loading
+    const RowsAt<8> ar8 = opaque(r8_);
+    const RowsAt<16> ar16 = opaque(r16_);
+    const ColsAt<16> ac16 = opaque(c16_);
     if (hh + 1 < hps) {
       load_x(hh + 1);
       load_dy(hh + 1, 0, sDy[0]);
     }
     f4 bg[2];  // B_j Gamma^T: rows j, columns p = 16 (2 team + k) + r
     zero(bg);
-    for (int ks = 0; ks < kn; ++ks) {
-      const bf16x8 a = frag_rows<16>(sB, 16 * wt, 4 * ks);
 #pragma unroll
-      for (int k = 0; k < 2; ++k) bg[k] = mfma(a, frag_rows<16>(sGam, 16 * (2 * team + k), 4 * ks), bg[k]);
+    for (int kh = 0; kh < KN; kh += 2) {  // two k-steps per batch of reads
+      bf16x8 fa[2], fb[2][2];
+#pragma unroll
+      for (int d = 0; d < 2; ++d) {
+        fa[d] = frag_rows(sB, 16 * wt, 4 * (kh + d), ar16);
+#pragma unroll
+        for (int k = 0; k < 2; ++k) fb[d][k] = frag_rows(sGam, 16 * (2 * team + k), 4 * (kh + d), ar16);
+      }
+      sched_ds_reads<6>();
+#pragma unroll
+      for (int d = 0; d < 2; ++d)
+#pragma unroll
+        for (int k = 0; k < 2; ++k) bg[k] = mfma(fa[d], fb[d][k], bg[k]);
+      sched_mfmas<4>();
+    }
+    // x_j Gamma for this team's d_state columns (the state part of dB)
+    f4 v[4];
+    zero(v);
+#pragma unroll
+    for (int ks = 0; ks < KP; ++ks) {
+      bf16x8 fa, fb[4];
+      fa = frag_rows(xt, 16 * wt, 4 * ks, ar8);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) fb[k] = frag_cols(sGam, 32 * ks, 16 * (4 * team + k), ac16);
+      sched_ds_reads<9>();
+#pragma unroll
+      for (int k = 0; k < 4; ++k) v[k] = mfma(fa, fb[k], v[k]);
+      sched_mfmas<4>();
     }
     const float s_end = sSh[Q - 1];
     float wj[4];
@@ -353,21 +430,11 @@ __global__ __launch_bounds__(BT) void bwd_col_bf16_kernel(
         }
       }
     }
-    // x_j Gamma for this team's d_state columns, into the state part of dB
-    {
-      f4 v[4];
-      zero(v);
-      for (int ks = 0; ks < kp; ++ks) {
-        const bf16x8 a = frag_rows<8>(xt, 16 * wt, 4 * ks);
 #pragma unroll
-        for (int k = 0; k < 4; ++k) v[k] = mfma(a, frag_cols<16>(sGam, 32 * ks, 16 * (4 * team + k)), v[k]);
-      }
+    for (int e = 0; e < 4; ++e) {
+      const float f = dtj[e] * wj[e];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float f = dtj[e] * wj[e];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) dbs[k][e] += f * v[k][e];
-      }
+      for (int k = 0; k < 4; ++k) dbs[k][e] += f * v[k][e];
     }
     if (hh + 1 < hps) scan_store(dtb, -__expf(A_log[head(hh + 1)]), sS[hb ^ 1], sDt[hb ^ 1]);
     wait_vm<0>();
@@ -394,12 +461,21 @@ __global__ __launch_bounds__(BT) void bwd_col_bf16_kernel(
       for (int d = 0; d < 2; ++d) {
         if (u0 + d < nib) {
           const lds_char* ct = d ? sGam : sX;
+          const ColsAt<2> ac2 = opaque(c2_);
+          const ColsAt<16> ac16 = opaque(c16_);
+          bf16x8 fa[2], fb[2][4];
 #pragma unroll
           for (int ks = 0; ks < 2; ++ks) {
-            const bf16x8 a = frag_cols<2>(wset[d] + (4 * ks + wt) * STRIP, 0, 0);
+            fa[ks] = frag_cols(wset[d] + (4 * ks + wt) * STRIP, 0, 0, ac2);
 #pragma unroll
-            for (int k = 0; k < 4; ++k) dbp[k] = mfma(a, frag_cols<16>(ct, 32 * ks, 16 * (4 * team + k)), dbp[k]);
+            for (int k = 0; k < 4; ++k) fb[ks][k] = frag_cols(ct, 32 * ks, 16 * (4 * team + k), ac16);
           }
+          sched_ds_reads<20>();
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int k = 0; k < 4; ++k) dbp[k] = mfma(fa[ks], fb[ks][k], dbp[k]);
+          sched_mfmas<8>();
         }
       }
       __syncthreads();
