@@ -551,6 +551,11 @@ __global__ __launch_bounds__(BT) void bwd_row_bf16_kernel(
   const int l = lane_id(), w = wave_id(), r = l & 15, q = l >> 4;
   const int team = w >> 2, wt = w & 3;
   const int tj = 32 * team;  // this team's columns inside every 64-column block
+  // per-lane fragment offsets (tiles of 2, 8 and 16 chunks per row)
+  const RowsAt<8> r8_ = rows_at<8>();
+  const RowsAt<16> r16_ = rows_at<16>();
+  const ColsAt<2> c2_ = cols_at<2>();
+  const ColsAt<16> c16_ = cols_at<16>();
   const int64_t row0 = static_cast<int64_t>(bi) * T + static_cast<int64_t>(c) * Q;
   const int i0 = ib * BQ, vi = min(BQ, Q - i0);
   const int nj = ib + 1;
@@ -558,7 +563,6 @@ __global__ __launch_bounds__(BT) void bwd_row_bf16_kernel(
   const uint32_t HPb = static_cast<uint32_t>(HP) * 2, GNb = static_cast<uint32_t>(GN) * 2;
   const uint32_t goff = static_cast<uint32_t>(g) * N * 2;
   const int pch = P >> 3, nch = N >> 3;
-  const int kp = (P + 31) >> 5, kn = (N + 31) >> 5;
   const i32x4 rx = make_rsrc(x + row0 * HP);
   const i32x4 rdy = make_rsrc(dy + row0 * HP);
   const i32x4 rb = make_rsrc(Bm + row0 * GN);
@@ -604,13 +608,22 @@ __global__ __launch_bounds__(BT) void bwd_row_bf16_kernel(
         const int jb = jb0 + d;
         if (jb < nj) {
           const lds_char* bt = d ? sH : sDy;
+          const RowsAt<16> ar16 = opaque(r16_);
           f4 cb[2];
           zero(cb);
-          for (int ks = 0; ks < kn; ++ks) {
-            const bf16x8 a = frag_rows<16>(sC, 16 * wt, 4 * ks);
+          bf16x8 fa[KN], fb[KN][2];
 #pragma unroll
-            for (int tt = 0; tt < 2; ++tt) cb[tt] = mfma(a, frag_rows<16>(bt, tj + 16 * tt, 4 * ks), cb[tt]);
+          for (int ks = 0; ks < KN; ++ks) {
+            fa[ks] = frag_rows(sC, 16 * wt, 4 * ks, ar16);
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) fb[ks][tt] = frag_rows(bt, tj + 16 * tt, 4 * ks, ar16);
           }
+          sched_ds_reads<3 * KN>();
+#pragma unroll
+          for (int ks = 0; ks < KN; ++ks)
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) cb[tt] = mfma(fa[ks], fb[ks][tt], cb[tt]);
+          sched_mfmas<2 * KN>();
           sCB[jb][0][w][l] = cb[0];
           sCB[jb][1][w][l] = cb[1];
         }
@@ -641,7 +654,8 @@ __global__ __launch_bounds__(BT) void bwd_row_bf16_kernel(
     for (int e = 0; e < 4; ++e) {
       const int iq = i0 + 16 * wt + 4 * q + e;
       si[e] = sSh[min(iq, Q - 1)];
-      rf[e] = (iq < Q) ? __expf(si[e] - sref) : 0.f;
+      const float ex = __expf(si[e] - sref);
+      rf[e] = (iq < Q) ? ex : 0.f;
     }
     float rm[4] = {0.f, 0.f, 0.f, 0.f};  // strictly-lower row sums of M over this team's columns
     float ddv = 0.f;                     // diagonal of yx
@@ -656,25 +670,48 @@ __global__ __launch_bounds__(BT) void bwd_row_bf16_kernel(
           tile_async<64, 16, BW>(sH, rh, h * P * N * 2, N * 2, P, nch);
           if (hh + 1 < hps) load_dt(hh + 1);
         }
-        // yx: rows i (this wave's 16), columns j = j0 + tj + 16 tt + r
+        // yx: rows i (this wave's 16), columns j = j0 + tj + 16 tt + r; the
+        // C.B^T tiles and the s and dt values of the columns are read with the
+        // fragments
+        const RowsAt<8> ar8 = opaque(r8_);
         f4 yx[2];
         zero(yx);
-        for (int ks = 0; ks < kp; ++ks) {
-          const bf16x8 a = frag_rows<8>(dyt, 16 * wt, 4 * ks);
+        f4 cbt[2];
+        float sjv[2], dtv[2];  // s and dt at columns j = j0 + tj + 16 tt + r (clamped)
+        {
+          bf16x8 fa[KP], fb[KP][2];
 #pragma unroll
-          for (int tt = 0; tt < 2; ++tt) yx[tt] = mfma(a, frag_rows<8>(xt, tj + 16 * tt, 4 * ks), yx[tt]);
+          for (int ks = 0; ks < KP; ++ks) {
+            fa[ks] = frag_rows(dyt, 16 * wt, 4 * ks, ar8);
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) fb[ks][tt] = frag_rows(xt, tj + 16 * tt, 4 * ks, ar8);
+          }
+          cbt[0] = sCB[jb][0][w][l];
+          cbt[1] = sCB[jb][1][w][l];
+#pragma unroll
+          for (int tt = 0; tt < 2; ++tt) {
+            const int jc = min(j0 + tj + 16 * tt + r, Q - 1);
+            sjv[tt] = sSh[jc];
+            dtv[tt] = sDh[jc];
+          }
+          sched_ds_reads<3 * KP + 6>();
+#pragma unroll
+          for (int ks = 0; ks < KP; ++ks)
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) yx[tt] = mfma(fa[ks], fb[ks][tt], yx[tt]);
+          sched_mfmas<2 * KP>();
         }
-        const f4 cbt[2] = {sCB[jb][0][w][l], sCB[jb][1][w][l]};
         if (jb == ib) {
 #pragma unroll
           for (int tt = 0; tt < 2; ++tt) {
             const int jq = j0 + tj + 16 * tt + r;
-            const float sj = sSh[min(jq, Q - 1)];
-            const float dtj = (jq < Q) ? sDh[jq] : 0.f;
+            const float sj = sjv[tt];
+            const float dtj = (jq < Q) ? dtv[tt] : 0.f;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               const int iq = i0 + 16 * wt + 4 * q + e;
-              const float L = (iq < Q && jq <= iq) ? __expf(si[e] - sj) : 0.f;
+              const float ex = __expf(si[e] - sj);
+              const float L = (iq < Q && jq <= iq) ? ex : 0.f;
               const float ly = L * yx[tt][e] * dtj;
               ws[jb][tt][e] += ly;
               if (jq < iq) rm[e] += ly * cbt[tt][e];
@@ -684,8 +721,7 @@ __global__ __launch_bounds__(BT) void bwd_row_bf16_kernel(
         } else {
 #pragma unroll
           for (int tt = 0; tt < 2; ++tt) {
-            const int jq = j0 + tj + 16 * tt + r;
-            const float cfd = __expf(sref - sSh[jq]) * sDh[jq];
+            const float cfd = __expf(sref - sjv[tt]) * dtv[tt];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               const float ly = rf[e] * cfd * yx[tt][e];
@@ -706,10 +742,20 @@ __global__ __launch_bounds__(BT) void bwd_row_bf16_kernel(
     }
     f4 u[4];  // U_i = dy_i H_c: rows i, columns n = 16 (4 team + k) + r
     zero(u);
-    for (int ks = 0; ks < kp; ++ks) {
-      const bf16x8 a = frag_rows<8>(dyt, 16 * wt, 4 * ks);
+    {
+      const RowsAt<8> ar8 = opaque(r8_);
+      const ColsAt<16> ac16 = opaque(c16_);
 #pragma unroll
-      for (int k = 0; k < 4; ++k) u[k] = mfma(a, frag_cols<16>(sH, 32 * ks, 16 * (4 * team + k)), u[k]);
+      for (int ks = 0; ks < KP; ++ks) {
+        bf16x8 fa, fb[4];
+        fa = frag_rows(dyt, 16 * wt, 4 * ks, ar8);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) fb[k] = frag_cols(sH, 32 * ks, 16 * (4 * team + k), ac16);
+        sched_ds_reads<9>();
+#pragma unroll
+        for (int k = 0; k < 4; ++k) u[k] = mfma(fa, fb[k], u[k]);
+        sched_mfmas<4>();
+      }
     }
     float ex[4];
 #pragma unroll
@@ -773,11 +819,18 @@ __global__ __launch_bounds__(BT) void bwd_row_bf16_kernel(
       for (int d = 0; d < 2; ++d) {
         if (jb0 + d < nj) {
           const lds_char* bt = d ? sH : sDy;
+          const ColsAt<2> ac2 = opaque(c2_);
+          const ColsAt<16> ac16 = opaque(c16_);
 #pragma unroll
           for (int ks = 0; ks < 2; ++ks) {
-            const bf16x8 a = frag_cols<2>(wset[d] + (4 * ks + wt) * STRIP, 0, 0);
+            bf16x8 fa, fb[4];
+            fa = frag_cols(wset[d] + (4 * ks + wt) * STRIP, 0, 0, ac2);
 #pragma unroll
-            for (int k = 0; k < 4; ++k) ua[k] = mfma(a, frag_cols<16>(bt, 32 * ks, 16 * (4 * team + k)), ua[k]);
+            for (int k = 0; k < 4; ++k) fb[k] = frag_cols(bt, 32 * ks, 16 * (4 * team + k), ac16);
+            sched_ds_reads<10>();
+#pragma unroll
+            for (int k = 0; k < 4; ++k) ua[k] = mfma(fa, fb[k], ua[k]);
+            sched_mfmas<4>();
           }
         }
       }

@@ -35,6 +35,9 @@ constexpr int FT = FW * WAVE;       // threads per workgroup
 constexpr int FTILE_N = 64 * 256;   // bytes of a 64 x 128 bf16 tile
 constexpr int FTILE_P = 64 * 128;   // bytes of a 64 x 64 bf16 tile
 constexpr int FSTRIP = 32 * 32;     // bytes of a 32 x 16 bf16 strip
+// k-steps of 32 over the largest d_state: tiles are zero past the problem's N,
+// so the contractions always run over the full tiles
+constexpr int FKN = NMAX / 32;
 
 // s and dt for t < Q from the dt bits of t = 4l .. 4l+3 (see the backward kernels).
 __device__ __forceinline__ void fwd_scan_store(const uint32_t (&dtb)[4], float A, float* s_out, float* dt_out) {
@@ -107,6 +110,10 @@ __global__ __launch_bounds__(FT) void out_fwd_bf16_kernel(
   const int l = lane_id(), w = wave_id(), r = l & 15, q = l >> 4;
   const int team = w >> 2, wt = w & 3;
   const int tj = 32 * team;
+  // per-lane fragment offsets (tiles of 2, 8 and 16 chunks per row)
+  const RowsAt<16> r16_ = rows_at<16>();
+  const ColsAt<2> c2_ = cols_at<2>();
+  const ColsAt<8> c8_ = cols_at<8>();
   const int64_t row0 = static_cast<int64_t>(bi) * T + static_cast<int64_t>(c) * Q;
   const int i0 = ib * BQ, vi = min(BQ, Q - i0);
   const int nj = ib + 1;
@@ -114,7 +121,6 @@ __global__ __launch_bounds__(FT) void out_fwd_bf16_kernel(
   const uint32_t HPb = static_cast<uint32_t>(HP) * 2, GNb = static_cast<uint32_t>(GN) * 2;
   const uint32_t goff = static_cast<uint32_t>(g) * N * 2;
   const int pch = P >> 3, nch = N >> 3;
-  const int kn = (N + 31) >> 5;
   const i32x4 rx = make_rsrc(x + row0 * HP);
   const i32x4 rb = make_rsrc(Bm + row0 * GN);
   const i32x4 rc = make_rsrc(Cm + row0 * GN);
@@ -156,13 +162,22 @@ __global__ __launch_bounds__(FT) void out_fwd_bf16_kernel(
         const int jb = jb0 + d;
         if (jb < nj) {
           const lds_char* bt = d ? sH : sXch;
+          const RowsAt<16> ar16 = opaque(r16_);
           f4 cb[2];
           zero(cb);
-          for (int ks = 0; ks < kn; ++ks) {
-            const bf16x8 a = frag_rows<16>(sC, 16 * wt, 4 * ks);
+          bf16x8 fa[FKN], fb[FKN][2];
 #pragma unroll
-            for (int tt = 0; tt < 2; ++tt) cb[tt] = mfma(a, frag_rows<16>(bt, tj + 16 * tt, 4 * ks), cb[tt]);
+          for (int ks = 0; ks < FKN; ++ks) {
+            fa[ks] = frag_rows(sC, 16 * wt, 4 * ks, ar16);
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) fb[ks][tt] = frag_rows(bt, tj + 16 * tt, 4 * ks, ar16);
           }
+          sched_ds_reads<3 * FKN>();
+#pragma unroll
+          for (int ks = 0; ks < FKN; ++ks)
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) cb[tt] = mfma(fa[ks], fb[ks][tt], cb[tt]);
+          sched_mfmas<2 * FKN>();
           sCB[jb][0][w][l] = cb[0];
           sCB[jb][1][w][l] = cb[1];
         }
@@ -185,7 +200,8 @@ __global__ __launch_bounds__(FT) void out_fwd_bf16_kernel(
     for (int e = 0; e < 4; ++e) {
       const int iq = i0 + 16 * wt + 4 * q + e;
       si[e] = sSh[min(iq, Q - 1)];
-      rf[e] = (iq < Q) ? __expf(si[e] - sref) : 0.f;
+      const float ex = __expf(si[e] - sref);
+      rf[e] = (iq < Q) ? ex : 0.f;
     }
     f4 ya[4];  // sum over this team's columns j of G_ij x_j: rows i, columns p = 16 pt + r
     zero(ya);
@@ -201,18 +217,36 @@ __global__ __launch_bounds__(FT) void out_fwd_bf16_kernel(
           tile_async<64, 16, FW>(sH, rh, h * P * N * 2, N * 2, P, nch);
           if (hh + 1 < hps) load_dt(hh + 1);
         }
-        const f4 cbt[2] = {sCB[jb][0][w][l], sCB[jb][1][w][l]};
+        // the step's C.B^T tiles, the s and dt values of its columns and the x
+        // fragments of the G x contraction are read together
+        const ColsAt<2> ac2 = opaque(c2_);
+        const ColsAt<8> ac8 = opaque(c8_);
+        f4 cbt[2];
+        float sjv[2], dtv[2];  // s and dt at columns j = j0 + tj + 16 tt + r (clamped)
+        bf16x8 fx[4];
+        cbt[0] = sCB[jb][0][w][l];
+        cbt[1] = sCB[jb][1][w][l];
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          const int jc = min(j0 + tj + 16 * tt + r, Q - 1);
+          sjv[tt] = sSh[jc];
+          dtv[tt] = sDh[jc];
+        }
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt) fx[pt] = frag_cols(xt, tj, 16 * pt, ac8);
+        sched_ds_reads<14>();
         f4 gv[2];
         if (jb == ib) {
 #pragma unroll
           for (int tt = 0; tt < 2; ++tt) {
             const int jq = j0 + tj + 16 * tt + r;
-            const float sj = sSh[min(jq, Q - 1)];
-            const float dtj = (jq < Q) ? sDh[jq] : 0.f;
+            const float sj = sjv[tt];
+            const float dtj = (jq < Q) ? dtv[tt] : 0.f;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               const int iq = i0 + 16 * wt + 4 * q + e;
-              const float L = (iq < Q && jq <= iq) ? __expf(si[e] - sj) : 0.f;
+              const float ex = __expf(si[e] - sj);
+              const float L = (iq < Q && jq <= iq) ? ex : 0.f;
               gv[tt][e] = L * dtj * cbt[tt][e];
             }
           }
@@ -224,17 +258,16 @@ __global__ __launch_bounds__(FT) void out_fwd_bf16_kernel(
         } else {
 #pragma unroll
           for (int tt = 0; tt < 2; ++tt) {
-            const int jq = j0 + tj + 16 * tt + r;
-            const float cfd = __expf(sref - sSh[jq]) * sDh[jq];
+            const float cfd = __expf(sref - sjv[tt]) * dtv[tt];
 #pragma unroll
             for (int e = 0; e < 4; ++e) gv[tt][e] = rf[e] * cfd * cbt[tt][e];
           }
         }
         fwd_put_strip(sG + w * FSTRIP, gv);
         {
-          const bf16x8 a = frag_cols<2>(sG + w * FSTRIP, 0, 0);
+          const bf16x8 a = frag_cols(sG + w * FSTRIP, 0, 0, ac2);
 #pragma unroll
-          for (int pt = 0; pt < 4; ++pt) ya[pt] = mfma(a, frag_cols<8>(xt, tj, 16 * pt), ya[pt]);
+          for (int pt = 0; pt < 4; ++pt) ya[pt] = mfma(a, fx[pt], ya[pt]);
         }
         wait_vm<0>();
         __syncthreads();
@@ -251,10 +284,24 @@ __global__ __launch_bounds__(FT) void out_fwd_bf16_kernel(
     }
     f4 yo[2];  // C_i . H_c^T: rows i, columns p = 16 (2 team + k) + r
     zero(yo);
-    for (int ks = 0; ks < kn; ++ks) {
-      const bf16x8 a = frag_rows<16>(sC, 16 * wt, 4 * ks);
+    {
+      const RowsAt<16> ar16 = opaque(r16_);
 #pragma unroll
-      for (int k = 0; k < 2; ++k) yo[k] = mfma(a, frag_rows<16>(sH, 16 * (2 * team + k), 4 * ks), yo[k]);
+      for (int kh = 0; kh < FKN; kh += 2) {  // two k-steps per batch of reads
+        bf16x8 fa[2], fb[2][2];
+#pragma unroll
+        for (int d = 0; d < 2; ++d) {
+          fa[d] = frag_rows(sC, 16 * wt, 4 * (kh + d), ar16);
+#pragma unroll
+          for (int k = 0; k < 2; ++k) fb[d][k] = frag_rows(sH, 16 * (2 * team + k), 4 * (kh + d), ar16);
+        }
+        sched_ds_reads<6>();
+#pragma unroll
+        for (int d = 0; d < 2; ++d)
+#pragma unroll
+          for (int k = 0; k < 2; ++k) yo[k] = mfma(fa[d], fb[d][k], yo[k]);
+        sched_mfmas<4>();
+      }
     }
     lds_barrier();
     const float Dh = D[h];
