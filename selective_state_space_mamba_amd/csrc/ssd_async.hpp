@@ -203,6 +203,38 @@ __device__ __forceinline__ bf16x8 frag_cols(const lds_char* t, int k0, int m0, C
   return __builtin_bit_cast(bf16x8, v);
 }
 
+// A 16 x 16 block of a tile in the MFMA accumulator layout: lane (r, q) gets
+// elements (m0 + 4q + e, n0 + r), e = 0..3, as bf16 pairs {e0 | e1 << 16,
+// e2 | e3 << 16}, from one transpose read (lane i of a 16-lane group reads the
+// 4 elements at row m0 + 4q + i/4, column n0 + 4 (i % 4)).  m0 and n0 are
+// multiples of 16; the per-lane offset is XOR-composed like the fragments'.
+template <int CPR>
+struct AccAt {
+  int b;
+};
+template <int CPR>
+__device__ __forceinline__ AccAt<CPR> acc_at() {
+  const int l = lane_id(), i = l & 15, q = l >> 4;
+  const int ra = 4 * q + (i >> 2);
+  return {ra * (CPR * 16) + ((((i >> 1) & 1) ^ swz<CPR>(ra)) << 4) + ((i & 1) << 3)};
+}
+template <int CPR>
+__device__ __forceinline__ AccAt<CPR> opaque(AccAt<CPR> a) {
+  asm volatile("" : "+v"(a.b));
+  return a;
+}
+template <int CPR>
+__device__ __forceinline__ u32x2 block_acc(const lds_char* t, int m0, int n0, AccAt<CPR> a) {
+  const short4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) short4_t*)(t + ((a.b ^ ((n0 >> 3) << 4)) + m0 * (CPR * 16))));
+  return __builtin_bit_cast(u32x2, v);
+}
+// Element e of a block_acc() result, as f32.
+__device__ __forceinline__ float acc_elem(const u32x2& v, int e) {
+  const uint32_t d = v[e >> 1];
+  return __uint_as_float((e & 1) ? (d & 0xFFFF0000u) : (d << 16));
+}
+
 // One element (row, col) of a swizzled tile, as f32.
 template <int CPR>
 __device__ __forceinline__ float tile_elem(const lds_char* t, int row, int col) {

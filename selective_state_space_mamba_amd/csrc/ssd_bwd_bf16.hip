@@ -124,13 +124,14 @@ __global__ __launch_bounds__(BT) void bwd_col_bf16_kernel(
 
   const int l = lane_id(), w = wave_id(), r = l & 15, q = l >> 4;
   const int team = w >> 2, wt = w & 3;
-  const int ti = 32 * team;
+  const int ti = 32 * team;  // this team's rows inside every 64-row block
   // per-lane fragment offsets (tiles of 2, 8 and 16 chunks per row)
   const RowsAt<8> r8_ = rows_at<8>();
   const RowsAt<16> r16_ = rows_at<16>();
   const ColsAt<2> c2_ = cols_at<2>();
   const ColsAt<8> c8_ = cols_at<8>();
-  const ColsAt<16> c16_ = cols_at<16>();  // this team's rows inside every 64-row block
+  const ColsAt<16> c16_ = cols_at<16>();
+  const AccAt<8> a8_ = acc_at<8>();
   const int64_t row0 = static_cast<int64_t>(bi) * T + static_cast<int64_t>(c) * Q;
   const int j0 = jb * BQ, vj = min(BQ, Q - j0);
   const int nib = nb - jb;
@@ -233,7 +234,7 @@ __global__ __launch_bounds__(BT) void bwd_col_bf16_kernel(
     f4 dxa[2];  // sum over rows i of G_ij dy_i: rows j, columns p = 16 (2 team + k) + r
     zero(dxa);
     float csum[4] = {0.f, 0.f, 0.f, 0.f}, dsum[4] = {0.f, 0.f, 0.f, 0.f};
-    uint32_t dsk[4];  // dy_j at columns p = ti + r and ti + 16 + r (bf16 pair)
+    u32x2 dsk[2];  // dy_j at columns p = ti + 16 k + r, accumulator layout
 
 #pragma unroll
     for (int u = 0; u < NBMAX; ++u) {
@@ -296,11 +297,9 @@ __global__ __launch_bounds__(BT) void bwd_col_bf16_kernel(
               gv[tt][e] = G1;
             }
           }
+          const AccAt<8> aa8 = opaque(a8_);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int jl = 16 * wt + 4 * q + e;
-            dsk[e] = pack_bf16(tile_elem<8>(dyt, jl, ti + r), tile_elem<8>(dyt, jl, ti + 16 + r));
-          }
+          for (int k = 0; k < 2; ++k) dsk[k] = block_acc(dyt, 16 * wt, ti + 16 * k, aa8);
         } else {
           float cf[4], cfd[4];
 #pragma unroll
@@ -387,15 +386,22 @@ __global__ __launch_bounds__(BT) void bwd_col_bf16_kernel(
       for (int k = 0; k < 4; ++k) v[k] = mfma(fa, fb[k], v[k]);
       sched_mfmas<4>();
     }
+    u32x2 xa[2];  // x_j at columns p = 16 (2 team + k) + r, accumulator layout
+    {
+      const AccAt<8> aa8 = opaque(a8_);
+#pragma unroll
+      for (int k = 0; k < 2; ++k) xa[k] = block_acc(xt, 16 * wt, 16 * (2 * team + k), aa8);
+    }
     const float s_end = sSh[Q - 1];
     float wj[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int jl = 16 * wt + 4 * q + e;
-      wj[e] = (j0 + jl < Q) ? __expf(s_end - sj[e]) : 0.f;
+      const float wx = __expf(s_end - sj[e]);
+      wj[e] = (j0 + jl < Q) ? wx : 0.f;
       float part = 0.f;
 #pragma unroll
-      for (int k = 0; k < 2; ++k) part += bg[k][e] * tile_elem<8>(xt, jl, 16 * (2 * team + k) + r);
+      for (int k = 0; k < 2; ++k) part += bg[k][e] * acc_elem(xa[k], e);
       part = row_sum16(part);
       const float cs = row_sum16(csum[e]), ds = row_sum16(dsum[e]);
       if (r == 15) {
@@ -412,8 +418,7 @@ __global__ __launch_bounds__(BT) void bwd_col_bf16_kernel(
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int jq = j0 + 16 * wt + 4 * q + e, p = 16 * (2 * team + k) + r;
-        const uint32_t pk = dsk[e];
-        const float dyv = __uint_as_float(k ? (pk & 0xFFFF0000u) : (pk << 16));
+        const float dyv = acc_elem(dsk[k], e);
         if (jq < Q && p < P)
           dx[(row0 + jq) * HP + static_cast<int64_t>(h) * P + p] =
               dtj[e] * (dxa[k][e] + wj[e] * bg[k][e]) + Dh * dyv;
@@ -556,6 +561,7 @@ __global__ __launch_bounds__(BT) void bwd_row_bf16_kernel(
   const RowsAt<16> r16_ = rows_at<16>();
   const ColsAt<2> c2_ = cols_at<2>();
   const ColsAt<16> c16_ = cols_at<16>();
+  const AccAt<16> a16_ = acc_at<16>();
   const int64_t row0 = static_cast<int64_t>(bi) * T + static_cast<int64_t>(c) * Q;
   const int i0 = ib * BQ, vi = min(BQ, Q - i0);
   const int nj = ib + 1;
@@ -757,15 +763,22 @@ __global__ __launch_bounds__(BT) void bwd_row_bf16_kernel(
         sched_mfmas<4>();
       }
     }
+    u32x2 ca[4];  // C_i at columns n = 16 (4 team + k) + r, accumulator layout
+    {
+      const AccAt<16> aa16 = opaque(a16_);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) ca[k] = block_acc(sC, 16 * wt, 16 * (4 * team + k), aa16);
+    }
     float ex[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int il = 16 * wt + 4 * q + e;
-      ex[e] = (i0 + il < Q) ? __expf(si[e]) : 0.f;
+      const float xe = __expf(si[e]);
+      ex[e] = (i0 + il < Q) ? xe : 0.f;
       float part = 0.f;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        part += u[k][e] * tile_elem<16>(sC, il, 16 * (4 * team + k) + r);
+        part += u[k][e] * acc_elem(ca[k], e);
         ua[k][e] += ex[e] * u[k][e];
       }
       part = row_sum16(part);

@@ -114,6 +114,7 @@ __global__ __launch_bounds__(FT) void out_fwd_bf16_kernel(
   const RowsAt<16> r16_ = rows_at<16>();
   const ColsAt<2> c2_ = cols_at<2>();
   const ColsAt<8> c8_ = cols_at<8>();
+  const AccAt<8> a8_ = acc_at<8>();
   const int64_t row0 = static_cast<int64_t>(bi) * T + static_cast<int64_t>(c) * Q;
   const int i0 = ib * BQ, vi = min(BQ, Q - i0);
   const int nj = ib + 1;
@@ -205,7 +206,7 @@ __global__ __launch_bounds__(FT) void out_fwd_bf16_kernel(
     }
     f4 ya[4];  // sum over this team's columns j of G_ij x_j: rows i, columns p = 16 pt + r
     zero(ya);
-    uint32_t xsk[4];  // x_i at columns p = 32 team + r and 32 team + 16 + r (bf16 pair)
+    u32x2 xsk[2];  // x_i at columns p = 32 team + 16 k + r, accumulator layout
 
 #pragma unroll
     for (int jb = 0; jb < NBMAX; ++jb) {
@@ -250,11 +251,9 @@ __global__ __launch_bounds__(FT) void out_fwd_bf16_kernel(
               gv[tt][e] = L * dtj * cbt[tt][e];
             }
           }
+          const AccAt<8> aa8 = opaque(a8_);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int il = 16 * wt + 4 * q + e;
-            xsk[e] = pack_bf16(tile_elem<8>(xt, il, 32 * team + r), tile_elem<8>(xt, il, 32 * team + 16 + r));
-          }
+          for (int k = 0; k < 2; ++k) xsk[k] = block_acc(xt, 16 * wt, 32 * team + 16 * k, aa8);
         } else {
 #pragma unroll
           for (int tt = 0; tt < 2; ++tt) {
@@ -312,8 +311,7 @@ __global__ __launch_bounds__(FT) void out_fwd_bf16_kernel(
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int iq = i0 + 16 * wt + 4 * q + e, p = 16 * pt + r;
-        const uint32_t pk = xsk[e];
-        const float xv = __uint_as_float(k ? (pk & 0xFFFF0000u) : (pk << 16));
+        const float xv = acc_elem(xsk[k], e);
         const float ex = __expf(si[e]);
         if (iq < Q && p < P)
           y[(row0 + iq) * HP + static_cast<int64_t>(h) * P + p] =
