@@ -169,10 +169,20 @@ __device__ __forceinline__ RowsAt<CPR> rows_at() {
   const int l = lane_id(), r = l & 15, q = l >> 4;
   return {r * (CPR * 16) + ((q ^ swz<CPR>(r)) << 4)};
 }
+// Strips (tiles of 32-byte rows that a wave writes from its MFMA output and
+// the transpose read consumes) are stored with rows 8..15 of every 16 moved
+// four rows on and their two 16-byte halves swapped: byte b of row R is at
+// (32 R + b) ^ (0x90 if bit 3 of R is set).  Unswizzled, the transpose read
+// (rows 8q + 0..3 per 16-lane group) and the 8-byte row writes meet the same
+// banks two ways.
+__device__ __forceinline__ int strip_off(int row, int byte) {
+  return (row * 32 + byte) ^ (((row >> 3) & 1) * 0x90);
+}
 template <int CPR>
 __device__ __forceinline__ ColsAt<CPR> cols_at() {
   const int l = lane_id(), i = l & 15, q = l >> 4;
   const int half = (i & 1) << 3, ra = 8 * q + (i >> 2);
+  if constexpr (CPR == 2) return {strip_off(ra, (((i >> 1) & 1) << 4) + half)};
   return {ra * (CPR * 16) + ((((i >> 1) & 1) ^ swz<CPR>(ra)) << 4) + half};
 }
 template <int CPR>
@@ -192,13 +202,15 @@ __device__ __forceinline__ bf16x8 frag_rows(const lds_char* t, int m0, int kc, R
 template <int CPR>
 __device__ __forceinline__ bf16x8 frag_cols(const lds_char* t, int k0, int m0, ColsAt<CPR> a) {
   // rows r and r + 4 (r % 8 < 4) differ in the low bit of the swizzle of 8-
-  // and 16-chunk rows, and not at all for the others
-  constexpr int flip = (CPR == 8 || CPR == 16) ? 16 : 0;
+  // and 16-chunk rows, not at all for 4- and 32-chunk rows; in a strip row
+  // r + 4 is the XOR of row r's offset with 128 (strip_off)
+  constexpr int flip = (CPR == 8 || CPR == 16) ? 16 : (CPR == 2 ? 128 : 0);
+  constexpr int four_rows = CPR == 2 ? 0 : 4 * CPR * 16;
   const int x = (m0 >> 3) << 4, o = k0 * (CPR * 16);
   const short4_t lo =
       __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) short4_t*)(t + ((a.b ^ x) + o)));
   const short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) short4_t*)(t + ((a.b ^ (x ^ flip)) + o + 4 * CPR * 16)));
+      (__attribute__((address_space(3))) short4_t*)(t + ((a.b ^ (x ^ flip)) + o + four_rows)));
   const short8_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   return __builtin_bit_cast(bf16x8, v);
 }

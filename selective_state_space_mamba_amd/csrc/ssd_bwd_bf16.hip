@@ -76,7 +76,7 @@ __device__ __forceinline__ void put_strip(lds_char* strip, const f4 (&v)[2]) {
   const int l = lane_id(), r = l & 15, q = l >> 4;
 #pragma unroll
   for (int tt = 0; tt < 2; ++tt)
-    *(__attribute__((address_space(3))) u32x2*)(strip + (16 * tt + r) * 32 + 8 * q) =
+    *(__attribute__((address_space(3))) u32x2*)(strip + strip_off(16 * tt + r, 8 * q)) =
         u32x2{pack_bf16(v[tt][0], v[tt][1]), pack_bf16(v[tt][2], v[tt][3])};
 }
 
