@@ -92,7 +92,9 @@ __global__ __launch_bounds__(BT) void bwd_col_bf16_kernel(
   __shared__ __attribute__((aligned(1024))) char sDy1_[TILE_P];        // dy rows i, odd steps
   __shared__ __attribute__((aligned(1024))) char sGam_[TILE_N];        // Gamma [p][n]; C tile slot
   __shared__ __attribute__((aligned(1024))) char sG_[BW * STRIP];      // per-wave strips [i][j]
-  __shared__ f4 sCB[NBMAX][2][BW][WAVE];                               // C.B^T, lane-linear
+  // C.B^T, lane-linear; before it is formed and after its last use, the C
+  // tiles of blocks ib (tile ib in the ib-th 16 KB)
+  __shared__ __attribute__((aligned(1024))) f4 sCB[NBMAX][2][BW][WAVE];
   __shared__ float sRed[2][BQ][3];                                     // column sums, diagonal, R' halves
   __shared__ __attribute__((aligned(16))) float sS[2][QMAX];
   __shared__ __attribute__((aligned(16))) float sDt[2][QMAX];
@@ -101,6 +103,7 @@ __global__ __launch_bounds__(BT) void bwd_col_bf16_kernel(
   lds_char* const sDy[2] = {lds_ptr(sDy0_), lds_ptr(sDy1_)};
   lds_char* const sGam = lds_ptr(sGam_);
   lds_char* const sG = lds_ptr(sG_);
+  lds_char* const sCt = lds_ptr(sCB);
 
   const int nc = T / Q, nb = (Q + BQ - 1) / BQ;
   const int hpg = H / G, hps = hpg / nsplit;
@@ -164,29 +167,40 @@ __global__ __launch_bounds__(BT) void bwd_col_bf16_kernel(
     const int i0 = (jb + u) * BQ;
     tile_async<64, 8, BW>(dst, rdy, i0 * HPb + head(hh) * P * 2, HPb, min(BQ, Q - i0), pch);
   };
-  auto load_c = [&](int u, lds_char* dst) {
-    const int i0 = (jb + u) * BQ;
-    tile_async<64, 16, BW>(dst, rc, i0 * GNb + goff, GNb, min(BQ, Q - i0), nch);
+  // the C tiles of blocks ib >= jb, each to its own 16 KB of the C.B^T area
+  auto load_cs = [&]() {
+#pragma unroll
+    for (int u = 0; u < NBMAX; ++u) {
+      if (u < nib) {
+        const int i0 = (jb + u) * BQ;
+        tile_async<64, 16, BW>(sCt + (jb + u) * TILE_N, rc, i0 * GNb + goff, GNb, min(BQ, Q - i0), nch);
+      }
+    }
   };
 
-  // ---- B rows of block jb, then C.B^T for every block ib >= jb (C tiles two at a time)
+  // ---- B rows of block jb, the C tiles of blocks ib >= jb and the first
+  // head's x and dy tiles, in flight together (the second block of a pair
+  // finds its C tiles where the first block's dB phase left them), then
+  // C.B^T for every block ib >= jb, over the C tiles once all are read
   tile_async<64, 16, BW>(sB, rb, j0 * GNb + goff, GNb, vj, nch);
+  if (pass == 0) load_cs();
   load_dt(0);
+  load_x(0);
+  load_dy(0, 0, sDy[0]);
+  wait_vm<0>();
+  __syncthreads();
+  // Two blocks at a time: C.B^T of blocks jb + u goes to slot u, which held
+  // the C tile of block u (ib >= u, read before the barrier) or none of ours
 #pragma unroll
   for (int u0 = 0; u0 < NBMAX; u0 += 2) {
     if (u0 < nib) {
-      load_c(u0, sX);
-      if (u0 + 1 < nib) load_c(u0 + 1, sGam);
-      wait_vm<0>();
-      __syncthreads();
+      f4 cbr[2][2];
 #pragma unroll
       for (int d = 0; d < 2; ++d) {
-        const int u = u0 + d;
-        if (u < nib) {
-          const lds_char* ct = d ? sGam : sX;
+        if (u0 + d < nib) {
+          const lds_char* ct = sCt + (jb + u0 + d) * TILE_N;
           const RowsAt<16> ar16 = opaque(r16_);
-          f4 cb[2];
-          zero(cb);
+          zero(cbr[d]);
           bf16x8 fa[KN], fb[KN][2];
 #pragma unroll
           for (int ks = 0; ks < KN; ++ks) {
@@ -198,18 +212,20 @@ __global__ __launch_bounds__(BT) void bwd_col_bf16_kernel(
 #pragma unroll
           for (int ks = 0; ks < KN; ++ks)
 #pragma unroll
-            for (int tt = 0; tt < 2; ++tt) cb[tt] = mfma(fa[ks], fb[ks][tt], cb[tt]);
+            for (int tt = 0; tt < 2; ++tt) cbr[d][tt] = mfma(fa[ks], fb[ks][tt], cbr[d][tt]);
           sched_mfmas<2 * KN>();
-          sCB[u][0][w][l] = cb[0];
-          sCB[u][1][w][l] = cb[1];
         }
       }
       __syncthreads();
+#pragma unroll
+      for (int d = 0; d < 2; ++d) {
+        if (u0 + d < nib) {
+          sCB[u0 + d][0][w][l] = cbr[d][0];
+          sCB[u0 + d][1][w][l] = cbr[d][1];
+        }
+      }
     }
   }
-  load_x(0);
-  load_dy(0, 0, sDy[0]);
-  wait_vm<0>();
   scan_store(dtb, -__expf(A_log[head(0)]), sS[0], sDt[0]);
   __syncthreads();
 
@@ -347,6 +363,8 @@ __global__ __launch_bounds__(BT) void bwd_col_bf16_kernel(
     }
 
     // ---- state terms of head hh; the next head's first tiles start loading
+    // (after the last head, the C tiles for the dB phase, over C.B^T)
+    if (hh + 1 == hps) load_cs();
     const RowsAt<8> ar8 = opaque(r8_);
     const RowsAt<16> ar16 = opaque(r16_);
     const ColsAt<16> ac16 = opaque(c16_);
@@ -447,43 +465,32 @@ __global__ __launch_bounds__(BT) void bwd_col_bf16_kernel(
   }
 
   // ---- dB_j = sum_i W_ij C_i + state terms, for this team's d_state columns
-  // over all rows i (own and partner strips); two blocks at a time, their C
-  // tiles in the x and Gamma regions and their W strips in sG and a dy slot
+  // over all rows i (own and partner strips): the W strips of block u go to
+  // wset[u], the C tiles are in place since the last head's state step
   f4 dbp[4];
   zero(dbp);
-  lds_char* const wset[2] = {sG, sDy[0]};
+  lds_char* const wset[NBMAX] = {sG, sDy[0], sDy[1], sGam};
 #pragma unroll
-  for (int u0 = 0; u0 < NBMAX; u0 += 2) {
-    if (u0 < nib) {
-      load_c(u0, sX);
-      if (u0 + 1 < nib) load_c(u0 + 1, sGam);
+  for (int u = 0; u < NBMAX; ++u)
+    if (u < nib) put_strip(wset[u] + w * STRIP, ws[u]);
+  __syncthreads();
 #pragma unroll
-      for (int d = 0; d < 2; ++d)
-        if (u0 + d < nib) put_strip(wset[d] + w * STRIP, ws[u0 + d]);
-      wait_vm<0>();
-      __syncthreads();
+  for (int u = 0; u < NBMAX; ++u) {
+    if (u < nib) {
+      const lds_char* ct = sCt + (jb + u) * TILE_N;
+      const ColsAt<2> ac2 = opaque(c2_);
+      const ColsAt<16> ac16 = opaque(c16_);
 #pragma unroll
-      for (int d = 0; d < 2; ++d) {
-        if (u0 + d < nib) {
-          const lds_char* ct = d ? sGam : sX;
-          const ColsAt<2> ac2 = opaque(c2_);
-          const ColsAt<16> ac16 = opaque(c16_);
-          bf16x8 fa[2], fb[2][4];
+      for (int ks = 0; ks < 2; ++ks) {
+        bf16x8 fa, fb[4];
+        fa = frag_cols(wset[u] + (4 * ks + wt) * STRIP, 0, 0, ac2);
 #pragma unroll
-          for (int ks = 0; ks < 2; ++ks) {
-            fa[ks] = frag_cols(wset[d] + (4 * ks + wt) * STRIP, 0, 0, ac2);
+        for (int k = 0; k < 4; ++k) fb[k] = frag_cols(ct, 32 * ks, 16 * (4 * team + k), ac16);
+        sched_ds_reads<10>();
 #pragma unroll
-            for (int k = 0; k < 4; ++k) fb[ks][k] = frag_cols(ct, 32 * ks, 16 * (4 * team + k), ac16);
-          }
-          sched_ds_reads<20>();
-#pragma unroll
-          for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-            for (int k = 0; k < 4; ++k) dbp[k] = mfma(fa[ks], fb[ks][k], dbp[k]);
-          sched_mfmas<8>();
-        }
+        for (int k = 0; k < 4; ++k) dbp[k] = mfma(fa, fb[k], dbp[k]);
+        sched_mfmas<4>();
       }
-      __syncthreads();
     }
   }
   const int64_t batch = gridDim.x / (npair * nsplit * G * nc);
@@ -523,7 +530,9 @@ __global__ __launch_bounds__(BT) void bwd_row_bf16_kernel(
   __shared__ __attribute__((aligned(1024))) char sX1_[TILE_P];         // x rows j, odd steps
   __shared__ __attribute__((aligned(1024))) char sH_[TILE_N];          // H_c [p][n] (bf16); B tile slot
   __shared__ __attribute__((aligned(1024))) char sG_[BW * STRIP];      // per-wave W strips [j][i]
-  __shared__ f4 sCB[NBMAX][2][BW][WAVE];                               // C.B^T, lane-linear
+  // C.B^T, lane-linear; before it is formed and after its last use, the B
+  // tiles of blocks jb (tile jb in the jb-th 16 KB)
+  __shared__ __attribute__((aligned(1024))) f4 sCB[NBMAX][2][BW][WAVE];
   __shared__ float sRed[2][BQ][2];                                     // row-sum and readout halves
   __shared__ float sDD[BW][4];                                         // dD partials
   __shared__ __attribute__((aligned(16))) float sS[2][QMAX];
@@ -533,6 +542,7 @@ __global__ __launch_bounds__(BT) void bwd_row_bf16_kernel(
   lds_char* const sX[2] = {lds_ptr(sX0_), lds_ptr(sX1_)};
   lds_char* const sH = lds_ptr(sH_);
   lds_char* const sG = lds_ptr(sG_);
+  lds_char* const sBt = lds_ptr(sCB);
 
   const int nc = T / Q, nb = (Q + BQ - 1) / BQ;
   const int hpg = H / G, hps = hpg / nsplit;
@@ -594,29 +604,40 @@ __global__ __launch_bounds__(BT) void bwd_row_bf16_kernel(
   auto load_dy = [&](int hh) {
     tile_async<64, 8, BW>(sDy + (hh & 1) * TILE_P, rdy, i0 * HPb + head(hh) * P * 2, HPb, vi, pch);
   };
-  auto load_b = [&](int jb, lds_char* dst) {
-    const int j0 = jb * BQ;
-    tile_async<64, 16, BW>(dst, rb, j0 * GNb + goff, GNb, min(BQ, Q - j0), nch);
+  // the B tiles of blocks jb <= ib, each to its own 16 KB of the C.B^T area
+  auto load_bs = [&]() {
+#pragma unroll
+    for (int jb = 0; jb < NBMAX; ++jb) {
+      if (jb < nj) {
+        const int j0 = jb * BQ;
+        tile_async<64, 16, BW>(sBt + jb * TILE_N, rb, j0 * GNb + goff, GNb, min(BQ, Q - j0), nch);
+      }
+    }
   };
 
-  // ---- C rows of block ib, then C.B^T for every block jb <= ib (B tiles two at a time)
+  // ---- C rows of block ib, the B tiles of blocks jb <= ib and the first
+  // head's dy and x tiles, in flight together (the second block of a pair
+  // finds its B tiles where the first block's dC phase left them), then
+  // C.B^T for every block jb <= ib, over the B tiles once all are read
   tile_async<64, 16, BW>(sC, rc, i0 * GNb + goff, GNb, vi, nch);
+  if (pass == 0) load_bs();
   load_dt(0);
+  load_dy(0);
+  load_x(0, 0, sX[0]);
+  wait_vm<0>();
+  __syncthreads();
+  // Two blocks at a time: C.B^T of block jb goes over the B tile of block jb,
+  // which every wave has read before the barrier
 #pragma unroll
   for (int jb0 = 0; jb0 < NBMAX; jb0 += 2) {
     if (jb0 < nj) {
-      load_b(jb0, sDy);
-      if (jb0 + 1 < nj) load_b(jb0 + 1, sH);
-      wait_vm<0>();
-      __syncthreads();
+      f4 cbr[2][2];
 #pragma unroll
       for (int d = 0; d < 2; ++d) {
-        const int jb = jb0 + d;
-        if (jb < nj) {
-          const lds_char* bt = d ? sH : sDy;
+        if (jb0 + d < nj) {
+          const lds_char* bt = sBt + (jb0 + d) * TILE_N;
           const RowsAt<16> ar16 = opaque(r16_);
-          f4 cb[2];
-          zero(cb);
+          zero(cbr[d]);
           bf16x8 fa[KN], fb[KN][2];
 #pragma unroll
           for (int ks = 0; ks < KN; ++ks) {
@@ -628,18 +649,20 @@ __global__ __launch_bounds__(BT) void bwd_row_bf16_kernel(
 #pragma unroll
           for (int ks = 0; ks < KN; ++ks)
 #pragma unroll
-            for (int tt = 0; tt < 2; ++tt) cb[tt] = mfma(fa[ks], fb[ks][tt], cb[tt]);
+            for (int tt = 0; tt < 2; ++tt) cbr[d][tt] = mfma(fa[ks], fb[ks][tt], cbr[d][tt]);
           sched_mfmas<2 * KN>();
-          sCB[jb][0][w][l] = cb[0];
-          sCB[jb][1][w][l] = cb[1];
         }
       }
       __syncthreads();
+#pragma unroll
+      for (int d = 0; d < 2; ++d) {
+        if (jb0 + d < nj) {
+          sCB[jb0 + d][0][w][l] = cbr[d][0];
+          sCB[jb0 + d][1][w][l] = cbr[d][1];
+        }
+      }
     }
   }
-  load_dy(0);
-  load_x(0, 0, sX[0]);
-  wait_vm<0>();
   scan_store(dtb, -__expf(A_log[head(0)]), sS[0], sDt[0]);
   __syncthreads();
 
@@ -741,7 +764,9 @@ __global__ __launch_bounds__(BT) void bwd_row_bf16_kernel(
       }
     }
 
-    // ---- per-head terms; the next head's first tiles start loading
+    // ---- per-head terms; the next head's first tiles start loading (after
+    // the last head, the B tiles for the dC phase, over C.B^T)
+    if (hh + 1 == hps) load_bs();
     if (hh + 1 < hps) {
       load_dy(hh + 1);
       load_x(hh + 1, 0, sX[0]);
@@ -816,38 +841,31 @@ __global__ __launch_bounds__(BT) void bwd_row_bf16_kernel(
   }
 
   // ---- dC_i = sum_j W_ij B_j + sum_h exp(s_i) U_i for this team's d_state
-  // columns over all columns j (own and partner strips); B tiles two at a time
-  lds_char* const wset[2] = {sG, sX[0]};
+  // columns over all columns j (own and partner strips): the W strips of
+  // block jb go to wset[jb], the B tiles are in place since the last head's
+  // per-head terms
+  lds_char* const wset[NBMAX] = {sG, sX[0], sX[1], sDy};
 #pragma unroll
-  for (int jb0 = 0; jb0 < NBMAX; jb0 += 2) {
-    if (jb0 < nj) {
-      load_b(jb0, sDy);
-      if (jb0 + 1 < nj) load_b(jb0 + 1, sH);
+  for (int jb = 0; jb < NBMAX; ++jb)
+    if (jb < nj) put_strip(wset[jb] + w * STRIP, ws[jb]);
+  __syncthreads();
 #pragma unroll
-      for (int d = 0; d < 2; ++d)
-        if (jb0 + d < nj) put_strip(wset[d] + w * STRIP, ws[jb0 + d]);
-      wait_vm<0>();
-      __syncthreads();
+  for (int jb = 0; jb < NBMAX; ++jb) {
+    if (jb < nj) {
+      const lds_char* bt = sBt + jb * TILE_N;
+      const ColsAt<2> ac2 = opaque(c2_);
+      const ColsAt<16> ac16 = opaque(c16_);
 #pragma unroll
-      for (int d = 0; d < 2; ++d) {
-        if (jb0 + d < nj) {
-          const lds_char* bt = d ? sH : sDy;
-          const ColsAt<2> ac2 = opaque(c2_);
-          const ColsAt<16> ac16 = opaque(c16_);
+      for (int ks = 0; ks < 2; ++ks) {
+        bf16x8 fa, fb[4];
+        fa = frag_cols(wset[jb] + (4 * ks + wt) * STRIP, 0, 0, ac2);
 #pragma unroll
-          for (int ks = 0; ks < 2; ++ks) {
-            bf16x8 fa, fb[4];
-            fa = frag_cols(wset[d] + (4 * ks + wt) * STRIP, 0, 0, ac2);
+        for (int kk = 0; kk < 4; ++kk) fb[kk] = frag_cols(bt, 32 * ks, 16 * (4 * team + kk), ac16);
+        sched_ds_reads<10>();
 #pragma unroll
-            for (int k = 0; k < 4; ++k) fb[k] = frag_cols(bt, 32 * ks, 16 * (4 * team + k), ac16);
-            sched_ds_reads<10>();
-#pragma unroll
-            for (int k = 0; k < 4; ++k) ua[k] = mfma(fa, fb[k], ua[k]);
-            sched_mfmas<4>();
-          }
-        }
+        for (int kk = 0; kk < 4; ++kk) ua[kk] = mfma(fa, fb[kk], ua[kk]);
+        sched_mfmas<4>();
       }
-      __syncthreads();
     }
   }
   const int64_t batch = gridDim.x / (npair * nsplit * G * nc);

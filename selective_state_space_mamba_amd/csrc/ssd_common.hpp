@@ -73,7 +73,9 @@ __device__ __forceinline__ f4 mfma(bf16x8 a, bf16x8 b, f4 c) {
 }
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (WAVE - 1); }
-__device__ __forceinline__ int wave_id() { return threadIdx.x / WAVE; }
+// Uniform across the wave; readfirstlane lets the compiler keep it, and the
+// LDS and tile addresses derived from it, in scalar registers.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE); }
 
 // Fragment of rows r0..r0+15 and k-slice starting at k0 of an LDS view.
 template <bool BF, bool KC>
