@@ -63,11 +63,17 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc_ptr(const void* base
 
 __device__ __forceinline__ lds_char* lds_ptr(void* p) { return (lds_char*)p; }
 
-// vmcnt(n) with the other counters left alone.
+// vmcnt(n) with the other counters left alone: at most n of this wave's
+// vector-memory operations (loads, stores, asynchronous copies; they retire
+// in issue order) remain outstanding.  The empty asm statements keep the
+// compiler from moving memory operations across the wait, so that n counts
+// what the source issued before it.
 template <int N>
 __device__ __forceinline__ void wait_vm() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
+  __asm__ volatile("" ::: "memory");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0070 | 0x0F00);
+  __asm__ volatile("" ::: "memory");
 }
 
 // Workgroup barrier for LDS data written with ds_write only: waits for this

@@ -49,6 +49,7 @@ constexpr int STRIP = 32 * 32;      // bytes of a 32 x 16 bf16 strip
 // problem's P and N, so the contractions always run over the full tiles
 constexpr int KP = PMAX / 32;
 constexpr int KN = NMAX / 32;
+static_assert(NBMAX <= 4, "the dB and dC phases hold at most four blocks' W strips");
 }  // namespace
 
 // s (within-chunk inclusive cumsum of dt A) and dt for t < Q, from the dt bits
@@ -120,6 +121,7 @@ __global__ __launch_bounds__(BT) void bwd_col_bf16_kernel(
   const int c = idx % nc;
   const int bi = idx / nc;
 
+  uint32_t dtb[4];  // dt bits of t = 4l .. 4l+3 for the next scan, converted when used
   for (int pass = 0; pass < 2; ++pass) {
   const int jb = pass ? nb - 1 - kpair : kpair;  // the block with the most rows i first
   if (pass && jb == kpair) break;
@@ -150,7 +152,6 @@ __global__ __launch_bounds__(BT) void bwd_col_bf16_kernel(
   const __amdgpu_buffer_rsrc_t rdt = make_rsrc_ptr(dt + row0 * H);
   auto head = [&](int hh) { return g * hpg + sp * hps + hh; };
 
-  uint32_t dtb[4];  // dt bits of t = 4l .. 4l+3 for the next scan, converted when used
   auto load_dt = [&](int hh) {
     const int h = head(hh);
 #pragma unroll
@@ -167,6 +168,17 @@ __global__ __launch_bounds__(BT) void bwd_col_bf16_kernel(
     const int i0 = (jb + u) * BQ;
     tile_async<64, 8, BW>(dst, rdy, i0 * HPb + head(hh) * P * 2, HPb, min(BQ, Q - i0), pch);
   };
+  auto load_gam = [&](int hh) { tile_async<64, 16, BW>(sGam, rg, head(hh) * P * N * 2, N * 2, P, nch); };
+  // B rows, the first head's x, dy, Gamma and dt for column block jx (this
+  // pass's, or the next pass's while this one finishes)
+  auto load_first = [&](int jx) {
+    const int jx0 = jx * BQ, vjx = min(BQ, Q - jx0);
+    tile_async<64, 16, BW>(sB, rb, jx0 * GNb + goff, GNb, vjx, nch);
+    tile_async<64, 8, BW>(sX, rx, jx0 * HPb + head(0) * P * 2, HPb, vjx, pch);
+    tile_async<64, 8, BW>(sDy[0], rdy, jx0 * HPb + head(0) * P * 2, HPb, vjx, pch);
+    load_gam(0);
+    load_dt(0);
+  };
   // the C tiles of blocks ib >= jb, each to its own 16 KB of the C.B^T area
   auto load_cs = [&]() {
 #pragma unroll
@@ -179,14 +191,13 @@ __global__ __launch_bounds__(BT) void bwd_col_bf16_kernel(
   };
 
   // ---- B rows of block jb, the C tiles of blocks ib >= jb and the first
-  // head's x and dy tiles, in flight together (the second block of a pair
-  // finds its C tiles where the first block's dB phase left them), then
-  // C.B^T for every block ib >= jb, over the C tiles once all are read
-  tile_async<64, 16, BW>(sB, rb, j0 * GNb + goff, GNb, vj, nch);
-  if (pass == 0) load_cs();
-  load_dt(0);
-  load_x(0);
-  load_dy(0, 0, sDy[0]);
+  // head's tiles, in flight together (the second block of a pair finds them
+  // where the first block's dB phase left or loaded them), then C.B^T for
+  // every block ib >= jb, over the C tiles once all are read
+  if (pass == 0) {
+    load_first(jb);
+    load_cs();
+  }
   wait_vm<0>();
   __syncthreads();
   // Two blocks at a time: C.B^T of blocks jb + u goes to slot u, which held
@@ -249,6 +260,12 @@ __global__ __launch_bounds__(BT) void bwd_col_bf16_kernel(
     }
     f4 dxa[2];  // sum over rows i of G_ij dy_i: rows j, columns p = 16 (2 team + k) + r
     zero(dxa);
+    float Dh = 0.f, An = 0.f;  // D of this head, A_log of the next (read at its first step)
+    // column factors exp(s_i0 - s_j) <= 1 of the current off-diagonal block
+    // (i0 its first row), formed at the first such block and then carried:
+    // each further block multiplies them by exp(s_i0 - s_i0'), the factor of
+    // the block advance (s does not increase, so every factor is <= 1)
+    float cfc[4], sprev = 0.f;
     float csum[4] = {0.f, 0.f, 0.f, 0.f}, dsum[4] = {0.f, 0.f, 0.f, 0.f};
     u32x2 dsk[2];  // dy_j at columns p = ti + 16 k + r, accumulator layout
 
@@ -260,11 +277,17 @@ __global__ __launch_bounds__(BT) void bwd_col_bf16_kernel(
         const ColsAt<8> ac8 = opaque(c8_);
         const int i0 = (jb + u) * BQ;
         const lds_char* dyt = sDy[u & 1];
-        // tiles of later steps start loading now
+        // the next block's dy tile starts loading now; at a head's first step
+        // the next head's dt, issued last so that the step's end need not
+        // wait for it (this head's Gamma was loaded during the previous
+        // head's state step)
         if (u + 1 < nib) load_dy(hh, u + 1, sDy[(u + 1) & 1]);
         if (u == 0) {
-          tile_async<64, 16, BW>(sGam, rg, h * P * N * 2, N * 2, P, nch);
-          if (hh + 1 < hps) load_dt(hh + 1);
+          Dh = D[h];
+          if (hh + 1 < hps) {
+            An = A_log[head(hh + 1)];
+            load_dt(hh + 1);
+          }
         }
 
         // yx^T: rows j (this wave's 16), columns i = i0 + ti + 16 tt + r; the
@@ -318,9 +341,18 @@ __global__ __launch_bounds__(BT) void bwd_col_bf16_kernel(
           for (int k = 0; k < 2; ++k) dsk[k] = block_acc(dyt, 16 * wt, ti + 16 * k, aa8);
         } else {
           float cf[4], cfd[4];
+          if (u == 1) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) cfc[e] = __expf(sref - sj[e]);
+          } else {
+            const float adv = __expf(sref - sprev);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) cfc[e] *= adv;
+          }
+          sprev = sref;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            cf[e] = __expf(sref - sj[e]);
+            cf[e] = cfc[e];
             cfd[e] = cf[e] * dtj[e];
           }
 #pragma unroll
@@ -357,13 +389,17 @@ __global__ __launch_bounds__(BT) void bwd_col_bf16_kernel(
             for (int k = 0; k < 2; ++k) dxa[k] = mfma(ga[ks], gb[ks][k], dxa[k]);
           sched_mfmas<4>();
         }
-        wait_vm<0>();
-        __syncthreads();
+        if (u == 0 && hh + 1 < hps)
+          wait_vm<4>();  // all but the 4 dt loads
+        else
+          wait_vm<0>();
+        lds_barrier();
       }
     }
 
-    // ---- state terms of head hh; the next head's first tiles start loading
-    // (after the last head, the C tiles for the dB phase, over C.B^T)
+    // ---- state terms of head hh; the next head's x and dy tiles start
+    // loading, its Gamma once this head's is read (after the last head, the C
+    // tiles for the dB phase, over C.B^T)
     if (hh + 1 == hps) load_cs();
     const RowsAt<8> ar8 = opaque(r8_);
     const RowsAt<16> ar16 = opaque(r16_);
@@ -429,29 +465,19 @@ __global__ __launch_bounds__(BT) void bwd_col_bf16_kernel(
       }
     }
     lds_barrier();
-    const float Dh = D[h];
-    const int64_t tb = (static_cast<int64_t>(bi) * H + h) * T + static_cast<int64_t>(c) * Q;
+    if (hh + 1 < hps) load_gam(hh + 1);  // this head's Gamma is no longer read
+    float dxv[2][4];
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
+    for (int k = 0; k < 2; ++k)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int jq = j0 + 16 * wt + 4 * q + e, p = 16 * (2 * team + k) + r;
-        const float dyv = acc_elem(dsk[k], e);
-        if (jq < Q && p < P)
-          dx[(row0 + jq) * HP + static_cast<int64_t>(h) * P + p] =
-              dtj[e] * (dxa[k][e] + wj[e] * bg[k][e]) + Dh * dyv;
-      }
-    }
-    if (team == 0 && r == 15) {
+      for (int e = 0; e < 4; ++e) dxv[k][e] = dtj[e] * (dxa[k][e] + wj[e] * bg[k][e]) + Dh * acc_elem(dsk[k], e);
+    float ce[4], de[4], re[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int jl = 16 * wt + 4 * q + e, jq = j0 + jl;
-        if (jq < Q) {
-          colE[tb + jq] = sRed[0][jl][0] + sRed[1][jl][0];
-          diagE[tb + jq] = sRed[0][jl][1] + sRed[1][jl][1];
-          Rp[tb + jq] = wj[e] * (sRed[0][jl][2] + sRed[1][jl][2]);
-        }
-      }
+    for (int e = 0; e < 4; ++e) {
+      const int jl = 16 * wt + 4 * q + e;
+      ce[e] = sRed[0][jl][0] + sRed[1][jl][0];
+      de[e] = sRed[0][jl][1] + sRed[1][jl][1];
+      re[e] = wj[e] * (sRed[0][jl][2] + sRed[1][jl][2]);
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -459,39 +485,75 @@ __global__ __launch_bounds__(BT) void bwd_col_bf16_kernel(
 #pragma unroll
       for (int k = 0; k < 4; ++k) dbs[k][e] += f * v[k][e];
     }
-    if (hh + 1 < hps) scan_store(dtb, -__expf(A_log[head(hh + 1)]), sS[hb ^ 1], sDt[hb ^ 1]);
-    wait_vm<0>();
-    __syncthreads();
+    // the next head's x and dy tiles (all but Gamma's 2 copies) must be in
+    // LDS at the barrier; the stores below are issued after the wait and
+    // complete during the next step
+    if (hh + 1 < hps)
+      wait_vm<2>();
+    else
+      wait_vm<0>();
+    const int64_t tb = (static_cast<int64_t>(bi) * H + h) * T + static_cast<int64_t>(c) * Q;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int jq = j0 + 16 * wt + 4 * q + e, p = 16 * (2 * team + k) + r;
+        if (jq < Q && p < P) dx[(row0 + jq) * HP + static_cast<int64_t>(h) * P + p] = dxv[k][e];
+      }
+    }
+    if (team == 0 && r == 15) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int jq = j0 + 16 * wt + 4 * q + e;
+        if (jq < Q) {
+          colE[tb + jq] = ce[e];
+          diagE[tb + jq] = de[e];
+          Rp[tb + jq] = re[e];
+        }
+      }
+    }
+    if (hh + 1 < hps) scan_store(dtb, -__expf(An), sS[hb ^ 1], sDt[hb ^ 1]);
+    lds_barrier();
   }
 
   // ---- dB_j = sum_i W_ij C_i + state terms, for this team's d_state columns
-  // over all rows i (own and partner strips): the W strips of block u go to
-  // wset[u], the C tiles are in place since the last head's state step
+  // over all rows i (own and partner strips), against the C tiles loaded
+  // during the last head's state step.  The W strips of blocks u = 0..2 go
+  // to wset[u] (block 3, if any, reuses wset[0] after them), leaving the B,
+  // first x, first dy and Gamma tiles free for the next pass's first tiles,
+  // which start loading now.
+  if (pass == 0 && nb - 1 - kpair != kpair) load_first(nb - 1 - kpair);
   f4 dbp[4];
   zero(dbp);
-  lds_char* const wset[NBMAX] = {sG, sDy[0], sDy[1], sGam};
+  lds_char* const wset[3] = {sG, sX + TILE_P, sDy[1]};
+  auto db_block = [&](int u, const lds_char* ws_strips) {
+    const lds_char* ct = sCt + (jb + u) * TILE_N;
+    const ColsAt<2> ac2 = opaque(c2_);
+    const ColsAt<16> ac16 = opaque(c16_);
 #pragma unroll
-  for (int u = 0; u < NBMAX; ++u)
-    if (u < nib) put_strip(wset[u] + w * STRIP, ws[u]);
-  __syncthreads();
+    for (int ks = 0; ks < 2; ++ks) {
+      bf16x8 fa, fb[4];
+      fa = frag_cols(ws_strips + (4 * ks + wt) * STRIP, 0, 0, ac2);
 #pragma unroll
-  for (int u = 0; u < NBMAX; ++u) {
-    if (u < nib) {
-      const lds_char* ct = sCt + (jb + u) * TILE_N;
-      const ColsAt<2> ac2 = opaque(c2_);
-      const ColsAt<16> ac16 = opaque(c16_);
+      for (int kk = 0; kk < 4; ++kk) fb[kk] = frag_cols(ct, 32 * ks, 16 * (4 * team + kk), ac16);
+      sched_ds_reads<10>();
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        bf16x8 fa, fb[4];
-        fa = frag_cols(wset[u] + (4 * ks + wt) * STRIP, 0, 0, ac2);
-#pragma unroll
-        for (int k = 0; k < 4; ++k) fb[k] = frag_cols(ct, 32 * ks, 16 * (4 * team + k), ac16);
-        sched_ds_reads<10>();
-#pragma unroll
-        for (int k = 0; k < 4; ++k) dbp[k] = mfma(fa, fb[k], dbp[k]);
-        sched_mfmas<4>();
-      }
+      for (int kk = 0; kk < 4; ++kk) dbp[kk] = mfma(fa, fb[kk], dbp[kk]);
+      sched_mfmas<4>();
     }
+  };
+#pragma unroll
+  for (int u = 0; u < 3; ++u)
+    if (u < nib) put_strip(wset[u] + w * STRIP, ws[u]);
+  lds_barrier();
+#pragma unroll
+  for (int u = 0; u < 3; ++u)
+    if (u < nib) db_block(u, wset[u]);
+  if (nib > 3) {
+    lds_barrier();
+    put_strip(wset[0] + w * STRIP, ws[3]);
+    lds_barrier();
+    db_block(3, wset[0]);
   }
   const int64_t batch = gridDim.x / (npair * nsplit * G * nc);
   float* dBo = dB_out + static_cast<int64_t>(sp) * batch * T * GN;
@@ -558,6 +620,7 @@ __global__ __launch_bounds__(BT) void bwd_row_bf16_kernel(
   const int c = idx % nc;
   const int bi = idx / nc;
 
+  uint32_t dtb[4];  // dt bits of t = 4l .. 4l+3 for the next scan, converted when used
   for (int pass = 0; pass < 2; ++pass) {
   const int ib = pass ? kpair : nb - 1 - kpair;  // the block with the most columns j first
   if (pass && ib == nb - 1 - kpair) break;
@@ -587,7 +650,6 @@ __global__ __launch_bounds__(BT) void bwd_row_bf16_kernel(
   const __amdgpu_buffer_rsrc_t rdt = make_rsrc_ptr(dt + row0 * H);
   auto head = [&](int hh) { return g * hpg + sp * hps + hh; };
 
-  uint32_t dtb[4];
   auto load_dt = [&](int hh) {
     const int h = head(hh);
 #pragma unroll
@@ -604,6 +666,17 @@ __global__ __launch_bounds__(BT) void bwd_row_bf16_kernel(
   auto load_dy = [&](int hh) {
     tile_async<64, 8, BW>(sDy + (hh & 1) * TILE_P, rdy, i0 * HPb + head(hh) * P * 2, HPb, vi, pch);
   };
+  auto load_h = [&](int hh) { tile_async<64, 16, BW>(sH, rh, head(hh) * P * N * 2, N * 2, P, nch); };
+  // C rows, the first head's dy, first x, H_c and dt for row block ix (this
+  // pass's, or the next pass's while this one finishes)
+  auto load_first = [&](int ix) {
+    const int ix0 = ix * BQ, vix = min(BQ, Q - ix0);
+    tile_async<64, 16, BW>(sC, rc, ix0 * GNb + goff, GNb, vix, nch);
+    tile_async<64, 8, BW>(sDy, rdy, ix0 * HPb + head(0) * P * 2, HPb, vix, pch);
+    load_x(0, 0, sX[0]);
+    load_h(0);
+    load_dt(0);
+  };
   // the B tiles of blocks jb <= ib, each to its own 16 KB of the C.B^T area
   auto load_bs = [&]() {
 #pragma unroll
@@ -616,14 +689,13 @@ __global__ __launch_bounds__(BT) void bwd_row_bf16_kernel(
   };
 
   // ---- C rows of block ib, the B tiles of blocks jb <= ib and the first
-  // head's dy and x tiles, in flight together (the second block of a pair
-  // finds its B tiles where the first block's dC phase left them), then
-  // C.B^T for every block jb <= ib, over the B tiles once all are read
-  tile_async<64, 16, BW>(sC, rc, i0 * GNb + goff, GNb, vi, nch);
-  if (pass == 0) load_bs();
-  load_dt(0);
-  load_dy(0);
-  load_x(0, 0, sX[0]);
+  // head's tiles, in flight together (the second block of a pair finds them
+  // where the first block's dC phase left or loaded them), then C.B^T for
+  // every block jb <= ib, over the B tiles once all are read
+  if (pass == 0) {
+    load_first(ib);
+    load_bs();
+  }
   wait_vm<0>();
   __syncthreads();
   // Two blocks at a time: C.B^T of block jb goes over the B tile of block jb,
@@ -688,16 +760,21 @@ __global__ __launch_bounds__(BT) void bwd_row_bf16_kernel(
     }
     float rm[4] = {0.f, 0.f, 0.f, 0.f};  // strictly-lower row sums of M over this team's columns
     float ddv = 0.f;                     // diagonal of yx
+    float An = 0.f;                      // A_log of the next head (read at this head's first step)
 
 #pragma unroll
     for (int jb = 0; jb < NBMAX; ++jb) {
       if (jb < nj) {
         const int j0 = jb * BQ;
         const lds_char* xt = sX[jb & 1];
+        // the next block's x tile starts loading now; at a head's first step
+        // the next head's dt, issued last so that the step's end need not
+        // wait for it (this head's H_c was loaded during the previous head's
+        // per-head terms)
         if (jb + 1 < nj) load_x(hh, jb + 1, sX[(jb + 1) & 1]);
-        if (jb == 0) {
-          tile_async<64, 16, BW>(sH, rh, h * P * N * 2, N * 2, P, nch);
-          if (hh + 1 < hps) load_dt(hh + 1);
+        if (jb == 0 && hh + 1 < hps) {
+          An = A_log[head(hh + 1)];
+          load_dt(hh + 1);
         }
         // yx: rows i (this wave's 16), columns j = j0 + tj + 16 tt + r; the
         // C.B^T tiles and the s and dt values of the columns are read with the
@@ -759,13 +836,17 @@ __global__ __launch_bounds__(BT) void bwd_row_bf16_kernel(
             }
           }
         }
-        wait_vm<0>();
-        __syncthreads();
+        if (jb == 0 && hh + 1 < hps)
+          wait_vm<4>();  // all but the 4 dt loads
+        else
+          wait_vm<0>();
+        lds_barrier();
       }
     }
 
-    // ---- per-head terms; the next head's first tiles start loading (after
-    // the last head, the B tiles for the dC phase, over C.B^T)
+    // ---- per-head terms; the next head's dy and x tiles start loading, its
+    // H_c once this head's is read (after the last head, the B tiles for the
+    // dC phase, over C.B^T)
     if (hh + 1 == hps) load_bs();
     if (hh + 1 < hps) {
       load_dy(hh + 1);
@@ -818,55 +899,76 @@ __global__ __launch_bounds__(BT) void bwd_row_bf16_kernel(
       if (r == 15) sDD[w][q] = dd;
     }
     lds_barrier();
+    if (hh + 1 < hps) load_h(hh + 1);  // this head's H_c is no longer read
+    float rmv[4], dso[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int il = 16 * wt + 4 * q + e;
+      rmv[e] = sRed[0][il][0] + sRed[1][il][0];
+      dso[e] = ex[e] * (sRed[0][il][1] + sRed[1][il][1]);
+    }
+    float tot = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < BW; ++kk) tot += sDD[kk][0] + sDD[kk][1] + sDD[kk][2] + sDD[kk][3];
+    // the next head's dy and x tiles (all but H_c's 2 copies) must be in LDS
+    // at the barrier; the stores below are issued after the wait and complete
+    // during the next step
+    if (hh + 1 < hps)
+      wait_vm<2>();
+    else
+      wait_vm<0>();
     const int64_t tb = (static_cast<int64_t>(bi) * H + h) * T + static_cast<int64_t>(c) * Q;
     if (team == 0 && r == 15) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int il = 16 * wt + 4 * q + e, iq = i0 + il;
+        const int iq = i0 + 16 * wt + 4 * q + e;
         if (iq < Q) {
-          rowM[tb + iq] = sRed[0][il][0] + sRed[1][il][0];
-          dsoff[tb + iq] = ex[e] * (sRed[0][il][1] + sRed[1][il][1]);
+          rowM[tb + iq] = rmv[e];
+          dsoff[tb + iq] = dso[e];
         }
       }
     }
-    if (threadIdx.x == 0) {
-      float tot = 0.f;
-#pragma unroll
-      for (int k = 0; k < BW; ++k) tot += sDD[k][0] + sDD[k][1] + sDD[k][2] + sDD[k][3];
-      dD_part[((static_cast<int64_t>(bi) * nc + c) * nb + ib) * H + h] = tot;
-    }
-    if (hh + 1 < hps) scan_store(dtb, -__expf(A_log[head(hh + 1)]), sS[hb ^ 1], sDt[hb ^ 1]);
-    wait_vm<0>();
-    __syncthreads();
+    if (threadIdx.x == 0) dD_part[((static_cast<int64_t>(bi) * nc + c) * nb + ib) * H + h] = tot;
+    if (hh + 1 < hps) scan_store(dtb, -__expf(An), sS[hb ^ 1], sDt[hb ^ 1]);
+    lds_barrier();
   }
 
   // ---- dC_i = sum_j W_ij B_j + sum_h exp(s_i) U_i for this team's d_state
-  // columns over all columns j (own and partner strips): the W strips of
-  // block jb go to wset[jb], the B tiles are in place since the last head's
-  // per-head terms
-  lds_char* const wset[NBMAX] = {sG, sX[0], sX[1], sDy};
+  // columns over all columns j (own and partner strips), against the B tiles
+  // loaded during the last head's per-head terms.  The W strips of blocks
+  // jb = 0..2 go to wset[jb] (block 3, if any, reuses wset[0] after them),
+  // leaving the C, first dy, first x and H_c tiles free for the next pass's
+  // first tiles, which start loading now.
+  if (pass == 0 && nb - 1 - kpair != kpair) load_first(kpair);
+  lds_char* const wset[3] = {sG, sX[1], sDy + TILE_P};
+  auto dc_block = [&](int jb, const lds_char* w_strips) {
+    const lds_char* bt = sBt + jb * TILE_N;
+    const ColsAt<2> ac2 = opaque(c2_);
+    const ColsAt<16> ac16 = opaque(c16_);
 #pragma unroll
-  for (int jb = 0; jb < NBMAX; ++jb)
-    if (jb < nj) put_strip(wset[jb] + w * STRIP, ws[jb]);
-  __syncthreads();
+    for (int ks = 0; ks < 2; ++ks) {
+      bf16x8 fa, fb[4];
+      fa = frag_cols(w_strips + (4 * ks + wt) * STRIP, 0, 0, ac2);
 #pragma unroll
-  for (int jb = 0; jb < NBMAX; ++jb) {
-    if (jb < nj) {
-      const lds_char* bt = sBt + jb * TILE_N;
-      const ColsAt<2> ac2 = opaque(c2_);
-      const ColsAt<16> ac16 = opaque(c16_);
+      for (int kk = 0; kk < 4; ++kk) fb[kk] = frag_cols(bt, 32 * ks, 16 * (4 * team + kk), ac16);
+      sched_ds_reads<10>();
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        bf16x8 fa, fb[4];
-        fa = frag_cols(wset[jb] + (4 * ks + wt) * STRIP, 0, 0, ac2);
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) fb[kk] = frag_cols(bt, 32 * ks, 16 * (4 * team + kk), ac16);
-        sched_ds_reads<10>();
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) ua[kk] = mfma(fa, fb[kk], ua[kk]);
-        sched_mfmas<4>();
-      }
+      for (int kk = 0; kk < 4; ++kk) ua[kk] = mfma(fa, fb[kk], ua[kk]);
+      sched_mfmas<4>();
     }
+  };
+#pragma unroll
+  for (int jb = 0; jb < 3; ++jb)
+    if (jb < nj) put_strip(wset[jb] + w * STRIP, ws[jb]);
+  lds_barrier();
+#pragma unroll
+  for (int jb = 0; jb < 3; ++jb)
+    if (jb < nj) dc_block(jb, wset[jb]);
+  if (nj > 3) {
+    lds_barrier();
+    put_strip(wset[0] + w * STRIP, ws[3]);
+    lds_barrier();
+    dc_block(3, wset[0]);
   }
   const int64_t batch = gridDim.x / (npair * nsplit * G * nc);
   float* dCo = dC_out + static_cast<int64_t>(sp) * batch * T * GN;
