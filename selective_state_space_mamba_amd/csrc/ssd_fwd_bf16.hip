@@ -78,7 +78,9 @@ __global__ __launch_bounds__(FT) void out_fwd_bf16_kernel(
   __shared__ __attribute__((aligned(1024))) char sH_[FTILE_N];          // H_c [p][n] (bf16); B tile slot
   __shared__ __attribute__((aligned(1024))) char sXch_[FTILE_N];        // y halves; B tile slot
   __shared__ __attribute__((aligned(1024))) char sG_[FW * FSTRIP];      // per-wave G strips [j][i]
-  __shared__ f4 sCB[NBMAX][2][FW][WAVE];                                // C.B^T, lane-linear
+  // C.B^T, lane-linear; before it is formed and after its last use, the B
+  // tiles of blocks jb (tile jb in the jb-th 16 KB)
+  __shared__ __attribute__((aligned(1024))) f4 sCB[NBMAX][2][FW][WAVE];
   __shared__ __attribute__((aligned(16))) float sS[2][QMAX];
   __shared__ __attribute__((aligned(16))) float sDt[2][QMAX];
   lds_char* const sC = lds_ptr(sC_);
@@ -86,6 +88,7 @@ __global__ __launch_bounds__(FT) void out_fwd_bf16_kernel(
   lds_char* const sH = lds_ptr(sH_);
   lds_char* const sXch = lds_ptr(sXch_);
   lds_char* const sG = lds_ptr(sG_);
+  lds_char* const sBt = lds_ptr(sCB);
 
   const int nc = T / Q, nb = (Q + BQ - 1) / BQ;
   const int hpg = H / G, hps = hpg / nsplit;
@@ -102,6 +105,7 @@ __global__ __launch_bounds__(FT) void out_fwd_bf16_kernel(
   const int c = idx % nc;
   const int bi = idx / nc;
 
+  uint32_t dtb[4];  // dt bits of t = 4l .. 4l+3 for the next scan, converted when used
   for (int pass = 0; pass < 2; ++pass) {
   const int ib = pass ? kpair : nb - 1 - kpair;  // the block with the most columns j first
   if (pass && ib == nb - 1 - kpair) break;
@@ -129,7 +133,6 @@ __global__ __launch_bounds__(FT) void out_fwd_bf16_kernel(
   const __amdgpu_buffer_rsrc_t rdt = make_rsrc_ptr(dt + row0 * H);
   auto head = [&](int hh) { return g * hpg + sp * hps + hh; };
 
-  uint32_t dtb[4];
   auto load_dt = [&](int hh) {
     const int h = head(hh);
 #pragma unroll
@@ -143,29 +146,50 @@ __global__ __launch_bounds__(FT) void out_fwd_bf16_kernel(
     const int j0 = jb * BQ;
     tile_async<64, 8, FW>(dst, rx, j0 * HPb + head(hh) * P * 2, HPb, min(BQ, Q - j0), pch);
   };
-  auto load_b = [&](int jb, lds_char* dst) {
-    const int j0 = jb * BQ;
-    tile_async<64, 16, FW>(dst, rb, j0 * GNb + goff, GNb, min(BQ, Q - j0), nch);
+  auto load_h = [&](int hh) { tile_async<64, 16, FW>(sH, rh, head(hh) * P * N * 2, N * 2, P, nch); };
+  // C rows, the first head's first x, H_c and dt for row block ix (this
+  // pass's, or the next pass's while this one finishes)
+  auto load_first = [&](int ix) {
+    const int ix0 = ix * BQ, vix = min(BQ, Q - ix0);
+    tile_async<64, 16, FW>(sC, rc, ix0 * GNb + goff, GNb, vix, nch);
+    load_x(0, 0, sX[0]);
+    load_h(0);
+    load_dt(0);
   };
+  // the B tiles of blocks jb <= jx, each to its own 16 KB of the C.B^T area
+  auto load_bs = [&](int jx) {
+#pragma unroll
+    for (int jb = 0; jb < NBMAX; ++jb) {
+      if (jb <= jx) {
+        const int j0 = jb * BQ;
+        tile_async<64, 16, FW>(sBt + jb * FTILE_N, rb, j0 * GNb + goff, GNb, min(BQ, Q - j0), nch);
+      }
+    }
+  };
+  // whether a second row block follows in this workgroup
+  const bool next = pass == 0 && nb - 1 - kpair != kpair;
 
-  // ---- C rows of block ib, then C.B^T for every block jb <= ib (B tiles two at a time)
-  tile_async<64, 16, FW>(sC, rc, i0 * GNb + goff, GNb, vi, nch);
-  load_dt(0);
+  // ---- C rows of block ib, the B tiles of blocks jb <= ib and the first
+  // head's tiles, in flight together (the second block of a pair finds them
+  // loaded during the first block's last head), then C.B^T for every block
+  // jb <= ib, over the B tiles once all are read, two blocks at a time (C.B^T
+  // of block jb goes over the B tile of block jb)
+  if (pass == 0) {
+    load_first(ib);
+    load_bs(ib);
+  }
+  wait_vm<0>();
+  __syncthreads();
 #pragma unroll
   for (int jb0 = 0; jb0 < NBMAX; jb0 += 2) {
     if (jb0 < nj) {
-      load_b(jb0, sXch);
-      if (jb0 + 1 < nj) load_b(jb0 + 1, sH);
-      wait_vm<0>();
-      __syncthreads();
+      f4 cbr[2][2];
 #pragma unroll
       for (int d = 0; d < 2; ++d) {
-        const int jb = jb0 + d;
-        if (jb < nj) {
-          const lds_char* bt = d ? sH : sXch;
+        if (jb0 + d < nj) {
+          const lds_char* bt = sBt + (jb0 + d) * FTILE_N;
           const RowsAt<16> ar16 = opaque(r16_);
-          f4 cb[2];
-          zero(cb);
+          zero(cbr[d]);
           bf16x8 fa[FKN], fb[FKN][2];
 #pragma unroll
           for (int ks = 0; ks < FKN; ++ks) {
@@ -177,17 +201,20 @@ __global__ __launch_bounds__(FT) void out_fwd_bf16_kernel(
 #pragma unroll
           for (int ks = 0; ks < FKN; ++ks)
 #pragma unroll
-            for (int tt = 0; tt < 2; ++tt) cb[tt] = mfma(fa[ks], fb[ks][tt], cb[tt]);
+            for (int tt = 0; tt < 2; ++tt) cbr[d][tt] = mfma(fa[ks], fb[ks][tt], cbr[d][tt]);
           sched_mfmas<2 * FKN>();
-          sCB[jb][0][w][l] = cb[0];
-          sCB[jb][1][w][l] = cb[1];
         }
       }
       __syncthreads();
+#pragma unroll
+      for (int d = 0; d < 2; ++d) {
+        if (jb0 + d < nj) {
+          sCB[jb0 + d][0][w][l] = cbr[d][0];
+          sCB[jb0 + d][1][w][l] = cbr[d][1];
+        }
+      }
     }
   }
-  load_x(0, 0, sX[0]);
-  wait_vm<0>();
   fwd_scan_store(dtb, -__expf(A_log[head(0)]), sS[0], sDt[0]);
   __syncthreads();
 
@@ -206,6 +233,7 @@ __global__ __launch_bounds__(FT) void out_fwd_bf16_kernel(
     }
     f4 ya[4];  // sum over this team's columns j of G_ij x_j: rows i, columns p = 16 pt + r
     zero(ya);
+    float Dh = 0.f, An = 0.f;  // D of this head, A_log of the next (read at its first step)
     u32x2 xsk[2];  // x_i at columns p = 32 team + 16 k + r, accumulator layout
 
 #pragma unroll
@@ -213,10 +241,17 @@ __global__ __launch_bounds__(FT) void out_fwd_bf16_kernel(
       if (jb < nj) {
         const int j0 = jb * BQ;
         const lds_char* xt = sX[jb & 1];
+        // the next block's x tile starts loading now; at a head's first step
+        // the next head's dt, issued last so that the step's end need not
+        // wait for it (this head's H_c was loaded during the previous head's
+        // last terms)
         if (jb + 1 < nj) load_x(hh, jb + 1, sX[(jb + 1) & 1]);
         if (jb == 0) {
-          tile_async<64, 16, FW>(sH, rh, h * P * N * 2, N * 2, P, nch);
-          if (hh + 1 < hps) load_dt(hh + 1);
+          Dh = D[h];
+          if (hh + 1 < hps) {
+            An = A_log[head(hh + 1)];
+            load_dt(hh + 1);
+          }
         }
         // the step's C.B^T tiles, the s and dt values of its columns and the x
         // fragments of the G x contraction are read together
@@ -268,13 +303,19 @@ __global__ __launch_bounds__(FT) void out_fwd_bf16_kernel(
 #pragma unroll
           for (int pt = 0; pt < 4; ++pt) ya[pt] = mfma(a, fx[pt], ya[pt]);
         }
-        wait_vm<0>();
-        __syncthreads();
+        if (jb == 0 && hh + 1 < hps)
+          wait_vm<4>();  // all but the 4 dt loads
+        else
+          wait_vm<0>();
+        lds_barrier();
       }
     }
 
-    // ---- finish head hh; the next head's first x tile starts loading
+    // ---- finish head hh; the next head's first x tile starts loading, its
+    // H_c once this head's is read (after the last head, the next block's B
+    // tiles over C.B^T and then its first tiles)
     if (hh + 1 < hps) load_x(hh + 1, 0, sX[0]);
+    if (hh + 1 == hps && next) load_bs(kpair);
     // hand the other team's headdim columns to it
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
@@ -303,24 +344,36 @@ __global__ __launch_bounds__(FT) void out_fwd_bf16_kernel(
       }
     }
     lds_barrier();
-    const float Dh = D[h];
+    if (hh + 1 < hps)
+      load_h(hh + 1);  // this head's H_c is no longer read
+    else if (next)
+      load_first(kpair);
+    uint16_t yv[2][4];
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
       const int pt = 2 * team + k;
       const f4 other = *(const __attribute__((address_space(3))) f4*)(sXch + ((wt * 4 + pt) * WAVE + l) * 16);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int iq = i0 + 16 * wt + 4 * q + e, p = 16 * pt + r;
         const float xv = acc_elem(xsk[k], e);
         const float ex = __expf(si[e]);
-        if (iq < Q && p < P)
-          y[(row0 + iq) * HP + static_cast<int64_t>(h) * P + p] =
-              f32_to_bf16_bits(ya[pt][e] + other[e] + ex * yo[k][e] + Dh * xv);
+        yv[k][e] = f32_to_bf16_bits(ya[pt][e] + other[e] + ex * yo[k][e] + Dh * xv);
       }
     }
-    if (hh + 1 < hps) fwd_scan_store(dtb, -__expf(A_log[head(hh + 1)]), sS[hb ^ 1], sDt[hb ^ 1]);
-    wait_vm<0>();
-    __syncthreads();
+    // the next head's first x tile (all but H_c's 2 copies) must be in LDS
+    // at the barrier; the stores below are issued after the wait and complete
+    // during the next step
+    if (hh + 1 < hps) wait_vm<2>();
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int iq = i0 + 16 * wt + 4 * q + e, p = 16 * (2 * team + k) + r;
+        if (iq < Q && p < P) y[(row0 + iq) * HP + static_cast<int64_t>(h) * P + p] = yv[k][e];
+      }
+    }
+    if (hh + 1 < hps) fwd_scan_store(dtb, -__expf(An), sS[hb ^ 1], sDt[hb ^ 1]);
+    lds_barrier();
   }
   }  // pass
 }
