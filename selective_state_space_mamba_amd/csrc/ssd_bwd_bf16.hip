@@ -150,10 +150,12 @@ __global__ __launch_bounds__(BT) void bwd_col_bf16_kernel(
   const i32x4 rc = make_rsrc(Cm + row0 * GN);
   const i32x4 rg = make_rsrc(gamma + (static_cast<int64_t>(bi) * nc + c) * HP * N);
   const __amdgpu_buffer_rsrc_t rdt = make_rsrc_ptr(dt + row0 * H);
-  auto head = [&](int hh) { return g * hpg + sp * hps + hh; };
+  // the second block of a pair takes the heads in reverse order, so that the
+  // heads' tiles the first block read last are still in L2
+  auto headp = [&](int pp, int hh) { return g * hpg + sp * hps + (pp ? hps - 1 - hh : hh); };
+  auto head = [&](int hh) { return headp(pass, hh); };
 
-  auto load_dt = [&](int hh) {
-    const int h = head(hh);
+  auto load_dt_abs = [&](int h) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int t = 4 * l + e;
@@ -161,6 +163,7 @@ __global__ __launch_bounds__(BT) void bwd_col_bf16_kernel(
       dtb[e] = __builtin_amdgcn_raw_buffer_load_b16(rdt, off, h * 2, 0);
     }
   };
+  auto load_dt = [&](int hh) { load_dt_abs(head(hh)); };
   auto load_x = [&](int hh) {
     tile_async<64, 8, BW>(sX + (hh & 1) * TILE_P, rx, j0 * HPb + head(hh) * P * 2, HPb, vj, pch);
   };
@@ -168,16 +171,17 @@ __global__ __launch_bounds__(BT) void bwd_col_bf16_kernel(
     const int i0 = (jb + u) * BQ;
     tile_async<64, 8, BW>(dst, rdy, i0 * HPb + head(hh) * P * 2, HPb, min(BQ, Q - i0), pch);
   };
-  auto load_gam = [&](int hh) { tile_async<64, 16, BW>(sGam, rg, head(hh) * P * N * 2, N * 2, P, nch); };
-  // B rows, the first head's x, dy, Gamma and dt for column block jx (this
-  // pass's, or the next pass's while this one finishes)
-  auto load_first = [&](int jx) {
-    const int jx0 = jx * BQ, vjx = min(BQ, Q - jx0);
+  auto load_gam_abs = [&](int h) { tile_async<64, 16, BW>(sGam, rg, h * P * N * 2, N * 2, P, nch); };
+  auto load_gam = [&](int hh) { load_gam_abs(head(hh)); };
+  // B rows, the first head's x, dy, Gamma and dt for column block jx of pass
+  // pp (this pass, or the next while this one finishes)
+  auto load_first = [&](int jx, int pp) {
+    const int jx0 = jx * BQ, vjx = min(BQ, Q - jx0), h0 = headp(pp, 0);
     tile_async<64, 16, BW>(sB, rb, jx0 * GNb + goff, GNb, vjx, nch);
-    tile_async<64, 8, BW>(sX, rx, jx0 * HPb + head(0) * P * 2, HPb, vjx, pch);
-    tile_async<64, 8, BW>(sDy[0], rdy, jx0 * HPb + head(0) * P * 2, HPb, vjx, pch);
-    load_gam(0);
-    load_dt(0);
+    tile_async<64, 8, BW>(sX, rx, jx0 * HPb + h0 * P * 2, HPb, vjx, pch);
+    tile_async<64, 8, BW>(sDy[0], rdy, jx0 * HPb + h0 * P * 2, HPb, vjx, pch);
+    load_gam_abs(h0);
+    load_dt_abs(h0);
   };
   // the C tiles of blocks ib >= jb, each to its own 16 KB of the C.B^T area
   auto load_cs = [&]() {
@@ -195,7 +199,7 @@ __global__ __launch_bounds__(BT) void bwd_col_bf16_kernel(
   // where the first block's dB phase left or loaded them), then C.B^T for
   // every block ib >= jb, over the C tiles once all are read
   if (pass == 0) {
-    load_first(jb);
+    load_first(jb, pass);
     load_cs();
   }
   wait_vm<0>();
@@ -522,7 +526,7 @@ __global__ __launch_bounds__(BT) void bwd_col_bf16_kernel(
   // to wset[u] (block 3, if any, reuses wset[0] after them), leaving the B,
   // first x, first dy and Gamma tiles free for the next pass's first tiles,
   // which start loading now.
-  if (pass == 0 && nb - 1 - kpair != kpair) load_first(nb - 1 - kpair);
+  if (pass == 0 && nb - 1 - kpair != kpair) load_first(nb - 1 - kpair, 1);
   f4 dbp[4];
   zero(dbp);
   lds_char* const wset[3] = {sG, sX + TILE_P, sDy[1]};
@@ -648,10 +652,12 @@ __global__ __launch_bounds__(BT) void bwd_row_bf16_kernel(
   const i32x4 rc = make_rsrc(Cm + row0 * GN);
   const i32x4 rh = make_rsrc(hbf + (static_cast<int64_t>(bi) * nc + c) * HP * N);
   const __amdgpu_buffer_rsrc_t rdt = make_rsrc_ptr(dt + row0 * H);
-  auto head = [&](int hh) { return g * hpg + sp * hps + hh; };
+  // the second block of a pair takes the heads in reverse order, so that the
+  // heads' tiles the first block read last are still in L2
+  auto headp = [&](int pp, int hh) { return g * hpg + sp * hps + (pp ? hps - 1 - hh : hh); };
+  auto head = [&](int hh) { return headp(pass, hh); };
 
-  auto load_dt = [&](int hh) {
-    const int h = head(hh);
+  auto load_dt_abs = [&](int h) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int t = 4 * l + e;
@@ -659,6 +665,7 @@ __global__ __launch_bounds__(BT) void bwd_row_bf16_kernel(
       dtb[e] = __builtin_amdgcn_raw_buffer_load_b16(rdt, off, h * 2, 0);
     }
   };
+  auto load_dt = [&](int hh) { load_dt_abs(head(hh)); };
   auto load_x = [&](int hh, int jb, lds_char* dst) {
     const int j0 = jb * BQ;
     tile_async<64, 8, BW>(dst, rx, j0 * HPb + head(hh) * P * 2, HPb, min(BQ, Q - j0), pch);
@@ -666,16 +673,17 @@ __global__ __launch_bounds__(BT) void bwd_row_bf16_kernel(
   auto load_dy = [&](int hh) {
     tile_async<64, 8, BW>(sDy + (hh & 1) * TILE_P, rdy, i0 * HPb + head(hh) * P * 2, HPb, vi, pch);
   };
-  auto load_h = [&](int hh) { tile_async<64, 16, BW>(sH, rh, head(hh) * P * N * 2, N * 2, P, nch); };
-  // C rows, the first head's dy, first x, H_c and dt for row block ix (this
-  // pass's, or the next pass's while this one finishes)
-  auto load_first = [&](int ix) {
-    const int ix0 = ix * BQ, vix = min(BQ, Q - ix0);
+  auto load_h_abs = [&](int h) { tile_async<64, 16, BW>(sH, rh, h * P * N * 2, N * 2, P, nch); };
+  auto load_h = [&](int hh) { load_h_abs(head(hh)); };
+  // C rows, the first head's dy, first x, H_c and dt for row block ix of
+  // pass pp (this pass, or the next while this one finishes)
+  auto load_first = [&](int ix, int pp) {
+    const int ix0 = ix * BQ, vix = min(BQ, Q - ix0), h0 = headp(pp, 0);
     tile_async<64, 16, BW>(sC, rc, ix0 * GNb + goff, GNb, vix, nch);
-    tile_async<64, 8, BW>(sDy, rdy, ix0 * HPb + head(0) * P * 2, HPb, vix, pch);
-    load_x(0, 0, sX[0]);
-    load_h(0);
-    load_dt(0);
+    tile_async<64, 8, BW>(sDy, rdy, ix0 * HPb + h0 * P * 2, HPb, vix, pch);
+    tile_async<64, 8, BW>(sX[0], rx, h0 * P * 2, HPb, min(BQ, Q), pch);
+    load_h_abs(h0);
+    load_dt_abs(h0);
   };
   // the B tiles of blocks jb <= ib, each to its own 16 KB of the C.B^T area
   auto load_bs = [&]() {
@@ -693,7 +701,7 @@ __global__ __launch_bounds__(BT) void bwd_row_bf16_kernel(
   // where the first block's dC phase left or loaded them), then C.B^T for
   // every block jb <= ib, over the B tiles once all are read
   if (pass == 0) {
-    load_first(ib);
+    load_first(ib, pass);
     load_bs();
   }
   wait_vm<0>();
@@ -939,7 +947,7 @@ __global__ __launch_bounds__(BT) void bwd_row_bf16_kernel(
   // jb = 0..2 go to wset[jb] (block 3, if any, reuses wset[0] after them),
   // leaving the C, first dy, first x and H_c tiles free for the next pass's
   // first tiles, which start loading now.
-  if (pass == 0 && nb - 1 - kpair != kpair) load_first(kpair);
+  if (pass == 0 && nb - 1 - kpair != kpair) load_first(kpair, 1);
   lds_char* const wset[3] = {sG, sX[1], sDy + TILE_P};
   auto dc_block = [&](int jb, const lds_char* w_strips) {
     const lds_char* bt = sBt + jb * TILE_N;
