@@ -93,9 +93,7 @@ __global__ __launch_bounds__(BT) void bwd_col_bf16_kernel(
   __shared__ __attribute__((aligned(1024))) char sDy1_[TILE_P];        // dy rows i, odd steps
   __shared__ __attribute__((aligned(1024))) char sGam_[TILE_N];        // Gamma [p][n]; C tile slot
   __shared__ __attribute__((aligned(1024))) char sG_[BW * STRIP];      // per-wave strips [i][j]
-  // C.B^T, lane-linear; before it is formed and after its last use, the C
-  // tiles of blocks ib (tile ib in the ib-th 16 KB)
-  __shared__ __attribute__((aligned(1024))) f4 sCB[NBMAX][2][BW][WAVE];
+  __shared__ __attribute__((aligned(1024))) char sCt_[NBMAX * TILE_N];  // C tiles of blocks ib, tile ib at ib * 16 KB
   __shared__ float sRed[2][BQ][3];                                     // column sums, diagonal, R' halves
   __shared__ __attribute__((aligned(16))) float sS[2][QMAX];
   __shared__ __attribute__((aligned(16))) float sDt[2][QMAX];
@@ -104,7 +102,7 @@ __global__ __launch_bounds__(BT) void bwd_col_bf16_kernel(
   lds_char* const sDy[2] = {lds_ptr(sDy0_), lds_ptr(sDy1_)};
   lds_char* const sGam = lds_ptr(sGam_);
   lds_char* const sG = lds_ptr(sG_);
-  lds_char* const sCt = lds_ptr(sCB);
+  lds_char* const sCt = lds_ptr(sCt_);
 
   const int nc = T / Q, nb = (Q + BQ - 1) / BQ;
   const int hpg = H / G, hps = hpg / nsplit;
@@ -183,7 +181,7 @@ __global__ __launch_bounds__(BT) void bwd_col_bf16_kernel(
     load_gam_abs(h0);
     load_dt_abs(h0);
   };
-  // the C tiles of blocks ib >= jb, each to its own 16 KB of the C.B^T area
+  // the C tiles of blocks ib >= jb, each to its own 16 KB
   auto load_cs = [&]() {
 #pragma unroll
     for (int u = 0; u < NBMAX; ++u) {
@@ -195,56 +193,44 @@ __global__ __launch_bounds__(BT) void bwd_col_bf16_kernel(
   };
 
   // ---- B rows of block jb, the C tiles of blocks ib >= jb and the first
-  // head's tiles, in flight together (the second block of a pair finds them
-  // where the first block's dB phase left or loaded them), then C.B^T for
-  // every block ib >= jb, over the C tiles once all are read
+  // head's tiles, in flight together, then C.B^T for every block ib >= jb.
+  // The C tiles stay for the dB phase and for the second block of a pair
+  // (whose blocks are a subset); its first tiles load during the first
+  // block's dB phase.
   if (pass == 0) {
     load_first(jb, pass);
     load_cs();
   }
   wait_vm<0>();
   __syncthreads();
-  // Two blocks at a time: C.B^T of blocks jb + u goes to slot u, which held
-  // the C tile of block u (ib >= u, read before the barrier) or none of ours
+  // C.B^T stays in registers for the whole block: tiles (rows j of this wave,
+  // columns i = (jb + u) * 64 + ti + 16 tt + r)
+  f4 cbk[NBMAX][2];
 #pragma unroll
-  for (int u0 = 0; u0 < NBMAX; u0 += 2) {
-    if (u0 < nib) {
-      f4 cbr[2][2];
+  for (int u = 0; u < NBMAX; ++u) {
+    zero(cbk[u]);
+    if (u < nib) {
+      const lds_char* ct = sCt + (jb + u) * TILE_N;
+      const RowsAt<16> ar16 = opaque(r16_);
+      bf16x8 fa[KN], fb[KN][2];
 #pragma unroll
-      for (int d = 0; d < 2; ++d) {
-        if (u0 + d < nib) {
-          const lds_char* ct = sCt + (jb + u0 + d) * TILE_N;
-          const RowsAt<16> ar16 = opaque(r16_);
-          zero(cbr[d]);
-          bf16x8 fa[KN], fb[KN][2];
+      for (int ks = 0; ks < KN; ++ks) {
+        fa[ks] = frag_rows(sB, 16 * wt, 4 * ks, ar16);
 #pragma unroll
-          for (int ks = 0; ks < KN; ++ks) {
-            fa[ks] = frag_rows(sB, 16 * wt, 4 * ks, ar16);
-#pragma unroll
-            for (int tt = 0; tt < 2; ++tt) fb[ks][tt] = frag_rows(ct, ti + 16 * tt, 4 * ks, ar16);
-          }
-          sched_ds_reads<3 * KN>();
-#pragma unroll
-          for (int ks = 0; ks < KN; ++ks)
-#pragma unroll
-            for (int tt = 0; tt < 2; ++tt) cbr[d][tt] = mfma(fa[ks], fb[ks][tt], cbr[d][tt]);
-          sched_mfmas<2 * KN>();
-        }
+        for (int tt = 0; tt < 2; ++tt) fb[ks][tt] = frag_rows(ct, ti + 16 * tt, 4 * ks, ar16);
       }
-      __syncthreads();
+      sched_ds_reads<3 * KN>();
 #pragma unroll
-      for (int d = 0; d < 2; ++d) {
-        if (u0 + d < nib) {
-          sCB[u0 + d][0][w][l] = cbr[d][0];
-          sCB[u0 + d][1][w][l] = cbr[d][1];
-        }
-      }
+      for (int ks = 0; ks < KN; ++ks)
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) cbk[u][tt] = mfma(fa[ks], fb[ks][tt], cbk[u][tt]);
+      sched_mfmas<2 * KN>();
     }
   }
   scan_store(dtb, -__expf(A_log[head(0)]), sS[0], sDt[0]);
   __syncthreads();
 
-  f4 ws[NBMAX][2];  // sum over heads of L yx dt: rows j, columns i as in sCB
+  f4 ws[NBMAX][2];  // sum over heads of L yx dt: rows j, columns i as in cbk
   f4 dbs[4];        // state part of dB: rows j, columns n = 16 (4 team + k) + r
 #pragma unroll
   for (int u = 0; u < NBMAX; ++u) zero(ws[u]);
@@ -272,6 +258,13 @@ __global__ __launch_bounds__(BT) void bwd_col_bf16_kernel(
     float cfc[4], sprev = 0.f;
     float csum[4] = {0.f, 0.f, 0.f, 0.f}, dsum[4] = {0.f, 0.f, 0.f, 0.f};
     u32x2 dsk[2];  // dy_j at columns p = ti + 16 k + r, accumulator layout
+    // this wave's x rows j, the first operand of every step's yx, read once
+    bf16x8 xf[KP];
+    {
+      const RowsAt<8> ar8 = opaque(r8_);
+#pragma unroll
+      for (int ks = 0; ks < KP; ++ks) xf[ks] = frag_rows(xt, 16 * wt, 4 * ks, ar8);
+    }
 
 #pragma unroll
     for (int u = 0; u < NBMAX; ++u) {
@@ -302,23 +295,21 @@ __global__ __launch_bounds__(BT) void bwd_col_bf16_kernel(
         float sv[2];  // s at rows i = i0 + ti + 16 tt + r (clamped)
         float sref;   // s at the block's first row
         {
-          bf16x8 fa[KP], fb[KP][2];
-#pragma unroll
-          for (int ks = 0; ks < KP; ++ks) {
-            fa[ks] = frag_rows(xt, 16 * wt, 4 * ks, ar8);
-#pragma unroll
-            for (int tt = 0; tt < 2; ++tt) fb[ks][tt] = frag_rows(dyt, ti + 16 * tt, 4 * ks, ar8);
-          }
-          cbt[0] = sCB[u][0][w][l];
-          cbt[1] = sCB[u][1][w][l];
-#pragma unroll
-          for (int tt = 0; tt < 2; ++tt) sv[tt] = sSh[min(i0 + ti + 16 * tt + r, Q - 1)];
-          sref = sSh[i0];
-          sched_ds_reads<3 * KP + 5>();
+          bf16x8 fb[KP][2];
 #pragma unroll
           for (int ks = 0; ks < KP; ++ks)
 #pragma unroll
-            for (int tt = 0; tt < 2; ++tt) yx[tt] = mfma(fa[ks], fb[ks][tt], yx[tt]);
+            for (int tt = 0; tt < 2; ++tt) fb[ks][tt] = frag_rows(dyt, ti + 16 * tt, 4 * ks, ar8);
+          cbt[0] = cbk[u][0];
+          cbt[1] = cbk[u][1];
+#pragma unroll
+          for (int tt = 0; tt < 2; ++tt) sv[tt] = sSh[min(i0 + ti + 16 * tt + r, Q - 1)];
+          sref = sSh[i0];
+          sched_ds_reads<2 * KP + 3>();
+#pragma unroll
+          for (int ks = 0; ks < KP; ++ks)
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) yx[tt] = mfma(xf[ks], fb[ks][tt], yx[tt]);
           sched_mfmas<2 * KP>();
         }
         f4 gv[2];
@@ -402,9 +393,7 @@ __global__ __launch_bounds__(BT) void bwd_col_bf16_kernel(
     }
 
     // ---- state terms of head hh; the next head's x and dy tiles start
-    // loading, its Gamma once this head's is read (after the last head, the C
-    // tiles for the dB phase, over C.B^T)
-    if (hh + 1 == hps) load_cs();
+    // loading, its Gamma once this head's is read
     const RowsAt<8> ar8 = opaque(r8_);
     const RowsAt<16> ar16 = opaque(r16_);
     const ColsAt<16> ac16 = opaque(c16_);
@@ -492,10 +481,7 @@ __global__ __launch_bounds__(BT) void bwd_col_bf16_kernel(
     // the next head's x and dy tiles (all but Gamma's 2 copies) must be in
     // LDS at the barrier; the stores below are issued after the wait and
     // complete during the next step
-    if (hh + 1 < hps)
-      wait_vm<2>();
-    else
-      wait_vm<0>();
+    if (hh + 1 < hps) wait_vm<2>();
     const int64_t tb = (static_cast<int64_t>(bi) * H + h) * T + static_cast<int64_t>(c) * Q;
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
@@ -521,8 +507,8 @@ __global__ __launch_bounds__(BT) void bwd_col_bf16_kernel(
   }
 
   // ---- dB_j = sum_i W_ij C_i + state terms, for this team's d_state columns
-  // over all rows i (own and partner strips), against the C tiles loaded
-  // during the last head's state step.  The W strips of blocks u = 0..2 go
+  // over all rows i (own and partner strips), against the C tiles of the
+  // prologue.  The W strips of blocks u = 0..2 go
   // to wset[u] (block 3, if any, reuses wset[0] after them), leaving the B,
   // first x, first dy and Gamma tiles free for the next pass's first tiles,
   // which start loading now.
@@ -576,7 +562,8 @@ __global__ __launch_bounds__(BT) void bwd_col_bf16_kernel(
 // Row kernel: a workgroup owns the 64 rows i of block ib of one chunk for the
 // heads of one group (or a run of them); wave (team, wt) owns rows
 // i0 + 16 wt .. +15 and, in every block jb <= ib, the columns j0 + 32 team
-// .. +31.  C_i.B_j for those tiles is formed once and kept in LDS.  A step
+// .. +31.  C_i.B_j for those tiles is formed once and kept in registers, as
+// are the wave's dy fragments for the head.  A step
 // (one head, one block jb) forms yx = dy_i . x_j with MFMA and applies the
 // decay: W = L yx dt_j (summed over heads in registers) and the strictly-lower
 // row sums of M = W CB.  Once per head: U_i = dy_i H_c with MFMA (H_c as bf16,
@@ -596,9 +583,7 @@ __global__ __launch_bounds__(BT) void bwd_row_bf16_kernel(
   __shared__ __attribute__((aligned(1024))) char sX1_[TILE_P];         // x rows j, odd steps
   __shared__ __attribute__((aligned(1024))) char sH_[TILE_N];          // H_c [p][n] (bf16); B tile slot
   __shared__ __attribute__((aligned(1024))) char sG_[BW * STRIP];      // per-wave W strips [j][i]
-  // C.B^T, lane-linear; before it is formed and after its last use, the B
-  // tiles of blocks jb (tile jb in the jb-th 16 KB)
-  __shared__ __attribute__((aligned(1024))) f4 sCB[NBMAX][2][BW][WAVE];
+  __shared__ __attribute__((aligned(1024))) char sBt_[NBMAX * TILE_N];  // B tiles of blocks jb, tile jb at jb * 16 KB
   __shared__ float sRed[2][BQ][2];                                     // row-sum and readout halves
   __shared__ float sDD[BW][4];                                         // dD partials
   __shared__ __attribute__((aligned(16))) float sS[2][QMAX];
@@ -608,7 +593,7 @@ __global__ __launch_bounds__(BT) void bwd_row_bf16_kernel(
   lds_char* const sX[2] = {lds_ptr(sX0_), lds_ptr(sX1_)};
   lds_char* const sH = lds_ptr(sH_);
   lds_char* const sG = lds_ptr(sG_);
-  lds_char* const sBt = lds_ptr(sCB);
+  lds_char* const sBt = lds_ptr(sBt_);
 
   const int nc = T / Q, nb = (Q + BQ - 1) / BQ;
   const int hpg = H / G, hps = hpg / nsplit;
@@ -685,7 +670,7 @@ __global__ __launch_bounds__(BT) void bwd_row_bf16_kernel(
     load_h_abs(h0);
     load_dt_abs(h0);
   };
-  // the B tiles of blocks jb <= ib, each to its own 16 KB of the C.B^T area
+  // the B tiles of blocks jb <= ib, each to its own 16 KB
   auto load_bs = [&]() {
 #pragma unroll
     for (int jb = 0; jb < NBMAX; ++jb) {
@@ -697,50 +682,38 @@ __global__ __launch_bounds__(BT) void bwd_row_bf16_kernel(
   };
 
   // ---- C rows of block ib, the B tiles of blocks jb <= ib and the first
-  // head's tiles, in flight together (the second block of a pair finds them
-  // where the first block's dC phase left or loaded them), then C.B^T for
-  // every block jb <= ib, over the B tiles once all are read
+  // head's tiles, in flight together, then C.B^T for every block jb <= ib.
+  // The B tiles stay for the dC phase and for the second block of a pair
+  // (whose blocks are a subset); its first tiles load during the first
+  // block's dC phase.
   if (pass == 0) {
     load_first(ib, pass);
     load_bs();
   }
   wait_vm<0>();
   __syncthreads();
-  // Two blocks at a time: C.B^T of block jb goes over the B tile of block jb,
-  // which every wave has read before the barrier
+  // C.B^T stays in registers for the whole block: tiles (rows i of this wave,
+  // columns j = jb * 64 + tj + 16 tt + r)
+  f4 cbk[NBMAX][2];
 #pragma unroll
-  for (int jb0 = 0; jb0 < NBMAX; jb0 += 2) {
-    if (jb0 < nj) {
-      f4 cbr[2][2];
+  for (int jb = 0; jb < NBMAX; ++jb) {
+    zero(cbk[jb]);
+    if (jb < nj) {
+      const lds_char* bt = sBt + jb * TILE_N;
+      const RowsAt<16> ar16 = opaque(r16_);
+      bf16x8 fa[KN], fb[KN][2];
 #pragma unroll
-      for (int d = 0; d < 2; ++d) {
-        if (jb0 + d < nj) {
-          const lds_char* bt = sBt + (jb0 + d) * TILE_N;
-          const RowsAt<16> ar16 = opaque(r16_);
-          zero(cbr[d]);
-          bf16x8 fa[KN], fb[KN][2];
+      for (int ks = 0; ks < KN; ++ks) {
+        fa[ks] = frag_rows(sC, 16 * wt, 4 * ks, ar16);
 #pragma unroll
-          for (int ks = 0; ks < KN; ++ks) {
-            fa[ks] = frag_rows(sC, 16 * wt, 4 * ks, ar16);
-#pragma unroll
-            for (int tt = 0; tt < 2; ++tt) fb[ks][tt] = frag_rows(bt, tj + 16 * tt, 4 * ks, ar16);
-          }
-          sched_ds_reads<3 * KN>();
-#pragma unroll
-          for (int ks = 0; ks < KN; ++ks)
-#pragma unroll
-            for (int tt = 0; tt < 2; ++tt) cbr[d][tt] = mfma(fa[ks], fb[ks][tt], cbr[d][tt]);
-          sched_mfmas<2 * KN>();
-        }
+        for (int tt = 0; tt < 2; ++tt) fb[ks][tt] = frag_rows(bt, tj + 16 * tt, 4 * ks, ar16);
       }
-      __syncthreads();
+      sched_ds_reads<3 * KN>();
 #pragma unroll
-      for (int d = 0; d < 2; ++d) {
-        if (jb0 + d < nj) {
-          sCB[jb0 + d][0][w][l] = cbr[d][0];
-          sCB[jb0 + d][1][w][l] = cbr[d][1];
-        }
-      }
+      for (int ks = 0; ks < KN; ++ks)
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) cbk[jb][tt] = mfma(fa[ks], fb[ks][tt], cbk[jb][tt]);
+      sched_mfmas<2 * KN>();
     }
   }
   scan_store(dtb, -__expf(A_log[head(0)]), sS[0], sDt[0]);
@@ -769,6 +742,13 @@ __global__ __launch_bounds__(BT) void bwd_row_bf16_kernel(
     float rm[4] = {0.f, 0.f, 0.f, 0.f};  // strictly-lower row sums of M over this team's columns
     float ddv = 0.f;                     // diagonal of yx
     float An = 0.f;                      // A_log of the next head (read at this head's first step)
+    // this wave's dy rows i, the first operand of every step's yx and of U
+    bf16x8 dyf[KP];
+    {
+      const RowsAt<8> ar8 = opaque(r8_);
+#pragma unroll
+      for (int ks = 0; ks < KP; ++ks) dyf[ks] = frag_rows(dyt, 16 * wt, 4 * ks, ar8);
+    }
 
 #pragma unroll
     for (int jb = 0; jb < NBMAX; ++jb) {
@@ -793,26 +773,24 @@ __global__ __launch_bounds__(BT) void bwd_row_bf16_kernel(
         f4 cbt[2];
         float sjv[2], dtv[2];  // s and dt at columns j = j0 + tj + 16 tt + r (clamped)
         {
-          bf16x8 fa[KP], fb[KP][2];
+          bf16x8 fb[KP][2];
 #pragma unroll
-          for (int ks = 0; ks < KP; ++ks) {
-            fa[ks] = frag_rows(dyt, 16 * wt, 4 * ks, ar8);
+          for (int ks = 0; ks < KP; ++ks)
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt) fb[ks][tt] = frag_rows(xt, tj + 16 * tt, 4 * ks, ar8);
-          }
-          cbt[0] = sCB[jb][0][w][l];
-          cbt[1] = sCB[jb][1][w][l];
+          cbt[0] = cbk[jb][0];
+          cbt[1] = cbk[jb][1];
 #pragma unroll
           for (int tt = 0; tt < 2; ++tt) {
             const int jc = min(j0 + tj + 16 * tt + r, Q - 1);
             sjv[tt] = sSh[jc];
             dtv[tt] = sDh[jc];
           }
-          sched_ds_reads<3 * KP + 6>();
+          sched_ds_reads<2 * KP + 4>();
 #pragma unroll
           for (int ks = 0; ks < KP; ++ks)
 #pragma unroll
-            for (int tt = 0; tt < 2; ++tt) yx[tt] = mfma(fa[ks], fb[ks][tt], yx[tt]);
+            for (int tt = 0; tt < 2; ++tt) yx[tt] = mfma(dyf[ks], fb[ks][tt], yx[tt]);
           sched_mfmas<2 * KP>();
         }
         if (jb == ib) {
@@ -853,9 +831,7 @@ __global__ __launch_bounds__(BT) void bwd_row_bf16_kernel(
     }
 
     // ---- per-head terms; the next head's dy and x tiles start loading, its
-    // H_c once this head's is read (after the last head, the B tiles for the
-    // dC phase, over C.B^T)
-    if (hh + 1 == hps) load_bs();
+    // H_c once this head's is read
     if (hh + 1 < hps) {
       load_dy(hh + 1);
       load_x(hh + 1, 0, sX[0]);
@@ -867,13 +843,12 @@ __global__ __launch_bounds__(BT) void bwd_row_bf16_kernel(
       const ColsAt<16> ac16 = opaque(c16_);
 #pragma unroll
       for (int ks = 0; ks < KP; ++ks) {
-        bf16x8 fa, fb[4];
-        fa = frag_rows(dyt, 16 * wt, 4 * ks, ar8);
+        bf16x8 fb[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) fb[k] = frag_cols(sH, 32 * ks, 16 * (4 * team + k), ac16);
-        sched_ds_reads<9>();
+        sched_ds_reads<8>();
 #pragma unroll
-        for (int k = 0; k < 4; ++k) u[k] = mfma(fa, fb[k], u[k]);
+        for (int k = 0; k < 4; ++k) u[k] = mfma(dyf[ks], fb[k], u[k]);
         sched_mfmas<4>();
       }
     }
@@ -921,10 +896,7 @@ __global__ __launch_bounds__(BT) void bwd_row_bf16_kernel(
     // the next head's dy and x tiles (all but H_c's 2 copies) must be in LDS
     // at the barrier; the stores below are issued after the wait and complete
     // during the next step
-    if (hh + 1 < hps)
-      wait_vm<2>();
-    else
-      wait_vm<0>();
+    if (hh + 1 < hps) wait_vm<2>();
     const int64_t tb = (static_cast<int64_t>(bi) * H + h) * T + static_cast<int64_t>(c) * Q;
     if (team == 0 && r == 15) {
 #pragma unroll
@@ -943,7 +915,7 @@ __global__ __launch_bounds__(BT) void bwd_row_bf16_kernel(
 
   // ---- dC_i = sum_j W_ij B_j + sum_h exp(s_i) U_i for this team's d_state
   // columns over all columns j (own and partner strips), against the B tiles
-  // loaded during the last head's per-head terms.  The W strips of blocks
+  // of the prologue.  The W strips of blocks
   // jb = 0..2 go to wset[jb] (block 3, if any, reuses wset[0] after them),
   // leaving the C, first dy, first x and H_c tiles free for the next pass's
   // first tiles, which start loading now.
