@@ -78,9 +78,7 @@ __global__ __launch_bounds__(FT) void out_fwd_bf16_kernel(
   __shared__ __attribute__((aligned(1024))) char sH_[FTILE_N];          // H_c [p][n] (bf16); B tile slot
   __shared__ __attribute__((aligned(1024))) char sXch_[FTILE_N];        // y halves; B tile slot
   __shared__ __attribute__((aligned(1024))) char sG_[FW * FSTRIP];      // per-wave G strips [j][i]
-  // C.B^T, lane-linear; before it is formed and after its last use, the B
-  // tiles of blocks jb (tile jb in the jb-th 16 KB)
-  __shared__ __attribute__((aligned(1024))) f4 sCB[NBMAX][2][FW][WAVE];
+  __shared__ __attribute__((aligned(1024))) char sBt_[NBMAX * FTILE_N];  // B tiles of blocks jb, tile jb at jb * 16 KB
   __shared__ __attribute__((aligned(16))) float sS[2][QMAX];
   __shared__ __attribute__((aligned(16))) float sDt[2][QMAX];
   lds_char* const sC = lds_ptr(sC_);
@@ -88,7 +86,7 @@ __global__ __launch_bounds__(FT) void out_fwd_bf16_kernel(
   lds_char* const sH = lds_ptr(sH_);
   lds_char* const sXch = lds_ptr(sXch_);
   lds_char* const sG = lds_ptr(sG_);
-  lds_char* const sBt = lds_ptr(sCB);
+  lds_char* const sBt = lds_ptr(sBt_);
 
   const int nc = T / Q, nb = (Q + BQ - 1) / BQ;
   const int hpg = H / G, hps = hpg / nsplit;
@@ -156,7 +154,7 @@ __global__ __launch_bounds__(FT) void out_fwd_bf16_kernel(
     load_h(0);
     load_dt(0);
   };
-  // the B tiles of blocks jb <= jx, each to its own 16 KB of the C.B^T area
+  // the B tiles of blocks jb <= jx, each to its own 16 KB
   auto load_bs = [&](int jx) {
 #pragma unroll
     for (int jb = 0; jb < NBMAX; ++jb) {
@@ -170,49 +168,36 @@ __global__ __launch_bounds__(FT) void out_fwd_bf16_kernel(
   const bool next = pass == 0 && nb - 1 - kpair != kpair;
 
   // ---- C rows of block ib, the B tiles of blocks jb <= ib and the first
-  // head's tiles, in flight together (the second block of a pair finds them
-  // loaded during the first block's last head), then C.B^T for every block
-  // jb <= ib, over the B tiles once all are read, two blocks at a time (C.B^T
-  // of block jb goes over the B tile of block jb)
+  // head's tiles, in flight together, then C.B^T for every block jb <= ib,
+  // kept in registers.  The B tiles stay for the second block of a pair
+  // (whose blocks are a subset); its first tiles load during the first
+  // block's last head.
   if (pass == 0) {
     load_first(ib);
     load_bs(ib);
   }
   wait_vm<0>();
   __syncthreads();
+  f4 cbk[NBMAX][2];  // rows i of this wave, columns j = jb * 64 + tj + 16 tt + r
 #pragma unroll
-  for (int jb0 = 0; jb0 < NBMAX; jb0 += 2) {
-    if (jb0 < nj) {
-      f4 cbr[2][2];
+  for (int jb = 0; jb < NBMAX; ++jb) {
+    zero(cbk[jb]);
+    if (jb < nj) {
+      const lds_char* bt = sBt + jb * FTILE_N;
+      const RowsAt<16> ar16 = opaque(r16_);
+      bf16x8 fa[FKN], fb[FKN][2];
 #pragma unroll
-      for (int d = 0; d < 2; ++d) {
-        if (jb0 + d < nj) {
-          const lds_char* bt = sBt + (jb0 + d) * FTILE_N;
-          const RowsAt<16> ar16 = opaque(r16_);
-          zero(cbr[d]);
-          bf16x8 fa[FKN], fb[FKN][2];
+      for (int ks = 0; ks < FKN; ++ks) {
+        fa[ks] = frag_rows(sC, 16 * wt, 4 * ks, ar16);
 #pragma unroll
-          for (int ks = 0; ks < FKN; ++ks) {
-            fa[ks] = frag_rows(sC, 16 * wt, 4 * ks, ar16);
-#pragma unroll
-            for (int tt = 0; tt < 2; ++tt) fb[ks][tt] = frag_rows(bt, tj + 16 * tt, 4 * ks, ar16);
-          }
-          sched_ds_reads<3 * FKN>();
-#pragma unroll
-          for (int ks = 0; ks < FKN; ++ks)
-#pragma unroll
-            for (int tt = 0; tt < 2; ++tt) cbr[d][tt] = mfma(fa[ks], fb[ks][tt], cbr[d][tt]);
-          sched_mfmas<2 * FKN>();
-        }
+        for (int tt = 0; tt < 2; ++tt) fb[ks][tt] = frag_rows(bt, tj + 16 * tt, 4 * ks, ar16);
       }
-      __syncthreads();
+      sched_ds_reads<3 * FKN>();
 #pragma unroll
-      for (int d = 0; d < 2; ++d) {
-        if (jb0 + d < nj) {
-          sCB[jb0 + d][0][w][l] = cbr[d][0];
-          sCB[jb0 + d][1][w][l] = cbr[d][1];
-        }
-      }
+      for (int ks = 0; ks < FKN; ++ks)
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) cbk[jb][tt] = mfma(fa[ks], fb[ks][tt], cbk[jb][tt]);
+      sched_mfmas<2 * FKN>();
     }
   }
   fwd_scan_store(dtb, -__expf(A_log[head(0)]), sS[0], sDt[0]);
@@ -253,15 +238,15 @@ __global__ __launch_bounds__(FT) void out_fwd_bf16_kernel(
             load_dt(hh + 1);
           }
         }
-        // the step's C.B^T tiles, the s and dt values of its columns and the x
-        // fragments of the G x contraction are read together
+        // the s and dt values of the step's columns and the x fragments of the
+        // G x contraction are read together
         const ColsAt<2> ac2 = opaque(c2_);
         const ColsAt<8> ac8 = opaque(c8_);
         f4 cbt[2];
         float sjv[2], dtv[2];  // s and dt at columns j = j0 + tj + 16 tt + r (clamped)
         bf16x8 fx[4];
-        cbt[0] = sCB[jb][0][w][l];
-        cbt[1] = sCB[jb][1][w][l];
+        cbt[0] = cbk[jb][0];
+        cbt[1] = cbk[jb][1];
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
           const int jc = min(j0 + tj + 16 * tt + r, Q - 1);
@@ -270,7 +255,7 @@ __global__ __launch_bounds__(FT) void out_fwd_bf16_kernel(
         }
 #pragma unroll
         for (int pt = 0; pt < 4; ++pt) fx[pt] = frag_cols(xt, tj, 16 * pt, ac8);
-        sched_ds_reads<14>();
+        sched_ds_reads<12>();
         f4 gv[2];
         if (jb == ib) {
 #pragma unroll
@@ -312,10 +297,9 @@ __global__ __launch_bounds__(FT) void out_fwd_bf16_kernel(
     }
 
     // ---- finish head hh; the next head's first x tile starts loading, its
-    // H_c once this head's is read (after the last head, the next block's B
-    // tiles over C.B^T and then its first tiles)
+    // H_c once this head's is read (after the last head, the next block's
+    // first tiles)
     if (hh + 1 < hps) load_x(hh + 1, 0, sX[0]);
-    if (hh + 1 == hps && next) load_bs(kpair);
     // hand the other team's headdim columns to it
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
