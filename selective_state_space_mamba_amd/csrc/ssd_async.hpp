@@ -253,6 +253,16 @@ __device__ __forceinline__ float acc_elem(const u32x2& v, int e) {
   return __uint_as_float((e & 1) ? (d & 0xFFFF0000u) : (d << 16));
 }
 
+// Raw buffer stores of one element at byte offset voff + soff (soff uniform).
+// A voff at or beyond OOB_OFFSET is out of the descriptor's range and the
+// store is dropped, which predicates stores without branches.
+__device__ __forceinline__ void store_f32(__amdgpu_buffer_rsrc_t rs, float v, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rs, voff, soff, 0);
+}
+__device__ __forceinline__ void store_b16(__amdgpu_buffer_rsrc_t rs, uint16_t v, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_buffer_store_b16(v, rs, voff, soff, 0);
+}
+
 // One element (row, col) of a swizzled tile, as f32.
 template <int CPR>
 __device__ __forceinline__ float tile_elem(const lds_char* t, int row, int col) {

@@ -148,6 +148,12 @@ __global__ __launch_bounds__(BT) void bwd_col_bf16_kernel(
   const i32x4 rc = make_rsrc(Cm + row0 * GN);
   const i32x4 rg = make_rsrc(gamma + (static_cast<int64_t>(bi) * nc + c) * HP * N);
   const __amdgpu_buffer_rsrc_t rdt = make_rsrc_ptr(dt + row0 * H);
+  // outputs: dx from the chunk's first row; the per-column sums of (bi, h = 0, c)
+  const __amdgpu_buffer_rsrc_t rdx = make_rsrc_ptr(dx + row0 * HP);
+  const int64_t sum0 = static_cast<int64_t>(bi) * H * T + static_cast<int64_t>(c) * Q;
+  const __amdgpu_buffer_rsrc_t rcol = make_rsrc_ptr(colE + sum0);
+  const __amdgpu_buffer_rsrc_t rdiag = make_rsrc_ptr(diagE + sum0);
+  const __amdgpu_buffer_rsrc_t rrp = make_rsrc_ptr(Rp + sum0);
   // the second block of a pair takes the heads in reverse order, so that the
   // heads' tiles the first block read last are still in L2
   auto headp = [&](int pp, int hh) { return g * hpg + sp * hps + (pp ? hps - 1 - hh : hh); };
@@ -454,7 +460,7 @@ __global__ __launch_bounds__(BT) void bwd_col_bf16_kernel(
       if (r == 15) {
         sRed[team][jl][0] = cs;
         sRed[team][jl][1] = ds;
-        sRed[team][jl][2] = part;
+        sRed[team][jl][2] = wj[e] * part;
       }
     }
     lds_barrier();
@@ -464,14 +470,12 @@ __global__ __launch_bounds__(BT) void bwd_col_bf16_kernel(
     for (int k = 0; k < 2; ++k)
 #pragma unroll
       for (int e = 0; e < 4; ++e) dxv[k][e] = dtj[e] * (dxa[k][e] + wj[e] * bg[k][e]) + Dh * acc_elem(dsk[k], e);
-    float ce[4], de[4], re[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int jl = 16 * wt + 4 * q + e;
-      ce[e] = sRed[0][jl][0] + sRed[1][jl][0];
-      de[e] = sRed[0][jl][1] + sRed[1][jl][1];
-      re[e] = wj[e] * (sRed[0][jl][2] + sRed[1][jl][2]);
-    }
+    // the per-column sums of this wave's columns j = 16 wt + (l % 16), one
+    // column per lane of each 16-lane row
+    const int jc = 16 * wt + r;
+    const float ce = sRed[0][jc][0] + sRed[1][jc][0];
+    const float de = sRed[0][jc][1] + sRed[1][jc][1];
+    const float re = sRed[0][jc][2] + sRed[1][jc][2];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const float f = dtj[e] * wj[e];
@@ -482,24 +486,24 @@ __global__ __launch_bounds__(BT) void bwd_col_bf16_kernel(
     // LDS at the barrier; the stores below are issued after the wait and
     // complete during the next step
     if (hh + 1 < hps) wait_vm<2>();
-    const int64_t tb = (static_cast<int64_t>(bi) * H + h) * T + static_cast<int64_t>(c) * Q;
+    // dx (element (jq, p) at byte (jq HP + h P + p) 4 from the chunk's first
+    // row) and the per-column sums; out-of-range offsets are dropped
+    {
+      const uint32_t vdx = (static_cast<uint32_t>(j0 + 16 * wt + 4 * q) * HP + 32 * team + r) * 4;
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
+      for (int k = 0; k < 2; ++k) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int jq = j0 + 16 * wt + 4 * q + e, p = 16 * (2 * team + k) + r;
-        if (jq < Q && p < P) dx[(row0 + jq) * HP + static_cast<int64_t>(h) * P + p] = dxv[k][e];
-      }
-    }
-    if (team == 0 && r == 15) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int jq = j0 + 16 * wt + 4 * q + e;
-        if (jq < Q) {
-          colE[tb + jq] = ce[e];
-          diagE[tb + jq] = de[e];
-          Rp[tb + jq] = re[e];
+        for (int e = 0; e < 4; ++e) {
+          const bool ok = j0 + 16 * wt + 4 * q + e < Q && 32 * team + 16 * k + r < P;
+          store_f32(rdx, dxv[k][e], ok ? vdx + 64 * k : OOB_OFFSET, static_cast<uint32_t>(e * HP + h * P) * 4);
         }
+      }
+      if (team == 0) {
+        const uint32_t vo = (q == 0 && j0 + jc < Q) ? static_cast<uint32_t>(j0 + jc) * 4 : OOB_OFFSET;
+        const uint32_t so = static_cast<uint32_t>(h) * T * 4;
+        store_f32(rcol, ce, vo, so);
+        store_f32(rdiag, de, vo, so);
+        store_f32(rrp, re, vo, so);
       }
     }
     if (hh + 1 < hps) scan_store(dtb, -__expf(An), sS[hb ^ 1], sDt[hb ^ 1]);
@@ -637,6 +641,10 @@ __global__ __launch_bounds__(BT) void bwd_row_bf16_kernel(
   const i32x4 rc = make_rsrc(Cm + row0 * GN);
   const i32x4 rh = make_rsrc(hbf + (static_cast<int64_t>(bi) * nc + c) * HP * N);
   const __amdgpu_buffer_rsrc_t rdt = make_rsrc_ptr(dt + row0 * H);
+  // outputs: the per-row sums of (bi, h = 0, c)
+  const int64_t sum0 = static_cast<int64_t>(bi) * H * T + static_cast<int64_t>(c) * Q;
+  const __amdgpu_buffer_rsrc_t rrow = make_rsrc_ptr(rowM + sum0);
+  const __amdgpu_buffer_rsrc_t rdso = make_rsrc_ptr(dsoff + sum0);
   // the second block of a pair takes the heads in reverse order, so that the
   // heads' tiles the first block read last are still in L2
   auto headp = [&](int pp, int hh) { return g * hpg + sp * hps + (pp ? hps - 1 - hh : hh); };
@@ -874,7 +882,7 @@ __global__ __launch_bounds__(BT) void bwd_row_bf16_kernel(
       const float rs = row_sum16(rm[e]);
       if (r == 15) {
         sRed[team][il][0] = rs;
-        sRed[team][il][1] = part;
+        sRed[team][il][1] = ex[e] * part;
       }
     }
     {
@@ -883,13 +891,11 @@ __global__ __launch_bounds__(BT) void bwd_row_bf16_kernel(
     }
     lds_barrier();
     if (hh + 1 < hps) load_h(hh + 1);  // this head's H_c is no longer read
-    float rmv[4], dso[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int il = 16 * wt + 4 * q + e;
-      rmv[e] = sRed[0][il][0] + sRed[1][il][0];
-      dso[e] = ex[e] * (sRed[0][il][1] + sRed[1][il][1]);
-    }
+    // the per-row sums of this wave's rows i = 16 wt + (l % 16), one row per
+    // lane of each 16-lane row
+    const int ic = 16 * wt + r;
+    const float rmv = sRed[0][ic][0] + sRed[1][ic][0];
+    const float dso = sRed[0][ic][1] + sRed[1][ic][1];
     float tot = 0.f;
 #pragma unroll
     for (int kk = 0; kk < BW; ++kk) tot += sDD[kk][0] + sDD[kk][1] + sDD[kk][2] + sDD[kk][3];
@@ -897,16 +903,12 @@ __global__ __launch_bounds__(BT) void bwd_row_bf16_kernel(
     // at the barrier; the stores below are issued after the wait and complete
     // during the next step
     if (hh + 1 < hps) wait_vm<2>();
-    const int64_t tb = (static_cast<int64_t>(bi) * H + h) * T + static_cast<int64_t>(c) * Q;
-    if (team == 0 && r == 15) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int iq = i0 + 16 * wt + 4 * q + e;
-        if (iq < Q) {
-          rowM[tb + iq] = rmv[e];
-          dsoff[tb + iq] = dso[e];
-        }
-      }
+    if (team == 0) {
+      // out-of-range offsets are dropped
+      const uint32_t vo = (q == 0 && i0 + ic < Q) ? static_cast<uint32_t>(i0 + ic) * 4 : OOB_OFFSET;
+      const uint32_t so = static_cast<uint32_t>(h) * T * 4;
+      store_f32(rrow, rmv, vo, so);
+      store_f32(rdso, dso, vo, so);
     }
     if (threadIdx.x == 0) dD_part[((static_cast<int64_t>(bi) * nc + c) * nb + ib) * H + h] = tot;
     if (hh + 1 < hps) scan_store(dtb, -__expf(An), sS[hb ^ 1], sDt[hb ^ 1]);

@@ -129,6 +129,7 @@ __global__ __launch_bounds__(FT) void out_fwd_bf16_kernel(
   const i32x4 rc = make_rsrc(Cm + row0 * GN);
   const i32x4 rh = make_rsrc(hbf + (static_cast<int64_t>(bi) * nc + c) * HP * N);
   const __amdgpu_buffer_rsrc_t rdt = make_rsrc_ptr(dt + row0 * H);
+  const __amdgpu_buffer_rsrc_t ry = make_rsrc_ptr(y + row0 * HP);
   auto head = [&](int hh) { return g * hpg + sp * hps + hh; };
 
   auto load_dt = [&](int hh) {
@@ -348,12 +349,17 @@ __global__ __launch_bounds__(FT) void out_fwd_bf16_kernel(
     // at the barrier; the stores below are issued after the wait and complete
     // during the next step
     if (hh + 1 < hps) wait_vm<2>();
+    // y (element (iq, p) at byte (iq HP + h P + p) 2 from the chunk's first
+    // row); out-of-range offsets are dropped
+    {
+      const uint32_t vy = (static_cast<uint32_t>(i0 + 16 * wt + 4 * q) * HP + 32 * team + r) * 2;
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
+      for (int k = 0; k < 2; ++k) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int iq = i0 + 16 * wt + 4 * q + e, p = 16 * (2 * team + k) + r;
-        if (iq < Q && p < P) y[(row0 + iq) * HP + static_cast<int64_t>(h) * P + p] = yv[k][e];
+        for (int e = 0; e < 4; ++e) {
+          const bool ok = i0 + 16 * wt + 4 * q + e < Q && 32 * team + 16 * k + r < P;
+          store_b16(ry, yv[k][e], ok ? vy + 32 * k : OOB_OFFSET, static_cast<uint32_t>(e * HP + h * P) * 2);
+        }
       }
     }
     if (hh + 1 < hps) fwd_scan_store(dtb, -__expf(An), sS[hb ^ 1], sDt[hb ^ 1]);
