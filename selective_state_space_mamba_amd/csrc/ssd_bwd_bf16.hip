@@ -6,11 +6,12 @@
 // contractions stays inside the wave.
 //
 // Column kernel: a workgroup owns the 64 columns j of block jb of one chunk
-// for the heads of one group (or a run of them).  Its 8 waves form two teams;
-// wave (team, wt) owns columns j0 + 16 wt .. +15 and, in every 64-row block
-// ib >= jb, the rows i0 + 32 team .. +31.  C.B^T for those tiles is formed
-// once (MFMA) and kept in LDS.  One step handles one head and one block ib;
-// in it the wave
+// for the heads of one group (or a run of them), and then those of block
+// nb - 1 - jb.  Its 8 waves form two teams; wave (team, wt) owns columns
+// j0 + 16 wt .. +15 and, in every 64-row block ib >= jb, the rows
+// i0 + 32 team .. +31.  C.B^T for those tiles is formed once (MFMA) and kept
+// in registers, as are the wave's x fragments for the head.  One step handles
+// one head and one block ib; in it the wave
 //   * forms yx^T = x_j . dy_i for its 16 x 32 tile with MFMA,
 //   * applies the decay: G = L CB (to a wave-private LDS strip, bf16),
 //     E = G yx (column and diagonal sums) and W = L yx dt_j (summed over heads
@@ -24,11 +25,9 @@
 // dB_j = sum_i W_ij C_i + state terms, each team finishing half of the
 // d_state columns.  The other workgroup barrier ends a step, where the next
 // step's tiles (loaded by all waves while this step computed) become visible.
-// Every ring slot that an asynchronous copy targets is its own LDS variable,
-// selected by a compile-time step index, so the compiler can tell that the
-// (The copies are issued from inline assembly, so the compiler adds no waits
-// of its own for them; the barriers inside a step wait for LDS operations
-// only.)
+// The copies are issued from inline assembly, so the compiler adds no waits
+// of its own for them; the kernels wait with counted vmcnt waits and use
+// barriers that wait for LDS operations only.
 //
 // Off the diagonal block every i exceeds every j, so with s non-increasing
 // L_ij = exp(s_i - s_i0) exp(s_i0 - s_j) (i0 the block's first row): factors

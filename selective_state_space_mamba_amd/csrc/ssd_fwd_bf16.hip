@@ -8,10 +8,10 @@
 //   y_i = sum_{j<=i} exp(s_i - s_j) (C_i . B_j) dt_j x_j + exp(s_i) C_i . H_c^T + D x_i.
 //
 // A workgroup owns the 64 rows i of block ib of one chunk for the heads of one
-// group (or a run of them).  Its 8 waves form two teams; wave (team, wt) owns
-// rows i0 + 16 wt .. +15 and, in every block jb <= ib, the columns
-// j0 + 32 team .. +31.  C_i.B_j for those tiles is formed once (MFMA) and
-// kept in LDS.  A step (one head, one block jb) applies the decay and dt_j,
+// group (or a run of them), and then those of block nb - 1 - ib.  Its 8 waves
+// form two teams; wave (team, wt) owns rows i0 + 16 wt .. +15 and, in every
+// block jb <= ib, the columns j0 + 32 team .. +31.  C_i.B_j for those tiles is
+// formed once (MFMA) and kept in registers.  A step (one head, one block jb) applies the decay and dt_j,
 // puts the bf16 result in a wave-private LDS strip and accumulates
 // sum_j G_ij x_j over the wave's 32 columns j with MFMA (G and x read down
 // their rows with the LDS transpose read).  Once per head the teams swap the
