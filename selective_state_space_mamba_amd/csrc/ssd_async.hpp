@@ -56,9 +56,38 @@ __device__ __forceinline__ void dma16(const i32x4& rs, lds_char* dst, uint32_t v
 #endif
 }
 
+// One wave's copy of 64 16-bit elements into LDS: a sub-dword LDS-direct load
+// writes one dword per lane, at dst + 4 * lane, holding the element
+// zero-extended (measured on gfx950).  voff at or beyond OOB_OFFSET gives 0.
+__device__ __forceinline__ void dma_u16(const i32x4& rs, lds_char* dst, uint32_t voff) {
+#if defined(__HIP_DEVICE_COMPILE__)  // gfx950 assembly: device pass only
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(dst)));
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_ushort %1, %2, 0 offen lds" ::"s"(m0v), "v"(voff), "s"(rs)
+               : "memory", "m0");
+#endif
+}
+
+// The chunk's Q <= 256 time steps of one 16-bit per-step series (dt of one
+// head: element t at byte t * stride from the descriptor's base) into LDS as
+// dwords (step t at dst + 4 t), zero past Q.  Every wave issues exactly one
+// copy instruction (waves beyond the four a chunk needs repeat a copy, with
+// identical data), so that counted waits stay the same in every wave.
+template <int NW>
+__device__ __forceinline__ void steps_async(lds_char* dst, const i32x4& rs, uint32_t stride, int Q) {
+  static_assert(NW >= 4, "four waves cover 256 steps");
+  const int w = wave_id() % 4, t = 64 * w + lane_id();
+  dma_u16(rs, dst + 256 * w, t < Q ? static_cast<uint32_t>(t) * stride : OOB_OFFSET);
+}
+
 // The same descriptor in the type the buffer-load builtins take.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc_ptr(const void* base) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0x7FFFFFF0, 0x00020000);
+}
+
+// The same for an optional output: a null pointer gets an empty range, so
+// every access through the descriptor is dropped.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc_opt(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, base ? 0x7FFFFFF0 : 0, 0x00020000);
 }
 
 __device__ __forceinline__ lds_char* lds_ptr(void* p) { return (lds_char*)p; }

@@ -73,6 +73,7 @@ __global__ __launch_bounds__(ST) void chunk_state_bf16_kernel(
   __shared__ __attribute__((aligned(1024))) char sB_[2 * BSLAB];
   __shared__ __attribute__((aligned(1024))) char sH_[REV ? 2 * HTILE : 16];  // bwd: H_c (f32), two chunks
   __shared__ __attribute__((aligned(16))) float sWt[SW][QMAX];                // per-wave step weights
+  __shared__ __attribute__((aligned(16))) uint32_t sDtb[2][QMAX];             // dt bits of a chunk, two chunks
   __shared__ float sGh[2][SW];
   lds_char* const sX = lds_ptr(sX_);
   lds_char* const sB = lds_ptr(sB_);
@@ -88,11 +89,12 @@ __global__ __launch_bounds__(ST) void chunk_state_bf16_kernel(
   const float A = -__expf(A_log[h]);
   const int l = lane_id(), w = wave_id(), r = l & 15, q = l >> 4;
   const int pw = w & 1, nw = w >> 1;
+  const ColsAt<4> c4_ = cols_at<4>();    // per-lane fragment offsets of the x (dy) and
+  const ColsAt<16> c16_ = cols_at<16>();  // B (C) slabs
   const int64_t HP = static_cast<int64_t>(H) * P, GN = static_cast<int64_t>(G) * N;
   const int64_t PN = static_cast<int64_t>(P) * N;
   const uint32_t HPb = static_cast<uint32_t>(HP) * 2, GNb = static_cast<uint32_t>(GN) * 2;
   const int pch = min(4, (P - p0) >> 3), nch = N >> 3;
-  const __amdgpu_buffer_rsrc_t rdt = make_rsrc_ptr(dt + static_cast<int64_t>(bi) * T * H);
   float* const wts = sWt[w];
 
   f4 st[2];  // rows p = p0 + 16 pw + 4q + e, columns n = 32 nw + 16 t + r
@@ -105,8 +107,9 @@ __global__ __launch_bounds__(ST) void chunk_state_bf16_kernel(
     }
 
   auto chunk_of = [&](int it) { return REV ? nc - 1 - it : it; };
-  uint32_t dtb[4];  // dt bits of t = 4l .. 4l+3 of the next chunk to scan
-  // slab sl of chunk it; with the first slab also the chunk's dt and (bwd) H_c
+  // slab sl of chunk it; with the first slab also the chunk's dt (to LDS, so
+  // that no load the compiler can see is in flight: its own wait for one would
+  // be vmcnt(0) and hold up every copy) and (bwd) H_c
   auto load_slab = [&](int it, int sl) {
     const int c = chunk_of(it);
     const int64_t row0 = static_cast<int64_t>(bi) * T + static_cast<int64_t>(c) * Q + sl * SSJ;
@@ -115,12 +118,8 @@ __global__ __launch_bounds__(ST) void chunk_state_bf16_kernel(
     tile_async<SSJ, 4, SW>(sX + buf * XSLAB, make_rsrc(X + row0 * HP), h * P * 2 + p0 * 2, HPb, vr, pch);
     tile_async<SSJ, 16, SW>(sB + buf * BSLAB, make_rsrc(Bm + row0 * GN), g * N * 2, GNb, vr, nch);
     if (sl == 0) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int t = 4 * l + e;
-        const uint32_t off = (t < Q) ? static_cast<uint32_t>((c * Q + t) * H) * 2 : OOB_OFFSET;
-        dtb[e] = __builtin_amdgcn_raw_buffer_load_b16(rdt, off, h * 2, 0);
-      }
+      steps_async<SW>(lds_ptr(sDtb[it & 1]), make_rsrc(dt + (static_cast<int64_t>(bi) * T + static_cast<int64_t>(c) * Q) * H + h),
+                      H * 2, Q);
       if constexpr (REV) {
         const int64_t sbase = ((static_cast<int64_t>(bi) * nc + c) * H + h) * PN + static_cast<int64_t>(p0) * N;
         tile_async<SPB, 32, SW>(sH + (it & 1) * HTILE, make_rsrc(hstates + sbase), 0, N * 4, P - p0, N >> 2);
@@ -140,8 +139,10 @@ __global__ __launch_bounds__(ST) void chunk_state_bf16_kernel(
       if (sl == 0) {
         // this chunk's step weights (every wave computes the scan itself)
         float d[4], a[4];
+        const uint4 db = *reinterpret_cast<const uint4*>(&sDtb[it & 1][4 * l]);
+        const uint32_t dbv[4] = {db.x, db.y, db.z, db.w};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) d[e] = bf16_bits_to_f32(static_cast<uint16_t>(dtb[e]));
+        for (int e = 0; e < 4; ++e) d[e] = bf16_bits_to_f32(static_cast<uint16_t>(dbv[e]));
         a[0] = d[0] * A;
 #pragma unroll
         for (int e = 1; e < 4; ++e) a[e] = a[e - 1] + d[e] * A;
@@ -166,10 +167,40 @@ __global__ __launch_bounds__(ST) void chunk_state_bf16_kernel(
       const lds_char* xs = sX + buf * XSLAB;
       const lds_char* bs = sB + buf * BSLAB;
       const int kw = min(SSJ, Q - sl * SSJ);
-      for (int k0 = 0; k0 < kw; k0 += 32) {
-        const bf16x8 ax = scale_frag(frag_cols<4>(xs, k0, 16 * pw), wts + sl * SSJ + k0 + 8 * q);
+      if (kw == SSJ) {
+        // a full slab: every fragment and weight read first, then the scaling
+        // and the MFMAs, so that the reads' latencies overlap
+        constexpr int KS = SSJ / 32;
+        const ColsAt<4> ac4 = opaque(c4_);
+        const ColsAt<16> ac16 = opaque(c16_);
+        bf16x8 xa[KS], bb[KS][2];
+        float4 wa[KS][2];
 #pragma unroll
-        for (int t = 0; t < 2; ++t) acc[t] = mfma(ax, frag_cols<16>(bs, k0, 32 * nw + 16 * t), acc[t]);
+        for (int ks = 0; ks < KS; ++ks) {
+          xa[ks] = frag_cols(xs, 32 * ks, 16 * pw, ac4);
+          const float* wp = wts + sl * SSJ + 32 * ks + 8 * q;
+          wa[ks][0] = *reinterpret_cast<const float4*>(wp);
+          wa[ks][1] = *reinterpret_cast<const float4*>(wp + 4);
+#pragma unroll
+          for (int t = 0; t < 2; ++t) bb[ks][t] = frag_cols(bs, 32 * ks, 32 * nw + 16 * t, ac16);
+        }
+        sched_ds_reads<KS * 8>();
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const float wv[8] = {wa[ks][0].x, wa[ks][0].y, wa[ks][0].z, wa[ks][0].w,
+                               wa[ks][1].x, wa[ks][1].y, wa[ks][1].z, wa[ks][1].w};
+          bf16x8 ax;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) ax[e] = static_cast<__bf16>(static_cast<float>(xa[ks][e]) * wv[e]);
+#pragma unroll
+          for (int t = 0; t < 2; ++t) acc[t] = mfma(ax, bb[ks][t], acc[t]);
+        }
+      } else {
+        for (int k0 = 0; k0 < kw; k0 += 32) {
+          const bf16x8 ax = scale_frag(frag_cols<4>(xs, k0, 16 * pw), wts + sl * SSJ + k0 + 8 * q);
+#pragma unroll
+          for (int t = 0; t < 2; ++t) acc[t] = mfma(ax, frag_cols<16>(bs, k0, 32 * nw + 16 * t), acc[t]);
+        }
       }
     }
 
@@ -178,22 +209,26 @@ __global__ __launch_bounds__(ST) void chunk_state_bf16_kernel(
     const int64_t sbase = ((static_cast<int64_t>(bi) * nc + c) * H + h) * PN;
     const float* ht = reinterpret_cast<const float*>(sH_ + (it & 1) * HTILE);
     float gh = 0.f;
+    // element (p, n) of the chunk's state at byte (p N + n) * size; invalid
+    // elements get an out-of-range offset and their stores are dropped
+    const __amdgpu_buffer_rsrc_t rsf = make_rsrc_opt(!REV && states_f32 ? states_f32 + sbase : nullptr);
+    const __amdgpu_buffer_rsrc_t rsb = make_rsrc_opt(states_bf ? states_bf + sbase : nullptr);
+    const __amdgpu_buffer_rsrc_t rhb = make_rsrc_opt(hbf_out ? hbf_out + sbase : nullptr);
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int pl = 16 * pw + 4 * q + e, p = p0 + pl, n = 32 * nw + 16 * t + r;
-        if (p < P && n < N) {
-          const int64_t o = sbase + p * N + n;
-          if constexpr (!REV) {
-            states_f32[o] = st[t][e];
-            if (states_bf) states_bf[o] = f32_to_bf16_bits(st[t][e]);
-          } else {
-            const float hv = ht[pl * NMAX + n];  // tile rows are 128 floats
-            states_bf[o] = f32_to_bf16_bits(st[t][e]);
-            gh += st[t][e] * hv;
-            if (hbf_out) hbf_out[o] = f32_to_bf16_bits(hv);
-          }
+        const bool ok = p < P && n < N;
+        const uint32_t eo = static_cast<uint32_t>(p * N + n);
+        if constexpr (!REV) {
+          store_f32(rsf, st[t][e], ok ? eo * 4 : OOB_OFFSET, 0);
+          if (states_bf) store_b16(rsb, f32_to_bf16_bits(st[t][e]), ok ? eo * 2 : OOB_OFFSET, 0);
+        } else {
+          const float hv = ok ? ht[pl * NMAX + n] : 0.f;  // tile rows are 128 floats
+          store_b16(rsb, f32_to_bf16_bits(st[t][e]), ok ? eo * 2 : OOB_OFFSET, 0);
+          gh += st[t][e] * hv;
+          if (hbf_out) store_b16(rhb, f32_to_bf16_bits(hv), ok ? eo * 2 : OOB_OFFSET, 0);
         }
         st[t][e] = decay * st[t][e] + acc[t][e];
       }
