@@ -52,13 +52,15 @@ static_assert(NBMAX <= 4, "the dB and dC phases hold at most four blocks' W stri
 }  // namespace
 
 // s (within-chunk inclusive cumsum of dt A) and dt for t < Q, from the dt bits
-// of t = 4l .. 4l+3 held by lane l; every wave computes the whole scan and
-// waves 0..3 each write a quarter.
-__device__ __forceinline__ void scan_store(const uint32_t (&dtb)[4], float A, float* s_out, float* dt_out) {
+// copied to LDS (one dword per step; lane l reads t = 4l .. 4l+3); every wave
+// computes the whole scan and waves 0..3 each write a quarter.
+__device__ __forceinline__ void scan_store(const uint32_t* dtb_lds, float A, float* s_out, float* dt_out) {
   const int l = lane_id(), w = wave_id();
   float d[4], a[4];
+  const uint4 db = *reinterpret_cast<const uint4*>(dtb_lds + 4 * l);
+  const uint32_t dbv[4] = {db.x, db.y, db.z, db.w};
 #pragma unroll
-  for (int e = 0; e < 4; ++e) d[e] = bf16_bits_to_f32(static_cast<uint16_t>(dtb[e]));
+  for (int e = 0; e < 4; ++e) d[e] = bf16_bits_to_f32(static_cast<uint16_t>(dbv[e]));
   a[0] = d[0] * A;
 #pragma unroll
   for (int e = 1; e < 4; ++e) a[e] = a[e - 1] + d[e] * A;
@@ -96,6 +98,7 @@ __global__ __launch_bounds__(BT) void bwd_col_bf16_kernel(
   __shared__ float sRed[2][BQ][3];                                     // column sums, diagonal, R' halves
   __shared__ __attribute__((aligned(16))) float sS[2][QMAX];
   __shared__ __attribute__((aligned(16))) float sDt[2][QMAX];
+  __shared__ __attribute__((aligned(16))) uint32_t sDtb[QMAX];  // dt bits of the next head to scan
   lds_char* const sB = lds_ptr(sB_);
   lds_char* const sX = lds_ptr(sX_);
   lds_char* const sDy[2] = {lds_ptr(sDy0_), lds_ptr(sDy1_)};
@@ -118,7 +121,6 @@ __global__ __launch_bounds__(BT) void bwd_col_bf16_kernel(
   const int c = idx % nc;
   const int bi = idx / nc;
 
-  uint32_t dtb[4];  // dt bits of t = 4l .. 4l+3 for the next scan, converted when used
   for (int pass = 0; pass < 2; ++pass) {
   const int jb = pass ? nb - 1 - kpair : kpair;  // the block with the most rows i first
   if (pass && jb == kpair) break;
@@ -146,7 +148,6 @@ __global__ __launch_bounds__(BT) void bwd_col_bf16_kernel(
   const i32x4 rb = make_rsrc(Bm + row0 * GN);
   const i32x4 rc = make_rsrc(Cm + row0 * GN);
   const i32x4 rg = make_rsrc(gamma + (static_cast<int64_t>(bi) * nc + c) * HP * N);
-  const __amdgpu_buffer_rsrc_t rdt = make_rsrc_ptr(dt + row0 * H);
   // outputs: dx from the chunk's first row; the per-column sums of (bi, h = 0, c)
   const __amdgpu_buffer_rsrc_t rdx = make_rsrc_ptr(dx + row0 * HP);
   const int64_t sum0 = static_cast<int64_t>(bi) * H * T + static_cast<int64_t>(c) * Q;
@@ -158,14 +159,9 @@ __global__ __launch_bounds__(BT) void bwd_col_bf16_kernel(
   auto headp = [&](int pp, int hh) { return g * hpg + sp * hps + (pp ? hps - 1 - hh : hh); };
   auto head = [&](int hh) { return headp(pass, hh); };
 
-  auto load_dt_abs = [&](int h) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int t = 4 * l + e;
-      const uint32_t off = (t < Q) ? static_cast<uint32_t>(t) * H * 2 : OOB_OFFSET;
-      dtb[e] = __builtin_amdgcn_raw_buffer_load_b16(rdt, off, h * 2, 0);
-    }
-  };
+  // the dt series of head h to LDS (one copy instruction per wave; no load
+  // the compiler can see, whose wait would be vmcnt(0) and hold up the copies)
+  auto load_dt_abs = [&](int h) { steps_async<BW>(lds_ptr(sDtb), make_rsrc(dt + row0 * H + h), H * 2, Q); };
   auto load_dt = [&](int hh) { load_dt_abs(head(hh)); };
   auto load_x = [&](int hh) {
     tile_async<64, 8, BW>(sX + (hh & 1) * TILE_P, rx, j0 * HPb + head(hh) * P * 2, HPb, vj, pch);
@@ -232,7 +228,7 @@ __global__ __launch_bounds__(BT) void bwd_col_bf16_kernel(
       sched_mfmas<2 * KN>();
     }
   }
-  scan_store(dtb, -__expf(A_log[head(0)]), sS[0], sDt[0]);
+  scan_store(sDtb, -__expf(A_log[head(0)]), sS[0], sDt[0]);
   __syncthreads();
 
   f4 ws[NBMAX][2];  // sum over heads of L yx dt: rows j, columns i as in cbk
@@ -390,7 +386,7 @@ __global__ __launch_bounds__(BT) void bwd_col_bf16_kernel(
           sched_mfmas<4>();
         }
         if (u == 0 && hh + 1 < hps)
-          wait_vm<4>();  // all but the 4 dt loads
+          wait_vm<1>();  // all but the dt copy
         else
           wait_vm<0>();
         lds_barrier();
@@ -462,6 +458,7 @@ __global__ __launch_bounds__(BT) void bwd_col_bf16_kernel(
         sRed[team][jl][2] = wj[e] * part;
       }
     }
+    if (hh + 1 < hps) wait_vm<2>();  // the next head's dt copy (its x and dy copies may be in flight)
     lds_barrier();
     if (hh + 1 < hps) load_gam(hh + 1);  // this head's Gamma is no longer read
     float dxv[2][4];
@@ -505,7 +502,7 @@ __global__ __launch_bounds__(BT) void bwd_col_bf16_kernel(
         store_f32(rrp, re, vo, so);
       }
     }
-    if (hh + 1 < hps) scan_store(dtb, -__expf(An), sS[hb ^ 1], sDt[hb ^ 1]);
+    if (hh + 1 < hps) scan_store(sDtb, -__expf(An), sS[hb ^ 1], sDt[hb ^ 1]);
     lds_barrier();
   }
 
@@ -591,6 +588,7 @@ __global__ __launch_bounds__(BT) void bwd_row_bf16_kernel(
   __shared__ float sDD[BW][4];                                         // dD partials
   __shared__ __attribute__((aligned(16))) float sS[2][QMAX];
   __shared__ __attribute__((aligned(16))) float sDt[2][QMAX];
+  __shared__ __attribute__((aligned(16))) uint32_t sDtb[QMAX];  // dt bits of the next head to scan
   lds_char* const sC = lds_ptr(sC_);
   lds_char* const sDy = lds_ptr(sDy_);
   lds_char* const sX[2] = {lds_ptr(sX0_), lds_ptr(sX1_)};
@@ -612,7 +610,6 @@ __global__ __launch_bounds__(BT) void bwd_row_bf16_kernel(
   const int c = idx % nc;
   const int bi = idx / nc;
 
-  uint32_t dtb[4];  // dt bits of t = 4l .. 4l+3 for the next scan, converted when used
   for (int pass = 0; pass < 2; ++pass) {
   const int ib = pass ? kpair : nb - 1 - kpair;  // the block with the most columns j first
   if (pass && ib == nb - 1 - kpair) break;
@@ -639,7 +636,6 @@ __global__ __launch_bounds__(BT) void bwd_row_bf16_kernel(
   const i32x4 rb = make_rsrc(Bm + row0 * GN);
   const i32x4 rc = make_rsrc(Cm + row0 * GN);
   const i32x4 rh = make_rsrc(hbf + (static_cast<int64_t>(bi) * nc + c) * HP * N);
-  const __amdgpu_buffer_rsrc_t rdt = make_rsrc_ptr(dt + row0 * H);
   // outputs: the per-row sums of (bi, h = 0, c)
   const int64_t sum0 = static_cast<int64_t>(bi) * H * T + static_cast<int64_t>(c) * Q;
   const __amdgpu_buffer_rsrc_t rrow = make_rsrc_ptr(rowM + sum0);
@@ -649,14 +645,9 @@ __global__ __launch_bounds__(BT) void bwd_row_bf16_kernel(
   auto headp = [&](int pp, int hh) { return g * hpg + sp * hps + (pp ? hps - 1 - hh : hh); };
   auto head = [&](int hh) { return headp(pass, hh); };
 
-  auto load_dt_abs = [&](int h) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int t = 4 * l + e;
-      const uint32_t off = (t < Q) ? static_cast<uint32_t>(t) * H * 2 : OOB_OFFSET;
-      dtb[e] = __builtin_amdgcn_raw_buffer_load_b16(rdt, off, h * 2, 0);
-    }
-  };
+  // the dt series of head h to LDS (one copy instruction per wave; no load
+  // the compiler can see, whose wait would be vmcnt(0) and hold up the copies)
+  auto load_dt_abs = [&](int h) { steps_async<BW>(lds_ptr(sDtb), make_rsrc(dt + row0 * H + h), H * 2, Q); };
   auto load_dt = [&](int hh) { load_dt_abs(head(hh)); };
   auto load_x = [&](int hh, int jb, lds_char* dst) {
     const int j0 = jb * BQ;
@@ -723,7 +714,7 @@ __global__ __launch_bounds__(BT) void bwd_row_bf16_kernel(
       sched_mfmas<2 * KN>();
     }
   }
-  scan_store(dtb, -__expf(A_log[head(0)]), sS[0], sDt[0]);
+  scan_store(sDtb, -__expf(A_log[head(0)]), sS[0], sDt[0]);
   __syncthreads();
 
   f4 ws[NBMAX][2];  // sum over heads of L yx dt: rows i, columns j = jb * 64 + tj + 16 tt + r
@@ -830,7 +821,7 @@ __global__ __launch_bounds__(BT) void bwd_row_bf16_kernel(
           }
         }
         if (jb == 0 && hh + 1 < hps)
-          wait_vm<4>();  // all but the 4 dt loads
+          wait_vm<1>();  // all but the dt copy
         else
           wait_vm<0>();
         lds_barrier();
@@ -888,6 +879,7 @@ __global__ __launch_bounds__(BT) void bwd_row_bf16_kernel(
       const float dd = row_sum16(ddv);
       if (r == 15) sDD[w][q] = dd;
     }
+    if (hh + 1 < hps) wait_vm<2>();  // the next head's dt copy (its dy and x copies may be in flight)
     lds_barrier();
     if (hh + 1 < hps) load_h(hh + 1);  // this head's H_c is no longer read
     // the per-row sums of this wave's rows i = 16 wt + (l % 16), one row per
@@ -910,7 +902,7 @@ __global__ __launch_bounds__(BT) void bwd_row_bf16_kernel(
       store_f32(rdso, dso, vo, so);
     }
     if (threadIdx.x == 0) dD_part[((static_cast<int64_t>(bi) * nc + c) * nb + ib) * H + h] = tot;
-    if (hh + 1 < hps) scan_store(dtb, -__expf(An), sS[hb ^ 1], sDt[hb ^ 1]);
+    if (hh + 1 < hps) scan_store(sDtb, -__expf(An), sS[hb ^ 1], sDt[hb ^ 1]);
     lds_barrier();
   }
 

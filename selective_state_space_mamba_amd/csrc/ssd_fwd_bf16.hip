@@ -39,12 +39,15 @@ constexpr int FSTRIP = 32 * 32;     // bytes of a 32 x 16 bf16 strip
 // so the contractions always run over the full tiles
 constexpr int FKN = NMAX / 32;
 
-// s and dt for t < Q from the dt bits of t = 4l .. 4l+3 (see the backward kernels).
-__device__ __forceinline__ void fwd_scan_store(const uint32_t (&dtb)[4], float A, float* s_out, float* dt_out) {
+// s and dt for t < Q from the dt bits copied to LDS, one dword per step (see
+// the backward kernels).
+__device__ __forceinline__ void fwd_scan_store(const uint32_t* dtb_lds, float A, float* s_out, float* dt_out) {
   const int l = lane_id(), w = wave_id();
   float d[4], a[4];
+  const uint4 db = *reinterpret_cast<const uint4*>(dtb_lds + 4 * l);
+  const uint32_t dbv[4] = {db.x, db.y, db.z, db.w};
 #pragma unroll
-  for (int e = 0; e < 4; ++e) d[e] = bf16_bits_to_f32(static_cast<uint16_t>(dtb[e]));
+  for (int e = 0; e < 4; ++e) d[e] = bf16_bits_to_f32(static_cast<uint16_t>(dbv[e]));
   a[0] = d[0] * A;
 #pragma unroll
   for (int e = 1; e < 4; ++e) a[e] = a[e - 1] + d[e] * A;
@@ -81,6 +84,7 @@ __global__ __launch_bounds__(FT) void out_fwd_bf16_kernel(
   __shared__ __attribute__((aligned(1024))) char sBt_[NBMAX * FTILE_N];  // B tiles of blocks jb, tile jb at jb * 16 KB
   __shared__ __attribute__((aligned(16))) float sS[2][QMAX];
   __shared__ __attribute__((aligned(16))) float sDt[2][QMAX];
+  __shared__ __attribute__((aligned(16))) uint32_t sDtb[QMAX];  // dt bits of the next head to scan
   lds_char* const sC = lds_ptr(sC_);
   lds_char* const sX[2] = {lds_ptr(sX0_), lds_ptr(sX1_)};
   lds_char* const sH = lds_ptr(sH_);
@@ -103,7 +107,6 @@ __global__ __launch_bounds__(FT) void out_fwd_bf16_kernel(
   const int c = idx % nc;
   const int bi = idx / nc;
 
-  uint32_t dtb[4];  // dt bits of t = 4l .. 4l+3 for the next scan, converted when used
   for (int pass = 0; pass < 2; ++pass) {
   const int ib = pass ? kpair : nb - 1 - kpair;  // the block with the most columns j first
   if (pass && ib == nb - 1 - kpair) break;
@@ -128,19 +131,12 @@ __global__ __launch_bounds__(FT) void out_fwd_bf16_kernel(
   const i32x4 rb = make_rsrc(Bm + row0 * GN);
   const i32x4 rc = make_rsrc(Cm + row0 * GN);
   const i32x4 rh = make_rsrc(hbf + (static_cast<int64_t>(bi) * nc + c) * HP * N);
-  const __amdgpu_buffer_rsrc_t rdt = make_rsrc_ptr(dt + row0 * H);
   const __amdgpu_buffer_rsrc_t ry = make_rsrc_ptr(y + row0 * HP);
   auto head = [&](int hh) { return g * hpg + sp * hps + hh; };
 
-  auto load_dt = [&](int hh) {
-    const int h = head(hh);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int t = 4 * l + e;
-      const uint32_t off = (t < Q) ? static_cast<uint32_t>(t) * H * 2 : OOB_OFFSET;
-      dtb[e] = __builtin_amdgcn_raw_buffer_load_b16(rdt, off, h * 2, 0);
-    }
-  };
+  // the dt series of head hh to LDS (one copy instruction per wave; no load
+  // the compiler can see, whose wait would be vmcnt(0) and hold up the copies)
+  auto load_dt = [&](int hh) { steps_async<FW>(lds_ptr(sDtb), make_rsrc(dt + row0 * H + head(hh)), H * 2, Q); };
   auto load_x = [&](int hh, int jb, lds_char* dst) {
     const int j0 = jb * BQ;
     tile_async<64, 8, FW>(dst, rx, j0 * HPb + head(hh) * P * 2, HPb, min(BQ, Q - j0), pch);
@@ -201,7 +197,7 @@ __global__ __launch_bounds__(FT) void out_fwd_bf16_kernel(
       sched_mfmas<2 * FKN>();
     }
   }
-  fwd_scan_store(dtb, -__expf(A_log[head(0)]), sS[0], sDt[0]);
+  fwd_scan_store(sDtb, -__expf(A_log[head(0)]), sS[0], sDt[0]);
   __syncthreads();
 
   for (int hh = 0; hh < hps; ++hh) {
@@ -290,7 +286,7 @@ __global__ __launch_bounds__(FT) void out_fwd_bf16_kernel(
           for (int pt = 0; pt < 4; ++pt) ya[pt] = mfma(a, fx[pt], ya[pt]);
         }
         if (jb == 0 && hh + 1 < hps)
-          wait_vm<4>();  // all but the 4 dt loads
+          wait_vm<1>();  // all but the dt copy
         else
           wait_vm<0>();
         lds_barrier();
@@ -328,6 +324,7 @@ __global__ __launch_bounds__(FT) void out_fwd_bf16_kernel(
         sched_mfmas<4>();
       }
     }
+    if (hh + 1 < hps) wait_vm<1>();  // the next head's dt copy (its x copy may be in flight)
     lds_barrier();
     if (hh + 1 < hps)
       load_h(hh + 1);  // this head's H_c is no longer read
@@ -362,7 +359,7 @@ __global__ __launch_bounds__(FT) void out_fwd_bf16_kernel(
         }
       }
     }
-    if (hh + 1 < hps) fwd_scan_store(dtb, -__expf(An), sS[hb ^ 1], sDt[hb ^ 1]);
+    if (hh + 1 < hps) fwd_scan_store(sDtb, -__expf(An), sS[hb ^ 1], sDt[hb ^ 1]);
     lds_barrier();
   }
   }  // pass
