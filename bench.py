@@ -6,6 +6,12 @@ batch of synthetic input already resident in HBM; for the block-slice workload
 the step also runs conv1d+SiLU and RMSNorm-gated forward and backward.
 Prints ONE JSON line on stdout (progress goes to stderr).
 
+After the warm-up, an untimed pass of the same number of steps records HIP
+events around every kernel (per-kernel times, `kernel_ms`).  The timed region
+then records events around the dominant kernel only: its live average duration
+gives `roofline`, and the other kernels run back to back as they do without
+profiling.
+
 The default workload is the grouped bf16 configuration (b=4, T=2048, H=32,
 P=64, N=128, G=8, chunk 256), the one the performance target is quoted on.
 """
@@ -26,7 +32,7 @@ if ROOT not in sys.path:
 METRIC = "SSD fwd+bwd tokens/sec on 1 MI355X; achieved HBM GB/s and MFMA % of peak"
 HBM_PEAK_GBS = 8000.0
 KERNELS_FWD = ["chunk_state_fwd", "chunk_out_fwd"]
-KERNELS_BWD = ["chunk_state_bwd", "chunk_bwd_col", "chunk_bwd_row", "bwd_dt", "bwd_reduce"]
+KERNELS_BWD = ["chunk_state_bwd", "chunk_bwd_col", "chunk_bwd_row", "bwd_dt", "bwd_split_sum"]
 KERNELS_SHELL = ["conv1d_silu_fwd", "rmsnorm_gated_fwd", "rmsnorm_gated_bwd", "conv1d_silu_bwd"]
 KERNEL_SOURCES = {
     "chunk_state_fwd": ["ssd_state.hip", "ssd_state_bf16.hip", "ssd_async.hpp", "ssd_common.hpp"],
@@ -283,34 +289,47 @@ def main():
     torch.cuda.synchronize()
     log(f"[bench] warmup {args.warmup} done; timing {args.steps} steps")
 
+    # Per-kernel times: an untimed pass of the same steps with HIP events
+    # around every kernel (the events hold the stream up a little between
+    # kernels, so they stay out of the timed region).
+    kernels = KERNELS_FWD + KERNELS_BWD + (KERNELS_SHELL if cfg.shell else [])
     ssd.profile_enable(True)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    kms = {}
+    for k in kernels:
+        ms, n = ssd.profile_kernel_ms(k)
+        if n:
+            kms[k] = ms / n
+    core = {k: v for k, v in kms.items() if k in KERNEL_SOURCES}
+    dom = max(core, key=core.get)
+
+    # Timed region: events around the dominant kernel only, whose live
+    # average duration gives the roofline figure.
+    ssd.profile_enable(True)
+    ssd.profile_only(dom)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
         step()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    kernels = KERNELS_FWD + KERNELS_BWD + (KERNELS_SHELL if cfg.shell else [])
-    kms = {}
-    for k in kernels:
-        ms, n = ssd.profile_kernel_ms(k)
-        if n:
-            kms[k] = ms / n
+    ms_dom, n_dom = ssd.profile_kernel_ms(dom)
+    ssd.profile_only("")
     ssd.profile_enable(False)
     ms_step = elapsed * 1e3 / args.steps
     value = cfg.tokens * args.steps / elapsed
-    log(f"[bench] {ms_step:.3f} ms/step, {value:.4g} tokens/s; per-kernel ms: "
-        + " ".join(f"{k}={v:.4f}" for k, v in kms.items()))
+    log(f"[bench] {ms_step:.3f} ms/step, {value:.4g} tokens/s; {dom} {ms_dom / n_dom:.4f} ms live; "
+        "per-kernel ms (profiling pass): " + " ".join(f"{k}={v:.4f}" for k, v in kms.items()))
 
-    core = {k: v for k, v in kms.items() if k in KERNEL_SOURCES}
-    dom = max(core, key=core.get)
-    t_dom = core[dom] * 1e-3
+    t_dom = ms_dom / n_dom * 1e-3
     alg = algorithmic_bytes(cfg, dom)
     achieved = alg / t_dom / 1e9
     traffic = measured_traffic(dom, cfg.name)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": dom, "kernel_ms": round(core[dom], 4), "algorithmic_bytes": alg,
+                "kernel": dom, "kernel_ms": round(t_dom * 1e3, 4), "algorithmic_bytes": alg,
                 "mfma_tflops": round(algorithmic_flops(cfg, dom) / t_dom / 1e12, 2)}
     t_bwd = sum(v for k, v in kms.items() if k in KERNELS_BWD) * 1e-3
     bwd_alg = backward_algorithmic_bytes(cfg)

@@ -156,10 +156,14 @@ const char* ssd_version(void);
  * caller's stream.  ssd_profile_kernel_ms waits for the recorded events and
  * returns the summed milliseconds and the number of launches of one kernel:
  * "chunk_state_fwd", "chunk_out_fwd", "chunk_state_fwd (recompute)",
- * "chunk_state_bwd", "chunk_bwd_col", "chunk_bwd_row", "bwd_dt", "bwd_reduce",
+ * "chunk_state_bwd", "chunk_bwd_col", "chunk_bwd_row", "bwd_dt", "bwd_split_sum",
  * "conv1d_silu_fwd", "conv1d_silu_bwd", "rmsnorm_gated_fwd",
  * "rmsnorm_gated_bwd".  Not for use while other threads call the library. */
 int ssd_profile_enable(int on);
+/* Restrict recording to one kernel name (NULL or "" records every kernel), so
+ * that the events of the others do not hold up the stream while one kernel is
+ * timed.  Takes effect for launches made after the call. */
+int ssd_profile_only(const char* kernel);
 int ssd_profile_kernel_ms(const char* kernel, double* total_ms, int64_t* launches);
 
 #ifdef __cplusplus

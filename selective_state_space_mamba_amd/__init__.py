@@ -16,6 +16,7 @@ from ._binding import (  # noqa: F401
     load_library,
     profile_enable,
     profile_kernel_ms,
+    profile_only,
     rmsnorm_gated_bwd,
     rmsnorm_gated_fwd,
     ssd_bwd,

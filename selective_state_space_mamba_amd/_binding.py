@@ -67,6 +67,8 @@ def load_library():
     lib.ssd_version.restype = ctypes.c_char_p
     lib.ssd_profile_enable.argtypes = [ctypes.c_int]
     lib.ssd_profile_enable.restype = ctypes.c_int
+    lib.ssd_profile_only.argtypes = [ctypes.c_char_p]
+    lib.ssd_profile_only.restype = ctypes.c_int
     lib.ssd_profile_kernel_ms.argtypes = [ctypes.c_char_p, ctypes.POINTER(ctypes.c_double),
                                           ctypes.POINTER(ctypes.c_int64)]
     lib.ssd_profile_kernel_ms.restype = ctypes.c_int
@@ -81,6 +83,11 @@ def version() -> str:
 def profile_enable(on: bool = True) -> None:
     """Clear earlier per-kernel timing records and turn recording on or off."""
     _check(load_library().ssd_profile_enable(int(on)))
+
+
+def profile_only(kernel: str = "") -> None:
+    """Record only this kernel's launches from now on ("" records every kernel)."""
+    _check(load_library().ssd_profile_only(kernel.encode()))
 
 
 def profile_kernel_ms(kernel: str) -> Tuple[float, int]:

@@ -98,7 +98,7 @@ struct FwdPlan {
 };
 struct BwdPlan {
   size_t states = 0, gamma = 0, hbf = 0, gh = 0, rowM = 0, colE = 0, diagE = 0, Rp = 0, dsoff = 0, dA = 0, dD = 0,
-         dB = 0, dC = 0, total = 0;
+         done = 0, dB = 0, dC = 0, total = 0;
   int nsplit = 1;
   bool bf16 = false;  // bf16 kernels with asynchronous staging (they also need a bf16 copy of the states)
 };
@@ -149,6 +149,7 @@ BwdPlan plan_bwd(const ssd::Dims& d, bool has_states, bool bf16) {
   p.dsoff = take(bht);
   p.dA = take(sizeof(float) * static_cast<size_t>(d.b) * d.nc() * d.H);
   p.dD = take(sizeof(float) * static_cast<size_t>(d.b) * d.nc() * d.nb() * d.H);
+  p.done = take(sizeof(unsigned));
   if (p.nsplit > 1) {
     const size_t part = sizeof(float) * static_cast<size_t>(p.nsplit) * d.b * d.T * d.G * d.N;
     p.dB = take(part);
@@ -175,6 +176,7 @@ struct ProfRecord {
 };
 std::mutex g_prof_mu;
 bool g_prof_on = false;
+std::string g_prof_only;  // record this kernel only (empty: every kernel)
 std::vector<ProfRecord> g_prof_records;
 std::vector<hipEvent_t> g_prof_pool;
 
@@ -184,14 +186,17 @@ hipEvent_t prof_event() {
     g_prof_pool.pop_back();
     return e;
   }
+  // timing only: no system-scope fence (a cache write-back and invalidate at
+  // each record, which otherwise holds up the next kernel); the events are
+  // read after the caller has synchronised the stream
   hipEvent_t e = nullptr;
-  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) return nullptr;
   return e;
 }
 
-hipEvent_t prof_begin(hipStream_t st) {
+hipEvent_t prof_begin(hipStream_t st, const char* name) {
   std::lock_guard<std::mutex> lk(g_prof_mu);
-  if (!g_prof_on) return nullptr;
+  if (!g_prof_on || (!g_prof_only.empty() && g_prof_only != name)) return nullptr;
   hipEvent_t e = prof_event();
   if (e && hipEventRecord(e, st) != hipSuccess) return nullptr;
   return e;
@@ -206,7 +211,7 @@ void prof_end(hipEvent_t start, const char* name, hipStream_t st) {
 
 #define SSD_LAUNCH(expr, what)                                \
   do {                                                        \
-    hipEvent_t p_ = prof_begin(st);                           \
+    hipEvent_t p_ = prof_begin(st, what);                     \
     hipError_t e_ = (expr);                                   \
     if (e_ != hipSuccess) return hip_fail(e_, what);          \
     prof_end(p_, what, st);                                   \
@@ -228,6 +233,12 @@ int ssd_profile_enable(int on) {
   }
   g_prof_records.clear();
   g_prof_on = on != 0;
+  return ok();
+}
+
+int ssd_profile_only(const char* kernel) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_prof_only = kernel ? kernel : "";
   return ok();
 }
 
@@ -346,6 +357,7 @@ int ssd_bwd(const ssd_problem* prob, const void* x, const void* dt, const float*
   s.gh_part = at<float>(workspace, plan.gh);
   s.dA_part = at<float>(workspace, plan.dA);
   s.dD_part = at<float>(workspace, plan.dD);
+  s.done = at<unsigned>(workspace, plan.done);
   s.dB_part = plan.nsplit > 1 ? at<float>(workspace, plan.dB) : nullptr;
   s.dC_part = plan.nsplit > 1 ? at<float>(workspace, plan.dC) : nullptr;
   void* gamma = at<float>(workspace, plan.gamma);
@@ -385,8 +397,8 @@ int ssd_bwd(const ssd_problem* prob, const void* x, const void* dt, const float*
                                          plan.nsplit > 1 ? s.dC_part : dC, s, st),
                "chunk_bwd_row");
   }
-  SSD_LAUNCH(ssd::launch_bwd_dt(d, act, dt, A_log, ddt, s, st), "bwd_dt");
-  SSD_LAUNCH(ssd::launch_bwd_reduce(d, plan.nsplit, A_log, dA_log, dD, dB, dC, s, st), "bwd_reduce");
+  SSD_LAUNCH(ssd::launch_bwd_dt(d, act, dt, A_log, ddt, dA_log, dD, s, st), "bwd_dt");
+  if (plan.nsplit > 1) SSD_LAUNCH(ssd::launch_bwd_split_sum(d, plan.nsplit, dB, dC, s, st), "bwd_split_sum");
   return ok();
 }
 

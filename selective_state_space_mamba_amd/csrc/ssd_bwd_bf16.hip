@@ -206,25 +206,31 @@ __global__ __launch_bounds__(BT) void bwd_col_bf16_kernel(
   __syncthreads();
   // C.B^T stays in registers for the whole block: tiles (rows j of this wave,
   // columns i = (jb + u) * 64 + ti + 16 tt + r)
+  // This wave's B rows j, the first operand of C.B^T and of every head's
+  // B_j Gamma^T, also stay in registers.
   f4 cbk[NBMAX][2];
+  bf16x8 bfr[KN];
+  {
+    const RowsAt<16> ar16 = opaque(r16_);
+#pragma unroll
+    for (int ks = 0; ks < KN; ++ks) bfr[ks] = frag_rows(sB, 16 * wt, 4 * ks, ar16);
+  }
 #pragma unroll
   for (int u = 0; u < NBMAX; ++u) {
     zero(cbk[u]);
     if (u < nib) {
       const lds_char* ct = sCt + (jb + u) * TILE_N;
       const RowsAt<16> ar16 = opaque(r16_);
-      bf16x8 fa[KN], fb[KN][2];
-#pragma unroll
-      for (int ks = 0; ks < KN; ++ks) {
-        fa[ks] = frag_rows(sB, 16 * wt, 4 * ks, ar16);
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) fb[ks][tt] = frag_rows(ct, ti + 16 * tt, 4 * ks, ar16);
-      }
-      sched_ds_reads<3 * KN>();
+      bf16x8 fb[KN][2];
 #pragma unroll
       for (int ks = 0; ks < KN; ++ks)
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt) cbk[u][tt] = mfma(fa[ks], fb[ks][tt], cbk[u][tt]);
+        for (int tt = 0; tt < 2; ++tt) fb[ks][tt] = frag_rows(ct, ti + 16 * tt, 4 * ks, ar16);
+      sched_ds_reads<2 * KN>();
+#pragma unroll
+      for (int ks = 0; ks < KN; ++ks)
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) cbk[u][tt] = mfma(bfr[ks], fb[ks][tt], cbk[u][tt]);
       sched_mfmas<2 * KN>();
     }
   }
@@ -395,7 +401,6 @@ __global__ __launch_bounds__(BT) void bwd_col_bf16_kernel(
 
     // ---- state terms of head hh; the next head's x and dy tiles start
     // loading, its Gamma once this head's is read
-    const RowsAt<8> ar8 = opaque(r8_);
     const RowsAt<16> ar16 = opaque(r16_);
     const ColsAt<16> ac16 = opaque(c16_);
     if (hh + 1 < hps) {
@@ -406,18 +411,16 @@ __global__ __launch_bounds__(BT) void bwd_col_bf16_kernel(
     zero(bg);
 #pragma unroll
     for (int kh = 0; kh < KN; kh += 2) {  // two k-steps per batch of reads
-      bf16x8 fa[2], fb[2][2];
-#pragma unroll
-      for (int d = 0; d < 2; ++d) {
-        fa[d] = frag_rows(sB, 16 * wt, 4 * (kh + d), ar16);
-#pragma unroll
-        for (int k = 0; k < 2; ++k) fb[d][k] = frag_rows(sGam, 16 * (2 * team + k), 4 * (kh + d), ar16);
-      }
-      sched_ds_reads<6>();
+      bf16x8 fb[2][2];
 #pragma unroll
       for (int d = 0; d < 2; ++d)
 #pragma unroll
-        for (int k = 0; k < 2; ++k) bg[k] = mfma(fa[d], fb[d][k], bg[k]);
+        for (int k = 0; k < 2; ++k) fb[d][k] = frag_rows(sGam, 16 * (2 * team + k), 4 * (kh + d), ar16);
+      sched_ds_reads<4>();
+#pragma unroll
+      for (int d = 0; d < 2; ++d)
+#pragma unroll
+        for (int k = 0; k < 2; ++k) bg[k] = mfma(bfr[kh + d], fb[d][k], bg[k]);
       sched_mfmas<4>();
     }
     // x_j Gamma for this team's d_state columns (the state part of dB)
@@ -425,13 +428,12 @@ __global__ __launch_bounds__(BT) void bwd_col_bf16_kernel(
     zero(v);
 #pragma unroll
     for (int ks = 0; ks < KP; ++ks) {
-      bf16x8 fa, fb[4];
-      fa = frag_rows(xt, 16 * wt, 4 * ks, ar8);
+      bf16x8 fb[4];
 #pragma unroll
       for (int k = 0; k < 4; ++k) fb[k] = frag_cols(sGam, 32 * ks, 16 * (4 * team + k), ac16);
-      sched_ds_reads<9>();
+      sched_ds_reads<8>();
 #pragma unroll
-      for (int k = 0; k < 4; ++k) v[k] = mfma(fa, fb[k], v[k]);
+      for (int k = 0; k < 4; ++k) v[k] = mfma(xf[ks], fb[k], v[k]);
       sched_mfmas<4>();
     }
     u32x2 xa[2];  // x_j at columns p = 16 (2 team + k) + r, accumulator layout
@@ -575,8 +577,8 @@ __global__ __launch_bounds__(BT) void bwd_row_bf16_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ Bm, const uint16_t* __restrict__ Cm,
     const uint16_t* __restrict__ dt, const uint16_t* __restrict__ dy, const float* __restrict__ A_log,
     const uint16_t* __restrict__ hbf, float* __restrict__ dC_out, float* __restrict__ rowM,
-    float* __restrict__ dsoff, float* __restrict__ dD_part, int T, int H, int P, int N, int G, int Q,
-    int nsplit) {
+    float* __restrict__ dsoff, float* __restrict__ dD_part, unsigned* __restrict__ done, int T, int H, int P,
+    int N, int G, int Q, int nsplit) {
   __shared__ __attribute__((aligned(1024))) char sC_[TILE_N];          // C rows i of block ib
   __shared__ __attribute__((aligned(1024))) char sDy_[2 * TILE_P];     // dy rows i, two heads; B tile slot
   __shared__ __attribute__((aligned(1024))) char sX0_[TILE_P];         // x rows j, even steps
@@ -693,24 +695,28 @@ __global__ __launch_bounds__(BT) void bwd_row_bf16_kernel(
   // C.B^T stays in registers for the whole block: tiles (rows i of this wave,
   // columns j = jb * 64 + tj + 16 tt + r)
   f4 cbk[NBMAX][2];
+  bf16x8 cfr[KN];  // this wave's C rows i, read once for every block jb
+  {
+    const RowsAt<16> ar16 = opaque(r16_);
+#pragma unroll
+    for (int ks = 0; ks < KN; ++ks) cfr[ks] = frag_rows(sC, 16 * wt, 4 * ks, ar16);
+  }
 #pragma unroll
   for (int jb = 0; jb < NBMAX; ++jb) {
     zero(cbk[jb]);
     if (jb < nj) {
       const lds_char* bt = sBt + jb * TILE_N;
       const RowsAt<16> ar16 = opaque(r16_);
-      bf16x8 fa[KN], fb[KN][2];
-#pragma unroll
-      for (int ks = 0; ks < KN; ++ks) {
-        fa[ks] = frag_rows(sC, 16 * wt, 4 * ks, ar16);
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) fb[ks][tt] = frag_rows(bt, tj + 16 * tt, 4 * ks, ar16);
-      }
-      sched_ds_reads<3 * KN>();
+      bf16x8 fb[KN][2];
 #pragma unroll
       for (int ks = 0; ks < KN; ++ks)
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt) cbk[jb][tt] = mfma(fa[ks], fb[ks][tt], cbk[jb][tt]);
+        for (int tt = 0; tt < 2; ++tt) fb[ks][tt] = frag_rows(bt, tj + 16 * tt, 4 * ks, ar16);
+      sched_ds_reads<2 * KN>();
+#pragma unroll
+      for (int ks = 0; ks < KN; ++ks)
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) cbk[jb][tt] = mfma(cfr[ks], fb[ks][tt], cbk[jb][tt]);
       sched_mfmas<2 * KN>();
     }
   }
@@ -955,6 +961,8 @@ __global__ __launch_bounds__(BT) void bwd_row_bf16_kernel(
     }
   }
   }  // pass
+  // the dt kernel that follows counts its finished workgroups from 0
+  if (blockIdx.x == 0 && threadIdx.x == 0) __hip_atomic_store(done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 bool bwd_bf16_supported(const Dims& d) {
@@ -971,7 +979,7 @@ hipError_t launch_bwd_row_bf16(const Dims& d, int nsplit, const void* x, const v
   hipLaunchKernelGGL(bwd_row_bf16_kernel, dim3(nblk), dim3(BT), 0, st, static_cast<const uint16_t*>(x),
                      static_cast<const uint16_t*>(B), static_cast<const uint16_t*>(C),
                      static_cast<const uint16_t*>(dt), static_cast<const uint16_t*>(dy), A_log,
-                     static_cast<const uint16_t*>(hbf), dC_out, s.rowM, s.dsoff, s.dD_part, d.T, d.H, d.P, d.N,
+                     static_cast<const uint16_t*>(hbf), dC_out, s.rowM, s.dsoff, s.dD_part, s.done, d.T, d.H, d.P, d.N,
                      d.G, d.Q, nsplit);
   return hipGetLastError();
 }

@@ -32,6 +32,7 @@
 // (no atomics), so results are bitwise reproducible.
 #include <type_traits>
 
+#include "ssd_async.hpp"
 #include "ssd_common.hpp"
 #include "ssd_launch.hpp"
 
@@ -406,9 +407,12 @@ __global__ __launch_bounds__(NT8) void chunk_bwd_row_kernel(
     const TI* __restrict__ x, const TI* __restrict__ Bm, const TI* __restrict__ Cm,
     const TI* __restrict__ dt, const TY* __restrict__ dy, const float* __restrict__ A_log,
     const float* __restrict__ hstates, float* __restrict__ dC_out, float* __restrict__ rowM,
-    float* __restrict__ dsoff, float* __restrict__ dD_part, int T, int H, int P, int N, int G, int Q,
-    int nsplit) {
+    float* __restrict__ dsoff, float* __restrict__ dD_part, unsigned* __restrict__ done, int T, int H, int P,
+    int N, int G, int Q, int nsplit) {
   typedef typename Op<BF>::T OT;
+  // the dt kernel that follows counts its finished workgroups from 0
+  if (blockIdx.x == 0 && threadIdx.x == 0) __hip_atomic_store(done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
   constexpr int PAD = BF ? 8 : 4;
   constexpr int JW = BwdSlab<BF>::W;
   constexpr int LDN = NMAX + PAD, LDP = PMAX + PAD, LDJ = JW + PAD;
@@ -685,64 +689,132 @@ __global__ __launch_bounds__(NT8) void chunk_bwd_row_kernel(
 }
 
 // ------------------------------------------------------------- dt finalize
+//
+// ddt, and the dA_log and dD sums.  A workgroup takes one chunk of one batch
+// row and up to DT_HEADS heads, one wave per head (lane l holds the chunk's
+// rows l + 64 e, so a chunk's scan and sums need no barrier).  dt and ddt
+// ([b, T, H]) pass through LDS, so that their global accesses run along the
+// heads.  Each wave leaves its head's dA partial for the chunk; the workgroup
+// that finishes last (by a device-scope counter, which the row kernel of the
+// same call zeroes) sums every head's partials in a fixed order, so the sums do
+// not depend on which workgroup that is.  The partials are stored and read
+// with device-coherent (agent-scope) atomic stores and loads, and every wave
+// has waited for its stores to complete before the workgroup counts itself:
+// no write-back of the whole L2 is needed.
+constexpr int DT_HEADS = 16;
+
+// Lane 63's value, in every lane.
+__device__ __forceinline__ float lane63(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), WAVE - 1));
+}
+// Sum over the 64 lanes of a wave, in every lane (DPP scan, then lane 63).
+__device__ __forceinline__ float wave_total(float v) { return lane63(wave_scan(v)); }
 
 template <typename TI>
-__global__ __launch_bounds__(NTHREADS) void bwd_dt_kernel(const TI* __restrict__ dt, const float* __restrict__ A_log,
-                                                          float* __restrict__ ddt, BwdScratch s, int T, int H, int Q,
-                                                          int npb) {
-  __shared__ float sTmp[8];
-  __shared__ float sLast;
-  const int c = blockIdx.x, h = blockIdx.y, bi = blockIdx.z;
-  const int nc = gridDim.x;
-  const int k = threadIdx.x;
-  const bool valid = k < Q;
-  const int64_t t0 = static_cast<int64_t>(c) * Q;
-  const float A = -__expf(A_log[h]);
-  const float dtv = valid ? load_f(dt, (static_cast<int64_t>(bi) * T + t0 + k) * H + h) : 0.f;
-  const float sv = block_inclusive_scan(dtv * A, sTmp);
-  if (k == Q - 1) sLast = sv;
-  const int64_t o = (static_cast<int64_t>(bi) * H + h) * T + t0 + k;
-  float colE = 0.f, Rp = 0.f, ds = 0.f;
-  if (valid) {
-    colE = s.colE[o];
-    Rp = s.Rp[o];
-    ds = s.rowM[o] - dtv * (colE - s.diagE[o]) + s.dsoff[o] - dtv * Rp;
+__global__ __launch_bounds__(DT_HEADS* WAVE) void bwd_dt_kernel(const TI* __restrict__ dt,
+                                                               const float* __restrict__ A_log,
+                                                               float* __restrict__ ddt, float* __restrict__ dA_log,
+                                                               float* __restrict__ dD, BwdScratch s, int T, int H,
+                                                               int Q, int npb, int nc, int nb) {
+  __shared__ float sT[QMAX][DT_HEADS + 1];  // dt in, then ddt out: [row][head]
+  __shared__ int sFinal;
+  const int u = blockIdx.x;  // chunk index bi * nc + c
+  const int hg0 = blockIdx.y * DT_HEADS;
+  const int nh = min(DT_HEADS, H - hg0);
+  const int bi = u / nc, c = u - bi * nc;
+  const int64_t r0 = static_cast<int64_t>(bi) * T + static_cast<int64_t>(c) * Q;  // the chunk's first row
+  const int tid = threadIdx.x, l = lane_id(), w = wave_id();
+  // this wave's head: the per-row sums are loaded first, so that their
+  // latency overlaps the dt staging
+  const int h = hg0 + min(w, nh - 1);
+  const int64_t o0 = (static_cast<int64_t>(bi) * H + h) * T + static_cast<int64_t>(c) * Q;
+  float cE[4], rP[4], rM[4], dE[4], dS[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int k = 64 * e + l;
+    cE[e] = rP[e] = rM[e] = dE[e] = dS[e] = 0.f;
+    if (k < Q && w < nh) {
+      cE[e] = s.colE[o0 + k];
+      rP[e] = s.Rp[o0 + k];
+      rM[e] = s.rowM[o0 + k];
+      dE[e] = s.diagE[o0 + k];
+      dS[e] = s.dsoff[o0 + k];
+    }
   }
-  const float totR = block_sum(dtv * Rp, sTmp);  // syncs make sLast visible
-  if (k == Q - 1) {
-    float gh = 0.f;
-    const float* ghp = s.gh_part + ((static_cast<int64_t>(bi) * nc + c) * H + h) * npb;
-    for (int pb = 0; pb < npb; ++pb) gh += ghp[pb];
-    ds += totR + __expf(sLast) * gh;
+  const float ghl = (l < npb && w < nh) ? s.gh_part[(static_cast<int64_t>(u) * H + h) * npb + l] : 0.f;
+  for (int i = tid; i < Q * DT_HEADS; i += DT_HEADS * WAVE) {
+    const int k = i / DT_HEADS, j = i % DT_HEADS;
+    sT[k][j] = j < nh ? load_f(dt, (r0 + k) * H + hg0 + j) : 0.f;
   }
-  const float incl = block_inclusive_scan(ds, sTmp);
   __syncthreads();
-  if (k == Q - 1) sLast = incl;
-  __syncthreads();
-  const float da = sLast - incl + ds;  // sum_{k' >= k} ds_k'
-  if (valid) ddt[(static_cast<int64_t>(bi) * T + t0 + k) * H + h] = colE + Rp + A * da;
-  const float dA = block_sum(dtv * da, sTmp);
-  if (k == 0) s.dA_part[(static_cast<int64_t>(bi) * nc + c) * H + h] = dA;
-}
-
-// ----------------------------------------------------------- final sums
-
-__global__ __launch_bounds__(NTHREADS) void bwd_param_reduce_kernel(const float* __restrict__ A_log,
-                                                                    float* __restrict__ dA_log,
-                                                                    float* __restrict__ dD, BwdScratch s, int nbc,
-                                                                    int nb, int H) {
-  __shared__ float sTmp[8];
-  const int h = blockIdx.x;
-  float a = 0.f, dd = 0.f;
-  for (int u = threadIdx.x; u < nbc; u += NTHREADS) {
-    a += s.dA_part[static_cast<int64_t>(u) * H + h];
-    for (int ib = 0; ib < nb; ++ib) dd += s.dD_part[(static_cast<int64_t>(u) * nb + ib) * H + h];
+  if (w < nh) {
+    const float A = -__expf(A_log[h]);
+    float dv[4], ds[4];
+    float sl = 0.f, tr = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int k = 64 * e + l;
+      dv[e] = k < Q ? sT[k][w] : 0.f;
+      ds[e] = rM[e] - dv[e] * (cE[e] - dE[e]) + dS[e] - dv[e] * rP[e];
+      sl += dv[e] * A;
+      tr += dv[e] * rP[e];
+    }
+    sl = wave_total(sl);  // s at the chunk's last row
+    tr = wave_total(tr);
+    const float gh = wave_total(ghl);
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (64 * e + l == Q - 1) ds[e] += tr + __expf(sl) * gh;
+    // da_k = sum of ds over rows k' >= k: the chunk total less the inclusive
+    // prefix, plus ds_k
+    float incl[4], carry = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float sc = wave_scan(ds[e]);
+      incl[e] = carry + sc;
+      carry += lane63(sc);
+    }
+    float pa = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int k = 64 * e + l;
+      const float da = carry - incl[e] + ds[e];
+      if (k < Q) sT[k][w] = cE[e] + rP[e] + A * da;
+      pa += dv[e] * da;
+    }
+    pa = wave_total(pa);
+    if (l == 0)
+      __hip_atomic_store(s.dA_part + static_cast<int64_t>(u) * H + h, pa, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
   }
-  a = block_sum(a, sTmp);
-  dd = block_sum(dd, sTmp);
-  if (threadIdx.x == 0) {
-    dA_log[h] = -__expf(A_log[h]) * a;
-    dD[h] = dd;
+  __syncthreads();
+  for (int i = tid; i < Q * DT_HEADS; i += DT_HEADS * WAVE) {
+    const int k = i / DT_HEADS, j = i % DT_HEADS;
+    if (j < nh) ddt[(r0 + k) * H + hg0 + j] = sT[k][j];
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's stores, the dA partial among them, are complete
+  __syncthreads();
+  if (tid == 0) {
+    const unsigned prev = __hip_atomic_fetch_add(s.done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    sFinal = prev + 1 == gridDim.x * gridDim.y;
+  }
+  __syncthreads();
+  if (!sFinal) return;
+  // the last workgroup: wave w sums heads w, w + DT_HEADS, ... over all chunks
+  const int nbc = gridDim.x;
+  for (int h = w; h < H; h += DT_HEADS) {
+    float a = 0.f, dd = 0.f;
+    for (int v = l; v < nbc; v += WAVE) {
+      a += __hip_atomic_load(s.dA_part + static_cast<int64_t>(v) * H + h, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+      for (int ib = 0; ib < nb; ++ib) dd += s.dD_part[(static_cast<int64_t>(v) * nb + ib) * H + h];
+    }
+    a = wave_total(a);
+    dd = wave_total(dd);
+    if (l == 0) {
+      dA_log[h] = -__expf(A_log[h]) * a;
+      dD[h] = dd;
+    }
   }
 }
 
@@ -806,7 +878,7 @@ static void row_launch(const Dims& d, int nsplit, const void* x, const void* B, 
   hipLaunchKernelGGL((chunk_bwd_row_kernel<TI, TY, BF>), dim3(nblocks_chunk(d, nsplit)), dim3(NT8), 0, st,
                      static_cast<const TI*>(x), static_cast<const TI*>(B), static_cast<const TI*>(C),
                      static_cast<const TI*>(dt), static_cast<const TY*>(dy), A_log, states, dC_out, s.rowM, s.dsoff,
-                     s.dD_part, d.T, d.H, d.P, d.N, d.G, d.Q, nsplit);
+                     s.dD_part, s.done, d.T, d.H, d.P, d.N, d.G, d.Q, nsplit);
 }
 
 hipError_t launch_chunk_bwd_row(const Dims& d, DType act, DType dyt, int nsplit, const void* x,
@@ -827,24 +899,22 @@ hipError_t launch_chunk_bwd_row(const Dims& d, DType act, DType dyt, int nsplit,
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_dt(const Dims& d, DType act, const void* dt, const float* A_log, float* ddt,
-                         const BwdScratch& s, hipStream_t st) {
-  dim3 grid(d.nc(), d.H, d.b);
+hipError_t launch_bwd_dt(const Dims& d, DType act, const void* dt, const float* A_log, float* ddt, float* dA_log,
+                         float* dD, const BwdScratch& s, hipStream_t st) {
+  const dim3 grid(d.b * d.nc(), (d.H + DT_HEADS - 1) / DT_HEADS);
   if (act == BF16)
-    hipLaunchKernelGGL((bwd_dt_kernel<uint16_t>), grid, dim3(NTHREADS), 0, st, static_cast<const uint16_t*>(dt),
-                       A_log, ddt, s, d.T, d.H, d.Q, state_npb(d));
+    hipLaunchKernelGGL((bwd_dt_kernel<uint16_t>), grid, dim3(DT_HEADS * WAVE), 0, st,
+                       static_cast<const uint16_t*>(dt), A_log, ddt, dA_log, dD, s, d.T, d.H, d.Q, state_npb(d),
+                       d.nc(), d.nb());
   else
-    hipLaunchKernelGGL((bwd_dt_kernel<float>), grid, dim3(NTHREADS), 0, st, static_cast<const float*>(dt), A_log,
-                       ddt, s, d.T, d.H, d.Q, state_npb(d));
+    hipLaunchKernelGGL((bwd_dt_kernel<float>), grid, dim3(DT_HEADS * WAVE), 0, st, static_cast<const float*>(dt),
+                       A_log, ddt, dA_log, dD, s, d.T, d.H, d.Q, state_npb(d), d.nc(), d.nb());
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_reduce(const Dims& d, int nsplit, const float* A_log, float* dA_log,
-                             float* dD, float* dB, float* dC, const BwdScratch& s, hipStream_t st) {
-  hipLaunchKernelGGL(bwd_param_reduce_kernel, dim3(d.H), dim3(NTHREADS), 0, st, A_log, dA_log, dD, s,
-                     d.b * d.nc(), d.nb(), d.H);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || nsplit == 1) return e;
+hipError_t launch_bwd_split_sum(const Dims& d, int nsplit, float* dB, float* dC, const BwdScratch& s,
+                                hipStream_t st) {
+  if (nsplit == 1) return hipSuccess;
   const int64_t n = static_cast<int64_t>(d.b) * d.T * d.G * d.N;
   const int64_t blocks = (n + 255) / 256;
   hipLaunchKernelGGL(split_sum_kernel, dim3(blocks), dim3(256), 0, st, s.dB_part, dB, n, nsplit);

@@ -62,6 +62,7 @@ struct BwdScratch {
   float* gh_part;  // [b,nc,H,npb]
   float* dA_part;  // [b,nc,H]
   float* dD_part;  // [b,nc,nb,H]
+  unsigned* done;  // one counter: the dt kernel's finished workgroups (zeroed by the row kernel)
   float* dB_part;  // [nsplit,b,T,G,N] or null when nsplit == 1
   float* dC_part;
 };
@@ -87,11 +88,15 @@ hipError_t launch_bwd_col_bf16(const Dims& d, int nsplit, const void* x, const v
                                const void* gamma, float* dx, float* dB_out, const BwdScratch& s,
                                hipStream_t st);
 
-hipError_t launch_bwd_dt(const Dims& d, DType act, const void* dt, const float* A_log, float* ddt,
-                         const BwdScratch& s, hipStream_t st);
+// dt gradient per token, and dA_log and dD (fixed-order sums of the per-chunk
+// partials, taken by the launch's last workgroup).  Needs s.done zeroed by an
+// earlier launch on the stream (the row kernel does it).
+hipError_t launch_bwd_dt(const Dims& d, DType act, const void* dt, const float* A_log, float* ddt, float* dA_log,
+                         float* dD, const BwdScratch& s, hipStream_t st);
 
-hipError_t launch_bwd_reduce(const Dims& d, int nsplit, const float* A_log, float* dA_log,
-                             float* dD, float* dB, float* dC, const BwdScratch& s, hipStream_t st);
+// dB and dC as sums of the head-split partials (nothing to do when nsplit == 1).
+hipError_t launch_bwd_split_sum(const Dims& d, int nsplit, float* dB, float* dC, const BwdScratch& s,
+                                hipStream_t st);
 
 // Writes `value` into n floats (used for empty problems).
 hipError_t launch_fill(float* p, int64_t n, float value, hipStream_t st);

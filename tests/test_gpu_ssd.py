@@ -61,6 +61,14 @@ def test_chunk_lengths(chunk):
     compare(gpu_ssd(cfg, d), oracle_ssd(d, chunk), TOL["f32"], label=f"chunk={chunk}")
 
 
+def test_many_chunks_bf16():
+    # 256 chunks per head (over 128): the dt gradient and the dA_log / dD sums
+    # take their two-launch form (the workloads above take the one-launch form)
+    cfg = SSDConfig("many", 2, 2048, 4, 64, 32, 2, 16, "bf16", init_state=True, seed=12)
+    d = make_inputs(cfg)
+    compare(gpu_ssd(cfg, d), oracle_ssd(d, cfg.chunk), TOL["bf16"], label="256 chunks per head, bf16")
+
+
 def test_single_chunk_whole_sequence():
     cfg = SSDConfig("one", 3, 256, 8, 64, 128, 8, 256, "bf16", init_state=True, seed=6)
     d = make_inputs(cfg)
