@@ -723,6 +723,12 @@ __global__ __launch_bounds__(BT) void bwd_row_bf16_kernel(
   scan_store(sDtb, -__expf(A_log[head(0)]), sS[0], sDt[0]);
   __syncthreads();
 
+  u32x2 ca[4];  // C_i at columns n = 16 (4 team + k) + r, accumulator layout, for every head
+  {
+    const AccAt<16> aa16 = opaque(a16_);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) ca[k] = block_acc(sC, 16 * wt, 16 * (4 * team + k), aa16);
+  }
   f4 ws[NBMAX][2];  // sum over heads of L yx dt: rows i, columns j = jb * 64 + tj + 16 tt + r
   f4 ua[4];         // sum over heads of exp(s_i) U_i: rows i, columns n = 16 (4 team + k) + r
 #pragma unroll
@@ -855,12 +861,6 @@ __global__ __launch_bounds__(BT) void bwd_row_bf16_kernel(
         for (int k = 0; k < 4; ++k) u[k] = mfma(dyf[ks], fb[k], u[k]);
         sched_mfmas<4>();
       }
-    }
-    u32x2 ca[4];  // C_i at columns n = 16 (4 team + k) + r, accumulator layout
-    {
-      const AccAt<16> aa16 = opaque(a16_);
-#pragma unroll
-      for (int k = 0; k < 4; ++k) ca[k] = block_acc(sC, 16 * wt, 16 * (4 * team + k), aa16);
     }
     float ex[4];
 #pragma unroll

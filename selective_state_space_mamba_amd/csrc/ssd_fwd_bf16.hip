@@ -175,25 +175,31 @@ __global__ __launch_bounds__(FT) void out_fwd_bf16_kernel(
   }
   wait_vm<0>();
   __syncthreads();
+  // This wave's C rows i, the first operand of C.B^T and of every head's
+  // C_i . H_c^T, also stay in registers.
   f4 cbk[NBMAX][2];  // rows i of this wave, columns j = jb * 64 + tj + 16 tt + r
+  bf16x8 cfr[FKN];
+  {
+    const RowsAt<16> ar16 = opaque(r16_);
+#pragma unroll
+    for (int ks = 0; ks < FKN; ++ks) cfr[ks] = frag_rows(sC, 16 * wt, 4 * ks, ar16);
+  }
 #pragma unroll
   for (int jb = 0; jb < NBMAX; ++jb) {
     zero(cbk[jb]);
     if (jb < nj) {
       const lds_char* bt = sBt + jb * FTILE_N;
       const RowsAt<16> ar16 = opaque(r16_);
-      bf16x8 fa[FKN], fb[FKN][2];
-#pragma unroll
-      for (int ks = 0; ks < FKN; ++ks) {
-        fa[ks] = frag_rows(sC, 16 * wt, 4 * ks, ar16);
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) fb[ks][tt] = frag_rows(bt, tj + 16 * tt, 4 * ks, ar16);
-      }
-      sched_ds_reads<3 * FKN>();
+      bf16x8 fb[FKN][2];
 #pragma unroll
       for (int ks = 0; ks < FKN; ++ks)
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt) cbk[jb][tt] = mfma(fa[ks], fb[ks][tt], cbk[jb][tt]);
+        for (int tt = 0; tt < 2; ++tt) fb[ks][tt] = frag_rows(bt, tj + 16 * tt, 4 * ks, ar16);
+      sched_ds_reads<2 * FKN>();
+#pragma unroll
+      for (int ks = 0; ks < FKN; ++ks)
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) cbk[jb][tt] = mfma(cfr[ks], fb[ks][tt], cbk[jb][tt]);
       sched_mfmas<2 * FKN>();
     }
   }
@@ -309,18 +315,16 @@ __global__ __launch_bounds__(FT) void out_fwd_bf16_kernel(
       const RowsAt<16> ar16 = opaque(r16_);
 #pragma unroll
       for (int kh = 0; kh < FKN; kh += 2) {  // two k-steps per batch of reads
-        bf16x8 fa[2], fb[2][2];
-#pragma unroll
-        for (int d = 0; d < 2; ++d) {
-          fa[d] = frag_rows(sC, 16 * wt, 4 * (kh + d), ar16);
-#pragma unroll
-          for (int k = 0; k < 2; ++k) fb[d][k] = frag_rows(sH, 16 * (2 * team + k), 4 * (kh + d), ar16);
-        }
-        sched_ds_reads<6>();
+        bf16x8 fb[2][2];
 #pragma unroll
         for (int d = 0; d < 2; ++d)
 #pragma unroll
-          for (int k = 0; k < 2; ++k) yo[k] = mfma(fa[d], fb[d][k], yo[k]);
+          for (int k = 0; k < 2; ++k) fb[d][k] = frag_rows(sH, 16 * (2 * team + k), 4 * (kh + d), ar16);
+        sched_ds_reads<4>();
+#pragma unroll
+        for (int d = 0; d < 2; ++d)
+#pragma unroll
+          for (int k = 0; k < 2; ++k) yo[k] = mfma(cfr[kh + d], fb[d][k], yo[k]);
         sched_mfmas<4>();
       }
     }
