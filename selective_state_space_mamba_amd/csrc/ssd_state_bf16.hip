@@ -13,13 +13,13 @@
 // p0 + 16 (w % 2) .. +15 and d_state columns 32 (w / 2) .. +31 of the state
 // in registers and walks the chunks in order (or in reverse).  Per chunk the
 // weighted sum is one MFMA contraction over time: the x (or dy) tile arrives
-// with time along its rows and is read down them with the LDS transpose read,
-// each fragment scaled by the per-step weights before the MFMA; the B (or C)
-// tile likewise.  Tiles come in 128-step slabs, double-buffered and copied
-// asynchronously while the previous slab computes, together with (backward)
-// the f32 state tile H_c; the chunk's dt values are prefetched into registers.
-// Every wave computes the within-chunk scan itself (DPP) into its own weight
-// row.
+// with time along its rows, is scaled in place by the per-step weights (one
+// 16-byte chunk per thread, once for the four waves that read each row) and
+// is read down its rows with the LDS transpose read; the B (or C) tile
+// likewise, unscaled.  Tiles come in 128-step slabs, double-buffered and
+// copied asynchronously while the previous slab computes, together with the
+// chunk's dt series and (backward) the f32 state tile H_c.  Every wave
+// computes the within-chunk scan itself (DPP) into its own weight row.
 #include "ssd_async.hpp"
 #include "ssd_common.hpp"
 #include "ssd_launch.hpp"
@@ -34,16 +34,6 @@ constexpr int SPB = 32;            // headdim rows per workgroup
 constexpr int XSLAB = SSJ * 64;    // bytes of a 128 x 32 bf16 slab
 constexpr int BSLAB = SSJ * 256;   // bytes of a 128 x 128 bf16 slab
 constexpr int HTILE = SPB * 512;   // bytes of a 32 x 128 f32 state tile
-
-__device__ __forceinline__ bf16x8 scale_frag(bf16x8 a, const float* w) {
-  const float4 w0 = *reinterpret_cast<const float4*>(w);
-  const float4 w1 = *reinterpret_cast<const float4*>(w + 4);
-  const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-  bf16x8 o;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) o[e] = static_cast<__bf16>(static_cast<float>(a[e]) * wv[e]);
-  return o;
-}
 
 // Sum over all 64 lanes of the wave (the row sums end in lanes 15, 31, 47, 63).
 __device__ __forceinline__ float wave_total(float v) {
@@ -158,46 +148,52 @@ __global__ __launch_bounds__(ST) void chunk_state_bf16_kernel(
         }
         *reinterpret_cast<float4*>(wts + 4 * l) = make_float4(wv[0], wv[1], wv[2], wv[3]);
       }
+      const int buf = (it * nsl + sl) & 1;
+      // the slab's x rows times their step weights, in place: one 16-byte
+      // chunk per thread (the swizzle keeps chunks inside their row), so that
+      // the four waves sharing a row do not each scale it
+      {
+        static_assert(XSLAB == ST * 16, "one chunk of the x slab per thread");
+        uint4* const cp = reinterpret_cast<uint4*>(sX_ + buf * XSLAB) + threadIdx.x;
+        const float wt = wts[sl * SSJ + (threadIdx.x >> 2)];
+        const uint4 v = *cp;
+        const uint32_t vv[4] = {v.x, v.y, v.z, v.w};
+        uint32_t o[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          o[k] = pack_bf16(__uint_as_float(vv[k] << 16) * wt, __uint_as_float(vv[k] & 0xFFFF0000u) * wt);
+        *cp = make_uint4(o[0], o[1], o[2], o[3]);
+      }
       // the next slab (or the next chunk's first, with its dt) starts loading
       if (sl + 1 < nsl)
         load_slab(it, sl + 1);
       else if (it + 1 < nc)
         load_slab(it + 1, 0);
-      const int buf = (it * nsl + sl) & 1;
+      lds_barrier();  // the scaled slab is visible
       const lds_char* xs = sX + buf * XSLAB;
       const lds_char* bs = sB + buf * BSLAB;
       const int kw = min(SSJ, Q - sl * SSJ);
       if (kw == SSJ) {
-        // a full slab: every fragment and weight read first, then the scaling
-        // and the MFMAs, so that the reads' latencies overlap
+        // a full slab: every fragment read first, then the MFMAs, so that the
+        // reads' latencies overlap
         constexpr int KS = SSJ / 32;
         const ColsAt<4> ac4 = opaque(c4_);
         const ColsAt<16> ac16 = opaque(c16_);
         bf16x8 xa[KS], bb[KS][2];
-        float4 wa[KS][2];
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
           xa[ks] = frag_cols(xs, 32 * ks, 16 * pw, ac4);
-          const float* wp = wts + sl * SSJ + 32 * ks + 8 * q;
-          wa[ks][0] = *reinterpret_cast<const float4*>(wp);
-          wa[ks][1] = *reinterpret_cast<const float4*>(wp + 4);
 #pragma unroll
           for (int t = 0; t < 2; ++t) bb[ks][t] = frag_cols(bs, 32 * ks, 32 * nw + 16 * t, ac16);
         }
-        sched_ds_reads<KS * 8>();
+        sched_ds_reads<KS * 6>();
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const float wv[8] = {wa[ks][0].x, wa[ks][0].y, wa[ks][0].z, wa[ks][0].w,
-                               wa[ks][1].x, wa[ks][1].y, wa[ks][1].z, wa[ks][1].w};
-          bf16x8 ax;
+        for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-          for (int e = 0; e < 8; ++e) ax[e] = static_cast<__bf16>(static_cast<float>(xa[ks][e]) * wv[e]);
-#pragma unroll
-          for (int t = 0; t < 2; ++t) acc[t] = mfma(ax, bb[ks][t], acc[t]);
-        }
+          for (int t = 0; t < 2; ++t) acc[t] = mfma(xa[ks], bb[ks][t], acc[t]);
       } else {
         for (int k0 = 0; k0 < kw; k0 += 32) {
-          const bf16x8 ax = scale_frag(frag_cols<4>(xs, k0, 16 * pw), wts + sl * SSJ + k0 + 8 * q);
+          const bf16x8 ax = frag_cols<4>(xs, k0, 16 * pw);
 #pragma unroll
           for (int t = 0; t < 2; ++t) acc[t] = mfma(ax, frag_cols<16>(bs, k0, 32 * nw + 16 * t), acc[t]);
         }
