@@ -270,6 +270,13 @@ __device__ __forceinline__ AccAt<CPR> opaque(AccAt<CPR> a) {
   asm volatile("" : "+v"(a.b));
   return a;
 }
+// A per-lane index the compiler must take as computed here: comparisons
+// derived from it stay in the branch that uses them instead of being hoisted
+// out of the loops as lane masks (which then spill to VGPR lanes).
+__device__ __forceinline__ int opaque_index(int v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
 template <int CPR>
 __device__ __forceinline__ u32x2 block_acc(const lds_char* t, int m0, int n0, AccAt<CPR> a) {
   const short4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(

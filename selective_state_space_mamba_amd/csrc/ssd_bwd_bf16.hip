@@ -321,13 +321,14 @@ __global__ __launch_bounds__(BT) void bwd_col_bf16_kernel(
         }
         f4 gv[2];
         if (u == 0) {
+          const int jq0 = opaque_index(j0 + 16 * wt + 4 * q);
 #pragma unroll
           for (int tt = 0; tt < 2; ++tt) {
             const int iq = i0 + ti + 16 * tt + r;
             const float si = sv[tt];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              const int jq = j0 + 16 * wt + 4 * q + e;
+              const int jq = jq0 + e;
               const float ex = __expf(si - sj[e]);
               const float L = (iq < Q && iq >= jq) ? ex : 0.f;
               const float G1 = L * cbt[tt][e];
@@ -804,6 +805,7 @@ __global__ __launch_bounds__(BT) void bwd_row_bf16_kernel(
           sched_mfmas<2 * KP>();
         }
         if (jb == ib) {
+          const int iq0 = opaque_index(i0 + 16 * wt + 4 * q);
 #pragma unroll
           for (int tt = 0; tt < 2; ++tt) {
             const int jq = j0 + tj + 16 * tt + r;
@@ -811,7 +813,7 @@ __global__ __launch_bounds__(BT) void bwd_row_bf16_kernel(
             const float dtj = (jq < Q) ? dtv[tt] : 0.f;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              const int iq = i0 + 16 * wt + 4 * q + e;
+              const int iq = iq0 + e;
               const float ex = __expf(si[e] - sj);
               const float L = (iq < Q && jq <= iq) ? ex : 0.f;
               const float ly = L * yx[tt][e] * dtj;

@@ -261,6 +261,7 @@ __global__ __launch_bounds__(FT) void out_fwd_bf16_kernel(
         sched_ds_reads<12>();
         f4 gv[2];
         if (jb == ib) {
+          const int iq0 = opaque_index(i0 + 16 * wt + 4 * q);
 #pragma unroll
           for (int tt = 0; tt < 2; ++tt) {
             const int jq = j0 + tj + 16 * tt + r;
@@ -268,7 +269,7 @@ __global__ __launch_bounds__(FT) void out_fwd_bf16_kernel(
             const float dtj = (jq < Q) ? dtv[tt] : 0.f;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              const int iq = i0 + 16 * wt + 4 * q + e;
+              const int iq = iq0 + e;
               const float ex = __expf(si[e] - sj);
               const float L = (iq < Q && jq <= iq) ? ex : 0.f;
               gv[tt][e] = L * dtj * cbt[tt][e];
