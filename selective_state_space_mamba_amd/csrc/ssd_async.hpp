@@ -56,6 +56,17 @@ __device__ __forceinline__ void dma16(const i32x4& rs, lds_char* dst, uint32_t v
 #endif
 }
 
+// The same with a uniform byte offset added in the instruction's scalar
+// offset (voff alone decides whether a lane is out of range).
+__device__ __forceinline__ void dma16_so(const i32x4& rs, lds_char* dst, uint32_t voff, uint32_t soff) {
+#if defined(__HIP_DEVICE_COMPILE__)  // gfx950 assembly: device pass only
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(dst)));
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds" ::"s"(m0v), "v"(voff), "s"(rs),
+               "s"(soff)
+               : "memory", "m0");
+#endif
+}
+
 // One wave's copy of 64 16-bit elements into LDS: a sub-dword LDS-direct load
 // writes one dword per lane, at dst + 4 * lane, holding the element
 // zero-extended (measured on gfx950).  voff at or beyond OOB_OFFSET gives 0.
@@ -158,6 +169,38 @@ __device__ __forceinline__ void tile_async(lds_char* dst, const i32x4& rs, uint3
     }
   }
 }
+
+// tile_async's per-lane addressing computed once, for a tile that is copied
+// many times from sources that differ by a uniform byte offset: each copy then
+// costs one compare and one select per instruction.
+template <int ROWS, int CPR, int NW>
+struct TileLanes {
+  static constexpr int LPI = 64 / CPR, NI = ROWS / LPI, PER = (NI + NW - 1) / NW;
+  static_assert(ROWS % LPI == 0, "tile rows");
+  uint32_t off[PER];  // r * ldb + 16 c, or OOB_OFFSET for chunks >= chunk_ok
+  int row[PER];       // r, or ROWS for instructions past the tile
+  __device__ __forceinline__ void init(uint32_t ldb, int chunk_ok) {
+    const int l = lane_id(), w = wave_id();
+    const int rl = l / CPR, pc = l % CPR;
+#pragma unroll
+    for (int it = 0; it < PER; ++it) {
+      const int ins = it * NW + w;
+      const int r = ins * LPI + rl;
+      const int c = pc ^ swz<CPR>(r);
+      off[it] = c < chunk_ok ? static_cast<uint32_t>(r) * ldb + (c << 4) : OOB_OFFSET;
+      row[it] = ((NI % NW) == 0 || ins < NI) ? r : ROWS;
+    }
+  }
+  // rows >= row_ok are zero; the tile's row 0 starts at byte soff
+  __device__ __forceinline__ void issue(lds_char* dst, const i32x4& rs, uint32_t soff, int row_ok) const {
+    const int w = wave_id();
+#pragma unroll
+    for (int it = 0; it < PER; ++it) {
+      const int ins = it * NW + w;
+      if ((NI % NW) == 0 || ins < NI) dma16_so(rs, dst + ins * 1024, row[it] < row_ok ? off[it] : OOB_OFFSET, soff);
+    }
+  }
+};
 
 // Fragment with k along the row: lane (r, q) gets row m0 + r, elements
 // 8 (kc + q) .. +7.

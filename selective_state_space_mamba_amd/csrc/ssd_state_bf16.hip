@@ -97,16 +97,24 @@ __global__ __launch_bounds__(ST) void chunk_state_bf16_kernel(
     }
 
   auto chunk_of = [&](int it) { return REV ? nc - 1 - it : it; };
+  // slab copies: one descriptor per batch row, the slab's first row as the
+  // scalar offset, the per-lane offsets computed once
+  const i32x4 rsX = make_rsrc(X + static_cast<int64_t>(bi) * T * HP);
+  const i32x4 rsB = make_rsrc(Bm + static_cast<int64_t>(bi) * T * GN);
+  TileLanes<SSJ, 4, SW> lx;
+  TileLanes<SSJ, 16, SW> lbs;
+  lx.init(HPb, pch);
+  lbs.init(GNb, nch);
   // slab sl of chunk it; with the first slab also the chunk's dt (to LDS, so
   // that no load the compiler can see is in flight: its own wait for one would
   // be vmcnt(0) and hold up every copy) and (bwd) H_c
   auto load_slab = [&](int it, int sl) {
     const int c = chunk_of(it);
-    const int64_t row0 = static_cast<int64_t>(bi) * T + static_cast<int64_t>(c) * Q + sl * SSJ;
+    const uint32_t t0 = static_cast<uint32_t>(c * Q + sl * SSJ);  // the slab's first step in the batch row
     const int vr = min(SSJ, Q - sl * SSJ);
     const int buf = (it * nsl + sl) & 1;
-    tile_async<SSJ, 4, SW>(sX + buf * XSLAB, make_rsrc(X + row0 * HP), h * P * 2 + p0 * 2, HPb, vr, pch);
-    tile_async<SSJ, 16, SW>(sB + buf * BSLAB, make_rsrc(Bm + row0 * GN), g * N * 2, GNb, vr, nch);
+    lx.issue(sX + buf * XSLAB, rsX, t0 * HPb + static_cast<uint32_t>(h * P + p0) * 2, vr);
+    lbs.issue(sB + buf * BSLAB, rsB, t0 * GNb + static_cast<uint32_t>(g * N) * 2, vr);
     if (sl == 0) {
       steps_async<SW>(lds_ptr(sDtb[it & 1]), make_rsrc(dt + (static_cast<int64_t>(bi) * T + static_cast<int64_t>(c) * Q) * H + h),
                       H * 2, Q);
