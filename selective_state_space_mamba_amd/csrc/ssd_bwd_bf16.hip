@@ -163,22 +163,26 @@ __global__ __launch_bounds__(BT) void bwd_col_bf16_kernel(
   // the compiler can see, whose wait would be vmcnt(0) and hold up the copies)
   auto load_dt_abs = [&](int h) { steps_async<BW>(lds_ptr(sDtb), make_rsrc(dt + row0 * H + h), H * 2, Q); };
   auto load_dt = [&](int hh) { load_dt_abs(head(hh)); };
-  auto load_x = [&](int hh) {
-    tile_async<64, 8, BW>(sX + (hh & 1) * TILE_P, rx, j0 * HPb + head(hh) * P * 2, HPb, vj, pch);
-  };
+  // x and dy tiles (64 rows of headdim) and Gamma (headdim rows of d_state):
+  // per-lane offsets computed once, the tile's first row as the scalar offset
+  TileLanes<64, 8, BW> tl8;
+  TileLanes<64, 16, BW> tlg;
+  tl8.init(HPb, pch);
+  tlg.init(N * 2, nch);
+  auto load_x = [&](int hh) { tl8.issue(sX + (hh & 1) * TILE_P, rx, j0 * HPb + head(hh) * P * 2, vj); };
   auto load_dy = [&](int hh, int u, lds_char* dst) {
     const int i0 = (jb + u) * BQ;
-    tile_async<64, 8, BW>(dst, rdy, i0 * HPb + head(hh) * P * 2, HPb, min(BQ, Q - i0), pch);
+    tl8.issue(dst, rdy, i0 * HPb + head(hh) * P * 2, min(BQ, Q - i0));
   };
-  auto load_gam_abs = [&](int h) { tile_async<64, 16, BW>(sGam, rg, h * P * N * 2, N * 2, P, nch); };
+  auto load_gam_abs = [&](int h) { tlg.issue(sGam, rg, h * P * N * 2, P); };
   auto load_gam = [&](int hh) { load_gam_abs(head(hh)); };
   // B rows, the first head's x, dy, Gamma and dt for column block jx of pass
   // pp (this pass, or the next while this one finishes)
   auto load_first = [&](int jx, int pp) {
     const int jx0 = jx * BQ, vjx = min(BQ, Q - jx0), h0 = headp(pp, 0);
     tile_async<64, 16, BW>(sB, rb, jx0 * GNb + goff, GNb, vjx, nch);
-    tile_async<64, 8, BW>(sX, rx, jx0 * HPb + h0 * P * 2, HPb, vjx, pch);
-    tile_async<64, 8, BW>(sDy[0], rdy, jx0 * HPb + h0 * P * 2, HPb, vjx, pch);
+    tl8.issue(sX, rx, jx0 * HPb + h0 * P * 2, vjx);
+    tl8.issue(sDy[0], rdy, jx0 * HPb + h0 * P * 2, vjx);
     load_gam_abs(h0);
     load_dt_abs(h0);
   };
@@ -652,22 +656,26 @@ __global__ __launch_bounds__(BT) void bwd_row_bf16_kernel(
   // the compiler can see, whose wait would be vmcnt(0) and hold up the copies)
   auto load_dt_abs = [&](int h) { steps_async<BW>(lds_ptr(sDtb), make_rsrc(dt + row0 * H + h), H * 2, Q); };
   auto load_dt = [&](int hh) { load_dt_abs(head(hh)); };
+  // x and dy tiles (64 rows of headdim) and H_c (headdim rows of d_state):
+  // per-lane offsets computed once, the tile's first row as the scalar offset
+  TileLanes<64, 8, BW> tl8;
+  TileLanes<64, 16, BW> tlh;
+  tl8.init(HPb, pch);
+  tlh.init(N * 2, nch);
   auto load_x = [&](int hh, int jb, lds_char* dst) {
     const int j0 = jb * BQ;
-    tile_async<64, 8, BW>(dst, rx, j0 * HPb + head(hh) * P * 2, HPb, min(BQ, Q - j0), pch);
+    tl8.issue(dst, rx, j0 * HPb + head(hh) * P * 2, min(BQ, Q - j0));
   };
-  auto load_dy = [&](int hh) {
-    tile_async<64, 8, BW>(sDy + (hh & 1) * TILE_P, rdy, i0 * HPb + head(hh) * P * 2, HPb, vi, pch);
-  };
-  auto load_h_abs = [&](int h) { tile_async<64, 16, BW>(sH, rh, h * P * N * 2, N * 2, P, nch); };
+  auto load_dy = [&](int hh) { tl8.issue(sDy + (hh & 1) * TILE_P, rdy, i0 * HPb + head(hh) * P * 2, vi); };
+  auto load_h_abs = [&](int h) { tlh.issue(sH, rh, h * P * N * 2, P); };
   auto load_h = [&](int hh) { load_h_abs(head(hh)); };
   // C rows, the first head's dy, first x, H_c and dt for row block ix of
   // pass pp (this pass, or the next while this one finishes)
   auto load_first = [&](int ix, int pp) {
     const int ix0 = ix * BQ, vix = min(BQ, Q - ix0), h0 = headp(pp, 0);
     tile_async<64, 16, BW>(sC, rc, ix0 * GNb + goff, GNb, vix, nch);
-    tile_async<64, 8, BW>(sDy, rdy, ix0 * HPb + h0 * P * 2, HPb, vix, pch);
-    tile_async<64, 8, BW>(sX[0], rx, h0 * P * 2, HPb, min(BQ, Q), pch);
+    tl8.issue(sDy, rdy, ix0 * HPb + h0 * P * 2, vix);
+    tl8.issue(sX[0], rx, h0 * P * 2, min(BQ, Q));
     load_h_abs(h0);
     load_dt_abs(h0);
   };

@@ -137,11 +137,17 @@ __global__ __launch_bounds__(FT) void out_fwd_bf16_kernel(
   // the dt series of head hh to LDS (one copy instruction per wave; no load
   // the compiler can see, whose wait would be vmcnt(0) and hold up the copies)
   auto load_dt = [&](int hh) { steps_async<FW>(lds_ptr(sDtb), make_rsrc(dt + row0 * H + head(hh)), H * 2, Q); };
+  // x tiles (64 rows of headdim) and H_c (headdim rows of d_state): per-lane
+  // offsets computed once, the tile's first row as the scalar offset
+  TileLanes<64, 8, FW> tl8;
+  TileLanes<64, 16, FW> tlh;
+  tl8.init(HPb, pch);
+  tlh.init(N * 2, nch);
   auto load_x = [&](int hh, int jb, lds_char* dst) {
     const int j0 = jb * BQ;
-    tile_async<64, 8, FW>(dst, rx, j0 * HPb + head(hh) * P * 2, HPb, min(BQ, Q - j0), pch);
+    tl8.issue(dst, rx, j0 * HPb + head(hh) * P * 2, min(BQ, Q - j0));
   };
-  auto load_h = [&](int hh) { tile_async<64, 16, FW>(sH, rh, head(hh) * P * N * 2, N * 2, P, nch); };
+  auto load_h = [&](int hh) { tlh.issue(sH, rh, head(hh) * P * N * 2, P); };
   // C rows, the first head's first x, H_c and dt for row block ix (this
   // pass's, or the next pass's while this one finishes)
   auto load_first = [&](int ix) {
