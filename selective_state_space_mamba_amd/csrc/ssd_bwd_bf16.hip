@@ -305,6 +305,10 @@ __global__ __launch_bounds__(BT) void bwd_col_bf16_kernel(
         f4 cbt[2];
         float sv[2];  // s at rows i = i0 + ti + 16 tt + r (clamped)
         float sref;   // s at the block's first row
+        // this lane's first row i, taken as computed here, so that the clamps
+        // and masks below are made in the step (not hoisted out of the head
+        // loop into spilled registers)
+        const int ib0 = opaque_index(i0 + ti + r);
         {
           bf16x8 fb[KP][2];
 #pragma unroll
@@ -314,7 +318,7 @@ __global__ __launch_bounds__(BT) void bwd_col_bf16_kernel(
           cbt[0] = cbk[u][0];
           cbt[1] = cbk[u][1];
 #pragma unroll
-          for (int tt = 0; tt < 2; ++tt) sv[tt] = sSh[min(i0 + ti + 16 * tt + r, Q - 1)];
+          for (int tt = 0; tt < 2; ++tt) sv[tt] = sSh[min(ib0 + 16 * tt, Q - 1)];
           sref = sSh[i0];
           sched_ds_reads<2 * KP + 3>();
 #pragma unroll
@@ -328,7 +332,7 @@ __global__ __launch_bounds__(BT) void bwd_col_bf16_kernel(
           const int jq0 = opaque_index(j0 + 16 * wt + 4 * q);
 #pragma unroll
           for (int tt = 0; tt < 2; ++tt) {
-            const int iq = i0 + ti + 16 * tt + r;
+            const int iq = ib0 + 16 * tt;
             const float si = sv[tt];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -364,7 +368,7 @@ __global__ __launch_bounds__(BT) void bwd_col_bf16_kernel(
           }
 #pragma unroll
           for (int tt = 0; tt < 2; ++tt) {
-            const int iq = i0 + ti + 16 * tt + r;
+            const int iq = ib0 + 16 * tt;
             const float rx = __expf(sv[tt] - sref);
             const float rf = (iq < Q) ? rx : 0.f;
 #pragma unroll
@@ -791,6 +795,9 @@ __global__ __launch_bounds__(BT) void bwd_row_bf16_kernel(
         zero(yx);
         f4 cbt[2];
         float sjv[2], dtv[2];  // s and dt at columns j = j0 + tj + 16 tt + r (clamped)
+        // this lane's first column j, taken as computed here (clamps and masks
+        // made in the step, not hoisted into spilled registers)
+        const int jb0 = opaque_index(j0 + tj + r);
         {
           bf16x8 fb[KP][2];
 #pragma unroll
@@ -801,7 +808,7 @@ __global__ __launch_bounds__(BT) void bwd_row_bf16_kernel(
           cbt[1] = cbk[jb][1];
 #pragma unroll
           for (int tt = 0; tt < 2; ++tt) {
-            const int jc = min(j0 + tj + 16 * tt + r, Q - 1);
+            const int jc = min(jb0 + 16 * tt, Q - 1);
             sjv[tt] = sSh[jc];
             dtv[tt] = sDh[jc];
           }
@@ -816,7 +823,7 @@ __global__ __launch_bounds__(BT) void bwd_row_bf16_kernel(
           const int iq0 = opaque_index(i0 + 16 * wt + 4 * q);
 #pragma unroll
           for (int tt = 0; tt < 2; ++tt) {
-            const int jq = j0 + tj + 16 * tt + r;
+            const int jq = jb0 + 16 * tt;
             const float sj = sjv[tt];
             const float dtj = (jq < Q) ? dtv[tt] : 0.f;
 #pragma unroll

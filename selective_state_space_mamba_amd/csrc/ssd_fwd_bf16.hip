@@ -254,11 +254,14 @@ __global__ __launch_bounds__(FT) void out_fwd_bf16_kernel(
         f4 cbt[2];
         float sjv[2], dtv[2];  // s and dt at columns j = j0 + tj + 16 tt + r (clamped)
         bf16x8 fx[4];
+        // this lane's first column j, taken as computed here (clamps and masks
+        // made in the step, not hoisted into spilled registers)
+        const int jb0 = opaque_index(j0 + tj + r);
         cbt[0] = cbk[jb][0];
         cbt[1] = cbk[jb][1];
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
-          const int jc = min(j0 + tj + 16 * tt + r, Q - 1);
+          const int jc = min(jb0 + 16 * tt, Q - 1);
           sjv[tt] = sSh[jc];
           dtv[tt] = sDh[jc];
         }
@@ -270,7 +273,7 @@ __global__ __launch_bounds__(FT) void out_fwd_bf16_kernel(
           const int iq0 = opaque_index(i0 + 16 * wt + 4 * q);
 #pragma unroll
           for (int tt = 0; tt < 2; ++tt) {
-            const int jq = j0 + tj + 16 * tt + r;
+            const int jq = jb0 + 16 * tt;
             const float sj = sjv[tt];
             const float dtj = (jq < Q) ? dtv[tt] : 0.f;
 #pragma unroll
