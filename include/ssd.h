@@ -92,8 +92,11 @@ int ssd_fwd(const ssd_problem* prob, const void* x, const void* dt, const float*
             float* final_state, float* chunk_states, void* workspace, size_t workspace_bytes,
             void* stream);
 
-/* Backward of L = sum(dy * y).
+/* Backward of L = sum(dy * y) + sum(d_final_state * final_state).
  *   inputs as in ssd_fwd; dy [b,T,H,P] in dy_dtype
+ *   d_final_state [b,H,P,N] f32, nullable (zeros): the gradient reaching the
+ *     state after the last step, so that consecutive segments of a sequence
+ *     can chain their backward passes (it starts the reverse state pass)
  *   chunk_states: nullable; when given it must be what ssd_fwd wrote for the
  *     same inputs (not checked); when null the states are recomputed
  *   outputs (f32, all required except d_init_state):
@@ -102,9 +105,9 @@ int ssd_fwd(const ssd_problem* prob, const void* x, const void* dt, const float*
  *     also when init_state is null: the gradient at a zero initial state). */
 int ssd_bwd(const ssd_problem* prob, const void* x, const void* dt, const float* A_log,
             const void* B, const void* C, const float* D, const float* init_state,
-            const float* chunk_states, const void* dy, float* dx, float* ddt, float* dA_log,
-            float* dB, float* dC, float* dD, float* d_init_state, void* workspace,
-            size_t workspace_bytes, void* stream);
+            const float* chunk_states, const void* dy, const float* d_final_state, float* dx,
+            float* ddt, float* dA_log, float* dB, float* dC, float* dD, float* d_init_state,
+            void* workspace, size_t workspace_bytes, void* stream);
 
 /* Causal depthwise conv1d (zero initial state) followed by SiLU, split into
  * the SSD inputs.  xbc [b,T,conv_dim] with conv_dim = d_inner + 2*ngroups*dstate

@@ -43,7 +43,7 @@ def _lib():
         lib = ctypes.CDLL(path)
         i64, dp, cint, cdbl = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_double
         lib.ssd_oracle_fwd.argtypes = [i64] * 7 + [dp] * 10 + [cint]
-        lib.ssd_oracle_bwd.argtypes = [i64] * 6 + [dp] * 15 + [cint]
+        lib.ssd_oracle_bwd.argtypes = [i64] * 6 + [dp] * 16 + [cint]
         lib.conv_oracle_fwd.argtypes = [i64] * 4 + [dp] * 5
         lib.conv_oracle_bwd.argtypes = [i64] * 4 + [dp] * 7
         lib.rmsnorm_oracle_fwd.argtypes = [i64, i64, cdbl] + [dp] * 5
@@ -98,11 +98,14 @@ def ssd_fwd(x, dt, A_log, B, C, D, h0=None, chunk: int = 0, nthreads: Optional[i
     return out
 
 
-def ssd_bwd(x, dt, A_log, B, C, D, dy, h0=None, nthreads: Optional[int] = None) -> Dict[str, np.ndarray]:
-    """Sequential analytic backward of L = sum(dy * y).  Returns dx, ddt,
-    dA_log, dB, dC, dD and dh0 (gradient of the initial state; zeros state is
-    used when h0 is None and dh0 is still returned)."""
-    x, dt, A_log, B, C, D, h0, dy = map(_f64, (x, dt, A_log, B, C, D, h0, dy))
+def ssd_bwd(x, dt, A_log, B, C, D, dy, h0=None, nthreads: Optional[int] = None,
+            dfinal=None) -> Dict[str, np.ndarray]:
+    """Sequential analytic backward of L = sum(dy * y) + sum(dfinal * final).
+    Returns dx, ddt, dA_log, dB, dC, dD and dh0 (gradient of the initial
+    state; zeros state is used when h0 is None and dh0 is still returned).
+    dfinal [b,H,P,N] (None: zeros) is the gradient of the state after the last
+    step: it is the reverse-time loop's carry before its first step."""
+    x, dt, A_log, B, C, D, h0, dy, dfinal = map(_f64, (x, dt, A_log, B, C, D, h0, dy, dfinal))
     b, T, H, P, N, G = _dims(x, B, dt)
     dx = np.empty_like(x)
     ddt = np.empty_like(dt)
@@ -112,7 +115,7 @@ def ssd_bwd(x, dt, A_log, B, C, D, dy, h0=None, nthreads: Optional[int] = None) 
     dD = np.empty(H)
     dh0 = np.empty((b, H, P, N))
     rc = _lib().ssd_oracle_bwd(b, T, H, P, N, G,
-                               *map(_ptr, (x, dt, A_log, B, C, D, h0, dy, dx, ddt, dA, dB, dC, dD, dh0)),
+                               *map(_ptr, (x, dt, A_log, B, C, D, h0, dy, dfinal, dx, ddt, dA, dB, dC, dD, dh0)),
                                nthreads or default_threads())
     if rc != 0:
         raise ValueError(f"ssd_oracle_bwd failed ({rc})")

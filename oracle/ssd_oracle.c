@@ -15,7 +15,9 @@
  *   ssd_oracle_bwd       the reverse-time loop of ssd_backward_reference, plus
  *                        the gradient of the initial state (the carry left after
  *                        the step t = 0; the page computes it but does not return
- *                        it).
+ *                        it), and optionally a gradient of the final state, which
+ *                        is the carry before the first reverse step (the page's
+ *                        loop starts from a zero carry).
  *   conv_oracle_fwd/bwd  depthwise_conv_preact_with_history, silu, and the
  *                        tap loop of the block backward's conv/SiLU fallback.
  *   rmsnorm_oracle_fwd/bwd  rmsnorm_gated_forward_from_inv_rms (with inv_rms
@@ -148,7 +150,7 @@ int ssd_oracle_fwd(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdi
 
 typedef struct {
   dims_t d;
-  const double *x, *dt, *A_log, *B, *C, *D, *h0, *dy;
+  const double *x, *dt, *A_log, *B, *C, *D, *h0, *dy, *dfinal;
   double *dx, *ddt, *dh0;
   double *dB_head, *dC_head; /* per-head partials [b,T,H,N] */
   double *ga_unit, *dD_unit; /* per-unit partials [b*H] */
@@ -181,6 +183,9 @@ static void bwd_unit(void *vctx, int64_t unit) {
   double *seg = (double *)malloc(sizeof(double) * PN * SEG);
   double *carry = (double *)calloc((size_t)PN, sizeof(double));
   double *Gs = (double *)malloc(sizeof(double) * PN);
+  /* the gradient of the final state enters the reverse loop as its carry
+   * (zero when the loss does not involve the final state) */
+  if (c->dfinal) memcpy(carry, c->dfinal + (bi * d.H + h) * PN, sizeof(double) * PN);
   double *st = (double *)malloc(sizeof(double) * PN);
   double ga = 0.0, dDacc = 0.0;
 
@@ -264,8 +269,8 @@ static void bwd_unit(void *vctx, int64_t unit) {
 int ssd_oracle_bwd(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int64_t dstate,
                    int64_t ngroups, const double *x, const double *dt, const double *A_log,
                    const double *B, const double *C, const double *D, const double *h0,
-                   const double *dy, double *dx, double *ddt, double *dA_log, double *dB,
-                   double *dC, double *dD, double *dh0, int nthreads) {
+                   const double *dy, const double *dfinal, double *dx, double *ddt, double *dA_log,
+                   double *dB, double *dC, double *dD, double *dh0, int nthreads) {
   if (batch < 0 || seqlen < 0 || nheads <= 0 || headdim <= 0 || dstate <= 0 || ngroups <= 0)
     return -1;
   if (nheads % ngroups) return -2;
@@ -279,7 +284,7 @@ int ssd_oracle_bwd(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdi
     free(dB_head); free(dC_head); free(ga_unit); free(dD_unit);
     return -3;
   }
-  bwd_ctx c = {{b, T, H, headdim, N, G}, x, dt, A_log, B, C, D, h0, dy, dx, ddt, dh0,
+  bwd_ctx c = {{b, T, H, headdim, N, G}, x, dt, A_log, B, C, D, h0, dy, dfinal, dx, ddt, dh0,
                dB_head, dC_head, ga_unit, dD_unit};
   run_units(bwd_unit, &c, nunit, nthreads);
 

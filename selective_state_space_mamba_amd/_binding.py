@@ -47,7 +47,7 @@ def load_library():
     lib.ssd_workspace_bytes.restype = sz
     lib.ssd_fwd.argtypes = [pp] + [vp] * 10 + [vp, sz, vp]
     lib.ssd_fwd.restype = ctypes.c_int
-    lib.ssd_bwd.argtypes = [pp] + [vp] * 16 + [vp, sz, vp]
+    lib.ssd_bwd.argtypes = [pp] + [vp] * 17 + [vp, sz, vp]
     lib.ssd_bwd.restype = ctypes.c_int
     lib.mamba2_conv1d_silu_fwd.argtypes = [i64] * 6 + [i32] + [vp] * 6 + [vp]
     lib.mamba2_conv1d_silu_fwd.restype = ctypes.c_int
@@ -191,14 +191,18 @@ def ssd_fwd(x, dt, A_log, B, C, D, init_state=None, chunk: int = 256, want_chunk
 
 def ssd_bwd(x, dt, A_log, B, C, D, dy, init_state=None, chunk_states=None, chunk: int = 256,
             want_d_init_state: bool = True, out: Optional[Dict[str, torch.Tensor]] = None,
-            workspace: Optional[torch.Tensor] = None, stream=None) -> Dict[str, torch.Tensor]:
-    """SSD backward of sum(dy * y).  Returns dx, ddt, dA_log, dB, dC, dD (f32)
-    and d_init_state (f32, or None when not requested)."""
+            workspace: Optional[torch.Tensor] = None, stream=None,
+            d_final_state: Optional[torch.Tensor] = None) -> Dict[str, torch.Tensor]:
+    """SSD backward of sum(dy * y) + sum(d_final_state * final_state).
+    Returns dx, ddt, dA_log, dB, dC, dD (f32) and d_init_state (f32, or None
+    when not requested)."""
     lib = load_library()
     b, T, H, P, N, G = _check_inputs(x, dt, A_log, B, C, D, init_state)
     if dy.dtype not in (torch.float32, torch.bfloat16):
         raise TypeError("dy must be float32 or bfloat16")
     _need(dy, "dy", (b, T, H, P), device=x.device)
+    if d_final_state is not None:
+        _need(d_final_state, "d_final_state", (b, H, P, N), torch.float32, x.device)
     if chunk_states is not None:
         _need(chunk_states, "chunk_states", (b, T // chunk, H, P, N), torch.float32, x.device)
     prob = make_problem(x, B, chunk, dy.dtype)
@@ -216,7 +220,8 @@ def ssd_bwd(x, dt, A_log, B, C, D, dy, init_state=None, chunk_states=None, chunk
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
     wsz = 0 if workspace is None else workspace.numel()
     _check(lib.ssd_bwd(ctypes.byref(prob), _ptr(x), _ptr(dt), _ptr(A_log), _ptr(B), _ptr(C), _ptr(D),
-                       _ptr(init_state), _ptr(chunk_states), _ptr(dy), _ptr(out["dx"]), _ptr(out["ddt"]),
+                       _ptr(init_state), _ptr(chunk_states), _ptr(dy), _ptr(d_final_state), _ptr(out["dx"]),
+                       _ptr(out["ddt"]),
                        _ptr(out["dA_log"]), _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out["dD"]), _ptr(dinit),
                        _ptr(workspace), wsz, _stream(stream)))
     out["d_init_state"] = dinit

@@ -319,8 +319,8 @@ int ssd_fwd(const ssd_problem* prob, const void* x, const void* dt, const float*
 
 int ssd_bwd(const ssd_problem* prob, const void* x, const void* dt, const float* A_log, const void* B,
             const void* C, const float* D, const float* init_state, const float* chunk_states, const void* dy,
-            float* dx, float* ddt, float* dA_log, float* dB, float* dC, float* dD, float* d_init_state,
-            void* workspace, size_t workspace_bytes, void* stream) {
+            const float* d_final_state, float* dx, float* ddt, float* dA_log, float* dB, float* dC, float* dD,
+            float* d_init_state, void* workspace, size_t workspace_bytes, void* stream) {
   ssd::Dims d;
   int rc = check_problem(prob, &d);
   if (rc != SSD_OK) return rc;
@@ -331,14 +331,21 @@ int ssd_bwd(const ssd_problem* prob, const void* x, const void* dt, const float*
   const bool empty = d.b == 0 || d.T == 0;
   if (!empty && (!x || !dt || !B || !C || !dy || !dx || !ddt || !dB || !dC))
     return fail(SSD_ERR_INVALID_ARG, "ssd_bwd: x, dt, B, C, dy, dx, ddt, dB and dC are required");
-  const void* ptrs[] = {x, dt, A_log, B, C, D, init_state, chunk_states, dy, dx, ddt, dA_log, dB, dC, dD, d_init_state};
+  const void* ptrs[] = {x,  dt, A_log, B,  C,  D,      init_state, chunk_states, dy, d_final_state,
+                        dx, ddt, dA_log, dB, dC, dD, d_init_state};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return fail(SSD_ERR_ALIGN, "ssd_bwd: a tensor pointer is not 16-byte aligned");
   if (empty) {
     SSD_LAUNCH(ssd::launch_fill(dA_log, d.H, 0.f, st), "fill");
     SSD_LAUNCH(ssd::launch_fill(dD, d.H, 0.f, st), "fill");
-    if (d_init_state)
-      SSD_LAUNCH(ssd::launch_fill(d_init_state, static_cast<int64_t>(d.b) * d.H * d.P * d.N, 0.f, st), "fill");
+    if (d_init_state) {
+      const int64_t n = static_cast<int64_t>(d.b) * d.H * d.P * d.N;
+      // no steps: the final state is the initial one
+      if (d_final_state)
+        SSD_LAUNCH(ssd::launch_copy(d_init_state, d_final_state, n, st), "copy");
+      else
+        SSD_LAUNCH(ssd::launch_fill(d_init_state, n, 0.f, st), "fill");
+    }
     return ok();
   }
   const BwdPlan plan = plan_bwd(d, chunk_states != nullptr, use_bf16_kernels(d, prob->act_dtype, prob->dy_dtype));
@@ -376,11 +383,13 @@ int ssd_bwd(const ssd_problem* prob, const void* x, const void* dt, const float*
     states = rec;
   }
   if (plan.bf16)
-    SSD_LAUNCH(ssd::launch_chunk_state_bwd_bf16(d, dy, C, dt, A_log, states, gamma, d_init_state, s.gh_part, hbf, st),
+    SSD_LAUNCH(ssd::launch_chunk_state_bwd_bf16(d, dy, C, dt, A_log, d_final_state, states, gamma, d_init_state,
+                                                s.gh_part, hbf, st),
                "chunk_state_bwd");
   else
     SSD_LAUNCH(
-        ssd::launch_chunk_state_bwd(d, act, dyt, dy, C, dt, A_log, states, gamma, d_init_state, s.gh_part, nullptr, st),
+        ssd::launch_chunk_state_bwd(d, act, dyt, dy, C, dt, A_log, d_final_state, states, gamma, d_init_state,
+                                    s.gh_part, nullptr, st),
         "chunk_state_bwd");
   if (plan.bf16) {
     SSD_LAUNCH(ssd::launch_bwd_col_bf16(d, plan.nsplit, x, B, C, dt, dy, A_log, D, gamma, dx,

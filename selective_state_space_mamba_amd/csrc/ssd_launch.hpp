@@ -32,7 +32,7 @@ hipError_t launch_chunk_state_fwd(const Dims& d, DType act, const void* x, const
 // gh_part[b,c,h,pb] = partial <gamma[b,c,h], states[b,c,h]> over headdim block pb;
 // hbf (nullable) = the states rounded to bf16, same layout.
 hipError_t launch_chunk_state_bwd(const Dims& d, DType act, DType dyt, const void* dy,
-                                  const void* C, const void* dt, const float* A_log,
+                                  const void* C, const void* dt, const float* A_log, const float* dfinal,
                                   const float* states, void* gamma, float* dinit, float* gh_part,
                                   void* hbf, hipStream_t st);
 
@@ -43,8 +43,8 @@ hipError_t launch_chunk_state_fwd_bf16(const Dims& d, const void* x, const void*
                                        const float* A_log, const float* init, float* states, float* final_state,
                                        void* hbf, hipStream_t st);
 hipError_t launch_chunk_state_bwd_bf16(const Dims& d, const void* dy, const void* C, const void* dt,
-                                       const float* A_log, const float* states, void* gamma, float* dinit,
-                                       float* gh_part, void* hbf, hipStream_t st);
+                                       const float* A_log, const float* dfinal, const float* states, void* gamma,
+                                       float* dinit, float* gh_part, void* hbf, hipStream_t st);
 hipError_t launch_out_fwd_bf16(const Dims& d, int nsplit, const void* x, const void* B, const void* C,
                                const void* dt, const float* A_log, const float* D, const void* hbf, void* y,
                                hipStream_t st);

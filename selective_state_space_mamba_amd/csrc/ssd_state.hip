@@ -13,7 +13,8 @@
 //
 //   Gamma_c = exp(s_end) Gamma_{c+1} + sum_i exp(s_i) dy_i (outer) C_i,
 //
-// with Gamma_nc = 0 and d(initial state) = Gamma_0.
+// with Gamma_nc the gradient of the final state (zero unless given) and
+// d(initial state) = Gamma_0.
 //
 // Both are one kernel: a workgroup owns 16 headdim rows of one (batch, head)
 // and walks the chunks in order (forward) or in reverse (backward), keeping its
@@ -39,7 +40,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void chunk_state_kernel(
     const TB* __restrict__ Bm,         // fwd: B; bwd: C             [b,T,G,N]
     const TDT* __restrict__ dt,        // [b,T,H]
     const float* __restrict__ A_log,   // [H]
-    const float* __restrict__ init,    // fwd: initial state (nullable); bwd: unused
+    const float* __restrict__ init,    // fwd: initial state; bwd: Gamma_nc, the final state's gradient (nullable)
     void* __restrict__ states_out_v,   // fwd: H_c (f32); bwd: Gamma_{c+1} (operand type) [b,nc,H,P,N]
     float* __restrict__ last_out,      // fwd: final state; bwd: d(initial state) (nullable)
     const float* __restrict__ hstates, // bwd: H_c, for <Gamma_{c+1}, H_c>
@@ -81,7 +82,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void chunk_state_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int p = p0 + 4 * q + i, n = 32 * w + 16 * t + r;
-      st[t][i] = (!REV && init && p < P && n < N) ? init[(static_cast<int64_t>(bi) * H + h) * PN + p * N + n] : 0.f;
+      st[t][i] = (init && p < P && n < N) ? init[(static_cast<int64_t>(bi) * H + h) * PN + p * N + n] : 0.f;
     }
 
   TransTile<TX, SJ, PB> tx;    // x (or dy) rows j, columns p0..p0+15 -> [p][j]
@@ -183,20 +184,20 @@ hipError_t launch_chunk_state_fwd(const Dims& d, DType act, const void* x, const
 }
 
 hipError_t launch_chunk_state_bwd(const Dims& d, DType act, DType dyt, const void* dy,
-                                  const void* C, const void* dt, const float* A_log,
+                                  const void* C, const void* dt, const float* A_log, const float* dfinal,
                                   const float* states, void* gamma, float* dinit, float* gh_part,
                                   void* hbf, hipStream_t st) {
   if (act == BF16) {
     if (dyt == BF16)
-      return launch_state<uint16_t, uint16_t, true, true>(d, dy, C, dt, A_log, nullptr, gamma, dinit,
+      return launch_state<uint16_t, uint16_t, true, true>(d, dy, C, dt, A_log, dfinal, gamma, dinit,
                                                           states, gh_part, st, hbf);
-    return launch_state<float, uint16_t, true, true>(d, dy, C, dt, A_log, nullptr, gamma, dinit, states,
+    return launch_state<float, uint16_t, true, true>(d, dy, C, dt, A_log, dfinal, gamma, dinit, states,
                                                      gh_part, st, hbf);
   }
   if (dyt == BF16)
-    return launch_state<uint16_t, float, false, true>(d, dy, C, dt, A_log, nullptr, gamma, dinit, states,
+    return launch_state<uint16_t, float, false, true>(d, dy, C, dt, A_log, dfinal, gamma, dinit, states,
                                                       gh_part, st);
-  return launch_state<float, float, false, true>(d, dy, C, dt, A_log, nullptr, gamma, dinit, states,
+  return launch_state<float, float, false, true>(d, dy, C, dt, A_log, dfinal, gamma, dinit, states,
                                                  gh_part, st);
 }
 

@@ -4,6 +4,7 @@
 //
 //   H_{c+1}   = exp(s_end) H_c + sum_j exp(s_end - s_j) dt_j x_j (outer) B_j
 //   Gamma_c   = exp(s_end) Gamma_{c+1} + sum_i exp(s_i) dy_i (outer) C_i
+//   (Gamma_nc = the gradient of the final state, zero unless given)
 //
 // (page-1 reference, burn_dragon_kernel mamba2/backward.rs: the recurrence of
 // ssd_forward_state_history_reference and the carry of ssd_backward_reference,
@@ -51,7 +52,7 @@ __global__ __launch_bounds__(ST) void chunk_state_bf16_kernel(
     const uint16_t* __restrict__ Bm,    // fwd: B; bwd: C        [b,T,G,N]
     const uint16_t* __restrict__ dt,    // [b,T,H]
     const float* __restrict__ A_log,    // [H]
-    const float* __restrict__ init,     // fwd: initial state (nullable)
+    const float* __restrict__ init,     // fwd: initial state; bwd: Gamma_nc, the final state's gradient (nullable)
     float* __restrict__ states_f32,     // fwd: H_c [b,nc,H,P,N]
     uint16_t* __restrict__ states_bf,   // fwd: H_c in bf16 (nullable); bwd: Gamma_{c+1} in bf16
     float* __restrict__ last_out,       // fwd: final state; bwd: d(initial state) (nullable)
@@ -93,7 +94,7 @@ __global__ __launch_bounds__(ST) void chunk_state_bf16_kernel(
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int p = p0 + 16 * pw + 4 * q + e, n = 32 * nw + 16 * t + r;
-      st[t][e] = (!REV && init && p < P && n < N) ? init[(static_cast<int64_t>(bi) * H + h) * PN + p * N + n] : 0.f;
+      st[t][e] = (init && p < P && n < N) ? init[(static_cast<int64_t>(bi) * H + h) * PN + p * N + n] : 0.f;
     }
 
   auto chunk_of = [&](int it) { return REV ? nc - 1 - it : it; };
@@ -282,11 +283,11 @@ hipError_t launch_chunk_state_fwd_bf16(const Dims& d, const void* x, const void*
 }
 
 hipError_t launch_chunk_state_bwd_bf16(const Dims& d, const void* dy, const void* C, const void* dt,
-                                       const float* A_log, const float* states, void* gamma, float* dinit,
-                                       float* gh_part, void* hbf, hipStream_t st) {
+                                       const float* A_log, const float* dfinal, const float* states, void* gamma,
+                                       float* dinit, float* gh_part, void* hbf, hipStream_t st) {
   const int64_t nblk = static_cast<int64_t>(d.b) * d.H * ((d.P + SPB - 1) / SPB);
   hipLaunchKernelGGL(chunk_state_bf16_kernel<true>, dim3(nblk), dim3(ST), 0, st, static_cast<const uint16_t*>(dy),
-                     static_cast<const uint16_t*>(C), static_cast<const uint16_t*>(dt), A_log, nullptr, nullptr,
+                     static_cast<const uint16_t*>(C), static_cast<const uint16_t*>(dt), A_log, dfinal, nullptr,
                      static_cast<uint16_t*>(gamma), dinit, states, gh_part, static_cast<uint16_t*>(hbf), d.T, d.H,
                      d.P, d.N, d.G, d.Q);
   return hipGetLastError();

@@ -44,7 +44,8 @@ def relerr(got, ref) -> float:
     return num / den
 
 
-def gpu_ssd(cfg: SSDConfig, d: dict, chunk: int | None = None, save_states: bool = True, dy=None):
+def gpu_ssd(cfg: SSDConfig, d: dict, chunk: int | None = None, save_states: bool = True, dy=None,
+            dfinal: np.ndarray | None = None):
     """Runs ssd_fwd then ssd_bwd on the device; returns host f64 arrays."""
     import selective_state_space_mamba_amd as ssd
     Q = chunk or cfg.chunk
@@ -53,17 +54,18 @@ def gpu_ssd(cfg: SSDConfig, d: dict, chunk: int | None = None, save_states: bool
     h0 = dev(d["h0"]) if d.get("h0") is not None else None
     dyd = dev(d["dy"]) if dy is None else dy
     y, fin, cs = ssd.ssd_fwd(x, dt, A_log, B, C, D, h0, chunk=Q, want_chunk_states=True)
-    g = ssd.ssd_bwd(x, dt, A_log, B, C, D, dyd, h0, chunk_states=cs if save_states else None, chunk=Q)
+    g = ssd.ssd_bwd(x, dt, A_log, B, C, D, dyd, h0, chunk_states=cs if save_states else None, chunk=Q,
+                    d_final_state=dev(dfinal))
     torch.cuda.synchronize()
     out = {"y": host(y), "final": host(fin), "chunk_states": host(cs)}
     out.update({k: host(v) for k, v in g.items()})
     return out
 
 
-def oracle_ssd(d: dict, chunk: int, dy_values=None):
+def oracle_ssd(d: dict, chunk: int, dy_values=None, dfinal: np.ndarray | None = None):
     args = (d["x"].values, d["dt"].values, d["A_log"], d["B"].values, d["C"].values, d["D"])
     f = oracle.ssd_fwd(*args, d.get("h0"), chunk=chunk)
-    g = oracle.ssd_bwd(*args, d["dy"].values if dy_values is None else dy_values, d.get("h0"))
+    g = oracle.ssd_bwd(*args, d["dy"].values if dy_values is None else dy_values, d.get("h0"), dfinal=dfinal)
     out = {"y": f["y"], "final": f["final"], "chunk_states": f["chunk_states"]}
     out.update(g)
     out["d_init_state"] = out.pop("dh0")

@@ -68,8 +68,8 @@ def call_bwd(lib, p, ws_bytes=1 << 30, misalign=None, null=None):
     if null:
         ptrs[null] = None
     return lib.ssd_bwd(ctypes.byref(p), ptrs["x"], ptrs["dt"], ptrs["A_log"], ptrs["B"], ptrs["C"], ptrs["D"],
-                       None, None, ptrs["dy"], ptrs["dx"], ptrs["ddt"], ptrs["dA_log"], ptrs["dB"], ptrs["dC"],
-                       ptrs["dD"], None, ptrs["ws"], ws_bytes, None)
+                       None, None, ptrs["dy"], None, ptrs["dx"], ptrs["ddt"], ptrs["dA_log"], ptrs["dB"],
+                       ptrs["dC"], ptrs["dD"], None, ptrs["ws"], ws_bytes, None)
 
 
 @pytest.mark.parametrize("kw,status,text", [

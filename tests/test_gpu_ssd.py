@@ -69,6 +69,18 @@ def test_many_chunks_bf16():
     compare(gpu_ssd(cfg, d), oracle_ssd(d, cfg.chunk), TOL["bf16"], label="256 chunks per head, bf16")
 
 
+@pytest.mark.parametrize("dtype,saved", [("f32", True), ("bf16", False), ("bf16", True)])
+def test_final_state_gradient(dtype, saved):
+    # With d_final_state the reverse state pass starts from it (consecutive
+    # segments of one sequence chain their backward passes this way); every
+    # gradient changes through Gamma of the last chunk.
+    cfg = SSDConfig("dfinal", 2, 512, 8, 64, 128, 2, 128, dtype, init_state=True, seed=21)
+    d = make_inputs(cfg)
+    dfin = (0.5 * np.random.default_rng(22).standard_normal((2, 8, 64, 128))).astype(np.float32)
+    compare(gpu_ssd(cfg, d, save_states=saved, dfinal=dfin), oracle_ssd(d, cfg.chunk, dfinal=dfin), TOL[dtype],
+            label=f"d_final_state {dtype} saved={saved}")
+
+
 def test_single_chunk_whole_sequence():
     cfg = SSDConfig("one", 3, 256, 8, 64, 128, 8, 256, "bf16", init_state=True, seed=6)
     d = make_inputs(cfg)
@@ -120,6 +132,11 @@ def test_empty_problems():
         assert y.shape == x.shape and torch.equal(fin, h0)
         assert torch.count_nonzero(g["dA_log"]) == 0 and torch.count_nonzero(g["dD"]) == 0
         assert torch.count_nonzero(g["d_init_state"]) == 0
+        # no steps: the final state is the initial one, so is its gradient
+        dfin = torch.randn((b, 4, 8, 16), device="cuda:0")
+        g = ssd.ssd_bwd(x, dt, A_log, B, B, D, x, h0, chunk_states=cs, chunk=16, d_final_state=dfin)
+        torch.cuda.synchronize()
+        assert torch.equal(g["d_init_state"], dfin)
 
 
 def test_errors_are_raised_not_hidden():

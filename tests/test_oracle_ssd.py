@@ -168,6 +168,53 @@ def test_finite_differences_p1_test_shape_sampled():
     _fd_check(p, bwd(p), ["x", "dt", "A_log", "B", "C", "D", "h0"], sample=24)
 
 
+def _loss_with_final(p):
+    f = fwd(p)
+    return float(np.sum(f["y"] * p["dy"]) + np.sum(f["final"] * p["dfinal"]))
+
+
+def test_finite_differences_with_final_state_gradient():
+    # L = sum(dy y) + <dfinal, final>: every gradient against central
+    # differences of the oracle's forward
+    p = rand_problem(11, b=2, T=6, H=4, G=2, P=2, N=3)
+    p["dfinal"] = np.random.default_rng(12).standard_normal((2, 4, 2, 3))
+    g = oracle.ssd_bwd(p["x"], p["dt"], p["A_log"], p["B"], p["C"], p["D"], p["dy"], p["h0"], dfinal=p["dfinal"])
+    gmap = {"x": "dx", "dt": "ddt", "A_log": "dA_log", "B": "dB", "C": "dC", "D": "dD", "h0": "dh0"}
+    eps = 1e-6
+    for name, gk in gmap.items():
+        an = g[gk].ravel()
+        scale = max(1.0, np.max(np.abs(an)))
+        for k in range(p[name].size):
+            q = {kk: (vv.copy() if isinstance(vv, np.ndarray) else vv) for kk, vv in p.items()}
+            q[name].ravel()[k] += eps
+            lp = _loss_with_final(q)
+            q[name].ravel()[k] -= 2 * eps
+            lm = _loss_with_final(q)
+            assert abs((lp - lm) / (2 * eps) - an[k]) / scale < 2e-7, (name, k)
+
+
+def test_final_state_gradient_only_closed_form():
+    # With dy = 0 the loss is <dfinal, final>, and unrolling the recurrence
+    # final = prod_t exp(dt_t A) h0 + sum_t exp(A sum_{s>t} dt_s) dt_t x_t (outer) B_t
+    # gives the gradients in closed form.
+    p = rand_problem(13, b=2, T=5, H=2, G=1, P=3, N=2)
+    p["dy"] = np.zeros_like(p["dy"])
+    dfin = np.random.default_rng(14).standard_normal((2, 2, 3, 2))
+    g = oracle.ssd_bwd(p["x"], p["dt"], p["A_log"], p["B"], p["C"], p["D"], p["dy"], p["h0"], dfinal=dfin)
+    A = -np.exp(p["A_log"])
+    b, T, H, P = p["x"].shape
+    for bi in range(b):
+        for h in range(H):
+            dts = p["dt"][bi, :, h]
+            np.testing.assert_allclose(g["dh0"][bi, h], np.exp(A[h] * dts.sum()) * dfin[bi, h], rtol=1e-13)
+            for t in range(T):
+                w = np.exp(A[h] * dts[t + 1:].sum()) * dts[t]
+                np.testing.assert_allclose(g["dx"][bi, t, h], w * dfin[bi, h] @ p["B"][bi, t, 0],
+                                           rtol=1e-12, atol=1e-14)
+    np.testing.assert_array_equal(g["dC"], 0.0)
+    np.testing.assert_array_equal(g["dD"], 0.0)
+
+
 def test_single_step_closed_form():
     p = rand_problem(8, b=1, T=1, H=2, G=1, P=3, N=4)
     x, dt, B, C, h0, dy = p["x"][0, 0], p["dt"][0, 0], p["B"][0, 0, 0], p["C"][0, 0, 0], p["h0"][0], p["dy"][0, 0]
