@@ -223,15 +223,26 @@ def make_step(cfg, d):
     xbc, z, gout = to_dev(d["xBC"]), to_dev(d["z"]), to_dev(d["gout"])
     conv_w, conv_b, norm_w = to_dev(d["conv_w"]), to_dev(d["conv_b"]), to_dev(d["norm_w"])
     di = cfg.d_inner
+    lib = ssd.load_library()
+    K = conv_w.shape[1]
+    u8 = dict(dtype=torch.uint8, device="cuda")
+    prob = ssd._binding.make_problem(x.view(b, T, H, P), B, Q, torch.bfloat16)
+    wsf = torch.empty(max(1, ssd.ssd_workspace_bytes(prob, False, True)), **u8)
+    wsb = torch.empty(max(1, ssd.ssd_workspace_bytes(prob, True, True)), **u8)
+    wsr = torch.empty(max(1, lib.mamba2_rmsnorm_gated_bwd_workspace_bytes(b * T, di)), **u8)
+    wsc = torch.empty(max(1, lib.mamba2_conv1d_silu_bwd_workspace_bytes(b, T, di, G, N, K)), **u8)
 
     def step():
         xs, Bs, Cs = ssd.conv1d_silu_fwd(xbc, conv_w, conv_b, di, G, N)
         xs = xs.view(b, T, H, P)
-        y, _, cs = ssd.ssd_fwd(xs, dt, A_log, Bs, Cs, D, h0, chunk=Q, out=fo)
+        y, _, cs = ssd.ssd_fwd(xs, dt, A_log, Bs, Cs, D, h0, chunk=Q, out=fo, workspace=wsf)
         out, inv = ssd.rmsnorm_gated_fwd(y.view(b, T, di), z, norm_w, cfg.norm_eps)
-        gy, gz, gw = ssd.rmsnorm_gated_bwd(y.view(b, T, di), z, norm_w, inv, gout)
-        g = ssd.ssd_bwd(xs, dt, A_log, Bs, Cs, D, gy.view(b, T, H, P), h0, chunk_states=cs, chunk=Q, out=go)
-        ssd.conv1d_silu_bwd(xbc, conv_w, conv_b, g["dx"].view(b, T, di), g["dB"], g["dC"], di, G, N)
+        gy, gz, gw = ssd.rmsnorm_gated_bwd(y.view(b, T, di), z, norm_w, inv, gout, workspace=wsr,
+                                           dy_dtype=torch.bfloat16)
+        g = ssd.ssd_bwd(xs, dt, A_log, Bs, Cs, D, gy.view(b, T, H, P), h0, chunk_states=cs, chunk=Q, out=go,
+                        workspace=wsb)
+        ssd.conv1d_silu_bwd(xbc, conv_w, conv_b, g["dx"].view(b, T, di), g["dB"], g["dC"], di, G, N,
+                            workspace=wsc)
     return step
 
 

@@ -141,11 +141,14 @@ int mamba2_rmsnorm_gated_fwd(int64_t rows, int64_t width, float eps, int32_t dty
 size_t mamba2_rmsnorm_gated_bwd_workspace_bytes(int64_t rows, int64_t width);
 
 /* RMSNorm-gated backward with the saved inv_rms.  g [rows,width] is the
- * gradient of `out` in `g_dtype`.  Outputs f32: dy, dz [rows,width], dw [width]. */
+ * gradient of `out` in `g_dtype`.  Outputs: dy [rows,width] in `dy_dtype`
+ * (SSD_F32, or SSD_BF16 rounded to nearest even, e.g. to feed ssd_bwd's bf16
+ * path as its dy); dz [rows,width] and dw [width] f32.  dw is a fixed-order
+ * sum of per-32-row partials held in the workspace. */
 int mamba2_rmsnorm_gated_bwd(int64_t rows, int64_t width, int32_t dtype, int32_t g_dtype,
-                             const void* y, const void* z, const float* w, const float* inv_rms,
-                             const void* g, float* dy, float* dz, float* dw, void* workspace,
-                             size_t workspace_bytes, void* stream);
+                             int32_t dy_dtype, const void* y, const void* z, const float* w,
+                             const float* inv_rms, const void* g, void* dy, float* dz, float* dw,
+                             void* workspace, size_t workspace_bytes, void* stream);
 
 /* Description of the last failure on the calling thread ("" after success). */
 const char* ssd_last_error(void);

@@ -59,7 +59,7 @@ def load_library():
     lib.mamba2_rmsnorm_gated_fwd.restype = ctypes.c_int
     lib.mamba2_rmsnorm_gated_bwd_workspace_bytes.argtypes = [i64, i64]
     lib.mamba2_rmsnorm_gated_bwd_workspace_bytes.restype = sz
-    lib.mamba2_rmsnorm_gated_bwd.argtypes = [i64, i64, i32, i32] + [vp] * 8 + [vp, sz, vp]
+    lib.mamba2_rmsnorm_gated_bwd.argtypes = [i64, i64, i32, i32, i32] + [vp] * 8 + [vp, sz, vp]
     lib.mamba2_rmsnorm_gated_bwd.restype = ctypes.c_int
     lib.ssd_last_error.argtypes = []
     lib.ssd_last_error.restype = ctypes.c_char_p
@@ -287,9 +287,9 @@ def rmsnorm_gated_fwd(y, z, w, eps: float = 1e-5, stream=None):
     return out, inv
 
 
-def rmsnorm_gated_bwd(y, z, w, inv_rms, g, workspace=None, stream=None):
+def rmsnorm_gated_bwd(y, z, w, inv_rms, g, workspace=None, stream=None, dy_dtype=torch.float32):
     """Backward of rmsnorm_gated_fwd with the saved inv_rms; returns
-    (dy, dz, dw) in f32."""
+    (dy in dy_dtype, dz f32, dw f32)."""
     lib = load_library()
     width = y.shape[-1]
     rows = y.numel() // width if width else 0
@@ -298,14 +298,15 @@ def rmsnorm_gated_bwd(y, z, w, inv_rms, g, workspace=None, stream=None):
     _need(inv_rms, "inv_rms", tuple(y.shape[:-1]), torch.float32, y.device)
     _need(g, "g", tuple(y.shape), None, y.device)
     f32 = dict(dtype=torch.float32, device=y.device)
-    dy = torch.empty(tuple(y.shape), **f32)
+    dy = torch.empty(tuple(y.shape), dtype=dy_dtype, device=y.device)
     dz = torch.empty(tuple(y.shape), **f32)
     dw = torch.empty((width,), **f32)
     need = lib.mamba2_rmsnorm_gated_bwd_workspace_bytes(rows, width)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=y.device)
     wsz = 0 if workspace is None else workspace.numel()
-    _check(lib.mamba2_rmsnorm_gated_bwd(rows, width, _code(y.dtype), _code(g.dtype), _ptr(y), _ptr(z), _ptr(w),
+    _check(lib.mamba2_rmsnorm_gated_bwd(rows, width, _code(y.dtype), _code(g.dtype), _code(dy_dtype), _ptr(y),
+                                        _ptr(z), _ptr(w),
                                         _ptr(inv_rms), _ptr(g), _ptr(dy), _ptr(dz), _ptr(dw), _ptr(workspace), wsz,
                                         _stream(stream)))
     return dy, dz, dw

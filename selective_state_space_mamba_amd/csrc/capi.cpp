@@ -515,12 +515,14 @@ int mamba2_rmsnorm_gated_fwd(int64_t rows, int64_t width, float eps, int32_t dty
   return ok();
 }
 
-int mamba2_rmsnorm_gated_bwd(int64_t rows, int64_t width, int32_t dtype, int32_t g_dtype, const void* y,
-                             const void* z, const float* w, const float* inv_rms, const void* g, float* dy,
-                             float* dz, float* dw, void* workspace, size_t workspace_bytes, void* stream) {
+int mamba2_rmsnorm_gated_bwd(int64_t rows, int64_t width, int32_t dtype, int32_t g_dtype, int32_t dy_dtype,
+                             const void* y, const void* z, const float* w, const float* inv_rms, const void* g,
+                             void* dy, float* dz, float* dw, void* workspace, size_t workspace_bytes, void* stream) {
   int rc = check_rms(rows, width, dtype);
   if (rc != SSD_OK) return rc;
   if (!valid_dtype(g_dtype)) return fail(SSD_ERR_DTYPE, "rmsnorm_gated_bwd: g_dtype %d is not SSD_F32 or SSD_BF16", g_dtype);
+  if (!valid_dtype(dy_dtype))
+    return fail(SSD_ERR_DTYPE, "rmsnorm_gated_bwd: dy_dtype %d is not SSD_F32 or SSD_BF16", dy_dtype);
   if (!dw) return fail(SSD_ERR_INVALID_ARG, "rmsnorm_gated_bwd: dw is required");
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (rows == 0) {
@@ -537,7 +539,8 @@ int mamba2_rmsnorm_gated_bwd(int64_t rows, int64_t width, int32_t dtype, int32_t
     return fail(SSD_ERR_WORKSPACE, "rmsnorm_gated_bwd: workspace of %zu bytes is smaller than the %zu needed",
                 workspace ? workspace_bytes : 0, need);
   SSD_LAUNCH(ssd::launch_rms_bwd(rows, static_cast<int>(width), static_cast<ssd::DType>(dtype),
-                                 static_cast<ssd::DType>(g_dtype), y, z, w, inv_rms, g, dy, dz, dw,
+                                 static_cast<ssd::DType>(g_dtype), static_cast<ssd::DType>(dy_dtype), y, z, w,
+                                 inv_rms, g, dy, dz, dw,
                                  static_cast<float*>(workspace), st),
              "rmsnorm_gated_bwd");
   return ok();

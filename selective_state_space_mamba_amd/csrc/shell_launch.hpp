@@ -22,8 +22,9 @@ hipError_t launch_conv_bwd(int b, int T, int d_inner, int gn, int K, DType dt, c
 hipError_t launch_rms_fwd(int64_t rows, int width, float eps, DType dt, const void* y, const void* z, const float* w,
                           void* out, float* inv_rms, hipStream_t st);
 // part: [rms_nparts(rows), width] floats of scratch
-hipError_t launch_rms_bwd(int64_t rows, int width, DType dt, DType gt, const void* y, const void* z, const float* w,
-                          const float* inv_rms, const void* g, float* dy, float* dz, float* dw, float* part,
-                          hipStream_t st);
+// dy in `ot` (f32 or bf16); dz, dw f32
+hipError_t launch_rms_bwd(int64_t rows, int width, DType dt, DType gt, DType ot, const void* y, const void* z,
+                          const float* w, const float* inv_rms, const void* g, void* dy, float* dz, float* dw,
+                          float* part, hipStream_t st);
 
 }  // namespace ssd

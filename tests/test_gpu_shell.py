@@ -30,6 +30,8 @@ def conv_case(seed, b, T, d_inner, G, N, K, dtype):
     (3, 129, 48, 1, 8, 1, "f32"),
     (3, 129, 48, 1, 8, 3, "f32"),
     (1, 64, 40, 1, 8, 8, "f32"),
+    (2, 200, 36, 1, 6, 4, "bf16"),   # channel counts not multiples of 8: the scalar kernels
+    (2, 70, 20, 2, 2, 2, "f32"),
     (8, 2048, 3072, 1, 128, 4, "bf16"),  # the block-slice shape
 ])
 def test_conv1d_silu(b, T, d_inner, G, N, K, dtype):
@@ -50,24 +52,30 @@ def test_conv1d_silu(b, T, d_inner, G, N, K, dtype):
     assert all(v <= tol for v in errs.values()), errs
 
 
-@pytest.mark.parametrize("rows,width,dtype,gdtype", [
-    ((3, 5), 64, "f32", "f32"),
-    ((2, 37), 200, "bf16", "f32"),
-    ((1, 1), 4096, "f32", "bf16"),
-    ((8, 2048), 3072, "bf16", "bf16"),  # the block-slice shape
+@pytest.mark.parametrize("rows,width,dtype,gdtype,dydtype", [
+    ((3, 5), 64, "f32", "f32", "f32"),
+    ((2, 37), 200, "bf16", "f32", "f32"),
+    ((2, 37), 200, "bf16", "f32", "bf16"),
+    ((1, 1), 4096, "f32", "bf16", "f32"),     # wider than the vector kernels hold: scalar kernels
+    ((5, 7), 2048, "f32", "f32", "f32"),
+    ((3, 33), 100, "bf16", "bf16", "bf16"),   # width not a multiple of 8: scalar kernels
+    ((8, 2048), 3072, "bf16", "bf16", "f32"),  # the block-slice shape
+    ((8, 2048), 3072, "bf16", "bf16", "bf16"),
 ])
-def test_rmsnorm_gated(rows, width, dtype, gdtype):
+def test_rmsnorm_gated(rows, width, dtype, gdtype, dydtype):
     rng = np.random.default_rng(12)
     y = Stored(rng.standard_normal(rows + (width,)).astype(np.float32), dtype)
     z = Stored(rng.standard_normal(rows + (width,)).astype(np.float32), dtype)
     w = (1.0 + 0.1 * rng.standard_normal(width)).astype(np.float32)
     g = Stored(rng.standard_normal(rows + (width,)).astype(np.float32), gdtype)
     out, inv = ssd.rmsnorm_gated_fwd(dev(y), dev(z), dev(w), 1e-5)
-    dy, dz, dw = ssd.rmsnorm_gated_bwd(dev(y), dev(z), dev(w), inv, dev(g))
+    dy, dz, dw = ssd.rmsnorm_gated_bwd(dev(y), dev(z), dev(w), inv, dev(g),
+                                       dy_dtype=torch.bfloat16 if dydtype == "bf16" else torch.float32)
     torch.cuda.synchronize()
+    assert dy.dtype == (torch.bfloat16 if dydtype == "bf16" else torch.float32)
     rout, rinv = oracle.rmsnorm_fwd(y.values, z.values, w, 1e-5)
     rdy, rdz, rdw = oracle.rmsnorm_bwd(y.values, z.values, w, rinv, g.values)
-    tol = TOL["bf16" if "bf16" in (dtype, gdtype) else "f32"]
+    tol = TOL["bf16" if "bf16" in (dtype, gdtype, dydtype) else "f32"]
     errs = {"out": relerr(host(out), rout), "inv_rms": relerr(host(inv), rinv), "dy": relerr(host(dy), rdy),
             "dz": relerr(host(dz), rdz), "dw": relerr(host(dw), rdw)}
     print("[parity rmsnorm]", errs, flush=True)
@@ -77,7 +85,9 @@ def test_rmsnorm_gated(rows, width, dtype, gdtype):
 def test_block_slice_end_to_end():
     """conv1d+SiLU -> SSD -> RMSNorm-gated forward and the backward through all
     three at the block-slice size, against the oracle chain run in f64 from the
-    same generated inputs (the HIP chain stores its intermediates in bf16)."""
+    same generated inputs.  The HIP chain stores its intermediates in bf16,
+    including the gradient that the RMSNorm backward hands to the SSD backward
+    (so the SSD backward runs its bf16 kernels), exactly as bench.py runs it."""
     cfg = CONFIGS["block"]
     d = make_inputs(cfg)
     b, T, H, P, N, G, Q, di = cfg.batch, cfg.seqlen, cfg.nheads, cfg.headdim, cfg.dstate, cfg.ngroups, cfg.chunk, cfg.d_inner
@@ -87,7 +97,7 @@ def test_block_slice_end_to_end():
     xs, Bs, Cs = ssd.conv1d_silu_fwd(xbc, cw, cb, di, G, N)
     y, _, cs = ssd.ssd_fwd(xs.view(b, T, H, P), dt, A_log, Bs, Cs, D, chunk=Q)
     out, inv = ssd.rmsnorm_gated_fwd(y.view(b, T, di), z, nw, cfg.norm_eps)
-    gy, gz, gw = ssd.rmsnorm_gated_bwd(y.view(b, T, di), z, nw, inv, gout)
+    gy, gz, gw = ssd.rmsnorm_gated_bwd(y.view(b, T, di), z, nw, inv, gout, dy_dtype=torch.bfloat16)
     g = ssd.ssd_bwd(xs.view(b, T, H, P), dt, A_log, Bs, Cs, D, gy.view(b, T, H, P), chunk_states=cs, chunk=Q)
     dxbc, dcw, dcb = ssd.conv1d_silu_bwd(xbc, cw, cb, g["dx"].view(b, T, di), g["dB"], g["dC"], di, G, N)
     torch.cuda.synchronize()
