@@ -144,7 +144,7 @@ size_t mamba2_rmsnorm_gated_bwd_workspace_bytes(int64_t rows, int64_t width);
  * gradient of `out` in `g_dtype`.  Outputs: dy [rows,width] in `dy_dtype`
  * (SSD_F32, or SSD_BF16 rounded to nearest even, e.g. to feed ssd_bwd's bf16
  * path as its dy); dz [rows,width] and dw [width] f32.  dw is a fixed-order
- * sum of per-32-row partials held in the workspace. */
+ * sum of per-64-row partials held in the workspace. */
 int mamba2_rmsnorm_gated_bwd(int64_t rows, int64_t width, int32_t dtype, int32_t g_dtype,
                              int32_t dy_dtype, const void* y, const void* z, const float* w,
                              const float* inv_rms, const void* g, void* dy, float* dz, float* dw,

@@ -11,14 +11,16 @@
 //
 // Vector paths (taken when the x / B / C channel counts are multiples of 8, or
 // the RMSNorm width is): a conv lane owns 8 (forward) or 4 (backward)
-// adjacent channels and walks a 32-step run with a register sliding window,
-// reading 8- or 16-byte pieces of consecutive channels; the four waves of a
-// workgroup take four consecutive runs and add their weight / bias gradient
-// partials in LDS in wave order, so one partial covers 128 steps.  RMSNorm-gated
-// takes one row per wave, holds the row in registers between its reduction and
-// its outputs, and reduces with a wave reduction (no barrier per row).  The
-// scalar kernels (one channel per thread, a row per workgroup) take the other
-// shapes.  Weight gradients are per-(batch, 128-step run) or per-32-row
+// adjacent channels and walks a run of steps (32 forward, 64 backward) with a
+// register sliding window, reading 8- or 16-byte pieces of consecutive
+// channels; in the backward the four waves of a workgroup take four
+// consecutive runs and add their weight / bias gradient partials in LDS in
+// wave order, so one partial covers 256 steps.  RMSNorm-gated takes one row per
+// wave, holds the row in registers between its reduction and its outputs, and
+// reduces with a wave reduction (no barrier per row).  Launch shapes are sized
+// so that the block-slice workload's grids run in one round of resident waves.
+// The scalar kernels (one channel per thread, a row per workgroup) take the
+// other shapes.  Weight gradients are per-(batch, 256-step run) or per-64-row
 // partials summed in a fixed order, so results are bitwise reproducible.
 #include "ssd_common.hpp"
 #include "shell_launch.hpp"
@@ -26,9 +28,10 @@
 namespace ssd {
 
 constexpr int CONV_KMAX = 8;
-constexpr int CONV_RUN = 128;            // steps per weight-gradient partial
-constexpr int CONV_WRUN = CONV_RUN / 4;  // steps per wave in the vector paths
-constexpr int CONV_U = 8;                // steps whose loads are issued together
+constexpr int CONV_RUN = 256;              // steps per weight-gradient partial
+constexpr int CONV_WRUN = CONV_RUN / 4;    // steps per wave in the vector backward
+constexpr int CONV_FRUN = 32;              // steps per wave in the vector forward
+constexpr int CONV_U = 4;                  // steps whose loads are issued together
 
 __device__ __forceinline__ float sigmoidf_(float v) { return 1.f / (1.f + __expf(-v)); }
 
@@ -217,8 +220,8 @@ __global__ __launch_bounds__(256) void conv_bwd_kernel(const TI* __restrict__ xb
   o[K] = accb;
 }
 
-// Vector conv forward.  grid (ceil(conv_dim / (8 * 64)), ceil(T / CONV_RUN), b):
-// lane l owns channels c0 .. c0+7, wave q the steps [CONV_RUN*y + 32q, +32).
+// Vector conv forward.  grid (ceil(conv_dim / (8 * 64)), ceil(T / (4 * CONV_FRUN)), b):
+// lane l owns channels c0 .. c0+7, wave q the steps [4*CONV_FRUN*y + CONV_FRUN*q, +CONV_FRUN).
 template <typename TI, int K>
 __global__ __launch_bounds__(256) void conv_fwd_vec_kernel(const TI* __restrict__ xbc, const float* __restrict__ w,
                                                           const float* __restrict__ bias, TI* __restrict__ x_out,
@@ -226,9 +229,9 @@ __global__ __launch_bounds__(256) void conv_fwd_vec_kernel(const TI* __restrict_
                                                           int Cd, int d_inner, int gn) {
   constexpr int V = 8;
   const int c0 = (blockIdx.x * WAVE + lane_id()) * V;
-  const int t0 = blockIdx.y * CONV_RUN + wave_id() * CONV_WRUN;
+  const int t0 = (blockIdx.y * 4 + wave_id()) * CONV_FRUN;
   if (c0 >= Cd || t0 >= T) return;
-  const int t1 = min(T, t0 + CONV_WRUN);
+  const int t1 = min(T, t0 + CONV_FRUN);
   const int64_t rb = static_cast<int64_t>(blockIdx.z) * T;
   float wk[K][V], bc[V];
   load_taps<V, K>(w, c0, wk);
@@ -276,19 +279,20 @@ __global__ __launch_bounds__(256) void conv_fwd_vec_kernel(const TI* __restrict_
   }
 }
 
-// Vector conv backward, same grid as the forward with 4 channels per lane.
+// Vector conv backward.  grid (ceil(conv_dim / (4 * 64)), ceil(T / CONV_RUN), b):
+// lane l owns channels c0 .. c0+3, wave q the steps [CONV_RUN*y + CONV_WRUN*q, +CONV_WRUN).
 // Lane state over steps u of its run:
 //   xw[m] = xbc[u - (K-1) + m], m = 0 .. 2K-2   (zero outside [0, T))
 //   gw[m] = gp[u + m],          m = 0 .. K-1    (zero at steps >= T)
 // The workgroup's four runs add their tap / bias partials in LDS in wave order
 // and store one partial [b, ceil(T/CONV_RUN), Cd, K+1] as the scalar kernel does.
 template <typename TI, int K>
-__global__ __launch_bounds__(256) void conv_bwd_vec_kernel(const TI* __restrict__ xbc, const float* __restrict__ w,
+__global__ __launch_bounds__(256, K <= 4 ? 4 : 2) void conv_bwd_vec_kernel(const TI* __restrict__ xbc, const float* __restrict__ w,
                                                           const float* __restrict__ bias, const float* __restrict__ dx,
                                                           const float* __restrict__ dB, const float* __restrict__ dC,
                                                           float* __restrict__ dxbc, float* __restrict__ part, int T,
                                                           int Cd, int d_inner, int gn) {
-  constexpr int V = 4;
+  constexpr int V = 4, U = 2;       // two steps of loads in flight keep 4 waves per SIMD at K = 4
   constexpr int NP = V * (K + 1);  // partial values per lane
   __shared__ float red[WAVE * NP];
   const int lane = lane_id(), wv = wave_id();
@@ -340,15 +344,15 @@ __global__ __launch_bounds__(256) void conv_bwd_vec_kernel(const TI* __restrict_
       gload(t0 + m, g);
       gp_of(g, xw + m, gw[m]);
     }
-    for (int u0 = t0; u0 < t1; u0 += CONV_U) {
-      float ng[CONV_U][V], nx[CONV_U][V];
+    for (int u0 = t0; u0 < t1; u0 += U) {
+      float ng[U][V], nx[U][V];
 #pragma unroll
-      for (int u = 0; u < CONV_U; ++u) {
+      for (int u = 0; u < U; ++u) {
         gload(u0 + u + K - 1, ng[u]);
         xload(u0 + u + K, nx[u]);
       }
 #pragma unroll
-      for (int u = 0; u < CONV_U; ++u) {
+      for (int u = 0; u < U; ++u) {
         if (u0 + u >= t1) break;
         gp_of(ng[u], xw + (K - 1), gw[K - 1]);
         float d[V];
@@ -432,7 +436,7 @@ __global__ __launch_bounds__(RED_WAVES * WAVE) void part_reduce_kernel(const flo
 
 // ------------------------------------------------------------ RMSNorm-gated
 
-constexpr int RMS_ROWS = 32;  // rows per workgroup (one dw partial) in the backward
+constexpr int RMS_ROWS = 64;  // rows per workgroup (one dw partial) in the backward
 
 __device__ __forceinline__ float block_sum256(float v, float* tmp) {
   v = wave_sum(v);
@@ -658,7 +662,7 @@ template <typename TI, int K>
 static void conv_fwd_launch(int b, int T, int Cd, int d_inner, int gn, const void* xbc, const float* w,
                             const float* bias, void* x_out, void* B_out, void* C_out, hipStream_t st) {
   if (conv_vec_ok(d_inner, gn)) {
-    dim3 grid((Cd / 8 + WAVE - 1) / WAVE, conv_nruns(T), b);
+    dim3 grid((Cd / 8 + WAVE - 1) / WAVE, (T + 4 * CONV_FRUN - 1) / (4 * CONV_FRUN), b);
     hipLaunchKernelGGL((conv_fwd_vec_kernel<TI, K>), grid, dim3(NTHREADS), 0, st, static_cast<const TI*>(xbc), w,
                        bias, static_cast<TI*>(x_out), static_cast<TI*>(B_out), static_cast<TI*>(C_out), T, Cd, d_inner,
                        gn);
