@@ -3,7 +3,8 @@
 
 One step = ssd_fwd (saving the chunk states) + ssd_bwd (reading them) over one
 batch of synthetic input already resident in HBM; for the block-slice workload
-the step also runs conv1d+SiLU and RMSNorm-gated forward and backward.
+the step also runs the dt activation (softplus of dt_raw + dt_bias), conv1d+SiLU
+and RMSNorm-gated, forward and backward.
 Prints ONE JSON line on stdout (progress goes to stderr).
 
 After the warm-up, an untimed pass of the same number of steps records HIP
@@ -33,7 +34,8 @@ METRIC = "SSD fwd+bwd tokens/sec on 1 MI355X; achieved HBM GB/s and MFMA % of pe
 HBM_PEAK_GBS = 8000.0
 KERNELS_FWD = ["chunk_state_fwd", "chunk_out_fwd"]
 KERNELS_BWD = ["chunk_state_bwd", "chunk_bwd_col", "chunk_bwd_row", "bwd_dt", "bwd_split_sum"]
-KERNELS_SHELL = ["conv1d_silu_fwd", "rmsnorm_gated_fwd", "rmsnorm_gated_bwd", "conv1d_silu_bwd"]
+KERNELS_SHELL = ["dt_softplus_fwd", "conv1d_silu_fwd", "rmsnorm_gated_fwd", "rmsnorm_gated_bwd", "conv1d_silu_bwd",
+                 "dt_softplus_bwd"]
 KERNEL_SOURCES = {
     "chunk_state_fwd": ["ssd_state.hip", "ssd_state_bf16.hip", "ssd_async.hpp", "ssd_common.hpp"],
     "chunk_state_bwd": ["ssd_state.hip", "ssd_state_bf16.hip", "ssd_async.hpp", "ssd_common.hpp"],
@@ -221,6 +223,7 @@ def make_step(cfg, d):
         return step
 
     xbc, z, gout = to_dev(d["xBC"]), to_dev(d["z"]), to_dev(d["gout"])
+    dt_raw, dt_bias = to_dev(d["dt_raw"]), to_dev(d["dt_bias"])
     conv_w, conv_b, norm_w = to_dev(d["conv_w"]), to_dev(d["conv_b"]), to_dev(d["norm_w"])
     di = cfg.d_inner
     lib = ssd.load_library()
@@ -231,8 +234,11 @@ def make_step(cfg, d):
     wsb = torch.empty(max(1, ssd.ssd_workspace_bytes(prob, True, True)), **u8)
     wsr = torch.empty(max(1, lib.mamba2_rmsnorm_gated_bwd_workspace_bytes(b * T, di)), **u8)
     wsc = torch.empty(max(1, lib.mamba2_conv1d_silu_bwd_workspace_bytes(b, T, di, G, N, K)), **u8)
+    wsd = torch.empty(max(1, lib.ssd_dt_softplus_bwd_workspace_bytes(b * T, H)), **u8)
+    dt = torch.empty_like(dt_raw)
 
     def step():
+        ssd.dt_softplus_fwd(dt_raw, dt_bias, out=dt)
         xs, Bs, Cs = ssd.conv1d_silu_fwd(xbc, conv_w, conv_b, di, G, N)
         xs = xs.view(b, T, H, P)
         y, _, cs = ssd.ssd_fwd(xs, dt, A_log, Bs, Cs, D, h0, chunk=Q, out=fo, workspace=wsf)
@@ -243,6 +249,7 @@ def make_step(cfg, d):
                         workspace=wsb)
         ssd.conv1d_silu_bwd(xbc, conv_w, conv_b, g["dx"].view(b, T, di), g["dB"], g["dC"], di, G, N,
                             workspace=wsc)
+        ssd.dt_softplus_bwd(dt_raw, dt_bias, g["ddt"], workspace=wsd)
     return step
 
 

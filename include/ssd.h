@@ -18,6 +18,8 @@
  *                             block backward's conv / SiLU tap loop.
  *   mamba2_rmsnorm_gated_*    rmsnorm_gated_{forward,backward}_from_inv_rms with
  *                             inv_rms = 1/sqrt(mean(y^2) + eps).
+ *   ssd_dt_softplus_*         dt = softplus(dt_raw + dt_bias) in front of the core
+ *                             and its gradient (dt_pre, grad_dt_pre, grad_dt_bias).
  *
  * Conventions (all entry points):
  *  - Every tensor pointer is a DEVICE pointer owned by the caller; the library
@@ -150,6 +152,26 @@ int mamba2_rmsnorm_gated_bwd(int64_t rows, int64_t width, int32_t dtype, int32_t
                              const float* inv_rms, const void* g, void* dy, float* dz, float* dw,
                              void* workspace, size_t workspace_bytes, void* stream);
 
+/* dt activation in front of the core (page 1, tensorized_mamba2_backward_impl:
+ * dt_pre = dt_raw + dt_bias, dt = softplus(dt_pre) with beta 1; after the fused
+ * backward, grad_dt_pre = grad_dt * sigmoid(dt_pre) and grad_dt_bias is its sum
+ * over batch and time).  Rows are the b*T steps of [b,T,nheads] arrays.
+ *   ssd_dt_softplus_fwd: dt_raw, dt [rows,nheads] in `dtype` (bf16 output is
+ *     rounded to nearest even, the form ssd_fwd / ssd_bwd read); dt_bias
+ *     [nheads] f32.  dt may be passed to ssd_fwd and ssd_bwd as their dt.
+ *   ssd_dt_softplus_bwd: ddt [rows,nheads] f32 is ssd_bwd's gradient of dt;
+ *     outputs f32 ddt_raw [rows,nheads] (the gradient of dt_raw, equal to that
+ *     of dt_pre) and d_dt_bias [nheads], a fixed-order sum of per-64-row
+ *     partials held in the workspace.
+ * softplus(v) is evaluated as max(v,0) + log1p(exp(-|v|)).  Pointers are
+ * 16-byte aligned device pointers; errors as for ssd_fwd. */
+int ssd_dt_softplus_fwd(int64_t rows, int64_t nheads, int32_t dtype, const void* dt_raw,
+                        const float* dt_bias, void* dt, void* stream);
+size_t ssd_dt_softplus_bwd_workspace_bytes(int64_t rows, int64_t nheads);
+int ssd_dt_softplus_bwd(int64_t rows, int64_t nheads, int32_t dtype, const void* dt_raw,
+                        const float* dt_bias, const float* ddt, float* ddt_raw, float* d_dt_bias,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
 /* Description of the last failure on the calling thread ("" after success). */
 const char* ssd_last_error(void);
 
@@ -164,7 +186,8 @@ const char* ssd_version(void);
  * "chunk_state_fwd", "chunk_out_fwd", "chunk_state_fwd (recompute)",
  * "chunk_state_bwd", "chunk_bwd_col", "chunk_bwd_row", "bwd_dt", "bwd_split_sum",
  * "conv1d_silu_fwd", "conv1d_silu_bwd", "rmsnorm_gated_fwd",
- * "rmsnorm_gated_bwd".  Not for use while other threads call the library. */
+ * "rmsnorm_gated_bwd", "dt_softplus_fwd", "dt_softplus_bwd".  Not for use
+ * while other threads call the library. */
 int ssd_profile_enable(int on);
 /* Restrict recording to one kernel name (NULL or "" records every kernel), so
  * that the events of the others do not hold up the stream while one kernel is

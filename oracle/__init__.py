@@ -14,6 +14,10 @@ burn_dragon_kernel 0.5.0 page "src/sequence/mamba2/backward.rs":
   ssd_bwd   -> ssd_backward_reference (reverse-time loop) + d(initial state)
   conv_fwd/conv_bwd -> depthwise_conv_preact_with_history, silu, conv tap loop
   rmsnorm_fwd/rmsnorm_bwd -> rmsnorm_gated_{forward,backward}_from_inv_rms
+  dt_softplus_fwd/dt_softplus_bwd -> the dt_pre / softplus lines of
+               tensorized_mamba2_backward_impl and the grad_dt_pre /
+               grad_dt_bias lines after its fused backward (elementwise, so
+               written here in numpy float64)
 
 Parity pins (tests/test_oracle_*.py): the dual quadratic form of the forward,
 central finite differences of every gradient, the A->0 and T=1 closed forms,
@@ -175,3 +179,21 @@ def rmsnorm_bwd(y, z, w, inv_rms, g):
     if rc != 0:
         raise ValueError("rmsnorm_oracle_bwd failed")
     return dy, dz, dw
+
+
+def dt_softplus_fwd(dt_raw, dt_bias):
+    """dt = softplus(dt_raw + dt_bias) with beta 1, i.e. log(1 + e^v), over
+    [..., H] (page 1: dt_pre = dt_raw + dt_bias, dt = softplus(dt_pre, 1.0)).
+    np.logaddexp(0, v) is log(e^0 + e^v), the same function, without overflow."""
+    v = _f64(dt_raw) + _f64(dt_bias)
+    return np.logaddexp(0.0, v)
+
+
+def dt_softplus_bwd(dt_raw, dt_bias, ddt):
+    """Gradient through dt_softplus_fwd (page 1: grad_dt_pre = grad_dt *
+    sigmoid(dt_pre); grad_dt_bias sums it over batch and time; grad_dt_raw is
+    grad_dt_pre).  Returns (ddt_raw [..., H], d_dt_bias [H])."""
+    v = _f64(dt_raw) + _f64(dt_bias)
+    g = _f64(ddt) / (1.0 + np.exp(-v))
+    H = g.shape[-1]
+    return g, g.reshape(-1, H).sum(axis=0)

@@ -1,5 +1,6 @@
 """MI355X (gfx950) Mamba-2 SSD core: forward and analytic backward, plus the
-conv1d+SiLU and RMSNorm-gated block-shell ops.
+conv1d+SiLU and RMSNorm-gated block-shell ops and the dt activation
+(softplus of dt_raw + dt_bias) in front of the core.
 
 Thin Python binding over the C ABI in include/ssd.h (libssd_mi355x.so, built
 by ``selective_state_space_mamba_amd.build``).  The binding only marshals
@@ -12,6 +13,8 @@ from ._binding import (  # noqa: F401
     SSDError,
     conv1d_silu_bwd,
     conv1d_silu_fwd,
+    dt_softplus_bwd,
+    dt_softplus_fwd,
     library_path,
     load_library,
     profile_enable,

@@ -61,6 +61,12 @@ def load_library():
     lib.mamba2_rmsnorm_gated_bwd_workspace_bytes.restype = sz
     lib.mamba2_rmsnorm_gated_bwd.argtypes = [i64, i64, i32, i32, i32] + [vp] * 8 + [vp, sz, vp]
     lib.mamba2_rmsnorm_gated_bwd.restype = ctypes.c_int
+    lib.ssd_dt_softplus_fwd.argtypes = [i64, i64, i32] + [vp] * 3 + [vp]
+    lib.ssd_dt_softplus_fwd.restype = ctypes.c_int
+    lib.ssd_dt_softplus_bwd_workspace_bytes.argtypes = [i64, i64]
+    lib.ssd_dt_softplus_bwd_workspace_bytes.restype = sz
+    lib.ssd_dt_softplus_bwd.argtypes = [i64, i64, i32] + [vp] * 5 + [vp, sz, vp]
+    lib.ssd_dt_softplus_bwd.restype = ctypes.c_int
     lib.ssd_last_error.argtypes = []
     lib.ssd_last_error.restype = ctypes.c_char_p
     lib.ssd_version.argtypes = []
@@ -310,3 +316,40 @@ def rmsnorm_gated_bwd(y, z, w, inv_rms, g, workspace=None, stream=None, dy_dtype
                                         _ptr(inv_rms), _ptr(g), _ptr(dy), _ptr(dz), _ptr(dw), _ptr(workspace), wsz,
                                         _stream(stream)))
     return dy, dz, dw
+
+
+def dt_softplus_fwd(dt_raw, dt_bias, out=None, stream=None):
+    """dt = softplus(dt_raw + dt_bias) over [..., H] in dt_raw's dtype (the form
+    ssd_fwd / ssd_bwd take as dt)."""
+    lib = load_library()
+    H = dt_raw.shape[-1]
+    rows = dt_raw.numel() // H if H else 0
+    _need(dt_raw, "dt_raw", tuple(dt_raw.shape), None, dt_raw.device)
+    _need(dt_bias, "dt_bias", (H,), torch.float32, dt_raw.device)
+    dt = torch.empty_like(dt_raw) if out is None else out
+    _need(dt, "out", tuple(dt_raw.shape), dt_raw.dtype, dt_raw.device)
+    _check(lib.ssd_dt_softplus_fwd(rows, H, _code(dt_raw.dtype), _ptr(dt_raw), _ptr(dt_bias), _ptr(dt),
+                                   _stream(stream)))
+    return dt
+
+
+def dt_softplus_bwd(dt_raw, dt_bias, ddt, workspace=None, out=None, stream=None):
+    """Backward of dt_softplus_fwd: returns (ddt_raw f32 [..., H], d_dt_bias f32 [H])
+    from ddt, the gradient of dt that ssd_bwd returns."""
+    lib = load_library()
+    H = dt_raw.shape[-1]
+    rows = dt_raw.numel() // H if H else 0
+    _need(dt_raw, "dt_raw", tuple(dt_raw.shape), None, dt_raw.device)
+    _need(dt_bias, "dt_bias", (H,), torch.float32, dt_raw.device)
+    _need(ddt, "ddt", tuple(dt_raw.shape), torch.float32, dt_raw.device)
+    f32 = dict(dtype=torch.float32, device=dt_raw.device)
+    if out is None:
+        out = (torch.empty(tuple(dt_raw.shape), **f32), torch.empty((H,), **f32))
+    ddt_raw, d_bias = out
+    need = lib.ssd_dt_softplus_bwd_workspace_bytes(rows, H)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dt_raw.device)
+    wsz = 0 if workspace is None else workspace.numel()
+    _check(lib.ssd_dt_softplus_bwd(rows, H, _code(dt_raw.dtype), _ptr(dt_raw), _ptr(dt_bias), _ptr(ddt),
+                                   _ptr(ddt_raw), _ptr(d_bias), _ptr(workspace), wsz, _stream(stream)))
+    return ddt_raw, d_bias

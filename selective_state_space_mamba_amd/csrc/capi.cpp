@@ -546,4 +546,62 @@ int mamba2_rmsnorm_gated_bwd(int64_t rows, int64_t width, int32_t dtype, int32_t
   return ok();
 }
 
+// ------------------------------------------------------------ dt activation
+
+static int check_dt(int64_t rows, int64_t nheads, int32_t dtype) {
+  if (!valid_dtype(dtype)) return fail(SSD_ERR_DTYPE, "dt_softplus: dtype %d is not SSD_F32 or SSD_BF16", dtype);
+  if (rows < 0 || nheads <= 0) return fail(SSD_ERR_INVALID_ARG, "dt_softplus: rows >= 0 and nheads > 0 required");
+  if (nheads > (int64_t(1) << 20) || rows > (int64_t(1) << 40) / nheads)
+    return fail(SSD_ERR_SHAPE, "dt_softplus: rows x nheads is too large");
+  return SSD_OK;
+}
+
+int ssd_dt_softplus_fwd(int64_t rows, int64_t nheads, int32_t dtype, const void* dt_raw, const float* dt_bias,
+                        void* dt, void* stream) {
+  int rc = check_dt(rows, nheads, dtype);
+  if (rc != SSD_OK) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (rows == 0) return ok();
+  if (!dt_raw || !dt_bias || !dt)
+    return fail(SSD_ERR_INVALID_ARG, "dt_softplus_fwd: dt_raw, dt_bias and dt are required");
+  const void* ptrs[] = {dt_raw, dt_bias, dt};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return fail(SSD_ERR_ALIGN, "dt_softplus_fwd: a tensor pointer is not 16-byte aligned");
+  SSD_LAUNCH(ssd::launch_dt_softplus_fwd(rows, static_cast<int>(nheads), static_cast<ssd::DType>(dtype), dt_raw,
+                                         dt_bias, dt, st),
+             "dt_softplus_fwd");
+  return ok();
+}
+
+size_t ssd_dt_softplus_bwd_workspace_bytes(int64_t rows, int64_t nheads) {
+  if (check_dt(rows, nheads, SSD_F32) != SSD_OK || rows == 0) return 0;
+  return align_up(sizeof(float) * static_cast<size_t>(ssd::dt_nparts(rows)) * nheads);
+}
+
+int ssd_dt_softplus_bwd(int64_t rows, int64_t nheads, int32_t dtype, const void* dt_raw, const float* dt_bias,
+                        const float* ddt, float* ddt_raw, float* d_dt_bias, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  int rc = check_dt(rows, nheads, dtype);
+  if (rc != SSD_OK) return rc;
+  if (!d_dt_bias) return fail(SSD_ERR_INVALID_ARG, "dt_softplus_bwd: d_dt_bias is required");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (rows == 0) {
+    SSD_LAUNCH(ssd::launch_fill(d_dt_bias, nheads, 0.f, st), "fill");
+    return ok();
+  }
+  if (!dt_raw || !dt_bias || !ddt || !ddt_raw)
+    return fail(SSD_ERR_INVALID_ARG, "dt_softplus_bwd: dt_raw, dt_bias, ddt and ddt_raw are required");
+  const void* ptrs[] = {dt_raw, dt_bias, ddt, ddt_raw, d_dt_bias, workspace};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return fail(SSD_ERR_ALIGN, "dt_softplus_bwd: a pointer is not 16-byte aligned");
+  const size_t need = ssd_dt_softplus_bwd_workspace_bytes(rows, nheads);
+  if (!workspace || workspace_bytes < need)
+    return fail(SSD_ERR_WORKSPACE, "dt_softplus_bwd: workspace of %zu bytes is smaller than the %zu needed",
+                workspace ? workspace_bytes : 0, need);
+  SSD_LAUNCH(ssd::launch_dt_softplus_bwd(rows, static_cast<int>(nheads), static_cast<ssd::DType>(dtype), dt_raw,
+                                         dt_bias, ddt, ddt_raw, d_dt_bias, static_cast<float*>(workspace), st),
+             "dt_softplus_bwd");
+  return ok();
+}
+
 }  // extern "C"

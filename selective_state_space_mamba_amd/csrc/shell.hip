@@ -648,6 +648,68 @@ __global__ __launch_bounds__(RMS_VEC_WAVES * WAVE) void rms_bwd_vec_kernel(
   for (int i = threadIdx.x; i < width; i += NT) part[static_cast<int64_t>(blockIdx.x) * width + i] = red[i];
 }
 
+// ------------------------------------------------------------ dt activation
+//
+// dt = softplus(dt_raw + dt_bias[h]) with beta 1, and its backward
+// ddt_raw = ddt * sigmoid(dt_raw + dt_bias[h]), d_dt_bias[h] = sum over rows of
+// ddt_raw, following the dt_pre / softplus lines of tensorized_mamba2_backward_impl
+// and the grad_dt_pre / grad_dt_bias lines after the fused backward on page 1
+// (burn_dragon_kernel mamba2/backward.rs).  softplus(v) = log(1 + e^v) is
+// evaluated as max(v, 0) + log1p(e^-|v|), the same function without overflow.
+// Rows are the b*T steps of a [b, T, H] array.
+
+constexpr int DT_ROWS = 64;  // rows per workgroup (one d_dt_bias partial) in the backward
+
+__device__ __forceinline__ float softplus1(float v) { return fmaxf(v, 0.f) + log1pf(expf(-fabsf(v))); }
+
+template <typename T>
+__global__ __launch_bounds__(256) void dt_softplus_fwd_kernel(const T* __restrict__ raw,
+                                                             const float* __restrict__ bias, T* __restrict__ dt,
+                                                             int64_t n, int H) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= n) return;
+  store_f(dt, i, softplus1(load_f(raw, i) + bias[i % H]));
+}
+
+// grid ceil(rows / DT_ROWS), 256 threads: thread t takes head h = hb + t % hpb
+// and rows r0 + t / hpb + k * (256 / hpb); the row lanes of a head are added in
+// LDS in lane order.  part: [gridDim.x, H].
+template <typename T>
+__global__ __launch_bounds__(256) void dt_softplus_bwd_kernel(const T* __restrict__ raw,
+                                                             const float* __restrict__ bias,
+                                                             const float* __restrict__ ddt,
+                                                             float* __restrict__ ddt_raw, float* __restrict__ part,
+                                                             int64_t rows, int H) {
+  __shared__ float red[256];
+  const int tid = threadIdx.x;
+  const int hpb = H < 256 ? H : 256;  // heads per pass
+  const int S = 256 / hpb;            // row lanes per head
+  const int hi = tid % hpb, s = tid / hpb;
+  const int64_t r0 = static_cast<int64_t>(blockIdx.x) * DT_ROWS;
+  const int64_t r1 = r0 + DT_ROWS < rows ? r0 + DT_ROWS : rows;
+  for (int hb = 0; hb < H; hb += hpb) {
+    const int h = hb + hi;
+    float acc = 0.f;
+    if (s < S && h < H) {
+      const float bh = bias[h];
+      for (int64_t r = r0 + s; r < r1; r += S) {
+        const int64_t i = r * H + h;
+        const float g = ddt[i] / (1.f + expf(-(load_f(raw, i) + bh)));
+        ddt_raw[i] = g;
+        acc += g;
+      }
+    }
+    red[tid] = acc;
+    __syncthreads();
+    if (tid < hpb && hb + tid < H) {
+      float sum = 0.f;
+      for (int q = 0; q < S; ++q) sum += red[q * hpb + tid];
+      part[static_cast<int64_t>(blockIdx.x) * H + hb + tid] = sum;
+    }
+    __syncthreads();
+  }
+}
+
 // ---------------------------------------------------------------- launchers
 
 int conv_nruns(int T) { return (T + CONV_RUN - 1) / CONV_RUN; }
@@ -823,6 +885,36 @@ hipError_t launch_rms_bwd(int64_t rows, int width, DType dt, DType gt, DType ot,
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   launch_part_reduce(part, dw, nullptr, rms_nparts(rows), width, 0, st);
+  return hipGetLastError();
+}
+
+int dt_nparts(int64_t rows) { return static_cast<int>((rows + DT_ROWS - 1) / DT_ROWS); }
+
+hipError_t launch_dt_softplus_fwd(int64_t rows, int H, DType dt, const void* raw, const float* bias, void* out,
+                                  hipStream_t st) {
+  const int64_t n = rows * H;
+  const dim3 grid(static_cast<unsigned>((n + 255) / 256));
+  if (dt == BF16)
+    hipLaunchKernelGGL(dt_softplus_fwd_kernel<uint16_t>, grid, dim3(256), 0, st, static_cast<const uint16_t*>(raw),
+                       bias, static_cast<uint16_t*>(out), n, H);
+  else
+    hipLaunchKernelGGL(dt_softplus_fwd_kernel<float>, grid, dim3(256), 0, st, static_cast<const float*>(raw), bias,
+                       static_cast<float*>(out), n, H);
+  return hipGetLastError();
+}
+
+hipError_t launch_dt_softplus_bwd(int64_t rows, int H, DType dt, const void* raw, const float* bias, const float* ddt,
+                                  float* ddt_raw, float* d_bias, float* part, hipStream_t st) {
+  const dim3 grid(dt_nparts(rows));
+  if (dt == BF16)
+    hipLaunchKernelGGL(dt_softplus_bwd_kernel<uint16_t>, grid, dim3(256), 0, st, static_cast<const uint16_t*>(raw),
+                       bias, ddt, ddt_raw, part, rows, H);
+  else
+    hipLaunchKernelGGL(dt_softplus_bwd_kernel<float>, grid, dim3(256), 0, st, static_cast<const float*>(raw), bias,
+                       ddt, ddt_raw, part, rows, H);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  launch_part_reduce(part, d_bias, nullptr, dt_nparts(rows), H, 0, st);
   return hipGetLastError();
 }
 

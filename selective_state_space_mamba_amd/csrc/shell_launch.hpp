@@ -27,4 +27,12 @@ hipError_t launch_rms_bwd(int64_t rows, int width, DType dt, DType gt, DType ot,
                           const float* w, const float* inv_rms, const void* g, void* dy, float* dz, float* dw,
                           float* part, hipStream_t st);
 
+// dt = softplus(raw + bias[h]) over rows x H, in `dt` (f32 or bf16)
+int dt_nparts(int64_t rows);
+hipError_t launch_dt_softplus_fwd(int64_t rows, int H, DType dt, const void* raw, const float* bias, void* out,
+                                  hipStream_t st);
+// part: [dt_nparts(rows), H] floats of scratch
+hipError_t launch_dt_softplus_bwd(int64_t rows, int H, DType dt, const void* raw, const float* bias, const float* ddt,
+                                  float* ddt_raw, float* d_bias, float* part, hipStream_t st);
+
 }  // namespace ssd

@@ -137,7 +137,9 @@ def make_inputs(cfg: SSDConfig, seed: Optional[int] = None) -> Dict[str, object]
     """Draw one workload.  Returns a dict of Stored activations and f32 params.
 
     Keys: x [b,T,H,P], dt [b,T,H], B, C [b,T,G,N], dy [b,T,H,P] (Stored);
-    A_log, D [H], dt_bias [H], h0 [b,H,P,N] or None (f32 numpy).
+    A_log, D [H], dt_bias [H], h0 [b,H,P,N] or None (f32 numpy); dt_raw
+    [b,T,H] (Stored), the N(0,1) draw that dt is the softplus of after adding
+    dt_bias.
     Shell workloads add xBC [b,T,conv_dim], z [b,T,d_inner], gout [b,T,d_inner]
     (Stored) and conv_w [conv_dim,d_conv], conv_b [conv_dim], norm_w [d_inner]
     (f32).  For shell workloads x, B, C, dy are still drawn (same order) so the
@@ -161,6 +163,7 @@ def make_inputs(cfg: SSDConfig, seed: Optional[int] = None) -> Dict[str, object]
         x=Stored(x, cfg.dtype), B=Stored(Bm, cfg.dtype), C=Stored(Cm, cfg.dtype),
         dt=Stored(dt, cfg.dtype), dy=Stored(dy, cfg.dtype),
         A_log=A_log, D=D, dt_bias=dt_bias, h0=h0,
+        dt_raw=Stored(dt_noise, cfg.dtype),  # the pre-activation, for the fused dt activation
     )
     if cfg.shell:
         cd, di, K = cfg.conv_dim, cfg.d_inner, cfg.d_conv

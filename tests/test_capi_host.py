@@ -31,7 +31,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("ssd_fwd", "ssd_bwd", "ssd_workspace_bytes", "ssd_last_error", "mamba2_conv1d_silu_fwd",
-              "mamba2_conv1d_silu_bwd", "mamba2_rmsnorm_gated_fwd", "mamba2_rmsnorm_gated_bwd"):
+              "mamba2_conv1d_silu_bwd", "mamba2_rmsnorm_gated_fwd", "mamba2_rmsnorm_gated_bwd",
+              "ssd_dt_softplus_fwd", "ssd_dt_softplus_bwd", "ssd_dt_softplus_bwd_workspace_bytes"):
         assert n in names
 
 
@@ -147,6 +148,20 @@ def test_shell_argument_checks(lib):
     assert lib.mamba2_rmsnorm_gated_bwd(100, 64, 0, 0, 0, f, f, f, f, f, f, f, f, f, need - 1, None) == -4
     assert lib.mamba2_rmsnorm_gated_bwd(100, 64, 0, 0, 7, f, f, f, f, f, f, f, f, f, need, None) == -3
     assert lib.mamba2_conv1d_silu_bwd_workspace_bytes(2, 300, 64, 1, 16, 4) > 0
+
+
+def test_dt_softplus_argument_checks(lib):
+    f = ctypes.c_void_p(FAKE)
+    lib.ssd_dt_softplus_bwd_workspace_bytes.restype = ctypes.c_size_t
+    i64 = ctypes.c_int64
+    assert lib.ssd_dt_softplus_fwd(i64(10), i64(4), 3, f, f, f, None) == -3      # unknown dtype
+    assert lib.ssd_dt_softplus_fwd(i64(10), i64(0), 0, f, f, f, None) == -1      # no heads
+    assert lib.ssd_dt_softplus_fwd(i64(10), i64(4), 0, f, None, f, None) == -1   # bias required
+    assert lib.ssd_dt_softplus_fwd(i64(10), i64(4), 0, ctypes.c_void_p(FAKE + 4), f, f, None) == -6
+    need = lib.ssd_dt_softplus_bwd_workspace_bytes(i64(100), i64(4))
+    assert need >= 2 * 4 * 4  # two 64-row partials of 4 heads
+    assert lib.ssd_dt_softplus_bwd(i64(100), i64(4), 0, f, f, f, f, f, f, ctypes.c_size_t(need - 1), None) == -4
+    assert lib.ssd_dt_softplus_bwd(i64(100), i64(4), 0, f, f, f, f, None, f, ctypes.c_size_t(need), None) == -1
 
 
 def test_product_path_does_not_import_the_oracle():

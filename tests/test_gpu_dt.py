@@ -1,0 +1,72 @@
+"""GPU parity of the dt activation in front of the core (dt = softplus(dt_raw +
+dt_bias) and its gradient) against the oracle, alone and chained with the SSD
+forward and backward on the grouped bf16 workload."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import selective_state_space_mamba_amd as ssd
+from ssd_inputs import CONFIGS, Stored, make_inputs
+from tests.gpu_util import TOL, dev, host, relerr
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("shape,dtype", [
+    ((1, 1, 1), "f32"),
+    ((2, 37, 7), "f32"),       # rows not a multiple of the 64-row partial, odd heads
+    ((3, 100, 300), "f32"),    # more heads than one pass of 256 threads
+    ((4, 2048, 32), "bf16"),   # the grouped workload's dt
+    ((8, 2048, 48), "bf16"),   # the block slice's dt
+])
+def test_dt_softplus(shape, dtype):
+    rng = np.random.default_rng(31)
+    H = shape[-1]
+    raw = Stored((3.0 * rng.standard_normal(shape)).astype(np.float32), dtype)
+    bias = rng.uniform(-4.0, -2.0, H).astype(np.float32)
+    ddt = rng.standard_normal(shape).astype(np.float32)
+    dt = ssd.dt_softplus_fwd(dev(raw), dev(bias))
+    g_raw, g_bias = ssd.dt_softplus_bwd(dev(raw), dev(bias), dev(ddt))
+    g_raw2, g_bias2 = ssd.dt_softplus_bwd(dev(raw), dev(bias), dev(ddt))
+    torch.cuda.synchronize()
+    r_dt = oracle.dt_softplus_fwd(raw.values, bias)
+    r_raw, r_bias = oracle.dt_softplus_bwd(raw.values, bias, ddt)
+    errs = {"dt": relerr(host(dt), r_dt), "ddt_raw": relerr(host(g_raw), r_raw), "d_dt_bias": relerr(host(g_bias), r_bias)}
+    print("[parity dt_softplus]", shape, dtype, errs, flush=True)
+    # dt is stored in the activation dtype: bf16 output carries its rounding
+    assert errs["dt"] <= TOL[dtype]
+    assert errs["ddt_raw"] <= TOL["f32"] and errs["d_dt_bias"] <= TOL["f32"], errs
+    assert torch.equal(g_bias, g_bias2) and torch.equal(g_raw, g_raw2)
+
+
+def test_dt_softplus_empty():
+    bias = torch.randn(5, device="cuda")
+    raw = torch.empty((0, 5), device="cuda")
+    ddt_raw, d_bias = ssd.dt_softplus_bwd(raw, bias, torch.empty((0, 5), device="cuda"))
+    torch.cuda.synchronize()
+    assert ddt_raw.shape == (0, 5) and torch.equal(d_bias, torch.zeros(5, device="cuda"))
+
+
+def test_dt_activation_chained_with_the_core():
+    """dt_raw, dt_bias -> dt -> ssd_fwd -> ssd_bwd -> (ddt_raw, d_dt_bias) on the
+    grouped bf16 workload, against the oracle chain in f64."""
+    cfg = CONFIGS["grouped"]
+    d = make_inputs(cfg)
+    x, B, C, A_log, D, dy = (dev(d[k]) for k in ("x", "B", "C", "A_log", "D", "dy"))
+    raw, bias = dev(d["dt_raw"]), dev(d["dt_bias"])
+    dt = ssd.dt_softplus_fwd(raw, bias)
+    y, _, cs = ssd.ssd_fwd(x, dt, A_log, B, C, D, chunk=cfg.chunk)
+    g = ssd.ssd_bwd(x, dt, A_log, B, C, D, dy, chunk_states=cs, chunk=cfg.chunk)
+    g_raw, g_bias = ssd.dt_softplus_bwd(raw, bias, g["ddt"])
+    torch.cuda.synchronize()
+    r_dt = oracle.dt_softplus_fwd(d["dt_raw"].values, d["dt_bias"])
+    args = (d["x"].values, r_dt, d["A_log"], d["B"].values, d["C"].values, d["D"])
+    ry = oracle.ssd_fwd(*args)["y"]
+    rg = oracle.ssd_bwd(*args, d["dy"].values)
+    r_raw, r_bias = oracle.dt_softplus_bwd(d["dt_raw"].values, d["dt_bias"], rg["ddt"])
+    errs = {"y": relerr(host(y), ry), "dx": relerr(host(g["dx"]), rg["dx"]),
+            "dA_log": relerr(host(g["dA_log"]), rg["dA_log"]),
+            "ddt_raw": relerr(host(g_raw), r_raw), "d_dt_bias": relerr(host(g_bias), r_bias)}
+    print("[parity dt chain]", {k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
+    assert all(v <= TOL["bf16"] for v in errs.values()), errs

@@ -83,8 +83,8 @@ def test_rmsnorm_gated(rows, width, dtype, gdtype, dydtype):
 
 
 def test_block_slice_end_to_end():
-    """conv1d+SiLU -> SSD -> RMSNorm-gated forward and the backward through all
-    three at the block-slice size, against the oracle chain run in f64 from the
+    """dt activation and conv1d+SiLU -> SSD -> RMSNorm-gated forward and the
+    backward through all of them at the block-slice size, against the oracle chain run in f64 from the
     same generated inputs.  The HIP chain stores its intermediates in bf16,
     including the gradient that the RMSNorm backward hands to the SSD backward
     (so the SSD backward runs its bf16 kernels), exactly as bench.py runs it."""
@@ -93,29 +93,35 @@ def test_block_slice_end_to_end():
     b, T, H, P, N, G, Q, di = cfg.batch, cfg.seqlen, cfg.nheads, cfg.headdim, cfg.dstate, cfg.ngroups, cfg.chunk, cfg.d_inner
     xbc, z, gout = dev(d["xBC"]), dev(d["z"]), dev(d["gout"])
     cw, cb, nw = dev(d["conv_w"]), dev(d["conv_b"]), dev(d["norm_w"])
-    dt, A_log, D = dev(d["dt"]), dev(d["A_log"]), dev(d["D"])
+    A_log, D = dev(d["A_log"]), dev(d["D"])
+    raw, bias = dev(d["dt_raw"]), dev(d["dt_bias"])
+    dt = ssd.dt_softplus_fwd(raw, bias)
     xs, Bs, Cs = ssd.conv1d_silu_fwd(xbc, cw, cb, di, G, N)
     y, _, cs = ssd.ssd_fwd(xs.view(b, T, H, P), dt, A_log, Bs, Cs, D, chunk=Q)
     out, inv = ssd.rmsnorm_gated_fwd(y.view(b, T, di), z, nw, cfg.norm_eps)
     gy, gz, gw = ssd.rmsnorm_gated_bwd(y.view(b, T, di), z, nw, inv, gout, dy_dtype=torch.bfloat16)
     g = ssd.ssd_bwd(xs.view(b, T, H, P), dt, A_log, Bs, Cs, D, gy.view(b, T, H, P), chunk_states=cs, chunk=Q)
     dxbc, dcw, dcb = ssd.conv1d_silu_bwd(xbc, cw, cb, g["dx"].view(b, T, di), g["dB"], g["dC"], di, G, N)
+    g_raw, g_bias = ssd.dt_softplus_bwd(raw, bias, g["ddt"])
     torch.cuda.synchronize()
 
     _, act = oracle.conv_fwd(d["xBC"].values, d["conv_w"], d["conv_b"])
     rx = act[..., :di].reshape(b, T, H, P)
     rB = act[..., di:di + G * N].reshape(b, T, G, N)
     rC = act[..., di + G * N:].reshape(b, T, G, N)
-    sargs = (rx, d["dt"].values, d["A_log"], rB, rC, d["D"])
+    r_dt = oracle.dt_softplus_fwd(d["dt_raw"].values, d["dt_bias"])
+    sargs = (rx, r_dt, d["A_log"], rB, rC, d["D"])
     ry = oracle.ssd_fwd(*sargs)["y"].reshape(b, T, di)
     rout, rinv = oracle.rmsnorm_fwd(ry, d["z"].values, d["norm_w"], cfg.norm_eps)
     rgy, rgz, rgw = oracle.rmsnorm_bwd(ry, d["z"].values, d["norm_w"], rinv, d["gout"].values)
     rg = oracle.ssd_bwd(*sargs, rgy.reshape(b, T, H, P))
     gact = np.concatenate([rg["dx"].reshape(b, T, di), rg["dB"].reshape(b, T, -1), rg["dC"].reshape(b, T, -1)], -1)
     rdxbc, rdcw, rdcb = oracle.conv_bwd(d["xBC"].values, d["conv_w"], d["conv_b"], gact)
+    r_raw, r_bias = oracle.dt_softplus_bwd(d["dt_raw"].values, d["dt_bias"], rg["ddt"])
     errs = {"out": relerr(host(out), rout), "dz": relerr(host(gz), rgz), "dnorm_w": relerr(host(gw), rgw),
             "ddt": relerr(host(g["ddt"]), rg["ddt"]), "dA_log": relerr(host(g["dA_log"]), rg["dA_log"]),
             "dD": relerr(host(g["dD"]), rg["dD"]), "dxbc": relerr(host(dxbc), rdxbc),
-            "dconv_w": relerr(host(dcw), rdcw), "dconv_b": relerr(host(dcb), rdcb)}
+            "dconv_w": relerr(host(dcw), rdcw), "dconv_b": relerr(host(dcb), rdcb),
+            "ddt_raw": relerr(host(g_raw), r_raw), "d_dt_bias": relerr(host(g_bias), r_bias)}
     print("[parity block chain]", {k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
     assert all(v <= TOL["bf16"] for v in errs.values()), errs
