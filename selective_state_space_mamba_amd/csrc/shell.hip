@@ -658,7 +658,7 @@ __global__ __launch_bounds__(RMS_VEC_WAVES * WAVE) void rms_bwd_vec_kernel(
 // evaluated as max(v, 0) + log1p(e^-|v|), the same function without overflow.
 // Rows are the b*T steps of a [b, T, H] array.
 
-constexpr int DT_ROWS = 64;  // rows per workgroup (one d_dt_bias partial) in the backward
+constexpr int DT_ROWS = 16;  // rows per workgroup (one d_dt_bias partial) in the backward
 
 __device__ __forceinline__ float softplus1(float v) { return fmaxf(v, 0.f) + log1pf(expf(-fabsf(v))); }
 

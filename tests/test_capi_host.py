@@ -159,7 +159,7 @@ def test_dt_softplus_argument_checks(lib):
     assert lib.ssd_dt_softplus_fwd(i64(10), i64(4), 0, f, None, f, None) == -1   # bias required
     assert lib.ssd_dt_softplus_fwd(i64(10), i64(4), 0, ctypes.c_void_p(FAKE + 4), f, f, None) == -6
     need = lib.ssd_dt_softplus_bwd_workspace_bytes(i64(100), i64(4))
-    assert need >= 2 * 4 * 4  # two 64-row partials of 4 heads
+    assert need >= 2 * 4 * 4  # two 64-row partials of 4 heads (at most 64 rows each)
     assert lib.ssd_dt_softplus_bwd(i64(100), i64(4), 0, f, f, f, f, f, f, ctypes.c_size_t(need - 1), None) == -4
     assert lib.ssd_dt_softplus_bwd(i64(100), i64(4), 0, f, f, f, f, None, f, ctypes.c_size_t(need), None) == -1
 
