@@ -74,9 +74,10 @@ typedef struct {
  * needs.  has_chunk_states tells whether the caller passes chunk_states (fwd:
  * as an output, bwd: as the saved history); without them the library keeps
  * the chunk states in the workspace.  bf16 problems (headdim and dstate
- * multiples of 8) also keep a bf16 copy of the chunk states there, so they
- * need a workspace even when chunk_states is given.  Returns 0 for an
- * invalid problem. */
+ * multiples of 8) also keep a bf16 copy of the chunk states there, and every
+ * problem keeps a [b, nc, H] f32 array of per-chunk decays, so a workspace is
+ * needed even when chunk_states is given.  Returns 0 for an invalid or empty
+ * problem. */
 size_t ssd_workspace_bytes(const ssd_problem* prob, int for_backward, int has_chunk_states);
 
 /* Forward.

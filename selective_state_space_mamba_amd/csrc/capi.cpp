@@ -93,12 +93,12 @@ constexpr int64_t kFwdTarget = 512;
 constexpr int64_t kBwdTarget = 256;
 
 struct FwdPlan {
-  size_t states = 0, hbf = 0, total = 0;
+  size_t states = 0, hbf = 0, send = 0, total = 0;
   bool bf16 = false;  // bf16 output kernel with asynchronous staging (reads a bf16 copy of the states)
 };
 struct BwdPlan {
   size_t states = 0, gamma = 0, hbf = 0, gh = 0, rowM = 0, colE = 0, diagE = 0, Rp = 0, dsoff = 0, dA = 0, dD = 0,
-         done = 0, dB = 0, dC = 0, total = 0;
+         done = 0, dB = 0, dC = 0, send = 0, total = 0;
   int nsplit = 1;
   bool bf16 = false;  // bf16 kernels with asynchronous staging (they also need a bf16 copy of the states)
 };
@@ -123,6 +123,8 @@ FwdPlan plan_fwd(const ssd::Dims& d, bool has_states, bool bf16) {
     p.hbf = off;
     off += align_up(state_bytes(d) / 2);
   }
+  p.send = off;  // per-chunk total log-decay of the two-pass f32 chunk-state form
+  off += align_up(sizeof(float) * static_cast<size_t>(d.b) * d.nc() * d.H);
   p.total = off;
   return p;
 }
@@ -150,6 +152,7 @@ BwdPlan plan_bwd(const ssd::Dims& d, bool has_states, bool bf16) {
   p.dA = take(sizeof(float) * static_cast<size_t>(d.b) * d.nc() * d.H);
   p.dD = take(sizeof(float) * static_cast<size_t>(d.b) * d.nc() * d.nb() * d.H);
   p.done = take(sizeof(unsigned));
+  p.send = take(sizeof(float) * static_cast<size_t>(d.b) * d.nc() * d.H);
   if (p.nsplit > 1) {
     const size_t part = sizeof(float) * static_cast<size_t>(p.nsplit) * d.b * d.T * d.G * d.N;
     p.dB = take(part);
@@ -295,7 +298,7 @@ int ssd_fwd(const ssd_problem* prob, const void* x, const void* dt, const float*
     return ok();
   }
   const FwdPlan plan = plan_fwd(d, chunk_states != nullptr, use_bf16_kernels(d, prob->act_dtype, prob->act_dtype));
-  if (plan.total > 0 && !workspace) return fail(SSD_ERR_WORKSPACE, "ssd_fwd: workspace is null (%zu bytes needed)", plan.total);
+  if (!workspace) return fail(SSD_ERR_WORKSPACE, "ssd_fwd: workspace is null (%zu bytes needed)", plan.total);
   if (workspace_bytes < plan.total)
     return fail(SSD_ERR_WORKSPACE, "ssd_fwd: workspace of %zu bytes is smaller than the %zu needed", workspace_bytes,
                 plan.total);
@@ -306,7 +309,8 @@ int ssd_fwd(const ssd_problem* prob, const void* x, const void* dt, const float*
     SSD_LAUNCH(ssd::launch_chunk_state_fwd_bf16(d, x, B, dt, A_log, init_state, states, final_state, hbf, st),
                "chunk_state_fwd");
   else
-    SSD_LAUNCH(ssd::launch_chunk_state_fwd(d, act, x, B, dt, A_log, init_state, states, final_state, nullptr, st),
+    SSD_LAUNCH(ssd::launch_chunk_state_fwd(d, act, x, B, dt, A_log, init_state, states, final_state, nullptr,
+                                           at<float>(workspace, plan.send), st),
                "chunk_state_fwd");
   if (plan.bf16)
     SSD_LAUNCH(ssd::launch_out_fwd_bf16(d, choose_nsplit(d, kFwdTarget, true), x, B, C, dt, A_log, D, hbf, y, st),
@@ -378,7 +382,8 @@ int ssd_bwd(const ssd_problem* prob, const void* x, const void* dt, const float*
       SSD_LAUNCH(ssd::launch_chunk_state_fwd_bf16(d, x, B, dt, A_log, init_state, rec, nullptr, nullptr, st),
                  "chunk_state_fwd (recompute)");
     else
-      SSD_LAUNCH(ssd::launch_chunk_state_fwd(d, act, x, B, dt, A_log, init_state, rec, nullptr, nullptr, st),
+      SSD_LAUNCH(ssd::launch_chunk_state_fwd(d, act, x, B, dt, A_log, init_state, rec, nullptr, nullptr,
+                                             at<float>(workspace, plan.send), st),
                  "chunk_state_fwd (recompute)");
     states = rec;
   }
@@ -389,7 +394,7 @@ int ssd_bwd(const ssd_problem* prob, const void* x, const void* dt, const float*
   else
     SSD_LAUNCH(
         ssd::launch_chunk_state_bwd(d, act, dyt, dy, C, dt, A_log, d_final_state, states, gamma, d_init_state,
-                                    s.gh_part, nullptr, st),
+                                    s.gh_part, nullptr, at<float>(workspace, plan.send), st),
         "chunk_state_bwd");
   if (plan.bf16) {
     SSD_LAUNCH(ssd::launch_bwd_col_bf16(d, plan.nsplit, x, B, C, dt, dy, A_log, D, gamma, dx,

@@ -22,9 +22,11 @@ inline int state_npb(const Dims& d) { return (d.P + STATE_PB - 1) / STATE_PB; }
 // Forward state passing: states[b,c,h] = state entering chunk c, final = state
 // after the last chunk.  `init` may be null (zero initial state), `final_state`
 // may be null; hbf (nullable) receives the states rounded to bf16.
+// send: [b, nc, H] floats of scratch (the f32 form writes each chunk's total
+// log-decay there between its two passes).
 hipError_t launch_chunk_state_fwd(const Dims& d, DType act, const void* x, const void* B,
                                   const void* dt, const float* A_log, const float* init,
-                                  float* states, float* final_state, void* hbf, hipStream_t st);
+                                  float* states, float* final_state, void* hbf, float* send, hipStream_t st);
 
 // Reverse state-gradient pass: gamma[b,c,h] = gradient reaching the state that
 // leaves chunk c, stored in the MFMA operand type (bf16 when act is BF16, else
@@ -34,7 +36,7 @@ hipError_t launch_chunk_state_fwd(const Dims& d, DType act, const void* x, const
 hipError_t launch_chunk_state_bwd(const Dims& d, DType act, DType dyt, const void* dy,
                                   const void* C, const void* dt, const float* A_log, const float* dfinal,
                                   const float* states, void* gamma, float* dinit, float* gh_part,
-                                  void* hbf, hipStream_t st);
+                                  void* hbf, float* send, hipStream_t st);
 
 // bf16 operands with asynchronous LDS staging (bwd_bf16_supported shapes):
 // the chunk-state passes (same outputs as launch_chunk_state_fwd/_bwd) and the

@@ -16,13 +16,22 @@
 // with Gamma_nc the gradient of the final state (zero unless given) and
 // d(initial state) = Gamma_0.
 //
-// Both are one kernel: a workgroup owns 16 headdim rows of one (batch, head)
-// and walks the chunks in order (forward) or in reverse (backward), keeping its
-// 16 x N slice of the state in registers.  Per chunk the weighted sum is one
-// MFMA contraction over the chunk's time steps (K = Q), the operands staged in
-// LDS in 64-step slabs.  Rows of the state are independent, so the headdim
-// split needs no communication.  All decay factors are exp of non-positive
-// numbers (dt > 0, A < 0).
+// With bf16 operands both are one kernel: a workgroup owns 16 headdim rows of
+// one (batch, head) and walks the chunks in order (forward) or in reverse
+// (backward), keeping its 16 x N slice of the state in registers.  Per chunk
+// the weighted sum is one MFMA contraction over the chunk's time steps
+// (K = Q), the operands staged in LDS in slabs.  Rows of the state are
+// independent, so the headdim split needs no communication.
+//
+// With f32 operands (MFMA at a sixteenth of the bf16 rate) the walk would
+// serialise the contractions of every chunk, so the work is split in two:
+// the same kernel in its LOCAL form computes each chunk's weighted sum S_c
+// (dS_c) with one workgroup per (batch, chunk, head, headdim block) and writes
+// it into the chunk's slot of the output, with the chunk's total log-decay
+// s_end; state_scan_kernel then walks the chunks once per (batch, head,
+// headdim block), combining H_{c+1} = exp(s_end) H_c + S_c (Gamma_c =
+// exp(s_end) Gamma_{c+1} + dS_c) in place.  All decay factors are exp of
+// non-positive numbers (dt > 0, A < 0).
 #include <type_traits>
 
 #include "ssd_common.hpp"
@@ -34,7 +43,7 @@ namespace ssd {
 // operands (64 KB of B), 128 for f32.
 template <bool BF> struct StateSlab { static constexpr int SJ = BF ? 256 : 128; };
 
-template <typename TX, typename TB, typename TDT, bool BF, bool REV>
+template <typename TX, typename TB, typename TDT, bool BF, bool REV, bool LOCAL>
 __global__ __launch_bounds__(NTHREADS, 2) void chunk_state_kernel(
     const TX* __restrict__ X,          // fwd: x; bwd: dy            [b,T,H,P]
     const TB* __restrict__ Bm,         // fwd: B; bwd: C             [b,T,G,N]
@@ -46,7 +55,9 @@ __global__ __launch_bounds__(NTHREADS, 2) void chunk_state_kernel(
     const float* __restrict__ hstates, // bwd: H_c, for <Gamma_{c+1}, H_c>
     float* __restrict__ gh_part,       // bwd: [b,nc,H,npb]
     uint16_t* __restrict__ hbf,        // bwd: H_c rounded to bf16 (nullable)
+    float* __restrict__ send,          // LOCAL: [b,nc,H] total log-decay of each chunk
     int T, int H, int P, int N, int G, int Q) {
+  static_assert(!(LOCAL && BF), "the two-pass form is for f32 operands");
   typedef typename Op<BF>::T OT;
   // The forward writes the f32 chunk states; the backward writes Gamma in the
   // operand type of the kernels that read it (its only use is as an MFMA operand).
@@ -63,12 +74,15 @@ __global__ __launch_bounds__(NTHREADS, 2) void chunk_state_kernel(
 
   // p-blocks of a head, then the heads of a group, are consecutive logical
   // blocks: they read the same B (or C) slab, so they share an XCD's L2.
+  // LOCAL: one chunk per workgroup, chunks outermost below the batch row.
   const int npb = (P + PB - 1) / PB;
+  const int nc = T / Q;
   const int lb = xcd_logical_block(blockIdx.x, gridDim.x);
-  const int pb = lb % npb, h = (lb / npb) % H, bi = lb / (npb * H);
+  const int pb = lb % npb, h = (lb / npb) % H;
+  const int cl = LOCAL ? (lb / (npb * H)) % nc : 0;
+  const int bi = LOCAL ? lb / (npb * H * nc) : lb / (npb * H);
   const int p0 = pb * PB;
   const int g = h / (H / G);
-  const int nc = T / Q;
   const int nslab = (Q + SJ - 1) / SJ;
   const float A = -__expf(A_log[h]);
   const int tid = threadIdx.x, w = wave_id(), l = lane_id(), r = l & 15, q = l >> 4;
@@ -82,13 +96,17 @@ __global__ __launch_bounds__(NTHREADS, 2) void chunk_state_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int p = p0 + 4 * q + i, n = 32 * w + 16 * t + r;
-      st[t][i] = (init && p < P && n < N) ? init[(static_cast<int64_t>(bi) * H + h) * PN + p * N + n] : 0.f;
+      st[t][i] = (!LOCAL && init && p < P && n < N) ? init[(static_cast<int64_t>(bi) * H + h) * PN + p * N + n] : 0.f;
     }
 
   TransTile<TX, SJ, PB> tx;    // x (or dy) rows j, columns p0..p0+15 -> [p][j]
   TransTile<TB, SJ, NMAX> tb;  // B (or C) rows j -> [n][j]
-  const int total = nc * nslab;
-  auto chunk_of = [&](int step) { const int it = step / nslab; return REV ? nc - 1 - it : it; };
+  const int total = (LOCAL ? 1 : nc) * nslab;
+  auto chunk_of = [&](int step) {
+    if (LOCAL) return cl;
+    const int it = step / nslab;
+    return REV ? nc - 1 - it : it;
+  };
   auto prefetch = [&](int step, float& dtn) {
     const int c = chunk_of(step), sl = step % nslab;
     const int64_t row0 = static_cast<int64_t>(bi) * T + static_cast<int64_t>(c) * Q + sl * SJ;
@@ -122,8 +140,20 @@ __global__ __launch_bounds__(NTHREADS, 2) void chunk_state_kernel(
     wave_gemm<BF, true, true, 2>(acc, sX, LDX, 1, sB + 32 * w * LDX, LDX, 1, round_up(min(SJ, Q - sl * SJ), Op<BF>::KS));
     if (sl != nslab - 1) continue;
 
-    const float decay = __expf(sS[Q - 1]);
     const int64_t sbase = ((static_cast<int64_t>(bi) * nc + c) * H + h) * PN;
+    if constexpr (LOCAL) {
+      // this chunk's weighted sum and its total log-decay, for state_scan_kernel
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int p = p0 + 4 * q + i, n = 32 * w + 16 * t + r;
+          if (p < P && n < N) store_f(states_out, sbase + p * N + n, acc[t][i]);
+        }
+      if (pb == 0 && tid == 0) send[(static_cast<int64_t>(bi) * nc + c) * H + h] = sS[Q - 1];
+      return;
+    }
+    const float decay = __expf(sS[Q - 1]);
     float gh = 0.f;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
@@ -161,44 +191,148 @@ __global__ __launch_bounds__(NTHREADS, 2) void chunk_state_kernel(
   }
 }
 
+// The chunk walk of the two-pass form.  A workgroup of 16 waves owns headdim
+// rows p0 .. p0+15 of one (batch, head); thread t holds elements t and t + 1024
+// of that contiguous 16 x N block.  Forward: slot c holds S_c on entry and H_c
+// on exit, run = H_0 = init (or 0), run <- exp(s_end_c) run + S_c, last = H_nc.
+// Backward: slot c holds dS_c on entry and Gamma_{c+1} on exit, run =
+// Gamma_nc = init (the final state's gradient, or 0), run <- exp(s_end_c) run +
+// dS_c, last = Gamma_0, and gh_part[b,c,h,pb] = <Gamma_{c+1}, H_c> over the
+// block.  The values of the next two chunks are in flight while a chunk's slot
+// is written.
+constexpr int SCAN_THREADS = 1024;
+constexpr int SCAN_EPT = STATE_PB * NMAX / SCAN_THREADS;  // elements per thread
+constexpr int SCAN_AHEAD = 2;                             // chunks loaded ahead
+template <bool REV>
+__global__ __launch_bounds__(SCAN_THREADS) void state_scan_kernel(float* __restrict__ states,
+                                                                 const float* __restrict__ send,
+                                                                 const float* __restrict__ init,
+                                                                 float* __restrict__ last,
+                                                                 const float* __restrict__ hstates,
+                                                                 float* __restrict__ gh_part, int nc, int H, int P,
+                                                                 int N) {
+  __shared__ float sTmp[SCAN_THREADS / WAVE];
+  const int npb = (P + STATE_PB - 1) / STATE_PB;
+  const int lb = blockIdx.x;
+  const int pb = lb % npb, h = (lb / npb) % H, bi = lb / (npb * H);
+  const int p0 = pb * STATE_PB;
+  const int nvalid = min(STATE_PB, P - p0) * N;  // contiguous elements of the block
+  const int64_t PN = static_cast<int64_t>(P) * N;
+  const int64_t off0 = static_cast<int64_t>(p0) * N;
+  const int tid = threadIdx.x;
+  float run[SCAN_EPT], buf[SCAN_AHEAD][SCAN_EPT];
+#pragma unroll
+  for (int k = 0; k < SCAN_EPT; ++k) {
+    const int e = tid + SCAN_THREADS * k;
+    run[k] = (init && e < nvalid) ? init[(static_cast<int64_t>(bi) * H + h) * PN + off0 + e] : 0.f;
+  }
+  auto chunk = [&](int it) { return REV ? nc - 1 - it : it; };
+  auto slot = [&](int it) { return ((static_cast<int64_t>(bi) * nc + chunk(it)) * H + h) * PN + off0; };
+  auto load = [&](int it, float (&v)[SCAN_EPT]) {
+#pragma unroll
+    for (int k = 0; k < SCAN_EPT; ++k) {
+      const int e = tid + SCAN_THREADS * k;
+      v[k] = (it < nc && e < nvalid) ? states[slot(it) + e] : 0.f;
+    }
+  };
+#pragma unroll
+  for (int a = 0; a < SCAN_AHEAD; ++a) load(a, buf[a]);
+  for (int it = 0; it < nc; ++it) {
+    const int c = chunk(it);
+    const int64_t base = slot(it);
+    const float decay = __expf(send[(static_cast<int64_t>(bi) * nc + c) * H + h]);
+    float cur[SCAN_EPT];
+#pragma unroll
+    for (int k = 0; k < SCAN_EPT; ++k) {
+      cur[k] = buf[0][k];
+#pragma unroll
+      for (int a = 0; a + 1 < SCAN_AHEAD; ++a) buf[a][k] = buf[a + 1][k];
+    }
+    load(it + SCAN_AHEAD, buf[SCAN_AHEAD - 1]);
+    float gh = 0.f;
+#pragma unroll
+    for (int k = 0; k < SCAN_EPT; ++k) {
+      const int e = tid + SCAN_THREADS * k;
+      if (e < nvalid) {
+        states[base + e] = run[k];
+        if (REV) gh += run[k] * hstates[base + e];
+      }
+      run[k] = decay * run[k] + cur[k];
+    }
+    if (REV) {
+      gh = wave_sum(gh);
+      if (lane_id() == 0) sTmp[wave_id()] = gh;
+      __syncthreads();
+      if (tid == 0) {
+        float t = 0.f;
+#pragma unroll
+        for (int q = 0; q < SCAN_THREADS / WAVE; ++q) t += sTmp[q];
+        gh_part[((static_cast<int64_t>(bi) * nc + c) * H + h) * npb + pb] = t;
+      }
+      __syncthreads();
+    }
+  }
+  if (last) {
+#pragma unroll
+    for (int k = 0; k < SCAN_EPT; ++k) {
+      const int e = tid + SCAN_THREADS * k;
+      if (e < nvalid) last[(static_cast<int64_t>(bi) * H + h) * PN + off0 + e] = run[k];
+    }
+  }
+}
+
 template <typename TX, typename TB, bool BF, bool REV>
 static hipError_t launch_state(const Dims& d, const void* X, const void* Bm, const void* dt,
                                const float* A_log, const float* init, void* states, float* last,
-                               const float* hstates, float* gh_part, hipStream_t st, void* hbf = nullptr) {
-  dim3 grid(state_npb(d) * d.H * d.b);
-  hipLaunchKernelGGL((chunk_state_kernel<TX, TB, TB, BF, REV>), grid, dim3(NTHREADS), 0, st,
-                     static_cast<const TX*>(X), static_cast<const TB*>(Bm), static_cast<const TB*>(dt),
-                     A_log, init, states, last, hstates, gh_part, static_cast<uint16_t*>(hbf), d.T, d.H, d.P,
-                     d.N, d.G, d.Q);
-  return hipGetLastError();
+                               const float* hstates, float* gh_part, float* send, hipStream_t st,
+                               void* hbf = nullptr) {
+  if constexpr (!BF) {
+    // two passes: per-chunk sums in parallel, then the walk over chunks
+    dim3 grid(state_npb(d) * d.H * d.nc() * d.b);
+    hipLaunchKernelGGL((chunk_state_kernel<TX, TB, TB, false, REV, true>), grid, dim3(NTHREADS), 0, st,
+                       static_cast<const TX*>(X), static_cast<const TB*>(Bm), static_cast<const TB*>(dt), A_log,
+                       nullptr, states, nullptr, nullptr, nullptr, nullptr, send, d.T, d.H, d.P, d.N, d.G, d.Q);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(state_scan_kernel<REV>, dim3(state_npb(d) * d.H * d.b), dim3(SCAN_THREADS), 0, st,
+                       static_cast<float*>(states), send, init, last, hstates, gh_part, d.nc(), d.H, d.P, d.N);
+    return hipGetLastError();
+  } else {
+    dim3 grid(state_npb(d) * d.H * d.b);
+    hipLaunchKernelGGL((chunk_state_kernel<TX, TB, TB, BF, REV, false>), grid, dim3(NTHREADS), 0, st,
+                       static_cast<const TX*>(X), static_cast<const TB*>(Bm), static_cast<const TB*>(dt),
+                       A_log, init, states, last, hstates, gh_part, static_cast<uint16_t*>(hbf), nullptr, d.T, d.H,
+                       d.P, d.N, d.G, d.Q);
+    return hipGetLastError();
+  }
 }
 
 hipError_t launch_chunk_state_fwd(const Dims& d, DType act, const void* x, const void* B,
                                   const void* dt, const float* A_log, const float* init,
-                                  float* states, float* final_state, void* hbf, hipStream_t st) {
+                                  float* states, float* final_state, void* hbf, float* send, hipStream_t st) {
   if (act == BF16)
     return launch_state<uint16_t, uint16_t, true, false>(d, x, B, dt, A_log, init, states, final_state,
-                                                         nullptr, nullptr, st, hbf);
+                                                         nullptr, nullptr, send, st, hbf);
   return launch_state<float, float, false, false>(d, x, B, dt, A_log, init, states, final_state, nullptr,
-                                                  nullptr, st);
+                                                  nullptr, send, st);
 }
 
 hipError_t launch_chunk_state_bwd(const Dims& d, DType act, DType dyt, const void* dy,
                                   const void* C, const void* dt, const float* A_log, const float* dfinal,
                                   const float* states, void* gamma, float* dinit, float* gh_part,
-                                  void* hbf, hipStream_t st) {
+                                  void* hbf, float* send, hipStream_t st) {
   if (act == BF16) {
     if (dyt == BF16)
       return launch_state<uint16_t, uint16_t, true, true>(d, dy, C, dt, A_log, dfinal, gamma, dinit,
-                                                          states, gh_part, st, hbf);
+                                                          states, gh_part, send, st, hbf);
     return launch_state<float, uint16_t, true, true>(d, dy, C, dt, A_log, dfinal, gamma, dinit, states,
-                                                     gh_part, st, hbf);
+                                                     gh_part, send, st, hbf);
   }
   if (dyt == BF16)
     return launch_state<uint16_t, float, false, true>(d, dy, C, dt, A_log, dfinal, gamma, dinit, states,
-                                                      gh_part, st);
+                                                      gh_part, send, st);
   return launch_state<float, float, false, true>(d, dy, C, dt, A_log, dfinal, gamma, dinit, states,
-                                                 gh_part, st);
+                                                 gh_part, send, st);
 }
 
 }  // namespace ssd
