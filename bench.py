@@ -184,6 +184,71 @@ def write_counter_summary(fetch_dir: str, write_dir: str, kernel: str, workload:
     print(path)
 
 
+def _kernel_base(name: str) -> str:
+    """Kernel name with its template arguments, without namespace and parameters."""
+    return name.split("(")[0].replace("void ", "").replace("ssd::", "").strip()
+
+
+def write_mfma_summary(d: str, workload: str) -> None:
+    """Per-kernel MFMA utilisation and counted MFMA flops from one rocprofv3
+    --pmc MfmaUtil MfmaFlopsBF16 MfmaFlopsF32 run (MfmaUtil = MFMA busy
+    cycles / (GPU busy cycles x SIMDs); MfmaFlops* = MFMA MOPs x 512)."""
+    rows = _counter_rows(d)
+    if not rows:
+        raise SystemExit(f"no counter rows under {d}")
+    acc = {}
+    for r in rows:
+        k = _kernel_base(r["Kernel_Name"])
+        acc.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    # bench kernel of each device kernel whose name says which one it is (the
+    # chunk-state kernels serve both directions and are listed only)
+    bench_of = {dev: k for k, devs in DEVICE_KERNELS.items() for dev in devs if not k.startswith("chunk_state")}
+    lines = [f"MFMA counters per kernel on the {workload} workload (rocprofv3, per launch)", "",
+             "Command (repository root, one MI355X, TMPDIR=/tmp):",
+             f"  rocprofv3 --pmc MfmaUtil MfmaFlopsBF16 MfmaFlopsF32 -f csv -d <DIR> -o run -- python3 bench.py "
+             f"--workload {workload} --steps 2 --warmup 1 --no-cpu-baseline",
+             f"  python3 bench.py --workload {workload} --mfma-summary <DIR>", "",
+             "MfmaUtil is 100 x SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x SIMDs), the share of SIMD cycles",
+             "the matrix cores were busy during the launch; MfmaFlops* count 512 flops per MFMA MOP (all issued",
+             "MFMAs, including the masked halves of diagonal tiles and zero padding).", "",
+             "| kernel | launches | MfmaUtil % | counted MFMA GFLOP per launch (bf16 + f32) |",
+             "|---|---|---|---|"]
+    out = {}
+    for k in sorted(acc):
+        c = acc[k]
+        if "MfmaUtil" not in c:
+            continue
+        n = len(c["MfmaUtil"])
+        util = sum(c["MfmaUtil"]) / n
+        fl = sum(sum(c.get(x, [0.0])) / max(1, len(c.get(x, []))) for x in ("MfmaFlopsBF16", "MfmaFlopsF32"))
+        lines.append(f"| `{k}` | {n} | {util:.2f} | {fl / 1e9:.3f} |")
+        if k.split("<")[0] in bench_of:
+            out[bench_of[k.split("<")[0]]] = (util, fl)
+    lines.append("")
+    for k, (util, fl) in sorted(out.items()):
+        lines.append(f"mfma_util_pct {k}: {util:.3f}")
+        lines.append(f"mfma_flops_per_launch {k}: {fl:.0f}")
+        lines.append(f"source_digest {k}: {source_digest(k)}")
+    lines += ["", "The digests cover each kernel's source files; bench.py reports a kernel's utilisation only while",
+              "its digest matches."]
+    path = os.path.join(ROOT, "profiles", f"mfma_counters_{workload}.txt")
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(path)
+
+
+def measured_mfma_util(kernel: str, workload: str):
+    path = os.path.join(ROOT, "profiles", f"mfma_counters_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_u = re.search(rf"^mfma_util_pct {re.escape(kernel)}:\s*([0-9.eE+-]+)", text, re.M)
+    m_d = re.search(rf"^source_digest {re.escape(kernel)}:\s*(\S+)", text, re.M)
+    if not m_u or not m_d or m_d.group(1) != source_digest(kernel):
+        return None
+    return float(m_u.group(1))
+
+
 def to_dev(a):
     import numpy as np
     import torch
@@ -284,7 +349,13 @@ def main():
     ap.add_argument("--counter-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write the HBM-traffic summary from two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) and exit")
     ap.add_argument("--kernel", default="chunk_bwd_col", help="kernel for --counter-summary")
+    ap.add_argument("--mfma-summary", metavar="DIR",
+                    help="write the per-kernel MFMA utilisation summary from a rocprofv3 --pmc MfmaUtil "
+                         "MfmaFlopsBF16 MfmaFlopsF32 run and exit")
     args = ap.parse_args()
+    if args.mfma_summary:
+        write_mfma_summary(args.mfma_summary, args.workload)
+        return
     if args.counter_summary:
         write_counter_summary(args.counter_summary[0], args.counter_summary[1], args.kernel, args.workload,
                               args.calibrate_copy_mb)
@@ -348,7 +419,8 @@ def main():
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "kernel": dom, "kernel_ms": round(t_dom * 1e3, 4), "algorithmic_bytes": alg,
-                "mfma_tflops": round(algorithmic_flops(cfg, dom) / t_dom / 1e12, 2)}
+                "mfma_tflops": round(algorithmic_flops(cfg, dom) / t_dom / 1e12, 2),
+                "mfma_util_pct": measured_mfma_util(dom, cfg.name)}
     t_bwd = sum(v for k, v in kms.items() if k in KERNELS_BWD) * 1e-3
     bwd_alg = backward_algorithmic_bytes(cfg)
     ssd_bwd = {"ms": round(t_bwd * 1e3, 4), "algorithmic_bytes": bwd_alg,
