@@ -25,12 +25,12 @@
 //
 // With f32 operands (MFMA at a sixteenth of the bf16 rate) the walk would
 // serialise the contractions of every chunk, so the work is split in two:
-// the same kernel in its LOCAL form computes each chunk's weighted sum S_c
-// (dS_c) with one workgroup per (batch, chunk, head, headdim block) and writes
-// it into the chunk's slot of the output, with the chunk's total log-decay
-// s_end; state_scan_kernel then walks the chunks once per (batch, head,
-// headdim block), combining H_{c+1} = exp(s_end) H_c + S_c (Gamma_c =
-// exp(s_end) Gamma_{c+1} + dS_c) in place.  All decay factors are exp of
+// chunk_sum_f32_kernel computes each chunk's weighted sum S_c (dS_c) with one
+// workgroup per (batch, chunk, head) and writes it into the chunk's slot of
+// the output, with the chunk's total log-decay s_end; state_scan_kernel then
+// walks the chunks once per (batch, head, headdim block), combining
+// H_{c+1} = exp(s_end) H_c + S_c (Gamma_c = exp(s_end) Gamma_{c+1} + dS_c) in
+// place.  All decay factors are exp of
 // non-positive numbers (dt > 0, A < 0).
 #include <type_traits>
 
@@ -43,7 +43,7 @@ namespace ssd {
 // operands (64 KB of B), 128 for f32.
 template <bool BF> struct StateSlab { static constexpr int SJ = BF ? 256 : 128; };
 
-template <typename TX, typename TB, typename TDT, bool BF, bool REV, bool LOCAL>
+template <typename TX, typename TB, typename TDT, bool BF, bool REV>
 __global__ __launch_bounds__(NTHREADS, 2) void chunk_state_kernel(
     const TX* __restrict__ X,          // fwd: x; bwd: dy            [b,T,H,P]
     const TB* __restrict__ Bm,         // fwd: B; bwd: C             [b,T,G,N]
@@ -55,9 +55,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void chunk_state_kernel(
     const float* __restrict__ hstates, // bwd: H_c, for <Gamma_{c+1}, H_c>
     float* __restrict__ gh_part,       // bwd: [b,nc,H,npb]
     uint16_t* __restrict__ hbf,        // bwd: H_c rounded to bf16 (nullable)
-    float* __restrict__ send,          // LOCAL: [b,nc,H] total log-decay of each chunk
     int T, int H, int P, int N, int G, int Q) {
-  static_assert(!(LOCAL && BF), "the two-pass form is for f32 operands");
   typedef typename Op<BF>::T OT;
   // The forward writes the f32 chunk states; the backward writes Gamma in the
   // operand type of the kernels that read it (its only use is as an MFMA operand).
@@ -74,13 +72,10 @@ __global__ __launch_bounds__(NTHREADS, 2) void chunk_state_kernel(
 
   // p-blocks of a head, then the heads of a group, are consecutive logical
   // blocks: they read the same B (or C) slab, so they share an XCD's L2.
-  // LOCAL: one chunk per workgroup, chunks outermost below the batch row.
   const int npb = (P + PB - 1) / PB;
   const int nc = T / Q;
   const int lb = xcd_logical_block(blockIdx.x, gridDim.x);
-  const int pb = lb % npb, h = (lb / npb) % H;
-  const int cl = LOCAL ? (lb / (npb * H)) % nc : 0;
-  const int bi = LOCAL ? lb / (npb * H * nc) : lb / (npb * H);
+  const int pb = lb % npb, h = (lb / npb) % H, bi = lb / (npb * H);
   const int p0 = pb * PB;
   const int g = h / (H / G);
   const int nslab = (Q + SJ - 1) / SJ;
@@ -96,17 +91,13 @@ __global__ __launch_bounds__(NTHREADS, 2) void chunk_state_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int p = p0 + 4 * q + i, n = 32 * w + 16 * t + r;
-      st[t][i] = (!LOCAL && init && p < P && n < N) ? init[(static_cast<int64_t>(bi) * H + h) * PN + p * N + n] : 0.f;
+      st[t][i] = (init && p < P && n < N) ? init[(static_cast<int64_t>(bi) * H + h) * PN + p * N + n] : 0.f;
     }
 
   TransTile<TX, SJ, PB> tx;    // x (or dy) rows j, columns p0..p0+15 -> [p][j]
   TransTile<TB, SJ, NMAX> tb;  // B (or C) rows j -> [n][j]
-  const int total = (LOCAL ? 1 : nc) * nslab;
-  auto chunk_of = [&](int step) {
-    if (LOCAL) return cl;
-    const int it = step / nslab;
-    return REV ? nc - 1 - it : it;
-  };
+  const int total = nc * nslab;
+  auto chunk_of = [&](int step) { const int it = step / nslab; return REV ? nc - 1 - it : it; };
   auto prefetch = [&](int step, float& dtn) {
     const int c = chunk_of(step), sl = step % nslab;
     const int64_t row0 = static_cast<int64_t>(bi) * T + static_cast<int64_t>(c) * Q + sl * SJ;
@@ -141,18 +132,6 @@ __global__ __launch_bounds__(NTHREADS, 2) void chunk_state_kernel(
     if (sl != nslab - 1) continue;
 
     const int64_t sbase = ((static_cast<int64_t>(bi) * nc + c) * H + h) * PN;
-    if constexpr (LOCAL) {
-      // this chunk's weighted sum and its total log-decay, for state_scan_kernel
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int p = p0 + 4 * q + i, n = 32 * w + 16 * t + r;
-          if (p < P && n < N) store_f(states_out, sbase + p * N + n, acc[t][i]);
-        }
-      if (pb == 0 && tid == 0) send[(static_cast<int64_t>(bi) * nc + c) * H + h] = sS[Q - 1];
-      return;
-    }
     const float decay = __expf(sS[Q - 1]);
     float gh = 0.f;
 #pragma unroll
@@ -189,6 +168,78 @@ __global__ __launch_bounds__(NTHREADS, 2) void chunk_state_kernel(
         if (p < P && n < N) last_out[(static_cast<int64_t>(bi) * H + h) * PN + p * N + n] = st[t][i];
       }
   }
+}
+
+// First pass of the f32 form: one workgroup per (batch, chunk, head) forms the
+// chunk's whole P x N weighted sum (forward S_c = sum_j exp(s_end - s_j) dt_j
+// x_j (outer) B_j, backward dS_c = sum_i exp(s_i) dy_i (outer) C_i) over slabs
+// of SUM_SJ steps, so each B (C) slab staged in LDS serves every headdim row
+// of the head; wave w owns rows 16w .. 16w+15 and all N columns.  The sum goes
+// to the chunk's slot of `sums`, the chunk's total log-decay s_end to `send`.
+constexpr int SUM_SJ = 64;
+template <typename TX, typename TB, bool REV>
+__global__ __launch_bounds__(NTHREADS, 2) void chunk_sum_f32_kernel(
+    const TX* __restrict__ X,         // fwd: x; bwd: dy            [b,T,H,P]
+    const TB* __restrict__ Bm,        // fwd: B; bwd: C             [b,T,G,N]
+    const TB* __restrict__ dt,        // [b,T,H]
+    const float* __restrict__ A_log,  // [H]
+    float* __restrict__ sums,         // [b,nc,H,P,N]
+    float* __restrict__ send,         // [b,nc,H]
+    int T, int H, int P, int N, int G, int Q) {
+  static_assert(NTHREADS / WAVE * 16 == PMAX, "one wave per 16 headdim rows");
+  constexpr int LDX = SUM_SJ + 4;  // [p][j] and [n][j]: time contiguous, padded
+  __shared__ __attribute__((aligned(16))) float sX[PMAX * LDX];
+  __shared__ __attribute__((aligned(16))) float sB[NMAX * LDX];
+  __shared__ float sW[QMAX];
+  __shared__ float sTmp[8];
+  const int nc = T / Q;
+  const int lb = xcd_logical_block(blockIdx.x, gridDim.x);  // heads of a chunk share an XCD
+  const int h = lb % H, c = (lb / H) % nc, bi = lb / (H * nc);
+  const int g = h / (H / G);
+  const float A = -__expf(A_log[h]);
+  const int tid = threadIdx.x, w = wave_id(), l = lane_id(), r = l & 15, q = l >> 4;
+  const int64_t HP = static_cast<int64_t>(H) * P, GN = static_cast<int64_t>(G) * N;
+  const int64_t PN = static_cast<int64_t>(P) * N;
+  const int64_t row_c = static_cast<int64_t>(bi) * T + static_cast<int64_t>(c) * Q;
+
+  TransTile<TX, SUM_SJ, PMAX, 4> tx;  // x (or dy) rows j -> [p][j], scaled by the step weights
+  TransTile<TB, SUM_SJ, NMAX, 4> tb;  // B (or C) rows j -> [n][j]
+  const int nslab = (Q + SUM_SJ - 1) / SUM_SJ;
+  auto load = [&](int sl) {
+    const int64_t row0 = row_c + sl * SUM_SJ;
+    const int vr = min(SUM_SJ, Q - sl * SUM_SJ);
+    tx.load(X + row0 * HP + static_cast<int64_t>(h) * P, HP, vr, P);
+    tb.load(Bm + row0 * GN + static_cast<int64_t>(g) * N, GN, vr, N);
+  };
+  load(0);
+
+  const float dtv = tid < Q ? load_f(dt, (row_c + tid) * H + h) : 0.f;
+  const float s = block_inclusive_scan(dtv * A, sTmp);
+  if (tid == Q - 1) sTmp[4] = s;
+  __syncthreads();
+  const float s_end = sTmp[4];
+  if (tid < Q) sW[tid] = REV ? __expf(s) : __expf(s_end - s) * dtv;
+  if (tid == 0) send[(static_cast<int64_t>(bi) * nc + c) * H + h] = s_end;
+
+  f4 acc[NMAX / 16];
+  zero(acc);
+  for (int sl = 0; sl < nslab; ++sl) {
+    __syncthreads();  // sW visible; the previous slab's reads of sX / sB done
+    tx.store(sX, LDX, sW + sl * SUM_SJ);
+    tb.store(sB, LDX);
+    if (sl + 1 < nslab) load(sl + 1);
+    __syncthreads();
+    wave_gemm<false, true, true, NMAX / 16>(acc, sX + 16 * w * LDX, LDX, 1, sB, LDX, 1,
+                                           round_up(min(SUM_SJ, Q - sl * SUM_SJ), Op<false>::KS));
+  }
+  const int64_t base = ((static_cast<int64_t>(bi) * nc + c) * H + h) * PN;
+#pragma unroll
+  for (int t = 0; t < NMAX / 16; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int p = 16 * w + 4 * q + i, n = 16 * t + r;
+      if (p < P && n < N) sums[base + p * N + n] = acc[t][i];
+    }
 }
 
 // The chunk walk of the two-pass form.  A workgroup of 16 waves owns headdim
@@ -288,10 +339,9 @@ static hipError_t launch_state(const Dims& d, const void* X, const void* Bm, con
                                void* hbf = nullptr) {
   if constexpr (!BF) {
     // two passes: per-chunk sums in parallel, then the walk over chunks
-    dim3 grid(state_npb(d) * d.H * d.nc() * d.b);
-    hipLaunchKernelGGL((chunk_state_kernel<TX, TB, TB, false, REV, true>), grid, dim3(NTHREADS), 0, st,
+    hipLaunchKernelGGL((chunk_sum_f32_kernel<TX, TB, REV>), dim3(d.H * d.nc() * d.b), dim3(NTHREADS), 0, st,
                        static_cast<const TX*>(X), static_cast<const TB*>(Bm), static_cast<const TB*>(dt), A_log,
-                       nullptr, states, nullptr, nullptr, nullptr, nullptr, send, d.T, d.H, d.P, d.N, d.G, d.Q);
+                       static_cast<float*>(states), send, d.T, d.H, d.P, d.N, d.G, d.Q);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(state_scan_kernel<REV>, dim3(state_npb(d) * d.H * d.b), dim3(SCAN_THREADS), 0, st,
@@ -299,9 +349,9 @@ static hipError_t launch_state(const Dims& d, const void* X, const void* Bm, con
     return hipGetLastError();
   } else {
     dim3 grid(state_npb(d) * d.H * d.b);
-    hipLaunchKernelGGL((chunk_state_kernel<TX, TB, TB, BF, REV, false>), grid, dim3(NTHREADS), 0, st,
+    hipLaunchKernelGGL((chunk_state_kernel<TX, TB, TB, BF, REV>), grid, dim3(NTHREADS), 0, st,
                        static_cast<const TX*>(X), static_cast<const TB*>(Bm), static_cast<const TB*>(dt),
-                       A_log, init, states, last, hstates, gh_part, static_cast<uint16_t*>(hbf), nullptr, d.T, d.H,
+                       A_log, init, states, last, hstates, gh_part, static_cast<uint16_t*>(hbf), d.T, d.H,
                        d.P, d.N, d.G, d.Q);
     return hipGetLastError();
   }
