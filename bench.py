@@ -32,6 +32,7 @@ if ROOT not in sys.path:
 
 METRIC = "SSD fwd+bwd tokens/sec on 1 MI355X; achieved HBM GB/s and MFMA % of peak"
 HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}  # MI355X dense matrix-core peaks
 KERNELS_FWD = ["chunk_state_fwd", "chunk_out_fwd"]
 KERNELS_BWD = ["chunk_state_bwd", "chunk_bwd_col", "chunk_bwd_row", "bwd_dt", "bwd_split_sum"]
 KERNELS_SHELL = ["dt_softplus_fwd", "conv1d_silu_fwd", "rmsnorm_gated_fwd", "rmsnorm_gated_bwd", "conv1d_silu_bwd",
@@ -414,13 +415,21 @@ def main():
 
     t_dom = ms_dom / n_dom * 1e-3
     alg = algorithmic_bytes(cfg, dom)
+    flops = algorithmic_flops(cfg, dom)
     achieved = alg / t_dom / 1e9
+    tflops = flops / t_dom / 1e12
     traffic = measured_traffic(dom, cfg.name)
-    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": dom, "kernel_ms": round(t_dom * 1e3, 4), "algorithmic_bytes": alg,
-                "mfma_tflops": round(algorithmic_flops(cfg, dom) / t_dom / 1e12, 2),
-                "mfma_util_pct": measured_mfma_util(dom, cfg.name)}
+    # The roof that bounds the kernel: HBM below the machine balance of the
+    # operand dtype's MFMA peak over the HBM peak, the MFMA peak above it.
+    mfma_peak = MFMA_PEAK_TFLOPS["bf16" if cfg.dtype == "bf16" else "f32"]
+    if flops / alg > mfma_peak * 1e3 / HBM_PEAK_GBS:
+        roofline = {"bound": "mfma", "achieved": round(tflops, 2), "peak": mfma_peak, "unit": "TFLOP/s",
+                    "frac": round(tflops / mfma_peak, 4), "traffic": traffic, "hbm_gbs": round(achieved, 1)}
+    else:
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic, "mfma_tflops": round(tflops, 2)}
+    roofline.update({"kernel": dom, "kernel_ms": round(t_dom * 1e3, 4), "algorithmic_bytes": alg,
+                     "algorithmic_flops": flops, "mfma_util_pct": measured_mfma_util(dom, cfg.name)})
     t_bwd = sum(v for k, v in kms.items() if k in KERNELS_BWD) * 1e-3
     bwd_alg = backward_algorithmic_bytes(cfg)
     ssd_bwd = {"ms": round(t_bwd * 1e3, 4), "algorithmic_bytes": bwd_alg,
