@@ -70,3 +70,42 @@ def test_dt_activation_chained_with_the_core():
             "ddt_raw": relerr(host(g_raw), r_raw), "d_dt_bias": relerr(host(g_bias), r_bias)}
     print("[parity dt chain]", {k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
     assert all(v <= TOL["bf16"] for v in errs.values()), errs
+
+
+@pytest.mark.parametrize("dtype,with_bias", [("f32", True), ("f32", False), ("bf16", True)])
+def test_autograd_ssd_scan(dtype, with_bias):
+    """ssd_scan's autograd gradients of sum(dy y) + <dfinal, final>, with a
+    carried initial state and (optionally) the dt activation, against the
+    oracle chain."""
+    from ssd_inputs import SSDConfig
+    cfg = SSDConfig("ag", 2, 512, 8, 64, 128, 2, 128, dtype, init_state=True, seed=77)
+    d = make_inputs(cfg)
+    rng = np.random.default_rng(78)
+    dfin = rng.standard_normal((2, 8, 64, 128)).astype(np.float32)
+    dt_src = d["dt_raw"] if with_bias else d["dt"]
+    leaves = [dev(d[k]).requires_grad_() for k in ("x",)] + [dev(dt_src).requires_grad_()]
+    x, dt = leaves
+    A_log, B, C, D = (dev(d[k]).requires_grad_() for k in ("A_log", "B", "C", "D"))
+    h0 = dev(d["h0"]).requires_grad_()
+    bias = dev(d["dt_bias"]).requires_grad_() if with_bias else None
+    y, fin = ssd.ssd_scan(x, dt, A_log, B, C, D, h0, chunk=cfg.chunk, dt_bias=bias)
+    loss = (y.float() * dev(d["dy"]).float()).sum() + (fin * dev(dfin)).sum()
+    loss.backward()
+    torch.cuda.synchronize()
+
+    r_dt = oracle.dt_softplus_fwd(d["dt_raw"].values, d["dt_bias"]) if with_bias else d["dt"].values
+    args = (d["x"].values, r_dt, d["A_log"], d["B"].values, d["C"].values, d["D"])
+    rf = oracle.ssd_fwd(*args, d["h0"])
+    rg = oracle.ssd_bwd(*args, d["dy"].values, d["h0"], dfinal=dfin)
+    r_ddt = rg["ddt"]
+    errs = {"y": relerr(host(y), rf["y"]), "final": relerr(host(fin), rf["final"]),
+            "dx": relerr(host(x.grad), rg["dx"]), "dA_log": relerr(host(A_log.grad), rg["dA_log"]),
+            "dB": relerr(host(B.grad), rg["dB"]), "dC": relerr(host(C.grad), rg["dC"]),
+            "dD": relerr(host(D.grad), rg["dD"]), "dh0": relerr(host(h0.grad), rg["dh0"])}
+    if with_bias:
+        r_raw, r_bias = oracle.dt_softplus_bwd(d["dt_raw"].values, d["dt_bias"], r_ddt)
+        errs.update(ddt_raw=relerr(host(dt.grad), r_raw), d_dt_bias=relerr(host(bias.grad), r_bias))
+    else:
+        errs.update(ddt=relerr(host(dt.grad), r_ddt))
+    print("[parity ssd_scan]", dtype, with_bias, {k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
+    assert all(v <= TOL[dtype] for v in errs.values()), errs
