@@ -319,7 +319,7 @@ def make_step(cfg, d):
     return step
 
 
-def cpu_baseline(cfg, d, batches: int):
+def cpu_baseline(cfg, d, batches: int, min_wall_s: float = 1.0):
     import numpy as np
     import oracle
     nb = min(cfg.batch, max(1, batches))
@@ -327,14 +327,20 @@ def cpu_baseline(cfg, d, batches: int):
     args = (d["x"].values[sl], d["dt"].values[sl], d["A_log"], d["B"].values[sl], d["C"].values[sl], d["D"])
     h0 = None if d.get("h0") is None else d["h0"][sl]
     threads = oracle.default_threads()
-    t0 = time.perf_counter()
-    oracle.ssd_fwd(*args, h0, chunk=cfg.chunk, nthreads=threads)
-    oracle.ssd_bwd(*args, d["dy"].values[sl], h0, nthreads=threads)
-    el = time.perf_counter() - t0
+    # repeat the sample until about a second of wall time (10-30 s of CPU
+    # work on a 16-thread host) has been measured
+    reps, el = 0, 0.0
+    while reps == 0 or el < min_wall_s:
+        t0 = time.perf_counter()
+        oracle.ssd_fwd(*args, h0, chunk=cfg.chunk, nthreads=threads)
+        oracle.ssd_bwd(*args, d["dy"].values[sl], h0, nthreads=threads)
+        el += time.perf_counter() - t0
+        reps += 1
     del np
-    return {"value": nb * cfg.seqlen / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+    return {"value": reps * nb * cfg.seqlen / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": (f"sequential f64 oracle, SSD fwd+bwd on batch rows 0..{nb - 1} of {cfg.batch} "
-                       f"({nb * cfg.seqlen} tokens, {el:.1f} s wall on {threads} threads); tokens/s of that sample")}
+                       f"({nb * cfg.seqlen} tokens) run {reps} times, {el:.1f} s wall on {threads} threads; "
+                       "tokens/s of that sample")}
 
 
 def main():

@@ -162,7 +162,7 @@ int mamba2_rmsnorm_gated_bwd(int64_t rows, int64_t width, int32_t dtype, int32_t
  *     [nheads] f32.  dt may be passed to ssd_fwd and ssd_bwd as their dt.
  *   ssd_dt_softplus_bwd: ddt [rows,nheads] f32 is ssd_bwd's gradient of dt;
  *     outputs f32 ddt_raw [rows,nheads] (the gradient of dt_raw, equal to that
- *     of dt_pre) and d_dt_bias [nheads], a fixed-order sum of per-16-row
+ *     of dt_pre) and d_dt_bias [nheads], a fixed-order sum of per-64-row
  *     partials held in the workspace.
  * softplus(v) is evaluated as max(v,0) + log1p(exp(-|v|)).  Pointers are
  * 16-byte aligned device pointers; errors as for ssd_fwd. */

@@ -658,7 +658,7 @@ __global__ __launch_bounds__(RMS_VEC_WAVES * WAVE) void rms_bwd_vec_kernel(
 // evaluated as max(v, 0) + log1p(e^-|v|), the same function without overflow.
 // Rows are the b*T steps of a [b, T, H] array.
 
-constexpr int DT_ROWS = 16;  // rows per workgroup (one d_dt_bias partial) in the backward
+constexpr int DT_ROWS = 64;  // rows per workgroup (one d_dt_bias partial) in the backward
 
 __device__ __forceinline__ float softplus1(float v) { return fmaxf(v, 0.f) + log1pf(expf(-fabsf(v))); }
 
@@ -692,6 +692,7 @@ __global__ __launch_bounds__(256) void dt_softplus_bwd_kernel(const T* __restric
     float acc = 0.f;
     if (s < S && h < H) {
       const float bh = bias[h];
+#pragma unroll 4
       for (int64_t r = r0 + s; r < r1; r += S) {
         const int64_t i = r * H + h;
         const float g = ddt[i] / (1.f + expf(-(load_f(raw, i) + bh)));
