@@ -320,25 +320,50 @@ def make_step(cfg, d):
 
 
 def cpu_baseline(cfg, d, batches: int, min_wall_s: float = 1.0):
+    """The oracle on the host over the first `batches` batch rows of the same
+    workload: SSD fwd + bwd, and for the block slice the whole chain the GPU
+    step runs (dt activation, conv1d + SiLU, SSD, RMSNorm-gated, forward and
+    backward)."""
     import numpy as np
     import oracle
     nb = min(cfg.batch, max(1, batches))
     sl = slice(0, nb)
-    args = (d["x"].values[sl], d["dt"].values[sl], d["A_log"], d["B"].values[sl], d["C"].values[sl], d["D"])
     h0 = None if d.get("h0") is None else d["h0"][sl]
     threads = oracle.default_threads()
+    b, T, H, P, G, N = nb, cfg.seqlen, cfg.nheads, cfg.headdim, cfg.ngroups, cfg.dstate
+
+    def run():
+        if not cfg.shell:
+            args = (d["x"].values[sl], d["dt"].values[sl], d["A_log"], d["B"].values[sl], d["C"].values[sl], d["D"])
+            oracle.ssd_fwd(*args, h0, chunk=cfg.chunk, nthreads=threads)
+            oracle.ssd_bwd(*args, d["dy"].values[sl], h0, nthreads=threads)
+            return
+        di = cfg.d_inner
+        dt = oracle.dt_softplus_fwd(d["dt_raw"].values[sl], d["dt_bias"])
+        _, act = oracle.conv_fwd(d["xBC"].values[sl], d["conv_w"], d["conv_b"])
+        x = act[..., :di].reshape(b, T, H, P)
+        Bm = act[..., di:di + G * N].reshape(b, T, G, N)
+        Cm = act[..., di + G * N:].reshape(b, T, G, N)
+        args = (x, dt, d["A_log"], Bm, Cm, d["D"])
+        y = oracle.ssd_fwd(*args, h0, chunk=cfg.chunk, nthreads=threads)["y"].reshape(b, T, di)
+        _, inv = oracle.rmsnorm_fwd(y, d["z"].values[sl], d["norm_w"], cfg.norm_eps)
+        gy, _, _ = oracle.rmsnorm_bwd(y, d["z"].values[sl], d["norm_w"], inv, d["gout"].values[sl])
+        g = oracle.ssd_bwd(*args, gy.reshape(b, T, H, P), h0, nthreads=threads)
+        gact = np.concatenate([g["dx"].reshape(b, T, di), g["dB"].reshape(b, T, -1), g["dC"].reshape(b, T, -1)], -1)
+        oracle.conv_bwd(d["xBC"].values[sl], d["conv_w"], d["conv_b"], gact)
+        oracle.dt_softplus_bwd(d["dt_raw"].values[sl], d["dt_bias"], g["ddt"])
+
     # repeat the sample until about a second of wall time (10-30 s of CPU
     # work on a 16-thread host) has been measured
     reps, el = 0, 0.0
     while reps == 0 or el < min_wall_s:
         t0 = time.perf_counter()
-        oracle.ssd_fwd(*args, h0, chunk=cfg.chunk, nthreads=threads)
-        oracle.ssd_bwd(*args, d["dy"].values[sl], h0, nthreads=threads)
+        run()
         el += time.perf_counter() - t0
         reps += 1
-    del np
+    what = "SSD fwd+bwd" if not cfg.shell else "dt activation + conv1d/SiLU + SSD + RMSNorm-gated, fwd+bwd"
     return {"value": reps * nb * cfg.seqlen / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": (f"sequential f64 oracle, SSD fwd+bwd on batch rows 0..{nb - 1} of {cfg.batch} "
+            "sample": (f"sequential f64 oracle, {what} on batch rows 0..{nb - 1} of {cfg.batch} "
                        f"({nb * cfg.seqlen} tokens) run {reps} times, {el:.1f} s wall on {threads} threads; "
                        "tokens/s of that sample")}
 
