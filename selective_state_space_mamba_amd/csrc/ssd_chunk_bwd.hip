@@ -614,11 +614,15 @@ __global__ __launch_bounds__(NT8) void chunk_bwd_row_kernel(
       if (q == 0) sRow[rw][32 * cw + 16 * t + r] = rr;
     }
     // dD partial over this block's rows
+    // (lane p of a 64-lane row group, rows il = tid / 64, +8, ...: no per-element division)
     float dd = 0.f;
-    for (int e = tid; e < vi * P; e += NT8) {
-      const int il = e / P, p = e % P;
-      const int64_t o = (row0 + i0 + il) * HP + static_cast<int64_t>(h) * P + p;
-      dd += load_f(dy, o) * load_f(x, o);
+    {
+      const int p = tid % PMAX;
+      if (p < P)
+        for (int il = tid / PMAX; il < vi; il += NT8 / PMAX) {
+          const int64_t o = (row0 + i0 + il) * HP + static_cast<int64_t>(h) * P + p;
+          dd += load_f(dy, o) * load_f(x, o);
+        }
     }
     dd = wave_sum(dd);
     if (l == 0) sTmp[8 + w] = dd;
