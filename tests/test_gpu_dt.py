@@ -109,3 +109,20 @@ def test_autograd_ssd_scan(dtype, with_bias):
         errs.update(ddt=relerr(host(dt.grad), r_ddt))
     print("[parity ssd_scan]", dtype, with_bias, {k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
     assert all(v <= TOL[dtype] for v in errs.values()), errs
+
+
+def test_dt_softplus_extreme_arguments():
+    """Large positive and negative pre-activations stay finite: softplus(v) -> v
+    and -> e^v, its gradient -> 1 and -> 0 (no overflow of e^v)."""
+    raw = np.array([[[-100.0, -30.0, 0.0, 30.0, 100.0, 88.0, -88.0, 1e-3]]], dtype=np.float32)
+    bias = np.zeros(8, dtype=np.float32)
+    ddt = np.ones_like(raw)
+    dt = ssd.dt_softplus_fwd(dev(raw), dev(bias))
+    g_raw, g_bias = ssd.dt_softplus_bwd(dev(raw), dev(bias), dev(ddt))
+    torch.cuda.synchronize()
+    r_dt = oracle.dt_softplus_fwd(raw, bias)
+    r_raw, r_bias = oracle.dt_softplus_bwd(raw, bias, ddt)
+    assert np.all(np.isfinite(host(dt))) and np.all(np.isfinite(host(g_raw)))
+    np.testing.assert_allclose(host(dt), r_dt, rtol=1e-6, atol=1e-30)
+    np.testing.assert_allclose(host(g_raw), r_raw, rtol=1e-6, atol=1e-30)
+    np.testing.assert_allclose(host(g_bias), r_bias, rtol=1e-6, atol=1e-30)
