@@ -61,6 +61,23 @@ def test_chunk_lengths(chunk):
     compare(gpu_ssd(cfg, d), oracle_ssd(d, chunk), TOL["f32"], label=f"chunk={chunk}")
 
 
+@pytest.mark.parametrize("chunk", [32, 64, 128])
+def test_chunk_lengths_bf16(chunk):
+    # the bf16 kernels at chunk lengths below the workloads' 256 (one, two and
+    # four 64-row blocks per chunk; a half block at 32)
+    cfg = SSDConfig("chunks_bf16", 2, 512, 8, 64, 128, 2, chunk, "bf16", init_state=True, seed=15)
+    d = make_inputs(cfg)
+    compare(gpu_ssd(cfg, d), oracle_ssd(d, chunk), TOL["bf16"], label=f"bf16 chunk={chunk}")
+
+
+def test_f32_three_heads_per_group():
+    # the f32 two-pass state form and the general kernels with an odd number of
+    # heads per group (3 groups of 3) and 40-wide headdim
+    cfg = SSDConfig("f32_hpg3", 2, 768, 9, 40, 64, 3, 256, "f32", init_state=True, seed=16)
+    d = make_inputs(cfg)
+    compare(gpu_ssd(cfg, d), oracle_ssd(d, cfg.chunk), TOL["f32"], label="f32 hpg=3 P=40")
+
+
 def test_many_chunks_bf16():
     # 256 chunks per head (over 128): the dt gradient and the dA_log / dD sums
     # take their two-launch form (the workloads above take the one-launch form)
