@@ -27,4 +27,4 @@ from ._binding import (  # noqa: F401
     ssd_workspace_bytes,
     version,
 )
-from .autograd import ssd_scan  # noqa: F401,E402
+from .autograd import mamba2_block_core, ssd_scan  # noqa: F401,E402

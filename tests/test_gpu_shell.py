@@ -125,3 +125,45 @@ def test_block_slice_end_to_end():
             "ddt_raw": relerr(host(g_raw), r_raw), "d_dt_bias": relerr(host(g_bias), r_bias)}
     print("[parity block chain]", {k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
     assert all(v <= TOL["bf16"] for v in errs.values()), errs
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_autograd_block_core(dtype):
+    """mamba2_block_core's autograd gradients of sum(gout * out) + <dfinal,
+    final> with a carried initial state, against the oracle chain."""
+    from ssd_inputs import SSDConfig
+    cfg = SSDConfig("blk_ag", 2, 256, 4, 64, 64, 1, 128, dtype, init_state=True, shell=True, seed=91)
+    d = make_inputs(cfg)
+    b, T, H, P, N, G, Q, di = cfg.batch, cfg.seqlen, cfg.nheads, cfg.headdim, cfg.dstate, cfg.ngroups, cfg.chunk, cfg.d_inner
+    dfin = np.random.default_rng(92).standard_normal((b, H, P, N)).astype(np.float32)
+    xbc, raw, z = (dev(d[k]).requires_grad_() for k in ("xBC", "dt_raw", "z"))
+    cw, cb, bias, A_log, D, nw = (dev(d[k]).requires_grad_() for k in ("conv_w", "conv_b", "dt_bias", "A_log", "D", "norm_w"))
+    h0 = dev(d["h0"]).requires_grad_()
+    out, fin = ssd.mamba2_block_core(xbc, raw, z, cw, cb, bias, A_log, D, nw, ngroups=G, dstate=N, headdim=P,
+                                     chunk=Q, eps=cfg.norm_eps, init_state=h0)
+    loss = (out.float() * dev(d["gout"]).float()).sum() + (fin * dev(dfin)).sum()
+    loss.backward()
+    torch.cuda.synchronize()
+
+    _, act = oracle.conv_fwd(d["xBC"].values, d["conv_w"], d["conv_b"])
+    rx = act[..., :di].reshape(b, T, H, P)
+    rB = act[..., di:di + G * N].reshape(b, T, G, N)
+    rC = act[..., di + G * N:].reshape(b, T, G, N)
+    r_dt = oracle.dt_softplus_fwd(d["dt_raw"].values, d["dt_bias"])
+    sargs = (rx, r_dt, d["A_log"], rB, rC, d["D"])
+    rf = oracle.ssd_fwd(*sargs, d["h0"])
+    ry = rf["y"].reshape(b, T, di)
+    rout, rinv = oracle.rmsnorm_fwd(ry, d["z"].values, d["norm_w"], cfg.norm_eps)
+    rgy, rgz, rgw = oracle.rmsnorm_bwd(ry, d["z"].values, d["norm_w"], rinv, d["gout"].values)
+    rg = oracle.ssd_bwd(*sargs, rgy.reshape(b, T, H, P), d["h0"], dfinal=dfin)
+    gact = np.concatenate([rg["dx"].reshape(b, T, di), rg["dB"].reshape(b, T, -1), rg["dC"].reshape(b, T, -1)], -1)
+    rdxbc, rdcw, rdcb = oracle.conv_bwd(d["xBC"].values, d["conv_w"], d["conv_b"], gact)
+    r_raw, r_bias = oracle.dt_softplus_bwd(d["dt_raw"].values, d["dt_bias"], rg["ddt"])
+    errs = {"out": relerr(host(out), rout), "final": relerr(host(fin), rf["final"]),
+            "dxbc": relerr(host(xbc.grad), rdxbc), "ddt_raw": relerr(host(raw.grad), r_raw),
+            "dz": relerr(host(z.grad), rgz), "dconv_w": relerr(host(cw.grad), rdcw),
+            "dconv_b": relerr(host(cb.grad), rdcb), "d_dt_bias": relerr(host(bias.grad), r_bias),
+            "dA_log": relerr(host(A_log.grad), rg["dA_log"]), "dD": relerr(host(D.grad), rg["dD"]),
+            "dnorm_w": relerr(host(nw.grad), rgw), "dh0": relerr(host(h0.grad), rg["dh0"])}
+    print("[parity block core autograd]", dtype, {k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
+    assert all(v <= TOL[dtype] for v in errs.values()), errs
