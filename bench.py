@@ -64,7 +64,7 @@ def log(*a):
 def algorithmic_bytes(cfg, kernel: str) -> float:
     """Bytes one launch must move at minimum: each input it needs read once and
     each output written once, at the storage dtypes (the per-token figures are
-    listed in DESIGN.md)."""
+    the per_token expressions below)."""
     s_a = 2 if cfg.dtype == "bf16" else 4
     s_y = s_a
     tok = cfg.batch * cfg.seqlen
@@ -393,8 +393,9 @@ def main():
                               args.calibrate_copy_mb)
         return
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): this build has no multi-GPU path; "
-              "see DESIGN.md for how the SSD would shard.", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the SSD path here has no multi-GPU "
+              "code; it would shard by batch rows, by groups of heads, or by time with one state exchange "
+              "per direction.", file=sys.stderr)
         sys.exit(2)
 
     import torch
