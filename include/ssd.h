@@ -173,6 +173,23 @@ int ssd_dt_softplus_bwd(int64_t rows, int64_t nheads, int32_t dtype, const void*
                         const float* dt_bias, const float* ddt, float* ddt_raw, float* d_dt_bias,
                         void* workspace, size_t workspace_bytes, void* stream);
 
+/* Plain GEMM for the input and output projections around the block slice
+ * (the in_proj / out_proj products of a Mamba-2 block's forward and
+ * backward): row-major C[m,n] = alpha * op(A) * op(B) + beta * C with bf16 A
+ * and B, f32 accumulation, and C in c_dtype (SSD_F32 or SSD_BF16).  op(A) is
+ * [m,k]: A stored [m,k], or [k,m] when trans_a != 0; op(B) is [k,n]: B stored
+ * [k,n], or [n,k] when trans_b != 0.  lda, ldb, ldc are row strides in
+ * elements.  Runs rocBLAS gemm_ex on the caller's stream; unlike the other
+ * entry points, the rocBLAS handle (one per device, created on first use)
+ * holds device memory of its own. */
+int ssd_gemm(int32_t trans_a, int32_t trans_b, int64_t m, int64_t n, int64_t k, float alpha,
+             const void* A, int64_t lda, const void* B, int64_t ldb, float beta, void* C,
+             int32_t c_dtype, int64_t ldc, void* stream);
+
+/* dst[i] = src[i] rounded to bf16 (nearest even), i < n: the f32 gradients of
+ * the block slice cast for the bf16 projection GEMMs. */
+int ssd_cast_f32_to_bf16(int64_t n, const float* src, void* dst, void* stream);
+
 /* Description of the last failure on the calling thread ("" after success). */
 const char* ssd_last_error(void);
 

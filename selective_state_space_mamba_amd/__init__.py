@@ -11,10 +11,12 @@ the library is missing the calls raise.
 """
 from ._binding import (  # noqa: F401
     SSDError,
+    cast_bf16,
     conv1d_silu_bwd,
     conv1d_silu_fwd,
     dt_softplus_bwd,
     dt_softplus_fwd,
+    gemm,
     library_path,
     load_library,
     profile_enable,
@@ -27,4 +29,4 @@ from ._binding import (  # noqa: F401
     ssd_workspace_bytes,
     version,
 )
-from .autograd import mamba2_block_core, ssd_scan  # noqa: F401,E402
+from .autograd import mamba2_block, mamba2_block_core, ssd_scan  # noqa: F401,E402

@@ -67,6 +67,10 @@ def load_library():
     lib.ssd_dt_softplus_bwd_workspace_bytes.restype = sz
     lib.ssd_dt_softplus_bwd.argtypes = [i64, i64, i32] + [vp] * 5 + [vp, sz, vp]
     lib.ssd_dt_softplus_bwd.restype = ctypes.c_int
+    lib.ssd_gemm.argtypes = [i32, i32, i64, i64, i64, f32, vp, i64, vp, i64, f32, vp, i32, i64, vp]
+    lib.ssd_gemm.restype = ctypes.c_int
+    lib.ssd_cast_f32_to_bf16.argtypes = [i64, vp, vp, vp]
+    lib.ssd_cast_f32_to_bf16.restype = ctypes.c_int
     lib.ssd_last_error.argtypes = []
     lib.ssd_last_error.restype = ctypes.c_char_p
     lib.ssd_version.argtypes = []
@@ -353,3 +357,36 @@ def dt_softplus_bwd(dt_raw, dt_bias, ddt, workspace=None, out=None, stream=None)
     _check(lib.ssd_dt_softplus_bwd(rows, H, _code(dt_raw.dtype), _ptr(dt_raw), _ptr(dt_bias), _ptr(ddt),
                                    _ptr(ddt_raw), _ptr(d_bias), _ptr(workspace), wsz, _stream(stream)))
     return ddt_raw, d_bias
+
+
+def gemm(A, B, trans_a: bool = False, trans_b: bool = False, out=None, out_dtype=torch.bfloat16,
+         alpha: float = 1.0, beta: float = 0.0, stream=None):
+    """out[m,n] = alpha * op(A) @ op(B) + beta * out for 2-D contiguous bf16 A, B
+    (op transposes when trans_*); out in out_dtype (bf16 or f32)."""
+    lib = load_library()
+    if A.dtype != torch.bfloat16 or B.dtype != torch.bfloat16:
+        raise TypeError("gemm takes bfloat16 operands")
+    if A.dim() != 2 or B.dim() != 2 or not A.is_contiguous() or not B.is_contiguous():
+        raise ValueError("gemm takes contiguous 2-D operands")
+    m, k = (A.shape[1], A.shape[0]) if trans_a else (A.shape[0], A.shape[1])
+    kb, n = (B.shape[1], B.shape[0]) if trans_b else (B.shape[0], B.shape[1])
+    if kb != k:
+        raise ValueError(f"gemm: inner sizes {k} and {kb} differ")
+    if out is None:
+        out = torch.empty((m, n), dtype=out_dtype, device=A.device)
+    _need(out, "out", (m, n), None, A.device)
+    _check(lib.ssd_gemm(int(trans_a), int(trans_b), m, n, k, float(alpha), _ptr(A), A.shape[1], _ptr(B),
+                        B.shape[1], float(beta), _ptr(out), _code(out.dtype), n, _stream(stream)))
+    return out
+
+
+def cast_bf16(src, out=None, stream=None):
+    """bf16 copy (round to nearest even) of a contiguous f32 tensor."""
+    lib = load_library()
+    if src.dtype != torch.float32 or not src.is_contiguous():
+        raise TypeError("cast_bf16 takes a contiguous float32 tensor")
+    if out is None:
+        out = torch.empty(src.shape, dtype=torch.bfloat16, device=src.device)
+    _need(out, "out", tuple(src.shape), torch.bfloat16, src.device)
+    _check(lib.ssd_cast_f32_to_bf16(src.numel(), _ptr(src), _ptr(out), _stream(stream)))
+    return out

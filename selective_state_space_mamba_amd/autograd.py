@@ -10,6 +10,8 @@ softplus backward inside the one function.
 ``mamba2_block_core`` does the same for the block slice between the input and
 output projections of a Mamba-2 block: dt activation, causal depthwise conv1d
 + SiLU split into x / B / C, the SSD, and the RMSNorm-gated output.
+``mamba2_block`` adds the projections (bf16 GEMMs through the library's
+rocBLAS entry point).
 
 Every computation runs in the library's kernels; the functions only route
 tensors.  Gradients come back in f32 (autograd casts them to a bf16 input's
@@ -58,43 +60,56 @@ def ssd_scan(x: torch.Tensor, dt: torch.Tensor, A_log: torch.Tensor, B: torch.Te
     return _SSDScan.apply(x, dt, A_log, B, C, D, init_state, dt_bias, chunk)
 
 
+def _core_fwd(xbc, dt_raw, z, conv_w, conv_b, dt_bias, A_log, D, norm_w, init_state, dims):
+    """Forward of the block slice; returns (out, final_state, tensors saved for _core_bwd)."""
+    ngroups, dstate, headdim, chunk, eps = dims
+    b, T, _ = xbc.shape
+    d_inner = z.shape[-1]
+    H = d_inner // headdim
+    dt = _b.dt_softplus_fwd(dt_raw, dt_bias)
+    xs, Bs, Cs = _b.conv1d_silu_fwd(xbc, conv_w, conv_b, d_inner, ngroups, dstate)
+    xs = xs.view(b, T, H, headdim)
+    y, fin, cs = _b.ssd_fwd(xs, dt, A_log, Bs, Cs, D, init_state, chunk=chunk)
+    out, inv = _b.rmsnorm_gated_fwd(y.view(b, T, d_inner), z, norm_w, eps)
+    return out, fin, (dt, xs, Bs, Cs, y, inv, cs)
+
+
+def _core_bwd(xbc, dt_raw, z, conv_w, conv_b, dt_bias, A_log, D, norm_w, init_state, saved, dims, gout, gfin,
+              want_dh0):
+    """Backward of the block slice: (dxbc, ddt_raw, dz, dconv_w, dconv_b, d_dt_bias,
+    dA_log, dD, dnorm_w, d_init_state), all f32."""
+    dt, xs, Bs, Cs, y, inv, cs = saved
+    ngroups, dstate, headdim, chunk, eps = dims
+    b, T, d_inner = z.shape
+    H = d_inner // headdim
+    # the gradient handed to the SSD backward is stored in the activation
+    # dtype, as the block-slice step does
+    gy, gz, gnw = _b.rmsnorm_gated_bwd(y.view(b, T, d_inner), z, norm_w, inv, gout, dy_dtype=xbc.dtype)
+    g = _b.ssd_bwd(xs, dt, A_log, Bs, Cs, D, gy.view(b, T, H, headdim), init_state, chunk_states=cs,
+                   chunk=chunk, want_d_init_state=want_dh0,
+                   d_final_state=None if gfin is None else gfin.float().contiguous())
+    dxbc, dcw, dcb = _b.conv1d_silu_bwd(xbc, conv_w, conv_b, g["dx"].view(b, T, d_inner), g["dB"], g["dC"],
+                                        d_inner, ngroups, dstate)
+    ddt_raw, d_bias = _b.dt_softplus_bwd(dt_raw, dt_bias, g["ddt"])
+    return dxbc, ddt_raw, gz, dcw, dcb, d_bias, g["dA_log"], g["dD"], gnw, g["d_init_state"]
+
+
 class _BlockCore(torch.autograd.Function):
     @staticmethod
     def forward(ctx, xbc, dt_raw, z, conv_w, conv_b, dt_bias, A_log, D, norm_w, init_state, dims):
-        ngroups, dstate, headdim, chunk, eps = dims
-        b, T, _ = xbc.shape
-        d_inner = z.shape[-1]
-        H = d_inner // headdim
-        dt = _b.dt_softplus_fwd(dt_raw, dt_bias)
-        xs, Bs, Cs = _b.conv1d_silu_fwd(xbc, conv_w, conv_b, d_inner, ngroups, dstate)
-        xs = xs.view(b, T, H, headdim)
-        y, fin, cs = _b.ssd_fwd(xs, dt, A_log, Bs, Cs, D, init_state, chunk=chunk)
-        out, inv = _b.rmsnorm_gated_fwd(y.view(b, T, d_inner), z, norm_w, eps)
-        ctx.save_for_backward(xbc, dt_raw, z, conv_w, conv_b, dt_bias, A_log, D, norm_w, init_state,
-                              dt, xs, Bs, Cs, y, inv, cs)
+        out, fin, saved = _core_fwd(xbc, dt_raw, z, conv_w, conv_b, dt_bias, A_log, D, norm_w, init_state, dims)
+        ctx.save_for_backward(xbc, dt_raw, z, conv_w, conv_b, dt_bias, A_log, D, norm_w, init_state, *saved)
         ctx.dims = dims
         return out, fin
 
     @staticmethod
     def backward(ctx, gout, gfin):
-        (xbc, dt_raw, z, conv_w, conv_b, dt_bias, A_log, D, norm_w, init_state,
-         dt, xs, Bs, Cs, y, inv, cs) = ctx.saved_tensors
-        ngroups, dstate, headdim, chunk, eps = ctx.dims
-        b, T, d_inner = z.shape
-        H = d_inner // headdim
+        t = ctx.saved_tensors
         if gout is None:
-            gout = torch.zeros_like(z)
-        # the gradient handed to the SSD backward is stored in the activation
-        # dtype, as the block-slice step does
-        gy, gz, gnw = _b.rmsnorm_gated_bwd(y.view(b, T, d_inner), z, norm_w, inv, gout.contiguous(),
-                                           dy_dtype=xbc.dtype)
-        g = _b.ssd_bwd(xs, dt, A_log, Bs, Cs, D, gy.view(b, T, H, headdim), init_state, chunk_states=cs,
-                       chunk=chunk, want_d_init_state=init_state is not None and ctx.needs_input_grad[9],
-                       d_final_state=None if gfin is None else gfin.float().contiguous())
-        dxbc, dcw, dcb = _b.conv1d_silu_bwd(xbc, conv_w, conv_b, g["dx"].view(b, T, d_inner), g["dB"], g["dC"],
-                                            d_inner, ngroups, dstate)
-        ddt_raw, d_bias = _b.dt_softplus_bwd(dt_raw, dt_bias, g["ddt"])
-        return (dxbc, ddt_raw, gz, dcw, dcb, d_bias, g["dA_log"], g["dD"], gnw, g["d_init_state"], None)
+            gout = torch.zeros_like(t[2])
+        grads = _core_bwd(*t[:10], t[10:], ctx.dims, gout.contiguous(), gfin,
+                          t[9] is not None and ctx.needs_input_grad[9])
+        return (*grads, None)
 
 
 def mamba2_block_core(xbc: torch.Tensor, dt_raw: torch.Tensor, z: torch.Tensor, conv_w: torch.Tensor,
@@ -109,3 +124,57 @@ def mamba2_block_core(xbc: torch.Tensor, dt_raw: torch.Tensor, z: torch.Tensor, 
     Returns (out [b,T,d_inner] = RMSNorm(y) * norm_w * silu(z), final_state)."""
     return _BlockCore.apply(xbc, dt_raw, z, conv_w, conv_b, dt_bias, A_log, D, norm_w, init_state,
                             (ngroups, dstate, headdim, chunk, eps))
+
+
+class _Block(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, u, W_z, W_xbc, W_dt, conv_w, conv_b, dt_bias, A_log, D, norm_w, W_out, init_state, dims):
+        b, T, dm = u.shape
+        u2 = u.reshape(b * T, dm)
+        z = _b.gemm(u2, W_z, trans_b=True).view(b, T, -1)
+        xbc = _b.gemm(u2, W_xbc, trans_b=True).view(b, T, -1)
+        dt_raw = _b.gemm(u2, W_dt, trans_b=True).view(b, T, -1)
+        out, fin, saved = _core_fwd(xbc, dt_raw, z, conv_w, conv_b, dt_bias, A_log, D, norm_w, init_state, dims)
+        o = _b.gemm(out.view(b * T, -1), W_out, trans_b=True).view(b, T, dm)
+        ctx.save_for_backward(u, W_z, W_xbc, W_dt, W_out, out, xbc, dt_raw, z, conv_w, conv_b, dt_bias, A_log, D,
+                              norm_w, init_state, *saved)
+        ctx.dims = dims
+        return o, fin
+
+    @staticmethod
+    def backward(ctx, go, gfin):
+        t = ctx.saved_tensors
+        u, W_z, W_xbc, W_dt, W_out, out = t[:6]
+        b, T, dm = u.shape
+        u2 = u.reshape(b * T, dm)
+        if go is None:
+            go = torch.zeros_like(u)
+        go2 = go.contiguous().view(b * T, dm)
+        gout = _b.gemm(go2, W_out, out_dtype=torch.float32).view(b, T, -1)
+        dW_out = _b.gemm(go2, out.view(b * T, -1), trans_a=True, out_dtype=torch.float32)
+        init_state = t[15]
+        (dxbc, ddt_raw, dz, dcw, dcb, d_bias, dA, dD, dnw, dh0) = _core_bwd(
+            *t[6:16], t[16:], ctx.dims, gout, gfin, init_state is not None and ctx.needs_input_grad[11])
+        du = None
+        dWs = []
+        for g, W in ((dz, W_z), (dxbc, W_xbc), (ddt_raw, W_dt)):
+            gb = _b.cast_bf16(g.view(b * T, -1))
+            du = _b.gemm(gb, W, out=du, out_dtype=torch.float32, beta=0.0 if du is None else 1.0)
+            dWs.append(_b.gemm(gb, u2, trans_a=True, out_dtype=torch.float32))
+        return (du.view(b, T, dm), dWs[0], dWs[1], dWs[2], dcw, dcb, d_bias, dA, dD, dnw, dW_out, dh0, None)
+
+
+def mamba2_block(u: torch.Tensor, W_z: torch.Tensor, W_xbc: torch.Tensor, W_dt: torch.Tensor,
+                 conv_w: torch.Tensor, conv_b: torch.Tensor, dt_bias: torch.Tensor, A_log: torch.Tensor,
+                 D: torch.Tensor, norm_w: torch.Tensor, W_out: torch.Tensor, *, ngroups: int, dstate: int,
+                 headdim: int, chunk: int = 256, eps: float = 1e-5, init_state: Optional[torch.Tensor] = None
+                 ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Differentiable Mamba-2 block with its projections, bf16 activations and
+    weights: z, xbc, dt_raw = u W_z^T, u W_xbc^T, u W_dt^T (the three parts of
+    in_proj, [out_features, d_model] each), the block slice of
+    mamba2_block_core, and o = out W_out^T (W_out [d_model, d_inner]).  The
+    projections run through ssd_gemm (rocBLAS, f32 accumulation); the slice's
+    f32 gradients are rounded to bf16 for the backward products.  Returns
+    (o [b,T,d_model], final_state)."""
+    return _Block.apply(u, W_z, W_xbc, W_dt, conv_w, conv_b, dt_bias, A_log, D, norm_w, W_out, init_state,
+                        (ngroups, dstate, headdim, chunk, eps))

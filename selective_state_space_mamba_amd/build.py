@@ -16,7 +16,7 @@ BUILD = os.path.join(HERE, "_build")
 LIB_NAME = "libssd_mi355x.so"
 ARCH = "gfx950"
 
-SOURCES = ["ssd_state.hip", "ssd_chunk_fwd.hip", "ssd_chunk_bwd.hip", "ssd_bwd_bf16.hip", "ssd_fwd_bf16.hip", "ssd_state_bf16.hip", "shell.hip", "capi.cpp"]
+SOURCES = ["ssd_state.hip", "ssd_chunk_fwd.hip", "ssd_chunk_bwd.hip", "ssd_bwd_bf16.hip", "ssd_fwd_bf16.hip", "ssd_state_bf16.hip", "shell.hip", "gemm.cpp", "capi.cpp"]
 
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
@@ -54,7 +54,9 @@ def build(verbose: bool = False) -> str:
         objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
     out = lib_path()
     tmp = out + ".tmp%d" % os.getpid()
-    cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-L" + os.path.join(rocm, "lib"),
+           "-lrocblas", "-Wl,-rpath," + os.path.join(rocm, "lib"), "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)

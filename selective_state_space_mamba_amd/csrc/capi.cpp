@@ -12,6 +12,7 @@
 
 #include "../../include/ssd.h"
 #include "ssd_common.hpp"
+#include "gemm_launch.hpp"
 #include "shell_launch.hpp"
 #include "ssd_launch.hpp"
 
@@ -617,6 +618,41 @@ int ssd_dt_softplus_bwd(int64_t rows, int64_t nheads, int32_t dtype, const void*
   SSD_LAUNCH(ssd::launch_dt_softplus_bwd(rows, static_cast<int>(nheads), static_cast<ssd::DType>(dtype), dt_raw,
                                          dt_bias, ddt, ddt_raw, d_dt_bias, static_cast<float*>(workspace), st),
              "dt_softplus_bwd");
+  return ok();
+}
+
+// ------------------------------------------------------------ projections
+
+int ssd_gemm(int32_t trans_a, int32_t trans_b, int64_t m, int64_t n, int64_t k, float alpha, const void* A,
+             int64_t lda, const void* B, int64_t ldb, float beta, void* C, int32_t c_dtype, int64_t ldc,
+             void* stream) {
+  if (!valid_dtype(c_dtype)) return fail(SSD_ERR_DTYPE, "gemm: c_dtype %d is not SSD_F32 or SSD_BF16", c_dtype);
+  if (m < 0 || n < 0 || k < 0) return fail(SSD_ERR_INVALID_ARG, "gemm: m, n, k must be >= 0");
+  if (m == 0 || n == 0) return ok();
+  if (!C || (k > 0 && (!A || !B))) return fail(SSD_ERR_INVALID_ARG, "gemm: A, B and C are required");
+  // row strides: op(A) rows of k (A stored [m,k]) or A stored [k,m]; likewise B
+  if (lda < (trans_a ? m : k) || ldb < (trans_b ? k : n) || ldc < n || lda < 1 || ldb < 1)
+    return fail(SSD_ERR_SHAPE, "gemm: a row stride is shorter than its row");
+  const void* ptrs[] = {A, B, C};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return fail(SSD_ERR_ALIGN, "gemm: a matrix pointer is not 16-byte aligned");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipEvent_t p_ = prof_begin(st, "gemm");
+  const ssd::GemmStatus gs = ssd::gemm_bf16(trans_a != 0, trans_b != 0, m, n, k, alpha, A, lda, B, ldb, beta, C,
+                                            c_dtype == SSD_BF16, ldc, st);
+  if (gs == ssd::GemmStatus::kHip) return fail(SSD_ERR_HIP, "gemm: no current HIP device");
+  if (gs == ssd::GemmStatus::kBlas) return fail(SSD_ERR_HIP, "gemm: rocBLAS gemm_ex failed");
+  prof_end(p_, "gemm", st);
+  return ok();
+}
+
+int ssd_cast_f32_to_bf16(int64_t n, const float* src, void* dst, void* stream) {
+  if (n < 0) return fail(SSD_ERR_INVALID_ARG, "cast: n must be >= 0");
+  if (n == 0) return ok();
+  if (!src || !dst) return fail(SSD_ERR_INVALID_ARG, "cast: src and dst are required");
+  if (!aligned16(src) || !aligned16(dst)) return fail(SSD_ERR_ALIGN, "cast: a pointer is not 16-byte aligned");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  SSD_LAUNCH(ssd::launch_cast_bf16(n, src, dst, st), "cast_bf16");
   return ok();
 }
 

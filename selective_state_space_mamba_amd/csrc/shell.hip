@@ -22,6 +22,7 @@
 // The scalar kernels (one channel per thread, a row per workgroup) take the
 // other shapes.  Weight gradients are per-(batch, 256-step run) or per-64-row
 // partials summed in a fixed order, so results are bitwise reproducible.
+#include "gemm_launch.hpp"
 #include "ssd_common.hpp"
 #include "shell_launch.hpp"
 
@@ -919,6 +920,27 @@ hipError_t launch_dt_softplus_bwd(int64_t rows, int H, DType dt, const void* raw
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   launch_part_reduce(part, d_bias, nullptr, dt_nparts(rows), H, 0, st);
+  return hipGetLastError();
+}
+
+// f32 -> bf16 (round to nearest even), four elements per thread when aligned.
+__global__ __launch_bounds__(256) void cast_bf16_kernel(const float* __restrict__ src, uint16_t* __restrict__ dst,
+                                                       int64_t n) {
+  const int64_t i = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 4;
+  if (i + 4 <= n) {
+    float f[4];
+    ldv<4>(src + i, f);
+    stv<4>(dst + i, f);
+  } else {
+    for (int64_t e = i; e < n; ++e) dst[e] = f32_to_bf16_bits(src[e]);
+  }
+}
+
+hipError_t launch_cast_bf16(int64_t n, const float* src, void* dst, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  const int64_t blocks = (n + 1023) / 1024;
+  hipLaunchKernelGGL(cast_bf16_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, src,
+                     static_cast<uint16_t*>(dst), n);
   return hipGetLastError();
 }
 

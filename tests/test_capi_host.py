@@ -173,3 +173,18 @@ def test_product_path_does_not_import_the_oracle():
             if fn.endswith((".py", ".cpp", ".hip", ".hpp", ".h")):
                 text = open(os.path.join(dirpath, fn)).read()
                 assert "oracle" not in text.lower(), fn
+
+
+def test_gemm_and_cast_argument_checks(lib):
+    f = ctypes.c_void_p(FAKE)
+    i64 = ctypes.c_int64
+    # c_dtype unknown, negative size, row stride shorter than the row, misaligned
+    assert lib.ssd_gemm(0, 0, i64(4), i64(4), i64(4), 1.0, f, i64(4), f, i64(4), 0.0, f, 9, i64(4), None) == -3
+    assert lib.ssd_gemm(0, 0, i64(-1), i64(4), i64(4), 1.0, f, i64(4), f, i64(4), 0.0, f, 0, i64(4), None) == -1
+    assert lib.ssd_gemm(0, 1, i64(4), i64(8), i64(16), 1.0, f, i64(16), f, i64(8), 0.0, f, 0, i64(8), None) == -2
+    assert lib.ssd_gemm(0, 0, i64(4), i64(4), i64(4), 1.0, ctypes.c_void_p(FAKE + 2), i64(4), f, i64(4), 0.0, f, 0,
+                        i64(4), None) == -6
+    assert lib.ssd_gemm(0, 0, i64(0), i64(4), i64(4), 1.0, None, i64(4), None, i64(4), 0.0, None, 0, i64(4), None) == 0
+    assert lib.ssd_cast_f32_to_bf16(i64(-1), f, f, None) == -1
+    assert lib.ssd_cast_f32_to_bf16(i64(8), None, f, None) == -1
+    assert lib.ssd_cast_f32_to_bf16(i64(0), None, None, None) == 0
