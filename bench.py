@@ -288,6 +288,8 @@ def make_step(cfg, d):
                         workspace=wsb)
         return step
 
+    if cfg.d_model:
+        return make_train_step(cfg, d)
     xbc, z, gout = to_dev(d["xBC"]), to_dev(d["z"]), to_dev(d["gout"])
     dt_raw, dt_bias = to_dev(d["dt_raw"]), to_dev(d["dt_bias"])
     conv_w, conv_b, norm_w = to_dev(d["conv_w"]), to_dev(d["conv_b"]), to_dev(d["norm_w"])
@@ -319,6 +321,80 @@ def make_step(cfg, d):
     return step
 
 
+def make_train_step(cfg, d):
+    """One training step of a Mamba-2 block with its projections: in_proj parts
+    (z, xBC, dt_raw), the block slice, out_proj, and the backward through all of
+    them, each a C-ABI call on preallocated buffers (the GEMMs through ssd_gemm)."""
+    import torch
+    import selective_state_space_mamba_amd as ssd
+    b, T, H, P, N, G, Q = cfg.batch, cfg.seqlen, cfg.nheads, cfg.headdim, cfg.dstate, cfg.ngroups, cfg.chunk
+    dm, di, cd, M = cfg.d_model, cfg.d_inner, cfg.conv_dim, cfg.batch * cfg.seqlen
+    lib = ssd.load_library()
+    u, Wz, Wx, Wd, Wo, go = (to_dev(d[k]) for k in ("u", "W_z", "W_xbc", "W_dt", "W_out", "go"))
+    conv_w, conv_b, dt_bias = to_dev(d["conv_w"]), to_dev(d["conv_b"]), to_dev(d["dt_bias"])
+    A_log, D, norm_w = to_dev(d["A_log"]), to_dev(d["D"]), to_dev(d["norm_w"])
+    bf = dict(dtype=torch.bfloat16, device="cuda")
+    f32 = dict(dtype=torch.float32, device="cuda")
+    u8 = dict(dtype=torch.uint8, device="cuda")
+    u2, go2 = u.view(M, dm), go.view(M, dm)
+    z, xbc, raw = torch.empty((M, di), **bf), torch.empty((M, cd), **bf), torch.empty((M, H), **bf)
+    dt = torch.empty((M, H), **bf)
+    o = torch.empty((M, dm), **bf)
+    fo = {"y": torch.empty((b, T, H, P), **bf), "final_state": torch.empty((b, H, P, N), **f32),
+          "chunk_states": torch.empty((b, T // Q, H, P, N), **f32)}
+    go_ = {"dx": torch.empty((b, T, H, P), **f32), "ddt": torch.empty((b, T, H), **f32),
+           "dA_log": torch.empty(H, **f32), "dB": torch.empty((b, T, G, N), **f32),
+           "dC": torch.empty((b, T, G, N), **f32), "dD": torch.empty(H, **f32)}
+    gact = torch.empty((M, di), **f32)
+    dWo, dWz, dWx, dWd = (torch.empty(s_, **f32) for s_ in ((dm, di), (di, dm), (cd, dm), (H, dm)))
+    du = torch.empty((M, dm), **f32)
+    gz_bf, gx_bf, gd_bf = torch.empty((M, di), **bf), torch.empty((M, cd), **bf), torch.empty((M, H), **bf)
+    prob = ssd._binding.make_problem(fo["y"], to_dev(d["B"]), Q, torch.bfloat16)
+    wsf = torch.empty(max(1, ssd.ssd_workspace_bytes(prob, False, True)), **u8)
+    wsb = torch.empty(max(1, ssd.ssd_workspace_bytes(prob, True, True)), **u8)
+    wsr = torch.empty(max(1, lib.mamba2_rmsnorm_gated_bwd_workspace_bytes(M, di)), **u8)
+    wsc = torch.empty(max(1, lib.mamba2_conv1d_silu_bwd_workspace_bytes(b, T, di, G, N, conv_w.shape[1])), **u8)
+    wsd = torch.empty(max(1, lib.ssd_dt_softplus_bwd_workspace_bytes(M, H)), **u8)
+
+    def step():
+        ssd.gemm(u2, Wz, trans_b=True, out=z)
+        ssd.gemm(u2, Wx, trans_b=True, out=xbc)
+        ssd.gemm(u2, Wd, trans_b=True, out=raw)
+        ssd.dt_softplus_fwd(raw, dt_bias, out=dt)
+        xs, Bs, Cs = ssd.conv1d_silu_fwd(xbc.view(b, T, cd), conv_w, conv_b, di, G, N)
+        xs = xs.view(b, T, H, P)
+        dt3 = dt.view(b, T, H)
+        y, _, cs = ssd.ssd_fwd(xs, dt3, A_log, Bs, Cs, D, None, chunk=Q, out=fo, workspace=wsf)
+        out, inv = ssd.rmsnorm_gated_fwd(y.view(b, T, di), z.view(b, T, di), norm_w, cfg.norm_eps)
+        ssd.gemm(out.view(M, di), Wo, trans_b=True, out=o)
+        # backward
+        ssd.gemm(go2, Wo, out=gact)
+        ssd.gemm(go2, out.view(M, di), trans_a=True, out=dWo)
+        gy, gz, gw = ssd.rmsnorm_gated_bwd(y.view(b, T, di), z.view(b, T, di), norm_w, inv, gact.view(b, T, di),
+                                           workspace=wsr, dy_dtype=torch.bfloat16)
+        g = ssd.ssd_bwd(xs, dt3, A_log, Bs, Cs, D, gy.view(b, T, H, P), None, chunk_states=cs, chunk=Q, out=go_,
+                        workspace=wsb, want_d_init_state=False)
+        dxbc, _, _ = ssd.conv1d_silu_bwd(xbc.view(b, T, cd), conv_w, conv_b, g["dx"].view(b, T, di), g["dB"],
+                                         g["dC"], di, G, N, workspace=wsc)
+        ddt_raw, _ = ssd.dt_softplus_bwd(raw, dt_bias, g["ddt"].view(M, H), workspace=wsd)
+        ssd.cast_bf16(gz.view(M, di), out=gz_bf)
+        ssd.cast_bf16(dxbc.view(M, cd), out=gx_bf)
+        ssd.cast_bf16(ddt_raw, out=gd_bf)
+        ssd.gemm(gz_bf, Wz, out=du)
+        ssd.gemm(gx_bf, Wx, out=du, beta=1.0)
+        ssd.gemm(gd_bf, Wd, out=du, beta=1.0)
+        ssd.gemm(gz_bf, u2, trans_a=True, out=dWz)
+        ssd.gemm(gx_bf, u2, trans_a=True, out=dWx)
+        ssd.gemm(gd_bf, u2, trans_a=True, out=dWd)
+    return step
+
+
+def train_step_flops(cfg) -> float:
+    """Flops of the projection GEMMs in one training step (forward 1x, backward 2x)."""
+    dm, di, cd, H = cfg.d_model, cfg.d_inner, cfg.conv_dim, cfg.nheads
+    return 3 * 2.0 * cfg.tokens * dm * (di + cd + H + di)
+
+
 def cpu_baseline(cfg, d, batches: int, min_wall_s: float = 1.0):
     """The oracle on the host over the first `batches` batch rows of the same
     workload: SSD fwd + bwd, and for the block slice the whole chain the GPU
@@ -339,19 +415,33 @@ def cpu_baseline(cfg, d, batches: int, min_wall_s: float = 1.0):
             oracle.ssd_bwd(*args, d["dy"].values[sl], h0, nthreads=threads)
             return
         di = cfg.d_inner
-        dt = oracle.dt_softplus_fwd(d["dt_raw"].values[sl], d["dt_bias"])
-        _, act = oracle.conv_fwd(d["xBC"].values[sl], d["conv_w"], d["conv_b"])
+        xbc_v, raw_v, z_v, gout_v = d["xBC"].values[sl], d["dt_raw"].values[sl], d["z"].values[sl], d["gout"].values[sl]
+        if cfg.d_model:  # the projections as f64 matrix products
+            U = d["u"].values[sl].astype(np.float64)
+            WZ, WX, WD, WO = (d[k].values.astype(np.float64) for k in ("W_z", "W_xbc", "W_dt", "W_out"))
+            z_v, xbc_v, raw_v = U @ WZ.T, U @ WX.T, U @ WD.T
+            gout_v = d["go"].values[sl].astype(np.float64) @ WO
+        dt = oracle.dt_softplus_fwd(raw_v, d["dt_bias"])
+        _, act = oracle.conv_fwd(xbc_v, d["conv_w"], d["conv_b"])
         x = act[..., :di].reshape(b, T, H, P)
         Bm = act[..., di:di + G * N].reshape(b, T, G, N)
         Cm = act[..., di + G * N:].reshape(b, T, G, N)
         args = (x, dt, d["A_log"], Bm, Cm, d["D"])
         y = oracle.ssd_fwd(*args, h0, chunk=cfg.chunk, nthreads=threads)["y"].reshape(b, T, di)
-        _, inv = oracle.rmsnorm_fwd(y, d["z"].values[sl], d["norm_w"], cfg.norm_eps)
-        gy, _, _ = oracle.rmsnorm_bwd(y, d["z"].values[sl], d["norm_w"], inv, d["gout"].values[sl])
+        out, inv = oracle.rmsnorm_fwd(y, z_v, d["norm_w"], cfg.norm_eps)
+        gy, gz, _ = oracle.rmsnorm_bwd(y, z_v, d["norm_w"], inv, gout_v)
         g = oracle.ssd_bwd(*args, gy.reshape(b, T, H, P), h0, nthreads=threads)
         gact = np.concatenate([g["dx"].reshape(b, T, di), g["dB"].reshape(b, T, -1), g["dC"].reshape(b, T, -1)], -1)
-        oracle.conv_bwd(d["xBC"].values[sl], d["conv_w"], d["conv_b"], gact)
-        oracle.dt_softplus_bwd(d["dt_raw"].values[sl], d["dt_bias"], g["ddt"])
+        dxbc, _, _ = oracle.conv_bwd(xbc_v, d["conv_w"], d["conv_b"], gact)
+        draw, _ = oracle.dt_softplus_bwd(raw_v, d["dt_bias"], g["ddt"])
+        if cfg.d_model:
+            _ = out.reshape(-1, di) @ WO.T
+            gof = d["go"].values[sl].astype(np.float64).reshape(-1, cfg.d_model)
+            _ = gof.T @ out.reshape(-1, di)
+            Uf = U.reshape(-1, cfg.d_model)
+            flat = [gz.reshape(-1, di), dxbc.reshape(-1, cfg.conv_dim), draw.reshape(-1, H)]
+            _ = sum(gf @ W for gf, W in zip(flat, (WZ, WX, WD)))
+            _ = [gf.T @ Uf for gf in flat]
 
     # repeat the sample until about a second of wall time (10-30 s of CPU
     # work on a 16-thread host) has been measured
@@ -362,6 +452,8 @@ def cpu_baseline(cfg, d, batches: int, min_wall_s: float = 1.0):
         el += time.perf_counter() - t0
         reps += 1
     what = "SSD fwd+bwd" if not cfg.shell else "dt activation + conv1d/SiLU + SSD + RMSNorm-gated, fwd+bwd"
+    if cfg.d_model:
+        what += " with the projections as numpy f64 matrix products"
     return {"value": reps * nb * cfg.seqlen / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": (f"sequential f64 oracle, {what} on batch rows 0..{nb - 1} of {cfg.batch} "
                        f"({nb * cfg.seqlen} tokens) run {reps} times, {el:.1f} s wall on {threads} threads; "
@@ -373,7 +465,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="grouped", choices=["tiny", "m130", "grouped", "long", "block"])
+    ap.add_argument("--workload", default="grouped",
+                    choices=["tiny", "m130", "grouped", "long", "block", "block_train"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-batches", type=int, default=0, help="batch rows in the oracle sample (0: workload default)")
     ap.add_argument("--calibrate-copy-mb", type=int, default=0,
@@ -414,7 +507,8 @@ def main():
     # Per-kernel times: an untimed pass of the same steps with HIP events
     # around every kernel (the events hold the stream up a little between
     # kernels, so they stay out of the timed region).
-    kernels = KERNELS_FWD + KERNELS_BWD + (KERNELS_SHELL if cfg.shell else [])
+    kernels = KERNELS_FWD + KERNELS_BWD + (KERNELS_SHELL if cfg.shell else []) + (
+        ["gemm", "cast_bf16"] if cfg.d_model else [])
     ssd.profile_enable(True)
     for _ in range(args.steps):
         step()
@@ -488,7 +582,8 @@ def main():
         "vs_baseline": None, "dtype": "bf16" if cfg.dtype == "bf16" else "f32", "data": "synthetic",
         "config": {"workload": (f"{cfg.name}: b={cfg.batch} T={cfg.seqlen} H={cfg.nheads} P={cfg.headdim} "
                                 f"N={cfg.dstate} G={cfg.ngroups} chunk={cfg.chunk} {cfg.dtype}"
-                                + (" + conv1d/SiLU + RMSNorm-gated" if cfg.shell else "")),
+                                + (" + conv1d/SiLU + RMSNorm-gated" if cfg.shell else "")
+                                + (f" + in/out projections d_model={cfg.d_model}" if cfg.d_model else "")),
                    "global_batch": cfg.batch, "seq_len": cfg.seqlen, "parallelism": "single-gpu"},
         "kernel_ms": {k: round(v, 4) for k, v in kms.items()},
         "roofline": roofline,

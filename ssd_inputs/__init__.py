@@ -43,6 +43,7 @@ class SSDConfig:
     dtype: str  # "f32" or "bf16": storage dtype of x, dt, B, C, dy, y
     init_state: bool = False
     shell: bool = False  # conv1d+SiLU before and RMSNorm-gated after the core
+    d_model: int = 0  # > 0: also the block's in/out projections from and to d_model
     d_conv: int = 4
     norm_eps: float = 1e-5
     seed: int = 0
@@ -79,6 +80,9 @@ CONFIGS: Dict[str, SSDConfig] = {
                       init_state=True, seed=1003),
     "block": SSDConfig("block", 8, 2048, 48, 64, 128, 1, 256, "bf16",
                        shell=True, seed=1004),
+    # the block slice's sizes with the block's projections, d_model = d_inner / 2
+    "block_train": SSDConfig("block_train", 8, 2048, 48, 64, 128, 1, 256, "bf16",
+                             shell=True, d_model=1536, seed=1004),
 }
 # The five configurations in the order the workload list gives them.
 CONFIG_ORDER = ["tiny", "m130", "grouped", "long", "block"]
@@ -175,6 +179,17 @@ def make_inputs(cfg: SSDConfig, seed: Optional[int] = None) -> Dict[str, object]
         gout = rng.standard_normal((b, T, di), dtype=f32)
         out.update(xBC=Stored(xbc, cfg.dtype), z=Stored(z, cfg.dtype), gout=Stored(gout, cfg.dtype),
                    conv_w=conv_w, conv_b=conv_b, norm_w=norm_w)
+    if cfg.d_model:
+        # projections: u ~ N(0,1); weights [out, in] ~ N(0, 1/in), so that the
+        # projected activations are about N(0,1); the gradient of the block's
+        # output ~ N(0,1)
+        dm, di, cd = cfg.d_model, cfg.d_inner, cfg.conv_dim
+        u = rng.standard_normal((b, T, dm), dtype=f32)
+        w_z, w_xbc, w_dt = ((rng.standard_normal((o, dm), dtype=f32) / np.sqrt(dm)).astype(f32) for o in (di, cd, H))
+        w_out = (rng.standard_normal((dm, di), dtype=f32) / np.sqrt(di)).astype(f32)
+        go = rng.standard_normal((b, T, dm), dtype=f32)
+        out.update(u=Stored(u, cfg.dtype), W_z=Stored(w_z, cfg.dtype), W_xbc=Stored(w_xbc, cfg.dtype),
+                   W_dt=Stored(w_dt, cfg.dtype), W_out=Stored(w_out, cfg.dtype), go=Stored(go, cfg.dtype))
     return out
 
 
