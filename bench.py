@@ -590,6 +590,12 @@ def main():
         "ssd_bwd": ssd_bwd,
         "cpu_baseline": cpu,
     }
+    if cfg.d_model and "gemm" in kms:
+        n_gemm = 12  # three in_proj products, out_proj, and their eight gradient products
+        t_g = kms["gemm"] * n_gemm * 1e-3
+        line["projections"] = {"ms_per_step": round(t_g * 1e3, 4), "calls": n_gemm,
+                               "tflops": round(train_step_flops(cfg) / t_g / 1e12, 1),
+                               "peak_tflops": MFMA_PEAK_TFLOPS["bf16"], "library": "rocBLAS gemm_ex"}
     print(json.dumps(line), flush=True)
 
 
