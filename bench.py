@@ -345,7 +345,7 @@ def make_train_step(cfg, d):
     go_ = {"dx": torch.empty((b, T, H, P), **f32), "ddt": torch.empty((b, T, H), **f32),
            "dA_log": torch.empty(H, **f32), "dB": torch.empty((b, T, G, N), **f32),
            "dC": torch.empty((b, T, G, N), **f32), "dD": torch.empty(H, **f32)}
-    gact = torch.empty((M, di), **f32)
+    gact = torch.empty((M, di), **bf)  # the out_proj input gradient, in the activation dtype
     dWo, dWz, dWx, dWd = (torch.empty(s_, **f32) for s_ in ((dm, di), (di, dm), (cd, dm), (H, dm)))
     du = torch.empty((M, dm), **f32)
     gz_bf, gx_bf, gd_bf = torch.empty((M, di), **bf), torch.empty((M, cd), **bf), torch.empty((M, H), **bf)

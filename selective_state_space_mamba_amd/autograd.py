@@ -150,7 +150,8 @@ class _Block(torch.autograd.Function):
         if go is None:
             go = torch.zeros_like(u)
         go2 = go.contiguous().view(b * T, dm)
-        gout = _b.gemm(go2, W_out, out_dtype=torch.float32).view(b, T, -1)
+        # the gradient of the slice's output, in the activation dtype (bf16)
+        gout = _b.gemm(go2, W_out).view(b, T, -1)
         dW_out = _b.gemm(go2, out.view(b * T, -1), trans_a=True, out_dtype=torch.float32)
         init_state = t[15]
         (dxbc, ddt_raw, dz, dcw, dcb, d_bias, dA, dD, dnw, dh0) = _core_bwd(
@@ -173,8 +174,9 @@ def mamba2_block(u: torch.Tensor, W_z: torch.Tensor, W_xbc: torch.Tensor, W_dt: 
     weights: z, xbc, dt_raw = u W_z^T, u W_xbc^T, u W_dt^T (the three parts of
     in_proj, [out_features, d_model] each), the block slice of
     mamba2_block_core, and o = out W_out^T (W_out [d_model, d_inner]).  The
-    projections run through ssd_gemm (rocBLAS, f32 accumulation); the slice's
-    f32 gradients are rounded to bf16 for the backward products.  Returns
+    projections run through ssd_gemm (rocBLAS, f32 accumulation); the gradient
+    entering the slice from out_proj is bf16 and the slice's f32 gradients are
+    rounded to bf16 for the backward products.  Returns
     (o [b,T,d_model], final_state)."""
     return _Block.apply(u, W_z, W_xbc, W_dt, conv_w, conv_b, dt_bias, A_log, D, norm_w, W_out, init_state,
                         (ngroups, dstate, headdim, chunk, eps))
