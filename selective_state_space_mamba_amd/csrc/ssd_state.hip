@@ -174,10 +174,13 @@ __global__ __launch_bounds__(NTHREADS, 2) void chunk_state_kernel(
 // chunk's whole P x N weighted sum (forward S_c = sum_j exp(s_end - s_j) dt_j
 // x_j (outer) B_j, backward dS_c = sum_i exp(s_i) dy_i (outer) C_i) over slabs
 // of SUM_SJ steps, so each B (C) slab staged in LDS serves every headdim row
-// of the head; wave w owns rows 16w .. 16w+15 and all N columns.  The sum goes
-// to the chunk's slot of `sums`, the chunk's total log-decay s_end to `send`.
+// of the head; wave w owns rows 16w .. 16w+15 and the workgroup's d_state
+// columns: all of them, or (NSPL = 2, for grids under two workgroups per CU)
+// one half, the two halves of a (batch, chunk, head) being adjacent blocks.
+// The sum goes to the chunk's slot of `sums`, the chunk's total log-decay
+// s_end to `send`.
 constexpr int SUM_SJ = 64;
-template <typename TX, typename TB, bool REV>
+template <typename TX, typename TB, bool REV, int NSPL>
 __global__ __launch_bounds__(NTHREADS, 2) void chunk_sum_f32_kernel(
     const TX* __restrict__ X,         // fwd: x; bwd: dy            [b,T,H,P]
     const TB* __restrict__ Bm,        // fwd: B; bwd: C             [b,T,G,N]
@@ -188,12 +191,15 @@ __global__ __launch_bounds__(NTHREADS, 2) void chunk_sum_f32_kernel(
     int T, int H, int P, int N, int G, int Q) {
   static_assert(NTHREADS / WAVE * 16 == PMAX, "one wave per 16 headdim rows");
   constexpr int LDX = SUM_SJ + 4;  // [p][j] and [n][j]: time contiguous, padded
+  constexpr int NW = NMAX / NSPL;  // d_state columns per workgroup
   __shared__ __attribute__((aligned(16))) float sX[PMAX * LDX];
-  __shared__ __attribute__((aligned(16))) float sB[NMAX * LDX];
+  __shared__ __attribute__((aligned(16))) float sB[NW * LDX];
   __shared__ float sW[QMAX];
   __shared__ float sTmp[8];
   const int nc = T / Q;
-  const int lb = xcd_logical_block(blockIdx.x, gridDim.x);  // heads of a chunk share an XCD
+  int lb = xcd_logical_block(blockIdx.x, gridDim.x);  // heads of a chunk share an XCD
+  const int n0 = (lb % NSPL) * NW;
+  lb /= NSPL;
   const int h = lb % H, c = (lb / H) % nc, bi = lb / (H * nc);
   const int g = h / (H / G);
   const float A = -__expf(A_log[h]);
@@ -203,13 +209,13 @@ __global__ __launch_bounds__(NTHREADS, 2) void chunk_sum_f32_kernel(
   const int64_t row_c = static_cast<int64_t>(bi) * T + static_cast<int64_t>(c) * Q;
 
   TransTile<TX, SUM_SJ, PMAX, 4> tx;  // x (or dy) rows j -> [p][j], scaled by the step weights
-  TransTile<TB, SUM_SJ, NMAX, 4> tb;  // B (or C) rows j -> [n][j]
+  TransTile<TB, SUM_SJ, NW, 4> tb;    // B (or C) rows j, this workgroup's columns -> [n][j]
   const int nslab = (Q + SUM_SJ - 1) / SUM_SJ;
   auto load = [&](int sl) {
     const int64_t row0 = row_c + sl * SUM_SJ;
     const int vr = min(SUM_SJ, Q - sl * SUM_SJ);
     tx.load(X + row0 * HP + static_cast<int64_t>(h) * P, HP, vr, P);
-    tb.load(Bm + row0 * GN + static_cast<int64_t>(g) * N, GN, vr, N);
+    tb.load(Bm + row0 * GN + static_cast<int64_t>(g) * N + n0, GN, vr, min(NW, N - n0));
   };
   load(0);
 
@@ -219,9 +225,9 @@ __global__ __launch_bounds__(NTHREADS, 2) void chunk_sum_f32_kernel(
   __syncthreads();
   const float s_end = sTmp[4];
   if (tid < Q) sW[tid] = REV ? __expf(s) : __expf(s_end - s) * dtv;
-  if (tid == 0) send[(static_cast<int64_t>(bi) * nc + c) * H + h] = s_end;
+  if (tid == 0 && n0 == 0) send[(static_cast<int64_t>(bi) * nc + c) * H + h] = s_end;
 
-  f4 acc[NMAX / 16];
+  f4 acc[NW / 16];
   zero(acc);
   for (int sl = 0; sl < nslab; ++sl) {
     __syncthreads();  // sW visible; the previous slab's reads of sX / sB done
@@ -229,15 +235,15 @@ __global__ __launch_bounds__(NTHREADS, 2) void chunk_sum_f32_kernel(
     tb.store(sB, LDX);
     if (sl + 1 < nslab) load(sl + 1);
     __syncthreads();
-    wave_gemm<false, true, true, NMAX / 16>(acc, sX + 16 * w * LDX, LDX, 1, sB, LDX, 1,
+    wave_gemm<false, true, true, NW / 16>(acc, sX + 16 * w * LDX, LDX, 1, sB, LDX, 1,
                                            round_up(min(SUM_SJ, Q - sl * SUM_SJ), Op<false>::KS));
   }
   const int64_t base = ((static_cast<int64_t>(bi) * nc + c) * H + h) * PN;
 #pragma unroll
-  for (int t = 0; t < NMAX / 16; ++t)
+  for (int t = 0; t < NW / 16; ++t)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int p = 16 * w + 4 * q + i, n = 16 * t + r;
+      const int p = 16 * w + 4 * q + i, n = n0 + 16 * t + r;
       if (p < P && n < N) sums[base + p * N + n] = acc[t][i];
     }
 }
@@ -339,9 +345,17 @@ static hipError_t launch_state(const Dims& d, const void* X, const void* Bm, con
                                void* hbf = nullptr) {
   if constexpr (!BF) {
     // two passes: per-chunk sums in parallel, then the walk over chunks
-    hipLaunchKernelGGL((chunk_sum_f32_kernel<TX, TB, REV>), dim3(d.H * d.nc() * d.b), dim3(NTHREADS), 0, st,
-                       static_cast<const TX*>(X), static_cast<const TB*>(Bm), static_cast<const TB*>(dt), A_log,
-                       static_cast<float*>(states), send, d.T, d.H, d.P, d.N, d.G, d.Q);
+    // half the d_state columns per workgroup when whole heads would leave
+    // fewer than two workgroups per CU (the smaller problems)
+    const int64_t units = static_cast<int64_t>(d.H) * d.nc() * d.b;
+    if (units < 512 && d.N > NMAX / 2)
+      hipLaunchKernelGGL((chunk_sum_f32_kernel<TX, TB, REV, 2>), dim3(2 * units), dim3(NTHREADS), 0, st,
+                         static_cast<const TX*>(X), static_cast<const TB*>(Bm), static_cast<const TB*>(dt), A_log,
+                         static_cast<float*>(states), send, d.T, d.H, d.P, d.N, d.G, d.Q);
+    else
+      hipLaunchKernelGGL((chunk_sum_f32_kernel<TX, TB, REV, 1>), dim3(units), dim3(NTHREADS), 0, st,
+                         static_cast<const TX*>(X), static_cast<const TB*>(Bm), static_cast<const TB*>(dt), A_log,
+                         static_cast<float*>(states), send, d.T, d.H, d.P, d.N, d.G, d.Q);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(state_scan_kernel<REV>, dim3(state_npb(d) * d.H * d.b), dim3(SCAN_THREADS), 0, st,
