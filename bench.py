@@ -263,6 +263,28 @@ def to_dev(a):
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
 
 
+def roofline_entry(cfg, kernel: str, t_s: float) -> dict:
+    """Roofline of one launch of `kernel` taking t_s seconds.  The roof that
+    bounds it is HBM when its algorithmic flops per algorithmic byte fall below
+    the machine balance of the operand dtype's MFMA peak over the HBM peak, and
+    that MFMA peak above it."""
+    alg = algorithmic_bytes(cfg, kernel)
+    flops = algorithmic_flops(cfg, kernel)
+    achieved = alg / t_s / 1e9
+    tflops = flops / t_s / 1e12
+    traffic = measured_traffic(kernel, cfg.name)
+    mfma_peak = MFMA_PEAK_TFLOPS["bf16" if cfg.dtype == "bf16" else "f32"]
+    if flops / alg > mfma_peak * 1e3 / HBM_PEAK_GBS:
+        r = {"bound": "mfma", "achieved": round(tflops, 2), "peak": mfma_peak, "unit": "TFLOP/s",
+             "frac": round(tflops / mfma_peak, 4), "traffic": traffic, "hbm_gbs": round(achieved, 1)}
+    else:
+        r = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic, "mfma_tflops": round(tflops, 2)}
+    r.update({"kernel": kernel, "kernel_ms": round(t_s * 1e3, 4), "algorithmic_bytes": alg,
+              "algorithmic_flops": flops, "mfma_util_pct": measured_mfma_util(kernel, cfg.name)})
+    return r
+
+
 def make_step(cfg, d):
     import torch
     import selective_state_space_mamba_amd as ssd
@@ -540,22 +562,7 @@ def main():
         "per-kernel ms (profiling pass): " + " ".join(f"{k}={v:.4f}" for k, v in kms.items()))
 
     t_dom = ms_dom / n_dom * 1e-3
-    alg = algorithmic_bytes(cfg, dom)
-    flops = algorithmic_flops(cfg, dom)
-    achieved = alg / t_dom / 1e9
-    tflops = flops / t_dom / 1e12
-    traffic = measured_traffic(dom, cfg.name)
-    # The roof that bounds the kernel: HBM below the machine balance of the
-    # operand dtype's MFMA peak over the HBM peak, the MFMA peak above it.
-    mfma_peak = MFMA_PEAK_TFLOPS["bf16" if cfg.dtype == "bf16" else "f32"]
-    if flops / alg > mfma_peak * 1e3 / HBM_PEAK_GBS:
-        roofline = {"bound": "mfma", "achieved": round(tflops, 2), "peak": mfma_peak, "unit": "TFLOP/s",
-                    "frac": round(tflops / mfma_peak, 4), "traffic": traffic, "hbm_gbs": round(achieved, 1)}
-    else:
-        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic, "mfma_tflops": round(tflops, 2)}
-    roofline.update({"kernel": dom, "kernel_ms": round(t_dom * 1e3, 4), "algorithmic_bytes": alg,
-                     "algorithmic_flops": flops, "mfma_util_pct": measured_mfma_util(dom, cfg.name)})
+    roofline = roofline_entry(cfg, dom, t_dom)
     t_bwd = sum(v for k, v in kms.items() if k in KERNELS_BWD) * 1e-3
     bwd_alg = backward_algorithmic_bytes(cfg)
     ssd_bwd = {"ms": round(t_bwd * 1e3, 4), "algorithmic_bytes": bwd_alg,
