@@ -106,6 +106,32 @@ __device__ __forceinline__ void wave_gemm(f4 (&acc)[NT], const typename Op<BF>::
   typedef typename Op<BF>::V V;
   constexpr int KS = Op<BF>::KS;
   if (K <= 0) return;
+  if constexpr (!BF) {
+    // f32: one element per lane per fragment and K = 4 per MFMA, so the reads
+    // of KU k-steps are issued together ahead of their MFMAs (one wait per
+    // batch instead of one LDS round trip per k-step); same accumulation order
+    constexpr int KU = 4;
+    int k0 = 0;
+    for (; k0 + KU * KS <= K; k0 += KU * KS) {
+      float a[KU], b[KU][NT];
+#pragma unroll
+      for (int u = 0; u < KU; ++u) {
+        a[u] = fetch<false, AKC>(A, asr, ask, 0, k0 + u * KS);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) b[u][t] = fetch<false, BKC>(B, bsr, bsk, 16 * t, k0 + u * KS);
+      }
+#pragma unroll
+      for (int u = 0; u < KU; ++u)
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[t] = mfma(a[u], b[u][t], acc[t]);
+    }
+    for (; k0 < K; k0 += KS) {
+      const float a = fetch<false, AKC>(A, asr, ask, 0, k0);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) acc[t] = mfma(a, fetch<false, BKC>(B, bsr, bsk, 16 * t, k0), acc[t]);
+    }
+    return;
+  }
   // the next k-step's A fragment is read from LDS while the current MFMAs run
   V a = fetch<BF, AKC>(A, asr, ask, 0, 0);
   for (int k0 = 0; k0 < K; k0 += KS) {
