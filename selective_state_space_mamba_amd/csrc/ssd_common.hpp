@@ -110,7 +110,7 @@ __device__ __forceinline__ void wave_gemm(f4 (&acc)[NT], const typename Op<BF>::
     // f32: one element per lane per fragment and K = 4 per MFMA, so the reads
     // of KU k-steps are issued together ahead of their MFMAs (one wait per
     // batch instead of one LDS round trip per k-step); same accumulation order
-    constexpr int KU = NT <= 2 ? 8 : 4;
+    constexpr int KU = NT <= 4 ? 8 : 4;
     int k0 = 0;
     for (; k0 + KU * KS <= K; k0 += KU * KS) {
       float a[KU], b[KU][NT];
