@@ -224,3 +224,35 @@ def test_autograd_full_block_with_projections():
             "dh0": relerr(host(h0.grad), rg["dh0"])}
     print("[parity full block]", {k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
     assert all(v <= TOL["bf16"] for v in errs.values()), errs
+
+
+@pytest.mark.parametrize("ta,tb", [(False, False), (False, True), (True, False), (True, True)])
+@pytest.mark.parametrize("m,n,k", [(1, 1, 1), (37, 45, 13), (128, 96, 257)])
+def test_gemm_entry_point(ta, tb, m, n, k):
+    """ssd_gemm against a float64 product of the same bf16 operands: both
+    transposes, odd sizes, f32 and bf16 results, beta accumulation."""
+    rng = np.random.default_rng(m * 1000 + n * 10 + k)
+    a = Stored(rng.standard_normal((k, m) if ta else (m, k)).astype(np.float32), "bf16")
+    b = Stored(rng.standard_normal((n, k) if tb else (k, n)).astype(np.float32), "bf16")
+    c0 = rng.standard_normal((m, n)).astype(np.float32)
+    A = a.values.astype(np.float64).T if ta else a.values.astype(np.float64)
+    B = b.values.astype(np.float64).T if tb else b.values.astype(np.float64)
+    ref = A @ B
+    got32 = ssd.gemm(dev(a), dev(b), trans_a=ta, trans_b=tb, out_dtype=torch.float32)
+    acc = dev(c0)
+    ssd.gemm(dev(a), dev(b), trans_a=ta, trans_b=tb, out=acc, alpha=0.5, beta=1.0)
+    got16 = ssd.gemm(dev(a), dev(b), trans_a=ta, trans_b=tb)
+    torch.cuda.synchronize()
+    assert got16.dtype == torch.bfloat16
+    assert relerr(host(got32), ref) <= 1e-5
+    assert relerr(host(acc), 0.5 * ref + c0) <= 1e-5
+    assert relerr(host(got16), ref) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("n", [1, 3, 4, 1027])
+def test_cast_bf16_entry_point(n):
+    src = np.random.default_rng(n).standard_normal(n).astype(np.float32) * 100
+    got = ssd.cast_bf16(dev(src))
+    torch.cuda.synchronize()
+    expect = Stored(src, "bf16").raw  # round to nearest even
+    assert np.array_equal(got.cpu().view(torch.int16).numpy().view(np.uint16), expect)
