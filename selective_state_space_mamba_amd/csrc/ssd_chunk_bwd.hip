@@ -695,7 +695,7 @@ __global__ __launch_bounds__(NT8) void chunk_bwd_row_kernel(
 // ------------------------------------------------------------- dt finalize
 //
 // ddt, and the dA_log and dD sums.  A workgroup takes one chunk of one batch
-// row and up to DT_HEADS heads, one wave per head (lane l holds the chunk's
+// row and up to NH heads, one wave per head (lane l holds the chunk's
 // rows l + 64 e, so a chunk's scan and sums need no barrier).  dt and ddt
 // ([b, T, H]) pass through LDS, so that their global accesses run along the
 // heads.  Each wave leaves its head's dA partial for the chunk; the workgroup
@@ -704,8 +704,9 @@ __global__ __launch_bounds__(NT8) void chunk_bwd_row_kernel(
 // not depend on which workgroup that is.  The partials are stored and read
 // with device-coherent (agent-scope) atomic stores and loads, and every wave
 // has waited for its stores to complete before the workgroup counts itself:
-// no write-back of the whole L2 is needed.
-constexpr int DT_HEADS = 16;
+// no write-back of the whole L2 is needed.  NH (16, 8 or 4 heads per
+// workgroup) is the widest that still gives a grid of 64 workgroups.  In the final sums each thread adds one head's partials over a strided
+// slice of the chunks, and one thread per head adds the slices in slice order.
 
 // Lane 63's value, in every lane.
 __device__ __forceinline__ float lane63(float v) {
@@ -714,17 +715,19 @@ __device__ __forceinline__ float lane63(float v) {
 // Sum over the 64 lanes of a wave, in every lane (DPP scan, then lane 63).
 __device__ __forceinline__ float wave_total(float v) { return lane63(wave_scan(v)); }
 
-template <typename TI>
-__global__ __launch_bounds__(DT_HEADS* WAVE) void bwd_dt_kernel(const TI* __restrict__ dt,
+template <typename TI, int NH>
+__global__ __launch_bounds__(NH* WAVE) void bwd_dt_kernel(const TI* __restrict__ dt,
                                                                const float* __restrict__ A_log,
                                                                float* __restrict__ ddt, float* __restrict__ dA_log,
                                                                float* __restrict__ dD, BwdScratch s, int T, int H,
                                                                int Q, int npb, int nc, int nb) {
-  __shared__ float sT[QMAX][DT_HEADS + 1];  // dt in, then ddt out: [row][head]
+  constexpr int NTH = NH * WAVE;
+  __shared__ float sT[QMAX][NH + 1];  // dt in, then ddt out: [row][head]
+  __shared__ float sRed[2][NTH];      // the final sums' slice partials
   __shared__ int sFinal;
   const int u = blockIdx.x;  // chunk index bi * nc + c
-  const int hg0 = blockIdx.y * DT_HEADS;
-  const int nh = min(DT_HEADS, H - hg0);
+  const int hg0 = blockIdx.y * NH;
+  const int nh = min(NH, H - hg0);
   const int bi = u / nc, c = u - bi * nc;
   const int64_t r0 = static_cast<int64_t>(bi) * T + static_cast<int64_t>(c) * Q;  // the chunk's first row
   const int tid = threadIdx.x, l = lane_id(), w = wave_id();
@@ -746,8 +749,8 @@ __global__ __launch_bounds__(DT_HEADS* WAVE) void bwd_dt_kernel(const TI* __rest
     }
   }
   const float ghl = (l < npb && w < nh) ? s.gh_part[(static_cast<int64_t>(u) * H + h) * npb + l] : 0.f;
-  for (int i = tid; i < Q * DT_HEADS; i += DT_HEADS * WAVE) {
-    const int k = i / DT_HEADS, j = i % DT_HEADS;
+  for (int i = tid; i < Q * NH; i += NTH) {
+    const int k = i / NH, j = i % NH;
     sT[k][j] = j < nh ? load_f(dt, (r0 + k) * H + hg0 + j) : 0.f;
   }
   __syncthreads();
@@ -792,8 +795,8 @@ __global__ __launch_bounds__(DT_HEADS* WAVE) void bwd_dt_kernel(const TI* __rest
                          __HIP_MEMORY_SCOPE_AGENT);
   }
   __syncthreads();
-  for (int i = tid; i < Q * DT_HEADS; i += DT_HEADS * WAVE) {
-    const int k = i / DT_HEADS, j = i % DT_HEADS;
+  for (int i = tid; i < Q * NH; i += NTH) {
+    const int k = i / NH, j = i % NH;
     if (j < nh) ddt[(r0 + k) * H + hg0 + j] = sT[k][j];
   }
   __builtin_amdgcn_s_waitcnt(0);  // this wave's stores, the dA partial among them, are complete
@@ -804,21 +807,34 @@ __global__ __launch_bounds__(DT_HEADS* WAVE) void bwd_dt_kernel(const TI* __rest
   }
   __syncthreads();
   if (!sFinal) return;
-  // the last workgroup: wave w sums heads w, w + DT_HEADS, ... over all chunks
+  // the last workgroup: thread tid adds head h0 + tid % hb over the chunks
+  // tid / hb, tid / hb + np, ...; then one thread per head adds the np slices
   const int nbc = gridDim.x;
-  for (int h = w; h < H; h += DT_HEADS) {
+  for (int h0 = 0; h0 < H; h0 += NTH) {
+    const int hb = min(NTH, H - h0), np = NTH / hb;
+    const int hh = tid % hb, part = tid / hb;
     float a = 0.f, dd = 0.f;
-    for (int v = l; v < nbc; v += WAVE) {
-      a += __hip_atomic_load(s.dA_part + static_cast<int64_t>(v) * H + h, __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT);
-      for (int ib = 0; ib < nb; ++ib) dd += s.dD_part[(static_cast<int64_t>(v) * nb + ib) * H + h];
+    if (part < np) {
+#pragma unroll 4
+      for (int v = part; v < nbc; v += np) {
+        a += __hip_atomic_load(s.dA_part + static_cast<int64_t>(v) * H + h0 + hh, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        for (int ib = 0; ib < nb; ++ib) dd += s.dD_part[(static_cast<int64_t>(v) * nb + ib) * H + h0 + hh];
+      }
     }
-    a = wave_total(a);
-    dd = wave_total(dd);
-    if (l == 0) {
-      dA_log[h] = -__expf(A_log[h]) * a;
-      dD[h] = dd;
+    sRed[0][tid] = a;
+    sRed[1][tid] = dd;
+    __syncthreads();
+    if (tid < hb) {
+      float ta = 0.f, td = 0.f;
+      for (int p = 0; p < np; ++p) {
+        ta += sRed[0][p * hb + tid];
+        td += sRed[1][p * hb + tid];
+      }
+      dA_log[h0 + tid] = -__expf(A_log[h0 + tid]) * ta;
+      dD[h0 + tid] = td;
     }
+    __syncthreads();
   }
 }
 
@@ -903,16 +919,39 @@ hipError_t launch_chunk_bwd_row(const Dims& d, DType act, DType dyt, int nsplit,
   return hipGetLastError();
 }
 
+// Fewest workgroups per call.  The kernel is short and latency-bound: a grid
+// of one workgroup per CU (4 heads each) measured slower than 64 workgroups of
+// 16 heads (every workgroup stages its rows and adds itself to the arrival
+// counter), while a grid of fewer than 64 gains from narrower workgroups.
+constexpr int64_t DT_GRID_TARGET = 64;
+
+template <typename TI, int NH>
+static void dt_launch(const Dims& d, const void* dt, const float* A_log, float* ddt, float* dA_log, float* dD,
+                      const BwdScratch& s, hipStream_t st) {
+  const dim3 grid(d.b * d.nc(), (d.H + NH - 1) / NH);
+  hipLaunchKernelGGL((bwd_dt_kernel<TI, NH>), grid, dim3(NH * WAVE), 0, st, static_cast<const TI*>(dt), A_log, ddt,
+                     dA_log, dD, s, d.T, d.H, d.Q, state_npb(d), d.nc(), d.nb());
+}
+
+template <typename TI>
+static void dt_dispatch(const Dims& d, const void* dt, const float* A_log, float* ddt, float* dA_log, float* dD,
+                        const BwdScratch& s, hipStream_t st) {
+  // the widest workgroup that still gives DT_GRID_TARGET workgroups
+  const int64_t units = static_cast<int64_t>(d.b) * d.nc();
+  if (units * ((d.H + 15) / 16) >= DT_GRID_TARGET)
+    dt_launch<TI, 16>(d, dt, A_log, ddt, dA_log, dD, s, st);
+  else if (units * ((d.H + 7) / 8) >= DT_GRID_TARGET)
+    dt_launch<TI, 8>(d, dt, A_log, ddt, dA_log, dD, s, st);
+  else
+    dt_launch<TI, 4>(d, dt, A_log, ddt, dA_log, dD, s, st);
+}
+
 hipError_t launch_bwd_dt(const Dims& d, DType act, const void* dt, const float* A_log, float* ddt, float* dA_log,
                          float* dD, const BwdScratch& s, hipStream_t st) {
-  const dim3 grid(d.b * d.nc(), (d.H + DT_HEADS - 1) / DT_HEADS);
   if (act == BF16)
-    hipLaunchKernelGGL((bwd_dt_kernel<uint16_t>), grid, dim3(DT_HEADS * WAVE), 0, st,
-                       static_cast<const uint16_t*>(dt), A_log, ddt, dA_log, dD, s, d.T, d.H, d.Q, state_npb(d),
-                       d.nc(), d.nb());
+    dt_dispatch<uint16_t>(d, dt, A_log, ddt, dA_log, dD, s, st);
   else
-    hipLaunchKernelGGL((bwd_dt_kernel<float>), grid, dim3(DT_HEADS * WAVE), 0, st, static_cast<const float*>(dt),
-                       A_log, ddt, dA_log, dD, s, d.T, d.H, d.Q, state_npb(d), d.nc(), d.nb());
+    dt_dispatch<float>(d, dt, A_log, ddt, dA_log, dD, s, st);
   return hipGetLastError();
 }
 
