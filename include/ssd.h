@@ -153,7 +153,8 @@ int mamba2_rmsnorm_gated_bwd(int64_t rows, int64_t width, int32_t dtype, int32_t
                              const float* inv_rms, const void* g, void* dy, float* dz, float* dw,
                              void* workspace, size_t workspace_bytes, void* stream);
 
-/* dt activation in front of the core (page 1, tensorized_mamba2_backward_impl:
+/* dt activation in front of the core (burn_dragon_kernel src/sequence/mamba2/backward.rs,
+ * tensorized_mamba2_backward_impl:
  * dt_pre = dt_raw + dt_bias, dt = softplus(dt_pre) with beta 1; after the fused
  * backward, grad_dt_pre = grad_dt * sigmoid(dt_pre) and grad_dt_bias is its sum
  * over batch and time).  Rows are the b*T steps of [b,T,nheads] arrays.

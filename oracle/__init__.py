@@ -183,14 +183,15 @@ def rmsnorm_bwd(y, z, w, inv_rms, g):
 
 def dt_softplus_fwd(dt_raw, dt_bias):
     """dt = softplus(dt_raw + dt_bias) with beta 1, i.e. log(1 + e^v), over
-    [..., H] (page 1: dt_pre = dt_raw + dt_bias, dt = softplus(dt_pre, 1.0)).
+    [..., H] (the burn_dragon_kernel backward.rs page: dt_pre = dt_raw + dt_bias, dt = softplus(dt_pre, 1.0)).
     np.logaddexp(0, v) is log(e^0 + e^v), the same function, without overflow."""
     v = _f64(dt_raw) + _f64(dt_bias)
     return np.logaddexp(0.0, v)
 
 
 def dt_softplus_bwd(dt_raw, dt_bias, ddt):
-    """Gradient through dt_softplus_fwd (page 1: grad_dt_pre = grad_dt *
+    """Gradient through dt_softplus_fwd (the burn_dragon_kernel
+    backward.rs page: grad_dt_pre = grad_dt *
     sigmoid(dt_pre); grad_dt_bias sums it over batch and time; grad_dt_raw is
     grad_dt_pre).  Returns (ddt_raw [..., H], d_dt_bias [H])."""
     v = _f64(dt_raw) + _f64(dt_bias)

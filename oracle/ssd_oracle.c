@@ -7,7 +7,7 @@
  *
  * Plain, slow and sequential in time, in double precision.  Each function
  * follows a passage of the burn_dragon_kernel 0.5.0 page
- * "src/sequence/mamba2/backward.rs" (page 1 of the source pages):
+ * "src/sequence/mamba2/backward.rs":
  *
  *   ssd_oracle_fwd       the recurrence of ssd_forward_state_history_reference,
  *                        with the readout y = C . h_t + D x_t of the tensorized

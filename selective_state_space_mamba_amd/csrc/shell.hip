@@ -1,7 +1,7 @@
 // Block-shell ops around the SSD core (bandwidth-bound, no contraction):
 //
 //  * causal depthwise conv1d + SiLU, following depthwise_conv_preact_with_history
-//    and silu on the page-1 reference (burn_dragon_kernel mamba2/backward.rs):
+//    and silu on the reference page (burn_dragon_kernel src/sequence/mamba2/backward.rs):
 //      preact[t,c] = bias[c] + sum_k w[c,k] xbc[t-(K-1)+k, c]   (zero before t=0)
 //    and the block backward's conv/SiLU chain:
 //      gp = g s (1 + p (1 - s)), s = sigmoid(p);  dbias = sum gp;
@@ -657,8 +657,8 @@ __global__ __launch_bounds__(RMS_VEC_WAVES * WAVE) void rms_bwd_vec_kernel(
 // dt = softplus(dt_raw + dt_bias[h]) with beta 1, and its backward
 // ddt_raw = ddt * sigmoid(dt_raw + dt_bias[h]), d_dt_bias[h] = sum over rows of
 // ddt_raw, following the dt_pre / softplus lines of tensorized_mamba2_backward_impl
-// and the grad_dt_pre / grad_dt_bias lines after the fused backward on page 1
-// (burn_dragon_kernel mamba2/backward.rs).  softplus(v) = log(1 + e^v) is
+// and the grad_dt_pre / grad_dt_bias lines after the fused backward on the page
+// (burn_dragon_kernel src/sequence/mamba2/backward.rs).  softplus(v) = log(1 + e^v) is
 // evaluated as max(v, 0) + log1p(e^-|v|), the same function without overflow.
 // Rows are the b*T steps of a [b, T, H] array.
 

@@ -1,7 +1,7 @@
 // Intra-chunk backward of the SSD for bf16 operands, with asynchronous LDS
 // staging (ssd_async.hpp).  Same outputs and formulas as the column and row
 // kernels of ssd_chunk_bwd.hip (derived there from the reverse-time loop of the
-// page-1 reference, burn_dragon_kernel mamba2/backward.rs,
+// reference page, burn_dragon_kernel src/sequence/mamba2/backward.rs,
 // ssd_backward_reference), organised so that each wave's chain of
 // contractions stays inside the wave.
 //

@@ -1,7 +1,7 @@
 // Intra-chunk backward of the SSD and the dt / A / D reductions.
 //
 // Gradients of L = sum(dy * y) for one chunk follow from the reverse-time loop
-// of the page-1 reference (burn_dragon_kernel mamba2/backward.rs,
+// of the reference page (burn_dragon_kernel src/sequence/mamba2/backward.rs,
 // ssd_backward_reference) regrouped by chunk.  Notation: s_i within-chunk
 // inclusive cumsum of dt A, L_ij = exp(s_i - s_j) for i >= j, CB_ij = C_i . B_j,
 // yx_ij = dy_i . x_j, H_c the state entering the chunk, Gamma the gradient

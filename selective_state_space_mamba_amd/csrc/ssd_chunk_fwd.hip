@@ -1,8 +1,8 @@
 // Chunk output of the SSD forward.
 //
 // Inside one chunk (s_i = within-chunk inclusive cumsum of dt A, H_c the state
-// entering the chunk) the recurrence of the page-1 reference
-// (burn_dragon_kernel mamba2/backward.rs, ssd_forward_state_history_reference,
+// entering the chunk) the recurrence of the reference page
+// (burn_dragon_kernel src/sequence/mamba2/backward.rs, ssd_forward_state_history_reference,
 // with the y readout of the block backward: y = sum_n ssm C + D x) is
 //
 //   y_i = sum_{j<=i} exp(s_i - s_j) (C_i . B_j) dt_j x_j     (intra-chunk part)

@@ -1,8 +1,8 @@
 // Chunk output of the SSD forward for bf16 operands, with asynchronous LDS
 // staging (ssd_async.hpp).  Same result as chunk_out_fwd_kernel
 // (ssd_chunk_fwd.hip): for the state H_c entering chunk c and s the
-// within-chunk cumsum of dt A (the recurrence of the page-1 reference,
-// burn_dragon_kernel mamba2/backward.rs, ssd_forward_state_history_reference,
+// within-chunk cumsum of dt A (the recurrence of the reference page,
+// burn_dragon_kernel src/sequence/mamba2/backward.rs, ssd_forward_state_history_reference,
 // with the y readout of the block backward),
 //
 //   y_i = sum_{j<=i} exp(s_i - s_j) (C_i . B_j) dt_j x_j + exp(s_i) C_i . H_c^T + D x_i.

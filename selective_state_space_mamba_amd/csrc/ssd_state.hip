@@ -1,8 +1,8 @@
 // Inter-chunk state passing (forward) and the reverse-time state-gradient pass
 // (backward) of the chunked SSD.
 //
-// The recurrence h_t = exp(dt_t A) h_{t-1} + dt_t x_t (outer) B_t of the page-1
-// reference (burn_dragon_kernel mamba2/backward.rs,
+// The recurrence h_t = exp(dt_t A) h_{t-1} + dt_t x_t (outer) B_t of the reference
+// page (burn_dragon_kernel src/sequence/mamba2/backward.rs,
 // ssd_forward_state_history_reference), unrolled over one chunk of Q steps with
 // s_i = sum_{r<=i} dt_r A (within the chunk), gives
 //

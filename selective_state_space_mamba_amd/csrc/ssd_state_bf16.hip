@@ -6,7 +6,7 @@
 //   Gamma_c   = exp(s_end) Gamma_{c+1} + sum_i exp(s_i) dy_i (outer) C_i
 //   (Gamma_nc = the gradient of the final state, zero unless given)
 //
-// (page-1 reference, burn_dragon_kernel mamba2/backward.rs: the recurrence of
+// (reference page, burn_dragon_kernel src/sequence/mamba2/backward.rs: the recurrence of
 // ssd_forward_state_history_reference and the carry of ssd_backward_reference,
 // unrolled over one chunk).
 //

@@ -5,8 +5,8 @@ This module is shared by the oracle side (tests, CPU baseline) and the HIP side
 holds none of the method's arithmetic (no recurrence, no gradient).
 
 Workloads (sizes follow the five synthetic SSD configurations the method is
-measured on, plus the deterministic shape from the page-1 parity test of
-burn_dragon_kernel ``mamba2/backward.rs``, ``make_realistic_cuda_inputs``):
+measured on, plus the deterministic shape from the parity test on the page
+burn_dragon_kernel ``src/sequence/mamba2/backward.rs``, ``make_realistic_cuda_inputs``):
 
   tiny        b=1  T=64    H=2  P=8  N=4   G=1 Q=16  f32
   m130        b=2  T=1024  H=24 P=64 N=128 G=1 Q=256 f32   (130M-shaped)
@@ -14,7 +14,7 @@ burn_dragon_kernel ``mamba2/backward.rs``, ``make_realistic_cuda_inputs``):
   long        b=1  T=16384 H=64 P=64 N=128 G=1 Q=256 f32   carried h0 ~ N(0, 0.1)
   block       b=8  T=2048  H=48 P=64 N=128 G=1 Q=256 bf16  + conv1d/SiLU and
                                                         RMSNorm-gated shell
-  p1test      b=1  T=32    H=4  P=64 N=16  G=4 Q=16  f32   page-1 test pattern
+  p1test      b=1  T=32    H=4  P=64 N=16  G=4 Q=16  f32   the page's test pattern
 
 Distributions: x, B, C, dy ~ N(0,1); dt = softplus(N(0,1) + dt_bias_h) with
 dt_bias ~ U(-4,-2) per head; A_log ~ U(log 1, log 16); D ~ N(0,1); initial
@@ -195,7 +195,7 @@ def make_inputs(cfg: SSDConfig, seed: Optional[int] = None) -> Dict[str, object]
 
 def make_p1test_inputs() -> Dict[str, object]:
     """The deterministic ``(idx % prime) / prime - offset`` pattern of the
-    page-1 parity test (burn_dragon_kernel mamba2/backward.rs, tests module,
+    parity test of the page (burn_dragon_kernel src/sequence/mamba2/backward.rs, tests module,
     ``make_realistic_cuda_inputs``): b=1, T=32, G=4, one head per group,
     P=64, N=16, with a nonzero initial state.  Flat index order is the
     row-major order of the page's grouped shapes, which is the same memory

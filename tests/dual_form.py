@@ -1,7 +1,7 @@
 """The SSD in its dual (quadratic, attention-like) form, brute force in numpy.
 
-Unrolling the recurrence of the page-1 reference
-(burn_dragon_kernel mamba2/backward.rs, ssd_forward_state_history_reference)
+Unrolling the recurrence of the reference page
+(burn_dragon_kernel src/sequence/mamba2/backward.rs, ssd_forward_state_history_reference)
 gives, per head with A = -exp(A_log) and the global inclusive cumulative sum
 S_t = sum_{r<=t} dt_r A,
 

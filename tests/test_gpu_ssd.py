@@ -30,7 +30,7 @@ def test_workload_parity_full_size(name):
 @pytest.mark.parametrize("chunk", [16, 32])
 @pytest.mark.parametrize("saved", [True, False])
 def test_page_test_pattern(chunk, saved):
-    # The deterministic inputs of the page-1 parity tests (b=1, T=32, G=4, one
+    # The deterministic inputs of the page's parity tests (b=1, T=32, G=4, one
     # head per group, P=64, N=16, nonzero initial state), with and without the
     # saved history.  Both our relative bar and the page's absolute 5e-4 hold.
     d = make_p1test_inputs()

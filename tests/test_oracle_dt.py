@@ -1,5 +1,5 @@
 """Pins of the oracle's dt activation (dt = softplus(dt_raw + dt_bias) and its
-gradient; page 1 of burn_dragon_kernel mamba2/backward.rs, the dt_pre and
+gradient; the burn_dragon_kernel src/sequence/mamba2/backward.rs page, the dt_pre and
 grad_dt_pre / grad_dt_bias lines of tensorized_mamba2_backward_impl) against
 closed forms of softplus and against central differences of the whole chain
 dt_raw, dt_bias -> dt -> SSD forward -> L = sum(dy * y)."""
