@@ -47,24 +47,52 @@ KERNEL_SOURCES = {
 }
 
 
-# Device kernels behind each profiled launch (bf16 variant first).
+# Device kernels behind each profiled launch (bf16 variant first), as
+# substrings of the kernel names rocprofv3 records.
 DEVICE_KERNELS = {
-    "chunk_state_fwd": ("chunk_state_bf16_kernel", "chunk_state_kernel"),
-    "chunk_state_bwd": ("chunk_state_bf16_kernel", "chunk_state_kernel"),
+    "chunk_state_fwd": ("chunk_state_bf16_kernel<false>", "chunk_state_kernel"),
+    "chunk_state_bwd": ("chunk_state_bf16_kernel<true>", "chunk_state_kernel"),
     "chunk_out_fwd": ("out_fwd_bf16_kernel", "chunk_out_fwd_kernel"),
     "chunk_bwd_col": ("bwd_col_bf16_kernel", "chunk_bwd_col_kernel"),
     "chunk_bwd_row": ("bwd_row_bf16_kernel", "chunk_bwd_row_kernel"),
+    "bwd_dt": ("bwd_dt_kernel",),
 }
+
+
+def _device_match(kernel: str, name: str) -> bool:
+    return any(n + "(" in name or n + "<" in name or (n.endswith(">") and n in name)
+               for n in DEVICE_KERNELS.get(kernel, (kernel + "_kernel",)))
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def method_bytes(cfg, kernel: str) -> float:
+    """The method's own inputs and outputs that one launch reads or writes,
+    each once, at their storage dtypes: x, dt, B, C, dy, y and the gradients
+    dx, ddt, dB, dC.  Intermediates (the chunk states and their gradients, the
+    per-head row and column sums) are not counted; the saved chunk states are
+    an optional output and are reported apart.  This is the denominator of the
+    headline roofline."""
+    s_a = 2 if cfg.dtype == "bf16" else 4
+    s_y = s_a
+    HP, GN, H = cfg.nheads * cfg.headdim, cfg.ngroups * cfg.dstate, cfg.nheads
+    per_token = {
+        "chunk_state_fwd": HP * s_a + GN * s_a + H * s_a,
+        "chunk_out_fwd": 2 * HP * s_a + 2 * GN * s_a + H * s_a,
+        "chunk_state_bwd": HP * s_y + GN * s_a + H * s_a,
+        "chunk_bwd_col": HP * s_a + 2 * GN * s_a + H * s_a + HP * s_y + HP * 4 + GN * 4,
+        "chunk_bwd_row": HP * s_a + 2 * GN * s_a + H * s_a + HP * s_y + GN * 4,
+        "bwd_dt": H * s_a + H * 4,
+    }
+    return per_token[kernel] * cfg.batch * cfg.seqlen
+
+
 def algorithmic_bytes(cfg, kernel: str) -> float:
-    """Bytes one launch must move at minimum: each input it needs read once and
-    each output written once, at the storage dtypes (the per-token figures are
-    the per_token expressions below)."""
+    """Bytes one launch must move at minimum counting its intermediates too:
+    each input it needs read once and each output written once, at the storage
+    dtypes (the per-token figures are the per_token expressions below)."""
     s_a = 2 if cfg.dtype == "bf16" else 4
     s_y = s_a
     tok = cfg.batch * cfg.seqlen
@@ -137,18 +165,21 @@ def _counter_rows(d: str):
 
 
 def write_counter_summary(fetch_dir: str, write_dir: str, kernel: str, workload: str, copy_mb: int) -> None:
-    """HBM bytes per launch of `kernel` from rocprofv3 FETCH_SIZE / WRITE_SIZE
-    runs (KiB per dispatch), each scaled by what the same counter reads for the
-    plain copy of `copy_mb` MiB that --calibrate-copy-mb ran in those runs."""
+    """HBM bytes per launch of `kernel` (or of each kernel of a comma list)
+    from rocprofv3 FETCH_SIZE / WRITE_SIZE runs (KiB per dispatch), each scaled
+    by what the same counter reads for the plain copy of `copy_mb` MiB that
+    --calibrate-copy-mb ran in those runs."""
+    if "," in kernel:
+        for k in kernel.split(","):
+            write_counter_summary(fetch_dir, write_dir, k, workload, copy_mb)
+        return
     if copy_mb <= 0:
         raise SystemExit("--counter-summary needs --calibrate-copy-mb (the calibration copy size)")
     known = float(copy_mb << 20)
     out = {}
     for label, d, counter in (("fetch", fetch_dir, "FETCH_SIZE"), ("write", write_dir, "WRITE_SIZE")):
         rows = [r for r in _counter_rows(d) if r["Counter_Name"] == counter]
-        names = DEVICE_KERNELS.get(kernel, (kernel + "_kernel",))
-        kv = [float(r["Counter_Value"]) for r in rows if any(n + "(" in r["Kernel_Name"] or n + "<" in r["Kernel_Name"]
-                                                             for n in names)]
+        kv = [float(r["Counter_Value"]) for r in rows if _device_match(kernel, r["Kernel_Name"])]
         copies = sorted(float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"])
         if not kv or not copies:
             raise SystemExit(f"no {counter} rows for {kernel} or for the calibration copy in {d}")
@@ -176,6 +207,8 @@ def write_counter_summary(fetch_dir: str, write_dir: str, kernel: str, workload:
         f"fetch_bytes_per_launch: {fetch_b:.0f}",
         f"write_bytes_per_launch: {write_b:.0f}",
         f"hbm_bytes_per_launch: {fetch_b + write_b:.0f}",
+        f"method_bytes_per_launch: {method_bytes(CONFIGS_BY_NAME()[workload], kernel):.0f}",
+        f"algorithmic_bytes_per_launch (with intermediates): {algorithmic_bytes(CONFIGS_BY_NAME()[workload], kernel):.0f}",
         f"source_digest: {source_digest(kernel)}",
         "",
         "The digest covers the kernel's source files; bench.py reports this traffic only while it matches.",
@@ -183,6 +216,11 @@ def write_counter_summary(fetch_dir: str, write_dir: str, kernel: str, workload:
     with open(path, "w") as f:
         f.write("\n".join(lines) + "\n")
     print(path)
+
+
+def CONFIGS_BY_NAME():
+    from ssd_inputs import CONFIGS
+    return CONFIGS
 
 
 def _kernel_base(name: str) -> str:
@@ -264,11 +302,13 @@ def to_dev(a):
 
 
 def roofline_entry(cfg, kernel: str, t_s: float) -> dict:
-    """Roofline of one launch of `kernel` taking t_s seconds.  The roof that
-    bounds it is HBM when its algorithmic flops per algorithmic byte fall below
+    """Roofline of one launch of `kernel` taking t_s seconds.  `achieved`
+    counts the method's inputs and outputs the launch moves (method_bytes); the
+    figure with its intermediates counted too is `with_intermediates_gbs`.  The
+    roof that bounds it is HBM when its algorithmic flops per byte fall below
     the machine balance of the operand dtype's MFMA peak over the HBM peak, and
     that MFMA peak above it."""
-    alg = algorithmic_bytes(cfg, kernel)
+    alg = method_bytes(cfg, kernel)
     flops = algorithmic_flops(cfg, kernel)
     achieved = alg / t_s / 1e9
     tflops = flops / t_s / 1e12
@@ -280,8 +320,10 @@ def roofline_entry(cfg, kernel: str, t_s: float) -> dict:
     else:
         r = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
              "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic, "mfma_tflops": round(tflops, 2)}
-    r.update({"kernel": kernel, "kernel_ms": round(t_s * 1e3, 4), "algorithmic_bytes": alg,
-              "algorithmic_flops": flops, "mfma_util_pct": measured_mfma_util(kernel, cfg.name)})
+    r.update({"scope": "dominant kernel (per launch)", "kernel": kernel, "kernel_ms": round(t_s * 1e3, 4),
+              "algorithmic_bytes": alg, "algorithmic_flops": flops,
+              "with_intermediates_gbs": round(algorithmic_bytes(cfg, kernel) / t_s / 1e9, 1),
+              "mfma_util_pct": measured_mfma_util(kernel, cfg.name)})
     return r
 
 
@@ -476,10 +518,16 @@ def cpu_baseline(cfg, d, batches: int, min_wall_s: float = 1.0):
     what = "SSD fwd+bwd" if not cfg.shell else "dt activation + conv1d/SiLU + SSD + RMSNorm-gated, fwd+bwd"
     if cfg.d_model:
         what += " with the projections as numpy f64 matrix products"
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        avail = os.cpu_count() or 1
     return {"value": reps * nb * cfg.seqlen / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "host_cpus": os.cpu_count(), "cpus_available": avail,
             "sample": (f"sequential f64 oracle, {what} on batch rows 0..{nb - 1} of {cfg.batch} "
-                       f"({nb * cfg.seqlen} tokens) run {reps} times, {el:.1f} s wall on {threads} threads; "
-                       "tokens/s of that sample")}
+                       f"({nb * cfg.seqlen} tokens) run {reps} times, {el:.1f} s wall on {threads} threads "
+                       f"(the host reports {os.cpu_count()} CPUs, {avail} available to this process; the oracle "
+                       "takes at most 16, one GPU's share of the host); tokens/s of that sample")}
 
 
 def main():

@@ -60,7 +60,14 @@ def _lib():
 
 
 def default_threads() -> int:
-    return max(1, min(16, os.cpu_count() or 1))
+    """Threads for the oracle's (batch, head) units: the CPUs this process may
+    run on, at most 16 (one GPU's share of the host's cores on the machines
+    the benchmark runs on, whatever the host's total)."""
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        avail = os.cpu_count() or 1
+    return max(1, min(16, avail))
 
 
 def _f64(a) -> Optional[np.ndarray]:

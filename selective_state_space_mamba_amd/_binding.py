@@ -143,6 +143,26 @@ def _need(t: torch.Tensor, name: str, shape, dtype=None, device=None):
         raise ValueError(f"{name} is on {t.device}, expected {device}")
 
 
+def _need_workspace(ws: Optional[torch.Tensor], device) -> int:
+    """Byte size of a caller-supplied workspace (a contiguous uint8 device buffer)."""
+    if ws is None:
+        return 0
+    if not isinstance(ws, torch.Tensor) or ws.dtype != torch.uint8:
+        raise TypeError("workspace must be a torch.uint8 tensor")
+    if not ws.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    if ws.device != device:
+        raise ValueError(f"workspace is on {ws.device}, expected {device}")
+    return ws.numel()
+
+
+def _on_gpu(t: torch.Tensor, name: str):
+    # the library takes device pointers only: a host pointer handed to a kernel
+    # would fault the GPU, so host tensors are refused here
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU (cuda/hip device) tensor")
+
+
 def make_problem(x: torch.Tensor, B: torch.Tensor, chunk: int, dy_dtype: Optional[torch.dtype] = None) -> Problem:
     b, T, H, P = x.shape
     G, N = B.shape[2], B.shape[3]
@@ -155,6 +175,9 @@ def ssd_workspace_bytes(prob: Problem, for_backward: bool, has_chunk_states: boo
 
 
 def _check_inputs(x, dt, A_log, B, C, D, init_state):
+    _on_gpu(x, "x")
+    if x.dim() != 4 or B.dim() != 4:
+        raise ValueError("x must be [b, T, H, P] and B, C [b, T, G, N]")
     b, T, H, P = x.shape
     G, N = B.shape[2], B.shape[3]
     dev = x.device
@@ -184,16 +207,21 @@ def ssd_fwd(x, dt, A_log, B, C, D, init_state=None, chunk: int = 256, want_chunk
     y = out.get("y")
     if y is None:
         y = torch.empty((b, T, H, P), dtype=x.dtype, device=x.device)
+    _need(y, "out['y']", (b, T, H, P), x.dtype, x.device)
     fin = out.get("final_state")
     if fin is None and want_final_state:
         fin = torch.empty((b, H, P, N), dtype=torch.float32, device=x.device)
+    if fin is not None:
+        _need(fin, "out['final_state']", (b, H, P, N), torch.float32, x.device)
     cs = out.get("chunk_states")
     if cs is None and want_chunk_states:
         cs = torch.empty((b, nc, H, P, N), dtype=torch.float32, device=x.device)
+    if cs is not None:
+        _need(cs, "out['chunk_states']", (b, nc, H, P, N), torch.float32, x.device)
     need = lib.ssd_workspace_bytes(ctypes.byref(prob), 0, int(cs is not None))
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
-    wsz = 0 if workspace is None else workspace.numel()
+    wsz = _need_workspace(workspace, x.device)
     _check(lib.ssd_fwd(ctypes.byref(prob), _ptr(x), _ptr(dt), _ptr(A_log), _ptr(B), _ptr(C), _ptr(D),
                        _ptr(init_state), _ptr(y), _ptr(fin), _ptr(cs), _ptr(workspace), wsz, _stream(stream)))
     return y, fin, cs
@@ -222,13 +250,16 @@ def ssd_bwd(x, dt, A_log, B, C, D, dy, init_state=None, chunk_states=None, chunk
     for k, s in shapes.items():
         if out.get(k) is None:
             out[k] = torch.empty(s, **f32)
+        _need(out[k], f"out['{k}']", s, torch.float32, x.device)
     if want_d_init_state and out.get("d_init_state") is None:
         out["d_init_state"] = torch.empty((b, H, P, N), **f32)
     dinit = out.get("d_init_state")
+    if dinit is not None:
+        _need(dinit, "out['d_init_state']", (b, H, P, N), torch.float32, x.device)
     need = lib.ssd_workspace_bytes(ctypes.byref(prob), 1, int(chunk_states is not None))
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
-    wsz = 0 if workspace is None else workspace.numel()
+    wsz = _need_workspace(workspace, x.device)
     _check(lib.ssd_bwd(ctypes.byref(prob), _ptr(x), _ptr(dt), _ptr(A_log), _ptr(B), _ptr(C), _ptr(D),
                        _ptr(init_state), _ptr(chunk_states), _ptr(dy), _ptr(d_final_state), _ptr(out["dx"]),
                        _ptr(out["ddt"]),
@@ -241,6 +272,7 @@ def ssd_bwd(x, dt, A_log, B, C, D, dy, init_state=None, chunk_states=None, chunk
 def conv1d_silu_fwd(xbc, w, bias, d_inner: int, ngroups: int, dstate: int, stream=None):
     """Causal depthwise conv1d + SiLU on xbc [b,T,conv_dim]; returns
     (x [b,T,d_inner], B [b,T,G,N], C [b,T,G,N]) in xbc's dtype."""
+    _on_gpu(xbc, "xbc")
     lib = load_library()
     b, T, cd = xbc.shape
     K = w.shape[1]
@@ -260,6 +292,7 @@ def conv1d_silu_bwd(xbc, w, bias, dx, dB, dC, d_inner: int, ngroups: int, dstate
                     stream=None):
     """Backward of conv1d_silu_fwd given f32 gradients of its outputs; returns
     (dxbc [b,T,conv_dim], dw [conv_dim,d_conv], dbias [conv_dim]) in f32."""
+    _on_gpu(xbc, "xbc")
     lib = load_library()
     b, T, cd = xbc.shape
     K = w.shape[1]
@@ -273,7 +306,7 @@ def conv1d_silu_bwd(xbc, w, bias, dx, dB, dC, d_inner: int, ngroups: int, dstate
     need = lib.mamba2_conv1d_silu_bwd_workspace_bytes(b, T, d_inner, ngroups, dstate, K)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=xbc.device)
-    wsz = 0 if workspace is None else workspace.numel()
+    wsz = _need_workspace(workspace, xbc.device)
     _check(lib.mamba2_conv1d_silu_bwd(b, T, d_inner, ngroups, dstate, K, _code(xbc.dtype), _ptr(xbc), _ptr(w),
                                       _ptr(bias), _ptr(dx), _ptr(dB), _ptr(dC), _ptr(dxbc), _ptr(dw), _ptr(db),
                                       _ptr(workspace), wsz, _stream(stream)))
@@ -283,6 +316,7 @@ def conv1d_silu_bwd(xbc, w, bias, dx, dB, dC, d_inner: int, ngroups: int, dstate
 def rmsnorm_gated_fwd(y, z, w, eps: float = 1e-5, stream=None):
     """RMSNorm over the last axis of y, times w * silu(z).  Returns
     (out in y's dtype, inv_rms f32 over the leading axes)."""
+    _on_gpu(y, "y")
     lib = load_library()
     width = y.shape[-1]
     rows = y.numel() // width if width else 0
@@ -300,6 +334,7 @@ def rmsnorm_gated_fwd(y, z, w, eps: float = 1e-5, stream=None):
 def rmsnorm_gated_bwd(y, z, w, inv_rms, g, workspace=None, stream=None, dy_dtype=torch.float32):
     """Backward of rmsnorm_gated_fwd with the saved inv_rms; returns
     (dy in dy_dtype, dz f32, dw f32)."""
+    _on_gpu(y, "y")
     lib = load_library()
     width = y.shape[-1]
     rows = y.numel() // width if width else 0
@@ -314,7 +349,7 @@ def rmsnorm_gated_bwd(y, z, w, inv_rms, g, workspace=None, stream=None, dy_dtype
     need = lib.mamba2_rmsnorm_gated_bwd_workspace_bytes(rows, width)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=y.device)
-    wsz = 0 if workspace is None else workspace.numel()
+    wsz = _need_workspace(workspace, y.device)
     _check(lib.mamba2_rmsnorm_gated_bwd(rows, width, _code(y.dtype), _code(g.dtype), _code(dy_dtype), _ptr(y),
                                         _ptr(z), _ptr(w),
                                         _ptr(inv_rms), _ptr(g), _ptr(dy), _ptr(dz), _ptr(dw), _ptr(workspace), wsz,
@@ -325,6 +360,7 @@ def rmsnorm_gated_bwd(y, z, w, inv_rms, g, workspace=None, stream=None, dy_dtype
 def dt_softplus_fwd(dt_raw, dt_bias, out=None, stream=None):
     """dt = softplus(dt_raw + dt_bias) over [..., H] in dt_raw's dtype (the form
     ssd_fwd / ssd_bwd take as dt)."""
+    _on_gpu(dt_raw, "dt_raw")
     lib = load_library()
     H = dt_raw.shape[-1]
     rows = dt_raw.numel() // H if H else 0
@@ -340,6 +376,7 @@ def dt_softplus_fwd(dt_raw, dt_bias, out=None, stream=None):
 def dt_softplus_bwd(dt_raw, dt_bias, ddt, workspace=None, out=None, stream=None):
     """Backward of dt_softplus_fwd: returns (ddt_raw f32 [..., H], d_dt_bias f32 [H])
     from ddt, the gradient of dt that ssd_bwd returns."""
+    _on_gpu(dt_raw, "dt_raw")
     lib = load_library()
     H = dt_raw.shape[-1]
     rows = dt_raw.numel() // H if H else 0
@@ -350,10 +387,12 @@ def dt_softplus_bwd(dt_raw, dt_bias, ddt, workspace=None, out=None, stream=None)
     if out is None:
         out = (torch.empty(tuple(dt_raw.shape), **f32), torch.empty((H,), **f32))
     ddt_raw, d_bias = out
+    _need(ddt_raw, "out[0] (ddt_raw)", tuple(dt_raw.shape), torch.float32, dt_raw.device)
+    _need(d_bias, "out[1] (d_dt_bias)", (H,), torch.float32, dt_raw.device)
     need = lib.ssd_dt_softplus_bwd_workspace_bytes(rows, H)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=dt_raw.device)
-    wsz = 0 if workspace is None else workspace.numel()
+    wsz = _need_workspace(workspace, dt_raw.device)
     _check(lib.ssd_dt_softplus_bwd(rows, H, _code(dt_raw.dtype), _ptr(dt_raw), _ptr(dt_bias), _ptr(ddt),
                                    _ptr(ddt_raw), _ptr(d_bias), _ptr(workspace), wsz, _stream(stream)))
     return ddt_raw, d_bias
@@ -363,7 +402,11 @@ def gemm(A, B, trans_a: bool = False, trans_b: bool = False, out=None, out_dtype
          alpha: float = 1.0, beta: float = 0.0, stream=None):
     """out[m,n] = alpha * op(A) @ op(B) + beta * out for 2-D contiguous bf16 A, B
     (op transposes when trans_*); out in out_dtype (bf16 or f32)."""
+    _on_gpu(A, "A")
     lib = load_library()
+    _on_gpu(B, "B")
+    if B.device != A.device:
+        raise ValueError(f"B is on {B.device}, expected {A.device}")
     if A.dtype != torch.bfloat16 or B.dtype != torch.bfloat16:
         raise TypeError("gemm takes bfloat16 operands")
     if A.dim() != 2 or B.dim() != 2 or not A.is_contiguous() or not B.is_contiguous():
@@ -382,6 +425,7 @@ def gemm(A, B, trans_a: bool = False, trans_b: bool = False, out=None, out_dtype
 
 def cast_bf16(src, out=None, stream=None):
     """bf16 copy (round to nearest even) of a contiguous f32 tensor."""
+    _on_gpu(src, "src")
     lib = load_library()
     if src.dtype != torch.float32 or not src.is_contiguous():
         raise TypeError("cast_bf16 takes a contiguous float32 tensor")

@@ -69,6 +69,17 @@ int check_problem(const ssd_problem* p, ssd::Dims* d) {
   const int64_t elems = p->batch * p->seqlen * p->nheads * p->headdim;
   if (p->seqlen > (int64_t(1) << 30) || elems > (int64_t(1) << 40))
     return fail(SSD_ERR_SHAPE, "problem too large");
+  // The largest launch grids: one workgroup per (batch, chunk, head, 64-row
+  // block) at most (general kernels, groups split down to single heads), one
+  // per 256 elements of dB / dC (head-split sums) and of the [b, T, H] dt
+  // series.  Each must fit a one-dimensional grid.
+  const int64_t nchunks = p->seqlen / p->chunk, nblocks = (p->chunk + 63) / 64;
+  const int64_t grid_max = (int64_t(1) << 31) - 1;
+  if (p->batch * nchunks * p->nheads * nblocks > grid_max ||
+      (p->batch * p->seqlen * p->ngroups * p->dstate + 255) / 256 > grid_max ||
+      (p->batch * p->seqlen * p->nheads + 255) / 256 > grid_max)
+    return fail(SSD_ERR_SHAPE, "problem too large: a launch grid would exceed %lld workgroups",
+                (long long)grid_max);
   d->b = static_cast<int>(p->batch);
   d->T = static_cast<int>(p->seqlen);
   d->H = static_cast<int>(p->nheads);

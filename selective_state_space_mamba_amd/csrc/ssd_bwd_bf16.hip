@@ -983,10 +983,16 @@ __global__ __launch_bounds__(BT) void bwd_row_bf16_kernel(
 }
 
 bool bwd_bf16_supported(const Dims& d) {
-  const int64_t HPb = int64_t(d.H) * d.P * 2, GNb = int64_t(d.G) * d.N * 2;
-  return d.P % 8 == 0 && d.N % 8 == 0 && int64_t(QMAX) * HPb < (int64_t(1) << 30) &&
-         int64_t(QMAX) * GNb < (int64_t(1) << 30) && HPb * d.N < (int64_t(1) << 30) &&
-         int64_t(QMAX) * d.H * 2 < (int64_t(1) << 30);
+  // Every buffer descriptor of the bf16 family starts at a chunk (x, dy, y,
+  // dx, B, C, dt), at one (batch, chunk) state block (Gamma, the bf16 states)
+  // or at one (batch, chunk) of the [b, H, T] per-head sums, and takes 32-bit
+  // byte offsets within its 2 GiB range.  The largest offsets are a chunk of
+  // f32 dx (Q H P 4), a state block (H P N 2) and a head's row of the sums
+  // (H T 4); problems past these bounds take the general kernels.
+  const int64_t lim = (int64_t(1) << 31) - 4096;
+  const int64_t HP = int64_t(d.H) * d.P, GN = int64_t(d.G) * d.N;
+  return d.P % 8 == 0 && d.N % 8 == 0 && int64_t(QMAX) * HP * 4 < lim && int64_t(QMAX) * GN * 4 < lim &&
+         HP * d.N * 2 < lim && int64_t(d.H) * d.T * 4 < lim && int64_t(QMAX) * d.H * 2 < lim;
 }
 
 hipError_t launch_bwd_row_bf16(const Dims& d, int nsplit, const void* x, const void* B, const void* C,

@@ -98,10 +98,10 @@ __global__ __launch_bounds__(ST) void chunk_state_bf16_kernel(
     }
 
   auto chunk_of = [&](int it) { return REV ? nc - 1 - it : it; };
-  // slab copies: one descriptor per batch row, the slab's first row as the
-  // scalar offset, the per-lane offsets computed once
-  const i32x4 rsX = make_rsrc(X + static_cast<int64_t>(bi) * T * HP);
-  const i32x4 rsB = make_rsrc(Bm + static_cast<int64_t>(bi) * T * GN);
+  // slab copies: one descriptor per chunk (a descriptor spans 2 GiB and its
+  // offsets are 32-bit, so a base per batch row would stop reaching the data
+  // once a row holds 2 GiB of x), the slab's first row as the scalar offset,
+  // the per-lane offsets computed once
   TileLanes<SSJ, 4, SW> lx;
   TileLanes<SSJ, 16, SW> lbs;
   lx.init(HPb, pch);
@@ -111,7 +111,10 @@ __global__ __launch_bounds__(ST) void chunk_state_bf16_kernel(
   // be vmcnt(0) and hold up every copy) and (bwd) H_c
   auto load_slab = [&](int it, int sl) {
     const int c = chunk_of(it);
-    const uint32_t t0 = static_cast<uint32_t>(c * Q + sl * SSJ);  // the slab's first step in the batch row
+    const int64_t crow = static_cast<int64_t>(bi) * T + static_cast<int64_t>(c) * Q;  // the chunk's first row
+    const i32x4 rsX = make_rsrc(X + crow * HP);
+    const i32x4 rsB = make_rsrc(Bm + crow * GN);
+    const uint32_t t0 = static_cast<uint32_t>(sl * SSJ);  // the slab's first step in the chunk
     const int vr = min(SSJ, Q - sl * SSJ);
     const int buf = (it * nsl + sl) & 1;
     lx.issue(sX + buf * XSLAB, rsX, t0 * HPb + static_cast<uint32_t>(h * P + p0) * 2, vr);

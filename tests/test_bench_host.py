@@ -27,11 +27,24 @@ def test_grouped_workload_algorithmic_bytes():
     assert round(bench.algorithmic_bytes(cfg, "chunk_bwd_col") / 1e6, 1) == 221.8
 
 
+def test_method_bytes_exclude_intermediates():
+    cfg = CONFIGS["grouped"]
+    tok = cfg.batch * cfg.seqlen
+    HP, GN, H = 32 * 64, 8 * 128, 32
+    # the column kernel moves x, B, C, dt, dy (bf16) and dx, dB (f32) of the
+    # method; Gamma and the per-row sums are intermediates
+    assert bench.method_bytes(cfg, "chunk_bwd_col") == (HP * 2 + 2 * GN * 2 + H * 2 + HP * 2 + HP * 4 + GN * 4) * tok
+    assert round(bench.method_bytes(cfg, "chunk_bwd_col") / 1e6, 1) == 201.9
+    # chunk states are an optional output, not counted
+    assert bench.method_bytes(cfg, "chunk_state_fwd") == (HP * 2 + GN * 2 + H * 2) * tok
+
+
 def test_roof_choice_follows_machine_balance():
     # bf16 grouped column kernel: about 97 flop/B, below 2.5 PFLOP/s / 8 TB/s
     r = bench.roofline_entry(CONFIGS["grouped"], "chunk_bwd_col", 88e-6)
     assert r["bound"] == "hbm" and r["unit"] == "GB/s"
-    assert abs(r["frac"] - bench.algorithmic_bytes(CONFIGS["grouped"], "chunk_bwd_col") / 88e-6 / 8e12) < 1e-4
+    assert abs(r["frac"] - bench.method_bytes(CONFIGS["grouped"], "chunk_bwd_col") / 88e-6 / 8e12) < 1e-4
+    assert r["with_intermediates_gbs"] > r["achieved"]
     # f32 long column kernel: above 157.3 TFLOP/s / 8 TB/s
     r = bench.roofline_entry(CONFIGS["long"], "chunk_bwd_col", 1.9e-3)
     assert r["bound"] == "mfma" and r["peak"] == 157.3

@@ -188,3 +188,101 @@ def test_gemm_and_cast_argument_checks(lib):
     assert lib.ssd_cast_f32_to_bf16(i64(-1), f, f, None) == -1
     assert lib.ssd_cast_f32_to_bf16(i64(8), None, f, None) == -1
     assert lib.ssd_cast_f32_to_bf16(i64(0), None, None, None) == 0
+
+
+def test_launch_grid_limit(lib):
+    # 65535 batch rows of 65536 one-step chunks: one workgroup per (row, chunk,
+    # head, block) would be 2^32 workgroups; rejected before any launch
+    p = prob(batch=65535, seqlen=65536, chunk=1, nheads=1, headdim=1, dstate=1, ngroups=1)
+    for f in (call_fwd, call_bwd):
+        assert f(lib, p) == -2
+        assert "launch grid" in lib.ssd_last_error().decode()
+    assert lib.ssd_workspace_bytes(ctypes.byref(p), 1, 0) == 0
+
+
+def _bf16_state_copy_bytes(lib, **kw):
+    # the bf16 kernel family keeps a bf16 copy of the chunk states in the
+    # backward workspace; the general kernels (here: bf16 activations with an
+    # f32 dy) do not, with everything else the same
+    a = lib.ssd_workspace_bytes(ctypes.byref(prob(act_dtype=1, dy_dtype=1, **kw)), 1, 1)
+    b = lib.ssd_workspace_bytes(ctypes.byref(prob(act_dtype=1, dy_dtype=0, **kw)), 1, 1)
+    return a - b
+
+
+def test_bf16_family_offset_bounds(lib):
+    big = dict(batch=1, nheads=64, headdim=64, dstate=128, ngroups=8, chunk=256)
+    states = lambda T: 4 * (T // 256) * 64 * 64 * 128
+    # a 262144-step row holds 2 GiB of bf16 x: the chunk-state kernel's
+    # descriptors start at each chunk, so the bf16 family still applies
+    assert _bf16_state_copy_bytes(lib, seqlen=262144, **big) == states(262144) // 2
+    # 2^23 steps of 64 heads: a head's row of the [b, H, T] per-head sums
+    # spans 2^31 bytes, past a descriptor's 32-bit range -> general kernels
+    assert _bf16_state_copy_bytes(lib, seqlen=1 << 23, **big) == 0
+
+
+@pytest.fixture
+def meta_binding(monkeypatch, lib):
+    # meta tensors carry shapes, dtypes and devices but no memory: every
+    # binding check runs, and a check that is missing lets a null pointer
+    # reach the library, which then answers SSDError (not the ValueError /
+    # TypeError the binding raises)
+    monkeypatch.setattr(bd, "_on_gpu", lambda t, name: None)
+    b, T, H, P, N, G = 1, 256, 4, 64, 32, 2
+    m = dict(device="meta")
+    t = dict(x=torch.empty((b, T, H, P), **m), dt=torch.empty((b, T, H), **m), B=torch.empty((b, T, G, N), **m),
+             C=torch.empty((b, T, G, N), **m), A_log=torch.empty(H, **m), D=torch.empty(H, **m))
+    return t, (b, T, H, P, N, G)
+
+
+import torch  # noqa: E402
+
+
+@pytest.mark.parametrize("key,shape,dtype", [
+    ("y", (1, 256, 4, 32), torch.float32),
+    ("y", (1, 256, 4, 64), torch.bfloat16),
+    ("final_state", (1, 4, 64, 16), torch.float32),
+    ("chunk_states", (1, 1, 4, 64, 32), torch.bfloat16),
+])
+def test_binding_checks_fwd_out_buffers(meta_binding, key, shape, dtype):
+    t, _ = meta_binding
+    bad = {key: torch.empty(shape, dtype=dtype, device="meta")}
+    with pytest.raises((ValueError, TypeError), match=key):
+        bd.ssd_fwd(t["x"], t["dt"], t["A_log"], t["B"], t["C"], t["D"], chunk=256, out=bad)
+
+
+@pytest.mark.parametrize("key,shape,dtype", [
+    ("dx", (1, 256, 4, 32), torch.float32),
+    ("dx", (1, 256, 4, 64), torch.bfloat16),
+    ("ddt", (1, 256, 3), torch.float32),
+    ("dA_log", (5,), torch.float32),
+    ("dB", (1, 256, 2, 16), torch.float32),
+    ("dC", (1, 256, 2, 32), torch.float64),
+    ("dD", (4, 1), torch.float32),
+    ("d_init_state", (1, 4, 64, 31), torch.float32),
+])
+def test_binding_checks_bwd_out_buffers(meta_binding, key, shape, dtype):
+    t, _ = meta_binding
+    bad = {key: torch.empty(shape, dtype=dtype, device="meta")}
+    with pytest.raises((ValueError, TypeError), match=key):
+        bd.ssd_bwd(t["x"], t["dt"], t["A_log"], t["B"], t["C"], t["D"], t["x"], chunk=256, out=bad)
+
+
+def test_binding_checks_workspace_and_dt_outputs(meta_binding):
+    t, (b, T, H, P, N, G) = meta_binding
+    with pytest.raises(TypeError, match="workspace"):
+        bd.ssd_fwd(t["x"], t["dt"], t["A_log"], t["B"], t["C"], t["D"], chunk=256,
+                   workspace=torch.empty(100, dtype=torch.float32, device="meta"))
+    raw, bias, ddt = t["dt"], t["A_log"], torch.empty((b, T, H), device="meta")
+    with pytest.raises(ValueError, match="ddt_raw"):
+        bd.dt_softplus_bwd(raw, bias, ddt, out=(torch.empty((b, T, H + 1), device="meta"), torch.empty(H, device="meta")))
+    with pytest.raises(ValueError, match="d_dt_bias"):
+        bd.dt_softplus_bwd(raw, bias, ddt, out=(torch.empty((b, T, H), device="meta"), torch.empty(H + 1, device="meta")))
+
+
+def test_binding_refuses_host_tensors(lib):
+    x = torch.zeros((1, 16, 2, 8))
+    B = torch.zeros((1, 16, 1, 4))
+    with pytest.raises(ValueError, match="GPU"):
+        bd.ssd_fwd(x, torch.zeros((1, 16, 2)), torch.zeros(2), B, B, torch.zeros(2), chunk=16)
+    with pytest.raises(ValueError, match="GPU"):
+        bd.rmsnorm_gated_fwd(torch.zeros((4, 8)), torch.zeros((4, 8)), torch.ones(8))

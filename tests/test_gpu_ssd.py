@@ -79,8 +79,9 @@ def test_f32_three_heads_per_group():
 
 
 def test_many_chunks_bf16():
-    # 256 chunks per head (over 128): the dt gradient and the dA_log / dD sums
-    # take their two-launch form (the workloads above take the one-launch form)
+    # 256 chunks per head with 16-step chunks and a 32-wide d_state: the dt
+    # kernel's final workgroup sums 512 chunk partials per head (every other
+    # test has at most 64)
     cfg = SSDConfig("many", 2, 2048, 4, 64, 32, 2, 16, "bf16", init_state=True, seed=12)
     d = make_inputs(cfg)
     compare(gpu_ssd(cfg, d), oracle_ssd(d, cfg.chunk), TOL["bf16"], label="256 chunks per head, bf16")
