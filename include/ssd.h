@@ -112,6 +112,25 @@ int ssd_bwd(const ssd_problem* prob, const void* x, const void* dt, const float*
             float* ddt, float* dA_log, float* dB, float* dC, float* dD, float* d_init_state,
             void* workspace, size_t workspace_bytes, void* stream);
 
+/* ssd_bwd for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments, results and errors as ssd_bwd, without the workspace: the
+ * scratch comes from a library-owned device array of SSD_NOALLOC_SCRATCH_BYTES
+ * on each GPU (held from the first call on that GPU until the process ends).
+ * Problems whose ssd_workspace_bytes(prob, 1, chunk_states != NULL) exceeds
+ * it are rejected with SSD_ERR_WORKSPACE.  The call allocates nothing: no
+ * hipMalloc, hipFree or allocating library routine.  Every call on one GPU
+ * uses that GPU's one array, so calls that overlap on a GPU (different
+ * streams, or threads, without ordering between them) race; order them on one
+ * stream.  The stream must belong to the current device (SSD_ERR_INVALID_ARG
+ * otherwise). */
+#define SSD_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int ssd_bwd_noalloc(const ssd_problem* prob, const void* x, const void* dt, const float* A_log,
+                    const void* B, const void* C, const float* D, const float* init_state,
+                    const float* chunk_states, const void* dy, const float* d_final_state, float* dx,
+                    float* ddt, float* dA_log, float* dB, float* dC, float* dD, float* d_init_state,
+                    void* stream);
+
 /* Causal depthwise conv1d (zero initial state) followed by SiLU, split into
  * the SSD inputs.  xbc [b,T,conv_dim] with conv_dim = d_inner + 2*ngroups*dstate
  * (channel order: x, then B, then C); w [conv_dim, d_conv] f32, tap d_conv-1

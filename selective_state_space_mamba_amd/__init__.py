@@ -25,6 +25,8 @@ from ._binding import (  # noqa: F401
     rmsnorm_gated_bwd,
     rmsnorm_gated_fwd,
     ssd_bwd,
+    ssd_bwd_noalloc,
+    NOALLOC_SCRATCH_BYTES,
     ssd_fwd,
     ssd_workspace_bytes,
     version,

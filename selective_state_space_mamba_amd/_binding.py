@@ -49,6 +49,8 @@ def load_library():
     lib.ssd_fwd.restype = ctypes.c_int
     lib.ssd_bwd.argtypes = [pp] + [vp] * 17 + [vp, sz, vp]
     lib.ssd_bwd.restype = ctypes.c_int
+    lib.ssd_bwd_noalloc.argtypes = [pp] + [vp] * 17 + [vp]
+    lib.ssd_bwd_noalloc.restype = ctypes.c_int
     lib.mamba2_conv1d_silu_fwd.argtypes = [i64] * 6 + [i32] + [vp] * 6 + [vp]
     lib.mamba2_conv1d_silu_fwd.restype = ctypes.c_int
     lib.mamba2_conv1d_silu_bwd_workspace_bytes.argtypes = [i64] * 6
@@ -266,6 +268,40 @@ def ssd_bwd(x, dt, A_log, B, C, D, dy, init_state=None, chunk_states=None, chunk
                        _ptr(out["dA_log"]), _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out["dD"]), _ptr(dinit),
                        _ptr(workspace), wsz, _stream(stream)))
     out["d_init_state"] = dinit
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20  # SSD_NOALLOC_SCRATCH_BYTES of include/ssd.h
+
+
+def ssd_bwd_noalloc(x, dt, A_log, B, C, D, dy, out: Dict[str, torch.Tensor], init_state=None, chunk_states=None,
+                    chunk: int = 256, stream=None, d_final_state: Optional[torch.Tensor] = None) -> Dict[str, torch.Tensor]:
+    """ssd_bwd through the entry point that allocates nothing (the library's
+    static scratch instead of a workspace).  `out` must hold every output
+    (dx, ddt, dA_log, dB, dC, dD, and d_init_state or None); nothing is
+    allocated here either."""
+    lib = load_library()
+    b, T, H, P, N, G = _check_inputs(x, dt, A_log, B, C, D, init_state)
+    if dy.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("dy must be float32 or bfloat16")
+    _need(dy, "dy", (b, T, H, P), device=x.device)
+    if d_final_state is not None:
+        _need(d_final_state, "d_final_state", (b, H, P, N), torch.float32, x.device)
+    if chunk_states is not None:
+        _need(chunk_states, "chunk_states", (b, T // chunk, H, P, N), torch.float32, x.device)
+    shapes = dict(dx=(b, T, H, P), ddt=(b, T, H), dA_log=(H,), dB=(b, T, G, N), dC=(b, T, G, N), dD=(H,))
+    for k, s_ in shapes.items():
+        if out.get(k) is None:
+            raise ValueError(f"out['{k}'] is required")
+        _need(out[k], f"out['{k}']", s_, torch.float32, x.device)
+    dinit = out.get("d_init_state")
+    if dinit is not None:
+        _need(dinit, "out['d_init_state']", (b, H, P, N), torch.float32, x.device)
+    prob = make_problem(x, B, chunk, dy.dtype)
+    _check(lib.ssd_bwd_noalloc(ctypes.byref(prob), _ptr(x), _ptr(dt), _ptr(A_log), _ptr(B), _ptr(C), _ptr(D),
+                               _ptr(init_state), _ptr(chunk_states), _ptr(dy), _ptr(d_final_state), _ptr(out["dx"]),
+                               _ptr(out["ddt"]), _ptr(out["dA_log"]), _ptr(out["dB"]), _ptr(out["dC"]),
+                               _ptr(out["dD"]), _ptr(dinit), _stream(stream)))
     return out
 
 

@@ -219,7 +219,12 @@ hipEvent_t prof_event() {
   return e;
 }
 
+// Set while ssd_bwd_noalloc runs: its launches record no events (creating one
+// is an allocation of the runtime's).
+thread_local bool g_prof_suppress = false;
+
 hipEvent_t prof_begin(hipStream_t st, const char* name) {
+  if (g_prof_suppress) return nullptr;
   std::lock_guard<std::mutex> lk(g_prof_mu);
   if (!g_prof_on || (!g_prof_only.empty() && g_prof_only != name)) return nullptr;
   hipEvent_t e = prof_event();
@@ -344,24 +349,64 @@ int ssd_fwd(const ssd_problem* prob, const void* x, const void* dt, const float*
   return ok();
 }
 
-int ssd_bwd(const ssd_problem* prob, const void* x, const void* dt, const float* A_log, const void* B,
-            const void* C, const float* D, const float* init_state, const float* chunk_states, const void* dy,
-            const float* d_final_state, float* dx, float* ddt, float* dA_log, float* dB, float* dC, float* dD,
-            float* d_init_state, void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The scratch of ssd_bwd_noalloc: one array per GPU, located per device with
+// hipGetSymbolAddress (its name is a host-side stand-in for the device
+// address and is never passed to a kernel).
+__device__ __align__(256) char scratch[SSD_NOALLOC_SCRATCH_BYTES];
+std::mutex g_scratch_mu;
+std::vector<void*> g_scratch_ptr;  // indexed by device ordinal
+
+// The device address of this device's scratch (taken once per device, with
+// that device current).
+int noalloc_scratch(hipStream_t st, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(SSD_ERR_HIP, "ssd_bwd_noalloc: hipGetDevice failed: %s", hipGetErrorString(e));
+  if (st) {
+    int sdev = -1;
+    e = hipStreamGetDevice(st, &sdev);
+    if (e != hipSuccess)
+      return fail(SSD_ERR_HIP, "ssd_bwd_noalloc: hipStreamGetDevice failed: %s", hipGetErrorString(e));
+    if (sdev != dev)
+      return fail(SSD_ERR_INVALID_ARG, "ssd_bwd_noalloc: the stream belongs to device %d, the current device is %d",
+                  sdev, dev);
+  }
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (static_cast<int>(g_scratch_ptr.size()) <= dev) g_scratch_ptr.resize(dev + 1, nullptr);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(SSD_ERR_HIP, "ssd_bwd_noalloc: hipGetSymbolAddress(scratch) failed on device %d: %s", dev,
+                  hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return SSD_OK;
+}
+
+int bwd_impl(const char* who, const ssd_problem* prob, const void* x, const void* dt, const float* A_log,
+             const void* B, const void* C, const float* D, const float* init_state, const float* chunk_states,
+             const void* dy, const float* d_final_state, float* dx, float* ddt, float* dA_log, float* dB, float* dC,
+             float* dD, float* d_init_state, void* workspace, size_t workspace_bytes, bool noalloc, void* stream) {
   ssd::Dims d;
   int rc = check_problem(prob, &d);
   if (rc != SSD_OK) return rc;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const ssd::DType act = static_cast<ssd::DType>(prob->act_dtype);
   const ssd::DType dyt = static_cast<ssd::DType>(prob->dy_dtype);
-  if (!A_log || !D || !dA_log || !dD) return fail(SSD_ERR_INVALID_ARG, "ssd_bwd: A_log, D, dA_log and dD are required");
+  if (!A_log || !D || !dA_log || !dD) return fail(SSD_ERR_INVALID_ARG, "%s: A_log, D, dA_log and dD are required", who);
   const bool empty = d.b == 0 || d.T == 0;
   if (!empty && (!x || !dt || !B || !C || !dy || !dx || !ddt || !dB || !dC))
-    return fail(SSD_ERR_INVALID_ARG, "ssd_bwd: x, dt, B, C, dy, dx, ddt, dB and dC are required");
+    return fail(SSD_ERR_INVALID_ARG, "%s: x, dt, B, C, dy, dx, ddt, dB and dC are required", who);
   const void* ptrs[] = {x,  dt, A_log, B,  C,  D,      init_state, chunk_states, dy, d_final_state,
                         dx, ddt, dA_log, dB, dC, dD, d_init_state};
   for (const void* p : ptrs)
-    if (p && !aligned16(p)) return fail(SSD_ERR_ALIGN, "ssd_bwd: a tensor pointer is not 16-byte aligned");
+    if (p && !aligned16(p)) return fail(SSD_ERR_ALIGN, "%s: a tensor pointer is not 16-byte aligned", who);
   if (empty) {
     SSD_LAUNCH(ssd::launch_fill(dA_log, d.H, 0.f, st), "fill");
     SSD_LAUNCH(ssd::launch_fill(dD, d.H, 0.f, st), "fill");
@@ -376,11 +421,22 @@ int ssd_bwd(const ssd_problem* prob, const void* x, const void* dt, const float*
     return ok();
   }
   const BwdPlan plan = plan_bwd(d, chunk_states != nullptr, use_bf16_kernels(d, prob->act_dtype, prob->dy_dtype));
-  if (!workspace) return fail(SSD_ERR_WORKSPACE, "ssd_bwd: workspace is null (%zu bytes needed)", plan.total);
+  if (noalloc) {
+    if (plan.total > SSD_NOALLOC_SCRATCH_BYTES)
+      return fail(SSD_ERR_WORKSPACE,
+                  "%s: the problem needs %zu bytes of scratch, more than the %zu of the library's static scratch "
+                  "(use ssd_bwd with a workspace%s)",
+                  who, plan.total, static_cast<size_t>(SSD_NOALLOC_SCRATCH_BYTES),
+                  chunk_states ? "" : ", or pass the saved chunk states");
+    rc = noalloc_scratch(static_cast<hipStream_t>(stream), &workspace);
+    if (rc != SSD_OK) return rc;
+    workspace_bytes = SSD_NOALLOC_SCRATCH_BYTES;
+  }
+  if (!workspace) return fail(SSD_ERR_WORKSPACE, "%s: workspace is null (%zu bytes needed)", who, plan.total);
   if (workspace_bytes < plan.total)
-    return fail(SSD_ERR_WORKSPACE, "ssd_bwd: workspace of %zu bytes is smaller than the %zu needed", workspace_bytes,
+    return fail(SSD_ERR_WORKSPACE, "%s: workspace of %zu bytes is smaller than the %zu needed", who, workspace_bytes,
                 plan.total);
-  if (!aligned16(workspace)) return fail(SSD_ERR_ALIGN, "ssd_bwd: workspace is not 16-byte aligned");
+  if (!aligned16(workspace)) return fail(SSD_ERR_ALIGN, "%s: workspace is not 16-byte aligned", who);
 
   ssd::BwdScratch s;
   s.rowM = at<float>(workspace, plan.rowM);
@@ -437,6 +493,29 @@ int ssd_bwd(const ssd_problem* prob, const void* x, const void* dt, const float*
   SSD_LAUNCH(ssd::launch_bwd_dt(d, act, dt, A_log, ddt, dA_log, dD, s, st), "bwd_dt");
   if (plan.nsplit > 1) SSD_LAUNCH(ssd::launch_bwd_split_sum(d, plan.nsplit, dB, dC, s, st), "bwd_split_sum");
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int ssd_bwd(const ssd_problem* prob, const void* x, const void* dt, const float* A_log, const void* B,
+            const void* C, const float* D, const float* init_state, const float* chunk_states, const void* dy,
+            const float* d_final_state, float* dx, float* ddt, float* dA_log, float* dB, float* dC, float* dD,
+            float* d_init_state, void* workspace, size_t workspace_bytes, void* stream) {
+  return bwd_impl("ssd_bwd", prob, x, dt, A_log, B, C, D, init_state, chunk_states, dy, d_final_state, dx, ddt,
+                  dA_log, dB, dC, dD, d_init_state, workspace, workspace_bytes, false, stream);
+}
+
+int ssd_bwd_noalloc(const ssd_problem* prob, const void* x, const void* dt, const float* A_log, const void* B,
+                    const void* C, const float* D, const float* init_state, const float* chunk_states,
+                    const void* dy, const float* d_final_state, float* dx, float* ddt, float* dA_log, float* dB,
+                    float* dC, float* dD, float* d_init_state, void* stream) {
+  g_prof_suppress = true;
+  const int rc = bwd_impl("ssd_bwd_noalloc", prob, x, dt, A_log, B, C, D, init_state, chunk_states, dy,
+                          d_final_state, dx, ddt, dA_log, dB, dC, dD, d_init_state, nullptr, 0, true, stream);
+  g_prof_suppress = false;
+  return rc;
 }
 
 // ------------------------------------------------------------------ shell

@@ -286,3 +286,19 @@ def test_binding_refuses_host_tensors(lib):
         bd.ssd_fwd(x, torch.zeros((1, 16, 2)), torch.zeros(2), B, B, torch.zeros(2), chunk=16)
     with pytest.raises(ValueError, match="GPU"):
         bd.rmsnorm_gated_fwd(torch.zeros((4, 8)), torch.zeros((4, 8)), torch.ones(8))
+
+
+def test_noalloc_scratch_size_matches_the_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define SSD_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == bd.NOALLOC_SCRATCH_BYTES
+
+
+def test_noalloc_refuses_a_problem_past_its_scratch_before_any_launch(lib):
+    # the f32 grouped-sized problem in recompute mode needs more scratch than
+    # the static array holds: refused before anything touches a device
+    p = prob(batch=4, seqlen=2048, nheads=32, ngroups=8)
+    assert lib.ssd_workspace_bytes(ctypes.byref(p), 1, 0) > bd.NOALLOC_SCRATCH_BYTES
+    f = ctypes.c_void_p(FAKE)
+    rc = lib.ssd_bwd_noalloc(ctypes.byref(p), f, f, f, f, f, f, None, None, f, None, f, f, f, f, f, f, None, None)
+    assert rc == -4 and "static scratch" in lib.ssd_last_error().decode()
