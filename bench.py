@@ -34,7 +34,7 @@ METRIC = "SSD fwd+bwd tokens/sec on 1 MI355X; achieved HBM GB/s and MFMA % of pe
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}  # MI355X dense matrix-core peaks
 KERNELS_FWD = ["chunk_state_fwd", "chunk_out_fwd"]
-KERNELS_BWD = ["chunk_state_bwd", "chunk_bwd_col", "chunk_bwd_row", "bwd_dt", "bwd_split_sum"]
+KERNELS_BWD = ["chunk_state_bwd", "chunk_bwd_fused", "chunk_bwd_col", "chunk_bwd_row", "bwd_dt", "bwd_split_sum"]
 KERNELS_SHELL = ["dt_softplus_fwd", "conv1d_silu_fwd", "rmsnorm_gated_fwd", "rmsnorm_gated_bwd", "conv1d_silu_bwd",
                  "dt_softplus_bwd"]
 KERNEL_SOURCES = {
@@ -43,6 +43,7 @@ KERNEL_SOURCES = {
     "chunk_out_fwd": ["ssd_chunk_fwd.hip", "ssd_fwd_bf16.hip", "ssd_async.hpp", "ssd_common.hpp"],
     "chunk_bwd_col": ["ssd_chunk_bwd.hip", "ssd_bwd_bf16.hip", "ssd_async.hpp", "ssd_common.hpp"],
     "chunk_bwd_row": ["ssd_chunk_bwd.hip", "ssd_bwd_bf16.hip", "ssd_async.hpp", "ssd_common.hpp"],
+    "chunk_bwd_fused": ["ssd_bwd_fused.hip", "ssd_async.hpp", "ssd_common.hpp"],
     "bwd_dt": ["ssd_chunk_bwd.hip", "ssd_common.hpp"],
 }
 
@@ -55,6 +56,7 @@ DEVICE_KERNELS = {
     "chunk_out_fwd": ("out_fwd_bf16_kernel", "chunk_out_fwd_kernel"),
     "chunk_bwd_col": ("bwd_col_bf16_kernel", "chunk_bwd_col_kernel"),
     "chunk_bwd_row": ("bwd_row_bf16_kernel", "chunk_bwd_row_kernel"),
+    "chunk_bwd_fused": ("bwd_fused_bf16_kernel",),
     "bwd_dt": ("bwd_dt_kernel",),
 }
 
@@ -84,6 +86,7 @@ def method_bytes(cfg, kernel: str) -> float:
         "chunk_state_bwd": HP * s_y + GN * s_a + H * s_a,
         "chunk_bwd_col": HP * s_a + 2 * GN * s_a + H * s_a + HP * s_y + HP * 4 + GN * 4,
         "chunk_bwd_row": HP * s_a + 2 * GN * s_a + H * s_a + HP * s_y + GN * 4,
+        "chunk_bwd_fused": HP * s_a + 2 * GN * s_a + H * s_a + HP * s_y + HP * 4 + 2 * GN * 4,
         "bwd_dt": H * s_a + H * 4,
     }
     return per_token[kernel] * cfg.batch * cfg.seqlen
@@ -105,6 +108,11 @@ def algorithmic_bytes(cfg, kernel: str) -> float:
         "chunk_state_bwd": HP * s_y + GN * s_a + H * s_a + st + sg,
         "chunk_bwd_col": HP * s_a + 2 * GN * s_a + H * s_a + HP * s_y + sg + HP * 4 + GN * 4 + 3 * H * 4,
         "chunk_bwd_row": HP * s_a + 2 * GN * s_a + H * s_a + HP * s_y + st + GN * 4 + 2 * H * 4,
+        # + Gamma and the bf16 states in; the per-head column sums, diagonal,
+        # R', readout term and the row sums of M (one slot per 64-column block
+        # at or before a row's block, (nb + 1) / 2 on average) out
+        "chunk_bwd_fused": (HP * s_a + 2 * GN * s_a + H * s_a + HP * s_y + 2 * sg + HP * 4 + 2 * GN * 4
+                            + 4 * H * 4 + H * 4 * (cfg.chunk // 64 + 1) / 2),
         "bwd_dt": H * s_a + 5 * H * 4 + H * 4,
     }
     return per_token[kernel] * tok
@@ -128,6 +136,8 @@ def algorithmic_flops(cfg, kernel: str) -> float:
         "chunk_state_bwd": 2 * H * P * N,
         "chunk_bwd_col": 2 * (0.5 * G * Q * N + 0.5 * G * Q * N + H * Q * P + 2 * H * P * N),
         "chunk_bwd_row": 2 * (0.5 * G * Q * N + 0.5 * G * Q * N + 0.5 * H * Q * P + H * P * N),
+        # C.B^T once; dB and dC; yx and dx; B Gamma^T, x Gamma and dy H_c
+        "chunk_bwd_fused": 2 * (1.5 * G * Q * N + H * Q * P + 3 * H * P * N),
         "bwd_dt": 0.0,
     }
     return per_token[kernel] * tok

@@ -16,7 +16,7 @@ BUILD = os.path.join(HERE, "_build")
 LIB_NAME = "libssd_mi355x.so"
 ARCH = "gfx950"
 
-SOURCES = ["ssd_state.hip", "ssd_chunk_fwd.hip", "ssd_chunk_bwd.hip", "ssd_bwd_bf16.hip", "ssd_fwd_bf16.hip", "ssd_state_bf16.hip", "shell.hip", "gemm.cpp", "capi.cpp"]
+SOURCES = ["ssd_state.hip", "ssd_chunk_fwd.hip", "ssd_chunk_bwd.hip", "ssd_bwd_bf16.hip", "ssd_bwd_fused.hip", "ssd_fwd_bf16.hip", "ssd_state_bf16.hip", "shell.hip", "gemm.cpp", "capi.cpp"]
 
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdarg>
+#include <cstdlib>
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
@@ -94,6 +95,12 @@ int check_problem(const ssd_problem* p, ssd::Dims* d) {
 // at least `target` workgroups (never more splits than heads per group).  The
 // bf16 kernels give one workgroup two 64-row blocks of a chunk (paired so that
 // every workgroup has the same work), the general ones one block.
+int choose_nsplit_base(const ssd::Dims& d, int64_t target, int64_t base) {
+  const int hpg = d.hpg();
+  for (int s = 1; s <= hpg; ++s)
+    if (hpg % s == 0 && base * s >= target) return s;
+  return hpg;
+}
 int choose_nsplit(const ssd::Dims& d, int64_t target, bool paired) {
   const int64_t base = static_cast<int64_t>(d.b) * d.nc() * d.G * (paired ? (d.nb() + 1) / 2 : d.nb());
   const int hpg = d.hpg();
@@ -122,8 +129,19 @@ struct BwdPlan {
   size_t states = 0, gamma = 0, hbf = 0, gh = 0, rowM = 0, colE = 0, diagE = 0, Rp = 0, dsoff = 0, dA = 0, dD = 0,
          done = 0, dB = 0, dC = 0, send = 0, total = 0;
   int nsplit = 1;
-  bool bf16 = false;  // bf16 kernels with asynchronous staging (they also need a bf16 copy of the states)
+  bool bf16 = false;   // bf16 kernels with asynchronous staging (they also need a bf16 copy of the states)
+  bool fused = false;  // the bf16 column and row work in one kernel (row sums of M in nb slots)
 };
+
+// The bf16 backward runs the fused column-and-row kernel unless SSD_BF16_BWD=split
+// selects the separate column and row kernels (kept for comparison).
+bool bf16_bwd_fused() {
+  static const bool fused = [] {
+    const char* v = std::getenv("SSD_BF16_BWD");
+    return !(v && std::strcmp(v, "split") == 0);
+  }();
+  return fused;
+}
 
 size_t state_bytes(const ssd::Dims& d) {
   return sizeof(float) * static_cast<size_t>(d.b) * d.nc() * d.H * d.P * d.N;
@@ -153,8 +171,11 @@ FwdPlan plan_fwd(const ssd::Dims& d, bool has_states, bool bf16) {
 
 BwdPlan plan_bwd(const ssd::Dims& d, bool has_states, bool bf16) {
   BwdPlan p;
-  p.nsplit = choose_nsplit(d, kBwdTarget, bf16);
   p.bf16 = bf16;
+  p.fused = bf16 && bf16_bwd_fused();
+  // the fused kernel takes one workgroup per (batch, chunk, group) and head split
+  p.nsplit = p.fused ? choose_nsplit_base(d, kBwdTarget, static_cast<int64_t>(d.b) * d.nc() * d.G)
+                     : choose_nsplit(d, kBwdTarget, bf16);
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t o = off;
@@ -166,7 +187,7 @@ BwdPlan plan_bwd(const ssd::Dims& d, bool has_states, bool bf16) {
   p.gamma = take(state_bytes(d));
   if (bf16) p.hbf = take(state_bytes(d) / 2);
   p.gh = take(sizeof(float) * static_cast<size_t>(d.b) * d.nc() * d.H * ssd::state_npb(d));
-  p.rowM = take(bht);
+  p.rowM = take(p.fused ? bht * d.nb() : bht);
   p.colE = take(bht);
   p.diagE = take(bht);
   p.Rp = take(bht);
@@ -450,6 +471,8 @@ int bwd_impl(const char* who, const ssd_problem* prob, const void* x, const void
   s.done = at<unsigned>(workspace, plan.done);
   s.dB_part = plan.nsplit > 1 ? at<float>(workspace, plan.dB) : nullptr;
   s.dC_part = plan.nsplit > 1 ? at<float>(workspace, plan.dC) : nullptr;
+  s.row_slots = plan.fused ? d.nb() : 0;
+  s.slot_elems = static_cast<int64_t>(d.b) * d.H * d.T;
   void* gamma = at<float>(workspace, plan.gamma);
   void* hbf = plan.bf16 ? at<float>(workspace, plan.hbf) : nullptr;
 
@@ -475,7 +498,11 @@ int bwd_impl(const char* who, const ssd_problem* prob, const void* x, const void
         ssd::launch_chunk_state_bwd(d, act, dyt, dy, C, dt, A_log, d_final_state, states, gamma, d_init_state,
                                     s.gh_part, nullptr, at<float>(workspace, plan.send), st),
         "chunk_state_bwd");
-  if (plan.bf16) {
+  if (plan.fused) {
+    SSD_LAUNCH(ssd::launch_bwd_fused_bf16(d, plan.nsplit, x, B, C, dt, dy, A_log, D, gamma, hbf, dx,
+                                          plan.nsplit > 1 ? s.dB_part : dB, plan.nsplit > 1 ? s.dC_part : dC, s, st),
+               "chunk_bwd_fused");
+  } else if (plan.bf16) {
     SSD_LAUNCH(ssd::launch_bwd_col_bf16(d, plan.nsplit, x, B, C, dt, dy, A_log, D, gamma, dx,
                                         plan.nsplit > 1 ? s.dB_part : dB, s, st),
                "chunk_bwd_col");

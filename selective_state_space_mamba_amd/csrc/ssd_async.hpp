@@ -393,4 +393,35 @@ __device__ __forceinline__ float wave_scan(float v) {
   return dpp_add_rows<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
 }
 
+// s (within-chunk inclusive cumsum of dt A) and dt for t < Q, from the dt bits
+// copied to LDS (one dword per step; lane l reads t = 4l .. 4l+3); every wave
+// computes the whole scan and waves 0..3 each write a quarter.
+__device__ __forceinline__ void scan_store(const uint32_t* dtb_lds, float A, float* s_out, float* dt_out) {
+  const int l = lane_id(), w = wave_id();
+  float d[4], a[4];
+  const uint4 db = *reinterpret_cast<const uint4*>(dtb_lds + 4 * l);
+  const uint32_t dbv[4] = {db.x, db.y, db.z, db.w};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) d[e] = bf16_bits_to_f32(static_cast<uint16_t>(dbv[e]));
+  a[0] = d[0] * A;
+#pragma unroll
+  for (int e = 1; e < 4; ++e) a[e] = a[e - 1] + d[e] * A;
+  const float incl = wave_scan(a[3]);
+  const float ex = incl - a[3];
+  if ((l >> 4) == w) {
+    *reinterpret_cast<float4*>(s_out + 4 * l) = make_float4(ex + a[0], ex + a[1], ex + a[2], ex + a[3]);
+    *reinterpret_cast<float4*>(dt_out + 4 * l) = make_float4(d[0], d[1], d[2], d[3]);
+  }
+}
+
+// Write two MFMA tiles (lane element e at row j = 4q + e, column i = 16 tt + r)
+// into a wave strip as bf16 [i][j] (32 rows i of 16 columns j).
+__device__ __forceinline__ void put_strip(lds_char* strip, const f4 (&v)[2]) {
+  const int l = lane_id(), r = l & 15, q = l >> 4;
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt)
+    *(__attribute__((address_space(3))) u32x2*)(strip + strip_off(16 * tt + r, 8 * q)) =
+        u32x2{pack_bf16(v[tt][0], v[tt][1]), pack_bf16(v[tt][2], v[tt][3])};
+}
+
 }  // namespace ssd

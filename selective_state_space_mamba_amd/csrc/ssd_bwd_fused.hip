@@ -1,0 +1,709 @@
+// Intra-chunk backward of the SSD for bf16 operands in one kernel: the column
+// work (dx, dB, column sums) and the row work (dC, row sums, readout term, dD)
+// of one (batch, chunk, group) read x, dy, B, C, Gamma and H_c once.
+//
+// Formulas: those at the head of ssd_chunk_bwd.hip (derived there from the
+// reverse-time loop of the reference page, burn_dragon_kernel
+// src/sequence/mamba2/backward.rs, ssd_backward_reference).  With s the
+// within-chunk cumsum of dt A, L_ij = exp(s_i - s_j), CB_ij = C_i . B_j and
+// yx_ij = dy_i . x_j, the per-head matrices are G = L CB (dx), W = L yx dt_j
+// (summed over heads: dB = W^T C, dC = W B) and M = W CB (row sums enter the
+// decay gradient); U_i = dy_i H_c gives the readout term and the state part of
+// dC.
+//
+// A workgroup owns one (batch, chunk, group) (or a run of the group's heads)
+// and makes one pass per 64-column block jb of the chunk, in order.  Each pass
+// is the column walk of ssd_bwd_bf16.hip (8 waves in two teams; a step is one
+// head and one 64-row block ib >= jb: yx^T by MFMA, the decay terms, G to
+// wave strips, dx_j += G^T dy on MFMA; per head the state terms with Gamma),
+// and additionally:
+//   * the strictly-lower row sums of M over the pass's 64 columns j, per step
+//     (lanes, then the four waves of a team through LDS), stored to row-sum
+//     slot jb (the dt kernel adds the slots jb <= ib of a row);
+//   * on the diagonal step (ib = jb): the diagonal of yx (dD), and
+//     U = dy_i H_c (MFMA, H_c in bf16 from LDS), the readout exp(s_i) U_i . C_i
+//     and its head sum exp(s_i) U_i (the state part of dC for block jb);
+//   * at the pass end: dC_i += sum_j W_ij B_j (+ the state part on the
+//     diagonal block) for every block ib >= jb, added in the L2 to what
+//     earlier passes of the same workgroup wrote (pass 0 stores; one lane owns
+//     each element in every pass and each pass's writes complete before the
+//     next pass's, so the sum order is fixed): dC of a block is complete after
+//     pass ib, and no other workgroup touches it; then dB_j = sum_i W_ij C_i.
+#include "ssd_async.hpp"
+#include "ssd_common.hpp"
+#include "ssd_launch.hpp"
+
+namespace ssd {
+
+namespace {
+constexpr int FW = 8;               // waves per workgroup
+constexpr int FT = FW * WAVE;       // threads per workgroup
+constexpr int TILE_N = 64 * 256;    // bytes of a 64 x 128 bf16 tile
+constexpr int TILE_P = 64 * 128;    // bytes of a 64 x 64 bf16 tile
+constexpr int STRIP = 32 * 32;      // bytes of a 32 x 16 bf16 strip
+constexpr int KP = PMAX / 32;
+constexpr int KN = NMAX / 32;
+static_assert(NBMAX <= 4, "the pass-end phase holds at most four blocks' W strips");
+
+// A fragment of W (rows i, k = j) from the [i][j] wave strips of one block:
+// rows i = 16 a + (lane % 16), columns j = 32 ks + 8 (lane / 16) .. +7.  Row i
+// lies in the strips of team i / 32, column j in the strip of wave j / 16 of
+// that team.
+__device__ __forceinline__ bf16x8 w_rows_frag(const lds_char* strips, int a, int ks) {
+  const int l = lane_id(), r = l & 15, q = l >> 4;
+  const int team = a >> 1, ri = 16 * (a & 1) + r;
+  const lds_char* strip = strips + (4 * team + 2 * ks + (q >> 1)) * STRIP;
+  return *(const __attribute__((address_space(3))) bf16x8*)(strip + strip_off(ri, 16 * (q & 1)));
+}
+}  // namespace
+
+__global__ __launch_bounds__(FT) void bwd_fused_bf16_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ Bm, const uint16_t* __restrict__ Cm,
+    const uint16_t* __restrict__ dt, const uint16_t* __restrict__ dy, const float* __restrict__ A_log,
+    const float* __restrict__ D, const uint16_t* __restrict__ gamma, const uint16_t* __restrict__ hbf,
+    float* __restrict__ dx, float* __restrict__ dB_out, float* __restrict__ dC_out, BwdScratch s, int T, int H,
+    int P, int N, int G, int Q, int nsplit) {
+  __shared__ __attribute__((aligned(1024))) char sB_[TILE_N];          // B rows j of block jb
+  __shared__ __attribute__((aligned(1024))) char sX_[2 * TILE_P];      // x rows j, two heads; W strip slot
+  __shared__ __attribute__((aligned(1024))) char sDy0_[TILE_P];        // dy rows i, even steps
+  __shared__ __attribute__((aligned(1024))) char sDy1_[TILE_P];        // dy rows i, odd steps; W strip slot
+  __shared__ __attribute__((aligned(1024))) char sGam_[TILE_N];        // Gamma [p][n]; W strip slot
+  __shared__ __attribute__((aligned(1024))) char sH_[TILE_N];          // H_c [p][n] (bf16)
+  __shared__ __attribute__((aligned(1024))) char sG_[FW * STRIP];      // per-wave strips [i][j]; W strip slot
+  __shared__ __attribute__((aligned(1024))) char sCt_[NBMAX * TILE_N];  // C tiles of blocks ib, tile ib at ib * 16 KB
+  __shared__ float sRed[2][BQ][4];  // column sums, diagonal, R', readout: team halves
+  __shared__ float sRm[4][BQ];      // one step's row sums of M per wave of a team; dD wave sums
+  __shared__ float sDiag[BQ];       // the diagonal of E on the pass's diagonal block
+  __shared__ __attribute__((aligned(16))) float sS[QMAX];
+  __shared__ __attribute__((aligned(16))) float sDt[QMAX];
+  __shared__ __attribute__((aligned(16))) uint32_t sDtb[QMAX];  // dt bits of the next head to scan
+  lds_char* const sB = lds_ptr(sB_);
+  lds_char* const sX = lds_ptr(sX_);
+  lds_char* const sDy[2] = {lds_ptr(sDy0_), lds_ptr(sDy1_)};
+  lds_char* const sGam = lds_ptr(sGam_);
+  lds_char* const sH = lds_ptr(sH_);
+  lds_char* const sG = lds_ptr(sG_);
+  lds_char* const sCt = lds_ptr(sCt_);
+
+  const int nc = T / Q, nb = (Q + BQ - 1) / BQ;
+  const int hpg = H / G, hps = hpg / nsplit;
+  int idx = xcd_logical_block(blockIdx.x, gridDim.x);
+  const int sp = idx % nsplit;
+  idx /= nsplit;
+  const int g = idx % G;
+  idx /= G;
+  const int c = idx % nc;
+  const int bi = idx / nc;
+  const int64_t batch = gridDim.x / (static_cast<int64_t>(nsplit) * G * nc);
+
+  const int l = lane_id(), w = wave_id(), r = l & 15, q = l >> 4;
+  const int team = w >> 2, wt = w & 3;
+  const int ti = 32 * team;  // this team's rows inside every 64-row block
+  const RowsAt<8> r8_ = rows_at<8>();
+  const RowsAt<16> r16_ = rows_at<16>();
+  const ColsAt<2> c2_ = cols_at<2>();
+  const ColsAt<8> c8_ = cols_at<8>();
+  const ColsAt<16> c16_ = cols_at<16>();
+  const AccAt<8> a8_ = acc_at<8>();
+  const AccAt<16> a16_ = acc_at<16>();
+  const int64_t row0 = static_cast<int64_t>(bi) * T + static_cast<int64_t>(c) * Q;
+  const int64_t HP = static_cast<int64_t>(H) * P, GN = static_cast<int64_t>(G) * N;
+  const uint32_t HPb = static_cast<uint32_t>(HP) * 2, GNb = static_cast<uint32_t>(GN) * 2;
+  const uint32_t goff = static_cast<uint32_t>(g) * N * 2;
+  const int pch = P >> 3, nch = N >> 3;
+  const i32x4 rx = make_rsrc(x + row0 * HP);
+  const i32x4 rdy = make_rsrc(dy + row0 * HP);
+  const i32x4 rb = make_rsrc(Bm + row0 * GN);
+  const i32x4 rc = make_rsrc(Cm + row0 * GN);
+  const i32x4 rg = make_rsrc(gamma + (static_cast<int64_t>(bi) * nc + c) * HP * N);
+  const i32x4 rh = make_rsrc(hbf + (static_cast<int64_t>(bi) * nc + c) * HP * N);
+  const __amdgpu_buffer_rsrc_t rdx = make_rsrc_ptr(dx + row0 * HP);
+  // the per-head sums of (bi, h = 0, c): [b, H, T]
+  const int64_t sum0 = static_cast<int64_t>(bi) * H * T + static_cast<int64_t>(c) * Q;
+  const int64_t bht = batch * H * T;
+  const __amdgpu_buffer_rsrc_t rcol = make_rsrc_ptr(s.colE + sum0);
+  const __amdgpu_buffer_rsrc_t rdiag = make_rsrc_ptr(s.diagE + sum0);
+  const __amdgpu_buffer_rsrc_t rrp = make_rsrc_ptr(s.Rp + sum0);
+  const __amdgpu_buffer_rsrc_t rdso = make_rsrc_ptr(s.dsoff + sum0);
+  // dB and dC (or this head split's partials) from the chunk's first row and the group's columns
+  float* const dBo = dB_out + static_cast<int64_t>(sp) * batch * T * GN + row0 * GN + static_cast<int64_t>(g) * N;
+  const __amdgpu_buffer_rsrc_t rdc =
+      make_rsrc_ptr(dC_out + static_cast<int64_t>(sp) * batch * T * GN + row0 * GN + static_cast<int64_t>(g) * N);
+
+  // x and dy tiles (64 rows of headdim), Gamma and H_c (headdim rows of
+  // d_state): per-lane offsets computed once, the tile's first row as the
+  // scalar offset
+  TileLanes<64, 8, FW> tl8;
+  TileLanes<64, 16, FW> tlg;
+  tl8.init(HPb, pch);
+  tlg.init(N * 2, nch);
+
+  // odd passes take the heads in reverse order, so that the tiles the
+  // previous pass read last are still in L2
+  auto head_of = [&](int jbp, int hh) { return g * hpg + sp * hps + ((jbp & 1) ? hps - 1 - hh : hh); };
+  // the first tiles of pass jbp (the pass over column block jbp): the first
+  // head's x (slot 0), dy on the diagonal block, H_c and dt; the B rows; the
+  // first head's Gamma.  A pass
+  // issues the next pass's tiles during its last phase, in that order (B once
+  // the phase's last B reads are done, Gamma last: it is first read at the
+  // first head's state step)
+  auto load_first_xdhd = [&](int jbp) {
+    const int h0 = head_of(jbp, 0), jx0 = jbp * BQ, vjx = min(BQ, Q - jx0);
+    tl8.issue(sX, rx, jx0 * HPb + h0 * P * 2, vjx);
+    tl8.issue(sDy[0], rdy, jx0 * HPb + h0 * P * 2, vjx);
+    tlg.issue(sH, rh, h0 * P * N * 2, P);
+    steps_async<FW>(lds_ptr(sDtb), make_rsrc(dt + row0 * H + h0), H * 2, Q);
+  };
+  auto load_first_b = [&](int jbp) {
+    const int jx0 = jbp * BQ;
+    tile_async<64, 16, FW>(sB, rb, jx0 * GNb + goff, GNb, min(BQ, Q - jx0), nch);
+  };
+  auto load_first_gam = [&](int jbp) { tlg.issue(sGam, rg, head_of(jbp, 0) * P * N * 2, P); };
+
+  unsigned written = 0;  // blocks of dC an earlier pass has written
+  // pass 0's first tiles and every block's C tile (later passes read a subset)
+  load_first_xdhd(0);
+  load_first_b(0);
+#pragma unroll
+  for (int u = 0; u < NBMAX; ++u) {
+    if (u < nb) {
+      const int i0 = u * BQ;
+      tile_async<64, 16, FW>(sCt + u * TILE_N, rc, i0 * GNb + goff, GNb, min(BQ, Q - i0), nch);
+    }
+  }
+  load_first_gam(0);
+
+  for (int jb = 0; jb < nb; ++jb) {
+    auto head = [&](int hh) { return head_of(jb, hh); };
+    const int j0 = jb * BQ, vj = min(BQ, Q - j0);
+    const int nib = nb - jb;
+    auto load_dt_abs = [&](int h) { steps_async<FW>(lds_ptr(sDtb), make_rsrc(dt + row0 * H + h), H * 2, Q); };
+    auto load_x = [&](int hh) { tl8.issue(sX + (hh & 1) * TILE_P, rx, j0 * HPb + head(hh) * P * 2, vj); };
+    auto load_dy = [&](int hh, int u, lds_char* dst) {
+      const int i0 = (jb + u) * BQ;
+      tl8.issue(dst, rdy, i0 * HPb + head(hh) * P * 2, min(BQ, Q - i0));
+    };
+    auto load_gam = [&](int hh) { tlg.issue(sGam, rg, head(hh) * P * N * 2, P); };
+    auto load_h = [&](int hh) { tlg.issue(sH, rh, head(hh) * P * N * 2, P); };
+    const __amdgpu_buffer_rsrc_t rrm = make_rsrc_ptr(s.rowM + static_cast<int64_t>(jb) * bht + sum0);
+
+    // ---- the pass's first tiles (issued before the loop or during the
+    // previous pass's last phase): all but the first head's Gamma must be in
+    // LDS; then C.B^T for every block ib >= jb
+    if (jb == 0)
+      wait_vm<0>();
+    else
+      wait_vm<2>();
+    lds_barrier();
+    f4 cbk[NBMAX][2];  // C.B^T: rows j of this wave, columns i = (jb + u) * 64 + ti + 16 tt + r
+#pragma unroll
+    for (int u = 0; u < NBMAX; ++u) {
+      zero(cbk[u]);
+      if (u < nib) {
+        bf16x8 bfr[KN];  // this wave's B rows j
+        {
+          const RowsAt<16> ar16 = opaque(r16_);
+#pragma unroll
+          for (int ks = 0; ks < KN; ++ks) bfr[ks] = frag_rows(sB, 16 * wt, 4 * ks, ar16);
+        }
+        const lds_char* ct = sCt + (jb + u) * TILE_N;
+        const RowsAt<16> ar16 = opaque(r16_);
+        bf16x8 fb[KN][2];
+#pragma unroll
+        for (int ks = 0; ks < KN; ++ks)
+#pragma unroll
+          for (int tt = 0; tt < 2; ++tt) fb[ks][tt] = frag_rows(ct, ti + 16 * tt, 4 * ks, ar16);
+        sched_ds_reads<2 * KN>();
+#pragma unroll
+        for (int ks = 0; ks < KN; ++ks)
+#pragma unroll
+          for (int tt = 0; tt < 2; ++tt) cbk[u][tt] = mfma(bfr[ks], fb[ks][tt], cbk[u][tt]);
+        sched_mfmas<2 * KN>();
+      }
+    }
+    scan_store(sDtb, -__expf(A_log[head(0)]), sS, sDt);
+    __syncthreads();
+
+    f4 ws[NBMAX][2];  // sum over heads of L yx dt: rows j, columns i as in cbk
+    f4 dbs[4];        // state part of dB: rows j, columns n = 16 (4 team + k) + r
+    f4 ua[4];         // sum over heads of exp(s_i) U_i on the diagonal block: rows i = j0 + 16 wt + 4q + e,
+                      // columns n = 16 (4 team + k) + r
+#pragma unroll
+    for (int u = 0; u < NBMAX; ++u) zero(ws[u]);
+    zero(dbs);
+    zero(ua);
+
+    for (int hh = 0; hh < hps; ++hh) {
+      const int h = head(hh), hb = hh & 1;
+      const lds_char* xt = sX + hb * TILE_P;
+      float sj[4], dtj[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int jq = j0 + 16 * wt + 4 * q + e;
+        sj[e] = sS[min(jq, Q - 1)];
+        dtj[e] = (jq < Q) ? sDt[jq] : 0.f;
+      }
+      f4 dxa[2];  // sum over rows i of G_ij dy_i: rows j, columns p = 16 (2 team + k) + r
+      zero(dxa);
+      float Dh = 0.f, An = 0.f;
+      float cfc[4], sprev = 0.f;
+      float csum[4] = {0.f, 0.f, 0.f, 0.f};
+      float ddv = 0.f;  // the diagonal of yx (dD)
+      u32x2 dsk[2];     // dy_j at columns p = ti + 16 k + r, accumulator layout
+      bf16x8 xf[KP];    // this wave's x rows j
+      {
+        const RowsAt<8> ar8 = opaque(r8_);
+#pragma unroll
+        for (int ks = 0; ks < KP; ++ks) xf[ks] = frag_rows(xt, 16 * wt, 4 * ks, ar8);
+      }
+
+#pragma unroll
+      for (int u = 0; u < NBMAX; ++u) {
+        if (u < nib) {
+          const RowsAt<8> ar8 = opaque(r8_);
+          const ColsAt<2> ac2 = opaque(c2_);
+          const ColsAt<8> ac8 = opaque(c8_);
+          const int i0 = (jb + u) * BQ;
+          const lds_char* dyt = sDy[u & 1];
+          // issue order of the step's copies: the next block's dy; at step 1
+          // the next head's H_c (this head's was read in step 0); at step 0 the
+          // next head's dt, last, so that the step's end need not wait for it
+          if (u + 1 < nib) load_dy(hh, u + 1, sDy[(u + 1) & 1]);
+          if (u == 1 && hh + 1 < hps) load_h(hh + 1);
+          if (u == 0) {
+            Dh = D[h];
+            if (hh + 1 < hps) {
+              An = A_log[head(hh + 1)];
+              load_dt_abs(head(hh + 1));
+            }
+          }
+
+          f4 yx[2];
+          zero(yx);
+          f4 cbt[2];
+          float sv[2];
+          float sref;
+          const int ib0 = opaque_index(i0 + ti + r);
+          {
+            bf16x8 fb[KP][2];
+#pragma unroll
+            for (int ks = 0; ks < KP; ++ks)
+#pragma unroll
+              for (int tt = 0; tt < 2; ++tt) fb[ks][tt] = frag_rows(dyt, ti + 16 * tt, 4 * ks, ar8);
+            cbt[0] = cbk[u][0];
+            cbt[1] = cbk[u][1];
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) sv[tt] = sS[min(ib0 + 16 * tt, Q - 1)];
+            sref = sS[i0];
+            sched_ds_reads<2 * KP + 3>();
+#pragma unroll
+            for (int ks = 0; ks < KP; ++ks)
+#pragma unroll
+              for (int tt = 0; tt < 2; ++tt) yx[tt] = mfma(xf[ks], fb[ks][tt], yx[tt]);
+            sched_mfmas<2 * KP>();
+          }
+          f4 gv[2];
+          float rmv[2] = {0.f, 0.f};  // row sums of M (rows i = i0 + ti + 16 tt + r) over this lane's 4 columns
+          if (u == 0) {
+            const int jq0 = opaque_index(j0 + 16 * wt + 4 * q);
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) {
+              const int iq = ib0 + 16 * tt;
+              const float si = sv[tt];
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const int jq = jq0 + e;
+                const float ex = __expf(si - sj[e]);
+                const float L = (iq < Q && iq >= jq) ? ex : 0.f;
+                const float G1 = L * cbt[tt][e];
+                const float E = G1 * yx[tt][e];
+                csum[e] += E;
+                if (iq == jq) {
+                  sDiag[jq - j0] = E;  // one lane of the workgroup holds each diagonal element
+                  ddv += yx[tt][e];
+                }
+                const float Wv = L * dtj[e] * yx[tt][e];
+                ws[u][tt][e] += Wv;
+                if (jq < iq) rmv[tt] += Wv * cbt[tt][e];
+                gv[tt][e] = G1;
+              }
+            }
+            const AccAt<8> aa8 = opaque(a8_);
+#pragma unroll
+            for (int k = 0; k < 2; ++k) dsk[k] = block_acc(dyt, 16 * wt, ti + 16 * k, aa8);
+          } else {
+            float cf[4], cfd[4];
+            if (u == 1) {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) cfc[e] = __expf(sref - sj[e]);
+            } else {
+              const float adv = __expf(sref - sprev);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) cfc[e] *= adv;
+            }
+            sprev = sref;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              cf[e] = cfc[e];
+              cfd[e] = cf[e] * dtj[e];
+            }
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) {
+              const int iq = ib0 + 16 * tt;
+              const float rx_ = __expf(sv[tt] - sref);
+              const float rf = (iq < Q) ? rx_ : 0.f;
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const float G1 = rf * cf[e] * cbt[tt][e];
+                const float E = G1 * yx[tt][e];
+                csum[e] += E;
+                const float Wv = rf * cfd[e] * yx[tt][e];
+                ws[u][tt][e] += Wv;
+                rmv[tt] += Wv * cbt[tt][e];
+                gv[tt][e] = G1;
+              }
+            }
+          }
+          put_strip(sG + w * STRIP, gv);
+          // this wave's row sums over its 16 columns (the 4 lane groups), to
+          // LDS for the team sum
+#pragma unroll
+          for (int tt = 0; tt < 2; ++tt) rmv[tt] = sum_q(rmv[tt]);
+          if (q == 0) {
+            sRm[wt][ti + r] = rmv[0];
+            sRm[wt][ti + 16 + r] = rmv[1];
+          }
+          if (u == 0) {
+            // U = dy_i H_c on the diagonal block: rows i = j0 + 16 wt + 4q + e,
+            // columns n = 16 (4 team + k) + r; its readout exp(s_i) U_i . C_i
+            // (team halves to LDS) and its head sum exp(s_i) U_i
+            f4 uu[4];
+            zero(uu);
+            const RowsAt<8> ar8u = opaque(r8_);
+            const ColsAt<16> ac16 = opaque(c16_);
+#pragma unroll
+            for (int ks = 0; ks < KP; ++ks) {
+              const bf16x8 fa = frag_rows(dyt, 16 * wt, 4 * ks, ar8u);
+              bf16x8 fb[4];
+#pragma unroll
+              for (int k = 0; k < 4; ++k) fb[k] = frag_cols(sH, 32 * ks, 16 * (4 * team + k), ac16);
+              sched_ds_reads<9>();
+#pragma unroll
+              for (int k = 0; k < 4; ++k) uu[k] = mfma(fa, fb[k], uu[k]);
+              sched_mfmas<4>();
+            }
+            const AccAt<16> aa16 = opaque(a16_);
+            u32x2 ca[4];  // C_i at columns n = 16 (4 team + k) + r, accumulator layout
+            const lds_char* ctd = sCt + jb * TILE_N;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) ca[k] = block_acc(ctd, 16 * wt, 16 * (4 * team + k), aa16);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int il = 16 * wt + 4 * q + e;
+              const float xe = __expf(sS[min(j0 + il, Q - 1)]);
+              const float exi = (j0 + il < Q) ? xe : 0.f;
+              float part = 0.f;
+#pragma unroll
+              for (int k = 0; k < 4; ++k) {
+                part += uu[k][e] * acc_elem(ca[k], e);
+                ua[k][e] += exi * uu[k][e];
+              }
+              part = row_sum16(part);
+              if (r == 15) sRed[team][il][3] = exi * part;
+            }
+          }
+          lds_barrier();
+          // dx_j += sum_i G_ij dy_i over the block's 64 rows i: k-step ks reads
+          // the strip of team ks
+          {
+            bf16x8 ga[2], gb[2][2];
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+              ga[ks] = frag_cols(sG + (4 * ks + wt) * STRIP, 0, 0, ac2);
+#pragma unroll
+              for (int k = 0; k < 2; ++k) gb[ks][k] = frag_cols(dyt, 32 * ks, 16 * (2 * team + k), ac8);
+            }
+            sched_ds_reads<12>();
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+              for (int k = 0; k < 2; ++k) dxa[k] = mfma(ga[ks], gb[ks][k], dxa[k]);
+            sched_mfmas<4>();
+          }
+          // the step's row sums of M: wave 0 adds the four waves of each team
+          // and stores them (row sum slot jb, rows i0 + l)
+          if (w == 0) {
+            const float rs = sRm[0][l] + sRm[1][l] + sRm[2][l] + sRm[3][l];
+            store_f32(rrm, rs, i0 + l < Q ? static_cast<uint32_t>(i0 + l) * 4 : OOB_OFFSET,
+                      static_cast<uint32_t>(h) * T * 4);
+          }
+          // wave 0's row-sum store is its youngest memory operation; every
+          // wave leaves the next head's dt copy in flight at step 0
+          if (u == 0 && hh + 1 < hps) {
+            if (w == 0)
+              wait_vm<2>();
+            else
+              wait_vm<1>();
+          } else {
+            if (w == 0)
+              wait_vm<1>();
+            else
+              wait_vm<0>();
+          }
+          lds_barrier();
+        }
+      }
+
+      // ---- state terms of head hh; the next head's x and dy tiles start
+      // loading (after its H_c when there was no step 1 to issue that), its
+      // Gamma once this head's is read
+      const RowsAt<16> ar16 = opaque(r16_);
+      const ColsAt<16> ac16 = opaque(c16_);
+      const bool h_here = nib == 1 && hh + 1 < hps;
+      if (h_here) load_h(hh + 1);
+      if (hh + 1 < hps) {
+        load_x(hh + 1);
+        load_dy(hh + 1, 0, sDy[0]);
+      }
+      f4 bg[2];  // B_j Gamma^T: rows j, columns p = 16 (2 team + k) + r
+      zero(bg);
+#pragma unroll
+      for (int kh = 0; kh < KN; kh += 2) {
+        bf16x8 fb[2][2], bfr[2];  // Gamma rows p; this wave's B rows j (from the pass's B tile)
+#pragma unroll
+        for (int d2 = 0; d2 < 2; ++d2) {
+          bfr[d2] = frag_rows(sB, 16 * wt, 4 * (kh + d2), ar16);
+#pragma unroll
+          for (int k = 0; k < 2; ++k) fb[d2][k] = frag_rows(sGam, 16 * (2 * team + k), 4 * (kh + d2), ar16);
+        }
+        sched_ds_reads<6>();
+#pragma unroll
+        for (int d2 = 0; d2 < 2; ++d2)
+#pragma unroll
+          for (int k = 0; k < 2; ++k) bg[k] = mfma(bfr[d2], fb[d2][k], bg[k]);
+        sched_mfmas<4>();
+      }
+      f4 v[4];  // x_j Gamma for this team's d_state columns
+      zero(v);
+#pragma unroll
+      for (int ks = 0; ks < KP; ++ks) {
+        bf16x8 fb[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) fb[k] = frag_cols(sGam, 32 * ks, 16 * (4 * team + k), ac16);
+        sched_ds_reads<8>();
+#pragma unroll
+        for (int k = 0; k < 4; ++k) v[k] = mfma(xf[ks], fb[k], v[k]);
+        sched_mfmas<4>();
+      }
+      u32x2 xa[2];
+      {
+        const AccAt<8> aa8 = opaque(a8_);
+#pragma unroll
+        for (int k = 0; k < 2; ++k) xa[k] = block_acc(xt, 16 * wt, 16 * (2 * team + k), aa8);
+      }
+      const float s_end = sS[Q - 1];
+      float wj[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int jl = 16 * wt + 4 * q + e;
+        const float wx = __expf(s_end - sj[e]);
+        wj[e] = (j0 + jl < Q) ? wx : 0.f;
+        float part = 0.f;
+#pragma unroll
+        for (int k = 0; k < 2; ++k) part += bg[k][e] * acc_elem(xa[k], e);
+        part = row_sum16(part);
+        const float cs = row_sum16(csum[e]);
+        if (r == 15) {
+          sRed[team][jl][0] = cs;
+          sRed[team][jl][2] = wj[e] * part;
+        }
+      }
+      {
+        const float dd = wave_sum(ddv);
+        if (l == 0) sRm[0][w] = dd;
+      }
+      // the next head's dt copy must be in LDS; its H_c (when issued here), x
+      // and dy copies may be in flight
+      if (h_here)
+        wait_vm<4>();
+      else if (hh + 1 < hps)
+        wait_vm<2>();
+      lds_barrier();
+      if (hh + 1 < hps) load_gam(hh + 1);  // this head's Gamma is no longer read
+      float dxv[2][4];
+#pragma unroll
+      for (int k = 0; k < 2; ++k)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dxv[k][e] = dtj[e] * (dxa[k][e] + wj[e] * bg[k][e]) + Dh * acc_elem(dsk[k], e);
+      const int jc = 16 * wt + r;
+      const float ce = sRed[0][jc][0] + sRed[1][jc][0];
+      const float de = sDiag[jc];
+      const float re = sRed[0][jc][2] + sRed[1][jc][2];
+      const float so = sRed[0][jc][3] + sRed[1][jc][3];
+      float dd_tot = 0.f;
+      if (w == 0 && l == 0) {
+#pragma unroll
+        for (int k = 0; k < FW; ++k) dd_tot += sRm[0][k];
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float f = dtj[e] * wj[e];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) dbs[k][e] += f * v[k][e];
+      }
+      // the next head's H_c, x and dy tiles (all but Gamma's 2 copies) must be
+      // in LDS at the barrier; the stores below are issued after the wait and
+      // complete during the next step
+      if (hh + 1 < hps) wait_vm<2>();
+      {
+        const uint32_t vdx = (static_cast<uint32_t>(j0 + 16 * wt + 4 * q) * HP + 32 * team + r) * 4;
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const bool ok = j0 + 16 * wt + 4 * q + e < Q && 32 * team + 16 * k + r < P;
+            store_f32(rdx, dxv[k][e], ok ? vdx + 64 * k : OOB_OFFSET, static_cast<uint32_t>(e * HP + h * P) * 4);
+          }
+        }
+        if (team == 0) {
+          const uint32_t vo = (q == 0 && j0 + jc < Q) ? static_cast<uint32_t>(j0 + jc) * 4 : OOB_OFFSET;
+          const uint32_t so4 = static_cast<uint32_t>(h) * T * 4;
+          store_f32(rcol, ce, vo, so4);
+          store_f32(rdiag, de, vo, so4);
+          store_f32(rrp, re, vo, so4);
+          store_f32(rdso, so, vo, so4);
+        }
+        if (w == 0 && l == 0) s.dD_part[((static_cast<int64_t>(bi) * nc + c) * nb + jb) * H + h] = dd_tot;
+      }
+      if (hh + 1 < hps) scan_store(sDtb, -__expf(An), sS, sDt);
+      lds_barrier();
+    }
+
+    // ---- pass end.  The W strips of blocks u = 0..3 go to four free 8 KB
+    // slots; dC_i += sum_j W_ij B_j (k = j along the strips, against the B
+    // tile) plus the state part on the diagonal block, for every block
+    // ib >= jb; then dB_j = sum_i W_ij C_i + state terms over all rows i (k = i
+    // down the strips, against the C tiles).  The next pass's first tiles load
+    // meanwhile.
+    // dC as earlier passes of this workgroup wrote it (the same lane, the same
+    // layout), for the blocks an earlier pass wrote: every load of the pass is
+    // issued first
+    float dco[NBMAX][4][4];
+#pragma unroll
+    for (int u = 0; u < NBMAX; ++u) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int n = 16 * (4 * team + k) + r;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          dco[u][k][e] = 0.f;
+          if (u < nib && ((written >> (jb + u)) & 1)) {
+            const int iq = (jb + u) * BQ + 16 * wt + 4 * q + e;
+            const uint32_t off =
+                (iq < Q && n < N) ? (static_cast<uint32_t>(iq) * static_cast<uint32_t>(GN) + n) * 4 : OOB_OFFSET;
+            dco[u][k][e] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rdc, off, 0, 0));
+          }
+        }
+      }
+    }
+    // x slot 0, dy buffer 0, H_c and the dt bits are free (the last head's
+    // state step is done; the strips below use the other slots)
+    if (jb + 1 < nb) load_first_xdhd(jb + 1);
+    lds_char* const wset[4] = {sG, sX + TILE_P, sDy[1], sGam};
+#pragma unroll
+    for (int u = 0; u < NBMAX; ++u)
+      if (u < nib) put_strip(wset[u] + w * STRIP, ws[u]);
+    lds_barrier();
+#pragma unroll
+    for (int u = 0; u < NBMAX; ++u) {
+      if (u < nib) {
+        // dC of block ib = jb + u: rows i = 16 wt + 4q + e, columns n = 16 (4 team + k) + r
+        const ColsAt<16> ac16 = opaque(c16_);
+        f4 pc[4];
+        if (u == 0) {
+#pragma unroll
+          for (int k = 0; k < 4; ++k) pc[k] = ua[k];
+        } else {
+          zero(pc);
+        }
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          bf16x8 fa, fb[4];
+          fa = w_rows_frag(wset[u], wt, ks);
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk) fb[kk] = frag_cols(sB, 32 * ks, 16 * (4 * team + kk), ac16);
+          sched_ds_reads<5>();
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk) pc[kk] = mfma(fa, fb[kk], pc[kk]);
+          sched_mfmas<4>();
+        }
+        const int i0 = (jb + u) * BQ;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int n = 16 * (4 * team + k) + r;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int iq = i0 + 16 * wt + 4 * q + e;
+            const uint32_t off =
+                (iq < Q && n < N) ? (static_cast<uint32_t>(iq) * static_cast<uint32_t>(GN) + n) * 4 : OOB_OFFSET;
+            store_f32(rdc, dco[u][k][e] + pc[k][e], off, 0);
+          }
+        }
+      }
+    }
+    lds_barrier();  // the B tile is no longer read
+    if (jb + 1 < nb) load_first_b(jb + 1);
+    f4 dbp[4];
+    zero(dbp);
+#pragma unroll
+    for (int u = 0; u < NBMAX; ++u) {
+      if (u < nib) {
+        const lds_char* ct = sCt + (jb + u) * TILE_N;
+        const ColsAt<2> ac2 = opaque(c2_);
+        const ColsAt<16> ac16 = opaque(c16_);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          bf16x8 fa, fb[4];
+          fa = frag_cols(wset[u] + (4 * ks + wt) * STRIP, 0, 0, ac2);
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk) fb[kk] = frag_cols(ct, 32 * ks, 16 * (4 * team + kk), ac16);
+          sched_ds_reads<10>();
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk) dbp[kk] = mfma(fa, fb[kk], dbp[kk]);
+          sched_mfmas<4>();
+        }
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int n = 16 * (4 * team + k) + r;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int jq = j0 + 16 * wt + 4 * q + e;
+        if (jq < Q && n < N) dBo[static_cast<int64_t>(jq) * GN + n] = dbp[k][e] + dbs[k][e];
+      }
+    }
+    written |= ((1u << nb) - 1) & ~((1u << jb) - 1);  // blocks jb .. nb - 1
+    if (jb + 1 < nb) {
+      lds_barrier();  // the strips in the Gamma slot are no longer read
+      load_first_gam(jb + 1);
+    }
+  }  // pass
+  // the dt kernel that follows counts its finished workgroups from 0
+  if (blockIdx.x == 0 && threadIdx.x == 0) __hip_atomic_store(s.done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+hipError_t launch_bwd_fused_bf16(const Dims& d, int nsplit, const void* x, const void* B, const void* C,
+                                 const void* dt, const void* dy, const float* A_log, const float* D,
+                                 const void* gamma, const void* hbf, float* dx, float* dB_out, float* dC_out,
+                                 const BwdScratch& s, hipStream_t st) {
+  const int64_t nblk = static_cast<int64_t>(d.b) * d.nc() * d.G * nsplit;
+  hipLaunchKernelGGL(bwd_fused_bf16_kernel, dim3(static_cast<unsigned>(nblk)), dim3(FT), 0, st,
+                     static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(B), static_cast<const uint16_t*>(C),
+                     static_cast<const uint16_t*>(dt), static_cast<const uint16_t*>(dy), A_log, D,
+                     static_cast<const uint16_t*>(gamma), static_cast<const uint16_t*>(hbf), dx, dB_out, dC_out, s, d.T,
+                     d.H, d.P, d.N, d.G, d.Q, nsplit);
+  return hipGetLastError();
+}
+
+}  // namespace ssd

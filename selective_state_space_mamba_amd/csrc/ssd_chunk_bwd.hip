@@ -755,7 +755,12 @@ __global__ __launch_bounds__(NH* WAVE) void bwd_dt_kernel(const TI* __restrict__
     if (k < Q && w < nh) {
       cE[e] = s.colE[o0 + k];
       rP[e] = s.Rp[o0 + k];
-      rM[e] = s.rowM[o0 + k];
+      if (s.row_slots == 0) {
+        rM[e] = s.rowM[o0 + k];
+      } else {
+        // the slots of the 64-column blocks at or before row k's block, in order
+        for (int jb = 0; jb <= (k >> 6) && jb < s.row_slots; ++jb) rM[e] += s.rowM[jb * s.slot_elems + o0 + k];
+      }
       dE[e] = s.diagE[o0 + k];
       dS[e] = s.dsoff[o0 + k];
     }

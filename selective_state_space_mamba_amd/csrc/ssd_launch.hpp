@@ -56,7 +56,8 @@ hipError_t launch_chunk_out_fwd(const Dims& d, DType act, int nsplit, const void
                                 const float* states, void* y, hipStream_t st);
 
 struct BwdScratch {
-  float* rowM;   // [b,H,T] strictly-lower row sums of the decay-gradient matrix
+  float* rowM;   // [b,H,T] strictly-lower row sums of the decay-gradient matrix; with row_slots > 0,
+                 // row_slots such arrays (slot jb: the part from 64-column block jb, rows of blocks >= jb)
   float* colE;   // [b,H,T] column sums (diagonal included) without the dt factor
   float* diagE;  // [b,H,T] diagonal entries
   float* Rp;     // [b,H,T] state-term of the dt gradient without the dt factor
@@ -67,6 +68,8 @@ struct BwdScratch {
   unsigned* done;  // one counter: the dt kernel's finished workgroups (zeroed by the row kernel)
   float* dB_part;  // [nsplit,b,T,G,N] or null when nsplit == 1
   float* dC_part;
+  int row_slots;      // 0: rowM holds the row sums; else the number of slots to add
+  int64_t slot_elems;  // b * H * T: elements of one row-sum slot
 };
 
 hipError_t launch_chunk_bwd_col(const Dims& d, DType act, DType dyt, int nsplit, const void* x,
@@ -89,6 +92,16 @@ hipError_t launch_bwd_col_bf16(const Dims& d, int nsplit, const void* x, const v
                                const void* dt, const void* dy, const float* A_log, const float* D,
                                const void* gamma, float* dx, float* dB_out, const BwdScratch& s,
                                hipStream_t st);
+
+// The column and row work of the bf16 kernels in one kernel (ssd_bwd_fused.hip):
+// one workgroup per (batch, chunk, group, head split); dx, dB and dC (or the
+// head-split partials), the per-column sums, the readout term, dD partials,
+// and the row sums of M in s.row_slots = nb slots.  Reads the bf16 copy of the
+// states (hbf) and Gamma; zeroes s.done for the dt kernel.
+hipError_t launch_bwd_fused_bf16(const Dims& d, int nsplit, const void* x, const void* B, const void* C,
+                                 const void* dt, const void* dy, const float* A_log, const float* D,
+                                 const void* gamma, const void* hbf, float* dx, float* dB_out, float* dC_out,
+                                 const BwdScratch& s, hipStream_t st);
 
 // dt gradient per token, and dA_log and dD (fixed-order sums of the per-chunk
 // partials, taken by the launch's last workgroup).  Needs s.done zeroed by an

@@ -201,9 +201,9 @@ def test_launch_grid_limit(lib):
 
 
 def _bf16_state_copy_bytes(lib, **kw):
-    # the bf16 kernel family keeps a bf16 copy of the chunk states in the
-    # backward workspace; the general kernels (here: bf16 activations with an
-    # f32 dy) do not, with everything else the same
+    # the bf16 kernel family keeps a bf16 copy of the chunk states (and per-block
+    # row-sum slots) in the backward workspace; the general kernels (here: bf16
+    # activations with an f32 dy) do not, with everything else the same
     a = lib.ssd_workspace_bytes(ctypes.byref(prob(act_dtype=1, dy_dtype=1, **kw)), 1, 1)
     b = lib.ssd_workspace_bytes(ctypes.byref(prob(act_dtype=1, dy_dtype=0, **kw)), 1, 1)
     return a - b
@@ -214,7 +214,7 @@ def test_bf16_family_offset_bounds(lib):
     states = lambda T: 4 * (T // 256) * 64 * 64 * 128
     # a 262144-step row holds 2 GiB of bf16 x: the chunk-state kernel's
     # descriptors start at each chunk, so the bf16 family still applies
-    assert _bf16_state_copy_bytes(lib, seqlen=262144, **big) == states(262144) // 2
+    assert _bf16_state_copy_bytes(lib, seqlen=262144, **big) >= states(262144) // 2
     # 2^23 steps of 64 heads: a head's row of the [b, H, T] per-head sums
     # spans 2^31 bytes, past a descriptor's 32-bit range -> general kernels
     assert _bf16_state_copy_bytes(lib, seqlen=1 << 23, **big) == 0

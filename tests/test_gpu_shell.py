@@ -169,27 +169,48 @@ def test_autograd_block_core(dtype):
     assert all(v <= TOL[dtype] for v in errs.values()), errs
 
 
-def test_autograd_full_block_with_projections():
-    """mamba2_block (in_proj parts, block slice, out_proj; bf16) against the
-    oracle chain with the projections as f64 matrix products."""
-    from ssd_inputs import SSDConfig
-    cfg = SSDConfig("blk_full", 2, 256, 4, 64, 64, 1, 128, "bf16", init_state=True, shell=True, seed=93)
+def _full_block_problem(size):
+    """Inputs of one mamba2_block call: the small shape (2 x 256 steps, 4
+    heads, d_model 128, carried initial state and a final-state gradient), or
+    the block training workload's shape at one batch row (2048 steps, 48 heads
+    of 64, d_state 128, d_model 1536, no initial state), with its weights and
+    output gradient drawn as the benchmark draws them."""
+    from ssd_inputs import CONFIGS, SSDConfig
+    if size == "small":
+        cfg = SSDConfig("blk_full", 2, 256, 4, 64, 64, 1, 128, "bf16", init_state=True, shell=True, seed=93)
+        d = make_inputs(cfg)
+        b, T, H, P, N = cfg.batch, cfg.seqlen, cfg.nheads, cfg.headdim, cfg.dstate
+        di, cd, dm = cfg.d_inner, cfg.conv_dim, 128
+        rng = np.random.default_rng(94)
+        u = Stored(rng.standard_normal((b, T, dm)).astype(np.float32), "bf16")
+        Wz, Wx, Wd = (Stored((rng.standard_normal((o, dm)) / np.sqrt(dm)).astype(np.float32), "bf16")
+                      for o in (di, cd, H))
+        Wo = Stored((rng.standard_normal((dm, di)) / np.sqrt(di)).astype(np.float32), "bf16")
+        go = Stored(rng.standard_normal((b, T, dm)).astype(np.float32), "bf16")
+        dfin = rng.standard_normal((b, H, P, N)).astype(np.float32)
+        return cfg, d, dm, (u, Wz, Wx, Wd, Wo, go), d["h0"], dfin
+    cfg = CONFIGS["block_train"].with_(batch=1)
     d = make_inputs(cfg)
+    return cfg, d, cfg.d_model, tuple(d[k] for k in ("u", "W_z", "W_xbc", "W_dt", "W_out", "go")), None, None
+
+
+@pytest.mark.parametrize("size", ["small", "bench"])
+def test_autograd_full_block_with_projections(size):
+    """mamba2_block (in_proj parts, block slice, out_proj; bf16) against the
+    oracle chain with the projections as f64 matrix products; `bench` is the
+    block training workload's shape (d_model 1536, 48 heads) at one batch row."""
+    cfg, d, dm, (u, Wz, Wx, Wd, Wo, go), h0_np, dfin = _full_block_problem(size)
     b, T, H, P, N, G, Q, di = cfg.batch, cfg.seqlen, cfg.nheads, cfg.headdim, cfg.dstate, cfg.ngroups, cfg.chunk, cfg.d_inner
-    dm, cd = 128, cfg.conv_dim
-    rng = np.random.default_rng(94)
-    u = Stored(rng.standard_normal((b, T, dm)).astype(np.float32), "bf16")
-    Wz, Wx, Wd = (Stored((rng.standard_normal((o, dm)) / np.sqrt(dm)).astype(np.float32), "bf16") for o in (di, cd, H))
-    Wo = Stored((rng.standard_normal((dm, di)) / np.sqrt(di)).astype(np.float32), "bf16")
-    go = Stored(rng.standard_normal((b, T, dm)).astype(np.float32), "bf16")
-    dfin = rng.standard_normal((b, H, P, N)).astype(np.float32)
+    print(f"[parity full block {size}] b={b} T={T} H={H} d_model={dm}", flush=True)
 
     tu, tWz, tWx, tWd, tWo = (dev(a).requires_grad_() for a in (u, Wz, Wx, Wd, Wo))
     cw, cb, bias, A_log, D, nw = (dev(d[k]).requires_grad_() for k in ("conv_w", "conv_b", "dt_bias", "A_log", "D", "norm_w"))
-    h0 = dev(d["h0"]).requires_grad_()
+    h0 = dev(h0_np).requires_grad_() if h0_np is not None else None
     o, fin = ssd.mamba2_block(tu, tWz, tWx, tWd, cw, cb, bias, A_log, D, nw, tWo, ngroups=G, dstate=N, headdim=P,
                               chunk=Q, eps=cfg.norm_eps, init_state=h0)
-    loss = (o.float() * dev(go).float()).sum() + (fin * dev(dfin)).sum()
+    loss = (o.float() * dev(go).float()).sum()
+    if dfin is not None:
+        loss = loss + (fin * dev(dfin)).sum()
     loss.backward()
     torch.cuda.synchronize()
 
@@ -201,14 +222,14 @@ def test_autograd_full_block_with_projections():
     rC = act[..., di + G * N:].reshape(b, T, G, N)
     r_dt = oracle.dt_softplus_fwd(raw, d["dt_bias"])
     sargs = (rx, r_dt, d["A_log"], rB, rC, d["D"])
-    rf = oracle.ssd_fwd(*sargs, d["h0"])
+    rf = oracle.ssd_fwd(*sargs, h0_np)
     ry = rf["y"].reshape(b, T, di)
     rout, rinv = oracle.rmsnorm_fwd(ry, z, d["norm_w"], cfg.norm_eps)
     ro = rout @ WO.T
     gout = GO @ WO
     r_dWo = GO.reshape(-1, dm).T @ rout.reshape(-1, di)
     rgy, rgz, rgw = oracle.rmsnorm_bwd(ry, z, d["norm_w"], rinv, gout)
-    rg = oracle.ssd_bwd(*sargs, rgy.reshape(b, T, H, P), d["h0"], dfinal=dfin)
+    rg = oracle.ssd_bwd(*sargs, rgy.reshape(b, T, H, P), h0_np, dfinal=dfin)
     gact = np.concatenate([rg["dx"].reshape(b, T, di), rg["dB"].reshape(b, T, -1), rg["dC"].reshape(b, T, -1)], -1)
     rdxbc, rdcw, rdcb = oracle.conv_bwd(xbc, d["conv_w"], d["conv_b"], gact)
     r_raw, r_bias = oracle.dt_softplus_bwd(raw, d["dt_bias"], rg["ddt"])
@@ -220,9 +241,10 @@ def test_autograd_full_block_with_projections():
             "dW_dt": relerr(host(tWd.grad), flat(r_raw).T @ flat(U)), "dW_out": relerr(host(tWo.grad), r_dWo),
             "dconv_w": relerr(host(cw.grad), rdcw), "dconv_b": relerr(host(cb.grad), rdcb),
             "d_dt_bias": relerr(host(bias.grad), r_bias), "dA_log": relerr(host(A_log.grad), rg["dA_log"]),
-            "dD": relerr(host(D.grad), rg["dD"]), "dnorm_w": relerr(host(nw.grad), rgw),
-            "dh0": relerr(host(h0.grad), rg["dh0"])}
-    print("[parity full block]", {k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
+            "dD": relerr(host(D.grad), rg["dD"]), "dnorm_w": relerr(host(nw.grad), rgw)}
+    if h0 is not None:
+        errs["dh0"] = relerr(host(h0.grad), rg["dh0"])
+    print(f"[parity full block {size}]", {k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
     assert all(v <= TOL["bf16"] for v in errs.values()), errs
 
 
