@@ -236,13 +236,18 @@ __global__ __launch_bounds__(FT) void bwd_fused_bf16_kernel(
     for (int hh = 0; hh < hps; ++hh) {
       const int h = head(hh), hb = hh & 1;
       const lds_char* xt = sX + hb * TILE_P;
-      float sj[4], dtj[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int jq = j0 + 16 * wt + 4 * q + e;
-        sj[e] = sS[min(jq, Q - 1)];
-        dtj[e] = (jq < Q) ? sDt[jq] : 0.f;
-      }
+      // s_j and dt_j of this lane's rows j = jq0 .. jq0 + 3, read where used
+      // (entries past Q hold the chunk's last cumsum value and dt = 0; every
+      // use at rows j >= Q is masked or multiplied by a zero operand)
+      const int jq0 = j0 + 16 * wt + 4 * q;
+      auto s_rows = [&](float (&v)[4]) {
+        const float4 t = *reinterpret_cast<const float4*>(sS + opaque_index(jq0));
+        v[0] = t.x, v[1] = t.y, v[2] = t.z, v[3] = t.w;
+      };
+      auto dt_rows = [&](float (&v)[4]) {
+        const float4 t = *reinterpret_cast<const float4*>(sDt + opaque_index(jq0));
+        v[0] = t.x, v[1] = t.y, v[2] = t.z, v[3] = t.w;
+      };
       f4 dxa[2];  // sum over rows i of G_ij dy_i: rows j, columns p = 16 (2 team + k) + r
       zero(dxa);
       float Dh = 0.f, An = 0.f;
@@ -250,12 +255,6 @@ __global__ __launch_bounds__(FT) void bwd_fused_bf16_kernel(
       float csum[4] = {0.f, 0.f, 0.f, 0.f};
       float ddv = 0.f;  // the diagonal of yx (dD)
       u32x2 dsk[2];     // dy_j at columns p = ti + 16 k + r, accumulator layout
-      bf16x8 xf[KP];    // this wave's x rows j
-      {
-        const RowsAt<8> ar8 = opaque(r8_);
-#pragma unroll
-        for (int ks = 0; ks < KP; ++ks) xf[ks] = frag_rows(xt, 16 * wt, 4 * ks, ar8);
-      }
 
 #pragma unroll
       for (int u = 0; u < NBMAX; ++u) {
@@ -285,17 +284,19 @@ __global__ __launch_bounds__(FT) void bwd_fused_bf16_kernel(
           float sref;
           const int ib0 = opaque_index(i0 + ti + r);
           {
-            bf16x8 fb[KP][2];
+            bf16x8 fb[KP][2], xf[KP];  // dy rows i; this wave's x rows j
 #pragma unroll
-            for (int ks = 0; ks < KP; ++ks)
+            for (int ks = 0; ks < KP; ++ks) {
+              xf[ks] = frag_rows(xt, 16 * wt, 4 * ks, ar8);
 #pragma unroll
               for (int tt = 0; tt < 2; ++tt) fb[ks][tt] = frag_rows(dyt, ti + 16 * tt, 4 * ks, ar8);
+            }
             cbt[0] = cbk[u][0];
             cbt[1] = cbk[u][1];
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt) sv[tt] = sS[min(ib0 + 16 * tt, Q - 1)];
             sref = sS[i0];
-            sched_ds_reads<2 * KP + 3>();
+            sched_ds_reads<3 * KP + 3>();
 #pragma unroll
             for (int ks = 0; ks < KP; ++ks)
 #pragma unroll
@@ -305,14 +306,16 @@ __global__ __launch_bounds__(FT) void bwd_fused_bf16_kernel(
           f4 gv[2];
           float rmv[2] = {0.f, 0.f};  // row sums of M (rows i = i0 + ti + 16 tt + r) over this lane's 4 columns
           if (u == 0) {
-            const int jq0 = opaque_index(j0 + 16 * wt + 4 * q);
+            float sj[4], dtj[4];
+            s_rows(sj);
+            dt_rows(dtj);
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt) {
               const int iq = ib0 + 16 * tt;
               const float si = sv[tt];
 #pragma unroll
               for (int e = 0; e < 4; ++e) {
-                const int jq = jq0 + e;
+                const int jq = opaque_index(jq0) + e;
                 const float ex = __expf(si - sj[e]);
                 const float L = (iq < Q && iq >= jq) ? ex : 0.f;
                 const float G1 = L * cbt[tt][e];
@@ -332,8 +335,11 @@ __global__ __launch_bounds__(FT) void bwd_fused_bf16_kernel(
 #pragma unroll
             for (int k = 0; k < 2; ++k) dsk[k] = block_acc(dyt, 16 * wt, ti + 16 * k, aa8);
           } else {
-            float cf[4], cfd[4];
+            float cf[4], cfd[4], dtj[4];
+            dt_rows(dtj);
             if (u == 1) {
+              float sj[4];
+              s_rows(sj);
 #pragma unroll
               for (int e = 0; e < 4; ++e) cfc[e] = __expf(sref - sj[e]);
             } else {
@@ -485,15 +491,19 @@ __global__ __launch_bounds__(FT) void bwd_fused_bf16_kernel(
       }
       f4 v[4];  // x_j Gamma for this team's d_state columns
       zero(v);
+      {
+        const RowsAt<8> ar8 = opaque(r8_);
 #pragma unroll
-      for (int ks = 0; ks < KP; ++ks) {
-        bf16x8 fb[4];
+        for (int ks = 0; ks < KP; ++ks) {
+          bf16x8 fb[4];
+          const bf16x8 xf = frag_rows(xt, 16 * wt, 4 * ks, ar8);
 #pragma unroll
-        for (int k = 0; k < 4; ++k) fb[k] = frag_cols(sGam, 32 * ks, 16 * (4 * team + k), ac16);
-        sched_ds_reads<8>();
+          for (int k = 0; k < 4; ++k) fb[k] = frag_cols(sGam, 32 * ks, 16 * (4 * team + k), ac16);
+          sched_ds_reads<9>();
 #pragma unroll
-        for (int k = 0; k < 4; ++k) v[k] = mfma(xf[ks], fb[k], v[k]);
-        sched_mfmas<4>();
+          for (int k = 0; k < 4; ++k) v[k] = mfma(xf, fb[k], v[k]);
+          sched_mfmas<4>();
+        }
       }
       u32x2 xa[2];
       {
@@ -502,12 +512,19 @@ __global__ __launch_bounds__(FT) void bwd_fused_bf16_kernel(
         for (int k = 0; k < 2; ++k) xa[k] = block_acc(xt, 16 * wt, 16 * (2 * team + k), aa8);
       }
       const float s_end = sS[Q - 1];
-      float wj[4];
+      float wj[4], dtj[4];
+      {
+        float sj[4];
+        s_rows(sj);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float wx = __expf(s_end - sj[e]);
+          wj[e] = (jq0 + e < Q) ? wx : 0.f;
+        }
+      }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int jl = 16 * wt + 4 * q + e;
-        const float wx = __expf(s_end - sj[e]);
-        wj[e] = (j0 + jl < Q) ? wx : 0.f;
         float part = 0.f;
 #pragma unroll
         for (int k = 0; k < 2; ++k) part += bg[k][e] * acc_elem(xa[k], e);
@@ -530,6 +547,7 @@ __global__ __launch_bounds__(FT) void bwd_fused_bf16_kernel(
         wait_vm<2>();
       lds_barrier();
       if (hh + 1 < hps) load_gam(hh + 1);  // this head's Gamma is no longer read
+      dt_rows(dtj);
       float dxv[2][4];
 #pragma unroll
       for (int k = 0; k < 2; ++k)
