@@ -45,6 +45,14 @@ __device__ __forceinline__ i32x4 make_rsrc(const void* base) {
   return i32x4{static_cast<int>(a), static_cast<int>((a >> 32) & 0xFFFFu), 0x7FFFFFF0, 0x00020000};
 }
 
+// A per-lane index the compiler must take as computed here: comparisons
+// derived from it stay in the branch that uses them instead of being hoisted
+// out of the loops as lane masks (which then spill to VGPR lanes).
+__device__ __forceinline__ int opaque_index(int v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
 // One wave's 16-byte-per-lane copy into LDS at dst + 16 * lane (dst uniform).
 __device__ __forceinline__ void dma16(const i32x4& rs, lds_char* dst, uint32_t voff) {
 #if defined(__HIP_DEVICE_COMPILE__)  // gfx950 assembly: device pass only
@@ -86,7 +94,10 @@ __device__ __forceinline__ void dma_u16(const i32x4& rs, lds_char* dst, uint32_t
 template <int NW>
 __device__ __forceinline__ void steps_async(lds_char* dst, const i32x4& rs, uint32_t stride, int Q) {
   static_assert(NW >= 4, "four waves cover 256 steps");
-  const int w = wave_id() % 4, t = 64 * w + lane_id();
+  // the lane index passes through opaque_index so that the offsets are
+  // recomputed here rather than hoisted out of the caller's loops (where they
+  // would hold registers for the whole kernel)
+  const int w = wave_id() % 4, t = 64 * w + opaque_index(lane_id());
   dma_u16(rs, dst + 256 * w, t < Q ? static_cast<uint32_t>(t) * stride : OOB_OFFSET);
 }
 
@@ -313,13 +324,6 @@ __device__ __forceinline__ AccAt<CPR> opaque(AccAt<CPR> a) {
   asm volatile("" : "+v"(a.b));
   return a;
 }
-// A per-lane index the compiler must take as computed here: comparisons
-// derived from it stay in the branch that uses them instead of being hoisted
-// out of the loops as lane masks (which then spill to VGPR lanes).
-__device__ __forceinline__ int opaque_index(int v) {
-  asm volatile("" : "+v"(v));
-  return v;
-}
 template <int CPR>
 __device__ __forceinline__ u32x2 block_acc(const lds_char* t, int m0, int n0, AccAt<CPR> a) {
   const short4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -397,7 +401,7 @@ __device__ __forceinline__ float wave_scan(float v) {
 // copied to LDS (one dword per step; lane l reads t = 4l .. 4l+3); every wave
 // computes the whole scan and waves 0..3 each write a quarter.
 __device__ __forceinline__ void scan_store(const uint32_t* dtb_lds, float A, float* s_out, float* dt_out) {
-  const int l = lane_id(), w = wave_id();
+  const int l = opaque_index(lane_id()), w = wave_id();  // recomputed, as in steps_async
   float d[4], a[4];
   const uint4 db = *reinterpret_cast<const uint4*>(dtb_lds + 4 * l);
   const uint32_t dbv[4] = {db.x, db.y, db.z, db.w};

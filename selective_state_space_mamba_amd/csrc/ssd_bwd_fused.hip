@@ -57,12 +57,17 @@ __device__ __forceinline__ bf16x8 w_rows_frag(const lds_char* strips, int a, int
 }
 }  // namespace
 
+// FULL: headdim PMAX, d_state NMAX and chunk QMAX (every tile full), which
+// lets the compiler drop the shape arguments and the row and column bounds
+// checks; otherwise any shape bwd_bf16_supported accepts.
+template <bool FULL>
 __global__ __launch_bounds__(FT) void bwd_fused_bf16_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ Bm, const uint16_t* __restrict__ Cm,
     const uint16_t* __restrict__ dt, const uint16_t* __restrict__ dy, const float* __restrict__ A_log,
     const float* __restrict__ D, const uint16_t* __restrict__ gamma, const uint16_t* __restrict__ hbf,
     float* __restrict__ dx, float* __restrict__ dB_out, float* __restrict__ dC_out, BwdScratch s, int T, int H,
-    int P, int N, int G, int Q, int nsplit) {
+    int P_, int N_, int G, int Q_, int nsplit) {
+  const int P = FULL ? PMAX : P_, N = FULL ? NMAX : N_, Q = FULL ? QMAX : Q_;
   __shared__ __attribute__((aligned(1024))) char sB_[TILE_N];          // B rows j of block jb
   __shared__ __attribute__((aligned(1024))) char sX_[2 * TILE_P];      // x rows j, two heads; W strip slot
   __shared__ __attribute__((aligned(1024))) char sDy0_[TILE_P];        // dy rows i, even steps
@@ -126,7 +131,8 @@ __global__ __launch_bounds__(FT) void bwd_fused_bf16_kernel(
   const __amdgpu_buffer_rsrc_t rrp = make_rsrc_ptr(s.Rp + sum0);
   const __amdgpu_buffer_rsrc_t rdso = make_rsrc_ptr(s.dsoff + sum0);
   // dB and dC (or this head split's partials) from the chunk's first row and the group's columns
-  float* const dBo = dB_out + static_cast<int64_t>(sp) * batch * T * GN + row0 * GN + static_cast<int64_t>(g) * N;
+  const __amdgpu_buffer_rsrc_t rdb =
+      make_rsrc_ptr(dB_out + static_cast<int64_t>(sp) * batch * T * GN + row0 * GN + static_cast<int64_t>(g) * N);
   const __amdgpu_buffer_rsrc_t rdc =
       make_rsrc_ptr(dC_out + static_cast<int64_t>(sp) * batch * T * GN + row0 * GN + static_cast<int64_t>(g) * N);
 
@@ -440,7 +446,8 @@ __global__ __launch_bounds__(FT) void bwd_fused_bf16_kernel(
           // and stores them (row sum slot jb, rows i0 + l)
           if (w == 0) {
             const float rs = sRm[0][l] + sRm[1][l] + sRm[2][l] + sRm[3][l];
-            store_f32(rrm, rs, i0 + l < Q ? static_cast<uint32_t>(i0 + l) * 4 : OOB_OFFSET,
+            const int il = i0 + opaque_index(l);  // recomputed here: hoisted per block it would stay live
+            store_f32(rrm, rs, il < Q ? static_cast<uint32_t>(il) * 4 : OOB_OFFSET,
                       static_cast<uint32_t>(h) * T * 4);
           }
           // wave 0's row-sum store is its youngest memory operation; every
@@ -539,6 +546,8 @@ __global__ __launch_bounds__(FT) void bwd_fused_bf16_kernel(
         const float dd = wave_sum(ddv);
         if (l == 0) sRm[0][w] = dd;
       }
+      // dt_j before the barrier: the scan at this step's end overwrites it
+      dt_rows(dtj);
       // the next head's dt copy must be in LDS; its H_c (when issued here), x
       // and dy copies may be in flight
       if (h_here)
@@ -547,7 +556,6 @@ __global__ __launch_bounds__(FT) void bwd_fused_bf16_kernel(
         wait_vm<2>();
       lds_barrier();
       if (hh + 1 < hps) load_gam(hh + 1);  // this head's Gamma is no longer read
-      dt_rows(dtj);
       float dxv[2][4];
 #pragma unroll
       for (int k = 0; k < 2; ++k)
@@ -574,17 +582,19 @@ __global__ __launch_bounds__(FT) void bwd_fused_bf16_kernel(
       // complete during the next step
       if (hh + 1 < hps) wait_vm<2>();
       {
-        const uint32_t vdx = (static_cast<uint32_t>(j0 + 16 * wt + 4 * q) * HP + 32 * team + r) * 4;
+        const int lf = opaque_index(l), rf = lf & 15, qf = lf >> 4;  // recomputed: see the row-sum store
+        const uint32_t vdx = (static_cast<uint32_t>(j0 + 16 * wt + 4 * qf) * HP + 32 * team + rf) * 4;
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const bool ok = j0 + 16 * wt + 4 * q + e < Q && 32 * team + 16 * k + r < P;
+            const bool ok = j0 + 16 * wt + 4 * qf + e < Q && 32 * team + 16 * k + rf < P;
             store_f32(rdx, dxv[k][e], ok ? vdx + 64 * k : OOB_OFFSET, static_cast<uint32_t>(e * HP + h * P) * 4);
           }
         }
         if (team == 0) {
-          const uint32_t vo = (q == 0 && j0 + jc < Q) ? static_cast<uint32_t>(j0 + jc) * 4 : OOB_OFFSET;
+          const int jcf = 16 * wt + rf;
+          const uint32_t vo = (qf == 0 && j0 + jcf < Q) ? static_cast<uint32_t>(j0 + jcf) * 4 : OOB_OFFSET;
           const uint32_t so4 = static_cast<uint32_t>(h) * T * 4;
           store_f32(rcol, ce, vo, so4);
           store_f32(rdiag, de, vo, so4);
@@ -606,21 +616,30 @@ __global__ __launch_bounds__(FT) void bwd_fused_bf16_kernel(
     // dC as earlier passes of this workgroup wrote it (the same lane, the same
     // layout), for the blocks an earlier pass wrote: every load of the pass is
     // issued first
+    // element (row0 + 4q + e, col0 + r) of a [rows][G N] f32 array (dB, dC)
+    // at byte offset voff + soff: the lane's part voff (OOB_OFFSET outside
+    // the chunk or d_state) and the uniform part soff
+    const int lg = opaque_index(l), rg_ = lg & 15, qg = lg >> 4;  // recomputed: see the row-sum store
+    const uint32_t gn_lane = (static_cast<uint32_t>(4 * qg) * static_cast<uint32_t>(GN) + rg_) * 4;
+    auto gn_voff = [&](int row0_, int col0, int e) -> uint32_t {
+      if (FULL) return gn_lane;
+      return (row0_ + 4 * qg + e < Q && col0 + rg_ < N) ? gn_lane : OOB_OFFSET;
+    };
+    auto gn_soff = [&](int row0_, int col0, int e) -> uint32_t {
+      return (static_cast<uint32_t>(row0_ + e) * static_cast<uint32_t>(GN) + col0) * 4;
+    };
     float dco[NBMAX][4][4];
 #pragma unroll
     for (int u = 0; u < NBMAX; ++u) {
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const int n = 16 * (4 * team + k) + r;
+        const int c0 = 16 * (4 * team + k), r0 = (jb + u) * BQ + 16 * wt;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           dco[u][k][e] = 0.f;
-          if (u < nib && ((written >> (jb + u)) & 1)) {
-            const int iq = (jb + u) * BQ + 16 * wt + 4 * q + e;
-            const uint32_t off =
-                (iq < Q && n < N) ? (static_cast<uint32_t>(iq) * static_cast<uint32_t>(GN) + n) * 4 : OOB_OFFSET;
-            dco[u][k][e] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rdc, off, 0, 0));
-          }
+          if (u < nib && ((written >> (jb + u)) & 1))
+            dco[u][k][e] = __uint_as_float(
+                __builtin_amdgcn_raw_buffer_load_b32(rdc, gn_voff(r0, c0, e), gn_soff(r0, c0, e), 0));
         }
       }
     }
@@ -655,17 +674,12 @@ __global__ __launch_bounds__(FT) void bwd_fused_bf16_kernel(
           for (int kk = 0; kk < 4; ++kk) pc[kk] = mfma(fa, fb[kk], pc[kk]);
           sched_mfmas<4>();
         }
-        const int i0 = (jb + u) * BQ;
+        const int r0 = (jb + u) * BQ + 16 * wt;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-          const int n = 16 * (4 * team + k) + r;
+          const int c0 = 16 * (4 * team + k);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int iq = i0 + 16 * wt + 4 * q + e;
-            const uint32_t off =
-                (iq < Q && n < N) ? (static_cast<uint32_t>(iq) * static_cast<uint32_t>(GN) + n) * 4 : OOB_OFFSET;
-            store_f32(rdc, dco[u][k][e] + pc[k][e], off, 0);
-          }
+          for (int e = 0; e < 4; ++e) store_f32(rdc, dco[u][k][e] + pc[k][e], gn_voff(r0, c0, e), gn_soff(r0, c0, e));
         }
       }
     }
@@ -694,12 +708,9 @@ __global__ __launch_bounds__(FT) void bwd_fused_bf16_kernel(
     }
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const int n = 16 * (4 * team + k) + r;
+      const int c0 = 16 * (4 * team + k), r0 = j0 + 16 * wt;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int jq = j0 + 16 * wt + 4 * q + e;
-        if (jq < Q && n < N) dBo[static_cast<int64_t>(jq) * GN + n] = dbp[k][e] + dbs[k][e];
-      }
+      for (int e = 0; e < 4; ++e) store_f32(rdb, dbp[k][e] + dbs[k][e], gn_voff(r0, c0, e), gn_soff(r0, c0, e));
     }
     written |= ((1u << nb) - 1) & ~((1u << jb) - 1);  // blocks jb .. nb - 1
     if (jb + 1 < nb) {
@@ -716,7 +727,9 @@ hipError_t launch_bwd_fused_bf16(const Dims& d, int nsplit, const void* x, const
                                  const void* gamma, const void* hbf, float* dx, float* dB_out, float* dC_out,
                                  const BwdScratch& s, hipStream_t st) {
   const int64_t nblk = static_cast<int64_t>(d.b) * d.nc() * d.G * nsplit;
-  hipLaunchKernelGGL(bwd_fused_bf16_kernel, dim3(static_cast<unsigned>(nblk)), dim3(FT), 0, st,
+  const bool full = d.P == PMAX && d.N == NMAX && d.Q == QMAX;
+  hipLaunchKernelGGL(full ? bwd_fused_bf16_kernel<true> : bwd_fused_bf16_kernel<false>, dim3(static_cast<unsigned>(nblk)),
+                     dim3(FT), 0, st,
                      static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(B), static_cast<const uint16_t*>(C),
                      static_cast<const uint16_t*>(dt), static_cast<const uint16_t*>(dy), A_log, D,
                      static_cast<const uint16_t*>(gamma), static_cast<const uint16_t*>(hbf), dx, dB_out, dC_out, s, d.T,
