@@ -491,7 +491,7 @@ int bwd_impl(const char* who, const ssd_problem* prob, const void* x, const void
   }
   if (plan.bf16)
     SSD_LAUNCH(ssd::launch_chunk_state_bwd_bf16(d, dy, C, dt, A_log, d_final_state, states, gamma, d_init_state,
-                                                s.gh_part, hbf, st),
+                                                s.gh_part, hbf, plan.fused ? s.done : nullptr, st),
                "chunk_state_bwd");
   else
     SSD_LAUNCH(
@@ -499,8 +499,10 @@ int bwd_impl(const char* who, const ssd_problem* prob, const void* x, const void
                                     s.gh_part, nullptr, at<float>(workspace, plan.send), st),
         "chunk_state_bwd");
   if (plan.fused) {
+    // the fused kernel also does the dt kernel's work (ddt, dA_log, dD)
     SSD_LAUNCH(ssd::launch_bwd_fused_bf16(d, plan.nsplit, x, B, C, dt, dy, A_log, D, gamma, hbf, dx,
-                                          plan.nsplit > 1 ? s.dB_part : dB, plan.nsplit > 1 ? s.dC_part : dC, s, st),
+                                          plan.nsplit > 1 ? s.dB_part : dB, plan.nsplit > 1 ? s.dC_part : dC, ddt,
+                                          dA_log, dD, s, st),
                "chunk_bwd_fused");
   } else if (plan.bf16) {
     SSD_LAUNCH(ssd::launch_bwd_col_bf16(d, plan.nsplit, x, B, C, dt, dy, A_log, D, gamma, dx,
@@ -517,7 +519,7 @@ int bwd_impl(const char* who, const ssd_problem* prob, const void* x, const void
                                          plan.nsplit > 1 ? s.dC_part : dC, s, st),
                "chunk_bwd_row");
   }
-  SSD_LAUNCH(ssd::launch_bwd_dt(d, act, dt, A_log, ddt, dA_log, dD, s, st), "bwd_dt");
+  if (!plan.fused) SSD_LAUNCH(ssd::launch_bwd_dt(d, act, dt, A_log, ddt, dA_log, dD, s, st), "bwd_dt");
   if (plan.nsplit > 1) SSD_LAUNCH(ssd::launch_bwd_split_sum(d, plan.nsplit, dB, dC, s, st), "bwd_split_sum");
   return ok();
 }

@@ -45,6 +45,12 @@ constexpr int KP = PMAX / 32;
 constexpr int KN = NMAX / 32;
 static_assert(NBMAX <= 4, "the pass-end phase holds at most four blocks' W strips");
 
+// Sum over the 64 lanes of a wave, in every lane (DPP scan, then lane 63).
+__device__ __forceinline__ float lane_last(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), WAVE - 1));
+}
+__device__ __forceinline__ float wave_tot(float v) { return lane_last(wave_scan(v)); }
+
 // A fragment of W (rows i, k = j) from the [i][j] wave strips of one block:
 // rows i = 16 a + (lane % 16), columns j = 32 ks + 8 (lane / 16) .. +7.  Row i
 // lies in the strips of team i / 32, column j in the strip of wave j / 16 of
@@ -65,8 +71,9 @@ __global__ __launch_bounds__(FT) void bwd_fused_bf16_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ Bm, const uint16_t* __restrict__ Cm,
     const uint16_t* __restrict__ dt, const uint16_t* __restrict__ dy, const float* __restrict__ A_log,
     const float* __restrict__ D, const uint16_t* __restrict__ gamma, const uint16_t* __restrict__ hbf,
-    float* __restrict__ dx, float* __restrict__ dB_out, float* __restrict__ dC_out, BwdScratch s, int T, int H,
-    int P_, int N_, int G, int Q_, int nsplit) {
+    float* __restrict__ dx, float* __restrict__ dB_out, float* __restrict__ dC_out, float* __restrict__ ddt,
+    float* __restrict__ dA_log_out, float* __restrict__ dD_out, BwdScratch s, int T, int H, int P_, int N_, int G,
+    int Q_, int nsplit, int npb) {
   const int P = FULL ? PMAX : P_, N = FULL ? NMAX : N_, Q = FULL ? QMAX : Q_;
   __shared__ __attribute__((aligned(1024))) char sB_[TILE_N];          // B rows j of block jb
   __shared__ __attribute__((aligned(1024))) char sX_[2 * TILE_P];      // x rows j, two heads; W strip slot
@@ -601,7 +608,10 @@ __global__ __launch_bounds__(FT) void bwd_fused_bf16_kernel(
           store_f32(rrp, re, vo, so4);
           store_f32(rdso, so, vo, so4);
         }
-        if (w == 0 && l == 0) s.dD_part[((static_cast<int64_t>(bi) * nc + c) * nb + jb) * H + h] = dd_tot;
+        // read by the last workgroup of this launch: stored at the device's coherence point
+        if (w == 0 && l == 0)
+          __hip_atomic_store(s.dD_part + ((static_cast<int64_t>(bi) * nc + c) * nb + jb) * H + h, dd_tot,
+                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
       if (hh + 1 < hps) scan_store(sDtb, -__expf(An), sS, sDt);
       lds_barrier();
@@ -718,22 +728,138 @@ __global__ __launch_bounds__(FT) void bwd_fused_bf16_kernel(
       load_first_gam(jb + 1);
     }
   }  // pass
-  // the dt kernel that follows counts its finished workgroups from 0
-  if (blockIdx.x == 0 && threadIdx.x == 0) __hip_atomic_store(s.done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+  // ---- ddt of this workgroup's heads over its chunk, then, in the last
+  // workgroup to finish, dA_log and dD (bwd_dt_kernel's work, in its order of
+  // operations): ds_t from the per-row sums, da_t its reverse cumsum inside
+  // the chunk, ddt_t = colE_t + R'_t + A da_t, and the chunk's dA partial
+  // sum_t dt_t da_t.  The per-row sums are this workgroup's own stores; the
+  // barrier's fence makes every wave's stores visible to the others.  One
+  // wave per head, lane l holding rows l + 64 e; eight heads at a time, their
+  // ddt staged in the B tile's slot so that the stores run along the heads.
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  float* const sT = reinterpret_cast<float*>(sB_);  // [QMAX][FW]
+  static_assert(QMAX * FW * 4 <= TILE_N, "ddt staging fits the B tile's slot");
+  const int tid = threadIdx.x;
+  const int hfirst = g * hpg + sp * hps;  // the workgroup's heads hfirst .. hfirst + hps - 1
+  for (int hh0 = 0; hh0 < hps; hh0 += FW) {
+    const int hn = min(FW, hps - hh0);
+    if (w < hn) {
+      const int h = hfirst + hh0 + w;
+      const int64_t o0 = sum0 + static_cast<int64_t>(h) * T;
+      const float A = -__expf(A_log[h]);
+      float cE[4], rP[4], rM[4], dE[4], dS[4], dv[4], ds[4];
+      float sl = 0.f, tr = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int k = 64 * e + l;
+        cE[e] = rP[e] = rM[e] = dE[e] = dS[e] = dv[e] = 0.f;
+        if (k < Q) {
+          cE[e] = s.colE[o0 + k];
+          rP[e] = s.Rp[o0 + k];
+          for (int jb = 0; jb <= (k >> 6); ++jb) rM[e] += s.rowM[jb * bht + o0 + k];
+          dE[e] = s.diagE[o0 + k];
+          dS[e] = s.dsoff[o0 + k];
+          dv[e] = bf16_bits_to_f32(dt[(row0 + k) * H + h]);
+        }
+        ds[e] = rM[e] - dv[e] * (cE[e] - dE[e]) + dS[e] - dv[e] * rP[e];
+        sl += dv[e] * A;
+        tr += dv[e] * rP[e];
+      }
+      const float ghl = l < npb ? s.gh_part[((static_cast<int64_t>(bi) * nc + c) * H + h) * npb + l] : 0.f;
+      sl = wave_tot(sl);  // s at the chunk's last row
+      tr = wave_tot(tr);
+      const float gh = wave_tot(ghl);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (64 * e + l == Q - 1) ds[e] += tr + __expf(sl) * gh;
+      // da_k = sum of ds over rows k' >= k: the chunk total less the inclusive
+      // prefix, plus ds_k
+      float incl[4], carry = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float sc = wave_scan(ds[e]);
+        incl[e] = carry + sc;
+        carry += lane_last(sc);
+      }
+      float pa = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int k = 64 * e + l;
+        const float da = carry - incl[e] + ds[e];
+        if (k < Q) sT[k * FW + w] = cE[e] + rP[e] + A * da;
+        pa += dv[e] * da;
+      }
+      pa = wave_tot(pa);
+      if (l == 0)
+        __hip_atomic_store(s.dA_part + (static_cast<int64_t>(bi) * nc + c) * H + h, pa, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    for (int i = tid; i < Q * hn; i += FT) {
+      const int k = i / hn, j = i - k * hn;
+      ddt[(row0 + k) * H + hfirst + hh0 + j] = sT[k * FW + j];
+    }
+    __syncthreads();
+  }
+  // every wave's partial stores are complete before the workgroup counts itself
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  __shared__ int sFinal;
+  if (tid == 0) {
+    const unsigned prev = __hip_atomic_fetch_add(s.done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    sFinal = prev + 1 == gridDim.x;
+  }
+  __syncthreads();
+  if (!sFinal) return;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  // the last workgroup: thread tid adds head h0 + tid % hb over the chunks
+  // tid / hb, tid / hb + np, ...; then one thread per head adds the np slices
+  float* const sFin = reinterpret_cast<float*>(sG_);  // [2][FT]
+  static_assert(2 * FT * 4 <= FW * STRIP, "final sums fit the strips' slot");
+  const int64_t nbc = batch * nc;
+  for (int h0 = 0; h0 < H; h0 += FT) {
+    const int hb = min(FT, H - h0), np = FT / hb;
+    const int hh = tid % hb, part = tid / hb;
+    float a = 0.f, dd = 0.f;
+    if (part < np) {
+      for (int64_t v = part; v < nbc; v += np) {
+        a += __hip_atomic_load(s.dA_part + v * H + h0 + hh, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int ib = 0; ib < nb; ++ib)
+          dd += __hip_atomic_load(s.dD_part + (v * nb + ib) * H + h0 + hh, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    sFin[tid] = a;
+    sFin[FT + tid] = dd;
+    __syncthreads();
+    if (tid < hb) {
+      float ta = 0.f, td = 0.f;
+      for (int p = 0; p < np; ++p) {
+        ta += sFin[p * hb + tid];
+        td += sFin[FT + p * hb + tid];
+      }
+      dA_log_out[h0 + tid] = -__expf(A_log[h0 + tid]) * ta;
+      dD_out[h0 + tid] = td;
+    }
+    __syncthreads();
+  }
+  // the next call counts from 0 again
+  if (tid == 0) __hip_atomic_store(s.done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 hipError_t launch_bwd_fused_bf16(const Dims& d, int nsplit, const void* x, const void* B, const void* C,
                                  const void* dt, const void* dy, const float* A_log, const float* D,
                                  const void* gamma, const void* hbf, float* dx, float* dB_out, float* dC_out,
-                                 const BwdScratch& s, hipStream_t st) {
+                                 float* ddt, float* dA_log, float* dD, const BwdScratch& s, hipStream_t st) {
   const int64_t nblk = static_cast<int64_t>(d.b) * d.nc() * d.G * nsplit;
   const bool full = d.P == PMAX && d.N == NMAX && d.Q == QMAX;
   hipLaunchKernelGGL(full ? bwd_fused_bf16_kernel<true> : bwd_fused_bf16_kernel<false>, dim3(static_cast<unsigned>(nblk)),
                      dim3(FT), 0, st,
                      static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(B), static_cast<const uint16_t*>(C),
                      static_cast<const uint16_t*>(dt), static_cast<const uint16_t*>(dy), A_log, D,
-                     static_cast<const uint16_t*>(gamma), static_cast<const uint16_t*>(hbf), dx, dB_out, dC_out, s, d.T,
-                     d.H, d.P, d.N, d.G, d.Q, nsplit);
+                     static_cast<const uint16_t*>(gamma), static_cast<const uint16_t*>(hbf), dx, dB_out, dC_out, ddt,
+                     dA_log, dD, s, d.T, d.H, d.P, d.N, d.G, d.Q, nsplit, state_npb(d));
   return hipGetLastError();
 }
 

@@ -44,9 +44,11 @@ hipError_t launch_chunk_state_bwd(const Dims& d, DType act, DType dyt, const voi
 hipError_t launch_chunk_state_fwd_bf16(const Dims& d, const void* x, const void* B, const void* dt,
                                        const float* A_log, const float* init, float* states, float* final_state,
                                        void* hbf, hipStream_t st);
+// counter (nullable): an arrival counter that the bf16 backward's fused kernel
+// counts on, zeroed by this launch.
 hipError_t launch_chunk_state_bwd_bf16(const Dims& d, const void* dy, const void* C, const void* dt,
                                        const float* A_log, const float* dfinal, const float* states, void* gamma,
-                                       float* dinit, float* gh_part, void* hbf, hipStream_t st);
+                                       float* dinit, float* gh_part, void* hbf, unsigned* counter, hipStream_t st);
 hipError_t launch_out_fwd_bf16(const Dims& d, int nsplit, const void* x, const void* B, const void* C,
                                const void* dt, const float* A_log, const float* D, const void* hbf, void* y,
                                hipStream_t st);
@@ -96,12 +98,15 @@ hipError_t launch_bwd_col_bf16(const Dims& d, int nsplit, const void* x, const v
 // The column and row work of the bf16 kernels in one kernel (ssd_bwd_fused.hip):
 // one workgroup per (batch, chunk, group, head split); dx, dB and dC (or the
 // head-split partials), the per-column sums, the readout term, dD partials,
-// and the row sums of M in s.row_slots = nb slots.  Reads the bf16 copy of the
-// states (hbf) and Gamma; zeroes s.done for the dt kernel.
+// and the row sums of M in s.row_slots = nb slots; then, per workgroup, ddt of
+// its heads and chunk, and in the last workgroup to finish dA_log and dD (the
+// dt kernel's work).  Reads the bf16 copy of the states (hbf), Gamma and
+// s.gh_part; needs s.done zeroed by an earlier launch on the stream (the
+// reverse chunk-state kernel does it) and leaves it zero.
 hipError_t launch_bwd_fused_bf16(const Dims& d, int nsplit, const void* x, const void* B, const void* C,
                                  const void* dt, const void* dy, const float* A_log, const float* D,
                                  const void* gamma, const void* hbf, float* dx, float* dB_out, float* dC_out,
-                                 const BwdScratch& s, hipStream_t st);
+                                 float* ddt, float* dA_log, float* dD, const BwdScratch& s, hipStream_t st);
 
 // dt gradient per token, and dA_log and dD (fixed-order sums of the per-chunk
 // partials, taken by the launch's last workgroup).  Needs s.done zeroed by an

@@ -59,6 +59,7 @@ __global__ __launch_bounds__(ST) void chunk_state_bf16_kernel(
     const float* __restrict__ hstates,  // bwd: H_c
     float* __restrict__ gh_part,        // bwd: [b,nc,H,ceil(P/16)] partial <Gamma_{c+1}, H_c>
     uint16_t* __restrict__ hbf_out,     // bwd: H_c in bf16 (nullable)
+    unsigned* __restrict__ counter,     // bwd: an arrival counter of the next kernel, zeroed here (nullable)
     int T, int H, int P, int N, int G, int Q) {
   __shared__ __attribute__((aligned(1024))) char sX_[2 * XSLAB];
   __shared__ __attribute__((aligned(1024))) char sB_[2 * BSLAB];
@@ -70,6 +71,8 @@ __global__ __launch_bounds__(ST) void chunk_state_bf16_kernel(
   lds_char* const sB = lds_ptr(sB_);
   lds_char* const sH = lds_ptr(sH_);
 
+  if (REV && counter && blockIdx.x == 0 && threadIdx.x == 0)
+    __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const int npb = (P + SPB - 1) / SPB, npb16 = (P + 15) / 16;
   const int lb = xcd_logical_block(blockIdx.x, gridDim.x);
   const int pb = lb % npb, h = (lb / npb) % H, bi = lb / (npb * H);
@@ -280,19 +283,19 @@ hipError_t launch_chunk_state_fwd_bf16(const Dims& d, const void* x, const void*
   const int64_t nblk = static_cast<int64_t>(d.b) * d.H * ((d.P + SPB - 1) / SPB);
   hipLaunchKernelGGL(chunk_state_bf16_kernel<false>, dim3(nblk), dim3(ST), 0, st, static_cast<const uint16_t*>(x),
                      static_cast<const uint16_t*>(B), static_cast<const uint16_t*>(dt), A_log, init, states,
-                     static_cast<uint16_t*>(hbf), final_state, nullptr, nullptr, nullptr, d.T, d.H, d.P, d.N, d.G,
-                     d.Q);
+                     static_cast<uint16_t*>(hbf), final_state, nullptr, nullptr, nullptr, nullptr, d.T, d.H, d.P, d.N,
+                     d.G, d.Q);
   return hipGetLastError();
 }
 
 hipError_t launch_chunk_state_bwd_bf16(const Dims& d, const void* dy, const void* C, const void* dt,
                                        const float* A_log, const float* dfinal, const float* states, void* gamma,
-                                       float* dinit, float* gh_part, void* hbf, hipStream_t st) {
+                                       float* dinit, float* gh_part, void* hbf, unsigned* counter, hipStream_t st) {
   const int64_t nblk = static_cast<int64_t>(d.b) * d.H * ((d.P + SPB - 1) / SPB);
   hipLaunchKernelGGL(chunk_state_bf16_kernel<true>, dim3(nblk), dim3(ST), 0, st, static_cast<const uint16_t*>(dy),
                      static_cast<const uint16_t*>(C), static_cast<const uint16_t*>(dt), A_log, dfinal, nullptr,
-                     static_cast<uint16_t*>(gamma), dinit, states, gh_part, static_cast<uint16_t*>(hbf), d.T, d.H,
-                     d.P, d.N, d.G, d.Q);
+                     static_cast<uint16_t*>(gamma), dinit, states, gh_part, static_cast<uint16_t*>(hbf), counter, d.T,
+                     d.H, d.P, d.N, d.G, d.Q);
   return hipGetLastError();
 }
 
