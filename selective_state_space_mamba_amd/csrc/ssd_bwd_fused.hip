@@ -756,11 +756,14 @@ __global__ __launch_bounds__(FT) void bwd_fused_bf16_kernel(
         const int k = 64 * e + l;
         cE[e] = rP[e] = rM[e] = dE[e] = dS[e] = dv[e] = 0.f;
         if (k < Q) {
-          cE[e] = s.colE[o0 + k];
-          rP[e] = s.Rp[o0 + k];
+          // through the descriptors the passes stored with (their bases stay
+          // in registers anyway): element (h, k) at byte (h T + k) 4
+          const uint32_t vk = static_cast<uint32_t>(k) * 4, sh = static_cast<uint32_t>(h) * T * 4;
+          cE[e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rcol, vk, sh, 0));
+          rP[e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rrp, vk, sh, 0));
+          dE[e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rdiag, vk, sh, 0));
+          dS[e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rdso, vk, sh, 0));
           for (int jb = 0; jb <= (k >> 6); ++jb) rM[e] += s.rowM[jb * bht + o0 + k];
-          dE[e] = s.diagE[o0 + k];
-          dS[e] = s.dsoff[o0 + k];
           dv[e] = bf16_bits_to_f32(dt[(row0 + k) * H + h]);
         }
         ds[e] = rM[e] - dv[e] * (cE[e] - dE[e]) + dS[e] - dv[e] * rP[e];
