@@ -86,7 +86,8 @@ def method_bytes(cfg, kernel: str) -> float:
         "chunk_state_bwd": HP * s_y + GN * s_a + H * s_a,
         "chunk_bwd_col": HP * s_a + 2 * GN * s_a + H * s_a + HP * s_y + HP * 4 + GN * 4,
         "chunk_bwd_row": HP * s_a + 2 * GN * s_a + H * s_a + HP * s_y + GN * 4,
-        "chunk_bwd_fused": HP * s_a + 2 * GN * s_a + H * s_a + HP * s_y + HP * 4 + 2 * GN * 4,
+        # dx, dB, dC and (the dt kernel's work folded in) ddt
+        "chunk_bwd_fused": HP * s_a + 2 * GN * s_a + H * s_a + HP * s_y + HP * 4 + 2 * GN * 4 + H * 4,
         "bwd_dt": H * s_a + H * 4,
     }
     return per_token[kernel] * cfg.batch * cfg.seqlen
@@ -110,9 +111,10 @@ def algorithmic_bytes(cfg, kernel: str) -> float:
         "chunk_bwd_row": HP * s_a + 2 * GN * s_a + H * s_a + HP * s_y + st + GN * 4 + 2 * H * 4,
         # + Gamma and the bf16 states in; the per-head column sums, diagonal,
         # R', readout term and the row sums of M (one slot per 64-column block
-        # at or before a row's block, (nb + 1) / 2 on average) out
+        # at or before a row's block, (nb + 1) / 2 on average) out, and read
+        # back for ddt (written, H * 4)
         "chunk_bwd_fused": (HP * s_a + 2 * GN * s_a + H * s_a + HP * s_y + 2 * sg + HP * 4 + 2 * GN * 4
-                            + 4 * H * 4 + H * 4 * (cfg.chunk // 64 + 1) / 2),
+                            + 2 * (4 * H * 4 + H * 4 * (cfg.chunk // 64 + 1) / 2) + H * 4),
         "bwd_dt": H * s_a + 5 * H * 4 + H * 4,
     }
     return per_token[kernel] * tok

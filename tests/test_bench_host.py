@@ -61,3 +61,14 @@ def test_more_than_one_gpu_is_refused():
     res = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
                          text=True, timeout=120)
     assert res.returncode == 2 and "one GPU" in res.stderr
+
+
+def test_fused_method_bytes_include_ddt():
+    # the fused backward kernel also writes ddt (the dt kernel's work)
+    cfg = CONFIGS["grouped"]
+    HP, GN, H = cfg.nheads * cfg.headdim, cfg.ngroups * cfg.dstate, cfg.nheads
+    tok = cfg.batch * cfg.seqlen
+    assert bench.method_bytes(cfg, "chunk_bwd_fused") == (HP * 2 + 2 * GN * 2 + H * 2 + HP * 2 + HP * 4 + 2 * GN * 4
+                                                          + H * 4) * tok
+    # so the fused kernel alone reads and writes every byte the whole backward must move
+    assert bench.method_bytes(cfg, "chunk_bwd_fused") == bench.backward_algorithmic_bytes(cfg)
