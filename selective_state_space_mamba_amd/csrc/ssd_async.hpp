@@ -213,6 +213,28 @@ struct TileLanes {
   }
 };
 
+// TileLanes' copy with the per-lane offsets recomputed at the issue from an
+// opaque lane index, for kernels where keeping them live across a loop would
+// spill them (a spilled offset's reload waits for every copy in flight).
+template <int ROWS, int CPR, int NW>
+__device__ __forceinline__ void tile_issue_fresh(lds_char* dst, const i32x4& rs, uint32_t ldb, int chunk_ok,
+                                                 uint32_t soff, int row_ok) {
+  constexpr int LPI = 64 / CPR, NI = ROWS / LPI;
+  static_assert(ROWS % LPI == 0, "tile rows");
+  const int l = opaque_index(lane_id()), w = wave_id();
+  const int rl = l / CPR, pc = l % CPR;
+#pragma unroll
+  for (int it = 0; it < (NI + NW - 1) / NW; ++it) {
+    const int ins = it * NW + w;
+    if ((NI % NW) == 0 || ins < NI) {
+      const int r = ins * LPI + rl;
+      const int c = pc ^ swz<CPR>(r);
+      const uint32_t off = (c < chunk_ok && r < row_ok) ? static_cast<uint32_t>(r) * ldb + (c << 4) : OOB_OFFSET;
+      dma16_so(rs, dst + ins * 1024, off, soff);
+    }
+  }
+}
+
 // Fragment with k along the row: lane (r, q) gets row m0 + r, elements
 // 8 (kc + q) .. +7.
 template <int CPR>

@@ -70,27 +70,30 @@ __device__ __forceinline__ void fwd_put_strip(lds_char* strip, const f4 (&v)[2])
 }
 }  // namespace
 
-__global__ __launch_bounds__(FT) void out_fwd_bf16_kernel(
+__global__ __launch_bounds__(FT) __attribute__((amdgpu_waves_per_eu(4, 4))) void out_fwd_bf16_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ Bm, const uint16_t* __restrict__ Cm,
     const uint16_t* __restrict__ dt, const float* __restrict__ A_log, const float* __restrict__ D,
     const uint16_t* __restrict__ hbf, uint16_t* __restrict__ y, int T, int H, int P, int N, int G, int Q,
     int nsplit) {
-  __shared__ __attribute__((aligned(1024))) char sC_[FTILE_N];          // C rows i of block ib
-  __shared__ __attribute__((aligned(1024))) char sX0_[FTILE_P];         // x rows j, even steps
-  __shared__ __attribute__((aligned(1024))) char sX1_[FTILE_P];         // x rows j, odd steps
-  __shared__ __attribute__((aligned(1024))) char sH_[FTILE_N];          // H_c [p][n] (bf16); B tile slot
-  __shared__ __attribute__((aligned(1024))) char sXch_[FTILE_N];        // y halves; B tile slot
-  __shared__ __attribute__((aligned(1024))) char sG_[FW * FSTRIP];      // per-wave G strips [j][i]
-  __shared__ __attribute__((aligned(1024))) char sBt_[NBMAX * FTILE_N];  // B tiles of blocks jb, tile jb at jb * 16 KB
-  __shared__ __attribute__((aligned(16))) float sS[2][QMAX];
-  __shared__ __attribute__((aligned(16))) float sDt[2][QMAX];
-  __shared__ __attribute__((aligned(16))) uint32_t sDtb[QMAX];  // dt bits of the next head to scan
-  lds_char* const sC = lds_ptr(sC_);
-  lds_char* const sX[2] = {lds_ptr(sX0_), lds_ptr(sX1_)};
-  lds_char* const sH = lds_ptr(sH_);
-  lds_char* const sXch = lds_ptr(sXch_);
-  lds_char* const sG = lds_ptr(sG_);
-  lds_char* const sBt = lds_ptr(sBt_);
+  // 77 KB, so that two workgroups share a CU:
+  //   C rows i of block ib (read for C.B^T and every head's C_i . H_c^T) | H_c
+  //   [p][n] | x rows j of even and odd steps | per-wave G strips [j][i] | the
+  //   teams' y halves | s and dt of two heads | the next head's dt bits.
+  // The B tiles are needed only for C.B^T at a block's start: they pass two
+  // at a time through [x odd | G strips] and [y halves] (16 KB each), which
+  // are idle then.
+  __shared__ __attribute__((aligned(1024))) char smem[3 * FTILE_N + 3 * FTILE_P + 5 * QMAX * 4];
+  static_assert(FW * FSTRIP == FTILE_P, "the strips and the odd x tile form one 16 KB B slot");
+  lds_char* const sC = lds_ptr(smem);
+  lds_char* const sH = sC + FTILE_N;
+  lds_char* const sX[2] = {sH + FTILE_N, sH + FTILE_N + FTILE_P};
+  lds_char* const sG = sX[1] + FTILE_P;
+  lds_char* const sXch = sG + FW * FSTRIP;
+  lds_char* const sBslot[2] = {sXch, sX[1]};
+  char* const tail = smem + 3 * FTILE_N + 3 * FTILE_P;
+  float (*const sS)[QMAX] = reinterpret_cast<float (*)[QMAX]>(tail);
+  float (*const sDt)[QMAX] = reinterpret_cast<float (*)[QMAX]>(tail + 2 * QMAX * 4);
+  uint32_t* const sDtb = reinterpret_cast<uint32_t*>(tail + 4 * QMAX * 4);
 
   const int nc = T / Q, nb = (Q + BQ - 1) / BQ;
   const int hpg = H / G, hps = hpg / nsplit;
@@ -137,17 +140,15 @@ __global__ __launch_bounds__(FT) void out_fwd_bf16_kernel(
   // the dt series of head hh to LDS (one copy instruction per wave; no load
   // the compiler can see, whose wait would be vmcnt(0) and hold up the copies)
   auto load_dt = [&](int hh) { steps_async<FW>(lds_ptr(sDtb), make_rsrc(dt + row0 * H + head(hh)), H * 2, Q); };
-  // x tiles (64 rows of headdim) and H_c (headdim rows of d_state): per-lane
-  // offsets computed once, the tile's first row as the scalar offset
-  TileLanes<64, 8, FW> tl8;
-  TileLanes<64, 16, FW> tlh;
-  tl8.init(HPb, pch);
-  tlh.init(N * 2, nch);
+  // x tiles (64 rows of headdim) and H_c (headdim rows of d_state), the
+  // tile's first row as the scalar offset; the per-lane offsets are
+  // recomputed at each copy (with four waves per SIMD they would not stay in
+  // registers)
   auto load_x = [&](int hh, int jb, lds_char* dst) {
     const int j0 = jb * BQ;
-    tl8.issue(dst, rx, j0 * HPb + head(hh) * P * 2, min(BQ, Q - j0));
+    tile_issue_fresh<64, 8, FW>(dst, rx, HPb, pch, j0 * HPb + head(hh) * P * 2, min(BQ, Q - j0));
   };
-  auto load_h = [&](int hh) { tlh.issue(sH, rh, head(hh) * P * N * 2, P); };
+  auto load_h = [&](int hh) { tile_issue_fresh<64, 16, FW>(sH, rh, N * 2, nch, head(hh) * P * N * 2, P); };
   // C rows, the first head's first x, H_c and dt for row block ix (this
   // pass's, or the next pass's while this one finishes)
   auto load_first = [&](int ix) {
@@ -157,33 +158,31 @@ __global__ __launch_bounds__(FT) void out_fwd_bf16_kernel(
     load_h(0);
     load_dt(0);
   };
-  // the B tiles of blocks jb <= jx, each to its own 16 KB
-  auto load_bs = [&](int jx) {
+  // the B tiles of blocks jp and jp + 1 (those <= ib) to the two B slots
+  auto load_bpair = [&](int jp) {
 #pragma unroll
-    for (int jb = 0; jb < NBMAX; ++jb) {
-      if (jb <= jx) {
-        const int j0 = jb * BQ;
-        tile_async<64, 16, FW>(sBt + jb * FTILE_N, rb, j0 * GNb + goff, GNb, min(BQ, Q - j0), nch);
+    for (int t = 0; t < 2; ++t) {
+      if (jp + t < nj) {
+        const int j0 = (jp + t) * BQ;
+        tile_async<64, 16, FW>(sBslot[t], rb, j0 * GNb + goff, GNb, min(BQ, Q - j0), nch);
       }
     }
   };
   // whether a second row block follows in this workgroup
   const bool next = pass == 0 && nb - 1 - kpair != kpair;
 
-  // ---- C rows of block ib, the B tiles of blocks jb <= ib and the first
-  // head's tiles, in flight together, then C.B^T for every block jb <= ib,
-  // kept in registers.  The B tiles stay for the second block of a pair
-  // (whose blocks are a subset); its first tiles load during the first
-  // block's last head.
-  if (pass == 0) {
-    load_first(ib);
-    load_bs(ib);
-  }
+  // ---- C rows of block ib, the first two B tiles and the first head's
+  // tiles, in flight together (the second block of a pair had its C, x, H_c
+  // and dt copies issued during the first block's last head), then C.B^T for
+  // every block jb <= ib, two B tiles at a time, kept in registers
+  if (pass == 0) load_first(ib);
+  load_bpair(0);
   wait_vm<0>();
   __syncthreads();
-  // This wave's C rows i, the first operand of C.B^T and of every head's
-  // C_i . H_c^T, also stay in registers.
-  f4 cbk[NBMAX][2];  // rows i of this wave, columns j = jb * 64 + tj + 16 tt + r
+  // C.B^T stays in registers as bf16 pairs (it only scales the bf16 G tiles:
+  // one more rounding of each element, and half the registers); this wave's C
+  // rows i are read from the C tile again for every head's C_i . H_c^T.
+  u32x2 cbk[NBMAX][2];  // rows i of this wave, columns j = jb * 64 + tj + 16 tt + r
   bf16x8 cfr[FKN];
   {
     const RowsAt<16> ar16 = opaque(r16_);
@@ -192,9 +191,16 @@ __global__ __launch_bounds__(FT) void out_fwd_bf16_kernel(
   }
 #pragma unroll
   for (int jb = 0; jb < NBMAX; ++jb) {
-    zero(cbk[jb]);
+    cbk[jb][0] = cbk[jb][1] = u32x2{0u, 0u};
+    if ((jb & 1) == 0 && jb > 0 && jb < nj) {
+      // the next two B tiles, once every wave has read the slots
+      lds_barrier();
+      load_bpair(jb);
+      wait_vm<0>();
+      lds_barrier();
+    }
     if (jb < nj) {
-      const lds_char* bt = sBt + jb * FTILE_N;
+      const lds_char* bt = sBslot[jb & 1];
       const RowsAt<16> ar16 = opaque(r16_);
       bf16x8 fb[FKN][2];
 #pragma unroll
@@ -202,13 +208,18 @@ __global__ __launch_bounds__(FT) void out_fwd_bf16_kernel(
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) fb[ks][tt] = frag_rows(bt, tj + 16 * tt, 4 * ks, ar16);
       sched_ds_reads<2 * FKN>();
+      f4 cb[2];
+      zero(cb);
 #pragma unroll
       for (int ks = 0; ks < FKN; ++ks)
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt) cbk[jb][tt] = mfma(cfr[ks], fb[ks][tt], cbk[jb][tt]);
+        for (int tt = 0; tt < 2; ++tt) cb[tt] = mfma(cfr[ks], fb[ks][tt], cb[tt]);
       sched_mfmas<2 * FKN>();
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) cbk[jb][tt] = u32x2{pack_bf16(cb[tt][0], cb[tt][1]), pack_bf16(cb[tt][2], cb[tt][3])};
     }
   }
+  lds_barrier();  // the B slots are free for the x, strip and y tiles
   fwd_scan_store(sDtb, -__expf(A_log[head(0)]), sS[0], sDt[0]);
   __syncthreads();
 
@@ -257,8 +268,10 @@ __global__ __launch_bounds__(FT) void out_fwd_bf16_kernel(
         // this lane's first column j, taken as computed here (clamps and masks
         // made in the step, not hoisted into spilled registers)
         const int jb0 = opaque_index(j0 + tj + r);
-        cbt[0] = cbk[jb][0];
-        cbt[1] = cbk[jb][1];
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) cbt[tt][e] = acc_elem(cbk[jb][tt], e);
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
           const int jc = min(jb0 + 16 * tt, Q - 1);
@@ -325,16 +338,18 @@ __global__ __launch_bounds__(FT) void out_fwd_bf16_kernel(
       const RowsAt<16> ar16 = opaque(r16_);
 #pragma unroll
       for (int kh = 0; kh < FKN; kh += 2) {  // two k-steps per batch of reads
-        bf16x8 fb[2][2];
+        bf16x8 fb[2][2], fc[2];
 #pragma unroll
-        for (int d = 0; d < 2; ++d)
+        for (int d = 0; d < 2; ++d) {
+          fc[d] = frag_rows(sC, 16 * wt, 4 * (kh + d), ar16);
 #pragma unroll
           for (int k = 0; k < 2; ++k) fb[d][k] = frag_rows(sH, 16 * (2 * team + k), 4 * (kh + d), ar16);
-        sched_ds_reads<4>();
+        }
+        sched_ds_reads<6>();
 #pragma unroll
         for (int d = 0; d < 2; ++d)
 #pragma unroll
-          for (int k = 0; k < 2; ++k) yo[k] = mfma(cfr[kh + d], fb[d][k], yo[k]);
+          for (int k = 0; k < 2; ++k) yo[k] = mfma(fc[d], fb[d][k], yo[k]);
         sched_mfmas<4>();
       }
     }
