@@ -101,6 +101,25 @@ __device__ __forceinline__ void steps_async(lds_char* dst, const i32x4& rs, uint
   dma_u16(rs, dst + 256 * w, t < Q ? static_cast<uint32_t>(t) * stride : OOB_OFFSET);
 }
 
+// A buffer descriptor kept as its 64-bit base and built where it is used:
+// the base passes through an empty asm first, so that the compiler cannot
+// hoist the built descriptor (four SGPRs) out of the loops and keeps only the
+// base (two).  For kernels short of SGPRs, whose spills cost v_readlane /
+// v_writelane pairs in the loops.
+struct LazyRsrc {
+  const void* p;
+  __device__ __forceinline__ i32x4 get() const {
+    uint64_t a = reinterpret_cast<uint64_t>(p);
+    asm volatile("" : "+s"(a));
+    return i32x4{static_cast<int>(a), static_cast<int>((a >> 32) & 0xFFFFu), 0x7FFFFFF0, 0x00020000};
+  }
+  __device__ __forceinline__ __amdgpu_buffer_rsrc_t ptr() const {
+    uint64_t a = reinterpret_cast<uint64_t>(p);
+    asm volatile("" : "+s"(a));
+    return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(a), 0, 0x7FFFFFF0, 0x00020000);
+  }
+};
+
 // The same descriptor in the type the buffer-load builtins take.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc_ptr(const void* base) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0x7FFFFFF0, 0x00020000);

@@ -123,25 +123,23 @@ __global__ __launch_bounds__(FT) void bwd_fused_bf16_kernel(
   const uint32_t HPb = static_cast<uint32_t>(HP) * 2, GNb = static_cast<uint32_t>(GN) * 2;
   const uint32_t goff = static_cast<uint32_t>(g) * N * 2;
   const int pch = P >> 3, nch = N >> 3;
-  const i32x4 rx = make_rsrc(x + row0 * HP);
-  const i32x4 rdy = make_rsrc(dy + row0 * HP);
-  const i32x4 rb = make_rsrc(Bm + row0 * GN);
-  const i32x4 rc = make_rsrc(Cm + row0 * GN);
-  const i32x4 rg = make_rsrc(gamma + (static_cast<int64_t>(bi) * nc + c) * HP * N);
-  const i32x4 rh = make_rsrc(hbf + (static_cast<int64_t>(bi) * nc + c) * HP * N);
-  const __amdgpu_buffer_rsrc_t rdx = make_rsrc_ptr(dx + row0 * HP);
+  const LazyRsrc rx{x + row0 * HP};
+  const LazyRsrc rdy{dy + row0 * HP};
+  const LazyRsrc rb{Bm + row0 * GN};
+  const LazyRsrc rc{Cm + row0 * GN};
+  const LazyRsrc rg{gamma + (static_cast<int64_t>(bi) * nc + c) * HP * N};
+  const LazyRsrc rh{hbf + (static_cast<int64_t>(bi) * nc + c) * HP * N};
+  const LazyRsrc rdx{dx + row0 * HP};
   // the per-head sums of (bi, h = 0, c): [b, H, T]
   const int64_t sum0 = static_cast<int64_t>(bi) * H * T + static_cast<int64_t>(c) * Q;
   const int64_t bht = batch * H * T;
-  const __amdgpu_buffer_rsrc_t rcol = make_rsrc_ptr(s.colE + sum0);
-  const __amdgpu_buffer_rsrc_t rdiag = make_rsrc_ptr(s.diagE + sum0);
-  const __amdgpu_buffer_rsrc_t rrp = make_rsrc_ptr(s.Rp + sum0);
-  const __amdgpu_buffer_rsrc_t rdso = make_rsrc_ptr(s.dsoff + sum0);
+  const LazyRsrc rcol{s.colE + sum0};
+  const LazyRsrc rdiag{s.diagE + sum0};
+  const LazyRsrc rrp{s.Rp + sum0};
+  const LazyRsrc rdso{s.dsoff + sum0};
   // dB and dC (or this head split's partials) from the chunk's first row and the group's columns
-  const __amdgpu_buffer_rsrc_t rdb =
-      make_rsrc_ptr(dB_out + static_cast<int64_t>(sp) * batch * T * GN + row0 * GN + static_cast<int64_t>(g) * N);
-  const __amdgpu_buffer_rsrc_t rdc =
-      make_rsrc_ptr(dC_out + static_cast<int64_t>(sp) * batch * T * GN + row0 * GN + static_cast<int64_t>(g) * N);
+  const LazyRsrc rdb{dB_out + static_cast<int64_t>(sp) * batch * T * GN + row0 * GN + static_cast<int64_t>(g) * N};
+  const LazyRsrc rdc{dC_out + static_cast<int64_t>(sp) * batch * T * GN + row0 * GN + static_cast<int64_t>(g) * N};
 
   // x and dy tiles (64 rows of headdim), Gamma and H_c (headdim rows of
   // d_state): per-lane offsets computed once, the tile's first row as the
@@ -162,16 +160,16 @@ __global__ __launch_bounds__(FT) void bwd_fused_bf16_kernel(
   // first head's state step)
   auto load_first_xdhd = [&](int jbp) {
     const int h0 = head_of(jbp, 0), jx0 = jbp * BQ, vjx = min(BQ, Q - jx0);
-    tl8.issue(sX, rx, jx0 * HPb + h0 * P * 2, vjx);
-    tl8.issue(sDy[0], rdy, jx0 * HPb + h0 * P * 2, vjx);
-    tlg.issue(sH, rh, h0 * P * N * 2, P);
+    tl8.issue(sX, rx.get(), jx0 * HPb + h0 * P * 2, vjx);
+    tl8.issue(sDy[0], rdy.get(), jx0 * HPb + h0 * P * 2, vjx);
+    tlg.issue(sH, rh.get(), h0 * P * N * 2, P);
     steps_async<FW>(lds_ptr(sDtb), make_rsrc(dt + row0 * H + h0), H * 2, Q);
   };
   auto load_first_b = [&](int jbp) {
     const int jx0 = jbp * BQ;
-    tile_async<64, 16, FW>(sB, rb, jx0 * GNb + goff, GNb, min(BQ, Q - jx0), nch);
+    tile_async<64, 16, FW>(sB, rb.get(), jx0 * GNb + goff, GNb, min(BQ, Q - jx0), nch);
   };
-  auto load_first_gam = [&](int jbp) { tlg.issue(sGam, rg, head_of(jbp, 0) * P * N * 2, P); };
+  auto load_first_gam = [&](int jbp) { tlg.issue(sGam, rg.get(), head_of(jbp, 0) * P * N * 2, P); };
 
   unsigned written = 0;  // blocks of dC an earlier pass has written
   // pass 0's first tiles and every block's C tile (later passes read a subset)
@@ -181,7 +179,7 @@ __global__ __launch_bounds__(FT) void bwd_fused_bf16_kernel(
   for (int u = 0; u < NBMAX; ++u) {
     if (u < nb) {
       const int i0 = u * BQ;
-      tile_async<64, 16, FW>(sCt + u * TILE_N, rc, i0 * GNb + goff, GNb, min(BQ, Q - i0), nch);
+      tile_async<64, 16, FW>(sCt + u * TILE_N, rc.get(), i0 * GNb + goff, GNb, min(BQ, Q - i0), nch);
     }
   }
   load_first_gam(0);
@@ -191,13 +189,13 @@ __global__ __launch_bounds__(FT) void bwd_fused_bf16_kernel(
     const int j0 = jb * BQ, vj = min(BQ, Q - j0);
     const int nib = nb - jb;
     auto load_dt_abs = [&](int h) { steps_async<FW>(lds_ptr(sDtb), make_rsrc(dt + row0 * H + h), H * 2, Q); };
-    auto load_x = [&](int hh) { tl8.issue(sX + (hh & 1) * TILE_P, rx, j0 * HPb + head(hh) * P * 2, vj); };
+    auto load_x = [&](int hh) { tl8.issue(sX + (hh & 1) * TILE_P, rx.get(), j0 * HPb + head(hh) * P * 2, vj); };
     auto load_dy = [&](int hh, int u, lds_char* dst) {
       const int i0 = (jb + u) * BQ;
-      tl8.issue(dst, rdy, i0 * HPb + head(hh) * P * 2, min(BQ, Q - i0));
+      tl8.issue(dst, rdy.get(), i0 * HPb + head(hh) * P * 2, min(BQ, Q - i0));
     };
-    auto load_gam = [&](int hh) { tlg.issue(sGam, rg, head(hh) * P * N * 2, P); };
-    auto load_h = [&](int hh) { tlg.issue(sH, rh, head(hh) * P * N * 2, P); };
+    auto load_gam = [&](int hh) { tlg.issue(sGam, rg.get(), head(hh) * P * N * 2, P); };
+    auto load_h = [&](int hh) { tlg.issue(sH, rh.get(), head(hh) * P * N * 2, P); };
     const __amdgpu_buffer_rsrc_t rrm = make_rsrc_ptr(s.rowM + static_cast<int64_t>(jb) * bht + sum0);
 
     // ---- the pass's first tiles (issued before the loop or during the
@@ -596,17 +594,17 @@ __global__ __launch_bounds__(FT) void bwd_fused_bf16_kernel(
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const bool ok = j0 + 16 * wt + 4 * qf + e < Q && 32 * team + 16 * k + rf < P;
-            store_f32(rdx, dxv[k][e], ok ? vdx + 64 * k : OOB_OFFSET, static_cast<uint32_t>(e * HP + h * P) * 4);
+            store_f32(rdx.ptr(), dxv[k][e], ok ? vdx + 64 * k : OOB_OFFSET, static_cast<uint32_t>(e * HP + h * P) * 4);
           }
         }
         if (team == 0) {
           const int jcf = 16 * wt + rf;
           const uint32_t vo = (qf == 0 && j0 + jcf < Q) ? static_cast<uint32_t>(j0 + jcf) * 4 : OOB_OFFSET;
           const uint32_t so4 = static_cast<uint32_t>(h) * T * 4;
-          store_f32(rcol, ce, vo, so4);
-          store_f32(rdiag, de, vo, so4);
-          store_f32(rrp, re, vo, so4);
-          store_f32(rdso, so, vo, so4);
+          store_f32(rcol.ptr(), ce, vo, so4);
+          store_f32(rdiag.ptr(), de, vo, so4);
+          store_f32(rrp.ptr(), re, vo, so4);
+          store_f32(rdso.ptr(), so, vo, so4);
         }
         // read by the last workgroup of this launch: stored at the device's coherence point
         if (w == 0 && l == 0)
@@ -649,7 +647,7 @@ __global__ __launch_bounds__(FT) void bwd_fused_bf16_kernel(
           dco[u][k][e] = 0.f;
           if (u < nib && ((written >> (jb + u)) & 1))
             dco[u][k][e] = __uint_as_float(
-                __builtin_amdgcn_raw_buffer_load_b32(rdc, gn_voff(r0, c0, e), gn_soff(r0, c0, e), 0));
+                __builtin_amdgcn_raw_buffer_load_b32(rdc.ptr(), gn_voff(r0, c0, e), gn_soff(r0, c0, e), 0));
         }
       }
     }
@@ -689,7 +687,7 @@ __global__ __launch_bounds__(FT) void bwd_fused_bf16_kernel(
         for (int k = 0; k < 4; ++k) {
           const int c0 = 16 * (4 * team + k);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) store_f32(rdc, dco[u][k][e] + pc[k][e], gn_voff(r0, c0, e), gn_soff(r0, c0, e));
+          for (int e = 0; e < 4; ++e) store_f32(rdc.ptr(), dco[u][k][e] + pc[k][e], gn_voff(r0, c0, e), gn_soff(r0, c0, e));
         }
       }
     }
@@ -720,7 +718,7 @@ __global__ __launch_bounds__(FT) void bwd_fused_bf16_kernel(
     for (int k = 0; k < 4; ++k) {
       const int c0 = 16 * (4 * team + k), r0 = j0 + 16 * wt;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) store_f32(rdb, dbp[k][e] + dbs[k][e], gn_voff(r0, c0, e), gn_soff(r0, c0, e));
+      for (int e = 0; e < 4; ++e) store_f32(rdb.ptr(), dbp[k][e] + dbs[k][e], gn_voff(r0, c0, e), gn_soff(r0, c0, e));
     }
     written |= ((1u << nb) - 1) & ~((1u << jb) - 1);  // blocks jb .. nb - 1
     if (jb + 1 < nb) {
@@ -759,10 +757,10 @@ __global__ __launch_bounds__(FT) void bwd_fused_bf16_kernel(
           // through the descriptors the passes stored with (their bases stay
           // in registers anyway): element (h, k) at byte (h T + k) 4
           const uint32_t vk = static_cast<uint32_t>(k) * 4, sh = static_cast<uint32_t>(h) * T * 4;
-          cE[e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rcol, vk, sh, 0));
-          rP[e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rrp, vk, sh, 0));
-          dE[e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rdiag, vk, sh, 0));
-          dS[e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rdso, vk, sh, 0));
+          cE[e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rcol.ptr(), vk, sh, 0));
+          rP[e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rrp.ptr(), vk, sh, 0));
+          dE[e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rdiag.ptr(), vk, sh, 0));
+          dS[e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rdso.ptr(), vk, sh, 0));
           for (int jb = 0; jb <= (k >> 6); ++jb) rM[e] += s.rowM[jb * bht + o0 + k];
           dv[e] = bf16_bits_to_f32(dt[(row0 + k) * H + h]);
         }
