@@ -130,11 +130,11 @@ __global__ __launch_bounds__(FT) __attribute__((amdgpu_waves_per_eu(4, 4))) void
   const uint32_t HPb = static_cast<uint32_t>(HP) * 2, GNb = static_cast<uint32_t>(GN) * 2;
   const uint32_t goff = static_cast<uint32_t>(g) * N * 2;
   const int pch = P >> 3, nch = N >> 3;
-  const i32x4 rx = make_rsrc(x + row0 * HP);
-  const i32x4 rb = make_rsrc(Bm + row0 * GN);
-  const i32x4 rc = make_rsrc(Cm + row0 * GN);
-  const i32x4 rh = make_rsrc(hbf + (static_cast<int64_t>(bi) * nc + c) * HP * N);
-  const __amdgpu_buffer_rsrc_t ry = make_rsrc_ptr(y + row0 * HP);
+  const LazyRsrc rx{x + row0 * HP};
+  const LazyRsrc rb{Bm + row0 * GN};
+  const LazyRsrc rc{Cm + row0 * GN};
+  const LazyRsrc rh{hbf + (static_cast<int64_t>(bi) * nc + c) * HP * N};
+  const LazyRsrc ry{y + row0 * HP};
   auto head = [&](int hh) { return g * hpg + sp * hps + hh; };
 
   // the dt series of head hh to LDS (one copy instruction per wave; no load
@@ -146,14 +146,14 @@ __global__ __launch_bounds__(FT) __attribute__((amdgpu_waves_per_eu(4, 4))) void
   // registers)
   auto load_x = [&](int hh, int jb, lds_char* dst) {
     const int j0 = jb * BQ;
-    tile_issue_fresh<64, 8, FW>(dst, rx, HPb, pch, j0 * HPb + head(hh) * P * 2, min(BQ, Q - j0));
+    tile_issue_fresh<64, 8, FW>(dst, rx.get(), HPb, pch, j0 * HPb + head(hh) * P * 2, min(BQ, Q - j0));
   };
-  auto load_h = [&](int hh) { tile_issue_fresh<64, 16, FW>(sH, rh, N * 2, nch, head(hh) * P * N * 2, P); };
+  auto load_h = [&](int hh) { tile_issue_fresh<64, 16, FW>(sH, rh.get(), N * 2, nch, head(hh) * P * N * 2, P); };
   // C rows, the first head's first x, H_c and dt for row block ix (this
   // pass's, or the next pass's while this one finishes)
   auto load_first = [&](int ix) {
     const int ix0 = ix * BQ, vix = min(BQ, Q - ix0);
-    tile_async<64, 16, FW>(sC, rc, ix0 * GNb + goff, GNb, vix, nch);
+    tile_async<64, 16, FW>(sC, rc.get(), ix0 * GNb + goff, GNb, vix, nch);
     load_x(0, 0, sX[0]);
     load_h(0);
     load_dt(0);
@@ -164,7 +164,7 @@ __global__ __launch_bounds__(FT) __attribute__((amdgpu_waves_per_eu(4, 4))) void
     for (int t = 0; t < 2; ++t) {
       if (jp + t < nj) {
         const int j0 = (jp + t) * BQ;
-        tile_async<64, 16, FW>(sBslot[t], rb, j0 * GNb + goff, GNb, min(BQ, Q - j0), nch);
+        tile_async<64, 16, FW>(sBslot[t], rb.get(), j0 * GNb + goff, GNb, min(BQ, Q - j0), nch);
       }
     }
   };
@@ -384,7 +384,7 @@ __global__ __launch_bounds__(FT) __attribute__((amdgpu_waves_per_eu(4, 4))) void
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const bool ok = i0 + 16 * wt + 4 * q + e < Q && 32 * team + 16 * k + r < P;
-          store_b16(ry, yv[k][e], ok ? vy + 32 * k : OOB_OFFSET, static_cast<uint32_t>(e * HP + h * P) * 2);
+          store_b16(ry.ptr(), yv[k][e], ok ? vy + 32 * k : OOB_OFFSET, static_cast<uint32_t>(e * HP + h * P) * 2);
         }
       }
     }
