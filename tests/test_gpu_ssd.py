@@ -79,12 +79,24 @@ def test_f32_three_heads_per_group():
 
 
 def test_many_chunks_bf16():
-    # 256 chunks per head with 16-step chunks and a 32-wide d_state: the dt
-    # kernel's final workgroup sums 512 chunk partials per head (every other
-    # test has at most 64)
+    # 256 chunks per head with 16-step chunks and a 32-wide d_state: the final
+    # workgroup of the fused backward kernel sums 512 chunk partials per head
+    # (every other test has at most 64)
     cfg = SSDConfig("many", 2, 2048, 4, 64, 32, 2, 16, "bf16", init_state=True, seed=12)
     d = make_inputs(cfg)
     compare(gpu_ssd(cfg, d), oracle_ssd(d, cfg.chunk), TOL["bf16"], label="256 chunks per head, bf16")
+
+
+def test_many_heads_bf16():
+    # 520 heads in 40 groups of 13, two batch rows of four chunks: the fused
+    # backward kernel takes all 13 heads of a group per workgroup (its ddt
+    # epilogue in two rounds of eight heads), and the last workgroup's dA_log
+    # and dD sums run over more heads than its 512 threads (two rounds)
+    cfg = SSDConfig("many_heads", 2, 1024, 520, 8, 8, 40, 256, "bf16", init_state=True, seed=41)
+    d = make_inputs(cfg)
+    got = gpu_ssd(cfg, d)
+    ref = oracle_ssd(d, cfg.chunk)
+    compare(got, ref, TOL["bf16"], label="many heads")
 
 
 @pytest.mark.parametrize("dtype,saved", [("f32", True), ("bf16", False), ("bf16", True)])
