@@ -33,6 +33,7 @@ typedef __attribute__((address_space(3))) char lds_char;
 typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef short short8_t __attribute__((ext_vector_type(8)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 // Byte offsets at or beyond this value are out of every descriptor's range.
@@ -385,6 +386,16 @@ __device__ __forceinline__ void store_f32(__amdgpu_buffer_rsrc_t rs, float v, ui
 }
 __device__ __forceinline__ void store_b16(__amdgpu_buffer_rsrc_t rs, uint16_t v, uint32_t voff, uint32_t soff) {
   __builtin_amdgcn_raw_buffer_store_b16(v, rs, voff, soff, 0);
+}
+// Four consecutive floats at a 16-byte aligned offset as one 16-byte store.
+__device__ __forceinline__ void store_f32x4(__amdgpu_buffer_rsrc_t rs, const f4& v, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs, voff, soff, 0);
+}
+// Eight consecutive floats rounded to bf16 as one 16-byte store.
+__device__ __forceinline__ void store_bf16x8(__amdgpu_buffer_rsrc_t rs, const float4& a, const float4& b,
+                                             uint32_t voff, uint32_t soff) {
+  const u32x4 v = {pack_bf16(a.x, a.y), pack_bf16(a.z, a.w), pack_bf16(b.x, b.y), pack_bf16(b.z, b.w)};
+  __builtin_amdgcn_raw_buffer_store_b128(v, rs, voff, soff, 0);
 }
 
 // One element (row, col) of a swizzled tile, as f32.

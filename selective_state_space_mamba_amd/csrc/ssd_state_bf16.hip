@@ -12,7 +12,12 @@
 //
 // A workgroup owns 32 headdim rows of one (batch, head); wave w holds rows
 // p0 + 16 (w % 2) .. +15 and d_state columns 32 (w / 2) .. +31 of the state
-// in registers and walks the chunks in order (or in reverse).  Per chunk the
+// in registers and walks the chunks in order (or in reverse).  The MFMAs
+// produce the state transposed (d_state along the accumulator rows), so a
+// lane holds four consecutive d_state columns of one headdim row; at a chunk
+// end the wave passes its part through a private LDS area and stores it in
+// whole 128-byte rows, 16 bytes a lane (the state stores were the kernel's
+// largest cost as 4-byte and 2-byte stores).  Per chunk the
 // weighted sum is one MFMA contraction over time: the x (or dy) tile arrives
 // with time along its rows, is scaled in place by the per-step weights (one
 // 16-byte chunk per thread, once for the four waves that read each row) and
@@ -35,6 +40,7 @@ constexpr int SPB = 32;            // headdim rows per workgroup
 constexpr int XSLAB = SSJ * 64;    // bytes of a 128 x 32 bf16 slab
 constexpr int BSLAB = SSJ * 256;   // bytes of a 128 x 128 bf16 slab
 constexpr int HTILE = SPB * 512;   // bytes of a 32 x 128 f32 state tile
+constexpr int SROW = 36;           // floats per staged state row
 
 // Sum over all 64 lanes of the wave (the row sums end in lanes 15, 31, 47, 63).
 __device__ __forceinline__ float wave_total(float v) {
@@ -67,6 +73,10 @@ __global__ __launch_bounds__(ST) void chunk_state_bf16_kernel(
   __shared__ __attribute__((aligned(16))) float sWt[SW][QMAX];                // per-wave step weights
   __shared__ __attribute__((aligned(16))) uint32_t sDtb[2][QMAX];             // dt bits of a chunk, two chunks
   __shared__ float sGh[2][SW];
+  // each wave's 16 x 32 part of the state, row-major with rows padded to 36
+  // floats (the 16 rows of a 16-byte write fall in distinct banks), to store
+  // it in whole 128-byte rows
+  __shared__ __attribute__((aligned(16))) float sStage[SW][16 * SROW];
   lds_char* const sX = lds_ptr(sX_);
   lds_char* const sB = lds_ptr(sB_);
   lds_char* const sH = lds_ptr(sH_);
@@ -91,12 +101,12 @@ __global__ __launch_bounds__(ST) void chunk_state_bf16_kernel(
   const int pch = min(4, (P - p0) >> 3), nch = N >> 3;
   float* const wts = sWt[w];
 
-  f4 st[2];  // rows p = p0 + 16 pw + 4q + e, columns n = 32 nw + 16 t + r
+  f4 st[2];  // row p = p0 + 16 pw + r, columns n = 32 nw + 16 t + 4q + e
 #pragma unroll
   for (int t = 0; t < 2; ++t)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int p = p0 + 16 * pw + 4 * q + e, n = 32 * nw + 16 * t + r;
+      const int p = p0 + 16 * pw + r, n = 32 * nw + 16 * t + 4 * q + e;
       st[t][e] = (init && p < P && n < N) ? init[(static_cast<int64_t>(bi) * H + h) * PN + p * N + n] : 0.f;
     }
 
@@ -205,12 +215,12 @@ __global__ __launch_bounds__(ST) void chunk_state_bf16_kernel(
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-          for (int t = 0; t < 2; ++t) acc[t] = mfma(xa[ks], bb[ks][t], acc[t]);
+          for (int t = 0; t < 2; ++t) acc[t] = mfma(bb[ks][t], xa[ks], acc[t]);
       } else {
         for (int k0 = 0; k0 < kw; k0 += 32) {
           const bf16x8 ax = frag_cols<4>(xs, k0, 16 * pw);
 #pragma unroll
-          for (int t = 0; t < 2; ++t) acc[t] = mfma(ax, frag_cols<16>(bs, k0, 32 * nw + 16 * t), acc[t]);
+          for (int t = 0; t < 2; ++t) acc[t] = mfma(frag_cols<16>(bs, k0, 32 * nw + 16 * t), ax, acc[t]);
         }
       }
     }
@@ -220,29 +230,53 @@ __global__ __launch_bounds__(ST) void chunk_state_bf16_kernel(
     const int64_t sbase = ((static_cast<int64_t>(bi) * nc + c) * H + h) * PN;
     const float* ht = reinterpret_cast<const float*>(sH_ + (it & 1) * HTILE);
     float gh = 0.f;
-    // element (p, n) of the chunk's state at byte (p N + n) * size; invalid
-    // elements get an out-of-range offset and their stores are dropped
+    // elements (p, n0 ..) of the chunk's state at byte (p N + n0) * size (N
+    // is a multiple of 8, so a lane's 4 or 8 are valid together); invalid
+    // ones get an out-of-range offset and their stores are dropped
     const __amdgpu_buffer_rsrc_t rsf = make_rsrc_opt(!REV && states_f32 ? states_f32 + sbase : nullptr);
     const __amdgpu_buffer_rsrc_t rsb = make_rsrc_opt(states_bf ? states_bf + sbase : nullptr);
     const __amdgpu_buffer_rsrc_t rhb = make_rsrc_opt(hbf_out ? hbf_out + sbase : nullptr);
+    // the wave's part (rows 16 pw + i, columns 32 nw + j) to its staging
+    // area; the same wave reads it back (LDS accesses of a wave are in order)
+    float* const stg = sStage[w];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+      *reinterpret_cast<float4*>(stg + r * SROW + 16 * t + 4 * q) = make_float4(st[t][0], st[t][1], st[t][2], st[t][3]);
+    if constexpr (!REV) {
+      // f32: rows i = l / 8 (+ 8), four columns j = 4 (l % 8) a lane
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int i = (l >> 3) + 8 * u, j = 4 * (l & 7), p = p0 + 16 * pw + i, n0 = 32 * nw + j;
+        const float4 v = *reinterpret_cast<const float4*>(stg + i * SROW + j);
+        const f4 vv = {v.x, v.y, v.z, v.w};
+        store_f32x4(rsf, vv, p < P && n0 < N ? static_cast<uint32_t>(p * N + n0) * 4 : OOB_OFFSET, 0);
+      }
+    }
+    {
+      // bf16: row i = l / 4, eight columns j = 8 (l % 4) a lane
+      const int i = l >> 2, j = 8 * (l & 3), p = p0 + 16 * pw + i, n0 = 32 * nw + j;
+      const bool ok = p < P && n0 < N;
+      const uint32_t eo = ok ? static_cast<uint32_t>(p * N + n0) * 2 : OOB_OFFSET;
+      const float4 a = *reinterpret_cast<const float4*>(stg + i * SROW + j);
+      const float4 b = *reinterpret_cast<const float4*>(stg + i * SROW + j + 4);
+      if constexpr (!REV) {
+        if (states_bf) store_bf16x8(rsb, a, b, eo, 0);
+      } else {
+        // H_c at the same elements (tile rows are 128 floats)
+        float4 ha = make_float4(0.f, 0.f, 0.f, 0.f), hb = ha;
+        if (ok) {
+          ha = *reinterpret_cast<const float4*>(ht + (16 * pw + i) * NMAX + n0);
+          hb = *reinterpret_cast<const float4*>(ht + (16 * pw + i) * NMAX + n0 + 4);
+        }
+        store_bf16x8(rsb, a, b, eo, 0);
+        gh += a.x * ha.x + a.y * ha.y + a.z * ha.z + a.w * ha.w + b.x * hb.x + b.y * hb.y + b.z * hb.z + b.w * hb.w;
+        if (hbf_out) store_bf16x8(rhb, ha, hb, eo, 0);
+      }
+    }
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int pl = 16 * pw + 4 * q + e, p = p0 + pl, n = 32 * nw + 16 * t + r;
-        const bool ok = p < P && n < N;
-        const uint32_t eo = static_cast<uint32_t>(p * N + n);
-        if constexpr (!REV) {
-          store_f32(rsf, st[t][e], ok ? eo * 4 : OOB_OFFSET, 0);
-          if (states_bf) store_b16(rsb, f32_to_bf16_bits(st[t][e]), ok ? eo * 2 : OOB_OFFSET, 0);
-        } else {
-          const float hv = ok ? ht[pl * NMAX + n] : 0.f;  // tile rows are 128 floats
-          store_b16(rsb, f32_to_bf16_bits(st[t][e]), ok ? eo * 2 : OOB_OFFSET, 0);
-          gh += st[t][e] * hv;
-          if (hbf_out) store_b16(rhb, f32_to_bf16_bits(hv), ok ? eo * 2 : OOB_OFFSET, 0);
-        }
-        st[t][e] = decay * st[t][e] + acc[t][e];
-      }
+      for (int e = 0; e < 4; ++e) st[t][e] = decay * st[t][e] + acc[t][e];
     if constexpr (REV) {
       // per 16-row headdim block (waves with the same pw), summed after the next barrier
       gh = wave_total(gh);
@@ -268,12 +302,12 @@ __global__ __launch_bounds__(ST) void chunk_state_bf16_kernel(
   }
   if (last_out) {
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int p = p0 + 16 * pw + 4 * q + e, n = 32 * nw + 16 * t + r;
-        if (p < P && n < N) last_out[(static_cast<int64_t>(bi) * H + h) * PN + p * N + n] = st[t][e];
-      }
+    for (int t = 0; t < 2; ++t) {
+      const int p = p0 + 16 * pw + r, n0 = 32 * nw + 16 * t + 4 * q;
+      if (p < P && n0 < N)
+        *reinterpret_cast<float4*>(last_out + (static_cast<int64_t>(bi) * H + h) * PN + p * N + n0) =
+            make_float4(st[t][0], st[t][1], st[t][2], st[t][3]);
+    }
   }
 }
 
