@@ -59,6 +59,10 @@ __device__ __forceinline__ void fwd_scan_store(const uint32_t* dtb_lds, float A,
   }
 }
 
+// bf16 per staged y row: 32 columns and 8 of padding (the 16-byte rows of
+// four lanes' writes fall in distinct banks; 80 bytes keeps rows 16-byte aligned)
+constexpr int YROW = 40;
+
 // Two MFMA tiles (lane element e at row 4q + e, column 16 tt + r) into a wave
 // strip as bf16 [column][row] (32 x 16).
 __device__ __forceinline__ void fwd_put_strip(lds_char* strip, const f4 (&v)[2]) {
@@ -376,17 +380,24 @@ __global__ __launch_bounds__(FT) __attribute__((amdgpu_waves_per_eu(4, 4))) void
     // during the next step
     if (hh + 1 < hps) wait_vm<2>();
     // y (element (iq, p) at byte (iq HP + h P + p) 2 from the chunk's first
-    // row); out-of-range offsets are dropped
+    // row) through this wave's two exchange slots, read above and untouched
+    // by other waves until the next head's exchange, after the barrier
+    // below: the wave's 16 rows x 32 columns row-major (rows padded to YROW
+    // bf16), then 16 bytes a lane (row l / 4, columns 8 (l % 4) ..) as one
+    // store (P is a multiple of 8, so a lane's eight are valid together);
+    // out-of-range offsets are dropped
     {
-      const uint32_t vy = (static_cast<uint32_t>(i0 + 16 * wt + 4 * q) * HP + 32 * team + r) * 2;
+      __attribute__((address_space(3))) uint16_t* const stg =
+          reinterpret_cast<__attribute__((address_space(3))) uint16_t*>(sXch + (wt * 4 + 2 * team) * WAVE * 16);
 #pragma unroll
-      for (int k = 0; k < 2; ++k) {
+      for (int k = 0; k < 2; ++k)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const bool ok = i0 + 16 * wt + 4 * q + e < Q && 32 * team + 16 * k + r < P;
-          store_b16(ry.ptr(), yv[k][e], ok ? vy + 32 * k : OOB_OFFSET, static_cast<uint32_t>(e * HP + h * P) * 2);
-        }
-      }
+        for (int e = 0; e < 4; ++e) stg[(4 * q + e) * YROW + 16 * k + r] = yv[k][e];
+      const int iy = l >> 2, jy = 8 * (l & 3);
+      const u32x4 v = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(stg + iy * YROW + jy);
+      const bool ok = i0 + 16 * wt + iy < Q && 32 * team + jy < P;
+      const uint32_t vo = (static_cast<uint32_t>(i0 + 16 * wt + iy) * HP + h * P + 32 * team + jy) * 2;
+      __builtin_amdgcn_raw_buffer_store_b128(v, ry.ptr(), ok ? vo : OOB_OFFSET, 0, 0);
     }
     if (hh + 1 < hps) fwd_scan_store(sDtb, -__expf(An), sS[hb ^ 1], sDt[hb ^ 1]);
     lds_barrier();
