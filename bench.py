@@ -93,6 +93,20 @@ def method_bytes(cfg, kernel: str) -> float:
     return per_token[kernel] * cfg.batch * cfg.seqlen
 
 
+# The saved state history a step keeps between its forward and backward: in
+# bf16 (ssd_fwd_ex / ssd_bwd_ex) for problems the bf16 kernels run, which read
+# the states only in bf16; --f32-history keeps the f32 one instead.
+F32_HISTORY = False
+
+
+def bf16_family(cfg) -> bool:
+    return cfg.dtype == "bf16" and cfg.headdim % 8 == 0 and cfg.dstate % 8 == 0
+
+
+def bf16_history(cfg) -> bool:
+    return bf16_family(cfg) and not F32_HISTORY
+
+
 def algorithmic_bytes(cfg, kernel: str) -> float:
     """Bytes one launch must move at minimum counting its intermediates too:
     each input it needs read once and each output written once, at the storage
@@ -103,10 +117,19 @@ def algorithmic_bytes(cfg, kernel: str) -> float:
     HP, GN, H = cfg.nheads * cfg.headdim, cfg.ngroups * cfg.dstate, cfg.nheads
     st = H * cfg.headdim * cfg.dstate * 4 / cfg.chunk  # chunk states per token (f32)
     sg = H * cfg.headdim * cfg.dstate * s_a / cfg.chunk  # state gradients per token (operand dtype)
+    # the chunk states each kernel writes or reads: the bf16 family's output
+    # and fused kernels read the bf16 copy (st / 2); with the bf16 history the
+    # forward pass writes only that copy and the reverse pass reads no states,
+    # with the f32 one the forward writes both and the reverse pass reads the
+    # f32 states and writes the bf16 copy
+    if bf16_family(cfg):
+        st_fwd, st_out, st_rev = (st / 2, st / 2, 0.0) if bf16_history(cfg) else (1.5 * st, st / 2, 1.5 * st)
+    else:
+        st_fwd = st_out = st_rev = st
     per_token = {
-        "chunk_state_fwd": HP * s_a + GN * s_a + H * s_a + st,
-        "chunk_out_fwd": HP * s_a + 2 * GN * s_a + H * s_a + st + HP * s_a,
-        "chunk_state_bwd": HP * s_y + GN * s_a + H * s_a + st + sg,
+        "chunk_state_fwd": HP * s_a + GN * s_a + H * s_a + st_fwd,
+        "chunk_out_fwd": HP * s_a + 2 * GN * s_a + H * s_a + st_out + HP * s_a,
+        "chunk_state_bwd": HP * s_y + GN * s_a + H * s_a + st_rev + sg,
         "chunk_bwd_col": HP * s_a + 2 * GN * s_a + H * s_a + HP * s_y + sg + HP * 4 + GN * 4 + 3 * H * 4,
         "chunk_bwd_row": HP * s_a + 2 * GN * s_a + H * s_a + HP * s_y + st + GN * 4 + 2 * H * 4,
         # + Gamma and the bf16 states in; the per-head column sums, diagonal,
@@ -347,21 +370,25 @@ def make_step(cfg, d):
     dy = to_dev(d["dy"])
     f32 = dict(dtype=torch.float32, device="cuda")
     b, T, H, P, N, G, Q = cfg.batch, cfg.seqlen, cfg.nheads, cfg.headdim, cfg.dstate, cfg.ngroups, cfg.chunk
+    hist = "chunk_states_bf16" if bf16_history(cfg) else "chunk_states"
     fo = {"y": torch.empty_like(x), "final_state": torch.empty((b, H, P, N), **f32),
-          "chunk_states": torch.empty((b, T // Q, H, P, N), **f32)}
+          hist: torch.empty((b, T // Q, H, P, N), dtype=torch.bfloat16 if bf16_history(cfg) else torch.float32,
+                            device="cuda")}
     go = {"dx": torch.empty((b, T, H, P), **f32), "ddt": torch.empty((b, T, H), **f32),
           "dA_log": torch.empty(H, **f32), "dB": torch.empty((b, T, G, N), **f32),
           "dC": torch.empty((b, T, G, N), **f32), "dD": torch.empty(H, **f32),
           "d_init_state": torch.empty((b, H, P, N), **f32)}
     if not cfg.shell:
         prob = ssd._binding.make_problem(x, B, Q, dy.dtype)
-        wsf = torch.empty(max(1, ssd.ssd_workspace_bytes(prob, False, True)), dtype=torch.uint8, device="cuda")
-        wsb = torch.empty(max(1, ssd.ssd_workspace_bytes(prob, True, True)), dtype=torch.uint8, device="cuda")
+        f32h = hist == "chunk_states"
+        wsf = torch.empty(max(1, ssd.ssd_workspace_bytes(prob, False, f32h)), dtype=torch.uint8, device="cuda")
+        wsb = torch.empty(max(1, ssd.ssd_workspace_bytes(prob, True, f32h)), dtype=torch.uint8, device="cuda")
 
         def step():
-            ssd.ssd_fwd(x, dt, A_log, B, C, D, h0, chunk=Q, out=fo, workspace=wsf)
-            ssd.ssd_bwd(x, dt, A_log, B, C, D, dy, h0, chunk_states=fo["chunk_states"], chunk=Q, out=go,
-                        workspace=wsb)
+            ssd.ssd_fwd_ex(x, dt, A_log, B, C, D, h0, chunk=Q, want_chunk_states=f32h, want_chunk_states_bf16=not f32h,
+                           out=fo, workspace=wsf)
+            ssd.ssd_bwd(x, dt, A_log, B, C, D, dy, h0, chunk_states=fo.get("chunk_states"),
+                        chunk_states_bf16=fo.get("chunk_states_bf16"), chunk=Q, out=go, workspace=wsb)
         return step
 
     if cfg.d_model:
@@ -374,8 +401,9 @@ def make_step(cfg, d):
     K = conv_w.shape[1]
     u8 = dict(dtype=torch.uint8, device="cuda")
     prob = ssd._binding.make_problem(x.view(b, T, H, P), B, Q, torch.bfloat16)
-    wsf = torch.empty(max(1, ssd.ssd_workspace_bytes(prob, False, True)), **u8)
-    wsb = torch.empty(max(1, ssd.ssd_workspace_bytes(prob, True, True)), **u8)
+    f32h = hist == "chunk_states"
+    wsf = torch.empty(max(1, ssd.ssd_workspace_bytes(prob, False, f32h)), **u8)
+    wsb = torch.empty(max(1, ssd.ssd_workspace_bytes(prob, True, f32h)), **u8)
     wsr = torch.empty(max(1, lib.mamba2_rmsnorm_gated_bwd_workspace_bytes(b * T, di)), **u8)
     wsc = torch.empty(max(1, lib.mamba2_conv1d_silu_bwd_workspace_bytes(b, T, di, G, N, K)), **u8)
     wsd = torch.empty(max(1, lib.ssd_dt_softplus_bwd_workspace_bytes(b * T, H)), **u8)
@@ -385,12 +413,14 @@ def make_step(cfg, d):
         ssd.dt_softplus_fwd(dt_raw, dt_bias, out=dt)
         xs, Bs, Cs = ssd.conv1d_silu_fwd(xbc, conv_w, conv_b, di, G, N)
         xs = xs.view(b, T, H, P)
-        y, _, cs = ssd.ssd_fwd(xs, dt, A_log, Bs, Cs, D, h0, chunk=Q, out=fo, workspace=wsf)
+        r = ssd.ssd_fwd_ex(xs, dt, A_log, Bs, Cs, D, h0, chunk=Q, want_chunk_states=f32h,
+                           want_chunk_states_bf16=not f32h, out=fo, workspace=wsf)
+        y = r["y"]
         out, inv = ssd.rmsnorm_gated_fwd(y.view(b, T, di), z, norm_w, cfg.norm_eps)
         gy, gz, gw = ssd.rmsnorm_gated_bwd(y.view(b, T, di), z, norm_w, inv, gout, workspace=wsr,
                                            dy_dtype=torch.bfloat16)
-        g = ssd.ssd_bwd(xs, dt, A_log, Bs, Cs, D, gy.view(b, T, H, P), h0, chunk_states=cs, chunk=Q, out=go,
-                        workspace=wsb)
+        g = ssd.ssd_bwd(xs, dt, A_log, Bs, Cs, D, gy.view(b, T, H, P), h0, chunk_states=r["chunk_states"],
+                        chunk_states_bf16=r["chunk_states_bf16"], chunk=Q, out=go, workspace=wsb)
         ssd.conv1d_silu_bwd(xbc, conv_w, conv_b, g["dx"].view(b, T, di), g["dB"], g["dC"], di, G, N,
                             workspace=wsc)
         ssd.dt_softplus_bwd(dt_raw, dt_bias, g["ddt"], workspace=wsd)
@@ -416,8 +446,10 @@ def make_train_step(cfg, d):
     z, xbc, raw = torch.empty((M, di), **bf), torch.empty((M, cd), **bf), torch.empty((M, H), **bf)
     dt = torch.empty((M, H), **bf)
     o = torch.empty((M, dm), **bf)
+    f32h = not bf16_history(cfg)
+    hist = "chunk_states" if f32h else "chunk_states_bf16"
     fo = {"y": torch.empty((b, T, H, P), **bf), "final_state": torch.empty((b, H, P, N), **f32),
-          "chunk_states": torch.empty((b, T // Q, H, P, N), **f32)}
+          hist: torch.empty((b, T // Q, H, P, N), **(f32 if f32h else bf))}
     go_ = {"dx": torch.empty((b, T, H, P), **f32), "ddt": torch.empty((b, T, H), **f32),
            "dA_log": torch.empty(H, **f32), "dB": torch.empty((b, T, G, N), **f32),
            "dC": torch.empty((b, T, G, N), **f32), "dD": torch.empty(H, **f32)}
@@ -426,8 +458,8 @@ def make_train_step(cfg, d):
     du = torch.empty((M, dm), **f32)
     gz_bf, gx_bf, gd_bf = torch.empty((M, di), **bf), torch.empty((M, cd), **bf), torch.empty((M, H), **bf)
     prob = ssd._binding.make_problem(fo["y"], to_dev(d["B"]), Q, torch.bfloat16)
-    wsf = torch.empty(max(1, ssd.ssd_workspace_bytes(prob, False, True)), **u8)
-    wsb = torch.empty(max(1, ssd.ssd_workspace_bytes(prob, True, True)), **u8)
+    wsf = torch.empty(max(1, ssd.ssd_workspace_bytes(prob, False, f32h)), **u8)
+    wsb = torch.empty(max(1, ssd.ssd_workspace_bytes(prob, True, f32h)), **u8)
     wsr = torch.empty(max(1, lib.mamba2_rmsnorm_gated_bwd_workspace_bytes(M, di)), **u8)
     wsc = torch.empty(max(1, lib.mamba2_conv1d_silu_bwd_workspace_bytes(b, T, di, G, N, conv_w.shape[1])), **u8)
     wsd = torch.empty(max(1, lib.ssd_dt_softplus_bwd_workspace_bytes(M, H)), **u8)
@@ -440,7 +472,9 @@ def make_train_step(cfg, d):
         xs, Bs, Cs = ssd.conv1d_silu_fwd(xbc.view(b, T, cd), conv_w, conv_b, di, G, N)
         xs = xs.view(b, T, H, P)
         dt3 = dt.view(b, T, H)
-        y, _, cs = ssd.ssd_fwd(xs, dt3, A_log, Bs, Cs, D, None, chunk=Q, out=fo, workspace=wsf)
+        r = ssd.ssd_fwd_ex(xs, dt3, A_log, Bs, Cs, D, None, chunk=Q, want_chunk_states=f32h,
+                           want_chunk_states_bf16=not f32h, out=fo, workspace=wsf)
+        y = r["y"]
         out, inv = ssd.rmsnorm_gated_fwd(y.view(b, T, di), z.view(b, T, di), norm_w, cfg.norm_eps)
         ssd.gemm(out.view(M, di), Wo, trans_b=True, out=o)
         # backward
@@ -448,7 +482,8 @@ def make_train_step(cfg, d):
         ssd.gemm(go2, out.view(M, di), trans_a=True, out=dWo)
         gy, gz, gw = ssd.rmsnorm_gated_bwd(y.view(b, T, di), z.view(b, T, di), norm_w, inv, gact.view(b, T, di),
                                            workspace=wsr, dy_dtype=torch.bfloat16)
-        g = ssd.ssd_bwd(xs, dt3, A_log, Bs, Cs, D, gy.view(b, T, H, P), None, chunk_states=cs, chunk=Q, out=go_,
+        g = ssd.ssd_bwd(xs, dt3, A_log, Bs, Cs, D, gy.view(b, T, H, P), None, chunk_states=r["chunk_states"],
+                        chunk_states_bf16=r["chunk_states_bf16"], chunk=Q, out=go_,
                         workspace=wsb, want_d_init_state=False)
         dxbc, _, _ = ssd.conv1d_silu_bwd(xbc.view(b, T, cd), conv_w, conv_b, g["dx"].view(b, T, di), g["dB"],
                                          g["dC"], di, G, N, workspace=wsc)
@@ -550,6 +585,8 @@ def main():
     ap.add_argument("--workload", default="grouped",
                     choices=["tiny", "m130", "grouped", "long", "block", "block_train"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--f32-history", action="store_true",
+                    help="keep the saved state history in f32 (default for bf16 problems: bf16, ssd_fwd_ex / ssd_bwd_ex)")
     ap.add_argument("--cpu-batches", type=int, default=0, help="batch rows in the oracle sample (0: workload default)")
     ap.add_argument("--calibrate-copy-mb", type=int, default=0,
                     help="after timing, run a plain device copy of this many MiB (3 times) for counter calibration")
@@ -560,6 +597,8 @@ def main():
                     help="write the per-kernel MFMA utilisation summary from a rocprofv3 --pmc MfmaUtil "
                          "MfmaFlopsBF16 MfmaFlopsF32 run and exit")
     args = ap.parse_args()
+    global F32_HISTORY
+    F32_HISTORY = args.f32_history
     if args.mfma_summary:
         write_mfma_summary(args.mfma_summary, args.workload)
         return
@@ -651,7 +690,8 @@ def main():
                                 f"N={cfg.dstate} G={cfg.ngroups} chunk={cfg.chunk} {cfg.dtype}"
                                 + (" + conv1d/SiLU + RMSNorm-gated" if cfg.shell else "")
                                 + (f" + in/out projections d_model={cfg.d_model}" if cfg.d_model else "")),
-                   "global_batch": cfg.batch, "seq_len": cfg.seqlen, "parallelism": "single-gpu"},
+                   "global_batch": cfg.batch, "seq_len": cfg.seqlen, "parallelism": "single-gpu",
+                   "state_history": "bf16" if bf16_history(cfg) else "f32"},
         "kernel_ms": {k: round(v, 4) for k, v in kms.items()},
         "roofline": roofline,
         "ssd_bwd": ssd_bwd,

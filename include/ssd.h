@@ -95,6 +95,20 @@ int ssd_fwd(const ssd_problem* prob, const void* x, const void* dt, const float*
             float* final_state, float* chunk_states, void* workspace, size_t workspace_bytes,
             void* stream);
 
+/* ssd_fwd with a bf16 copy of the chunk states as a second, optional output
+ * (the same recurrence and reference as ssd_fwd).
+ *   chunk_states_bf16 [b,T/chunk,H,P,N] bf16 (round to nearest even of the
+ *     f32 states), nullable (output).  Only for problems the bf16 kernels run
+ *     (act_dtype SSD_BF16, headdim and dstate multiples of 8; SSD_ERR_INVALID_ARG
+ *     otherwise).  Half the size of chunk_states and all that the bf16
+ *     backward reads of the history: pass it to ssd_bwd_ex.
+ * Other arguments, results and errors as for ssd_fwd (ssd_fwd is this call
+ * with chunk_states_bf16 = NULL). */
+int ssd_fwd_ex(const ssd_problem* prob, const void* x, const void* dt, const float* A_log,
+               const void* B, const void* C, const float* D, const float* init_state, void* y,
+               float* final_state, float* chunk_states, void* chunk_states_bf16, void* workspace,
+               size_t workspace_bytes, void* stream);
+
 /* Backward of L = sum(dy * y) + sum(d_final_state * final_state).
  *   inputs as in ssd_fwd; dy [b,T,H,P] in dy_dtype
  *   d_final_state [b,H,P,N] f32, nullable (zeros): the gradient reaching the
@@ -111,6 +125,26 @@ int ssd_bwd(const ssd_problem* prob, const void* x, const void* dt, const float*
             const float* chunk_states, const void* dy, const float* d_final_state, float* dx,
             float* ddt, float* dA_log, float* dB, float* dC, float* dD, float* d_init_state,
             void* workspace, size_t workspace_bytes, void* stream);
+
+/* ssd_bwd taking the saved history in bf16 (the same gradients and reference
+ * as ssd_bwd).
+ *   chunk_states_bf16: nullable; when given it must be what ssd_fwd_ex wrote
+ *     for the same inputs (not checked), and only for problems the bf16
+ *     kernels run (act_dtype and dy_dtype SSD_BF16, headdim and dstate
+ *     multiples of 8; SSD_ERR_INVALID_ARG otherwise).  The fused bf16
+ *     backward then reads no f32 states (chunk_states may be NULL, and is
+ *     not read if given); the split form (SSD_BF16_BWD=split) ignores it and
+ *     uses chunk_states or recomputes.  The bf16 backward reads the states
+ *     only in bf16 in either case (its inner product <Gamma, H_c> and the
+ *     readout term take the bf16 copy).
+ * ssd_workspace_bytes(prob, 1, 0) is enough when only chunk_states_bf16 is
+ * given.  Other arguments, results and errors as for ssd_bwd (ssd_bwd is
+ * this call with chunk_states_bf16 = NULL). */
+int ssd_bwd_ex(const ssd_problem* prob, const void* x, const void* dt, const float* A_log,
+               const void* B, const void* C, const float* D, const float* init_state,
+               const float* chunk_states, const void* chunk_states_bf16, const void* dy,
+               const float* d_final_state, float* dx, float* ddt, float* dA_log, float* dB, float* dC,
+               float* dD, float* d_init_state, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ssd_bwd for callers that cannot allocate device memory: code under HIP
  * graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same

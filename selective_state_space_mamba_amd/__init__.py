@@ -28,6 +28,7 @@ from ._binding import (  # noqa: F401
     ssd_bwd_noalloc,
     NOALLOC_SCRATCH_BYTES,
     ssd_fwd,
+    ssd_fwd_ex,
     ssd_workspace_bytes,
     version,
 )

@@ -49,6 +49,10 @@ def load_library():
     lib.ssd_fwd.restype = ctypes.c_int
     lib.ssd_bwd.argtypes = [pp] + [vp] * 17 + [vp, sz, vp]
     lib.ssd_bwd.restype = ctypes.c_int
+    lib.ssd_fwd_ex.argtypes = [pp] + [vp] * 11 + [vp, sz, vp]
+    lib.ssd_fwd_ex.restype = ctypes.c_int
+    lib.ssd_bwd_ex.argtypes = [pp] + [vp] * 18 + [vp, sz, vp]
+    lib.ssd_bwd_ex.restype = ctypes.c_int
     lib.ssd_bwd_noalloc.argtypes = [pp] + [vp] * 17 + [vp]
     lib.ssd_bwd_noalloc.restype = ctypes.c_int
     lib.mamba2_conv1d_silu_fwd.argtypes = [i64] * 6 + [i32] + [vp] * 6 + [vp]
@@ -201,6 +205,25 @@ def ssd_fwd(x, dt, A_log, B, C, D, init_state=None, chunk: int = 256, want_chunk
     """SSD forward.  Returns (y, final_state, chunk_states); the last two are
     None when not requested.  `out` may hold preallocated y / final_state /
     chunk_states; `workspace` a preallocated uint8 device buffer."""
+    r = _fwd(x, dt, A_log, B, C, D, init_state, chunk, want_chunk_states, False, want_final_state, out, workspace,
+             stream)
+    return r["y"], r["final_state"], r["chunk_states"]
+
+
+def ssd_fwd_ex(x, dt, A_log, B, C, D, init_state=None, chunk: int = 256, want_chunk_states: bool = False,
+               want_chunk_states_bf16: bool = True, want_final_state: bool = True,
+               out: Optional[Dict[str, torch.Tensor]] = None, workspace: Optional[torch.Tensor] = None,
+               stream=None) -> Dict[str, Optional[torch.Tensor]]:
+    """ssd_fwd_ex: the forward with the chunk states also (or only) in bf16,
+    for problems the bf16 kernels run.  Returns a dict of y, final_state,
+    chunk_states (f32) and chunk_states_bf16, None for those not requested;
+    `out` may hold any of them preallocated."""
+    return _fwd(x, dt, A_log, B, C, D, init_state, chunk, want_chunk_states, want_chunk_states_bf16,
+                want_final_state, out, workspace, stream)
+
+
+def _fwd(x, dt, A_log, B, C, D, init_state, chunk, want_chunk_states, want_chunk_states_bf16, want_final_state,
+         out, workspace, stream) -> Dict[str, Optional[torch.Tensor]]:
     lib = load_library()
     b, T, H, P, N, G = _check_inputs(x, dt, A_log, B, C, D, init_state)
     prob = make_problem(x, B, chunk)
@@ -220,22 +243,30 @@ def ssd_fwd(x, dt, A_log, B, C, D, init_state=None, chunk: int = 256, want_chunk
         cs = torch.empty((b, nc, H, P, N), dtype=torch.float32, device=x.device)
     if cs is not None:
         _need(cs, "out['chunk_states']", (b, nc, H, P, N), torch.float32, x.device)
+    csb = out.get("chunk_states_bf16")
+    if csb is None and want_chunk_states_bf16:
+        csb = torch.empty((b, nc, H, P, N), dtype=torch.bfloat16, device=x.device)
+    if csb is not None:
+        _need(csb, "out['chunk_states_bf16']", (b, nc, H, P, N), torch.bfloat16, x.device)
     need = lib.ssd_workspace_bytes(ctypes.byref(prob), 0, int(cs is not None))
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
     wsz = _need_workspace(workspace, x.device)
-    _check(lib.ssd_fwd(ctypes.byref(prob), _ptr(x), _ptr(dt), _ptr(A_log), _ptr(B), _ptr(C), _ptr(D),
-                       _ptr(init_state), _ptr(y), _ptr(fin), _ptr(cs), _ptr(workspace), wsz, _stream(stream)))
-    return y, fin, cs
+    _check(lib.ssd_fwd_ex(ctypes.byref(prob), _ptr(x), _ptr(dt), _ptr(A_log), _ptr(B), _ptr(C), _ptr(D),
+                          _ptr(init_state), _ptr(y), _ptr(fin), _ptr(cs), _ptr(csb), _ptr(workspace), wsz,
+                          _stream(stream)))
+    return {"y": y, "final_state": fin, "chunk_states": cs, "chunk_states_bf16": csb}
 
 
 def ssd_bwd(x, dt, A_log, B, C, D, dy, init_state=None, chunk_states=None, chunk: int = 256,
             want_d_init_state: bool = True, out: Optional[Dict[str, torch.Tensor]] = None,
             workspace: Optional[torch.Tensor] = None, stream=None,
-            d_final_state: Optional[torch.Tensor] = None) -> Dict[str, torch.Tensor]:
+            d_final_state: Optional[torch.Tensor] = None,
+            chunk_states_bf16: Optional[torch.Tensor] = None) -> Dict[str, torch.Tensor]:
     """SSD backward of sum(dy * y) + sum(d_final_state * final_state).
     Returns dx, ddt, dA_log, dB, dC, dD (f32) and d_init_state (f32, or None
-    when not requested)."""
+    when not requested).  `chunk_states_bf16` is the bf16 history that
+    ssd_fwd_ex wrote (ssd_bwd_ex of the library)."""
     lib = load_library()
     b, T, H, P, N, G = _check_inputs(x, dt, A_log, B, C, D, init_state)
     if dy.dtype not in (torch.float32, torch.bfloat16):
@@ -245,6 +276,8 @@ def ssd_bwd(x, dt, A_log, B, C, D, dy, init_state=None, chunk_states=None, chunk
         _need(d_final_state, "d_final_state", (b, H, P, N), torch.float32, x.device)
     if chunk_states is not None:
         _need(chunk_states, "chunk_states", (b, T // chunk, H, P, N), torch.float32, x.device)
+    if chunk_states_bf16 is not None:
+        _need(chunk_states_bf16, "chunk_states_bf16", (b, T // chunk, H, P, N), torch.bfloat16, x.device)
     prob = make_problem(x, B, chunk, dy.dtype)
     out = dict(out or {})
     f32 = dict(dtype=torch.float32, device=x.device)
@@ -262,11 +295,11 @@ def ssd_bwd(x, dt, A_log, B, C, D, dy, init_state=None, chunk_states=None, chunk
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
     wsz = _need_workspace(workspace, x.device)
-    _check(lib.ssd_bwd(ctypes.byref(prob), _ptr(x), _ptr(dt), _ptr(A_log), _ptr(B), _ptr(C), _ptr(D),
-                       _ptr(init_state), _ptr(chunk_states), _ptr(dy), _ptr(d_final_state), _ptr(out["dx"]),
-                       _ptr(out["ddt"]),
-                       _ptr(out["dA_log"]), _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out["dD"]), _ptr(dinit),
-                       _ptr(workspace), wsz, _stream(stream)))
+    _check(lib.ssd_bwd_ex(ctypes.byref(prob), _ptr(x), _ptr(dt), _ptr(A_log), _ptr(B), _ptr(C), _ptr(D),
+                          _ptr(init_state), _ptr(chunk_states), _ptr(chunk_states_bf16), _ptr(dy),
+                          _ptr(d_final_state), _ptr(out["dx"]), _ptr(out["ddt"]), _ptr(out["dA_log"]),
+                          _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out["dD"]), _ptr(dinit), _ptr(workspace), wsz,
+                          _stream(stream)))
     out["d_init_state"] = dinit
     return out
 

@@ -155,7 +155,9 @@ FwdPlan plan_fwd(const ssd::Dims& d, bool has_states, bool bf16) {
   FwdPlan p;
   p.bf16 = bf16;
   size_t off = 0;
-  if (!has_states) {
+  // the bf16 family's output kernel reads the bf16 copy of the states, so
+  // the f32 ones are written only when the caller asks for them
+  if (!has_states && !bf16) {
     p.states = off;
     off += align_up(state_bytes(d));
   }
@@ -183,10 +185,13 @@ BwdPlan plan_bwd(const ssd::Dims& d, bool has_states, bool bf16) {
     return o;
   };
   const size_t bht = sizeof(float) * static_cast<size_t>(d.b) * d.H * d.T;
-  if (!has_states) p.states = take(state_bytes(d));
+  // the fused form reads only the bf16 copy of the states (recomputed into
+  // hbf when no history is given); the others need the f32 states
+  if (!has_states && !p.fused) p.states = take(state_bytes(d));
   p.gamma = take(state_bytes(d));
   if (bf16) p.hbf = take(state_bytes(d) / 2);
-  p.gh = take(sizeof(float) * static_cast<size_t>(d.b) * d.nc() * d.H * ssd::state_npb(d));
+  p.gh = take(sizeof(float) * static_cast<size_t>(d.b) * d.nc() * d.H *
+              (p.fused ? ssd::FUSED_GH_SLOTS : ssd::state_npb(d)));
   p.rowM = take(p.fused ? bht * d.nb() : bht);
   p.colE = take(bht);
   p.diagE = take(bht);
@@ -323,6 +328,14 @@ size_t ssd_workspace_bytes(const ssd_problem* prob, int for_backward, int has_ch
 int ssd_fwd(const ssd_problem* prob, const void* x, const void* dt, const float* A_log, const void* B,
             const void* C, const float* D, const float* init_state, void* y, float* final_state,
             float* chunk_states, void* workspace, size_t workspace_bytes, void* stream) {
+  return ssd_fwd_ex(prob, x, dt, A_log, B, C, D, init_state, y, final_state, chunk_states, nullptr, workspace,
+                    workspace_bytes, stream);
+}
+
+int ssd_fwd_ex(const ssd_problem* prob, const void* x, const void* dt, const float* A_log, const void* B,
+               const void* C, const float* D, const float* init_state, void* y, float* final_state,
+               float* chunk_states, void* chunk_states_bf16, void* workspace, size_t workspace_bytes,
+               void* stream) {
   ssd::Dims d;
   int rc = check_problem(prob, &d);
   if (rc != SSD_OK) return rc;
@@ -332,7 +345,11 @@ int ssd_fwd(const ssd_problem* prob, const void* x, const void* dt, const float*
   const bool empty = d.b == 0 || d.T == 0;
   if (!empty && (!x || !dt || !B || !C || !y))
     return fail(SSD_ERR_INVALID_ARG, "ssd_fwd: x, dt, B, C and y are required");
-  const void* ptrs[] = {x, dt, A_log, B, C, D, init_state, y, final_state, chunk_states};
+  if (chunk_states_bf16 && !use_bf16_kernels(d, prob->act_dtype, prob->act_dtype))
+    return fail(SSD_ERR_INVALID_ARG,
+                "ssd_fwd: chunk_states_bf16 needs a problem the bf16 kernels run (bf16 activations, headdim and "
+                "dstate multiples of 8)");
+  const void* ptrs[] = {x, dt, A_log, B, C, D, init_state, y, final_state, chunk_states, chunk_states_bf16};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return fail(SSD_ERR_ALIGN, "ssd_fwd: a tensor pointer is not 16-byte aligned");
   const int64_t state_elems = static_cast<int64_t>(d.b) * d.H * d.P * d.N;
@@ -351,8 +368,10 @@ int ssd_fwd(const ssd_problem* prob, const void* x, const void* dt, const float*
     return fail(SSD_ERR_WORKSPACE, "ssd_fwd: workspace of %zu bytes is smaller than the %zu needed", workspace_bytes,
                 plan.total);
   if (workspace && !aligned16(workspace)) return fail(SSD_ERR_ALIGN, "ssd_fwd: workspace is not 16-byte aligned");
-  float* states = chunk_states ? chunk_states : at<float>(workspace, plan.states);
-  void* hbf = plan.bf16 ? at<float>(workspace, plan.hbf) : nullptr;
+  // bf16 family: f32 states only when asked for, the bf16 copy (read by the
+  // output kernel) into the caller's buffer when given
+  float* states = chunk_states ? chunk_states : plan.bf16 ? nullptr : at<float>(workspace, plan.states);
+  void* hbf = plan.bf16 ? (chunk_states_bf16 ? chunk_states_bf16 : at<float>(workspace, plan.hbf)) : nullptr;
   if (plan.bf16)
     SSD_LAUNCH(ssd::launch_chunk_state_fwd_bf16(d, x, B, dt, A_log, init_state, states, final_state, hbf, st),
                "chunk_state_fwd");
@@ -412,7 +431,7 @@ int noalloc_scratch(hipStream_t st, void** out) {
 
 int bwd_impl(const char* who, const ssd_problem* prob, const void* x, const void* dt, const float* A_log,
              const void* B, const void* C, const float* D, const float* init_state, const float* chunk_states,
-             const void* dy, const float* d_final_state, float* dx, float* ddt, float* dA_log, float* dB, float* dC,
+             const void* chunk_states_bf16, const void* dy, const float* d_final_state, float* dx, float* ddt, float* dA_log, float* dB, float* dC,
              float* dD, float* d_init_state, void* workspace, size_t workspace_bytes, bool noalloc, void* stream) {
   ssd::Dims d;
   int rc = check_problem(prob, &d);
@@ -424,7 +443,7 @@ int bwd_impl(const char* who, const ssd_problem* prob, const void* x, const void
   const bool empty = d.b == 0 || d.T == 0;
   if (!empty && (!x || !dt || !B || !C || !dy || !dx || !ddt || !dB || !dC))
     return fail(SSD_ERR_INVALID_ARG, "%s: x, dt, B, C, dy, dx, ddt, dB and dC are required", who);
-  const void* ptrs[] = {x,  dt, A_log, B,  C,  D,      init_state, chunk_states, dy, d_final_state,
+  const void* ptrs[] = {x,  dt,  A_log,  B,  C,  D,  init_state,   chunk_states, chunk_states_bf16, dy, d_final_state,
                         dx, ddt, dA_log, dB, dC, dD, d_init_state};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return fail(SSD_ERR_ALIGN, "%s: a tensor pointer is not 16-byte aligned", who);
@@ -441,6 +460,11 @@ int bwd_impl(const char* who, const ssd_problem* prob, const void* x, const void
     }
     return ok();
   }
+  if (chunk_states_bf16 && !use_bf16_kernels(d, prob->act_dtype, prob->dy_dtype))
+    return fail(SSD_ERR_INVALID_ARG,
+                "%s: chunk_states_bf16 needs a problem the bf16 kernels run (bf16 activations and dy, headdim and "
+                "dstate multiples of 8)",
+                who);
   const BwdPlan plan = plan_bwd(d, chunk_states != nullptr, use_bf16_kernels(d, prob->act_dtype, prob->dy_dtype));
   if (noalloc) {
     if (plan.total > SSD_NOALLOC_SCRATCH_BYTES)
@@ -476,6 +500,37 @@ int bwd_impl(const char* who, const ssd_problem* prob, const void* x, const void
   void* gamma = at<float>(workspace, plan.gamma);
   void* hbf = plan.bf16 ? at<float>(workspace, plan.hbf) : nullptr;
 
+  if (plan.fused) {
+    // The fused kernel reads H_c in bf16 and forms <Gamma_{c+1}, H_c> itself,
+    // so the reverse pass needs H_c only to make the bf16 copy: not at all
+    // with the saved bf16 history, from the f32 history otherwise, and
+    // without a history the forward chunk-state kernel recomputes the bf16
+    // copy alone.
+    const float* hstates = nullptr;
+    void* hbf_out = nullptr;
+    if (chunk_states_bf16) {
+      hbf = const_cast<void*>(chunk_states_bf16);
+    } else if (chunk_states) {
+      hstates = chunk_states;
+      hbf_out = hbf;
+    } else {
+      SSD_LAUNCH(ssd::launch_chunk_state_fwd_bf16(d, x, B, dt, A_log, init_state, nullptr, nullptr, hbf, st),
+                 "chunk_state_fwd (recompute)");
+    }
+    SSD_LAUNCH(ssd::launch_chunk_state_bwd_bf16(d, dy, C, dt, A_log, d_final_state, hstates, gamma, d_init_state,
+                                                nullptr, hbf_out, s.done, st),
+               "chunk_state_bwd");
+    // the fused kernel also does the dt kernel's work (ddt, dA_log, dD)
+    SSD_LAUNCH(ssd::launch_bwd_fused_bf16(d, plan.nsplit, x, B, C, dt, dy, A_log, D, gamma, hbf, dx,
+                                          plan.nsplit > 1 ? s.dB_part : dB, plan.nsplit > 1 ? s.dC_part : dC, ddt,
+                                          dA_log, dD, s, st),
+               "chunk_bwd_fused");
+    if (plan.nsplit > 1) SSD_LAUNCH(ssd::launch_bwd_split_sum(d, plan.nsplit, dB, dC, s, st), "bwd_split_sum");
+    return ok();
+  }
+
+  // the split bf16 form and the general family: the f32 states (the bf16
+  // history, if given, is not used)
   const float* states = chunk_states;
   if (!states) {
     float* rec = at<float>(workspace, plan.states);
@@ -491,20 +546,14 @@ int bwd_impl(const char* who, const ssd_problem* prob, const void* x, const void
   }
   if (plan.bf16)
     SSD_LAUNCH(ssd::launch_chunk_state_bwd_bf16(d, dy, C, dt, A_log, d_final_state, states, gamma, d_init_state,
-                                                s.gh_part, hbf, plan.fused ? s.done : nullptr, st),
+                                                s.gh_part, hbf, nullptr, st),
                "chunk_state_bwd");
   else
     SSD_LAUNCH(
         ssd::launch_chunk_state_bwd(d, act, dyt, dy, C, dt, A_log, d_final_state, states, gamma, d_init_state,
                                     s.gh_part, nullptr, at<float>(workspace, plan.send), st),
         "chunk_state_bwd");
-  if (plan.fused) {
-    // the fused kernel also does the dt kernel's work (ddt, dA_log, dD)
-    SSD_LAUNCH(ssd::launch_bwd_fused_bf16(d, plan.nsplit, x, B, C, dt, dy, A_log, D, gamma, hbf, dx,
-                                          plan.nsplit > 1 ? s.dB_part : dB, plan.nsplit > 1 ? s.dC_part : dC, ddt,
-                                          dA_log, dD, s, st),
-               "chunk_bwd_fused");
-  } else if (plan.bf16) {
+  if (plan.bf16) {
     SSD_LAUNCH(ssd::launch_bwd_col_bf16(d, plan.nsplit, x, B, C, dt, dy, A_log, D, gamma, dx,
                                         plan.nsplit > 1 ? s.dB_part : dB, s, st),
                "chunk_bwd_col");
@@ -519,7 +568,7 @@ int bwd_impl(const char* who, const ssd_problem* prob, const void* x, const void
                                          plan.nsplit > 1 ? s.dC_part : dC, s, st),
                "chunk_bwd_row");
   }
-  if (!plan.fused) SSD_LAUNCH(ssd::launch_bwd_dt(d, act, dt, A_log, ddt, dA_log, dD, s, st), "bwd_dt");
+  SSD_LAUNCH(ssd::launch_bwd_dt(d, act, dt, A_log, ddt, dA_log, dD, s, st), "bwd_dt");
   if (plan.nsplit > 1) SSD_LAUNCH(ssd::launch_bwd_split_sum(d, plan.nsplit, dB, dC, s, st), "bwd_split_sum");
   return ok();
 }
@@ -532,8 +581,17 @@ int ssd_bwd(const ssd_problem* prob, const void* x, const void* dt, const float*
             const void* C, const float* D, const float* init_state, const float* chunk_states, const void* dy,
             const float* d_final_state, float* dx, float* ddt, float* dA_log, float* dB, float* dC, float* dD,
             float* d_init_state, void* workspace, size_t workspace_bytes, void* stream) {
-  return bwd_impl("ssd_bwd", prob, x, dt, A_log, B, C, D, init_state, chunk_states, dy, d_final_state, dx, ddt,
-                  dA_log, dB, dC, dD, d_init_state, workspace, workspace_bytes, false, stream);
+  return bwd_impl("ssd_bwd", prob, x, dt, A_log, B, C, D, init_state, chunk_states, nullptr, dy, d_final_state, dx,
+                  ddt, dA_log, dB, dC, dD, d_init_state, workspace, workspace_bytes, false, stream);
+}
+
+int ssd_bwd_ex(const ssd_problem* prob, const void* x, const void* dt, const float* A_log, const void* B,
+               const void* C, const float* D, const float* init_state, const float* chunk_states,
+               const void* chunk_states_bf16, const void* dy, const float* d_final_state, float* dx, float* ddt,
+               float* dA_log, float* dB, float* dC, float* dD, float* d_init_state, void* workspace,
+               size_t workspace_bytes, void* stream) {
+  return bwd_impl("ssd_bwd_ex", prob, x, dt, A_log, B, C, D, init_state, chunk_states, chunk_states_bf16, dy,
+                  d_final_state, dx, ddt, dA_log, dB, dC, dD, d_init_state, workspace, workspace_bytes, false, stream);
 }
 
 int ssd_bwd_noalloc(const ssd_problem* prob, const void* x, const void* dt, const float* A_log, const void* B,
@@ -541,7 +599,7 @@ int ssd_bwd_noalloc(const ssd_problem* prob, const void* x, const void* dt, cons
                     const void* dy, const float* d_final_state, float* dx, float* ddt, float* dA_log, float* dB,
                     float* dC, float* dD, float* d_init_state, void* stream) {
   g_prof_suppress = true;
-  const int rc = bwd_impl("ssd_bwd_noalloc", prob, x, dt, A_log, B, C, D, init_state, chunk_states, dy,
+  const int rc = bwd_impl("ssd_bwd_noalloc", prob, x, dt, A_log, B, C, D, init_state, chunk_states, nullptr, dy,
                           d_final_state, dx, ddt, dA_log, dB, dC, dD, d_init_state, nullptr, 0, true, stream);
   g_prof_suppress = false;
   return rc;

@@ -44,6 +44,7 @@ constexpr int STRIP = 32 * 32;      // bytes of a 32 x 16 bf16 strip
 constexpr int KP = PMAX / 32;
 constexpr int KN = NMAX / 32;
 static_assert(NBMAX <= 4, "the pass-end phase holds at most four blocks' W strips");
+static_assert(FUSED_GH_SLOTS == FW, "one <Gamma, H_c> partial per wave");
 
 // Sum over the 64 lanes of a wave, in every lane (DPP scan, then lane 63).
 __device__ __forceinline__ float lane_last(float v) {
@@ -73,7 +74,7 @@ __global__ __launch_bounds__(FT) void bwd_fused_bf16_kernel(
     const float* __restrict__ D, const uint16_t* __restrict__ gamma, const uint16_t* __restrict__ hbf,
     float* __restrict__ dx, float* __restrict__ dB_out, float* __restrict__ dC_out, float* __restrict__ ddt,
     float* __restrict__ dA_log_out, float* __restrict__ dD_out, BwdScratch s, int T, int H, int P_, int N_, int G,
-    int Q_, int nsplit, int npb) {
+    int Q_, int nsplit) {
   const int P = FULL ? PMAX : P_, N = FULL ? NMAX : N_, Q = FULL ? QMAX : Q_;
   __shared__ __attribute__((aligned(1024))) char sB_[TILE_N];          // B rows j of block jb
   __shared__ __attribute__((aligned(1024))) char sX_[2 * TILE_P];      // x rows j, two heads; W strip slot
@@ -137,6 +138,8 @@ __global__ __launch_bounds__(FT) void bwd_fused_bf16_kernel(
   const LazyRsrc rdiag{s.diagE + sum0};
   const LazyRsrc rrp{s.Rp + sum0};
   const LazyRsrc rdso{s.dsoff + sum0};
+  // the per-wave partials of <Gamma_{c+1}, H_c> of (bi, c, h = 0)
+  const LazyRsrc rgh{s.gh_part + (static_cast<int64_t>(bi) * nc + c) * H * FUSED_GH_SLOTS};
   // dB and dC (or this head split's partials) from the chunk's first row and the group's columns
   const LazyRsrc rdb{dB_out + static_cast<int64_t>(sp) * batch * T * GN + row0 * GN + static_cast<int64_t>(g) * N};
   const LazyRsrc rdc{dC_out + static_cast<int64_t>(sp) * batch * T * GN + row0 * GN + static_cast<int64_t>(g) * N};
@@ -469,6 +472,26 @@ __global__ __launch_bounds__(FT) void bwd_fused_bf16_kernel(
               wait_vm<0>();
           }
           lds_barrier();
+          if (jb == 0 && u == 0) {
+            // <Gamma_{c+1}, H_c> of head h, while both tiles are this head's
+            // (Gamma has landed: this step's waits covered every copy issued
+            // before it; H_c is replaced from step 1 or the state step on):
+            // the two tiles share one layout, so matching 16-byte chunks hold
+            // matching elements.  One partial per wave, added in wave order
+            // by the dt epilogue.
+            float gp = 0.f;
+            const int tg = opaque_index(static_cast<int>(threadIdx.x));  // recomputed here: see the row-sum store
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+              const int off = (half * FT + tg) * 16;
+              const bf16x8 ga = *(const __attribute__((address_space(3))) bf16x8*)(sGam + off);
+              const bf16x8 ha = *(const __attribute__((address_space(3))) bf16x8*)(sH + off);
+#pragma unroll
+              for (int k = 0; k < 8; ++k) gp += static_cast<float>(ga[k]) * static_cast<float>(ha[k]);
+            }
+            gp = wave_tot(gp);
+            store_f32(rgh.ptr(), gp, l == 0 ? 0u : OOB_OFFSET, static_cast<uint32_t>(h * FUSED_GH_SLOTS + w) * 4);
+          }
         }
       }
 
@@ -768,7 +791,7 @@ __global__ __launch_bounds__(FT) void bwd_fused_bf16_kernel(
         sl += dv[e] * A;
         tr += dv[e] * rP[e];
       }
-      const float ghl = l < npb ? s.gh_part[((static_cast<int64_t>(bi) * nc + c) * H + h) * npb + l] : 0.f;
+      const float ghl = l < FUSED_GH_SLOTS ? s.gh_part[((static_cast<int64_t>(bi) * nc + c) * H + h) * FUSED_GH_SLOTS + l] : 0.f;
       sl = wave_tot(sl);  // s at the chunk's last row
       tr = wave_tot(tr);
       const float gh = wave_tot(ghl);
@@ -860,7 +883,7 @@ hipError_t launch_bwd_fused_bf16(const Dims& d, int nsplit, const void* x, const
                      static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(B), static_cast<const uint16_t*>(C),
                      static_cast<const uint16_t*>(dt), static_cast<const uint16_t*>(dy), A_log, D,
                      static_cast<const uint16_t*>(gamma), static_cast<const uint16_t*>(hbf), dx, dB_out, dC_out, ddt,
-                     dA_log, dD, s, d.T, d.H, d.P, d.N, d.G, d.Q, nsplit, state_npb(d));
+                     dA_log, dD, s, d.T, d.H, d.P, d.N, d.G, d.Q, nsplit);
   return hipGetLastError();
 }
 

@@ -18,6 +18,8 @@ struct Dims {
 // Number of headdim rows one chunk-state workgroup owns.
 constexpr int STATE_PB = 16;
 inline int state_npb(const Dims& d) { return (d.P + STATE_PB - 1) / STATE_PB; }
+// per-wave partials of <Gamma_{c+1}, H_c> that the fused backward kernel writes per (b, chunk, head)
+constexpr int FUSED_GH_SLOTS = 8;
 
 // Forward state passing: states[b,c,h] = state entering chunk c, final = state
 // after the last chunk.  `init` may be null (zero initial state), `final_state`
@@ -64,7 +66,8 @@ struct BwdScratch {
   float* diagE;  // [b,H,T] diagonal entries
   float* Rp;     // [b,H,T] state-term of the dt gradient without the dt factor
   float* dsoff;  // [b,H,T] decay gradient from the incoming-state readout
-  float* gh_part;  // [b,nc,H,npb]
+  float* gh_part;  // [b,nc,H,npb] partial <Gamma_{c+1}, H_c> of the reverse chunk-state pass, or (fused
+                   // kernel) [b,nc,H,FUSED_GH_SLOTS], one per wave of the fused kernel's workgroup
   float* dA_part;  // [b,nc,H]
   float* dD_part;  // [b,nc,nb,H]
   unsigned* done;  // one counter: the dt kernel's finished workgroups (zeroed by the row kernel)

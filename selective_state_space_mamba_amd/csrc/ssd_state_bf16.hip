@@ -62,8 +62,8 @@ __global__ __launch_bounds__(ST) void chunk_state_bf16_kernel(
     float* __restrict__ states_f32,     // fwd: H_c [b,nc,H,P,N]
     uint16_t* __restrict__ states_bf,   // fwd: H_c in bf16 (nullable); bwd: Gamma_{c+1} in bf16
     float* __restrict__ last_out,       // fwd: final state; bwd: d(initial state) (nullable)
-    const float* __restrict__ hstates,  // bwd: H_c
-    float* __restrict__ gh_part,        // bwd: [b,nc,H,ceil(P/16)] partial <Gamma_{c+1}, H_c>
+    const float* __restrict__ hstates,  // bwd: H_c (read only when gh_part or hbf_out is given)
+    float* __restrict__ gh_part,        // bwd: [b,nc,H,ceil(P/16)] partial <Gamma_{c+1}, H_c> (nullable)
     uint16_t* __restrict__ hbf_out,     // bwd: H_c in bf16 (nullable)
     unsigned* __restrict__ counter,     // bwd: an arrival counter of the next kernel, zeroed here (nullable)
     int T, int H, int P, int N, int G, int Q) {
@@ -99,6 +99,8 @@ __global__ __launch_bounds__(ST) void chunk_state_bf16_kernel(
   const int64_t PN = static_cast<int64_t>(P) * N;
   const uint32_t HPb = static_cast<uint32_t>(HP) * 2, GNb = static_cast<uint32_t>(GN) * 2;
   const int pch = min(4, (P - p0) >> 3), nch = N >> 3;
+  // bwd: whether H_c is read at all (for the <Gamma_{c+1}, H_c> partials or its bf16 copy)
+  const bool need_h = REV && (gh_part != nullptr || hbf_out != nullptr);
   float* const wts = sWt[w];
 
   f4 st[2];  // row p = p0 + 16 pw + r, columns n = 32 nw + 16 t + 4q + e
@@ -135,7 +137,7 @@ __global__ __launch_bounds__(ST) void chunk_state_bf16_kernel(
     if (sl == 0) {
       steps_async<SW>(lds_ptr(sDtb[it & 1]), make_rsrc(dt + (static_cast<int64_t>(bi) * T + static_cast<int64_t>(c) * Q) * H + h),
                       H * 2, Q);
-      if constexpr (REV) {
+      if (need_h) {
         const int64_t sbase = ((static_cast<int64_t>(bi) * nc + c) * H + h) * PN + static_cast<int64_t>(p0) * N;
         tile_async<SPB, 32, SW>(sH + (it & 1) * HTILE, make_rsrc(hstates + sbase), 0, N * 4, P - p0, N >> 2);
       }
@@ -242,7 +244,7 @@ __global__ __launch_bounds__(ST) void chunk_state_bf16_kernel(
 #pragma unroll
     for (int t = 0; t < 2; ++t)
       *reinterpret_cast<float4*>(stg + r * SROW + 16 * t + 4 * q) = make_float4(st[t][0], st[t][1], st[t][2], st[t][3]);
-    if constexpr (!REV) {
+    if (!REV && states_f32) {
       // f32: rows i = l / 8 (+ 8), four columns j = 4 (l % 8) a lane
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
@@ -264,7 +266,7 @@ __global__ __launch_bounds__(ST) void chunk_state_bf16_kernel(
       } else {
         // H_c at the same elements (tile rows are 128 floats)
         float4 ha = make_float4(0.f, 0.f, 0.f, 0.f), hb = ha;
-        if (ok) {
+        if (ok && need_h) {
           ha = *reinterpret_cast<const float4*>(ht + (16 * pw + i) * NMAX + n0);
           hb = *reinterpret_cast<const float4*>(ht + (16 * pw + i) * NMAX + n0 + 4);
         }
@@ -277,7 +279,7 @@ __global__ __launch_bounds__(ST) void chunk_state_bf16_kernel(
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int e = 0; e < 4; ++e) st[t][e] = decay * st[t][e] + acc[t][e];
-    if constexpr (REV) {
+    if (REV && gh_part) {
       // per 16-row headdim block (waves with the same pw), summed after the next barrier
       gh = wave_total(gh);
       if (l == 0) sGh[it & 1][w] = gh;
@@ -290,7 +292,7 @@ __global__ __launch_bounds__(ST) void chunk_state_bf16_kernel(
       }
     }
   }
-  if constexpr (REV) {
+  if (REV && gh_part) {
     __syncthreads();
     if (threadIdx.x < 2) {
       const int cp = chunk_of(nc - 1), pbi = 2 * pb + threadIdx.x;

@@ -30,7 +30,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("ssd_fwd", "ssd_bwd", "ssd_workspace_bytes", "ssd_last_error", "mamba2_conv1d_silu_fwd",
+    for n in ("ssd_fwd", "ssd_bwd", "ssd_fwd_ex", "ssd_bwd_ex", "ssd_workspace_bytes", "ssd_last_error",
+              "mamba2_conv1d_silu_fwd",
               "mamba2_conv1d_silu_bwd", "mamba2_rmsnorm_gated_fwd", "mamba2_rmsnorm_gated_bwd",
               "ssd_dt_softplus_fwd", "ssd_dt_softplus_bwd", "ssd_dt_softplus_bwd_workspace_bytes"):
         assert n in names
@@ -136,6 +137,36 @@ def test_workspace_sizes_follow_the_plan(lib):
     wb1 = lib.ssd_workspace_bytes(ctypes.byref(p), 1, 1)
     wb0 = lib.ssd_workspace_bytes(ctypes.byref(p), 1, 0)
     assert wb1 >= states and wb0 == wb1 + states
+
+
+def test_bf16_workspace_sizes(lib, monkeypatch):
+    # bf16 problems: the forward keeps only the bf16 copy of the states (its
+    # output kernel reads that), whether or not the caller takes the f32
+    # ones; the fused backward reads the states only in bf16, so it needs no
+    # f32 slot for recomputed states either
+    monkeypatch.delenv("SSD_BF16_BWD", raising=False)
+    p = prob(act_dtype=1, dy_dtype=1)
+    nc = 512 // 256
+    states = 4 * 2 * nc * 8 * 64 * 128
+    send = 256
+    assert lib.ssd_workspace_bytes(ctypes.byref(p), 0, 0) == states // 2 + send
+    assert lib.ssd_workspace_bytes(ctypes.byref(p), 0, 1) == states // 2 + send
+    assert lib.ssd_workspace_bytes(ctypes.byref(p), 1, 0) == lib.ssd_workspace_bytes(ctypes.byref(p), 1, 1)
+
+
+def test_bf16_history_needs_a_bf16_problem(lib):
+    # an f32 problem (or bf16 activations with f32 dy in the backward) has no
+    # bf16 history: rejected before any launch
+    f = ctypes.c_void_p(FAKE)
+    for kw in (dict(), dict(act_dtype=1, dy_dtype=0), dict(act_dtype=1, dy_dtype=1, headdim=60)):
+        p = prob(**kw)
+        assert lib.ssd_bwd_ex(ctypes.byref(p), f, f, f, f, f, f, None, None, f, f, None, f, f, f, f, f, f, None, f,
+                              1 << 30, None) == -1
+        assert "chunk_states_bf16" in lib.ssd_last_error().decode()
+    for kw in (dict(), dict(act_dtype=1, headdim=60)):
+        p = prob(**kw)
+        assert lib.ssd_fwd_ex(ctypes.byref(p), f, f, f, f, f, f, None, f, None, None, f, f, 1 << 30, None) == -1
+        assert "chunk_states_bf16" in lib.ssd_last_error().decode()
 
 
 def test_shell_argument_checks(lib):

@@ -138,6 +138,41 @@ def test_recompute_matches_saved_history_bitwise():
         assert np.array_equal(a[k], b[k]), k
 
 
+@pytest.mark.parametrize("cfg", [
+    SSDConfig("hist", 2, 1024, 8, 64, 128, 2, 256, "bf16", init_state=True, seed=21),
+    SSDConfig("hist_ragged", 2, 240, 6, 40, 72, 3, 80, "bf16", init_state=True, seed=22),
+], ids=["full_tiles", "ragged"])
+def test_bf16_history(cfg):
+    # ssd_fwd_ex writes the bf16 copy of the chunk states (the round to
+    # nearest even of the f32 ones) and the same y as ssd_fwd; ssd_bwd_ex with
+    # only that copy gives the gradients of the f32 history and of the
+    # recompute mode bit for bit (the backward reads the states only in
+    # bf16), within the bf16 bar of the oracle
+    import selective_state_space_mamba_amd as ssd
+    d = make_inputs(cfg)
+    x, dt, B, C = dev(d["x"]), dev(d["dt"]), dev(d["B"]), dev(d["C"])
+    A_log, D, h0, dy = dev(d["A_log"]), dev(d["D"]), dev(d["h0"]), dev(d["dy"])
+    Q = cfg.chunk
+    y0, fin0, cs0 = ssd.ssd_fwd(x, dt, A_log, B, C, D, h0, chunk=Q)
+    r = ssd.ssd_fwd_ex(x, dt, A_log, B, C, D, h0, chunk=Q, want_chunk_states=True, want_chunk_states_bf16=True)
+    r1 = ssd.ssd_fwd_ex(x, dt, A_log, B, C, D, h0, chunk=Q)  # the bf16 history alone
+    torch.cuda.synchronize()
+    assert torch.equal(r["y"], y0) and torch.equal(r["final_state"], fin0) and torch.equal(r["chunk_states"], cs0)
+    assert r1["chunk_states"] is None and torch.equal(r1["y"], y0) and torch.equal(r1["final_state"], fin0)
+    assert torch.equal(r["chunk_states_bf16"], cs0.to(torch.bfloat16))
+    assert torch.equal(r1["chunk_states_bf16"], r["chunk_states_bf16"])
+    g_bf = ssd.ssd_bwd(x, dt, A_log, B, C, D, dy, h0, chunk_states_bf16=r1["chunk_states_bf16"], chunk=Q)
+    g_f32 = ssd.ssd_bwd(x, dt, A_log, B, C, D, dy, h0, chunk_states=cs0, chunk=Q)
+    g_re = ssd.ssd_bwd(x, dt, A_log, B, C, D, dy, h0, chunk=Q)
+    torch.cuda.synchronize()
+    for k in ("dx", "ddt", "dA_log", "dB", "dC", "dD", "d_init_state"):
+        assert torch.equal(g_bf[k], g_f32[k]), k
+        assert torch.equal(g_bf[k], g_re[k]), k
+    got = {"y": host(r1["y"]), "final": host(r1["final_state"]), "chunk_states": host(r["chunk_states"])}
+    got.update({k: host(v) for k, v in g_bf.items()})
+    compare(got, oracle_ssd(d, Q), TOL["bf16"], label=f"bf16 history {cfg.name}")
+
+
 def test_deterministic_bitwise():
     cfg = CONFIGS["grouped"].with_(batch=1, seqlen=1024)
     d = make_inputs(cfg)

@@ -65,9 +65,9 @@ def test_noalloc_allocates_no_device_memory():
 
 def test_noalloc_refuses_problems_past_its_scratch():
     import selective_state_space_mamba_amd as ssd
-    # the grouped workload without saved chunk states recomputes them into the
-    # scratch: more than the static array holds
-    b, T, H, P, N, G, Q = 4, 2048, 32, 64, 128, 8, 256
+    # the grouped workload's shape at twice its batch, without saved chunk
+    # states (recomputed into the scratch): more than the static array holds
+    b, T, H, P, N, G, Q = 8, 2048, 32, 64, 128, 8, 256
     bf = dict(dtype=torch.bfloat16, device="cuda:0")
     f32 = dict(dtype=torch.float32, device="cuda:0")
     x = torch.zeros((b, T, H, P), **bf)
