@@ -3,8 +3,9 @@
 ``ssd_scan`` wraps ssd_fwd / ssd_bwd (and, with ``dt_bias``, the dt activation
 dt = softplus(dt_raw + dt_bias) in front of the core) in one
 ``torch.autograd.Function``: the forward saves the chunk states that ssd_fwd
-writes, the backward hands them to ssd_bwd together with the gradients of y
-and of the final state.  The dt gradient stays f32 between ssd_bwd and the
+writes (in bf16 for the problems the bf16 kernels run, which read them only in
+bf16: ssd_fwd_ex), the backward hands them to ssd_bwd together with the
+gradients of y and of the final state.  The dt gradient stays f32 between ssd_bwd and the
 softplus backward inside the one function.
 
 ``mamba2_block_core`` does the same for the block slice between the input and
@@ -26,21 +27,45 @@ import torch
 from . import _binding as _b
 
 
+def _fwd_with_history(x, dt, A_log, B, C, D, init_state, chunk):
+    """ssd_fwd keeping the chunk states for the backward: (y, final_state,
+    f32 states or None, bf16 states or None).  bf16 problems with headdim and
+    d_state multiples of 8 keep them in bf16 (the library refuses the bf16
+    history for problems its bf16 kernels do not run, e.g. past their size
+    limits: those keep the f32 states)."""
+    if x.dtype == torch.bfloat16 and x.shape[-1] % 8 == 0 and B.shape[-1] % 8 == 0:
+        try:
+            r = _b.ssd_fwd_ex(x, dt, A_log, B, C, D, init_state, chunk=chunk)
+            return r["y"], r["final_state"], None, r["chunk_states_bf16"]
+        except _b.SSDError as e:
+            if "chunk_states_bf16" not in str(e):
+                raise
+    y, fin, cs = _b.ssd_fwd(x, dt, A_log, B, C, D, init_state, chunk=chunk)
+    return y, fin, cs, None
+
+
+def _history_args(cs, csb, dy):
+    """The saved history as ssd_bwd's arguments: the bf16 one only for a bf16
+    dy (an f32 dy takes the general kernels, which recompute the f32 states)."""
+    return dict(chunk_states=cs, chunk_states_bf16=csb if dy.dtype == torch.bfloat16 else None)
+
+
 class _SSDScan(torch.autograd.Function):
     @staticmethod
     def forward(ctx, x, dt_in, A_log, B, C, D, init_state, dt_bias, chunk):
         dt = _b.dt_softplus_fwd(dt_in, dt_bias) if dt_bias is not None else dt_in
-        y, fin, cs = _b.ssd_fwd(x, dt, A_log, B, C, D, init_state, chunk=chunk)
-        ctx.save_for_backward(x, dt_in, dt, A_log, B, C, D, init_state, dt_bias, cs)
+        y, fin, cs, csb = _fwd_with_history(x, dt, A_log, B, C, D, init_state, chunk)
+        ctx.save_for_backward(x, dt_in, dt, A_log, B, C, D, init_state, dt_bias, cs, csb)
         ctx.chunk = chunk
         return y, fin
 
     @staticmethod
     def backward(ctx, gy, gfin):
-        x, dt_in, dt, A_log, B, C, D, init_state, dt_bias, cs = ctx.saved_tensors
+        x, dt_in, dt, A_log, B, C, D, init_state, dt_bias, cs, csb = ctx.saved_tensors
         if gy is None:
             gy = torch.zeros_like(x)
-        g = _b.ssd_bwd(x, dt, A_log, B, C, D, gy.contiguous(), init_state, chunk_states=cs, chunk=ctx.chunk,
+        gy = gy.contiguous()
+        g = _b.ssd_bwd(x, dt, A_log, B, C, D, gy, init_state, chunk=ctx.chunk, **_history_args(cs, csb, gy),
                        want_d_init_state=init_state is not None and ctx.needs_input_grad[6],
                        d_final_state=None if gfin is None else gfin.float().contiguous())
         ddt, d_bias = g["ddt"], None
@@ -69,23 +94,24 @@ def _core_fwd(xbc, dt_raw, z, conv_w, conv_b, dt_bias, A_log, D, norm_w, init_st
     dt = _b.dt_softplus_fwd(dt_raw, dt_bias)
     xs, Bs, Cs = _b.conv1d_silu_fwd(xbc, conv_w, conv_b, d_inner, ngroups, dstate)
     xs = xs.view(b, T, H, headdim)
-    y, fin, cs = _b.ssd_fwd(xs, dt, A_log, Bs, Cs, D, init_state, chunk=chunk)
+    y, fin, cs, csb = _fwd_with_history(xs, dt, A_log, Bs, Cs, D, init_state, chunk)
     out, inv = _b.rmsnorm_gated_fwd(y.view(b, T, d_inner), z, norm_w, eps)
-    return out, fin, (dt, xs, Bs, Cs, y, inv, cs)
+    return out, fin, (dt, xs, Bs, Cs, y, inv, cs, csb)
 
 
 def _core_bwd(xbc, dt_raw, z, conv_w, conv_b, dt_bias, A_log, D, norm_w, init_state, saved, dims, gout, gfin,
               want_dh0):
     """Backward of the block slice: (dxbc, ddt_raw, dz, dconv_w, dconv_b, d_dt_bias,
     dA_log, dD, dnorm_w, d_init_state), all f32."""
-    dt, xs, Bs, Cs, y, inv, cs = saved
+    dt, xs, Bs, Cs, y, inv, cs, csb = saved
     ngroups, dstate, headdim, chunk, eps = dims
     b, T, d_inner = z.shape
     H = d_inner // headdim
     # the gradient handed to the SSD backward is stored in the activation
     # dtype, as the block-slice step does
     gy, gz, gnw = _b.rmsnorm_gated_bwd(y.view(b, T, d_inner), z, norm_w, inv, gout, dy_dtype=xbc.dtype)
-    g = _b.ssd_bwd(xs, dt, A_log, Bs, Cs, D, gy.view(b, T, H, headdim), init_state, chunk_states=cs,
+    gy = gy.view(b, T, H, headdim)
+    g = _b.ssd_bwd(xs, dt, A_log, Bs, Cs, D, gy, init_state, **_history_args(cs, csb, gy),
                    chunk=chunk, want_d_init_state=want_dh0,
                    d_final_state=None if gfin is None else gfin.float().contiguous())
     dxbc, dcw, dcb = _b.conv1d_silu_bwd(xbc, conv_w, conv_b, g["dx"].view(b, T, d_inner), g["dB"], g["dC"],
