@@ -35,10 +35,7 @@ namespace ssd {
 namespace {
 constexpr int SW = 8;              // waves per workgroup
 constexpr int ST = SW * WAVE;      // threads
-constexpr int SSJ = 128;           // time steps per slab
 constexpr int SPB = 32;            // headdim rows per workgroup
-constexpr int XSLAB = SSJ * 64;    // bytes of a 128 x 32 bf16 slab
-constexpr int BSLAB = SSJ * 256;   // bytes of a 128 x 128 bf16 slab
 constexpr int HTILE = SPB * 512;   // bytes of a 32 x 128 f32 state tile
 constexpr int SROW = 36;           // floats per staged state row
 
@@ -52,7 +49,10 @@ __device__ __forceinline__ float wave_total(float v) {
 }
 }  // namespace
 
-template <bool REV>
+// SSJ: time steps per slab (128; 64 for grids of several rounds, whose LDS
+// then lets two workgroups share a CU).  HAS_H: the reverse pass reads H_c
+// (for the <Gamma_{c+1}, H_c> partials or its bf16 copy).
+template <bool REV, int SSJ, bool HAS_H>
 __global__ __launch_bounds__(ST) void chunk_state_bf16_kernel(
     const uint16_t* __restrict__ X,     // fwd: x; bwd: dy       [b,T,H,P]
     const uint16_t* __restrict__ Bm,    // fwd: B; bwd: C        [b,T,G,N]
@@ -67,9 +67,12 @@ __global__ __launch_bounds__(ST) void chunk_state_bf16_kernel(
     uint16_t* __restrict__ hbf_out,     // bwd: H_c in bf16 (nullable)
     unsigned* __restrict__ counter,     // bwd: an arrival counter of the next kernel, zeroed here (nullable)
     int T, int H, int P, int N, int G, int Q) {
+  constexpr int XSLAB = SSJ * 64;   // bytes of an SSJ x 32 bf16 slab
+  constexpr int BSLAB = SSJ * 256;  // bytes of an SSJ x 128 bf16 slab
+  static_assert(!HAS_H || REV, "H_c is read by the reverse pass only");
   __shared__ __attribute__((aligned(1024))) char sX_[2 * XSLAB];
   __shared__ __attribute__((aligned(1024))) char sB_[2 * BSLAB];
-  __shared__ __attribute__((aligned(1024))) char sH_[REV ? 2 * HTILE : 16];  // bwd: H_c (f32), two chunks
+  __shared__ __attribute__((aligned(1024))) char sH_[HAS_H ? 2 * HTILE : 16];  // bwd: H_c (f32), two chunks
   __shared__ __attribute__((aligned(16))) float sWt[SW][QMAX];                // per-wave step weights
   __shared__ __attribute__((aligned(16))) uint32_t sDtb[2][QMAX];             // dt bits of a chunk, two chunks
   __shared__ float sGh[2][SW];
@@ -99,8 +102,7 @@ __global__ __launch_bounds__(ST) void chunk_state_bf16_kernel(
   const int64_t PN = static_cast<int64_t>(P) * N;
   const uint32_t HPb = static_cast<uint32_t>(HP) * 2, GNb = static_cast<uint32_t>(GN) * 2;
   const int pch = min(4, (P - p0) >> 3), nch = N >> 3;
-  // bwd: whether H_c is read at all (for the <Gamma_{c+1}, H_c> partials or its bf16 copy)
-  const bool need_h = REV && (gh_part != nullptr || hbf_out != nullptr);
+  constexpr bool need_h = HAS_H;
   float* const wts = sWt[w];
 
   f4 st[2];  // row p = p0 + 16 pw + r, columns n = 32 nw + 16 t + 4q + e
@@ -177,10 +179,11 @@ __global__ __launch_bounds__(ST) void chunk_state_bf16_kernel(
       }
       const int buf = (it * nsl + sl) & 1;
       // the slab's x rows times their step weights, in place: one 16-byte
-      // chunk per thread (the swizzle keeps chunks inside their row), so that
-      // the four waves sharing a row do not each scale it
-      {
-        static_assert(XSLAB == ST * 16, "one chunk of the x slab per thread");
+      // chunk per thread (the swizzle keeps chunks inside their row; with
+      // 64-step slabs half the threads), so that the four waves sharing a row
+      // do not each scale it
+      static_assert(XSLAB <= ST * 16, "at most one chunk of the x slab per thread");
+      if (XSLAB == ST * 16 || static_cast<int>(threadIdx.x) < XSLAB / 16) {
         uint4* const cp = reinterpret_cast<uint4*>(sX_ + buf * XSLAB) + threadIdx.x;
         const float wt = wts[sl * SSJ + (threadIdx.x >> 2)];
         const uint4 v = *cp;
@@ -313,11 +316,31 @@ __global__ __launch_bounds__(ST) void chunk_state_bf16_kernel(
   }
 }
 
+namespace {
+// Compute units of the current device (looked up once).
+int device_cus() {
+  static const int cus = [] {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return 256;
+    return n > 0 ? n : 256;
+  }();
+  return cus;
+}
+}  // namespace
+
+// Grids of more workgroups than CUs take 64-step slabs: 69 KB of LDS, so two
+// workgroups share a CU and the grid runs in half the rounds (block slice:
+// 768 workgroups, 107 -> 103 us forward and 149 -> 127 us backward when this
+// was first measured); a grid of one round keeps 128-step slabs, with half
+// the barriers per chunk (grouped workload: 36 us against 43 with 64 steps).
+// The reverse pass that reads H_c (two 16 KB f32 tiles more) keeps 128.
 hipError_t launch_chunk_state_fwd_bf16(const Dims& d, const void* x, const void* B, const void* dt,
                                        const float* A_log, const float* init, float* states, float* final_state,
                                        void* hbf, hipStream_t st) {
   const int64_t nblk = static_cast<int64_t>(d.b) * d.H * ((d.P + SPB - 1) / SPB);
-  hipLaunchKernelGGL(chunk_state_bf16_kernel<false>, dim3(nblk), dim3(ST), 0, st, static_cast<const uint16_t*>(x),
+  auto kern = nblk > device_cus() ? chunk_state_bf16_kernel<false, 64, false> : chunk_state_bf16_kernel<false, 128, false>;
+  hipLaunchKernelGGL(kern, dim3(nblk), dim3(ST), 0, st, static_cast<const uint16_t*>(x),
                      static_cast<const uint16_t*>(B), static_cast<const uint16_t*>(dt), A_log, init, states,
                      static_cast<uint16_t*>(hbf), final_state, nullptr, nullptr, nullptr, nullptr, d.T, d.H, d.P, d.N,
                      d.G, d.Q);
@@ -328,7 +351,11 @@ hipError_t launch_chunk_state_bwd_bf16(const Dims& d, const void* dy, const void
                                        const float* A_log, const float* dfinal, const float* states, void* gamma,
                                        float* dinit, float* gh_part, void* hbf, unsigned* counter, hipStream_t st) {
   const int64_t nblk = static_cast<int64_t>(d.b) * d.H * ((d.P + SPB - 1) / SPB);
-  hipLaunchKernelGGL(chunk_state_bf16_kernel<true>, dim3(nblk), dim3(ST), 0, st, static_cast<const uint16_t*>(dy),
+  const bool has_h = gh_part != nullptr || hbf != nullptr;
+  auto kern = has_h ? chunk_state_bf16_kernel<true, 128, true>
+                    : nblk > device_cus() ? chunk_state_bf16_kernel<true, 64, false>
+                                          : chunk_state_bf16_kernel<true, 128, false>;
+  hipLaunchKernelGGL(kern, dim3(nblk), dim3(ST), 0, st, static_cast<const uint16_t*>(dy),
                      static_cast<const uint16_t*>(C), static_cast<const uint16_t*>(dt), A_log, dfinal, nullptr,
                      static_cast<uint16_t*>(gamma), dinit, states, gh_part, static_cast<uint16_t*>(hbf), counter, d.T,
                      d.H, d.P, d.N, d.G, d.Q);

@@ -141,7 +141,9 @@ def test_recompute_matches_saved_history_bitwise():
 @pytest.mark.parametrize("cfg", [
     SSDConfig("hist", 2, 1024, 8, 64, 128, 2, 256, "bf16", init_state=True, seed=21),
     SSDConfig("hist_ragged", 2, 240, 6, 40, 72, 3, 80, "bf16", init_state=True, seed=22),
-], ids=["full_tiles", "ragged"])
+    # 320 chunk-state workgroups, more than the CUs: the 64-step-slab kernels
+    SSDConfig("hist_rounds", 2, 1024, 80, 64, 128, 4, 256, "bf16", init_state=True, seed=23),
+], ids=["full_tiles", "ragged", "several_rounds"])
 def test_bf16_history(cfg):
     # ssd_fwd_ex writes the bf16 copy of the chunk states (the round to
     # nearest even of the f32 ones) and the same y as ssd_fwd; ssd_bwd_ex with
