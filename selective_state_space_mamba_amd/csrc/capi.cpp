@@ -127,7 +127,7 @@ struct FwdPlan {
 };
 struct BwdPlan {
   size_t states = 0, gamma = 0, hbf = 0, gh = 0, rowM = 0, colE = 0, diagE = 0, Rp = 0, dsoff = 0, dA = 0, dD = 0,
-         done = 0, dB = 0, dC = 0, send = 0, total = 0;
+         done = 0, wst = 0, dB = 0, dC = 0, send = 0, total = 0;
   int nsplit = 1;
   bool bf16 = false;   // bf16 kernels with asynchronous staging (they also need a bf16 copy of the states)
   bool fused = false;  // the bf16 column and row work in one kernel (row sums of M in nb slots)
@@ -201,6 +201,9 @@ BwdPlan plan_bwd(const ssd::Dims& d, bool has_states, bool bf16) {
   p.dD = take(sizeof(float) * static_cast<size_t>(d.b) * d.nc() * d.nb() * d.H);
   p.done = take(sizeof(unsigned));
   p.send = take(sizeof(float) * static_cast<size_t>(d.b) * d.nc() * d.H);
+  if (p.fused)
+    p.wst = take(static_cast<size_t>(d.b) * d.nc() * d.G * p.nsplit * ssd::fused_w_pairs(d) *
+                 ssd::FUSED_W_PAIR_BYTES);
   if (p.nsplit > 1) {
     const size_t part = sizeof(float) * static_cast<size_t>(p.nsplit) * d.b * d.T * d.G * d.N;
     p.dB = take(part);
@@ -493,6 +496,7 @@ int bwd_impl(const char* who, const ssd_problem* prob, const void* x, const void
   s.dA_part = at<float>(workspace, plan.dA);
   s.dD_part = at<float>(workspace, plan.dD);
   s.done = at<unsigned>(workspace, plan.done);
+  s.wstrips = plan.fused ? at<uint16_t>(workspace, plan.wst) : nullptr;
   s.dB_part = plan.nsplit > 1 ? at<float>(workspace, plan.dB) : nullptr;
   s.dC_part = plan.nsplit > 1 ? at<float>(workspace, plan.dC) : nullptr;
   s.row_slots = plan.fused ? d.nb() : 0;

@@ -23,12 +23,13 @@
 //   * on the diagonal step (ib = jb): the diagonal of yx (dD), and
 //     U = dy_i H_c (MFMA, H_c in bf16 from LDS), the readout exp(s_i) U_i . C_i
 //     and its head sum exp(s_i) U_i (the state part of dC for block jb);
-//   * at the pass end: dC_i += sum_j W_ij B_j (+ the state part on the
-//     diagonal block) for every block ib >= jb, added in the L2 to what
-//     earlier passes of the same workgroup wrote (pass 0 stores; one lane owns
-//     each element in every pass and each pass's writes complete before the
-//     next pass's, so the sum order is fixed): dC of a block is complete after
-//     pass ib, and no other workgroup touches it; then dB_j = sum_i W_ij C_i.
+//   * at the pass end: the head-summed W of the blocks below the diagonal
+//     (ib > jb) to the workgroup's W area (bf16, one 8 KB block per pair
+//     (ib, jb), read back by pass ib); dC of block jb, whole and stored once:
+//     its state part plus sum_{j <= jb} W_{jb,j} B_j, the earlier passes' W
+//     blocks copied from the W area and their B tiles kept in the C slots
+//     those passes freed (C tile j is last read at the end of pass j); then
+//     dB_j = sum_i W_ij C_i.
 #include "ssd_async.hpp"
 #include "ssd_common.hpp"
 #include "ssd_launch.hpp"
@@ -41,6 +42,7 @@ constexpr int FT = FW * WAVE;       // threads per workgroup
 constexpr int TILE_N = 64 * 256;    // bytes of a 64 x 128 bf16 tile
 constexpr int TILE_P = 64 * 128;    // bytes of a 64 x 64 bf16 tile
 constexpr int STRIP = 32 * 32;      // bytes of a 32 x 16 bf16 strip
+constexpr int WPAIR_BYTES = FUSED_W_PAIR_BYTES;  // one 64 x 64 block of W in bf16
 constexpr int KP = PMAX / 32;
 constexpr int KN = NMAX / 32;
 static_assert(NBMAX <= 4, "the pass-end phase holds at most four blocks' W strips");
@@ -56,8 +58,8 @@ __device__ __forceinline__ float wave_tot(float v) { return lane_last(wave_scan(
 // rows i = 16 a + (lane % 16), columns j = 32 ks + 8 (lane / 16) .. +7.  Row i
 // lies in the strips of team i / 32, column j in the strip of wave j / 16 of
 // that team.
-__device__ __forceinline__ bf16x8 w_rows_frag(const lds_char* strips, int a, int ks) {
-  const int l = lane_id(), r = l & 15, q = l >> 4;
+__device__ __forceinline__ bf16x8 w_rows_frag(const lds_char* strips, int a, int ks, int l = lane_id()) {
+  const int r = l & 15, q = l >> 4;
   const int team = a >> 1, ri = 16 * (a & 1) + r;
   const lds_char* strip = strips + (4 * team + 2 * ks + (q >> 1)) * STRIP;
   return *(const __attribute__((address_space(3))) bf16x8*)(strip + strip_off(ri, 16 * (q & 1)));
@@ -143,6 +145,9 @@ __global__ __launch_bounds__(FT) void bwd_fused_bf16_kernel(
   // dB and dC (or this head split's partials) from the chunk's first row and the group's columns
   const LazyRsrc rdb{dB_out + static_cast<int64_t>(sp) * batch * T * GN + row0 * GN + static_cast<int64_t>(g) * N};
   const LazyRsrc rdc{dC_out + static_cast<int64_t>(sp) * batch * T * GN + row0 * GN + static_cast<int64_t>(g) * N};
+  // this workgroup's W area: the head-summed W of its off-diagonal block pairs, bf16
+  const int64_t wgi = ((static_cast<int64_t>(bi) * nc + c) * G + g) * nsplit + sp;
+  const LazyRsrc rws{s.wstrips + wgi * (nb * (nb - 1) / 2) * (WPAIR_BYTES / 2)};
 
   // x and dy tiles (64 rows of headdim), Gamma and H_c (headdim rows of
   // d_state): per-lane offsets computed once, the tile's first row as the
@@ -174,7 +179,6 @@ __global__ __launch_bounds__(FT) void bwd_fused_bf16_kernel(
   };
   auto load_first_gam = [&](int jbp) { tlg.issue(sGam, rg.get(), head_of(jbp, 0) * P * N * 2, P); };
 
-  unsigned written = 0;  // blocks of dC an earlier pass has written
   // pass 0's first tiles and every block's C tile (later passes read a subset)
   load_first_xdhd(0);
   load_first_b(0);
@@ -207,7 +211,7 @@ __global__ __launch_bounds__(FT) void bwd_fused_bf16_kernel(
     if (jb == 0)
       wait_vm<0>();
     else
-      wait_vm<2>();
+      wait_vm<4>();  // the first head's Gamma and the previous pass's B tile (read at this pass's end) may be in flight
     lds_barrier();
     f4 cbk[NBMAX][2];  // C.B^T: rows j of this wave, columns i = (jb + u) * 64 + ti + 16 tt + r
 #pragma unroll
@@ -639,14 +643,15 @@ __global__ __launch_bounds__(FT) void bwd_fused_bf16_kernel(
     }
 
     // ---- pass end.  The W strips of blocks u = 0..3 go to four free 8 KB
-    // slots; dC_i += sum_j W_ij B_j (k = j along the strips, against the B
-    // tile) plus the state part on the diagonal block, for every block
-    // ib >= jb; then dB_j = sum_i W_ij C_i + state terms over all rows i (k = i
-    // down the strips, against the C tiles).  The next pass's first tiles load
+    // slots; the strips of the blocks below the diagonal (ib > jb) also go to
+    // the workgroup's W area in global memory, read back by pass ib.  dC of
+    // the diagonal block is formed whole: its state part plus
+    // sum_{j <= jb} W_{jb,j} B_j, k = j along the strips (this pass's) or the
+    // W area (earlier passes'), against the B tile (j = jb) or the B tiles that
+    // earlier passes left in the freed C slots (j < jb); then
+    // dB_j = sum_i W_ij C_i + state terms over all rows i (k = i down the
+    // strips, against the C tiles).  The next pass's first tiles load
     // meanwhile.
-    // dC as earlier passes of this workgroup wrote it (the same lane, the same
-    // layout), for the blocks an earlier pass wrote: every load of the pass is
-    // issued first
     // element (row0 + 4q + e, col0 + r) of a [rows][G N] f32 array (dB, dC)
     // at byte offset voff + soff: the lane's part voff (OOB_OFFSET outside
     // the chunk or d_state) and the uniform part soff
@@ -659,21 +664,24 @@ __global__ __launch_bounds__(FT) void bwd_fused_bf16_kernel(
     auto gn_soff = [&](int row0_, int col0, int e) -> uint32_t {
       return (static_cast<uint32_t>(row0_ + e) * static_cast<uint32_t>(GN) + col0) * 4;
     };
-    float dco[NBMAX][4][4];
+    // W fragments (rows i = 16 a + (lane % 16) of block ib, k = j = 32 ks +
+    // 8 (lane / 16) .. + 7 of block j) in the W area: pair (ib, j), j < ib, at
+    // WPAIR_BYTES (ib (ib - 1) / 2 + j), fragment (a, ks) at 1 KB (2 a + ks),
+    // 16 bytes a lane.  This pass's pairs (jb, j < jb) are copied first, into
+    // slots the strips below leave free (the Gamma tile's, then dy buffer 1)
+    const uint32_t wlane = static_cast<uint32_t>(lg) * 16;
+    auto wfrag_off = [&](int ib, int j, int a, int ks) -> uint32_t {
+      return static_cast<uint32_t>((ib * (ib - 1) / 2 + j) * WPAIR_BYTES + (2 * a + ks) * 1024);
+    };
+    lds_char* const wprev[NBMAX - 1] = {sGam, sGam + WPAIR_BYTES, sDy[1]};
+    static_assert(2 * WPAIR_BYTES <= TILE_N && WPAIR_BYTES <= TILE_P, "earlier W pairs fit the free slots");
+    // (the wave index passes through an empty asm: copy addresses hoisted
+    // out of the pass loop would hold registers for the whole kernel)
+    int wo = w;
+    asm volatile("" : "+s"(wo));
 #pragma unroll
-    for (int u = 0; u < NBMAX; ++u) {
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int c0 = 16 * (4 * team + k), r0 = (jb + u) * BQ + 16 * wt;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          dco[u][k][e] = 0.f;
-          if (u < nib && ((written >> (jb + u)) & 1))
-            dco[u][k][e] = __uint_as_float(
-                __builtin_amdgcn_raw_buffer_load_b32(rdc.ptr(), gn_voff(r0, c0, e), gn_soff(r0, c0, e), 0));
-        }
-      }
-    }
+    for (int j = 0; j < NBMAX - 1; ++j)
+      if (j < jb) dma16_so(rws.get(), wprev[j] + wo * 1024, wlane, wfrag_off(jb, j, 0, 0) + wo * 1024);
     // x slot 0, dy buffer 0, H_c and the dt bits are free (the last head's
     // state step is done; the strips below use the other slots)
     if (jb + 1 < nb) load_first_xdhd(jb + 1);
@@ -681,37 +689,65 @@ __global__ __launch_bounds__(FT) void bwd_fused_bf16_kernel(
 #pragma unroll
     for (int u = 0; u < NBMAX; ++u)
       if (u < nib) put_strip(wset[u] + w * STRIP, ws[u]);
+    // the earlier W pairs must be in LDS; the next pass's first tiles (5
+    // copies) may be in flight
+    if (jb > 0) {
+      if (jb + 1 < nb)
+        wait_vm<5>();
+      else
+        wait_vm<0>();
+    }
     lds_barrier();
+    // the strips of blocks ib = jb + u > jb to the W area: wave w stores
+    // fragment (a, ks) = (w % 4, w / 4) of each.  Pass ib reads them after
+    // the waits and barriers of the passes between (each of its waves waits
+    // for every store it issued before the next pass's Gamma copy, then meets
+    // the others at a barrier), from lines no earlier load of this launch
+    // touched
 #pragma unroll
-    for (int u = 0; u < NBMAX; ++u) {
+    for (int u = 1; u < NBMAX; ++u) {
       if (u < nib) {
-        // dC of block ib = jb + u: rows i = 16 wt + 4q + e, columns n = 16 (4 team + k) + r
-        const ColsAt<16> ac16 = opaque(c16_);
-        f4 pc[4];
-        if (u == 0) {
+        // the lane passes through opaque_index: offsets hoisted out of the
+        // pass loop would be spilled, and a spill's reload waits for every
+        // copy in flight
+        const bf16x8 fw = w_rows_frag(wset[u], wt, team, opaque_index(lane_id()));
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, fw), rws.ptr(), wlane,
+                                               wfrag_off(jb + u, jb, 0, 0) + (2 * (wo & 3) + (wo >> 2)) * 1024, 0);
+      }
+    }
+    {
+      // dC of block jb: rows i = 16 wt + 4q + e, columns n = 16 (4 team + k) + r
+      const ColsAt<16> ac16 = opaque(c16_);
+      f4 pc[4];
 #pragma unroll
-          for (int k = 0; k < 4; ++k) pc[k] = ua[k];
-        } else {
-          zero(pc);
+      for (int k = 0; k < 4; ++k) pc[k] = ua[k];
+#pragma unroll
+      for (int j = 0; j < NBMAX; ++j) {
+        if (j <= jb) {
+          const lds_char* bt = j == jb ? sB : sCt + j * TILE_N;
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) {
+            bf16x8 fa, fb[4];
+            if (j == jb)
+              fa = w_rows_frag(wset[0], wt, ks);
+            else
+              fa = *(const __attribute__((address_space(3))) bf16x8*)(wprev[j < NBMAX - 1 ? j : 0] +
+                                                                       (2 * wt + ks) * 1024 + wlane);
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) fb[kk] = frag_cols(bt, 32 * ks, 16 * (4 * team + kk), ac16);
+            sched_ds_reads<5>();
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) pc[kk] = mfma(fa, fb[kk], pc[kk]);
+            sched_mfmas<4>();
+          }
         }
+      }
+      const int r0 = j0 + 16 * wt;
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          bf16x8 fa, fb[4];
-          fa = w_rows_frag(wset[u], wt, ks);
+      for (int k = 0; k < 4; ++k) {
+        const int c0 = 16 * (4 * team + k);
 #pragma unroll
-          for (int kk = 0; kk < 4; ++kk) fb[kk] = frag_cols(sB, 32 * ks, 16 * (4 * team + kk), ac16);
-          sched_ds_reads<5>();
-#pragma unroll
-          for (int kk = 0; kk < 4; ++kk) pc[kk] = mfma(fa, fb[kk], pc[kk]);
-          sched_mfmas<4>();
-        }
-        const int r0 = (jb + u) * BQ + 16 * wt;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const int c0 = 16 * (4 * team + k);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) store_f32(rdc.ptr(), dco[u][k][e] + pc[k][e], gn_voff(r0, c0, e), gn_soff(r0, c0, e));
-        }
+        for (int e = 0; e < 4; ++e) store_f32(rdc.ptr(), pc[k][e], gn_voff(r0, c0, e), gn_soff(r0, c0, e));
       }
     }
     lds_barrier();  // the B tile is no longer read
@@ -743,10 +779,11 @@ __global__ __launch_bounds__(FT) void bwd_fused_bf16_kernel(
 #pragma unroll
       for (int e = 0; e < 4; ++e) store_f32(rdb.ptr(), dbp[k][e] + dbs[k][e], gn_voff(r0, c0, e), gn_soff(r0, c0, e));
     }
-    written |= ((1u << nb) - 1) & ~((1u << jb) - 1);  // blocks jb .. nb - 1
     if (jb + 1 < nb) {
-      lds_barrier();  // the strips in the Gamma slot are no longer read
+      lds_barrier();  // the strips in the Gamma slot and C tile jb are no longer read
       load_first_gam(jb + 1);
+      // B rows of block jb into C tile jb's slot, for the dC of the later passes
+      tile_async<64, 16, FW>(sCt + jb * TILE_N, rb.get(), j0 * GNb + goff, GNb, vj, nch);
     }
   }  // pass
 

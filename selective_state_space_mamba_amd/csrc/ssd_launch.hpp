@@ -20,6 +20,10 @@ constexpr int STATE_PB = 16;
 inline int state_npb(const Dims& d) { return (d.P + STATE_PB - 1) / STATE_PB; }
 // per-wave partials of <Gamma_{c+1}, H_c> that the fused backward kernel writes per (b, chunk, head)
 constexpr int FUSED_GH_SLOTS = 8;
+// the fused backward kernel's W area: per workgroup one 64 x 64 bf16 block of
+// the head-summed W for each block pair (ib, j) below the diagonal
+constexpr int FUSED_W_PAIR_BYTES = 64 * 64 * 2;
+inline int fused_w_pairs(const Dims& d) { return d.nb() * (d.nb() - 1) / 2; }
 
 // Forward state passing: states[b,c,h] = state entering chunk c, final = state
 // after the last chunk.  `init` may be null (zero initial state), `final_state`
@@ -71,6 +75,7 @@ struct BwdScratch {
   float* dA_part;  // [b,nc,H]
   float* dD_part;  // [b,nc,nb,H]
   unsigned* done;  // one counter: the dt kernel's finished workgroups (zeroed by the row kernel)
+  uint16_t* wstrips;  // fused kernel: [b,nc,G,nsplit][fused_w_pairs] blocks of FUSED_W_PAIR_BYTES
   float* dB_part;  // [nsplit,b,T,G,N] or null when nsplit == 1
   float* dC_part;
   int row_slots;      // 0: rowM holds the row sums; else the number of slots to add
