@@ -51,8 +51,8 @@ KERNEL_SOURCES = {
 # Device kernels behind each profiled launch (bf16 variant first), as
 # substrings of the kernel names rocprofv3 records.
 DEVICE_KERNELS = {
-    "chunk_state_fwd": ("chunk_state_bf16_kernel<false>", "chunk_state_kernel"),
-    "chunk_state_bwd": ("chunk_state_bf16_kernel<true>", "chunk_state_kernel"),
+    "chunk_state_fwd": ("chunk_state_bf16_kernel<false", "chunk_state_kernel"),
+    "chunk_state_bwd": ("chunk_state_bf16_kernel<true", "chunk_state_kernel"),
     "chunk_out_fwd": ("out_fwd_bf16_kernel", "chunk_out_fwd_kernel"),
     "chunk_bwd_col": ("bwd_col_bf16_kernel", "chunk_bwd_col_kernel"),
     "chunk_bwd_row": ("bwd_row_bf16_kernel", "chunk_bwd_row_kernel"),
@@ -62,8 +62,15 @@ DEVICE_KERNELS = {
 
 
 def _device_match(kernel: str, name: str) -> bool:
-    return any(n + "(" in name or n + "<" in name or (n.endswith(">") and n in name)
-               for n in DEVICE_KERNELS.get(kernel, (kernel + "_kernel",)))
+    """Whether the recorded kernel name holds one of the kernel's device names
+    followed by its argument or template list (or the next template argument)."""
+    for n in DEVICE_KERNELS.get(kernel, (kernel + "_kernel",)):
+        i = name.find(n)
+        while i >= 0:
+            if name[i + len(n):i + len(n) + 1] in ("(", "<", ">", ","):
+                return True
+            i = name.find(n, i + 1)
+    return False
 
 
 def log(*a):
@@ -169,10 +176,16 @@ def algorithmic_flops(cfg, kernel: str) -> float:
 
 
 def source_digest(kernel: str) -> str:
+    """Digest of the code of the kernel's source files: comments removed and
+    white space collapsed, so that a change of comments keeps the counters
+    taken with that code."""
     h = hashlib.sha256()
     for fn in KERNEL_SOURCES.get(kernel, []):
-        with open(os.path.join(ROOT, "selective_state_space_mamba_amd", "csrc", fn), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "selective_state_space_mamba_amd", "csrc", fn), encoding="utf-8") as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -22,9 +22,11 @@
 // with time along its rows, is scaled in place by the per-step weights (one
 // 16-byte chunk per thread, once for the four waves that read each row) and
 // is read down its rows with the LDS transpose read; the B (or C) tile
-// likewise, unscaled.  Tiles come in 128-step slabs, double-buffered and
-// copied asynchronously while the previous slab computes, together with the
-// chunk's dt series and (backward) the f32 state tile H_c.  Every wave
+// likewise, unscaled.  Tiles come in slabs of 128 steps (64 when the grid
+// is larger than one workgroup per CU, so that two share a CU),
+// double-buffered and copied asynchronously while the previous slab
+// computes, together with the chunk's dt series and (backward, when H_c is
+// read) the f32 state tile H_c.  Every wave
 // computes the within-chunk scan itself (DPP) into its own weight row.
 #include "ssd_async.hpp"
 #include "ssd_common.hpp"
