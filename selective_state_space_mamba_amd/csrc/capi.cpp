@@ -120,6 +120,23 @@ int general_fwd_nsplit(const ssd::Dims& d) {
   const int s = choose_nsplit(d, kFwdTarget, false);
   return d.hpg() / s >= 3 ? s : choose_nsplit(d, kBwdTarget, false);
 }
+// Paired row blocks (nb - 1 - k and k in one workgroup) give every workgroup
+// the same work, but half the workgroups: taken when the paired grid still
+// fills the CUs once with at least three heads per workgroup (long workload,
+// 64 heads: 256 workgroups of 32 heads and two blocks instead of 512 of 32
+// heads and one); the split is then the smallest that does.
+struct GeneralFwdShape {
+  int nsplit;
+  bool paired;
+};
+GeneralFwdShape general_fwd_shape(const ssd::Dims& d) {
+  const int64_t base = static_cast<int64_t>(d.b) * d.nc() * d.G * ((d.nb() + 1) / 2);
+  const int hpg = d.hpg();
+  if (d.nb() > 1)
+    for (int s = 1; s <= hpg / 3; ++s)
+      if (hpg % s == 0 && base * s >= kBwdTarget) return {s, true};
+  return {general_fwd_nsplit(d), false};
+}
 
 struct FwdPlan {
   size_t states = 0, hbf = 0, send = 0, total = 0;
@@ -385,10 +402,11 @@ int ssd_fwd_ex(const ssd_problem* prob, const void* x, const void* dt, const flo
   if (plan.bf16)
     SSD_LAUNCH(ssd::launch_out_fwd_bf16(d, choose_nsplit(d, kFwdTarget, true), x, B, C, dt, A_log, D, hbf, y, st),
                "chunk_out_fwd");
-  else
-    SSD_LAUNCH(ssd::launch_chunk_out_fwd(d, act, general_fwd_nsplit(d), x, B, C, dt, A_log, D,
-                                         states, y, st),
+  else {
+    const GeneralFwdShape sh = general_fwd_shape(d);
+    SSD_LAUNCH(ssd::launch_chunk_out_fwd(d, act, sh.nsplit, sh.paired, x, B, C, dt, A_log, D, states, y, st),
                "chunk_out_fwd");
+  }
   return ok();
 }
 

@@ -34,7 +34,7 @@ __global__ __launch_bounds__(NT8) void chunk_out_fwd_kernel(
     const TI* __restrict__ x, const TI* __restrict__ Bm, const TI* __restrict__ Cm,
     const TI* __restrict__ dt, const float* __restrict__ A_log, const float* __restrict__ D,
     const float* __restrict__ hstates, TI* __restrict__ y, int T, int H, int P, int N, int G, int Q,
-    int nsplit) {
+    int nsplit, int paired) {
   typedef typename Op<BF>::T OT;
   constexpr int PAD = BF ? 8 : 4;
   constexpr int JW = OutSlab<BF>::JW;  // chunk columns staged per slab
@@ -54,9 +54,13 @@ __global__ __launch_bounds__(NT8) void chunk_out_fwd_kernel(
 
   const int nc = T / Q, nb = (Q + BQ - 1) / BQ;
   const int hpg = H / G, hps = hpg / nsplit;
+  // paired: row blocks nb - 1 - k and then k, so that every workgroup has the
+  // same number of (row block, column block) tiles; else one block, the
+  // heavier ones first
+  const int nunit = paired ? (nb + 1) >> 1 : nb;
   int idx = xcd_logical_block(blockIdx.x, gridDim.x);
-  const int ib = nb - 1 - idx % nb;  // heavier row blocks first
-  idx /= nb;
+  const int unit = idx % nunit;
+  idx /= nunit;
   const int sp = idx % nsplit;
   idx /= nsplit;
   const int g = idx % G;
@@ -68,6 +72,10 @@ __global__ __launch_bounds__(NT8) void chunk_out_fwd_kernel(
   const int rw = w & 3, cw = w >> 2;
   (void)l;
   const int64_t row0 = static_cast<int64_t>(bi) * T + static_cast<int64_t>(c) * Q;
+  for (int pass = 0; pass < 2; ++pass) {
+  const int ib = pass ? unit : nb - 1 - unit;
+  if (pass && (!paired || ib == nb - 1 - unit)) break;
+  if (pass) __syncthreads();  // the first block's last head is done with sC and sU
   const int i0 = ib * BQ;
   const int vi = min(BQ, Q - i0);
   const int jend = min(Q, i0 + BQ);  // columns j < jend are needed
@@ -204,22 +212,23 @@ __global__ __launch_bounds__(NT8) void chunk_out_fwd_kernel(
         }
       }
   }
+  }  // pass
 }
 
-hipError_t launch_chunk_out_fwd(const Dims& d, DType act, int nsplit, const void* x, const void* B,
+hipError_t launch_chunk_out_fwd(const Dims& d, DType act, int nsplit, bool paired, const void* x, const void* B,
                                 const void* C, const void* dt, const float* A_log, const float* D,
                                 const float* states, void* y, hipStream_t st) {
-  const int64_t nblk = static_cast<int64_t>(d.b) * d.nc() * d.G * nsplit * d.nb();
+  const int64_t nblk = static_cast<int64_t>(d.b) * d.nc() * d.G * nsplit * (paired ? (d.nb() + 1) / 2 : d.nb());
   if (act == BF16) {
     hipLaunchKernelGGL((chunk_out_fwd_kernel<uint16_t, true>), dim3(nblk), dim3(NT8), 0, st,
                        static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(B),
                        static_cast<const uint16_t*>(C), static_cast<const uint16_t*>(dt), A_log, D, states,
-                       static_cast<uint16_t*>(y), d.T, d.H, d.P, d.N, d.G, d.Q, nsplit);
+                       static_cast<uint16_t*>(y), d.T, d.H, d.P, d.N, d.G, d.Q, nsplit, paired ? 1 : 0);
   } else {
     hipLaunchKernelGGL((chunk_out_fwd_kernel<float, false>), dim3(nblk), dim3(NT8), 0, st,
                        static_cast<const float*>(x), static_cast<const float*>(B),
                        static_cast<const float*>(C), static_cast<const float*>(dt), A_log, D, states,
-                       static_cast<float*>(y), d.T, d.H, d.P, d.N, d.G, d.Q, nsplit);
+                       static_cast<float*>(y), d.T, d.H, d.P, d.N, d.G, d.Q, nsplit, paired ? 1 : 0);
   }
   return hipGetLastError();
 }

@@ -99,7 +99,9 @@ __device__ __forceinline__ typename Op<BF>::V fetch(const typename Op<BF>::T* p,
 // A is the view (row = output row, k) and B the view (row = output column, k).
 // K must be a multiple of Op<BF>::KS; the LDS operands are zero beyond the
 // logical extent.
-template <bool BF, bool AKC, bool BKC, int NT>
+// V4 (f32 only): the 16-byte reads below; false keeps one 4-byte read per
+// k-step (fewer registers held across the reads).
+template <bool BF, bool AKC, bool BKC, int NT, bool V4 = true>
 __device__ __forceinline__ void wave_gemm(f4 (&acc)[NT], const typename Op<BF>::T* A, int asr,
                                           int ask, const typename Op<BF>::T* B, int bsr, int bsk,
                                           int K) {
@@ -107,11 +109,47 @@ __device__ __forceinline__ void wave_gemm(f4 (&acc)[NT], const typename Op<BF>::
   constexpr int KS = Op<BF>::KS;
   if (K <= 0) return;
   if constexpr (!BF) {
-    // f32: one element per lane per fragment and K = 4 per MFMA, so the reads
-    // of KU k-steps are issued together ahead of their MFMAs (one wait per
-    // batch instead of one LDS round trip per k-step); same accumulation order
-    constexpr int KU = NT <= 4 ? 8 : 4;
+    // f32: K = 4 per MFMA, one element per lane.  Lane (r, q) of MFMA u of a
+    // group of four takes k = k0 + 4q + u (both operands alike, so the four
+    // MFMAs still sum over k0 .. k0 + 15 exactly once): a k-contiguous
+    // operand then comes as one 16-byte read of four consecutive k per lane
+    // instead of four 4-byte reads.  The reads of NG groups (two for up to
+    // four output tiles, else one: the same registers as eight or four
+    // k-steps of single reads) are issued ahead of their MFMAs.
+    constexpr int NG = NT <= 4 ? 2 : 1;
     int k0 = 0;
+    for (; V4 && k0 + 16 * NG <= K; k0 += 16 * NG) {
+      float a[NG][4], b[NG][NT][4];
+      const int l = lane_id(), r = l & 15, q = l >> 4;
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        const int kg = k0 + 16 * g + 4 * q;
+        if constexpr (AKC) {
+          const float4 v = *reinterpret_cast<const float4*>(A + r * asr + kg);
+          a[g][0] = v.x, a[g][1] = v.y, a[g][2] = v.z, a[g][3] = v.w;
+        } else {
+#pragma unroll
+          for (int u = 0; u < 4; ++u) a[g][u] = A[r * asr + (kg + u) * ask];
+        }
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          if constexpr (BKC) {
+            const float4 v = *reinterpret_cast<const float4*>(B + (16 * t + r) * bsr + kg);
+            b[g][t][0] = v.x, b[g][t][1] = v.y, b[g][t][2] = v.z, b[g][t][3] = v.w;
+          } else {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) b[g][t][u] = B[(16 * t + r) * bsr + (kg + u) * bsk];
+          }
+        }
+      }
+#pragma unroll
+      for (int g = 0; g < NG; ++g)
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int t = 0; t < NT; ++t) acc[t] = mfma(a[g][u], b[g][t][u], acc[t]);
+    }
+    constexpr int KU = NT <= 4 ? 8 : 4;
     for (; k0 + KU * KS <= K; k0 += KU * KS) {
       float a[KU], b[KU][NT];
 #pragma unroll

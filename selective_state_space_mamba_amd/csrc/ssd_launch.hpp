@@ -59,7 +59,9 @@ hipError_t launch_out_fwd_bf16(const Dims& d, int nsplit, const void* x, const v
                                const void* dt, const float* A_log, const float* D, const void* hbf, void* y,
                                hipStream_t st);
 
-hipError_t launch_chunk_out_fwd(const Dims& d, DType act, int nsplit, const void* x, const void* B,
+// paired: a workgroup takes row blocks nb - 1 - k and k of its chunk (grid
+// b nc G nsplit ceil(nb / 2)); else one row block (grid b nc G nsplit nb).
+hipError_t launch_chunk_out_fwd(const Dims& d, DType act, int nsplit, bool paired, const void* x, const void* B,
                                 const void* C, const void* dt, const float* A_log, const float* D,
                                 const float* states, void* y, hipStream_t st);
 

@@ -235,7 +235,9 @@ __global__ __launch_bounds__(NTHREADS, 2) void chunk_sum_f32_kernel(
     tb.store(sB, LDX);
     if (sl + 1 < nslab) load(sl + 1);
     __syncthreads();
-    wave_gemm<false, true, true, NW / 16>(acc, sX + 16 * w * LDX, LDX, 1, sB, LDX, 1,
+    // one 4-byte read per k-step: the 16-byte reads cost this kernel a wave
+    // per SIMD of occupancy and were slower (long workload 318 -> 353 us)
+    wave_gemm<false, true, true, NW / 16, false>(acc, sX + 16 * w * LDX, LDX, 1, sB, LDX, 1,
                                            round_up(min(SUM_SJ, Q - sl * SUM_SJ), Op<false>::KS));
   }
   const int64_t base = ((static_cast<int64_t>(bi) * nc + c) * H + h) * PN;
