@@ -125,17 +125,22 @@ int general_fwd_nsplit(const ssd::Dims& d) {
 // fills the CUs once with at least three heads per workgroup (long workload,
 // 64 heads: 256 workgroups of 32 heads and two blocks instead of 512 of 32
 // heads and one); the split is then the smallest that does.
-struct GeneralFwdShape {
+// The same choice for the general backward's column and row kernels.
+struct GeneralShape {
   int nsplit;
   bool paired;
 };
-GeneralFwdShape general_fwd_shape(const ssd::Dims& d) {
+int general_paired_nsplit(const ssd::Dims& d) {
   const int64_t base = static_cast<int64_t>(d.b) * d.nc() * d.G * ((d.nb() + 1) / 2);
   const int hpg = d.hpg();
   if (d.nb() > 1)
     for (int s = 1; s <= hpg / 3; ++s)
-      if (hpg % s == 0 && base * s >= kBwdTarget) return {s, true};
-  return {general_fwd_nsplit(d), false};
+      if (hpg % s == 0 && base * s >= kBwdTarget) return s;
+  return 0;
+}
+GeneralShape general_fwd_shape(const ssd::Dims& d) {
+  const int s = general_paired_nsplit(d);
+  return s ? GeneralShape{s, true} : GeneralShape{general_fwd_nsplit(d), false};
 }
 
 struct FwdPlan {
@@ -146,6 +151,7 @@ struct BwdPlan {
   size_t states = 0, gamma = 0, hbf = 0, gh = 0, rowM = 0, colE = 0, diagE = 0, Rp = 0, dsoff = 0, dA = 0, dD = 0,
          done = 0, wst = 0, dB = 0, dC = 0, send = 0, total = 0;
   int nsplit = 1;
+  bool paired = false;  // general column and row kernels: two row blocks per workgroup
   bool bf16 = false;   // bf16 kernels with asynchronous staging (they also need a bf16 copy of the states)
   bool fused = false;  // the bf16 column and row work in one kernel (row sums of M in nb slots)
 };
@@ -195,6 +201,10 @@ BwdPlan plan_bwd(const ssd::Dims& d, bool has_states, bool bf16) {
   // the fused kernel takes one workgroup per (batch, chunk, group) and head split
   p.nsplit = p.fused ? choose_nsplit_base(d, kBwdTarget, static_cast<int64_t>(d.b) * d.nc() * d.G)
                      : choose_nsplit(d, kBwdTarget, bf16);
+  if (!bf16) {
+    const int s = general_paired_nsplit(d);
+    if (s) p.nsplit = s, p.paired = true;
+  }
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t o = off;
@@ -403,7 +413,7 @@ int ssd_fwd_ex(const ssd_problem* prob, const void* x, const void* dt, const flo
     SSD_LAUNCH(ssd::launch_out_fwd_bf16(d, choose_nsplit(d, kFwdTarget, true), x, B, C, dt, A_log, D, hbf, y, st),
                "chunk_out_fwd");
   else {
-    const GeneralFwdShape sh = general_fwd_shape(d);
+    const GeneralShape sh = general_fwd_shape(d);
     SSD_LAUNCH(ssd::launch_chunk_out_fwd(d, act, sh.nsplit, sh.paired, x, B, C, dt, A_log, D, states, y, st),
                "chunk_out_fwd");
   }
@@ -583,10 +593,10 @@ int bwd_impl(const char* who, const ssd_problem* prob, const void* x, const void
                                         plan.nsplit > 1 ? s.dC_part : dC, s, st),
                "chunk_bwd_row");
   } else {
-    SSD_LAUNCH(ssd::launch_chunk_bwd_col(d, act, dyt, plan.nsplit, x, B, C, dt, dy, A_log, D, gamma, dx,
+    SSD_LAUNCH(ssd::launch_chunk_bwd_col(d, act, dyt, plan.nsplit, plan.paired, x, B, C, dt, dy, A_log, D, gamma, dx,
                                          plan.nsplit > 1 ? s.dB_part : dB, s, st),
                "chunk_bwd_col");
-    SSD_LAUNCH(ssd::launch_chunk_bwd_row(d, act, dyt, plan.nsplit, x, B, C, dt, dy, A_log, states,
+    SSD_LAUNCH(ssd::launch_chunk_bwd_row(d, act, dyt, plan.nsplit, plan.paired, x, B, C, dt, dy, A_log, states,
                                          plan.nsplit > 1 ? s.dC_part : dC, s, st),
                "chunk_bwd_row");
   }

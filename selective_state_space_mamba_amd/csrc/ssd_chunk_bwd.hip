@@ -65,7 +65,9 @@ constexpr int cmax(int a, int b) { return a > b ? a : b; }
 
 constexpr int NT8 = 512;
 
-template <typename TI, typename TY, bool BF>
+// PAIRED: a workgroup takes column blocks k and then nb - 1 - k (its own
+// instantiation: the pass loop costs registers that the one-block form keeps)
+template <typename TI, typename TY, bool BF, bool PAIRED>
 __global__ __launch_bounds__(NT8) void chunk_bwd_col_kernel(
     const TI* __restrict__ x, const TI* __restrict__ Bm, const TI* __restrict__ Cm,
     const TI* __restrict__ dt, const TY* __restrict__ dy, const float* __restrict__ A_log,
@@ -105,9 +107,12 @@ __global__ __launch_bounds__(NT8) void chunk_bwd_col_kernel(
 
   const int nc = T / Q, nb = (Q + BQ - 1) / BQ;
   const int hpg = H / G, hps = hpg / nsplit;
+  // paired: column blocks k and then nb - 1 - k, so that every workgroup has
+  // the same number of (row block, column block) tiles; else one block
+  const int nunit = PAIRED ? (nb + 1) >> 1 : nb;
   int idx = xcd_logical_block(blockIdx.x, gridDim.x);
-  const int jb = idx % nb;
-  idx /= nb;
+  const int unit = idx % nunit;
+  idx /= nunit;
   const int sp = idx % nsplit;
   idx /= nsplit;
   const int g = idx % G;
@@ -118,6 +123,16 @@ __global__ __launch_bounds__(NT8) void chunk_bwd_col_kernel(
   const int tid = threadIdx.x, w = wave_id(), l = lane_id(), r = l & 15, q = l >> 4;
   const int rw = w & 3, cw = w >> 2;
   const int64_t row0 = static_cast<int64_t>(bi) * T + static_cast<int64_t>(c) * Q;
+#pragma unroll 1
+  for (int pass = 0; pass < (PAIRED ? 2 : 1); ++pass) {
+  const int jb = pass ? nb - 1 - unit : unit;
+  if (pass && jb == unit) break;
+  if (pass) __syncthreads();  // the first block is done with every tile
+  // paired: the lane indices taken afresh in each pass, so that offsets
+  // derived from them are not hoisted out of the pass loop and held across it
+  const int lp = PAIRED ? opaque_index(lane_id()) : lane_id();
+  const int l = lp, r = lp & 15, q = lp >> 4;
+  (void)l;
   const int j0 = jb * BQ, vj = min(BQ, Q - j0);
   const int i_lo = j0;                          // rows i >= j0 feed this column block
   const int nsl = (Q - i_lo + IW - 1) / IW;     // slabs of i-rows
@@ -383,7 +398,7 @@ __global__ __launch_bounds__(NT8) void chunk_bwd_col_kernel(
     else
       wave_gemm<BF, true, false, 4>(dbs, sWt + 16 * rw * LDI, LDI, 1, sCf + 64 * cw, 1, LDN, kw);
   }
-  const int64_t batch = gridDim.x / (nb * nsplit * G * nc);
+  const int64_t batch = gridDim.x / (nunit * nsplit * G * nc);
   float* dBo = dB_out + static_cast<int64_t>(sp) * batch * T * GN;
 #pragma unroll
   for (int t = 0; t < 4; ++t)
@@ -392,6 +407,7 @@ __global__ __launch_bounds__(NT8) void chunk_bwd_col_kernel(
       const int jq = j0 + 16 * rw + 4 * q + e, n = 64 * cw + 16 * t + r;
       if (jq < Q && n < N) dBo[(row0 + jq) * GN + static_cast<int64_t>(g) * N + n] = dbs[t][e];
     }
+  }  // pass
 }
 
 // --------------------------------------------------------------- row kernel
@@ -402,7 +418,8 @@ __global__ __launch_bounds__(NT8) void chunk_bwd_col_kernel(
 // incoming-state term U = dy H_c (rows i, d_state columns) uses rows i 16*rw,
 // columns n 64*cw..+63, as does dC.
 
-template <typename TI, typename TY, bool BF>
+// PAIRED: row blocks nb - 1 - k and then k (see the column kernel)
+template <typename TI, typename TY, bool BF, bool PAIRED>
 __global__ __launch_bounds__(NT8) void chunk_bwd_row_kernel(
     const TI* __restrict__ x, const TI* __restrict__ Bm, const TI* __restrict__ Cm,
     const TI* __restrict__ dt, const TY* __restrict__ dy, const float* __restrict__ A_log,
@@ -438,9 +455,12 @@ __global__ __launch_bounds__(NT8) void chunk_bwd_row_kernel(
 
   const int nc = T / Q, nb = (Q + BQ - 1) / BQ;
   const int hpg = H / G, hps = hpg / nsplit;
+  // paired: row blocks nb - 1 - k and then k (equal work per workgroup);
+  // else one block, the heavier ones first
+  const int nunit = PAIRED ? (nb + 1) >> 1 : nb;
   int idx = xcd_logical_block(blockIdx.x, gridDim.x);
-  const int ib = nb - 1 - idx % nb;  // heavier row blocks first
-  idx /= nb;
+  const int unit = idx % nunit;
+  idx /= nunit;
   const int sp = idx % nsplit;
   idx /= nsplit;
   const int g = idx % G;
@@ -451,6 +471,15 @@ __global__ __launch_bounds__(NT8) void chunk_bwd_row_kernel(
   const int tid = threadIdx.x, w = wave_id(), l = lane_id(), r = l & 15, q = l >> 4;
   const int rw = w & 3, cw = w >> 2;
   const int64_t row0 = static_cast<int64_t>(bi) * T + static_cast<int64_t>(c) * Q;
+#pragma unroll 1
+  for (int pass = 0; pass < (PAIRED ? 2 : 1); ++pass) {
+  const int ib = pass ? unit : nb - 1 - unit;
+  if (pass && ib == nb - 1 - unit) break;
+  if (pass) __syncthreads();  // the first block is done with every tile
+  // paired: the lane indices taken afresh in each pass (see the column kernel)
+  const int lp = PAIRED ? opaque_index(lane_id()) : lane_id();
+  const int l = lp, r = lp & 15, q = lp >> 4;
+  (void)l;
   const int i0 = ib * BQ, vi = min(BQ, Q - i0);
   const int jend = min(Q, i0 + BQ);
   const int nsl = (jend + JW - 1) / JW;
@@ -681,7 +710,7 @@ __global__ __launch_bounds__(NT8) void chunk_bwd_row_kernel(
     else
       wave_gemm<BF, true, false, 4>(dca, sW + 16 * rw * LDJ, LDJ, 1, sBf + 64 * cw, 1, LDN, kw);
   }
-  const int64_t batch = gridDim.x / (nb * nsplit * G * nc);
+  const int64_t batch = gridDim.x / (nunit * nsplit * G * nc);
   float* dCo = dC_out + static_cast<int64_t>(sp) * batch * T * GN;
 #pragma unroll
   for (int t = 0; t < 4; ++t)
@@ -690,6 +719,7 @@ __global__ __launch_bounds__(NT8) void chunk_bwd_row_kernel(
       const int iq = i0 + 16 * rw + 4 * q + e, n = 64 * cw + 16 * t + r;
       if (iq < Q && n < N) dCo[(row0 + iq) * GN + static_cast<int64_t>(g) * N + n] = dca[t][e];
     }
+  }  // pass
 }
 
 // ------------------------------------------------------------- dt finalize
@@ -876,63 +906,65 @@ __global__ void copy_kernel(float* __restrict__ dst, const float* __restrict__ s
 
 // ---------------------------------------------------------------- launchers
 
-static int64_t nblocks_chunk(const Dims& d, int nsplit) {
-  return static_cast<int64_t>(d.b) * d.nc() * d.G * nsplit * d.nb();
+static int64_t nblocks_chunk(const Dims& d, int nsplit, bool paired) {
+  return static_cast<int64_t>(d.b) * d.nc() * d.G * nsplit * (paired ? (d.nb() + 1) / 2 : d.nb());
 }
 
 template <typename TI, typename TY, bool BF>
-static void col_launch(const Dims& d, int nsplit, const void* x, const void* B, const void* C, const void* dt,
+static void col_launch(const Dims& d, int nsplit, bool paired, const void* x, const void* B, const void* C, const void* dt,
                        const void* dy, const float* A_log, const float* D, const void* gamma, float* dx,
                        float* dB_out, const BwdScratch& s, hipStream_t st) {
-  hipLaunchKernelGGL((chunk_bwd_col_kernel<TI, TY, BF>), dim3(nblocks_chunk(d, nsplit)), dim3(NT8), 0, st,
+  hipLaunchKernelGGL((paired ? chunk_bwd_col_kernel<TI, TY, BF, true> : chunk_bwd_col_kernel<TI, TY, BF, false>),
+                     dim3(nblocks_chunk(d, nsplit, paired)), dim3(NT8), 0, st,
                      static_cast<const TI*>(x), static_cast<const TI*>(B), static_cast<const TI*>(C),
                      static_cast<const TI*>(dt), static_cast<const TY*>(dy), A_log, D,
                      static_cast<const typename Op<BF>::T*>(gamma), dx, dB_out, s.colE,
                      s.diagE, s.Rp, d.T, d.H, d.P, d.N, d.G, d.Q, nsplit);
 }
 
-hipError_t launch_chunk_bwd_col(const Dims& d, DType act, DType dyt, int nsplit, const void* x,
+hipError_t launch_chunk_bwd_col(const Dims& d, DType act, DType dyt, int nsplit, bool paired, const void* x,
                                 const void* B, const void* C, const void* dt, const void* dy,
                                 const float* A_log, const float* D, const void* gamma, float* dx,
                                 float* dB_out, const BwdScratch& s, hipStream_t st) {
   if (act == BF16) {
     if (dyt == BF16)
-      col_launch<uint16_t, uint16_t, true>(d, nsplit, x, B, C, dt, dy, A_log, D, gamma, dx, dB_out, s, st);
+      col_launch<uint16_t, uint16_t, true>(d, nsplit, paired, x, B, C, dt, dy, A_log, D, gamma, dx, dB_out, s, st);
     else
-      col_launch<uint16_t, float, true>(d, nsplit, x, B, C, dt, dy, A_log, D, gamma, dx, dB_out, s, st);
+      col_launch<uint16_t, float, true>(d, nsplit, paired, x, B, C, dt, dy, A_log, D, gamma, dx, dB_out, s, st);
   } else {
     if (dyt == BF16)
-      col_launch<float, uint16_t, false>(d, nsplit, x, B, C, dt, dy, A_log, D, gamma, dx, dB_out, s, st);
+      col_launch<float, uint16_t, false>(d, nsplit, paired, x, B, C, dt, dy, A_log, D, gamma, dx, dB_out, s, st);
     else
-      col_launch<float, float, false>(d, nsplit, x, B, C, dt, dy, A_log, D, gamma, dx, dB_out, s, st);
+      col_launch<float, float, false>(d, nsplit, paired, x, B, C, dt, dy, A_log, D, gamma, dx, dB_out, s, st);
   }
   return hipGetLastError();
 }
 
 template <typename TI, typename TY, bool BF>
-static void row_launch(const Dims& d, int nsplit, const void* x, const void* B, const void* C, const void* dt,
+static void row_launch(const Dims& d, int nsplit, bool paired, const void* x, const void* B, const void* C, const void* dt,
                        const void* dy, const float* A_log, const float* states, float* dC_out, const BwdScratch& s,
                        hipStream_t st) {
-  hipLaunchKernelGGL((chunk_bwd_row_kernel<TI, TY, BF>), dim3(nblocks_chunk(d, nsplit)), dim3(NT8), 0, st,
+  hipLaunchKernelGGL((paired ? chunk_bwd_row_kernel<TI, TY, BF, true> : chunk_bwd_row_kernel<TI, TY, BF, false>),
+                     dim3(nblocks_chunk(d, nsplit, paired)), dim3(NT8), 0, st,
                      static_cast<const TI*>(x), static_cast<const TI*>(B), static_cast<const TI*>(C),
                      static_cast<const TI*>(dt), static_cast<const TY*>(dy), A_log, states, dC_out, s.rowM, s.dsoff,
                      s.dD_part, s.done, d.T, d.H, d.P, d.N, d.G, d.Q, nsplit);
 }
 
-hipError_t launch_chunk_bwd_row(const Dims& d, DType act, DType dyt, int nsplit, const void* x,
+hipError_t launch_chunk_bwd_row(const Dims& d, DType act, DType dyt, int nsplit, bool paired, const void* x,
                                 const void* B, const void* C, const void* dt, const void* dy,
                                 const float* A_log, const float* states, float* dC_out,
                                 const BwdScratch& s, hipStream_t st) {
   if (act == BF16) {
     if (dyt == BF16)
-      row_launch<uint16_t, uint16_t, true>(d, nsplit, x, B, C, dt, dy, A_log, states, dC_out, s, st);
+      row_launch<uint16_t, uint16_t, true>(d, nsplit, paired, x, B, C, dt, dy, A_log, states, dC_out, s, st);
     else
-      row_launch<uint16_t, float, true>(d, nsplit, x, B, C, dt, dy, A_log, states, dC_out, s, st);
+      row_launch<uint16_t, float, true>(d, nsplit, paired, x, B, C, dt, dy, A_log, states, dC_out, s, st);
   } else {
     if (dyt == BF16)
-      row_launch<float, uint16_t, false>(d, nsplit, x, B, C, dt, dy, A_log, states, dC_out, s, st);
+      row_launch<float, uint16_t, false>(d, nsplit, paired, x, B, C, dt, dy, A_log, states, dC_out, s, st);
     else
-      row_launch<float, float, false>(d, nsplit, x, B, C, dt, dy, A_log, states, dC_out, s, st);
+      row_launch<float, float, false>(d, nsplit, paired, x, B, C, dt, dy, A_log, states, dC_out, s, st);
   }
   return hipGetLastError();
 }

@@ -20,6 +20,7 @@
 // whole chunk width at once (one slab); f32 operands go 64 columns at a time.
 // 8 waves: wave (rw, cw) = (w % 4, w / 4) owns rows 16*rw..+15 and columns
 // 32*cw..+31 of every 64 x 64 tile, so two waves share each SIMD.
+#include "ssd_async.hpp"
 #include "ssd_common.hpp"
 #include "ssd_launch.hpp"
 
@@ -72,10 +73,14 @@ __global__ __launch_bounds__(NT8) void chunk_out_fwd_kernel(
   const int rw = w & 3, cw = w >> 2;
   (void)l;
   const int64_t row0 = static_cast<int64_t>(bi) * T + static_cast<int64_t>(c) * Q;
+#pragma unroll 1
   for (int pass = 0; pass < 2; ++pass) {
   const int ib = pass ? unit : nb - 1 - unit;
   if (pass && (!paired || ib == nb - 1 - unit)) break;
   if (pass) __syncthreads();  // the first block's last head is done with sC and sU
+  // the lane indices taken afresh in each pass: offsets derived from them
+  // would otherwise be hoisted out of the pass loop and held across it
+  const int r = opaque_index(lane_id()) & 15, q = opaque_index(lane_id()) >> 4;
   const int i0 = ib * BQ;
   const int vi = min(BQ, Q - i0);
   const int jend = min(Q, i0 + BQ);  // columns j < jend are needed

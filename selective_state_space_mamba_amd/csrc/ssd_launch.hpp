@@ -84,12 +84,14 @@ struct BwdScratch {
   int64_t slot_elems;  // b * H * T: elements of one row-sum slot
 };
 
-hipError_t launch_chunk_bwd_col(const Dims& d, DType act, DType dyt, int nsplit, const void* x,
+// paired: a workgroup takes blocks k and nb - 1 - k of its chunk (grid
+// b nc G nsplit ceil(nb / 2)); else one block (grid b nc G nsplit nb).
+hipError_t launch_chunk_bwd_col(const Dims& d, DType act, DType dyt, int nsplit, bool paired, const void* x,
                                 const void* B, const void* C, const void* dt, const void* dy,
                                 const float* A_log, const float* D, const void* gamma, float* dx,
                                 float* dB_out, const BwdScratch& s, hipStream_t st);
 
-hipError_t launch_chunk_bwd_row(const Dims& d, DType act, DType dyt, int nsplit, const void* x,
+hipError_t launch_chunk_bwd_row(const Dims& d, DType act, DType dyt, int nsplit, bool paired, const void* x,
                                 const void* B, const void* C, const void* dt, const void* dy,
                                 const float* A_log, const float* states, float* dC_out,
                                 const BwdScratch& s, hipStream_t st);
