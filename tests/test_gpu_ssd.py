@@ -78,6 +78,25 @@ def test_f32_three_heads_per_group():
     compare(gpu_ssd(cfg, d), oracle_ssd(d, cfg.chunk), TOL["f32"], label="f32 hpg=3 P=40")
 
 
+@pytest.mark.parametrize("dy_dtype", ["f32", "f32dy_bf16act"])
+def test_paired_general_blocks(dy_dtype):
+    # the general forward output, column and row kernels with paired blocks
+    # (a workgroup takes blocks k and nb - 1 - k): 64 chunks of 200 steps (three
+    # full 64-row blocks and an 8-row tail) give 2 * 32 * 2 = 128 block pairs,
+    # so two head splits of three heads fill 256 workgroups; ragged headdim and
+    # d_state; carried state.  With bf16 activations and f32 dy the backward
+    # takes the same general kernels.
+    act = "f32" if dy_dtype == "f32" else "bf16"
+    cfg = SSDConfig("paired", 2, 6400, 6, 40, 72, 1, 200, act, init_state=True, seed=51)
+    d = make_inputs(cfg)
+    if act == "f32":
+        got, ref = gpu_ssd(cfg, d), oracle_ssd(d, cfg.chunk)
+    else:
+        dy = np.random.default_rng(52).standard_normal(d["x"].shape).astype(np.float32)
+        got, ref = gpu_ssd(cfg, d, dy=dev(dy)), oracle_ssd(d, cfg.chunk, dy_values=dy)
+    compare(got, ref, TOL[act], label=f"paired general {dy_dtype}")
+
+
 def test_many_chunks_bf16():
     # 256 chunks per head with 16-step chunks and a 32-wide d_state: the final
     # workgroup of the fused backward kernel sums 512 chunk partials per head
