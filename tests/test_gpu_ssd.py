@@ -61,11 +61,14 @@ def test_chunk_lengths(chunk):
     compare(gpu_ssd(cfg, d), oracle_ssd(d, chunk), TOL["f32"], label=f"chunk={chunk}")
 
 
-@pytest.mark.parametrize("chunk", [32, 64, 128])
+@pytest.mark.parametrize("chunk", [32, 64, 128, 192, 200])
 def test_chunk_lengths_bf16(chunk):
-    # the bf16 kernels at chunk lengths below the workloads' 256 (one, two and
-    # four 64-row blocks per chunk; a half block at 32)
-    cfg = SSDConfig("chunks_bf16", 2, 512, 8, 64, 128, 2, chunk, "bf16", init_state=True, seed=15)
+    # the bf16 kernels at chunk lengths other than the workloads' 256: a half
+    # block at 32, one, two and three 64-row blocks per chunk, and four with an
+    # 8-row tail at 200 (the fused backward's W area with one, three and six
+    # block pairs)
+    seqlen = {192: 576, 200: 600}.get(chunk, 512)
+    cfg = SSDConfig("chunks_bf16", 2, seqlen, 8, 64, 128, 2, chunk, "bf16", init_state=True, seed=15)
     d = make_inputs(cfg)
     compare(gpu_ssd(cfg, d), oracle_ssd(d, chunk), TOL["bf16"], label=f"bf16 chunk={chunk}")
 
