@@ -238,13 +238,17 @@ __global__ __launch_bounds__(NT8) void chunk_bwd_col_kernel(
               ws[t] = wsr[ib][t];
             }
           }
-          const int ir0 = il + 16 * rw + 4 * q;  // the lane's four rows inside the slab
+          // the lane index taken here: masks and offsets built from it once
+          // for the whole head loop would be spilled (one lane mask per
+          // (block, tile, element))
+          const int lo = opaque_index(lane_id()), ro = lo & 15, qo = lo >> 4;
+          const int ir0 = il + 16 * rw + 4 * qo;  // the lane's four rows inside the slab
           float si[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) si[e] = sS[min(s0 + ir0 + e, Q - 1)];
 #pragma unroll
           for (int t = 0; t < 2; ++t) {
-            const int jl = 32 * cw + 16 * t + r, jq = j0 + jl;
+            const int jl = 32 * cw + 16 * t + ro, jq = j0 + jl;
             float g4[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -610,10 +614,14 @@ __global__ __launch_bounds__(NT8) void chunk_bwd_row_kernel(
               ws[t] = wsr[jb][t];
             }
           }
+          // the lane index taken here: masks and offsets built from it once
+          // for the whole head loop would be spilled (one lane mask per
+          // (block, tile, element))
+          const int lo = opaque_index(lane_id()), ro = lo & 15, qo = lo >> 4;
           float sjv[4], dtjv[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const int jq = min(jb * BQ + 16 * rw + 4 * q + e, Q - 1);
+            const int jq = min(jb * BQ + 16 * rw + 4 * qo + e, Q - 1);
             sjv[e] = sS[jq];
             dtjv[e] = sDt[jq];
           }
@@ -621,7 +629,7 @@ __global__ __launch_bounds__(NT8) void chunk_bwd_row_kernel(
           for (int t = 0; t < 2; ++t)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              const int iq = i0 + 32 * cw + 16 * t + r, jq = jb * BQ + 16 * rw + 4 * q + e;
+              const int iq = i0 + 32 * cw + 16 * t + ro, jq = jb * BQ + 16 * rw + 4 * qo + e;
               const bool valid = iq < Q && jq <= iq;
               const float ly = valid ? __expf(si[t] - sjv[e]) * yx[t][e] * dtjv[e] : 0.f;
               ws[t][e] += ly;

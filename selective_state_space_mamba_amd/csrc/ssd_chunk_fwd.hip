@@ -174,11 +174,14 @@ __global__ __launch_bounds__(NT8) void chunk_out_fwd_kernel(
       for (int jb = 0; jb < NBMAX; ++jb) {
         const int jl = jb * BQ - j0;
         if (jb <= ib && jl >= 0 && jl < JW) {
+          // the lane index taken here: masks and offsets built from it once
+          // for the whole head loop would be spilled
+          const int lo = opaque_index(lane_id()), ro = lo & 15, qo = lo >> 4;
 #pragma unroll
           for (int t = 0; t < 2; ++t) {
             // lane holds B.C^T rows j = jb*64 + 16rw + 4q + e (e = 0..3), column i = i0 + 32cw + 16t + r
-            const int il = 32 * cw + 16 * t + r, iq = i0 + il;
-            const int jw = 16 * rw + 4 * q;  // first of the lane's four j inside block jb
+            const int il = 32 * cw + 16 * t + ro, iq = i0 + il;
+            const int jw = 16 * rw + 4 * qo;  // first of the lane's four j inside block jb
             const float si = sS[min(iq, Q - 1)];
             float v4[4];
 #pragma unroll
