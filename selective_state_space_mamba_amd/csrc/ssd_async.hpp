@@ -46,14 +46,6 @@ __device__ __forceinline__ i32x4 make_rsrc(const void* base) {
   return i32x4{static_cast<int>(a), static_cast<int>((a >> 32) & 0xFFFFu), 0x7FFFFFF0, 0x00020000};
 }
 
-// A per-lane index the compiler must take as computed here: comparisons
-// derived from it stay in the branch that uses them instead of being hoisted
-// out of the loops as lane masks (which then spill to VGPR lanes).
-__device__ __forceinline__ int opaque_index(int v) {
-  asm volatile("" : "+v"(v));
-  return v;
-}
-
 // One wave's 16-byte-per-lane copy into LDS at dst + 16 * lane (dst uniform).
 __device__ __forceinline__ void dma16(const i32x4& rs, lds_char* dst, uint32_t voff) {
 #if defined(__HIP_DEVICE_COMPILE__)  // gfx950 assembly: device pass only

@@ -72,6 +72,14 @@ __device__ __forceinline__ f4 mfma(bf16x8 a, bf16x8 b, f4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// A per-lane index the compiler must take as computed here: comparisons
+// derived from it stay in the branch that uses them instead of being hoisted
+// out of the loops as lane masks (which then spill to VGPR lanes).
+__device__ __forceinline__ int opaque_index(int v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (WAVE - 1); }
 // Uniform across the wave; readfirstlane lets the compiler keep it, and the
 // LDS and tile addresses derived from it, in scalar registers.
