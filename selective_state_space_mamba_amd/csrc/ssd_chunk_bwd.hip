@@ -303,14 +303,18 @@ __global__ __launch_bounds__(NT8) void chunk_bwd_col_kernel(
     }
     if (hh + 1 < hps) load_head(hh + 1);
     __syncthreads();
+    // the lane index taken per head (see the step loop): the row and column
+    // masks of the skip loads, the state terms and the dx stores are built
+    // here, not hoisted out of the head loop
+    const int lh = opaque_index(lane_id()), rh = lh & 15, qh = lh >> 4;
     // skip term D dy_j (loaded here, while the MFMAs below run) for this wave's output rows j, columns p
     float dsk[4][2];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int jq = j0 + 16 * rw + 4 * q + e;
+      const int jq = j0 + 16 * rw + 4 * qh + e;
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        const int p = 32 * cw + 16 * t + r;
+        const int p = 32 * cw + 16 * t + rh;
         dsk[e][t] = (jq < Q && p < P) ? load_f(dy, (row0 + jq) * HP + static_cast<int64_t>(h) * P + p) : 0.f;
       }
     }
@@ -333,21 +337,21 @@ __global__ __launch_bounds__(NT8) void chunk_bwd_col_kernel(
     const float s_end = sS[Q - 1];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int jl = 16 * rw + 4 * q + e, jq = j0 + jl;
+      const int jl = 16 * rw + 4 * qh + e, jq = j0 + jl;
       const bool valid = jq < Q;
       const float wj = valid ? __expf(s_end - sS[jq]) : 0.f;
       const float dtj = valid ? sDt[jq] : 0.f;
       // R'_j / w_j = x_j . (B_j Gamma^T): partial over this wave's columns p
       float part = 0.f;
 #pragma unroll
-      for (int t = 0; t < 2; ++t) part += bg[t][e] * Op<BF>::back(sX[jl * LDP + 32 * cw + 16 * t + r]);
+      for (int t = 0; t < 2; ++t) part += bg[t][e] * Op<BF>::back(sX[jl * LDP + 32 * cw + 16 * t + rh]);
       part = sum16(part);
-      if (r == 0) sRp[cw][jl] = part;
+      if (rh == 0) sRp[cw][jl] = part;
 #pragma unroll
       for (int t = 0; t < 4; ++t) dbs[t][e] += dtj * wj * v[t][e];
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        const int p = 32 * cw + 16 * t + r;
+        const int p = 32 * cw + 16 * t + rh;
         if (valid && p < P) {
           const int64_t o = (row0 + jq) * HP + static_cast<int64_t>(h) * P + p;
           dx[o] = dtj * (dxa[t][e] + wj * bg[t][e]) + Dh * dsk[e][t];
