@@ -257,8 +257,8 @@ __global__ __launch_bounds__(NTHREADS, 2) void chunk_sum_f32_kernel(
 // Backward: slot c holds dS_c on entry and Gamma_{c+1} on exit, run =
 // Gamma_nc = init (the final state's gradient, or 0), run <- exp(s_end_c) run +
 // dS_c, last = Gamma_0, and gh_part[b,c,h,pb] = <Gamma_{c+1}, H_c> over the
-// block.  The values of the next two chunks are in flight while a chunk's slot
-// is written.
+// block.  The values of the next two chunks (and, backward, their H_c) are in
+// flight while a chunk's slot is written.
 constexpr int SCAN_THREADS = 1024;
 constexpr int SCAN_EPT = STATE_PB * NMAX / SCAN_THREADS;  // elements per thread
 constexpr int SCAN_AHEAD = 2;                             // chunks loaded ahead
@@ -280,6 +280,7 @@ __global__ __launch_bounds__(SCAN_THREADS) void state_scan_kernel(float* __restr
   const int64_t off0 = static_cast<int64_t>(p0) * N;
   const int tid = threadIdx.x;
   float run[SCAN_EPT], buf[SCAN_AHEAD][SCAN_EPT];
+  float hbuf[SCAN_AHEAD][SCAN_EPT];  // backward: H_c of the chunks in flight
 #pragma unroll
   for (int k = 0; k < SCAN_EPT; ++k) {
     const int e = tid + SCAN_THREADS * k;
@@ -287,34 +288,40 @@ __global__ __launch_bounds__(SCAN_THREADS) void state_scan_kernel(float* __restr
   }
   auto chunk = [&](int it) { return REV ? nc - 1 - it : it; };
   auto slot = [&](int it) { return ((static_cast<int64_t>(bi) * nc + chunk(it)) * H + h) * PN + off0; };
-  auto load = [&](int it, float (&v)[SCAN_EPT]) {
+  auto load = [&](int it, float (&v)[SCAN_EPT], float (&hv)[SCAN_EPT]) {
 #pragma unroll
     for (int k = 0; k < SCAN_EPT; ++k) {
       const int e = tid + SCAN_THREADS * k;
-      v[k] = (it < nc && e < nvalid) ? states[slot(it) + e] : 0.f;
+      const bool ok = it < nc && e < nvalid;
+      v[k] = ok ? states[slot(it) + e] : 0.f;
+      if (REV) hv[k] = ok ? hstates[slot(it) + e] : 0.f;
     }
   };
 #pragma unroll
-  for (int a = 0; a < SCAN_AHEAD; ++a) load(a, buf[a]);
+  for (int a = 0; a < SCAN_AHEAD; ++a) load(a, buf[a], hbuf[a]);
   for (int it = 0; it < nc; ++it) {
     const int c = chunk(it);
     const int64_t base = slot(it);
     const float decay = __expf(send[(static_cast<int64_t>(bi) * nc + c) * H + h]);
-    float cur[SCAN_EPT];
+    float cur[SCAN_EPT], hcur[SCAN_EPT];
 #pragma unroll
     for (int k = 0; k < SCAN_EPT; ++k) {
       cur[k] = buf[0][k];
+      hcur[k] = hbuf[0][k];
 #pragma unroll
-      for (int a = 0; a + 1 < SCAN_AHEAD; ++a) buf[a][k] = buf[a + 1][k];
+      for (int a = 0; a + 1 < SCAN_AHEAD; ++a) {
+        buf[a][k] = buf[a + 1][k];
+        hbuf[a][k] = hbuf[a + 1][k];
+      }
     }
-    load(it + SCAN_AHEAD, buf[SCAN_AHEAD - 1]);
+    load(it + SCAN_AHEAD, buf[SCAN_AHEAD - 1], hbuf[SCAN_AHEAD - 1]);
     float gh = 0.f;
 #pragma unroll
     for (int k = 0; k < SCAN_EPT; ++k) {
       const int e = tid + SCAN_THREADS * k;
       if (e < nvalid) {
         states[base + e] = run[k];
-        if (REV) gh += run[k] * hstates[base + e];
+        if (REV) gh += run[k] * hcur[k];
       }
       run[k] = decay * run[k] + cur[k];
     }
