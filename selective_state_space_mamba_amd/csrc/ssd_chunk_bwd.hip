@@ -659,11 +659,20 @@ __global__ __launch_bounds__(NT8) void chunk_bwd_row_kernel(
     float dd = 0.f;
     {
       const int p = tid % PMAX;
-      if (p < P)
-        for (int il = tid / PMAX; il < vi; il += NT8 / PMAX) {
-          const int64_t o = (row0 + i0 + il) * HP + static_cast<int64_t>(h) * P + p;
-          dd += load_f(dy, o) * load_f(x, o);
-        }
+      if constexpr (!BF) {
+        // f32 operands: this block's dy rows (sDy) and x rows (the last x
+        // slab, JW = BQ rows from i0) are both still in LDS
+        static_assert(BF || JW == BQ, "one block per f32 slab");
+        if (p < P)
+          for (int il = tid / PMAX; il < vi; il += NT8 / PMAX) dd += sDy[il * LDP + p] * sXr[il * LDP + p];
+      } else {
+        // (the staged dy is rounded to bf16 here: the products take dy as given)
+        if (p < P)
+          for (int il = tid / PMAX; il < vi; il += NT8 / PMAX) {
+            const int64_t o = (row0 + i0 + il) * HP + static_cast<int64_t>(h) * P + p;
+            dd += load_f(dy, o) * load_f(x, o);
+          }
+      }
     }
     dd = wave_sum(dd);
     if (l == 0) sTmp[8 + w] = dd;
