@@ -85,7 +85,8 @@ __global__ __launch_bounds__(FT) void bwd_fused_bf16_kernel(
   __shared__ __attribute__((aligned(1024))) char sGam_[TILE_N];        // Gamma [p][n]; W strip slot
   __shared__ __attribute__((aligned(1024))) char sH_[TILE_N];          // H_c [p][n] (bf16)
   __shared__ __attribute__((aligned(1024))) char sG_[FW * STRIP];      // per-wave strips [i][j]; W strip slot
-  __shared__ __attribute__((aligned(1024))) char sCt_[NBMAX * TILE_N];  // C tiles of blocks ib, tile ib at ib * 16 KB
+  // C tile of block ib at ib * 16 KB; after pass ib, B rows of block ib there
+  __shared__ __attribute__((aligned(1024))) char sCt_[NBMAX * TILE_N];
   __shared__ float sRed[2][BQ][4];  // column sums, diagonal, R', readout: team halves
   __shared__ float sRm[4][BQ];      // one step's row sums of M per wave of a team; dD wave sums
   __shared__ float sDiag[BQ];       // the diagonal of E on the pass's diagonal block
