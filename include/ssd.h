@@ -233,9 +233,13 @@ int ssd_dt_softplus_bwd(int64_t rows, int64_t nheads, int32_t dtype, const void*
  * and B, f32 accumulation, and C in c_dtype (SSD_F32 or SSD_BF16).  op(A) is
  * [m,k]: A stored [m,k], or [k,m] when trans_a != 0; op(B) is [k,n]: B stored
  * [k,n], or [n,k] when trans_b != 0.  lda, ldb, ldc are row strides in
- * elements.  Runs rocBLAS gemm_ex on the caller's stream; unlike the other
- * entry points, the rocBLAS handle (one per device, created on first use)
- * holds device memory of its own. */
+ * elements.  Runs on the caller's stream through hipBLASLt (the fastest of
+ * its heuristic's candidates for the shape, timed on the shape's first call,
+ * which synchronises the stream and allocates a scratch output for the
+ * trials), or rocBLAS gemm_ex where hipBLASLt offers no algorithm or
+ * SSD_GEMM=rocblas is set.  Unlike the other entry points, the library
+ * handles and the 32 MiB hipBLASLt workspace (one each per device, created on
+ * first use) hold device memory of their own. */
 int ssd_gemm(int32_t trans_a, int32_t trans_b, int64_t m, int64_t n, int64_t k, float alpha,
              const void* A, int64_t lda, const void* B, int64_t ldb, float beta, void* C,
              int32_t c_dtype, int64_t ldc, void* stream);

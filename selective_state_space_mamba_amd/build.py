@@ -56,7 +56,7 @@ def build(verbose: bool = False) -> str:
     tmp = out + ".tmp%d" % os.getpid()
     rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
     cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-L" + os.path.join(rocm, "lib"),
-           "-lrocblas", "-Wl,-rpath," + os.path.join(rocm, "lib"), "-o", tmp]
+           "-lrocblas", "-lhipblaslt", "-Wl,-rpath," + os.path.join(rocm, "lib"), "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
