@@ -715,7 +715,8 @@ def main():
         t_g = kms["gemm"] * n_gemm * 1e-3
         line["projections"] = {"ms_per_step": round(t_g * 1e3, 4), "calls": n_gemm,
                                "tflops": round(train_step_flops(cfg) / t_g / 1e12, 1),
-                               "peak_tflops": MFMA_PEAK_TFLOPS["bf16"], "library": "rocBLAS gemm_ex"}
+                               "peak_tflops": MFMA_PEAK_TFLOPS["bf16"],
+                               "library": "rocBLAS gemm_ex" if os.environ.get("SSD_GEMM") == "rocblas" else "hipBLASLt"}
     print(json.dumps(line), flush=True)
 
 
