@@ -6,7 +6,7 @@
 // hipBLASLt by default: per device one handle and one workspace, created on
 // first use, and per problem shape the descriptors and an algorithm, kept for
 // the later calls of that shape.  The algorithm is the fastest of the (up to
-// eight) candidates the library's heuristic offers, timed on the shape's first
+// 32) candidates the library's heuristic offers, timed on the shape's first
 // call into a scratch output (so that an accumulating call, beta != 0, does
 // not see the trial runs); that first call synchronises its stream.  rocBLAS
 // (gemm_ex) takes the shapes for which hipBLASLt offers no algorithm, and all
@@ -76,7 +76,7 @@ GemmStatus rocblas_gemm(int dev, bool trans_a, bool trans_b, int64_t m, int64_t 
   return st == rocblas_status_success ? GemmStatus::kOk : GemmStatus::kBlas;
 }
 
-constexpr int kLtCandidates = 8;
+constexpr int kLtCandidates = 32;
 
 // Mean time in ms of `reps` runs of one algorithm (negative if it fails).
 float lt_time(LtDevice& d, const LtPlan& p, const hipblasLtMatmulAlgo_t& algo, size_t ws, const void* A,
