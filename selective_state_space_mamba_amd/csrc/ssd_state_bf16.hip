@@ -15,9 +15,9 @@
 // in registers and walks the chunks in order (or in reverse).  The MFMAs
 // produce the state transposed (d_state along the accumulator rows), so a
 // lane holds four consecutive d_state columns of one headdim row; at a chunk
-// end the wave passes its part through a private LDS area and stores it in
-// whole 128-byte rows, 16 bytes a lane (the state stores were the kernel's
-// largest cost as 4-byte and 2-byte stores).  Per chunk the
+// end the wave passes its part through LDS (the buffer of the chunk's last
+// slab) and stores it in whole 128-byte rows, 16 bytes a lane (the state
+// stores were the kernel's largest cost as 4-byte and 2-byte stores).  Per chunk the
 // weighted sum is one MFMA contraction over time: the x (or dy) tile arrives
 // with time along its rows, is scaled in place by the per-step weights (one
 // 16-byte chunk per thread, once for the four waves that read each row) and
@@ -54,8 +54,10 @@ __device__ __forceinline__ float wave_total(float v) {
 // SSJ: time steps per slab (128; 64 for grids of several rounds, whose LDS
 // then lets two workgroups share a CU).  HAS_H: the reverse pass reads H_c
 // (for the <Gamma_{c+1}, H_c> partials or its bf16 copy).
+// Kernels with 64-step slabs are held to 80 VGPRs, the budget of three
+// workgroups (six waves a SIMD) on one CU.
 template <bool REV, int SSJ, bool HAS_H>
-__global__ __launch_bounds__(ST) void chunk_state_bf16_kernel(
+__global__ __launch_bounds__(ST) __attribute__((amdgpu_waves_per_eu(SSJ == 64 ? 6 : 1))) void chunk_state_bf16_kernel(
     const uint16_t* __restrict__ X,     // fwd: x; bwd: dy       [b,T,H,P]
     const uint16_t* __restrict__ Bm,    // fwd: B; bwd: C        [b,T,G,N]
     const uint16_t* __restrict__ dt,    // [b,T,H]
@@ -71,19 +73,20 @@ __global__ __launch_bounds__(ST) void chunk_state_bf16_kernel(
     int T, int H, int P, int N, int G, int Q) {
   constexpr int XSLAB = SSJ * 64;   // bytes of an SSJ x 32 bf16 slab
   constexpr int BSLAB = SSJ * 256;  // bytes of an SSJ x 128 bf16 slab
+  constexpr int SLAB = BSLAB + XSLAB;  // one buffer: the B (C) slab, then the x (dy) slab
   static_assert(!HAS_H || REV, "H_c is read by the reverse pass only");
-  __shared__ __attribute__((aligned(1024))) char sX_[2 * XSLAB];
-  __shared__ __attribute__((aligned(1024))) char sB_[2 * BSLAB];
+  __shared__ __attribute__((aligned(1024))) char sS_[2 * SLAB];
   __shared__ __attribute__((aligned(1024))) char sH_[HAS_H ? 2 * HTILE : 16];  // bwd: H_c (f32), two chunks
   __shared__ __attribute__((aligned(16))) float sWt[SW][QMAX];                // per-wave step weights
   __shared__ __attribute__((aligned(16))) uint32_t sDtb[2][QMAX];             // dt bits of a chunk, two chunks
   __shared__ float sGh[2][SW];
-  // each wave's 16 x 32 part of the state, row-major with rows padded to 36
-  // floats (the 16 rows of a 16-byte write fall in distinct banks), to store
-  // it in whole 128-byte rows
-  __shared__ __attribute__((aligned(16))) float sStage[SW][16 * SROW];
-  lds_char* const sX = lds_ptr(sX_);
-  lds_char* const sB = lds_ptr(sB_);
+  // At a chunk end each wave stages its 16 x 32 part of the state, row-major
+  // with rows padded to 36 floats (the 16 rows of a 16-byte write fall in
+  // distinct banks), in the slab buffer the chunk's last slab used, to store
+  // it in whole 128-byte rows.  Without an area of its own the kernel takes
+  // 51 KB of LDS, so three workgroups share a CU.
+  static_assert(SW * 16 * SROW * 4 <= SLAB, "the staging areas fit in one slab buffer");
+  lds_char* const sS = lds_ptr(sS_);
   lds_char* const sH = lds_ptr(sH_);
 
   if (REV && counter && blockIdx.x == 0 && threadIdx.x == 0)
@@ -136,8 +139,8 @@ __global__ __launch_bounds__(ST) void chunk_state_bf16_kernel(
     const uint32_t t0 = static_cast<uint32_t>(sl * SSJ);  // the slab's first step in the chunk
     const int vr = min(SSJ, Q - sl * SSJ);
     const int buf = (it * nsl + sl) & 1;
-    lx.issue(sX + buf * XSLAB, rsX, t0 * HPb + static_cast<uint32_t>(h * P + p0) * 2, vr);
-    lbs.issue(sB + buf * BSLAB, rsB, t0 * GNb + static_cast<uint32_t>(g * N) * 2, vr);
+    lx.issue(sS + buf * SLAB + BSLAB, rsX, t0 * HPb + static_cast<uint32_t>(h * P + p0) * 2, vr);
+    lbs.issue(sS + buf * SLAB, rsB, t0 * GNb + static_cast<uint32_t>(g * N) * 2, vr);
     if (sl == 0) {
       steps_async<SW>(lds_ptr(sDtb[it & 1]), make_rsrc(dt + (static_cast<int64_t>(bi) * T + static_cast<int64_t>(c) * Q) * H + h),
                       H * 2, Q);
@@ -186,7 +189,7 @@ __global__ __launch_bounds__(ST) void chunk_state_bf16_kernel(
       // do not each scale it
       static_assert(XSLAB <= ST * 16, "at most one chunk of the x slab per thread");
       if (XSLAB == ST * 16 || static_cast<int>(threadIdx.x) < XSLAB / 16) {
-        uint4* const cp = reinterpret_cast<uint4*>(sX_ + buf * XSLAB) + threadIdx.x;
+        uint4* const cp = reinterpret_cast<uint4*>(sS_ + buf * SLAB + BSLAB) + threadIdx.x;
         const float wt = wts[sl * SSJ + (threadIdx.x >> 2)];
         const uint4 v = *cp;
         const uint32_t vv[4] = {v.x, v.y, v.z, v.w};
@@ -202,8 +205,8 @@ __global__ __launch_bounds__(ST) void chunk_state_bf16_kernel(
       else if (it + 1 < nc)
         load_slab(it + 1, 0);
       lds_barrier();  // the scaled slab is visible
-      const lds_char* xs = sX + buf * XSLAB;
-      const lds_char* bs = sB + buf * BSLAB;
+      const lds_char* xs = sS + buf * SLAB + BSLAB;
+      const lds_char* bs = sS + buf * SLAB;
       const int kw = min(SSJ, Q - sl * SSJ);
       if (kw == SSJ) {
         // a full slab: every fragment read first, then the MFMAs, so that the
@@ -244,8 +247,11 @@ __global__ __launch_bounds__(ST) void chunk_state_bf16_kernel(
     const __amdgpu_buffer_rsrc_t rsb = make_rsrc_opt(states_bf ? states_bf + sbase : nullptr);
     const __amdgpu_buffer_rsrc_t rhb = make_rsrc_opt(hbf_out ? hbf_out + sbase : nullptr);
     // the wave's part (rows 16 pw + i, columns 32 nw + j) to its staging
-    // area; the same wave reads it back (LDS accesses of a wave are in order)
-    float* const stg = sStage[w];
+    // area, once every wave is done with the last slab's buffer (the next
+    // copy into it is issued after the next barrier); the same wave reads it
+    // back (LDS accesses of a wave are in order)
+    lds_barrier();
+    float* const stg = reinterpret_cast<float*>(sS_ + ((it * nsl + nsl - 1) & 1) * SLAB) + w * 16 * SROW;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
       *reinterpret_cast<float4*>(stg + r * SROW + 16 * t + 4 * q) = make_float4(st[t][0], st[t][1], st[t][2], st[t][3]);
@@ -331,11 +337,10 @@ int device_cus() {
 }
 }  // namespace
 
-// Grids of more workgroups than CUs take 64-step slabs: 69 KB of LDS, so two
-// workgroups share a CU and the grid runs in half the rounds (block slice:
-// 768 workgroups, 107 -> 103 us forward and 149 -> 127 us backward when this
-// was first measured); a grid of one round keeps 128-step slabs, with half
-// the barriers per chunk (grouped workload: 36 us against 43 with 64 steps).
+// Grids of more workgroups than CUs take 64-step slabs: 51 KB of LDS, so
+// three workgroups share a CU (block slice: 768 workgroups in one round); a
+// grid of one round keeps 128-step slabs, with half the barriers per chunk
+// (grouped workload: 36 us against 43 with 64 steps).
 // The reverse pass that reads H_c (two 16 KB f32 tiles more) keeps 128.
 hipError_t launch_chunk_state_fwd_bf16(const Dims& d, const void* x, const void* B, const void* dt,
                                        const float* A_log, const float* init, float* states, float* final_state,
