@@ -283,6 +283,29 @@ __global__ __launch_bounds__(256) void conv_fwd_vec_kernel(const TI* __restrict_
   }
 }
 
+// One step of four channels of the conv input as loaded: bf16 pairs (two
+// words) or f32 (four), unpacked where used, so that the backward's window of
+// 2K - 1 steps takes half the registers with bf16 activations.
+template <typename TI>
+struct XStep {
+  float f[4];
+  __device__ __forceinline__ void load(const float* p) { ldv<4>(p, f); }
+  __device__ __forceinline__ void zero() { zerov<4>(f); }
+  __device__ __forceinline__ float get(int v) const { return f[v]; }
+};
+template <>
+struct XStep<uint16_t> {
+  uint32_t u[2];
+  __device__ __forceinline__ void load(const uint16_t* p) {
+    const uint2 t = *reinterpret_cast<const uint2*>(p);
+    u[0] = t.x, u[1] = t.y;
+  }
+  __device__ __forceinline__ void zero() { u[0] = u[1] = 0u; }
+  __device__ __forceinline__ float get(int v) const {
+    return (v & 1) ? __uint_as_float(u[v >> 1] & 0xFFFF0000u) : __uint_as_float(u[v >> 1] << 16);
+  }
+};
+
 // Vector conv backward.  grid (ceil(conv_dim / (4 * 64)), ceil(T / CONV_RUN), b):
 // lane l owns channels c0 .. c0+3, wave q the steps [CONV_RUN*y + CONV_WRUN*q, +CONV_WRUN).
 // Lane state over steps u of its run:
@@ -296,7 +319,9 @@ __global__ __launch_bounds__(256, K <= 4 ? 4 : 2) void conv_bwd_vec_kernel(const
                                                           const float* __restrict__ dB, const float* __restrict__ dC,
                                                           float* __restrict__ dxbc, float* __restrict__ part, int T,
                                                           int Cd, int d_inner, int gn) {
-  constexpr int V = 4, U = 2;       // two steps of loads in flight keep 4 waves per SIMD at K = 4
+  // steps of loads in flight: four with bf16 activations (their packed window
+  // leaves room at 4 waves per SIMD for K = 4), two with f32
+  constexpr int V = 4, U = sizeof(TI) == 2 ? 3 : 2;
   constexpr int NP = V * (K + 1);  // partial values per lane
   __shared__ float red[WAVE * NP];
   const int lane = lane_id(), wv = wave_id();
@@ -316,11 +341,11 @@ __global__ __launch_bounds__(256, K <= 4 ? 4 : 2) void conv_bwd_vec_kernel(const
     else
       zerov<V>(bc);
     const SplitAt<const float> gi = split_at(dx, dB, dC, c0, d_inner, gn);
-    auto xload = [&](int t, float (&f)[V]) {
+    auto xload = [&](int t, XStep<TI>& f) {
       if (t >= 0 && t < T)
-        ldv<V>(xbc + (rb + t) * Cd + c0, f);
+        f.load(xbc + (rb + t) * Cd + c0);
       else
-        zerov<V>(f);
+        f.zero();
     };
     auto gload = [&](int t, float (&f)[V]) {
       if (t < T)
@@ -329,17 +354,18 @@ __global__ __launch_bounds__(256, K <= 4 ? 4 : 2) void conv_bwd_vec_kernel(const
         zerov<V>(f);
     };
     // gp = g s (1 + p (1 - s)) for the K inputs win[0..K-1] ending at its step
-    auto gp_of = [&](const float (&g)[V], float (*win)[V], float (&out)[V]) {
+    auto gp_of = [&](const float (&g)[V], const XStep<TI>* win, float (&out)[V]) {
 #pragma unroll
       for (int v = 0; v < V; ++v) {
         float p = bc[v];
 #pragma unroll
-        for (int k = 0; k < K; ++k) p += wk[k][v] * win[k][v];
+        for (int k = 0; k < K; ++k) p += wk[k][v] * win[k].get(v);
         const float s = sigmoidf_(p);
         out[v] = g[v] * s * (1.f + p * (1.f - s));
       }
     };
-    float xw[2 * K - 1][V], gw[K][V];
+    XStep<TI> xw[2 * K - 1];
+    float gw[K][V];
 #pragma unroll
     for (int m = 0; m < 2 * K - 1; ++m) xload(t0 - (K - 1) + m, xw[m]);
 #pragma unroll
@@ -349,7 +375,8 @@ __global__ __launch_bounds__(256, K <= 4 ? 4 : 2) void conv_bwd_vec_kernel(const
       gp_of(g, xw + m, gw[m]);
     }
     for (int u0 = t0; u0 < t1; u0 += U) {
-      float ng[U][V], nx[U][V];
+      float ng[U][V];
+      XStep<TI> nx[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         gload(u0 + u + K - 1, ng[u]);
@@ -372,18 +399,15 @@ __global__ __launch_bounds__(256, K <= 4 ? 4 : 2) void conv_bwd_vec_kernel(const
         for (int v = 0; v < V; ++v) {
           acc[K][v] += gw[0][v];
 #pragma unroll
-          for (int k = 0; k < K; ++k) acc[k][v] += gw[0][v] * xw[k][v];
+          for (int k = 0; k < K; ++k) acc[k][v] += gw[0][v] * xw[k].get(v);
         }
 #pragma unroll
         for (int m = 0; m < K - 1; ++m)
 #pragma unroll
           for (int v = 0; v < V; ++v) gw[m][v] = gw[m + 1][v];
 #pragma unroll
-        for (int m = 0; m < 2 * K - 2; ++m)
-#pragma unroll
-          for (int v = 0; v < V; ++v) xw[m][v] = xw[m + 1][v];
-#pragma unroll
-        for (int v = 0; v < V; ++v) xw[2 * K - 2][v] = nx[u][v];
+        for (int m = 0; m < 2 * K - 2; ++m) xw[m] = xw[m + 1];
+        xw[2 * K - 2] = nx[u];
       }
     }
   }
