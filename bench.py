@@ -469,7 +469,7 @@ def make_train_step(cfg, d):
     gact = torch.empty((M, di), **bf)  # the out_proj input gradient, in the activation dtype
     dWo, dWz, dWx, dWd = (torch.empty(s_, **f32) for s_ in ((dm, di), (di, dm), (cd, dm), (H, dm)))
     du = torch.empty((M, dm), **f32)
-    gz_bf, gx_bf, gd_bf = torch.empty((M, di), **bf), torch.empty((M, cd), **bf), torch.empty((M, H), **bf)
+    gd_bf = torch.empty((M, H), **bf)
     prob = ssd._binding.make_problem(fo["y"], to_dev(d["B"]), Q, torch.bfloat16)
     wsf = torch.empty(max(1, ssd.ssd_workspace_bytes(prob, False, f32h)), **u8)
     wsb = torch.empty(max(1, ssd.ssd_workspace_bytes(prob, True, f32h)), **u8)
@@ -494,15 +494,16 @@ def make_train_step(cfg, d):
         ssd.gemm(go2, Wo, out=gact)
         ssd.gemm(go2, out.view(M, di), trans_a=True, out=dWo)
         gy, gz, gw = ssd.rmsnorm_gated_bwd(y.view(b, T, di), z.view(b, T, di), norm_w, inv, gact.view(b, T, di),
-                                           workspace=wsr, dy_dtype=torch.bfloat16)
+                                           workspace=wsr, dy_dtype=torch.bfloat16, dz_dtype=torch.bfloat16)
         g = ssd.ssd_bwd(xs, dt3, A_log, Bs, Cs, D, gy.view(b, T, H, P), None, chunk_states=r["chunk_states"],
                         chunk_states_bf16=r["chunk_states_bf16"], chunk=Q, out=go_,
                         workspace=wsb, want_d_init_state=False)
         dxbc, _, _ = ssd.conv1d_silu_bwd(xbc.view(b, T, cd), conv_w, conv_b, g["dx"].view(b, T, di), g["dB"],
-                                         g["dC"], di, G, N, workspace=wsc)
+                                         g["dC"], di, G, N, workspace=wsc, dxbc_dtype=torch.bfloat16)
         ddt_raw, _ = ssd.dt_softplus_bwd(raw, dt_bias, g["ddt"].view(M, H), workspace=wsd)
-        ssd.cast_bf16(gz.view(M, di), out=gz_bf)
-        ssd.cast_bf16(dxbc.view(M, cd), out=gx_bf)
+        # dz and dxbc come out of their kernels in bf16 (the values a cast of
+        # the f32 gradients gives); ddt_raw is cast
+        gz_bf, gx_bf = gz.view(M, di), dxbc.view(M, cd)
         ssd.cast_bf16(ddt_raw, out=gd_bf)
         ssd.gemm(gz_bf, Wz, out=du)
         ssd.gemm(gx_bf, Wx, out=du, beta=1.0)

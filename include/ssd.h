@@ -179,13 +179,15 @@ size_t mamba2_conv1d_silu_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int
                                               int64_t ngroups, int64_t dstate, int64_t d_conv);
 
 /* Backward of mamba2_conv1d_silu_fwd.  dx [b,T,d_inner], dB, dC [b,T,G,N] are
- * the f32 gradients of its three outputs.  Outputs f32: dxbc [b,T,conv_dim],
- * dw [conv_dim,d_conv], dbias [conv_dim]. */
+ * the f32 gradients of its three outputs.  Outputs: dxbc [b,T,conv_dim] in
+ * `dxbc_dtype` (SSD_F32, or SSD_BF16 rounded to nearest even: the values an
+ * f32 -> bf16 cast of the f32 output gives, e.g. as a GEMM operand); dw
+ * [conv_dim,d_conv] and dbias [conv_dim] f32. */
 int mamba2_conv1d_silu_bwd(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t ngroups,
                            int64_t dstate, int64_t d_conv, int32_t dtype, const void* xbc,
                            const float* w, const float* bias, const float* dx, const float* dB,
-                           const float* dC, float* dxbc, float* dw, float* dbias, void* workspace,
-                           size_t workspace_bytes, void* stream);
+                           const float* dC, int32_t dxbc_dtype, void* dxbc, float* dw, float* dbias,
+                           void* workspace, size_t workspace_bytes, void* stream);
 
 /* RMSNorm-gated forward over rows of `width`: inv_rms = 1/sqrt(mean(y^2)+eps),
  * out = y * inv_rms * w * silu(z).  y, z, out in `dtype`; w [width] f32;
@@ -199,12 +201,12 @@ size_t mamba2_rmsnorm_gated_bwd_workspace_bytes(int64_t rows, int64_t width);
 /* RMSNorm-gated backward with the saved inv_rms.  g [rows,width] is the
  * gradient of `out` in `g_dtype`.  Outputs: dy [rows,width] in `dy_dtype`
  * (SSD_F32, or SSD_BF16 rounded to nearest even, e.g. to feed ssd_bwd's bf16
- * path as its dy); dz [rows,width] and dw [width] f32.  dw is a fixed-order
- * sum of per-64-row partials held in the workspace. */
+ * path as its dy); dz [rows,width] in `dz_dtype` (likewise); dw [width] f32, a
+ * fixed-order sum of per-64-row partials held in the workspace. */
 int mamba2_rmsnorm_gated_bwd(int64_t rows, int64_t width, int32_t dtype, int32_t g_dtype,
-                             int32_t dy_dtype, const void* y, const void* z, const float* w,
-                             const float* inv_rms, const void* g, void* dy, float* dz, float* dw,
-                             void* workspace, size_t workspace_bytes, void* stream);
+                             int32_t dy_dtype, int32_t dz_dtype, const void* y, const void* z,
+                             const float* w, const float* inv_rms, const void* g, void* dy, void* dz,
+                             float* dw, void* workspace, size_t workspace_bytes, void* stream);
 
 /* dt activation in front of the core (burn_dragon_kernel src/sequence/mamba2/backward.rs,
  * tensorized_mamba2_backward_impl:

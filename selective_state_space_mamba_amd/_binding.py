@@ -59,13 +59,13 @@ def load_library():
     lib.mamba2_conv1d_silu_fwd.restype = ctypes.c_int
     lib.mamba2_conv1d_silu_bwd_workspace_bytes.argtypes = [i64] * 6
     lib.mamba2_conv1d_silu_bwd_workspace_bytes.restype = sz
-    lib.mamba2_conv1d_silu_bwd.argtypes = [i64] * 6 + [i32] + [vp] * 9 + [vp, sz, vp]
+    lib.mamba2_conv1d_silu_bwd.argtypes = [i64] * 6 + [i32] + [vp] * 6 + [i32] + [vp] * 3 + [vp, sz, vp]
     lib.mamba2_conv1d_silu_bwd.restype = ctypes.c_int
     lib.mamba2_rmsnorm_gated_fwd.argtypes = [i64, i64, f32, i32] + [vp] * 5 + [vp]
     lib.mamba2_rmsnorm_gated_fwd.restype = ctypes.c_int
     lib.mamba2_rmsnorm_gated_bwd_workspace_bytes.argtypes = [i64, i64]
     lib.mamba2_rmsnorm_gated_bwd_workspace_bytes.restype = sz
-    lib.mamba2_rmsnorm_gated_bwd.argtypes = [i64, i64, i32, i32, i32] + [vp] * 8 + [vp, sz, vp]
+    lib.mamba2_rmsnorm_gated_bwd.argtypes = [i64, i64, i32, i32, i32, i32] + [vp] * 8 + [vp, sz, vp]
     lib.mamba2_rmsnorm_gated_bwd.restype = ctypes.c_int
     lib.ssd_dt_softplus_fwd.argtypes = [i64, i64, i32] + [vp] * 3 + [vp]
     lib.ssd_dt_softplus_fwd.restype = ctypes.c_int
@@ -358,9 +358,10 @@ def conv1d_silu_fwd(xbc, w, bias, d_inner: int, ngroups: int, dstate: int, strea
 
 
 def conv1d_silu_bwd(xbc, w, bias, dx, dB, dC, d_inner: int, ngroups: int, dstate: int, workspace=None,
-                    stream=None):
+                    stream=None, dxbc_dtype=torch.float32):
     """Backward of conv1d_silu_fwd given f32 gradients of its outputs; returns
-    (dxbc [b,T,conv_dim], dw [conv_dim,d_conv], dbias [conv_dim]) in f32."""
+    (dxbc [b,T,conv_dim] in dxbc_dtype (f32, or bf16 rounded to nearest even),
+    dw [conv_dim,d_conv] f32, dbias [conv_dim] f32)."""
     _on_gpu(xbc, "xbc")
     lib = load_library()
     b, T, cd = xbc.shape
@@ -368,8 +369,10 @@ def conv1d_silu_bwd(xbc, w, bias, dx, dB, dC, d_inner: int, ngroups: int, dstate
     _need(dx, "dx", (b, T, d_inner), torch.float32, xbc.device)
     _need(dB, "dB", (b, T, ngroups, dstate), torch.float32, xbc.device)
     _need(dC, "dC", (b, T, ngroups, dstate), torch.float32, xbc.device)
+    if dxbc_dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("dxbc_dtype must be torch.float32 or torch.bfloat16")
     f32 = dict(dtype=torch.float32, device=xbc.device)
-    dxbc = torch.empty((b, T, cd), **f32)
+    dxbc = torch.empty((b, T, cd), dtype=dxbc_dtype, device=xbc.device)
     dw = torch.empty((cd, K), **f32)
     db = torch.empty((cd,), **f32)
     need = lib.mamba2_conv1d_silu_bwd_workspace_bytes(b, T, d_inner, ngroups, dstate, K)
@@ -377,7 +380,8 @@ def conv1d_silu_bwd(xbc, w, bias, dx, dB, dC, d_inner: int, ngroups: int, dstate
         workspace = torch.empty(need, dtype=torch.uint8, device=xbc.device)
     wsz = _need_workspace(workspace, xbc.device)
     _check(lib.mamba2_conv1d_silu_bwd(b, T, d_inner, ngroups, dstate, K, _code(xbc.dtype), _ptr(xbc), _ptr(w),
-                                      _ptr(bias), _ptr(dx), _ptr(dB), _ptr(dC), _ptr(dxbc), _ptr(dw), _ptr(db),
+                                      _ptr(bias), _ptr(dx), _ptr(dB), _ptr(dC), _code(dxbc_dtype), _ptr(dxbc),
+                                      _ptr(dw), _ptr(db),
                                       _ptr(workspace), wsz, _stream(stream)))
     return dxbc, dw, db
 
@@ -400,9 +404,11 @@ def rmsnorm_gated_fwd(y, z, w, eps: float = 1e-5, stream=None):
     return out, inv
 
 
-def rmsnorm_gated_bwd(y, z, w, inv_rms, g, workspace=None, stream=None, dy_dtype=torch.float32):
+def rmsnorm_gated_bwd(y, z, w, inv_rms, g, workspace=None, stream=None, dy_dtype=torch.float32,
+                      dz_dtype=torch.float32):
     """Backward of rmsnorm_gated_fwd with the saved inv_rms; returns
-    (dy in dy_dtype, dz f32, dw f32)."""
+    (dy in dy_dtype, dz in dz_dtype, dw f32); bf16 outputs are rounded to
+    nearest even."""
     _on_gpu(y, "y")
     lib = load_library()
     width = y.shape[-1]
@@ -411,16 +417,19 @@ def rmsnorm_gated_bwd(y, z, w, inv_rms, g, workspace=None, stream=None, dy_dtype
     _need(w, "w", (width,), torch.float32, y.device)
     _need(inv_rms, "inv_rms", tuple(y.shape[:-1]), torch.float32, y.device)
     _need(g, "g", tuple(y.shape), None, y.device)
+    for name, dt_ in (("dy_dtype", dy_dtype), ("dz_dtype", dz_dtype)):
+        if dt_ not in (torch.float32, torch.bfloat16):
+            raise TypeError(f"{name} must be torch.float32 or torch.bfloat16")
     f32 = dict(dtype=torch.float32, device=y.device)
     dy = torch.empty(tuple(y.shape), dtype=dy_dtype, device=y.device)
-    dz = torch.empty(tuple(y.shape), **f32)
+    dz = torch.empty(tuple(y.shape), dtype=dz_dtype, device=y.device)
     dw = torch.empty((width,), **f32)
     need = lib.mamba2_rmsnorm_gated_bwd_workspace_bytes(rows, width)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=y.device)
     wsz = _need_workspace(workspace, y.device)
-    _check(lib.mamba2_rmsnorm_gated_bwd(rows, width, _code(y.dtype), _code(g.dtype), _code(dy_dtype), _ptr(y),
-                                        _ptr(z), _ptr(w),
+    _check(lib.mamba2_rmsnorm_gated_bwd(rows, width, _code(y.dtype), _code(g.dtype), _code(dy_dtype),
+                                        _code(dz_dtype), _ptr(y), _ptr(z), _ptr(w),
                                         _ptr(inv_rms), _ptr(g), _ptr(dy), _ptr(dz), _ptr(dw), _ptr(workspace), wsz,
                                         _stream(stream)))
     return dy, dz, dw

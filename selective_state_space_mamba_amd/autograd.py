@@ -100,22 +100,25 @@ def _core_fwd(xbc, dt_raw, z, conv_w, conv_b, dt_bias, A_log, D, norm_w, init_st
 
 
 def _core_bwd(xbc, dt_raw, z, conv_w, conv_b, dt_bias, A_log, D, norm_w, init_state, saved, dims, gout, gfin,
-              want_dh0):
+              want_dh0, act_grad_dtype=torch.float32):
     """Backward of the block slice: (dxbc, ddt_raw, dz, dconv_w, dconv_b, d_dt_bias,
-    dA_log, dD, dnorm_w, d_init_state), all f32."""
+    dA_log, dD, dnorm_w, d_init_state), f32 but for dxbc and dz, which the
+    kernels write in act_grad_dtype (bf16: rounded to nearest even, the values
+    a cast of the f32 gradients gives)."""
     dt, xs, Bs, Cs, y, inv, cs, csb = saved
     ngroups, dstate, headdim, chunk, eps = dims
     b, T, d_inner = z.shape
     H = d_inner // headdim
     # the gradient handed to the SSD backward is stored in the activation
     # dtype, as the block-slice step does
-    gy, gz, gnw = _b.rmsnorm_gated_bwd(y.view(b, T, d_inner), z, norm_w, inv, gout, dy_dtype=xbc.dtype)
+    gy, gz, gnw = _b.rmsnorm_gated_bwd(y.view(b, T, d_inner), z, norm_w, inv, gout, dy_dtype=xbc.dtype,
+                                       dz_dtype=act_grad_dtype)
     gy = gy.view(b, T, H, headdim)
     g = _b.ssd_bwd(xs, dt, A_log, Bs, Cs, D, gy, init_state, **_history_args(cs, csb, gy),
                    chunk=chunk, want_d_init_state=want_dh0,
                    d_final_state=None if gfin is None else gfin.float().contiguous())
     dxbc, dcw, dcb = _b.conv1d_silu_bwd(xbc, conv_w, conv_b, g["dx"].view(b, T, d_inner), g["dB"], g["dC"],
-                                        d_inner, ngroups, dstate)
+                                        d_inner, ngroups, dstate, dxbc_dtype=act_grad_dtype)
     ddt_raw, d_bias = _b.dt_softplus_bwd(dt_raw, dt_bias, g["ddt"])
     return dxbc, ddt_raw, gz, dcw, dcb, d_bias, g["dA_log"], g["dD"], gnw, g["d_init_state"]
 
@@ -180,12 +183,15 @@ class _Block(torch.autograd.Function):
         gout = _b.gemm(go2, W_out).view(b, T, -1)
         dW_out = _b.gemm(go2, out.view(b * T, -1), trans_a=True, out_dtype=torch.float32)
         init_state = t[15]
+        # dz and dxbc come out of their kernels in bf16, the operand dtype of
+        # the products below (the same values as a cast of the f32 gradients)
         (dxbc, ddt_raw, dz, dcw, dcb, d_bias, dA, dD, dnw, dh0) = _core_bwd(
-            *t[6:16], t[16:], ctx.dims, gout, gfin, init_state is not None and ctx.needs_input_grad[11])
+            *t[6:16], t[16:], ctx.dims, gout, gfin, init_state is not None and ctx.needs_input_grad[11],
+            act_grad_dtype=torch.bfloat16)
         du = None
         dWs = []
         for g, W in ((dz, W_z), (dxbc, W_xbc), (ddt_raw, W_dt)):
-            gb = _b.cast_bf16(g.view(b * T, -1))
+            gb = g.view(b * T, -1) if g.dtype == torch.bfloat16 else _b.cast_bf16(g.view(b * T, -1))
             du = _b.gemm(gb, W, out=du, out_dtype=torch.float32, beta=0.0 if du is None else 1.0)
             dWs.append(_b.gemm(gb, u2, trans_a=True, out_dtype=torch.float32))
         return (du.view(b, T, dm), dWs[0], dWs[1], dWs[2], dcw, dcb, d_bias, dA, dD, dnw, dW_out, dh0, None)
@@ -200,9 +206,10 @@ def mamba2_block(u: torch.Tensor, W_z: torch.Tensor, W_xbc: torch.Tensor, W_dt: 
     weights: z, xbc, dt_raw = u W_z^T, u W_xbc^T, u W_dt^T (the three parts of
     in_proj, [out_features, d_model] each), the block slice of
     mamba2_block_core, and o = out W_out^T (W_out [d_model, d_inner]).  The
-    projections run through ssd_gemm (rocBLAS, f32 accumulation); the gradient
-    entering the slice from out_proj is bf16 and the slice's f32 gradients are
-    rounded to bf16 for the backward products.  Returns
+    projections run through ssd_gemm (hipBLASLt, f32 accumulation); the
+    gradient entering the slice from out_proj is bf16 and the slice's
+    gradients of z, xbc and dt_raw are rounded to bf16 for the backward
+    products (z and xbc by the kernels that form them).  Returns
     (o [b,T,d_model], final_state)."""
     return _Block.apply(u, W_z, W_xbc, W_dt, conv_w, conv_b, dt_bias, A_log, D, norm_w, W_out, init_state,
                         (ngroups, dstate, headdim, chunk, eps))

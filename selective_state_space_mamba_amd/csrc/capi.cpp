@@ -680,10 +680,12 @@ int mamba2_conv1d_silu_fwd(int64_t batch, int64_t seqlen, int64_t d_inner, int64
 
 int mamba2_conv1d_silu_bwd(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t ngroups, int64_t dstate,
                            int64_t d_conv, int32_t dtype, const void* xbc, const float* w, const float* bias,
-                           const float* dx, const float* dB, const float* dC, float* dxbc, float* dw, float* dbias,
-                           void* workspace, size_t workspace_bytes, void* stream) {
+                           const float* dx, const float* dB, const float* dC, int32_t dxbc_dtype, void* dxbc,
+                           float* dw, float* dbias, void* workspace, size_t workspace_bytes, void* stream) {
   int rc = check_conv(batch, seqlen, d_inner, ngroups, dstate, d_conv, dtype);
   if (rc != SSD_OK) return rc;
+  if (!valid_dtype(dxbc_dtype))
+    return fail(SSD_ERR_DTYPE, "conv1d_silu_bwd: dxbc_dtype %d is not SSD_F32 or SSD_BF16", dxbc_dtype);
   if (!dw || !dbias) return fail(SSD_ERR_INVALID_ARG, "conv1d_silu_bwd: dw and dbias are required");
   const int64_t cd = d_inner + 2 * ngroups * dstate;
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -703,8 +705,8 @@ int mamba2_conv1d_silu_bwd(int64_t batch, int64_t seqlen, int64_t d_inner, int64
                 workspace ? workspace_bytes : 0, need);
   SSD_LAUNCH(ssd::launch_conv_bwd(static_cast<int>(batch), static_cast<int>(seqlen), static_cast<int>(d_inner),
                                   static_cast<int>(ngroups * dstate), static_cast<int>(d_conv),
-                                  static_cast<ssd::DType>(dtype), xbc, w, bias, dx, dB, dC, dxbc, dw, dbias,
-                                  static_cast<float*>(workspace), st),
+                                  static_cast<ssd::DType>(dtype), xbc, w, bias, dx, dB, dC, dxbc,
+                                  static_cast<ssd::DType>(dxbc_dtype), dw, dbias, static_cast<float*>(workspace), st),
              "conv1d_silu_bwd");
   return ok();
 }
@@ -742,13 +744,16 @@ int mamba2_rmsnorm_gated_fwd(int64_t rows, int64_t width, float eps, int32_t dty
 }
 
 int mamba2_rmsnorm_gated_bwd(int64_t rows, int64_t width, int32_t dtype, int32_t g_dtype, int32_t dy_dtype,
-                             const void* y, const void* z, const float* w, const float* inv_rms, const void* g,
-                             void* dy, float* dz, float* dw, void* workspace, size_t workspace_bytes, void* stream) {
+                             int32_t dz_dtype, const void* y, const void* z, const float* w, const float* inv_rms,
+                             const void* g, void* dy, void* dz, float* dw, void* workspace, size_t workspace_bytes,
+                             void* stream) {
   int rc = check_rms(rows, width, dtype);
   if (rc != SSD_OK) return rc;
   if (!valid_dtype(g_dtype)) return fail(SSD_ERR_DTYPE, "rmsnorm_gated_bwd: g_dtype %d is not SSD_F32 or SSD_BF16", g_dtype);
   if (!valid_dtype(dy_dtype))
     return fail(SSD_ERR_DTYPE, "rmsnorm_gated_bwd: dy_dtype %d is not SSD_F32 or SSD_BF16", dy_dtype);
+  if (!valid_dtype(dz_dtype))
+    return fail(SSD_ERR_DTYPE, "rmsnorm_gated_bwd: dz_dtype %d is not SSD_F32 or SSD_BF16", dz_dtype);
   if (!dw) return fail(SSD_ERR_INVALID_ARG, "rmsnorm_gated_bwd: dw is required");
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (rows == 0) {
@@ -766,7 +771,7 @@ int mamba2_rmsnorm_gated_bwd(int64_t rows, int64_t width, int32_t dtype, int32_t
                 workspace ? workspace_bytes : 0, need);
   SSD_LAUNCH(ssd::launch_rms_bwd(rows, static_cast<int>(width), static_cast<ssd::DType>(dtype),
                                  static_cast<ssd::DType>(g_dtype), static_cast<ssd::DType>(dy_dtype), y, z, w,
-                                 inv_rms, g, dy, dz, dw,
+                                 inv_rms, g, dy, dz, static_cast<ssd::DType>(dz_dtype), dw,
                                  static_cast<float*>(workspace), st),
              "rmsnorm_gated_bwd");
   return ok();

@@ -87,6 +87,26 @@ __device__ __forceinline__ void zerov(float (&f)[V]) {
   for (int i = 0; i < V; ++i) f[i] = 0.f;
 }
 
+// A gradient output whose dtype is chosen at run time: f32, or bf16 rounded to
+// nearest even (the values a later f32 -> bf16 cast of the f32 output gives).
+struct GradOut {
+  void* p;
+  int bf;  // nonzero: bf16
+  __device__ __forceinline__ void put(int64_t i, float v) const {
+    if (bf)
+      static_cast<uint16_t*>(p)[i] = f32_to_bf16_bits(v);
+    else
+      static_cast<float*>(p)[i] = v;
+  }
+  template <int V>
+  __device__ __forceinline__ void putv(int64_t i, const float (&f)[V]) const {
+    if (bf)
+      stv<V>(static_cast<uint16_t*>(p) + i, f);
+    else
+      stv<V>(static_cast<float*>(p) + i, f);
+  }
+};
+
 // Where channel c0 of the conv's channel axis (x, then B, then C) lives among
 // the three split tensors: base pointer, row length, offset in the row.
 template <typename T>
@@ -174,7 +194,7 @@ template <typename TI, int K>
 __global__ __launch_bounds__(256) void conv_bwd_kernel(const TI* __restrict__ xbc, const float* __restrict__ w,
                                                       const float* __restrict__ bias, const float* __restrict__ dx,
                                                       const float* __restrict__ dB, const float* __restrict__ dC,
-                                                      float* __restrict__ dxbc, float* __restrict__ part, int T,
+                                                      GradOut dxbc, float* __restrict__ part, int T,
                                                       int Cd, int d_inner, int gn, int run) {
   const int c = blockIdx.x * blockDim.x + threadIdx.x;
   if (c >= Cd) return;
@@ -208,7 +228,7 @@ __global__ __launch_bounds__(256) void conv_bwd_kernel(const TI* __restrict__ xb
     float dsum = 0.f;
 #pragma unroll
     for (int k = 0; k < K; ++k) dsum += gw[K - 1 - k] * wk[k];
-    dxbc[(rb + u) * Cd + c] = dsum;
+    dxbc.put((rb + u) * Cd + c, dsum);
     accb += gw[0];
 #pragma unroll
     for (int k = 0; k < K; ++k) acc[k] += gw[0] * xw[k];
@@ -313,15 +333,17 @@ struct XStep<uint16_t> {
 //   gw[m] = gp[u + m],          m = 0 .. K-1    (zero at steps >= T)
 // The workgroup's four runs add their tap / bias partials in LDS in wave order
 // and store one partial [b, ceil(T/CONV_RUN), Cd, K+1] as the scalar kernel does.
-template <typename TI, int K>
+// dxbc is written in TD (f32, or bf16 rounded to nearest even).
+template <typename TI, int K, typename TD>
 __global__ __launch_bounds__(256, K <= 4 ? 4 : 2) void conv_bwd_vec_kernel(const TI* __restrict__ xbc, const float* __restrict__ w,
                                                           const float* __restrict__ bias, const float* __restrict__ dx,
                                                           const float* __restrict__ dB, const float* __restrict__ dC,
-                                                          float* __restrict__ dxbc, float* __restrict__ part, int T,
+                                                          TD* __restrict__ dxbc, float* __restrict__ part, int T,
                                                           int Cd, int d_inner, int gn) {
-  // steps of loads in flight: four with bf16 activations (their packed window
-  // leaves room at 4 waves per SIMD for K = 4), two with f32
-  constexpr int V = 4, U = sizeof(TI) == 2 ? 3 : 2;
+  // steps of loads in flight: three with bf16 activations and an f32 dxbc
+  // (their packed window leaves room at 4 waves per SIMD for K = 4), two
+  // otherwise (the bf16 rounding of dxbc takes that room)
+  constexpr int V = 4, U = sizeof(TI) == 2 && sizeof(TD) == 4 ? 3 : 2;
   constexpr int NP = V * (K + 1);  // partial values per lane
   __shared__ float red[WAVE * NP];
   const int lane = lane_id(), wv = wave_id();
@@ -500,7 +522,7 @@ template <typename TI, typename TG, typename TO>
 __global__ __launch_bounds__(256) void rms_bwd_kernel(const TI* __restrict__ y, const TI* __restrict__ z,
                                                      const float* __restrict__ w, const float* __restrict__ inv_rms,
                                                      const TG* __restrict__ g, TO* __restrict__ dy,
-                                                     float* __restrict__ dz, float* __restrict__ part, int64_t rows,
+                                                     GradOut dz, float* __restrict__ part, int64_t rows,
                                                      int width) {
   __shared__ float tmp[4];
   constexpr int MAXPER = 16;  // width <= 256 * MAXPER
@@ -525,7 +547,7 @@ __global__ __launch_bounds__(256) void rms_bwd_kernel(const TI* __restrict__ y, 
       const float gw = gv * gate;
       dwacc[k] += gw * normalized;
       store_f(dy, base + i, gw * w[i] * inv - yv * coef);
-      dz[base + i] = gv * normalized * w[i] * s * (1.f + zv * (1.f - s));
+      dz.put(base + i, gv * normalized * w[i] * s * (1.f + zv * (1.f - s)));
     }
   }
   for (int i = threadIdx.x, k = 0; i < width; i += 256, ++k) part[static_cast<int64_t>(blockIdx.x) * width + i] = dwacc[k];
@@ -587,7 +609,7 @@ constexpr int RMS_VEC_WAVES = 8;
 template <typename TI, typename TG, typename TO, int KCH>
 __global__ __launch_bounds__(RMS_VEC_WAVES * WAVE) void rms_bwd_vec_kernel(
     const TI* __restrict__ y, const TI* __restrict__ z, const float* __restrict__ w,
-    const float* __restrict__ inv_rms, const TG* __restrict__ g, TO* __restrict__ dy, float* __restrict__ dz,
+    const float* __restrict__ inv_rms, const TG* __restrict__ g, TO* __restrict__ dy, GradOut dz,
     float* __restrict__ part, int64_t rows, int width) {
   constexpr int NT = RMS_VEC_WAVES * WAVE;
   __shared__ float wl[8 * WAVE * KCH];
@@ -655,7 +677,7 @@ __global__ __launch_bounds__(RMS_VEC_WAVES * WAVE) void rms_bwd_vec_kernel(
         o_dz[e] = gv * normalized * wv * s * (1.f + zv * (1.f - s));
       }
       stv<8>(dy + base + 8 * c, o_dy);
-      stv<8>(dz + base + 8 * c, o_dz);
+      dz.putv<8>(base + 8 * c, o_dz);
     }
   }
   for (int q = 0; q < RMS_VEC_WAVES; ++q) {
@@ -767,12 +789,18 @@ static void conv_fwd_launch(int b, int T, int Cd, int d_inner, int gn, const voi
 
 template <typename TI, int K>
 static void conv_bwd_launch(int b, int T, int Cd, int d_inner, int gn, const void* xbc, const float* w,
-                            const float* bias, const float* dx, const float* dB, const float* dC, float* dxbc,
+                            const float* bias, const float* dx, const float* dB, const float* dC, GradOut dxbc,
                             float* part, hipStream_t st) {
   if (conv_vec_ok(d_inner, gn)) {
     dim3 grid((Cd / 4 + WAVE - 1) / WAVE, conv_nruns(T), b);
-    hipLaunchKernelGGL((conv_bwd_vec_kernel<TI, K>), grid, dim3(NTHREADS), 0, st, static_cast<const TI*>(xbc), w,
-                       bias, dx, dB, dC, dxbc, part, T, Cd, d_inner, gn);
+    if (dxbc.bf)
+      hipLaunchKernelGGL((conv_bwd_vec_kernel<TI, K, uint16_t>), grid, dim3(NTHREADS), 0, st,
+                         static_cast<const TI*>(xbc), w, bias, dx, dB, dC, static_cast<uint16_t*>(dxbc.p), part, T,
+                         Cd, d_inner, gn);
+    else
+      hipLaunchKernelGGL((conv_bwd_vec_kernel<TI, K, float>), grid, dim3(NTHREADS), 0, st,
+                         static_cast<const TI*>(xbc), w, bias, dx, dB, dC, static_cast<float*>(dxbc.p), part, T, Cd,
+                         d_inner, gn);
   } else {
     dim3 grid((Cd + 255) / 256, conv_nruns(T), b);
     hipLaunchKernelGGL((conv_bwd_kernel<TI, K>), grid, dim3(256), 0, st, static_cast<const TI*>(xbc), w, bias, dx,
@@ -810,13 +838,14 @@ hipError_t launch_conv_fwd(int b, int T, int d_inner, int gn, int K, DType dt, c
 }
 
 hipError_t launch_conv_bwd(int b, int T, int d_inner, int gn, int K, DType dt, const void* xbc, const float* w,
-                           const float* bias, const float* dx, const float* dB, const float* dC, float* dxbc,
-                           float* dw, float* dbias, float* part, hipStream_t st) {
+                           const float* bias, const float* dx, const float* dB, const float* dC, void* dxbc,
+                           DType dxt, float* dw, float* dbias, float* part, hipStream_t st) {
   const int Cd = d_inner + 2 * gn;
+  const GradOut go{dxbc, dxt == BF16 ? 1 : 0};
   if (dt == BF16) {
-    SSD_CONV_DISPATCH(conv_bwd_launch, uint16_t, b, T, Cd, d_inner, gn, xbc, w, bias, dx, dB, dC, dxbc, part, st)
+    SSD_CONV_DISPATCH(conv_bwd_launch, uint16_t, b, T, Cd, d_inner, gn, xbc, w, bias, dx, dB, dC, go, part, st)
   } else {
-    SSD_CONV_DISPATCH(conv_bwd_launch, float, b, T, Cd, d_inner, gn, xbc, w, bias, dx, dB, dC, dxbc, part, st)
+    SSD_CONV_DISPATCH(conv_bwd_launch, float, b, T, Cd, d_inner, gn, xbc, w, bias, dx, dB, dC, go, part, st)
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -861,7 +890,7 @@ hipError_t launch_rms_fwd(int64_t rows, int width, float eps, DType dt, const vo
 
 template <typename TI, typename TG, typename TO>
 static void rms_bwd_launch(int64_t rows, int width, const void* y, const void* z, const float* w,
-                           const float* inv_rms, const void* g, void* dy, float* dz, float* part, hipStream_t st) {
+                           const float* inv_rms, const void* g, void* dy, GradOut dz, float* part, hipStream_t st) {
   const TI* yp = static_cast<const TI*>(y);
   const TI* zp = static_cast<const TI*>(z);
   const TG* gp = static_cast<const TG*>(g);
@@ -890,7 +919,7 @@ static void rms_bwd_launch(int64_t rows, int width, const void* y, const void* z
 
 template <typename TI, typename TG>
 static void rms_bwd_launch_o(DType ot, int64_t rows, int width, const void* y, const void* z, const float* w,
-                             const float* inv_rms, const void* g, void* dy, float* dz, float* part, hipStream_t st) {
+                             const float* inv_rms, const void* g, void* dy, GradOut dz, float* part, hipStream_t st) {
   if (ot == BF16)
     rms_bwd_launch<TI, TG, uint16_t>(rows, width, y, z, w, inv_rms, g, dy, dz, part, st);
   else
@@ -898,18 +927,19 @@ static void rms_bwd_launch_o(DType ot, int64_t rows, int width, const void* y, c
 }
 
 hipError_t launch_rms_bwd(int64_t rows, int width, DType dt, DType gt, DType ot, const void* y, const void* z,
-                          const float* w, const float* inv_rms, const void* g, void* dy, float* dz, float* dw,
-                          float* part, hipStream_t st) {
+                          const float* w, const float* inv_rms, const void* g, void* dy, void* dz, DType zt,
+                          float* dw, float* part, hipStream_t st) {
+  const GradOut go{dz, zt == BF16 ? 1 : 0};
   if (dt == BF16) {
     if (gt == BF16)
-      rms_bwd_launch_o<uint16_t, uint16_t>(ot, rows, width, y, z, w, inv_rms, g, dy, dz, part, st);
+      rms_bwd_launch_o<uint16_t, uint16_t>(ot, rows, width, y, z, w, inv_rms, g, dy, go, part, st);
     else
-      rms_bwd_launch_o<uint16_t, float>(ot, rows, width, y, z, w, inv_rms, g, dy, dz, part, st);
+      rms_bwd_launch_o<uint16_t, float>(ot, rows, width, y, z, w, inv_rms, g, dy, go, part, st);
   } else {
     if (gt == BF16)
-      rms_bwd_launch_o<float, uint16_t>(ot, rows, width, y, z, w, inv_rms, g, dy, dz, part, st);
+      rms_bwd_launch_o<float, uint16_t>(ot, rows, width, y, z, w, inv_rms, g, dy, go, part, st);
     else
-      rms_bwd_launch_o<float, float>(ot, rows, width, y, z, w, inv_rms, g, dy, dz, part, st);
+      rms_bwd_launch_o<float, float>(ot, rows, width, y, z, w, inv_rms, g, dy, go, part, st);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

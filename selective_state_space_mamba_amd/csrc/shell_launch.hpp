@@ -15,17 +15,18 @@ int conv_max_k();
 
 hipError_t launch_conv_fwd(int b, int T, int d_inner, int gn, int K, DType dt, const void* xbc, const float* w,
                            const float* bias, void* x_out, void* B_out, void* C_out, hipStream_t st);
-// part: [b * conv_nruns(T), conv_dim, K + 1] floats of scratch
+// part: [b * conv_nruns(T), conv_dim, K + 1] floats of scratch; dxbc in `dxt`
+// (f32 or bf16)
 hipError_t launch_conv_bwd(int b, int T, int d_inner, int gn, int K, DType dt, const void* xbc, const float* w,
-                           const float* bias, const float* dx, const float* dB, const float* dC, float* dxbc,
-                           float* dw, float* dbias, float* part, hipStream_t st);
+                           const float* bias, const float* dx, const float* dB, const float* dC, void* dxbc,
+                           DType dxt, float* dw, float* dbias, float* part, hipStream_t st);
 hipError_t launch_rms_fwd(int64_t rows, int width, float eps, DType dt, const void* y, const void* z, const float* w,
                           void* out, float* inv_rms, hipStream_t st);
 // part: [rms_nparts(rows), width] floats of scratch
-// dy in `ot` (f32 or bf16); dz, dw f32
+// dy in `ot`, dz in `zt` (f32 or bf16); dw f32
 hipError_t launch_rms_bwd(int64_t rows, int width, DType dt, DType gt, DType ot, const void* y, const void* z,
-                          const float* w, const float* inv_rms, const void* g, void* dy, float* dz, float* dw,
-                          float* part, hipStream_t st);
+                          const float* w, const float* inv_rms, const void* g, void* dy, void* dz, DType zt,
+                          float* dw, float* part, hipStream_t st);
 
 // dt = softplus(raw + bias[h]) over rows x H, in `dt` (f32 or bf16)
 int dt_nparts(int64_t rows);

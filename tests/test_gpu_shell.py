@@ -82,6 +82,54 @@ def test_rmsnorm_gated(rows, width, dtype, gdtype, dydtype):
     assert all(v <= tol for v in errs.values()), errs
 
 
+@pytest.mark.parametrize("b,T,d_inner,G,N,K,dtype", [
+    (2, 300, 64, 2, 16, 4, "bf16"),      # vector kernel
+    (2, 300, 64, 1, 16, 3, "f32"),
+    (2, 200, 36, 1, 6, 4, "bf16"),       # scalar kernel
+    (8, 2048, 3072, 1, 128, 4, "bf16"),  # the block-slice shape
+])
+def test_conv1d_silu_bwd_bf16_dxbc_is_the_cast(b, T, d_inner, G, N, K, dtype):
+    """dxbc written in bf16 by the kernel equals, bit for bit, the f32 dxbc
+    rounded by ssd_cast_f32_to_bf16; the other outputs do not change."""
+    xbc, w, bias, gact = conv_case(13, b, T, d_inner, G, N, K, dtype)
+    gx = dev(np.ascontiguousarray(gact[..., :d_inner]))
+    gB = dev(np.ascontiguousarray(gact[..., d_inner:d_inner + G * N].reshape(b, T, G, N)))
+    gC = dev(np.ascontiguousarray(gact[..., d_inner + G * N:].reshape(b, T, G, N)))
+    args = (dev(xbc), dev(w), dev(bias), gx, gB, gC, d_inner, G, N)
+    d32, dw32, db32 = ssd.conv1d_silu_bwd(*args)
+    d16, dw16, db16 = ssd.conv1d_silu_bwd(*args, dxbc_dtype=torch.bfloat16)
+    ref = ssd.cast_bf16(d32.reshape(-1)).view(d16.shape)
+    torch.cuda.synchronize()
+    assert d16.dtype == torch.bfloat16
+    assert torch.equal(d16.view(torch.int16), ref.view(torch.int16))
+    assert torch.equal(dw16, dw32) and torch.equal(db16, db32)
+
+
+@pytest.mark.parametrize("rows,width,dtype,gdtype", [
+    ((2, 37), 200, "bf16", "f32"),      # vector kernel
+    ((8, 2048), 3072, "bf16", "bf16"),  # the block-slice shape
+    ((3, 33), 100, "bf16", "bf16"),     # scalar kernel
+    ((1, 1), 4096, "f32", "bf16"),
+])
+def test_rmsnorm_gated_bwd_bf16_dz_is_the_cast(rows, width, dtype, gdtype):
+    """dz written in bf16 by the kernel equals, bit for bit, the f32 dz rounded
+    by ssd_cast_f32_to_bf16; dy and dw do not change."""
+    rng = np.random.default_rng(14)
+    y = Stored(rng.standard_normal(rows + (width,)).astype(np.float32), dtype)
+    z = Stored(rng.standard_normal(rows + (width,)).astype(np.float32), dtype)
+    w = (1.0 + 0.1 * rng.standard_normal(width)).astype(np.float32)
+    g = Stored(rng.standard_normal(rows + (width,)).astype(np.float32), gdtype)
+    _, inv = ssd.rmsnorm_gated_fwd(dev(y), dev(z), dev(w), 1e-5)
+    args = (dev(y), dev(z), dev(w), inv, dev(g))
+    dy32, dz32, dw32 = ssd.rmsnorm_gated_bwd(*args)
+    dy16, dz16, dw16 = ssd.rmsnorm_gated_bwd(*args, dz_dtype=torch.bfloat16)
+    ref = ssd.cast_bf16(dz32.reshape(-1)).view(dz16.shape)
+    torch.cuda.synchronize()
+    assert dz16.dtype == torch.bfloat16
+    assert torch.equal(dz16.view(torch.int16), ref.view(torch.int16))
+    assert torch.equal(dy16, dy32) and torch.equal(dw16, dw32)
+
+
 def test_block_slice_end_to_end():
     """dt activation and conv1d+SiLU -> SSD -> RMSNorm-gated forward and the
     backward through all of them at the block-slice size, against the oracle chain run in f64 from the
