@@ -449,7 +449,16 @@ def make_train_step(cfg, d):
     b, T, H, P, N, G, Q = cfg.batch, cfg.seqlen, cfg.nheads, cfg.headdim, cfg.dstate, cfg.ngroups, cfg.chunk
     dm, di, cd, M = cfg.d_model, cfg.d_inner, cfg.conv_dim, cfg.batch * cfg.seqlen
     lib = ssd.load_library()
-    u, Wz, Wx, Wd, Wo, go = (to_dev(d[k]) for k in ("u", "W_z", "W_xbc", "W_dt", "W_out", "go"))
+    u, Wz, Wo, go = (to_dev(d[k]) for k in ("u", "W_z", "W_out", "go"))
+    # W_xbc and W_dt as the row blocks of one [conv_dim + H, d_model] matrix,
+    # so that the gradients of xBC and dt_raw, written side by side, meet them
+    # in one product each for du and for the weight gradients
+    # (rows padded with zeros to a multiple of 64, the products' k-tile)
+    cdh = -(-(cd + H) // 64) * 64
+    Wxd = torch.zeros((cdh, dm), dtype=torch.bfloat16, device="cuda")
+    Wxd[:cd] = to_dev(d["W_xbc"])
+    Wxd[cd:cd + H] = to_dev(d["W_dt"])
+    Wx, Wd = Wxd[:cd], Wxd[cd:cd + H]
     conv_w, conv_b, dt_bias = to_dev(d["conv_w"]), to_dev(d["conv_b"]), to_dev(d["dt_bias"])
     A_log, D, norm_w = to_dev(d["A_log"]), to_dev(d["D"]), to_dev(d["norm_w"])
     bf = dict(dtype=torch.bfloat16, device="cuda")
@@ -467,15 +476,18 @@ def make_train_step(cfg, d):
            "dA_log": torch.empty(H, **f32), "dB": torch.empty((b, T, G, N), **f32),
            "dC": torch.empty((b, T, G, N), **f32), "dD": torch.empty(H, **f32)}
     gact = torch.empty((M, di), **bf)  # the out_proj input gradient, in the activation dtype
-    dWo, dWz, dWx, dWd = (torch.empty(s_, **f32) for s_ in ((dm, di), (di, dm), (cd, dm), (H, dm)))
+    dWo, dWz, dWxd = (torch.empty(s_, **f32) for s_ in ((dm, di), (di, dm), (cdh, dm)))
     du = torch.empty((M, dm), **f32)
-    gd_bf = torch.empty((M, H), **bf)
+    # [d xBC | d dt_raw | zeros] in bf16, one row per token
+    gxd = torch.zeros((M, cdh), **bf)
+    gx_view, gd_view = gxd[:, :cd].view(b, T, cd), gxd[:, cd:cd + H]
     prob = ssd._binding.make_problem(fo["y"], to_dev(d["B"]), Q, torch.bfloat16)
     wsf = torch.empty(max(1, ssd.ssd_workspace_bytes(prob, False, f32h)), **u8)
     wsb = torch.empty(max(1, ssd.ssd_workspace_bytes(prob, True, f32h)), **u8)
     wsr = torch.empty(max(1, lib.mamba2_rmsnorm_gated_bwd_workspace_bytes(M, di)), **u8)
     wsc = torch.empty(max(1, lib.mamba2_conv1d_silu_bwd_workspace_bytes(b, T, di, G, N, conv_w.shape[1])), **u8)
     wsd = torch.empty(max(1, lib.ssd_dt_softplus_bwd_workspace_bytes(M, H)), **u8)
+    d_dt_bias = torch.empty(H, **f32)
 
     def step():
         ssd.gemm(u2, Wz, trans_b=True, out=z)
@@ -498,19 +510,18 @@ def make_train_step(cfg, d):
         g = ssd.ssd_bwd(xs, dt3, A_log, Bs, Cs, D, gy.view(b, T, H, P), None, chunk_states=r["chunk_states"],
                         chunk_states_bf16=r["chunk_states_bf16"], chunk=Q, out=go_,
                         workspace=wsb, want_d_init_state=False)
-        dxbc, _, _ = ssd.conv1d_silu_bwd(xbc.view(b, T, cd), conv_w, conv_b, g["dx"].view(b, T, di), g["dB"],
-                                         g["dC"], di, G, N, workspace=wsc, dxbc_dtype=torch.bfloat16)
-        ddt_raw, _ = ssd.dt_softplus_bwd(raw, dt_bias, g["ddt"].view(M, H), workspace=wsd)
-        # dz and dxbc come out of their kernels in bf16 (the values a cast of
-        # the f32 gradients gives); ddt_raw is cast
-        gz_bf, gx_bf = gz.view(M, di), dxbc.view(M, cd)
-        ssd.cast_bf16(ddt_raw, out=gd_bf)
+        # the gradients of z, xBC and dt_raw come out of their kernels in bf16
+        # (the values a cast of the f32 gradients gives), those of xBC and
+        # dt_raw side by side in gxd
+        ssd.conv1d_silu_bwd(xbc.view(b, T, cd), conv_w, conv_b, g["dx"].view(b, T, di), g["dB"], g["dC"], di, G,
+                            N, workspace=wsc, dxbc_dtype=torch.bfloat16, out=gx_view)
+        ssd.dt_softplus_bwd(raw, dt_bias, g["ddt"].view(M, H), workspace=wsd, out_dtype=torch.bfloat16,
+                            out=(gd_view, d_dt_bias))
+        gz_bf = gz.view(M, di)
         ssd.gemm(gz_bf, Wz, out=du)
-        ssd.gemm(gx_bf, Wx, out=du, beta=1.0)
-        ssd.gemm(gd_bf, Wd, out=du, beta=1.0)
+        ssd.gemm(gxd, Wxd, out=du, beta=1.0)
         ssd.gemm(gz_bf, u2, trans_a=True, out=dWz)
-        ssd.gemm(gx_bf, u2, trans_a=True, out=dWx)
-        ssd.gemm(gd_bf, u2, trans_a=True, out=dWd)
+        ssd.gemm(gxd, u2, trans_a=True, out=dWxd)
     return step
 
 
@@ -643,7 +654,7 @@ def main():
     # around every kernel (the events hold the stream up a little between
     # kernels, so they stay out of the timed region).
     kernels = KERNELS_FWD + KERNELS_BWD + (KERNELS_SHELL if cfg.shell else []) + (
-        ["gemm", "cast_bf16"] if cfg.d_model else [])
+        ["gemm"] if cfg.d_model else [])
     ssd.profile_enable(True)
     for _ in range(args.steps):
         step()
@@ -712,7 +723,10 @@ def main():
         "cpu_baseline": cpu,
     }
     if cfg.d_model and "gemm" in kms:
-        n_gemm = 12  # three in_proj products, out_proj, and their eight gradient products
+        # three in_proj products, out_proj, and its two gradient products; the
+        # in_proj gradients as two products for du and two for the weights
+        # (those of xBC and dt_raw together)
+        n_gemm = 10
         t_g = kms["gemm"] * n_gemm * 1e-3
         line["projections"] = {"ms_per_step": round(t_g * 1e3, 4), "calls": n_gemm,
                                "tflops": round(train_step_flops(cfg) / t_g / 1e12, 1),

@@ -179,15 +179,18 @@ size_t mamba2_conv1d_silu_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int
                                               int64_t ngroups, int64_t dstate, int64_t d_conv);
 
 /* Backward of mamba2_conv1d_silu_fwd.  dx [b,T,d_inner], dB, dC [b,T,G,N] are
- * the f32 gradients of its three outputs.  Outputs: dxbc [b,T,conv_dim] in
- * `dxbc_dtype` (SSD_F32, or SSD_BF16 rounded to nearest even: the values an
- * f32 -> bf16 cast of the f32 output gives, e.g. as a GEMM operand); dw
+ * the f32 gradients of its three outputs.  Outputs: dxbc, b*T rows of
+ * conv_dim elements, dxbc_ld elements apart (0: conv_dim; else a multiple of
+ * 4 >= conv_dim, e.g. to leave room for the dt_raw gradient beside it as one
+ * GEMM operand), in `dxbc_dtype` (SSD_F32, or SSD_BF16 rounded to nearest
+ * even: the values an f32 -> bf16 cast of the f32 output gives); dw
  * [conv_dim,d_conv] and dbias [conv_dim] f32. */
 int mamba2_conv1d_silu_bwd(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t ngroups,
                            int64_t dstate, int64_t d_conv, int32_t dtype, const void* xbc,
                            const float* w, const float* bias, const float* dx, const float* dB,
-                           const float* dC, int32_t dxbc_dtype, void* dxbc, float* dw, float* dbias,
-                           void* workspace, size_t workspace_bytes, void* stream);
+                           const float* dC, int32_t dxbc_dtype, void* dxbc, int64_t dxbc_ld,
+                           float* dw, float* dbias, void* workspace, size_t workspace_bytes,
+                           void* stream);
 
 /* RMSNorm-gated forward over rows of `width`: inv_rms = 1/sqrt(mean(y^2)+eps),
  * out = y * inv_rms * w * silu(z).  y, z, out in `dtype`; w [width] f32;
@@ -217,17 +220,20 @@ int mamba2_rmsnorm_gated_bwd(int64_t rows, int64_t width, int32_t dtype, int32_t
  *     rounded to nearest even, the form ssd_fwd / ssd_bwd read); dt_bias
  *     [nheads] f32.  dt may be passed to ssd_fwd and ssd_bwd as their dt.
  *   ssd_dt_softplus_bwd: ddt [rows,nheads] f32 is ssd_bwd's gradient of dt;
- *     outputs f32 ddt_raw [rows,nheads] (the gradient of dt_raw, equal to that
- *     of dt_pre) and d_dt_bias [nheads], a fixed-order sum of per-64-row
- *     partials held in the workspace.
+ *     outputs ddt_raw (the gradient of dt_raw, equal to that of dt_pre), rows
+ *     of nheads elements ddt_raw_ld apart (0: nheads), in `ddt_raw_dtype`
+ *     (SSD_F32, or SSD_BF16 rounded to nearest even), and f32 d_dt_bias
+ *     [nheads], a fixed-order sum of per-64-row partials held in the
+ *     workspace.
  * softplus(v) is evaluated as max(v,0) + log1p(exp(-|v|)).  Pointers are
  * 16-byte aligned device pointers; errors as for ssd_fwd. */
 int ssd_dt_softplus_fwd(int64_t rows, int64_t nheads, int32_t dtype, const void* dt_raw,
                         const float* dt_bias, void* dt, void* stream);
 size_t ssd_dt_softplus_bwd_workspace_bytes(int64_t rows, int64_t nheads);
 int ssd_dt_softplus_bwd(int64_t rows, int64_t nheads, int32_t dtype, const void* dt_raw,
-                        const float* dt_bias, const float* ddt, float* ddt_raw, float* d_dt_bias,
-                        void* workspace, size_t workspace_bytes, void* stream);
+                        const float* dt_bias, const float* ddt, int32_t ddt_raw_dtype, void* ddt_raw,
+                        int64_t ddt_raw_ld, float* d_dt_bias, void* workspace, size_t workspace_bytes,
+                        void* stream);
 
 /* Plain GEMM for the input and output projections around the block slice
  * (the in_proj / out_proj products of a Mamba-2 block's forward and

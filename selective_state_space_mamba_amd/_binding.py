@@ -59,7 +59,7 @@ def load_library():
     lib.mamba2_conv1d_silu_fwd.restype = ctypes.c_int
     lib.mamba2_conv1d_silu_bwd_workspace_bytes.argtypes = [i64] * 6
     lib.mamba2_conv1d_silu_bwd_workspace_bytes.restype = sz
-    lib.mamba2_conv1d_silu_bwd.argtypes = [i64] * 6 + [i32] + [vp] * 6 + [i32] + [vp] * 3 + [vp, sz, vp]
+    lib.mamba2_conv1d_silu_bwd.argtypes = [i64] * 6 + [i32] + [vp] * 6 + [i32, vp, i64, vp, vp] + [vp, sz, vp]
     lib.mamba2_conv1d_silu_bwd.restype = ctypes.c_int
     lib.mamba2_rmsnorm_gated_fwd.argtypes = [i64, i64, f32, i32] + [vp] * 5 + [vp]
     lib.mamba2_rmsnorm_gated_fwd.restype = ctypes.c_int
@@ -71,7 +71,7 @@ def load_library():
     lib.ssd_dt_softplus_fwd.restype = ctypes.c_int
     lib.ssd_dt_softplus_bwd_workspace_bytes.argtypes = [i64, i64]
     lib.ssd_dt_softplus_bwd_workspace_bytes.restype = sz
-    lib.ssd_dt_softplus_bwd.argtypes = [i64, i64, i32] + [vp] * 5 + [vp, sz, vp]
+    lib.ssd_dt_softplus_bwd.argtypes = [i64, i64, i32] + [vp] * 3 + [i32, vp, i64, vp] + [vp, sz, vp]
     lib.ssd_dt_softplus_bwd.restype = ctypes.c_int
     lib.ssd_gemm.argtypes = [i32, i32, i64, i64, i64, f32, vp, i64, vp, i64, f32, vp, i32, i64, vp]
     lib.ssd_gemm.restype = ctypes.c_int
@@ -147,6 +147,31 @@ def _need(t: torch.Tensor, name: str, shape, dtype=None, device=None):
         raise ValueError(f"{name} must be contiguous")
     if device is not None and t.device != device:
         raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _need_rows(t: torch.Tensor, name: str, shape, dtype, device) -> int:
+    """Check an output whose rows (all but the last axis, flattened) may lie a
+    fixed stride apart, e.g. a column slice of a wider matrix; returns that
+    stride in elements."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dim() < 2 or t.stride(-1) != 1:
+        raise ValueError(f"{name} must have unit stride along its last axis")
+    ld = t.stride(-2)
+    expect = ld
+    for i in range(t.dim() - 2, -1, -1):
+        if t.shape[i] > 1 and t.stride(i) != expect:
+            raise ValueError(f"{name}'s rows must lie a fixed stride apart")
+        expect *= t.shape[i]
+    if ld < shape[-1]:
+        raise ValueError(f"{name}'s row stride {ld} is below its row length {shape[-1]}")
+    return ld
 
 
 def _need_workspace(ws: Optional[torch.Tensor], device) -> int:
@@ -358,10 +383,12 @@ def conv1d_silu_fwd(xbc, w, bias, d_inner: int, ngroups: int, dstate: int, strea
 
 
 def conv1d_silu_bwd(xbc, w, bias, dx, dB, dC, d_inner: int, ngroups: int, dstate: int, workspace=None,
-                    stream=None, dxbc_dtype=torch.float32):
+                    stream=None, dxbc_dtype=torch.float32, out=None):
     """Backward of conv1d_silu_fwd given f32 gradients of its outputs; returns
     (dxbc [b,T,conv_dim] in dxbc_dtype (f32, or bf16 rounded to nearest even),
-    dw [conv_dim,d_conv] f32, dbias [conv_dim] f32)."""
+    dw [conv_dim,d_conv] f32, dbias [conv_dim] f32).  `out` may give dxbc: its
+    rows may lie a fixed stride apart (a column slice of a wider matrix, with
+    the stride a multiple of 4)."""
     _on_gpu(xbc, "xbc")
     lib = load_library()
     b, T, cd = xbc.shape
@@ -372,7 +399,12 @@ def conv1d_silu_bwd(xbc, w, bias, dx, dB, dC, d_inner: int, ngroups: int, dstate
     if dxbc_dtype not in (torch.float32, torch.bfloat16):
         raise TypeError("dxbc_dtype must be torch.float32 or torch.bfloat16")
     f32 = dict(dtype=torch.float32, device=xbc.device)
-    dxbc = torch.empty((b, T, cd), dtype=dxbc_dtype, device=xbc.device)
+    if out is None:
+        dxbc = torch.empty((b, T, cd), dtype=dxbc_dtype, device=xbc.device)
+        ld = cd
+    else:
+        dxbc = out
+        ld = _need_rows(dxbc, "out (dxbc)", (b, T, cd), dxbc_dtype, xbc.device)
     dw = torch.empty((cd, K), **f32)
     db = torch.empty((cd,), **f32)
     need = lib.mamba2_conv1d_silu_bwd_workspace_bytes(b, T, d_inner, ngroups, dstate, K)
@@ -380,7 +412,7 @@ def conv1d_silu_bwd(xbc, w, bias, dx, dB, dC, d_inner: int, ngroups: int, dstate
         workspace = torch.empty(need, dtype=torch.uint8, device=xbc.device)
     wsz = _need_workspace(workspace, xbc.device)
     _check(lib.mamba2_conv1d_silu_bwd(b, T, d_inner, ngroups, dstate, K, _code(xbc.dtype), _ptr(xbc), _ptr(w),
-                                      _ptr(bias), _ptr(dx), _ptr(dB), _ptr(dC), _code(dxbc_dtype), _ptr(dxbc),
+                                      _ptr(bias), _ptr(dx), _ptr(dB), _ptr(dC), _code(dxbc_dtype), _ptr(dxbc), ld,
                                       _ptr(dw), _ptr(db),
                                       _ptr(workspace), wsz, _stream(stream)))
     return dxbc, dw, db
@@ -451,9 +483,11 @@ def dt_softplus_fwd(dt_raw, dt_bias, out=None, stream=None):
     return dt
 
 
-def dt_softplus_bwd(dt_raw, dt_bias, ddt, workspace=None, out=None, stream=None):
-    """Backward of dt_softplus_fwd: returns (ddt_raw f32 [..., H], d_dt_bias f32 [H])
-    from ddt, the gradient of dt that ssd_bwd returns."""
+def dt_softplus_bwd(dt_raw, dt_bias, ddt, workspace=None, out=None, stream=None, out_dtype=torch.float32):
+    """Backward of dt_softplus_fwd: returns (ddt_raw [..., H] in out_dtype (f32,
+    or bf16 rounded to nearest even), d_dt_bias f32 [H]) from ddt, the gradient
+    of dt that ssd_bwd returns.  A given ddt_raw (out[0]) may have its rows a
+    fixed stride apart (a column slice of a wider matrix)."""
     _on_gpu(dt_raw, "dt_raw")
     lib = load_library()
     H = dt_raw.shape[-1]
@@ -461,18 +495,24 @@ def dt_softplus_bwd(dt_raw, dt_bias, ddt, workspace=None, out=None, stream=None)
     _need(dt_raw, "dt_raw", tuple(dt_raw.shape), None, dt_raw.device)
     _need(dt_bias, "dt_bias", (H,), torch.float32, dt_raw.device)
     _need(ddt, "ddt", tuple(dt_raw.shape), torch.float32, dt_raw.device)
+    if out_dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("out_dtype must be torch.float32 or torch.bfloat16")
     f32 = dict(dtype=torch.float32, device=dt_raw.device)
     if out is None:
-        out = (torch.empty(tuple(dt_raw.shape), **f32), torch.empty((H,), **f32))
+        out = (torch.empty(tuple(dt_raw.shape), dtype=out_dtype, device=dt_raw.device), torch.empty((H,), **f32))
     ddt_raw, d_bias = out
-    _need(ddt_raw, "out[0] (ddt_raw)", tuple(dt_raw.shape), torch.float32, dt_raw.device)
+    ld = _need_rows(ddt_raw, "out[0] (ddt_raw)", tuple(dt_raw.shape), out_dtype, dt_raw.device) \
+        if ddt_raw.dim() >= 2 else H
+    if ddt_raw.dim() < 2:
+        _need(ddt_raw, "out[0] (ddt_raw)", tuple(dt_raw.shape), out_dtype, dt_raw.device)
     _need(d_bias, "out[1] (d_dt_bias)", (H,), torch.float32, dt_raw.device)
     need = lib.ssd_dt_softplus_bwd_workspace_bytes(rows, H)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=dt_raw.device)
     wsz = _need_workspace(workspace, dt_raw.device)
     _check(lib.ssd_dt_softplus_bwd(rows, H, _code(dt_raw.dtype), _ptr(dt_raw), _ptr(dt_bias), _ptr(ddt),
-                                   _ptr(ddt_raw), _ptr(d_bias), _ptr(workspace), wsz, _stream(stream)))
+                                   _code(out_dtype), _ptr(ddt_raw), ld, _ptr(d_bias), _ptr(workspace), wsz,
+                                   _stream(stream)))
     return ddt_raw, d_bias
 
 

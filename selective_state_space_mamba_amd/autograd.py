@@ -100,11 +100,12 @@ def _core_fwd(xbc, dt_raw, z, conv_w, conv_b, dt_bias, A_log, D, norm_w, init_st
 
 
 def _core_bwd(xbc, dt_raw, z, conv_w, conv_b, dt_bias, A_log, D, norm_w, init_state, saved, dims, gout, gfin,
-              want_dh0, act_grad_dtype=torch.float32):
+              want_dh0, act_grad_dtype=torch.float32, gxd=None):
     """Backward of the block slice: (dxbc, ddt_raw, dz, dconv_w, dconv_b, d_dt_bias,
-    dA_log, dD, dnorm_w, d_init_state), f32 but for dxbc and dz, which the
-    kernels write in act_grad_dtype (bf16: rounded to nearest even, the values
-    a cast of the f32 gradients gives)."""
+    dA_log, dD, dnorm_w, d_init_state), f32 but for dz, dxbc and ddt_raw, which
+    the kernels write in act_grad_dtype (bf16: rounded to nearest even, the
+    values a cast of the f32 gradients gives); with gxd ([b*T, conv_dim + H] in
+    act_grad_dtype) dxbc and ddt_raw go into its two column blocks."""
     dt, xs, Bs, Cs, y, inv, cs, csb = saved
     ngroups, dstate, headdim, chunk, eps = dims
     b, T, d_inner = z.shape
@@ -117,9 +118,13 @@ def _core_bwd(xbc, dt_raw, z, conv_w, conv_b, dt_bias, A_log, D, norm_w, init_st
     g = _b.ssd_bwd(xs, dt, A_log, Bs, Cs, D, gy, init_state, **_history_args(cs, csb, gy),
                    chunk=chunk, want_d_init_state=want_dh0,
                    d_final_state=None if gfin is None else gfin.float().contiguous())
+    cd = xbc.shape[-1]
     dxbc, dcw, dcb = _b.conv1d_silu_bwd(xbc, conv_w, conv_b, g["dx"].view(b, T, d_inner), g["dB"], g["dC"],
-                                        d_inner, ngroups, dstate, dxbc_dtype=act_grad_dtype)
-    ddt_raw, d_bias = _b.dt_softplus_bwd(dt_raw, dt_bias, g["ddt"])
+                                        d_inner, ngroups, dstate, dxbc_dtype=act_grad_dtype,
+                                        out=None if gxd is None else gxd[:, :cd].view(b, T, cd))
+    ddt_out = None if gxd is None else (gxd[:, cd:cd + H].view(b, T, H),
+                                        torch.empty(H, dtype=torch.float32, device=xbc.device))
+    ddt_raw, d_bias = _b.dt_softplus_bwd(dt_raw, dt_bias, g["ddt"], out=ddt_out, out_dtype=act_grad_dtype)
     return dxbc, ddt_raw, gz, dcw, dcb, d_bias, g["dA_log"], g["dD"], gnw, g["d_init_state"]
 
 
@@ -183,18 +188,38 @@ class _Block(torch.autograd.Function):
         gout = _b.gemm(go2, W_out).view(b, T, -1)
         dW_out = _b.gemm(go2, out.view(b * T, -1), trans_a=True, out_dtype=torch.float32)
         init_state = t[15]
-        # dz and dxbc come out of their kernels in bf16, the operand dtype of
-        # the products below (the same values as a cast of the f32 gradients)
+        # the gradients of z, xbc and dt_raw come out of their kernels in bf16,
+        # the operand dtype of the products below (the same values as a cast of
+        # the f32 gradients), those of xbc and dt_raw side by side, so that one
+        # product each against [W_xbc; W_dt] gives their parts of du and dW
+        # (rows padded with zero columns to a multiple of 64, the products'
+        # k-tile; the dt_raw block starts 16-byte aligned when conv_dim % 8 ==
+        # 0, otherwise the two gradients take a product each)
+        cd, H = W_xbc.shape[0], W_dt.shape[0]
+        side = cd % 8 == 0
+        cdh = -(-(cd + H) // 64) * 64
+        gxd = None
+        if side:
+            gxd = torch.empty((b * T, cdh), dtype=torch.bfloat16, device=u.device)
+            gxd[:, cd + H:].zero_()
         (dxbc, ddt_raw, dz, dcw, dcb, d_bias, dA, dD, dnw, dh0) = _core_bwd(
             *t[6:16], t[16:], ctx.dims, gout, gfin, init_state is not None and ctx.needs_input_grad[11],
-            act_grad_dtype=torch.bfloat16)
-        du = None
-        dWs = []
-        for g, W in ((dz, W_z), (dxbc, W_xbc), (ddt_raw, W_dt)):
-            gb = g.view(b * T, -1) if g.dtype == torch.bfloat16 else _b.cast_bf16(g.view(b * T, -1))
-            du = _b.gemm(gb, W, out=du, out_dtype=torch.float32, beta=0.0 if du is None else 1.0)
-            dWs.append(_b.gemm(gb, u2, trans_a=True, out_dtype=torch.float32))
-        return (du.view(b, T, dm), dWs[0], dWs[1], dWs[2], dcw, dcb, d_bias, dA, dD, dnw, dW_out, dh0, None)
+            act_grad_dtype=torch.bfloat16, gxd=gxd)
+        gz = dz.view(b * T, -1)
+        du = _b.gemm(gz, W_z, out_dtype=torch.float32)
+        dWz = _b.gemm(gz, u2, trans_a=True, out_dtype=torch.float32)
+        if side:
+            Wxd = torch.cat([W_xbc, W_dt, W_dt.new_zeros((cdh - cd - H, W_dt.shape[1]))], dim=0)
+            du = _b.gemm(gxd, Wxd, out=du, out_dtype=torch.float32, beta=1.0)
+            dWxd = _b.gemm(gxd, u2, trans_a=True, out_dtype=torch.float32)
+            dWx, dWd = dWxd[:cd], dWxd[cd:cd + H]
+        else:
+            gx, gd = dxbc.reshape(b * T, cd), ddt_raw.reshape(b * T, H)
+            du = _b.gemm(gx, W_xbc, out=du, out_dtype=torch.float32, beta=1.0)
+            du = _b.gemm(gd, W_dt, out=du, out_dtype=torch.float32, beta=1.0)
+            dWx = _b.gemm(gx, u2, trans_a=True, out_dtype=torch.float32)
+            dWd = _b.gemm(gd, u2, trans_a=True, out_dtype=torch.float32)
+        return (du.view(b, T, dm), dWz, dWx, dWd, dcw, dcb, d_bias, dA, dD, dnw, dW_out, dh0, None)
 
 
 def mamba2_block(u: torch.Tensor, W_z: torch.Tensor, W_xbc: torch.Tensor, W_dt: torch.Tensor,

@@ -681,13 +681,19 @@ int mamba2_conv1d_silu_fwd(int64_t batch, int64_t seqlen, int64_t d_inner, int64
 int mamba2_conv1d_silu_bwd(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t ngroups, int64_t dstate,
                            int64_t d_conv, int32_t dtype, const void* xbc, const float* w, const float* bias,
                            const float* dx, const float* dB, const float* dC, int32_t dxbc_dtype, void* dxbc,
-                           float* dw, float* dbias, void* workspace, size_t workspace_bytes, void* stream) {
+                           int64_t dxbc_ld, float* dw, float* dbias, void* workspace, size_t workspace_bytes,
+                           void* stream) {
   int rc = check_conv(batch, seqlen, d_inner, ngroups, dstate, d_conv, dtype);
   if (rc != SSD_OK) return rc;
   if (!valid_dtype(dxbc_dtype))
     return fail(SSD_ERR_DTYPE, "conv1d_silu_bwd: dxbc_dtype %d is not SSD_F32 or SSD_BF16", dxbc_dtype);
   if (!dw || !dbias) return fail(SSD_ERR_INVALID_ARG, "conv1d_silu_bwd: dw and dbias are required");
   const int64_t cd = d_inner + 2 * ngroups * dstate;
+  if (dxbc_ld == 0) dxbc_ld = cd;
+  // a row's elements stay 16 bytes (f32) or 8 bytes (bf16) aligned in groups of four
+  if (dxbc_ld < cd || dxbc_ld % 4 != 0)
+    return fail(SSD_ERR_INVALID_ARG, "conv1d_silu_bwd: dxbc_ld %lld must be 0 or a multiple of 4 >= %lld",
+                (long long)dxbc_ld, (long long)cd);
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (batch == 0 || seqlen == 0) {
     SSD_LAUNCH(ssd::launch_fill(dw, cd * d_conv, 0.f, st), "fill");
@@ -706,7 +712,8 @@ int mamba2_conv1d_silu_bwd(int64_t batch, int64_t seqlen, int64_t d_inner, int64
   SSD_LAUNCH(ssd::launch_conv_bwd(static_cast<int>(batch), static_cast<int>(seqlen), static_cast<int>(d_inner),
                                   static_cast<int>(ngroups * dstate), static_cast<int>(d_conv),
                                   static_cast<ssd::DType>(dtype), xbc, w, bias, dx, dB, dC, dxbc,
-                                  static_cast<ssd::DType>(dxbc_dtype), dw, dbias, static_cast<float*>(workspace), st),
+                                  static_cast<ssd::DType>(dxbc_dtype), dxbc_ld, dw, dbias,
+                                  static_cast<float*>(workspace), st),
              "conv1d_silu_bwd");
   return ok();
 }
@@ -810,10 +817,16 @@ size_t ssd_dt_softplus_bwd_workspace_bytes(int64_t rows, int64_t nheads) {
 }
 
 int ssd_dt_softplus_bwd(int64_t rows, int64_t nheads, int32_t dtype, const void* dt_raw, const float* dt_bias,
-                        const float* ddt, float* ddt_raw, float* d_dt_bias, void* workspace, size_t workspace_bytes,
-                        void* stream) {
+                        const float* ddt, int32_t ddt_raw_dtype, void* ddt_raw, int64_t ddt_raw_ld,
+                        float* d_dt_bias, void* workspace, size_t workspace_bytes, void* stream) {
   int rc = check_dt(rows, nheads, dtype);
   if (rc != SSD_OK) return rc;
+  if (!valid_dtype(ddt_raw_dtype))
+    return fail(SSD_ERR_DTYPE, "dt_softplus_bwd: ddt_raw_dtype %d is not SSD_F32 or SSD_BF16", ddt_raw_dtype);
+  if (ddt_raw_ld == 0) ddt_raw_ld = nheads;
+  if (ddt_raw_ld < nheads)
+    return fail(SSD_ERR_INVALID_ARG, "dt_softplus_bwd: ddt_raw_ld %lld is below nheads %lld",
+                (long long)ddt_raw_ld, (long long)nheads);
   if (!d_dt_bias) return fail(SSD_ERR_INVALID_ARG, "dt_softplus_bwd: d_dt_bias is required");
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (rows == 0) {
@@ -830,7 +843,8 @@ int ssd_dt_softplus_bwd(int64_t rows, int64_t nheads, int32_t dtype, const void*
     return fail(SSD_ERR_WORKSPACE, "dt_softplus_bwd: workspace of %zu bytes is smaller than the %zu needed",
                 workspace ? workspace_bytes : 0, need);
   SSD_LAUNCH(ssd::launch_dt_softplus_bwd(rows, static_cast<int>(nheads), static_cast<ssd::DType>(dtype), dt_raw,
-                                         dt_bias, ddt, ddt_raw, d_dt_bias, static_cast<float*>(workspace), st),
+                                         dt_bias, ddt, ddt_raw, static_cast<ssd::DType>(ddt_raw_dtype), ddt_raw_ld,
+                                         d_dt_bias, static_cast<float*>(workspace), st),
              "dt_softplus_bwd");
   return ok();
 }

@@ -88,10 +88,12 @@ __device__ __forceinline__ void zerov(float (&f)[V]) {
 }
 
 // A gradient output whose dtype is chosen at run time: f32, or bf16 rounded to
-// nearest even (the values a later f32 -> bf16 cast of the f32 output gives).
+// nearest even (the values a later f32 -> bf16 cast of the f32 output gives),
+// and whose rows (where the kernel takes them from here) are ld elements apart.
 struct GradOut {
   void* p;
-  int bf;  // nonzero: bf16
+  int bf;      // nonzero: bf16
+  int64_t ld;  // row stride in elements
   __device__ __forceinline__ void put(int64_t i, float v) const {
     if (bf)
       static_cast<uint16_t*>(p)[i] = f32_to_bf16_bits(v);
@@ -228,7 +230,7 @@ __global__ __launch_bounds__(256) void conv_bwd_kernel(const TI* __restrict__ xb
     float dsum = 0.f;
 #pragma unroll
     for (int k = 0; k < K; ++k) dsum += gw[K - 1 - k] * wk[k];
-    dxbc.put((rb + u) * Cd + c, dsum);
+    dxbc.put((rb + u) * dxbc.ld + c, dsum);
     accb += gw[0];
 #pragma unroll
     for (int k = 0; k < K; ++k) acc[k] += gw[0] * xw[k];
@@ -338,8 +340,8 @@ template <typename TI, int K, typename TD>
 __global__ __launch_bounds__(256, K <= 4 ? 4 : 2) void conv_bwd_vec_kernel(const TI* __restrict__ xbc, const float* __restrict__ w,
                                                           const float* __restrict__ bias, const float* __restrict__ dx,
                                                           const float* __restrict__ dB, const float* __restrict__ dC,
-                                                          TD* __restrict__ dxbc, float* __restrict__ part, int T,
-                                                          int Cd, int d_inner, int gn) {
+                                                          TD* __restrict__ dxbc, int64_t ldo, float* __restrict__ part,
+                                                          int T, int Cd, int d_inner, int gn) {
   // steps of loads in flight: three with bf16 activations and an f32 dxbc
   // (their packed window leaves room at 4 waves per SIMD for K = 4), two
   // otherwise (the bf16 rounding of dxbc takes that room)
@@ -416,7 +418,7 @@ __global__ __launch_bounds__(256, K <= 4 ? 4 : 2) void conv_bwd_vec_kernel(const
           for (int k = 0; k < K; ++k) sacc += gw[K - 1 - k][v] * wk[k][v];
           d[v] = sacc;
         }
-        stv<V>(dxbc + (rb + u0 + u) * Cd + c0, d);
+        stv<V>(dxbc + (rb + u0 + u) * ldo + c0, d);
 #pragma unroll
         for (int v = 0; v < V; ++v) {
           acc[K][v] += gw[0][v];
@@ -727,9 +729,8 @@ __global__ __launch_bounds__(256) void dt_softplus_fwd_kernel(const T* __restric
 template <typename T>
 __global__ __launch_bounds__(256) void dt_softplus_bwd_kernel(const T* __restrict__ raw,
                                                              const float* __restrict__ bias,
-                                                             const float* __restrict__ ddt,
-                                                             float* __restrict__ ddt_raw, float* __restrict__ part,
-                                                             int64_t rows, int H) {
+                                                             const float* __restrict__ ddt, GradOut ddt_raw,
+                                                             float* __restrict__ part, int64_t rows, int H) {
   __shared__ float red[256];
   const int tid = threadIdx.x;
   const int hpb = H < 256 ? H : 256;  // heads per pass
@@ -746,7 +747,7 @@ __global__ __launch_bounds__(256) void dt_softplus_bwd_kernel(const T* __restric
       for (int64_t r = r0 + s; r < r1; r += S) {
         const int64_t i = r * H + h;
         const float g = ddt[i] / (1.f + expf(-(load_f(raw, i) + bh)));
-        ddt_raw[i] = g;
+        ddt_raw.put(r * ddt_raw.ld + h, g);
         acc += g;
       }
     }
@@ -795,12 +796,12 @@ static void conv_bwd_launch(int b, int T, int Cd, int d_inner, int gn, const voi
     dim3 grid((Cd / 4 + WAVE - 1) / WAVE, conv_nruns(T), b);
     if (dxbc.bf)
       hipLaunchKernelGGL((conv_bwd_vec_kernel<TI, K, uint16_t>), grid, dim3(NTHREADS), 0, st,
-                         static_cast<const TI*>(xbc), w, bias, dx, dB, dC, static_cast<uint16_t*>(dxbc.p), part, T,
-                         Cd, d_inner, gn);
+                         static_cast<const TI*>(xbc), w, bias, dx, dB, dC, static_cast<uint16_t*>(dxbc.p), dxbc.ld,
+                         part, T, Cd, d_inner, gn);
     else
       hipLaunchKernelGGL((conv_bwd_vec_kernel<TI, K, float>), grid, dim3(NTHREADS), 0, st,
-                         static_cast<const TI*>(xbc), w, bias, dx, dB, dC, static_cast<float*>(dxbc.p), part, T, Cd,
-                         d_inner, gn);
+                         static_cast<const TI*>(xbc), w, bias, dx, dB, dC, static_cast<float*>(dxbc.p), dxbc.ld,
+                         part, T, Cd, d_inner, gn);
   } else {
     dim3 grid((Cd + 255) / 256, conv_nruns(T), b);
     hipLaunchKernelGGL((conv_bwd_kernel<TI, K>), grid, dim3(256), 0, st, static_cast<const TI*>(xbc), w, bias, dx,
@@ -839,9 +840,9 @@ hipError_t launch_conv_fwd(int b, int T, int d_inner, int gn, int K, DType dt, c
 
 hipError_t launch_conv_bwd(int b, int T, int d_inner, int gn, int K, DType dt, const void* xbc, const float* w,
                            const float* bias, const float* dx, const float* dB, const float* dC, void* dxbc,
-                           DType dxt, float* dw, float* dbias, float* part, hipStream_t st) {
+                           DType dxt, int64_t dxbc_ld, float* dw, float* dbias, float* part, hipStream_t st) {
   const int Cd = d_inner + 2 * gn;
-  const GradOut go{dxbc, dxt == BF16 ? 1 : 0};
+  const GradOut go{dxbc, dxt == BF16 ? 1 : 0, dxbc_ld};
   if (dt == BF16) {
     SSD_CONV_DISPATCH(conv_bwd_launch, uint16_t, b, T, Cd, d_inner, gn, xbc, w, bias, dx, dB, dC, go, part, st)
   } else {
@@ -929,7 +930,7 @@ static void rms_bwd_launch_o(DType ot, int64_t rows, int width, const void* y, c
 hipError_t launch_rms_bwd(int64_t rows, int width, DType dt, DType gt, DType ot, const void* y, const void* z,
                           const float* w, const float* inv_rms, const void* g, void* dy, void* dz, DType zt,
                           float* dw, float* part, hipStream_t st) {
-  const GradOut go{dz, zt == BF16 ? 1 : 0};
+  const GradOut go{dz, zt == BF16 ? 1 : 0, width};
   if (dt == BF16) {
     if (gt == BF16)
       rms_bwd_launch_o<uint16_t, uint16_t>(ot, rows, width, y, z, w, inv_rms, g, dy, go, part, st);
@@ -963,14 +964,15 @@ hipError_t launch_dt_softplus_fwd(int64_t rows, int H, DType dt, const void* raw
 }
 
 hipError_t launch_dt_softplus_bwd(int64_t rows, int H, DType dt, const void* raw, const float* bias, const float* ddt,
-                                  float* ddt_raw, float* d_bias, float* part, hipStream_t st) {
+                                  void* ddt_raw, DType ot, int64_t ld, float* d_bias, float* part, hipStream_t st) {
   const dim3 grid(dt_nparts(rows));
+  const GradOut go{ddt_raw, ot == BF16 ? 1 : 0, ld};
   if (dt == BF16)
     hipLaunchKernelGGL(dt_softplus_bwd_kernel<uint16_t>, grid, dim3(256), 0, st, static_cast<const uint16_t*>(raw),
-                       bias, ddt, ddt_raw, part, rows, H);
+                       bias, ddt, go, part, rows, H);
   else
     hipLaunchKernelGGL(dt_softplus_bwd_kernel<float>, grid, dim3(256), 0, st, static_cast<const float*>(raw), bias,
-                       ddt, ddt_raw, part, rows, H);
+                       ddt, go, part, rows, H);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   launch_part_reduce(part, d_bias, nullptr, dt_nparts(rows), H, 0, st);

@@ -183,7 +183,13 @@ def test_shell_argument_checks(lib):
     assert lib.mamba2_rmsnorm_gated_bwd(100, 64, 0, 0, 0, 7, f, f, f, f, f, f, f, f, f, need, None) == -3
     cneed = lib.mamba2_conv1d_silu_bwd_workspace_bytes(2, 300, 64, 1, 16, 4)
     assert cneed > 0
-    assert lib.mamba2_conv1d_silu_bwd(2, 300, 64, 1, 16, 4, 0, f, f, f, f, f, f, 7, f, f, f, f, cneed, None) == -3
+    assert lib.mamba2_conv1d_silu_bwd(2, 300, 64, 1, 16, 4, 0, f, f, f, f, f, f, 7, f, 0, f, f, f, cneed, None) == -3
+    # dxbc_ld below conv_dim (96) or not a multiple of 4
+    assert lib.mamba2_conv1d_silu_bwd(2, 300, 64, 1, 16, 4, 0, f, f, f, f, f, f, 0, f, 92, f, f, f, cneed, None) == -1
+    assert lib.mamba2_conv1d_silu_bwd(2, 300, 64, 1, 16, 4, 0, f, f, f, f, f, f, 0, f, 98, f, f, f, cneed, None) == -1
+    dneed = lib.ssd_dt_softplus_bwd_workspace_bytes(100, 8)
+    assert lib.ssd_dt_softplus_bwd(100, 8, 0, f, f, f, 7, f, 0, f, f, dneed, None) == -3
+    assert lib.ssd_dt_softplus_bwd(100, 8, 0, f, f, f, 0, f, 4, f, f, dneed, None) == -1  # ld below nheads
 
 
 def test_dt_softplus_argument_checks(lib):
@@ -196,8 +202,10 @@ def test_dt_softplus_argument_checks(lib):
     assert lib.ssd_dt_softplus_fwd(i64(10), i64(4), 0, ctypes.c_void_p(FAKE + 4), f, f, None) == -6
     need = lib.ssd_dt_softplus_bwd_workspace_bytes(i64(100), i64(4))
     assert need >= 2 * 4 * 4  # two 64-row partials of 4 heads (at most 64 rows each)
-    assert lib.ssd_dt_softplus_bwd(i64(100), i64(4), 0, f, f, f, f, f, f, ctypes.c_size_t(need - 1), None) == -4
-    assert lib.ssd_dt_softplus_bwd(i64(100), i64(4), 0, f, f, f, f, None, f, ctypes.c_size_t(need), None) == -1
+    assert lib.ssd_dt_softplus_bwd(i64(100), i64(4), 0, f, f, f, 0, f, i64(0), f, f, ctypes.c_size_t(need - 1),
+                                   None) == -4
+    assert lib.ssd_dt_softplus_bwd(i64(100), i64(4), 0, f, f, f, 0, None, i64(0), f, f, ctypes.c_size_t(need),
+                                   None) == -1
 
 
 def test_product_path_does_not_import_the_oracle():

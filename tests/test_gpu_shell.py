@@ -130,6 +130,38 @@ def test_rmsnorm_gated_bwd_bf16_dz_is_the_cast(rows, width, dtype, gdtype):
     assert torch.equal(dy16, dy32) and torch.equal(dw16, dw32)
 
 
+@pytest.mark.parametrize("b,T,d_inner,G,N,K,H", [
+    (2, 300, 64, 2, 16, 4, 4),           # vector conv kernel
+    (2, 200, 36, 1, 6, 4, 4),            # scalar conv kernel (conv_dim 48)
+    (4, 2048, 3072, 1, 128, 4, 48),      # the block training shape, four batch rows
+])
+def test_side_by_side_gradient_outputs(b, T, d_inner, G, N, K, H):
+    """The conv backward's bf16 dxbc and the dt backward's bf16 ddt_raw written
+    as the two column blocks of one [b*T, conv_dim + H] matrix equal, bit for
+    bit, the same outputs written on their own, and fill every column."""
+    xbc, w, bias, gact = conv_case(15, b, T, d_inner, G, N, K, "bf16")
+    cd = d_inner + 2 * G * N
+    gx = dev(np.ascontiguousarray(gact[..., :d_inner]))
+    gB = dev(np.ascontiguousarray(gact[..., d_inner:d_inner + G * N].reshape(b, T, G, N)))
+    gC = dev(np.ascontiguousarray(gact[..., d_inner + G * N:].reshape(b, T, G, N)))
+    rng = np.random.default_rng(16)
+    raw = dev(Stored(rng.standard_normal((b, T, H)).astype(np.float32), "bf16"))
+    dtb = dev(rng.standard_normal(H).astype(np.float32))
+    ddt = dev(rng.standard_normal((b, T, H)).astype(np.float32))
+    cargs = (dev(xbc), dev(w), dev(bias), gx, gB, gC, d_inner, G, N)
+    dx_ref, _, _ = ssd.conv1d_silu_bwd(*cargs, dxbc_dtype=torch.bfloat16)
+    dd_ref, db_ref = ssd.dt_softplus_bwd(raw, dtb, ddt, out_dtype=torch.bfloat16)
+    gxd = torch.full((b * T, cd + H), float("nan"), dtype=torch.bfloat16, device=dx_ref.device)
+    ssd.conv1d_silu_bwd(*cargs, dxbc_dtype=torch.bfloat16, out=gxd[:, :cd].view(b, T, cd))
+    _, db = ssd.dt_softplus_bwd(raw, dtb, ddt, out_dtype=torch.bfloat16,
+                                out=(gxd[:, cd:].view(b, T, H), torch.empty(H, device=dx_ref.device)))
+    torch.cuda.synchronize()
+    assert torch.equal(gxd[:, :cd].reshape(b, T, cd).view(torch.int16), dx_ref.view(torch.int16))
+    assert torch.equal(gxd[:, cd:].reshape(b, T, H).view(torch.int16), dd_ref.view(torch.int16))
+    assert torch.equal(db, db_ref)
+    assert not torch.isnan(gxd).any()
+
+
 def test_block_slice_end_to_end():
     """dt activation and conv1d+SiLU -> SSD -> RMSNorm-gated forward and the
     backward through all of them at the block-slice size, against the oracle chain run in f64 from the
@@ -224,8 +256,12 @@ def _full_block_problem(size):
     of 64, d_state 128, d_model 1536, no initial state), with its weights and
     output gradient drawn as the benchmark draws them."""
     from ssd_inputs import CONFIGS, SSDConfig
-    if size == "small":
-        cfg = SSDConfig("blk_full", 2, 256, 4, 64, 64, 1, 128, "bf16", init_state=True, shell=True, seed=93)
+    if size in ("small", "odd"):
+        # odd: three heads and d_state 66, so conv_dim (324) is not a multiple
+        # of 8 and the gradients of xbc and dt_raw take a product each instead
+        # of one together (and the SSD takes its general kernels)
+        nh, ns = (3, 66) if size == "odd" else (4, 64)
+        cfg = SSDConfig("blk_full", 2, 256, nh, 64, ns, 1, 128, "bf16", init_state=True, shell=True, seed=93)
         d = make_inputs(cfg)
         b, T, H, P, N = cfg.batch, cfg.seqlen, cfg.nheads, cfg.headdim, cfg.dstate
         di, cd, dm = cfg.d_inner, cfg.conv_dim, 128
@@ -242,7 +278,7 @@ def _full_block_problem(size):
     return cfg, d, cfg.d_model, tuple(d[k] for k in ("u", "W_z", "W_xbc", "W_dt", "W_out", "go")), None, None
 
 
-@pytest.mark.parametrize("size", ["small", "bench"])
+@pytest.mark.parametrize("size", ["small", "odd", "bench"])
 def test_autograd_full_block_with_projections(size):
     """mamba2_block (in_proj parts, block slice, out_proj; bf16) against the
     oracle chain with the projections as f64 matrix products; `bench` is the
