@@ -246,7 +246,7 @@ int ssd_dt_softplus_bwd(int64_t rows, int64_t nheads, int32_t dtype, const void*
  * which synchronises the stream and allocates a scratch output for the
  * trials), or rocBLAS gemm_ex where hipBLASLt offers no algorithm or
  * SSD_GEMM=rocblas is set.  Unlike the other entry points, the library
- * handles and the 32 MiB hipBLASLt workspace (one each per device, created on
+ * handles and the 128 MiB hipBLASLt workspace (one each per device, created on
  * first use) hold device memory of their own. */
 int ssd_gemm(int32_t trans_a, int32_t trans_b, int64_t m, int64_t n, int64_t k, float alpha,
              const void* A, int64_t lda, const void* B, int64_t ldb, float beta, void* C,

@@ -30,7 +30,7 @@ namespace {
 std::mutex g_blas_mu;
 std::map<int, rocblas_handle> g_blas;
 
-constexpr size_t kLtWorkspace = size_t(32) << 20;  // bytes of hipBLASLt workspace per device
+constexpr size_t kLtWorkspace = size_t(128) << 20;  // bytes of hipBLASLt workspace per device
 
 struct LtDevice {
   hipblasLtHandle_t handle = nullptr;
