@@ -180,9 +180,9 @@ size_t mamba2_conv1d_silu_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int
 
 /* Backward of mamba2_conv1d_silu_fwd.  dx [b,T,d_inner], dB, dC [b,T,G,N] are
  * the f32 gradients of its three outputs.  Outputs: dxbc, b*T rows of
- * conv_dim elements, dxbc_ld elements apart (0: conv_dim; else a multiple of
- * 4 >= conv_dim, e.g. to leave room for the dt_raw gradient beside it as one
- * GEMM operand), in `dxbc_dtype` (SSD_F32, or SSD_BF16 rounded to nearest
+ * conv_dim elements, dxbc_ld elements apart (0 or conv_dim: packed; else a
+ * multiple of 4 above conv_dim, e.g. to leave room for the dt_raw gradient
+ * beside it as one GEMM operand), in `dxbc_dtype` (SSD_F32, or SSD_BF16 rounded to nearest
  * even: the values an f32 -> bf16 cast of the f32 output gives); dw
  * [conv_dim,d_conv] and dbias [conv_dim] f32. */
 int mamba2_conv1d_silu_bwd(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t ngroups,

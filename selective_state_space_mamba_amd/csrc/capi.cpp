@@ -690,9 +690,10 @@ int mamba2_conv1d_silu_bwd(int64_t batch, int64_t seqlen, int64_t d_inner, int64
   if (!dw || !dbias) return fail(SSD_ERR_INVALID_ARG, "conv1d_silu_bwd: dw and dbias are required");
   const int64_t cd = d_inner + 2 * ngroups * dstate;
   if (dxbc_ld == 0) dxbc_ld = cd;
-  // a row's elements stay 16 bytes (f32) or 8 bytes (bf16) aligned in groups of four
-  if (dxbc_ld < cd || dxbc_ld % 4 != 0)
-    return fail(SSD_ERR_INVALID_ARG, "conv1d_silu_bwd: dxbc_ld %lld must be 0 or a multiple of 4 >= %lld",
+  // a wider row keeps its elements 16 bytes (f32) or 8 bytes (bf16) aligned
+  // in groups of four, as the vector kernel stores them
+  if (dxbc_ld < cd || (dxbc_ld != cd && dxbc_ld % 4 != 0))
+    return fail(SSD_ERR_INVALID_ARG, "conv1d_silu_bwd: dxbc_ld %lld must be 0, %lld, or a multiple of 4 above it",
                 (long long)dxbc_ld, (long long)cd);
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (batch == 0 || seqlen == 0) {

@@ -187,6 +187,11 @@ def test_shell_argument_checks(lib):
     # dxbc_ld below conv_dim (96) or not a multiple of 4
     assert lib.mamba2_conv1d_silu_bwd(2, 300, 64, 1, 16, 4, 0, f, f, f, f, f, f, 0, f, 92, f, f, f, cneed, None) == -1
     assert lib.mamba2_conv1d_silu_bwd(2, 300, 64, 1, 16, 4, 0, f, f, f, f, f, f, 0, f, 98, f, f, f, cneed, None) == -1
+    # a packed row of a conv_dim that is not a multiple of 4 (65 + 2 * 1 = 67) passes the stride
+    # check: the call stops at the next one, the (too small) workspace, before any launch
+    need67 = lib.mamba2_conv1d_silu_bwd_workspace_bytes(2, 300, 65, 1, 1, 4)
+    assert lib.mamba2_conv1d_silu_bwd(2, 300, 65, 1, 1, 4, 0, f, f, f, f, f, f, 0, f, 67, f, f, f, need67 - 1,
+                                      None) == -4
     dneed = lib.ssd_dt_softplus_bwd_workspace_bytes(100, 8)
     assert lib.ssd_dt_softplus_bwd(100, 8, 0, f, f, f, 7, f, 0, f, f, dneed, None) == -3
     assert lib.ssd_dt_softplus_bwd(100, 8, 0, f, f, f, 0, f, 4, f, f, dneed, None) == -1  # ld below nheads
