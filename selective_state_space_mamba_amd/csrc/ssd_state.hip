@@ -257,11 +257,11 @@ __global__ __launch_bounds__(NTHREADS, 2) void chunk_sum_f32_kernel(
 // Backward: slot c holds dS_c on entry and Gamma_{c+1} on exit, run =
 // Gamma_nc = init (the final state's gradient, or 0), run <- exp(s_end_c) run +
 // dS_c, last = Gamma_0, and gh_part[b,c,h,pb] = <Gamma_{c+1}, H_c> over the
-// block.  The values of the next two chunks (and, backward, their H_c) are in
+// block.  The values of the next four chunks (and, backward, their H_c) are in
 // flight while a chunk's slot is written.
 constexpr int SCAN_THREADS = 1024;
 constexpr int SCAN_EPT = STATE_PB * NMAX / SCAN_THREADS;  // elements per thread
-constexpr int SCAN_AHEAD = 2;                             // chunks loaded ahead
+constexpr int SCAN_AHEAD = 4;                             // chunks loaded ahead
 template <bool REV>
 __global__ __launch_bounds__(SCAN_THREADS) void state_scan_kernel(float* __restrict__ states,
                                                                  const float* __restrict__ send,
