@@ -246,6 +246,30 @@ __global__ __launch_bounds__(256) void conv_bwd_kernel(const TI* __restrict__ xb
   o[K] = accb;
 }
 
+// One step of eight channels of the conv input as loaded (bf16 pairs or f32),
+// unpacked where used: the forward's window of K steps takes half the
+// registers with bf16 activations, which leaves room for twice the loads in
+// flight.
+template <typename TI>
+struct XStep8 {
+  float f[8];
+  __device__ __forceinline__ void load(const float* p) { ldv<8>(p, f); }
+  __device__ __forceinline__ void zero() { zerov<8>(f); }
+  __device__ __forceinline__ float get(int v) const { return f[v]; }
+};
+template <>
+struct XStep8<uint16_t> {
+  uint32_t u[4];
+  __device__ __forceinline__ void load(const uint16_t* p) {
+    const uint4 t = *reinterpret_cast<const uint4*>(p);
+    u[0] = t.x, u[1] = t.y, u[2] = t.z, u[3] = t.w;
+  }
+  __device__ __forceinline__ void zero() { u[0] = u[1] = u[2] = u[3] = 0u; }
+  __device__ __forceinline__ float get(int v) const {
+    return (v & 1) ? __uint_as_float(u[v >> 1] & 0xFFFF0000u) : __uint_as_float(u[v >> 1] << 16);
+  }
+};
+
 // Vector conv forward.  grid (ceil(conv_dim / (8 * 64)), ceil(T / (4 * CONV_FRUN)), b):
 // lane l owns channels c0 .. c0+7, wave q the steps [4*CONV_FRUN*y + CONV_FRUN*q, +CONV_FRUN).
 template <typename TI, int K>
@@ -266,41 +290,41 @@ __global__ __launch_bounds__(256) void conv_fwd_vec_kernel(const TI* __restrict_
   else
     zerov<V>(bc);
   const SplitAt<TI> o = split_at(x_out, B_out, C_out, c0, d_inner, gn);
-  float win[K][V];  // win[k] = xbc[t - (K-1) + k]
+  // steps of loads in flight: CONV_U + 2 with bf16 activations (their packed
+  // window makes the room)
+  constexpr int U = sizeof(TI) == 2 ? CONV_U + 2 : CONV_U;
+  XStep8<TI> win[K];  // win[k] = xbc[t - (K-1) + k]
 #pragma unroll
   for (int k = 0; k < K - 1; ++k) {
     const int src = t0 - (K - 1) + k;
     if (src >= 0)
-      ldv<V>(xbc + (rb + src) * Cd + c0, win[k]);
+      win[k].load(xbc + (rb + src) * Cd + c0);
     else
-      zerov<V>(win[k]);
+      win[k].zero();
   }
-  for (int t = t0; t < t1; t += CONV_U) {
-    float nx[CONV_U][V];
+  for (int t = t0; t < t1; t += U) {
+    XStep8<TI> nx[U];
 #pragma unroll
-    for (int u = 0; u < CONV_U; ++u) {
+    for (int u = 0; u < U; ++u) {
       if (t + u < t1)
-        ldv<V>(xbc + (rb + t + u) * Cd + c0, nx[u]);
+        nx[u].load(xbc + (rb + t + u) * Cd + c0);
       else
-        zerov<V>(nx[u]);
+        nx[u].zero();
     }
 #pragma unroll
-    for (int u = 0; u < CONV_U; ++u) {
-#pragma unroll
-      for (int v = 0; v < V; ++v) win[K - 1][v] = nx[u][v];
+    for (int u = 0; u < U; ++u) {
+      win[K - 1] = nx[u];
       float a[V];
 #pragma unroll
       for (int v = 0; v < V; ++v) {
         float p = bc[v];
 #pragma unroll
-        for (int k = 0; k < K; ++k) p += wk[k][v] * win[k][v];
+        for (int k = 0; k < K; ++k) p += wk[k][v] * win[k].get(v);
         a[v] = p * sigmoidf_(p);
       }
       if (t + u < t1) stv<V>(o.p + (rb + t + u) * o.ld + o.off, a);
 #pragma unroll
-      for (int k = 0; k < K - 1; ++k)
-#pragma unroll
-        for (int v = 0; v < V; ++v) win[k][v] = win[k + 1][v];
+      for (int k = 0; k < K - 1; ++k) win[k] = win[k + 1];
     }
   }
 }
