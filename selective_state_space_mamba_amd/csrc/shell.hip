@@ -246,30 +246,6 @@ __global__ __launch_bounds__(256) void conv_bwd_kernel(const TI* __restrict__ xb
   o[K] = accb;
 }
 
-// One step of eight channels of the conv input as loaded (bf16 pairs or f32),
-// unpacked where used: the forward's window of K steps takes half the
-// registers with bf16 activations, which leaves room for twice the loads in
-// flight.
-template <typename TI>
-struct XStep8 {
-  float f[8];
-  __device__ __forceinline__ void load(const float* p) { ldv<8>(p, f); }
-  __device__ __forceinline__ void zero() { zerov<8>(f); }
-  __device__ __forceinline__ float get(int v) const { return f[v]; }
-};
-template <>
-struct XStep8<uint16_t> {
-  uint32_t u[4];
-  __device__ __forceinline__ void load(const uint16_t* p) {
-    const uint4 t = *reinterpret_cast<const uint4*>(p);
-    u[0] = t.x, u[1] = t.y, u[2] = t.z, u[3] = t.w;
-  }
-  __device__ __forceinline__ void zero() { u[0] = u[1] = u[2] = u[3] = 0u; }
-  __device__ __forceinline__ float get(int v) const {
-    return (v & 1) ? __uint_as_float(u[v >> 1] & 0xFFFF0000u) : __uint_as_float(u[v >> 1] << 16);
-  }
-};
-
 // Vector conv forward.  grid (ceil(conv_dim / (8 * 64)), ceil(T / (4 * CONV_FRUN)), b):
 // lane l owns channels c0 .. c0+7, wave q the steps [4*CONV_FRUN*y + CONV_FRUN*q, +CONV_FRUN).
 template <typename TI, int K>
@@ -290,10 +266,10 @@ __global__ __launch_bounds__(256) void conv_fwd_vec_kernel(const TI* __restrict_
   else
     zerov<V>(bc);
   const SplitAt<TI> o = split_at(x_out, B_out, C_out, c0, d_inner, gn);
-  // steps of loads in flight: CONV_U + 2 with bf16 activations (their packed
-  // window makes the room)
+  // steps of loads in flight: CONV_U + 2 with bf16 activations (their window,
+  // kept as the loaded words and unpacked where used, makes the room)
   constexpr int U = sizeof(TI) == 2 ? CONV_U + 2 : CONV_U;
-  XStep8<TI> win[K];  // win[k] = xbc[t - (K-1) + k]
+  Vec8<TI> win[K];  // win[k] = xbc[t - (K-1) + k]
 #pragma unroll
   for (int k = 0; k < K - 1; ++k) {
     const int src = t0 - (K - 1) + k;
@@ -303,7 +279,7 @@ __global__ __launch_bounds__(256) void conv_fwd_vec_kernel(const TI* __restrict_
       win[k].zero();
   }
   for (int t = t0; t < t1; t += U) {
-    XStep8<TI> nx[U];
+    Vec8<TI> nx[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (t + u < t1)
@@ -579,6 +555,16 @@ __global__ __launch_bounds__(256) void rms_bwd_kernel(const TI* __restrict__ y, 
   for (int i = threadIdx.x, k = 0; i < width; i += 256, ++k) part[static_cast<int64_t>(blockIdx.x) * width + i] = dwacc[k];
 }
 
+// The loaded words of a Vec8, opaque to the compiler: values unpacked from
+// them before this point are not kept live past it.
+__device__ __forceinline__ void opaque_words(Vec8<uint16_t>& v) {
+  asm volatile("" : "+v"(v.v.x), "+v"(v.v.y), "+v"(v.v.z), "+v"(v.v.w));
+}
+__device__ __forceinline__ void opaque_words(Vec8<float>& v) {
+  asm volatile("" : "+v"(v.a.x), "+v"(v.a.y), "+v"(v.a.z), "+v"(v.a.w));
+  asm volatile("" : "+v"(v.b.x), "+v"(v.b.y), "+v"(v.b.z), "+v"(v.b.w));
+}
+
 // Vector RMSNorm-gated: one row per wave; lane l holds the 8-element chunks
 // l, l + 64, ... (KCH of them) of its row.  Needs width % 8 == 0 and
 // width <= 64 * 8 * KCH.
@@ -592,19 +578,22 @@ __global__ __launch_bounds__(256) void rms_fwd_vec_kernel(const TI* __restrict__
   if (row >= rows) return;
   const int nch = width / 8;
   const int64_t base = row * width;
-  float yv[KCH][8];
+  Vec8<TI> yr[KCH];  // the row's loaded words, unpacked where used
   float ss = 0.f;
 #pragma unroll
   for (int j = 0; j < KCH; ++j) {
     const int c = lane + WAVE * j;
     if (c < nch)
-      ldv<8>(y + base + 8 * c, yv[j]);
+      yr[j].load(y + base + 8 * c);
     else
-      zerov<8>(yv[j]);
+      yr[j].zero();
 #pragma unroll
-    for (int e = 0; e < 8; ++e) ss += yv[j][e] * yv[j][e];
+    for (int e = 0; e < 8; ++e) ss += yr[j].get(e) * yr[j].get(e);
   }
   ss = wave_sum(ss);
+  // only the loaded words stay live across the reduction (see the backward)
+#pragma unroll
+  for (int j = 0; j < KCH; ++j) opaque_words(yr[j]);
   const float inv = 1.f / sqrtf(ss / static_cast<float>(width) + eps);
   if (lane == 0) inv_rms[row] = inv;
 #pragma unroll
@@ -615,17 +604,9 @@ __global__ __launch_bounds__(256) void rms_fwd_vec_kernel(const TI* __restrict__
     ldv<8>(z + base + 8 * c, zv);
     ldv<8>(w + 8 * c, wv);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) o[e] = yv[j][e] * inv * wv[e] * zv[e] * sigmoidf_(zv[e]);
+    for (int e = 0; e < 8; ++e) o[e] = yr[j].get(e) * inv * wv[e] * zv[e] * sigmoidf_(zv[e]);
     stv<8>(out + base + 8 * c, o);
   }
-}
-
-__device__ __forceinline__ void opaque_words(Vec8<uint16_t>& v) {
-  asm volatile("" : "+v"(v.v.x), "+v"(v.v.y), "+v"(v.v.z), "+v"(v.v.w));
-}
-__device__ __forceinline__ void opaque_words(Vec8<float>& v) {
-  asm volatile("" : "+v"(v.a.x), "+v"(v.a.y), "+v"(v.a.z), "+v"(v.a.w));
-  asm volatile("" : "+v"(v.b.x), "+v"(v.b.y), "+v"(v.b.z), "+v"(v.b.w));
 }
 
 // Vector backward: 8 waves, RMS_ROWS rows per workgroup (wave q takes rows
