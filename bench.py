@@ -449,16 +449,18 @@ def make_train_step(cfg, d):
     b, T, H, P, N, G, Q = cfg.batch, cfg.seqlen, cfg.nheads, cfg.headdim, cfg.dstate, cfg.ngroups, cfg.chunk
     dm, di, cd, M = cfg.d_model, cfg.d_inner, cfg.conv_dim, cfg.batch * cfg.seqlen
     lib = ssd.load_library()
-    u, Wz, Wo, go = (to_dev(d[k]) for k in ("u", "W_z", "W_out", "go"))
-    # W_xbc and W_dt as the row blocks of one [conv_dim + H, d_model] matrix,
-    # so that the gradients of xBC and dt_raw, written side by side, meet them
-    # in one product each for du and for the weight gradients
-    # (rows padded with zeros to a multiple of 64, the products' k-tile)
-    cdh = -(-(cd + H) // 64) * 64
-    Wxd = torch.zeros((cdh, dm), dtype=torch.bfloat16, device="cuda")
-    Wxd[:cd] = to_dev(d["W_xbc"])
-    Wxd[cd:cd + H] = to_dev(d["W_dt"])
-    Wx, Wd = Wxd[:cd], Wxd[cd:cd + H]
+    u, Wo, go = (to_dev(d[k]) for k in ("u", "W_out", "go"))
+    # W_z, W_xbc and W_dt as the row blocks of one in_proj matrix, so that the
+    # gradients of z, xBC and dt_raw, written side by side, meet it in one
+    # product for du and one for the weight gradients (rows padded with zeros
+    # to a multiple of 64, the products' k-tile)
+    nin = di + cd + H
+    ninp = -(-nin // 64) * 64
+    Win = torch.zeros((ninp, dm), dtype=torch.bfloat16, device="cuda")
+    Win[:di] = to_dev(d["W_z"])
+    Win[di:di + cd] = to_dev(d["W_xbc"])
+    Win[di + cd:nin] = to_dev(d["W_dt"])
+    Wz, Wx, Wd = Win[:di], Win[di:di + cd], Win[di + cd:nin]
     conv_w, conv_b, dt_bias = to_dev(d["conv_w"]), to_dev(d["conv_b"]), to_dev(d["dt_bias"])
     A_log, D, norm_w = to_dev(d["A_log"]), to_dev(d["D"]), to_dev(d["norm_w"])
     bf = dict(dtype=torch.bfloat16, device="cuda")
@@ -476,11 +478,11 @@ def make_train_step(cfg, d):
            "dA_log": torch.empty(H, **f32), "dB": torch.empty((b, T, G, N), **f32),
            "dC": torch.empty((b, T, G, N), **f32), "dD": torch.empty(H, **f32)}
     gact = torch.empty((M, di), **bf)  # the out_proj input gradient, in the activation dtype
-    dWo, dWz, dWxd = (torch.empty(s_, **f32) for s_ in ((dm, di), (di, dm), (cdh, dm)))
+    dWo, dWin = (torch.empty(s_, **f32) for s_ in ((dm, di), (ninp, dm)))
     du = torch.empty((M, dm), **f32)
-    # [d xBC | d dt_raw | zeros] in bf16, one row per token
-    gxd = torch.zeros((M, cdh), **bf)
-    gx_view, gd_view = gxd[:, :cd].view(b, T, cd), gxd[:, cd:cd + H]
+    # [dz | d xBC | d dt_raw | zeros] in bf16, one row per token
+    gin = torch.zeros((M, ninp), **bf)
+    gz_view, gx_view, gd_view = gin[:, :di].view(b, T, di), gin[:, di:di + cd].view(b, T, cd), gin[:, di + cd:nin]
     prob = ssd._binding.make_problem(fo["y"], to_dev(d["B"]), Q, torch.bfloat16)
     wsf = torch.empty(max(1, ssd.ssd_workspace_bytes(prob, False, f32h)), **u8)
     wsb = torch.empty(max(1, ssd.ssd_workspace_bytes(prob, True, f32h)), **u8)
@@ -505,23 +507,20 @@ def make_train_step(cfg, d):
         # backward
         ssd.gemm(go2, Wo, out=gact)
         ssd.gemm(go2, out.view(M, di), trans_a=True, out=dWo)
-        gy, gz, gw = ssd.rmsnorm_gated_bwd(y.view(b, T, di), z.view(b, T, di), norm_w, inv, gact.view(b, T, di),
-                                           workspace=wsr, dy_dtype=torch.bfloat16, dz_dtype=torch.bfloat16)
+        gy, _, gw = ssd.rmsnorm_gated_bwd(y.view(b, T, di), z.view(b, T, di), norm_w, inv, gact.view(b, T, di),
+                                          workspace=wsr, dy_dtype=torch.bfloat16, dz_dtype=torch.bfloat16,
+                                          dz_out=gz_view)
         g = ssd.ssd_bwd(xs, dt3, A_log, Bs, Cs, D, gy.view(b, T, H, P), None, chunk_states=r["chunk_states"],
                         chunk_states_bf16=r["chunk_states_bf16"], chunk=Q, out=go_,
                         workspace=wsb, want_d_init_state=False)
         # the gradients of z, xBC and dt_raw come out of their kernels in bf16
-        # (the values a cast of the f32 gradients gives), those of xBC and
-        # dt_raw side by side in gxd
+        # (the values a cast of the f32 gradients gives), side by side in gin
         ssd.conv1d_silu_bwd(xbc.view(b, T, cd), conv_w, conv_b, g["dx"].view(b, T, di), g["dB"], g["dC"], di, G,
                             N, workspace=wsc, dxbc_dtype=torch.bfloat16, out=gx_view)
         ssd.dt_softplus_bwd(raw, dt_bias, g["ddt"].view(M, H), workspace=wsd, out_dtype=torch.bfloat16,
                             out=(gd_view, d_dt_bias))
-        gz_bf = gz.view(M, di)
-        ssd.gemm(gz_bf, Wz, out=du)
-        ssd.gemm(gxd, Wxd, out=du, beta=1.0)
-        ssd.gemm(gz_bf, u2, trans_a=True, out=dWz)
-        ssd.gemm(gxd, u2, trans_a=True, out=dWxd)
+        ssd.gemm(gin, Win, out=du)
+        ssd.gemm(gin, u2, trans_a=True, out=dWin)
     return step
 
 
@@ -724,9 +723,8 @@ def main():
     }
     if cfg.d_model and "gemm" in kms:
         # three in_proj products, out_proj, and its two gradient products; the
-        # in_proj gradients as two products for du and two for the weights
-        # (those of xBC and dt_raw together)
-        n_gemm = 10
+        # in_proj gradients as one product for du and one for the weights
+        n_gemm = 8
         t_g = kms["gemm"] * n_gemm * 1e-3
         line["projections"] = {"ms_per_step": round(t_g * 1e3, 4), "calls": n_gemm,
                                "tflops": round(train_step_flops(cfg) / t_g / 1e12, 1),

@@ -204,12 +204,15 @@ size_t mamba2_rmsnorm_gated_bwd_workspace_bytes(int64_t rows, int64_t width);
 /* RMSNorm-gated backward with the saved inv_rms.  g [rows,width] is the
  * gradient of `out` in `g_dtype`.  Outputs: dy [rows,width] in `dy_dtype`
  * (SSD_F32, or SSD_BF16 rounded to nearest even, e.g. to feed ssd_bwd's bf16
- * path as its dy); dz [rows,width] in `dz_dtype` (likewise); dw [width] f32, a
+ * path as its dy); dz, rows of width elements dz_ld apart (0 or width:
+ * packed; else a multiple of 8 above width, e.g. beside the other in_proj
+ * gradients as one GEMM operand), in `dz_dtype` (likewise); dw [width] f32, a
  * fixed-order sum of per-64-row partials held in the workspace. */
 int mamba2_rmsnorm_gated_bwd(int64_t rows, int64_t width, int32_t dtype, int32_t g_dtype,
                              int32_t dy_dtype, int32_t dz_dtype, const void* y, const void* z,
                              const float* w, const float* inv_rms, const void* g, void* dy, void* dz,
-                             float* dw, void* workspace, size_t workspace_bytes, void* stream);
+                             int64_t dz_ld, float* dw, void* workspace, size_t workspace_bytes,
+                             void* stream);
 
 /* dt activation in front of the core (burn_dragon_kernel src/sequence/mamba2/backward.rs,
  * tensorized_mamba2_backward_impl:

@@ -65,7 +65,7 @@ def load_library():
     lib.mamba2_rmsnorm_gated_fwd.restype = ctypes.c_int
     lib.mamba2_rmsnorm_gated_bwd_workspace_bytes.argtypes = [i64, i64]
     lib.mamba2_rmsnorm_gated_bwd_workspace_bytes.restype = sz
-    lib.mamba2_rmsnorm_gated_bwd.argtypes = [i64, i64, i32, i32, i32, i32] + [vp] * 8 + [vp, sz, vp]
+    lib.mamba2_rmsnorm_gated_bwd.argtypes = [i64, i64, i32, i32, i32, i32] + [vp] * 7 + [i64, vp] + [vp, sz, vp]
     lib.mamba2_rmsnorm_gated_bwd.restype = ctypes.c_int
     lib.ssd_dt_softplus_fwd.argtypes = [i64, i64, i32] + [vp] * 3 + [vp]
     lib.ssd_dt_softplus_fwd.restype = ctypes.c_int
@@ -437,10 +437,11 @@ def rmsnorm_gated_fwd(y, z, w, eps: float = 1e-5, stream=None):
 
 
 def rmsnorm_gated_bwd(y, z, w, inv_rms, g, workspace=None, stream=None, dy_dtype=torch.float32,
-                      dz_dtype=torch.float32):
+                      dz_dtype=torch.float32, dz_out=None):
     """Backward of rmsnorm_gated_fwd with the saved inv_rms; returns
     (dy in dy_dtype, dz in dz_dtype, dw f32); bf16 outputs are rounded to
-    nearest even."""
+    nearest even.  dz_out may give dz: its rows may lie a fixed stride apart
+    (a column slice of a wider matrix, the stride a multiple of 8)."""
     _on_gpu(y, "y")
     lib = load_library()
     width = y.shape[-1]
@@ -454,7 +455,12 @@ def rmsnorm_gated_bwd(y, z, w, inv_rms, g, workspace=None, stream=None, dy_dtype
             raise TypeError(f"{name} must be torch.float32 or torch.bfloat16")
     f32 = dict(dtype=torch.float32, device=y.device)
     dy = torch.empty(tuple(y.shape), dtype=dy_dtype, device=y.device)
-    dz = torch.empty(tuple(y.shape), dtype=dz_dtype, device=y.device)
+    if dz_out is None:
+        dz = torch.empty(tuple(y.shape), dtype=dz_dtype, device=y.device)
+        zld = width
+    else:
+        dz = dz_out
+        zld = _need_rows(dz, "dz_out", tuple(y.shape), dz_dtype, y.device)
     dw = torch.empty((width,), **f32)
     need = lib.mamba2_rmsnorm_gated_bwd_workspace_bytes(rows, width)
     if workspace is None and need > 0:
@@ -462,7 +468,7 @@ def rmsnorm_gated_bwd(y, z, w, inv_rms, g, workspace=None, stream=None, dy_dtype
     wsz = _need_workspace(workspace, y.device)
     _check(lib.mamba2_rmsnorm_gated_bwd(rows, width, _code(y.dtype), _code(g.dtype), _code(dy_dtype),
                                         _code(dz_dtype), _ptr(y), _ptr(z), _ptr(w),
-                                        _ptr(inv_rms), _ptr(g), _ptr(dy), _ptr(dz), _ptr(dw), _ptr(workspace), wsz,
+                                        _ptr(inv_rms), _ptr(g), _ptr(dy), _ptr(dz), zld, _ptr(dw), _ptr(workspace), wsz,
                                         _stream(stream)))
     return dy, dz, dw
 

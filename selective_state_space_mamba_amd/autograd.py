@@ -100,29 +100,32 @@ def _core_fwd(xbc, dt_raw, z, conv_w, conv_b, dt_bias, A_log, D, norm_w, init_st
 
 
 def _core_bwd(xbc, dt_raw, z, conv_w, conv_b, dt_bias, A_log, D, norm_w, init_state, saved, dims, gout, gfin,
-              want_dh0, act_grad_dtype=torch.float32, gxd=None):
+              want_dh0, act_grad_dtype=torch.float32, gin=None):
     """Backward of the block slice: (dxbc, ddt_raw, dz, dconv_w, dconv_b, d_dt_bias,
     dA_log, dD, dnorm_w, d_init_state), f32 but for dz, dxbc and ddt_raw, which
     the kernels write in act_grad_dtype (bf16: rounded to nearest even, the
-    values a cast of the f32 gradients gives); with gxd ([b*T, conv_dim + H] in
-    act_grad_dtype) dxbc and ddt_raw go into its two column blocks."""
+    values a cast of the f32 gradients gives); with gin ([b*T, >= d_inner +
+    conv_dim + H] in act_grad_dtype) dz, dxbc and ddt_raw go into its first
+    three column blocks."""
     dt, xs, Bs, Cs, y, inv, cs, csb = saved
     ngroups, dstate, headdim, chunk, eps = dims
     b, T, d_inner = z.shape
     H = d_inner // headdim
     # the gradient handed to the SSD backward is stored in the activation
     # dtype, as the block-slice step does
+    cd = xbc.shape[-1]
     gy, gz, gnw = _b.rmsnorm_gated_bwd(y.view(b, T, d_inner), z, norm_w, inv, gout, dy_dtype=xbc.dtype,
-                                       dz_dtype=act_grad_dtype)
+                                       dz_dtype=act_grad_dtype,
+                                       dz_out=None if gin is None else gin[:, :d_inner].view(b, T, d_inner))
     gy = gy.view(b, T, H, headdim)
     g = _b.ssd_bwd(xs, dt, A_log, Bs, Cs, D, gy, init_state, **_history_args(cs, csb, gy),
                    chunk=chunk, want_d_init_state=want_dh0,
                    d_final_state=None if gfin is None else gfin.float().contiguous())
-    cd = xbc.shape[-1]
+    o = d_inner + cd  # the dt_raw block's first column in gin
     dxbc, dcw, dcb = _b.conv1d_silu_bwd(xbc, conv_w, conv_b, g["dx"].view(b, T, d_inner), g["dB"], g["dC"],
                                         d_inner, ngroups, dstate, dxbc_dtype=act_grad_dtype,
-                                        out=None if gxd is None else gxd[:, :cd].view(b, T, cd))
-    ddt_out = None if gxd is None else (gxd[:, cd:cd + H].view(b, T, H),
+                                        out=None if gin is None else gin[:, d_inner:o].view(b, T, cd))
+    ddt_out = None if gin is None else (gin[:, o:o + H].view(b, T, H),
                                         torch.empty(H, dtype=torch.float32, device=xbc.device))
     ddt_raw, d_bias = _b.dt_softplus_bwd(dt_raw, dt_bias, g["ddt"], out=ddt_out, out_dtype=act_grad_dtype)
     return dxbc, ddt_raw, gz, dcw, dcb, d_bias, g["dA_log"], g["dD"], gnw, g["d_init_state"]
@@ -190,35 +193,35 @@ class _Block(torch.autograd.Function):
         init_state = t[15]
         # the gradients of z, xbc and dt_raw come out of their kernels in bf16,
         # the operand dtype of the products below (the same values as a cast of
-        # the f32 gradients), those of xbc and dt_raw side by side, so that one
-        # product each against [W_xbc; W_dt] gives their parts of du and dW
-        # (rows padded with zero columns to a multiple of 64, the products'
-        # k-tile; the dt_raw block starts 16-byte aligned when conv_dim % 8 ==
-        # 0, otherwise the two gradients take a product each)
-        cd, H = W_xbc.shape[0], W_dt.shape[0]
-        side = cd % 8 == 0
-        cdh = -(-(cd + H) // 64) * 64
-        gxd = None
+        # the f32 gradients), side by side, so that one product against
+        # [W_z; W_xbc; W_dt] gives du and one the weight gradients (rows padded
+        # with zero columns to a multiple of 64, the products' k-tile; the
+        # blocks start 16-byte aligned when d_inner and conv_dim are multiples
+        # of 8, otherwise each gradient takes its own products)
+        di, cd, H = W_z.shape[0], W_xbc.shape[0], W_dt.shape[0]
+        side = di % 8 == 0 and cd % 8 == 0
+        nin = di + cd + H
+        ninp = -(-nin // 64) * 64
+        gin = None
         if side:
-            gxd = torch.empty((b * T, cdh), dtype=torch.bfloat16, device=u.device)
-            gxd[:, cd + H:].zero_()
+            gin = torch.empty((b * T, ninp), dtype=torch.bfloat16, device=u.device)
+            gin[:, nin:].zero_()
         (dxbc, ddt_raw, dz, dcw, dcb, d_bias, dA, dD, dnw, dh0) = _core_bwd(
             *t[6:16], t[16:], ctx.dims, gout, gfin, init_state is not None and ctx.needs_input_grad[11],
-            act_grad_dtype=torch.bfloat16, gxd=gxd)
-        gz = dz.view(b * T, -1)
-        du = _b.gemm(gz, W_z, out_dtype=torch.float32)
-        dWz = _b.gemm(gz, u2, trans_a=True, out_dtype=torch.float32)
+            act_grad_dtype=torch.bfloat16, gin=gin)
         if side:
-            Wxd = torch.cat([W_xbc, W_dt, W_dt.new_zeros((cdh - cd - H, W_dt.shape[1]))], dim=0)
-            du = _b.gemm(gxd, Wxd, out=du, out_dtype=torch.float32, beta=1.0)
-            dWxd = _b.gemm(gxd, u2, trans_a=True, out_dtype=torch.float32)
-            dWx, dWd = dWxd[:cd], dWxd[cd:cd + H]
+            Win = torch.cat([W_z, W_xbc, W_dt, W_dt.new_zeros((ninp - nin, W_dt.shape[1]))], dim=0)
+            du = _b.gemm(gin, Win, out_dtype=torch.float32)
+            dWin = _b.gemm(gin, u2, trans_a=True, out_dtype=torch.float32)
+            dWz, dWx, dWd = dWin[:di], dWin[di:di + cd], dWin[di + cd:nin]
         else:
-            gx, gd = dxbc.reshape(b * T, cd), ddt_raw.reshape(b * T, H)
-            du = _b.gemm(gx, W_xbc, out=du, out_dtype=torch.float32, beta=1.0)
-            du = _b.gemm(gd, W_dt, out=du, out_dtype=torch.float32, beta=1.0)
-            dWx = _b.gemm(gx, u2, trans_a=True, out_dtype=torch.float32)
-            dWd = _b.gemm(gd, u2, trans_a=True, out_dtype=torch.float32)
+            du = None
+            dWs = []
+            for gr, W in ((dz, W_z), (dxbc, W_xbc), (ddt_raw, W_dt)):
+                g2 = gr.reshape(b * T, -1)
+                du = _b.gemm(g2, W, out=du, out_dtype=torch.float32, beta=0.0 if du is None else 1.0)
+                dWs.append(_b.gemm(g2, u2, trans_a=True, out_dtype=torch.float32))
+            dWz, dWx, dWd = dWs
         return (du.view(b, T, dm), dWz, dWx, dWd, dcw, dcb, d_bias, dA, dD, dnw, dW_out, dh0, None)
 
 

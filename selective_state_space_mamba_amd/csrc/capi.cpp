@@ -753,8 +753,8 @@ int mamba2_rmsnorm_gated_fwd(int64_t rows, int64_t width, float eps, int32_t dty
 
 int mamba2_rmsnorm_gated_bwd(int64_t rows, int64_t width, int32_t dtype, int32_t g_dtype, int32_t dy_dtype,
                              int32_t dz_dtype, const void* y, const void* z, const float* w, const float* inv_rms,
-                             const void* g, void* dy, void* dz, float* dw, void* workspace, size_t workspace_bytes,
-                             void* stream) {
+                             const void* g, void* dy, void* dz, int64_t dz_ld, float* dw, void* workspace,
+                             size_t workspace_bytes, void* stream) {
   int rc = check_rms(rows, width, dtype);
   if (rc != SSD_OK) return rc;
   if (!valid_dtype(g_dtype)) return fail(SSD_ERR_DTYPE, "rmsnorm_gated_bwd: g_dtype %d is not SSD_F32 or SSD_BF16", g_dtype);
@@ -762,6 +762,11 @@ int mamba2_rmsnorm_gated_bwd(int64_t rows, int64_t width, int32_t dtype, int32_t
     return fail(SSD_ERR_DTYPE, "rmsnorm_gated_bwd: dy_dtype %d is not SSD_F32 or SSD_BF16", dy_dtype);
   if (!valid_dtype(dz_dtype))
     return fail(SSD_ERR_DTYPE, "rmsnorm_gated_bwd: dz_dtype %d is not SSD_F32 or SSD_BF16", dz_dtype);
+  if (dz_ld == 0) dz_ld = width;
+  // a wider row keeps the 16-byte groups of eight that the vector kernel stores aligned
+  if (dz_ld < width || (dz_ld != width && dz_ld % 8 != 0))
+    return fail(SSD_ERR_INVALID_ARG, "rmsnorm_gated_bwd: dz_ld %lld must be 0, %lld, or a multiple of 8 above it",
+                (long long)dz_ld, (long long)width);
   if (!dw) return fail(SSD_ERR_INVALID_ARG, "rmsnorm_gated_bwd: dw is required");
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (rows == 0) {
@@ -779,7 +784,7 @@ int mamba2_rmsnorm_gated_bwd(int64_t rows, int64_t width, int32_t dtype, int32_t
                 workspace ? workspace_bytes : 0, need);
   SSD_LAUNCH(ssd::launch_rms_bwd(rows, static_cast<int>(width), static_cast<ssd::DType>(dtype),
                                  static_cast<ssd::DType>(g_dtype), static_cast<ssd::DType>(dy_dtype), y, z, w,
-                                 inv_rms, g, dy, dz, static_cast<ssd::DType>(dz_dtype), dw,
+                                 inv_rms, g, dy, dz, static_cast<ssd::DType>(dz_dtype), dz_ld, dw,
                                  static_cast<float*>(workspace), st),
              "rmsnorm_gated_bwd");
   return ok();

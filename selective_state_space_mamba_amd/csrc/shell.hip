@@ -549,7 +549,7 @@ __global__ __launch_bounds__(256) void rms_bwd_kernel(const TI* __restrict__ y, 
       const float gw = gv * gate;
       dwacc[k] += gw * normalized;
       store_f(dy, base + i, gw * w[i] * inv - yv * coef);
-      dz.put(base + i, gv * normalized * w[i] * s * (1.f + zv * (1.f - s)));
+      dz.put(row * dz.ld + i, gv * normalized * w[i] * s * (1.f + zv * (1.f - s)));
     }
   }
   for (int i = threadIdx.x, k = 0; i < width; i += 256, ++k) part[static_cast<int64_t>(blockIdx.x) * width + i] = dwacc[k];
@@ -684,7 +684,7 @@ __global__ __launch_bounds__(RMS_VEC_WAVES * WAVE) void rms_bwd_vec_kernel(
         o_dz[e] = gv * normalized * wv * s * (1.f + zv * (1.f - s));
       }
       stv<8>(dy + base + 8 * c, o_dy);
-      dz.putv<8>(base + 8 * c, o_dz);
+      dz.putv<8>(row * dz.ld + 8 * c, o_dz);
     }
   }
   for (int q = 0; q < RMS_VEC_WAVES; ++q) {
@@ -934,8 +934,8 @@ static void rms_bwd_launch_o(DType ot, int64_t rows, int width, const void* y, c
 
 hipError_t launch_rms_bwd(int64_t rows, int width, DType dt, DType gt, DType ot, const void* y, const void* z,
                           const float* w, const float* inv_rms, const void* g, void* dy, void* dz, DType zt,
-                          float* dw, float* part, hipStream_t st) {
-  const GradOut go{dz, zt == BF16 ? 1 : 0, width};
+                          int64_t dz_ld, float* dw, float* part, hipStream_t st) {
+  const GradOut go{dz, zt == BF16 ? 1 : 0, dz_ld};
   if (dt == BF16) {
     if (gt == BF16)
       rms_bwd_launch_o<uint16_t, uint16_t>(ot, rows, width, y, z, w, inv_rms, g, dy, go, part, st);

@@ -23,10 +23,10 @@ hipError_t launch_conv_bwd(int b, int T, int d_inner, int gn, int K, DType dt, c
 hipError_t launch_rms_fwd(int64_t rows, int width, float eps, DType dt, const void* y, const void* z, const float* w,
                           void* out, float* inv_rms, hipStream_t st);
 // part: [rms_nparts(rows), width] floats of scratch
-// dy in `ot`, dz in `zt` (f32 or bf16); dw f32
+// dy in `ot`, dz in `zt` (f32 or bf16), dz's rows dz_ld elements apart; dw f32
 hipError_t launch_rms_bwd(int64_t rows, int width, DType dt, DType gt, DType ot, const void* y, const void* z,
                           const float* w, const float* inv_rms, const void* g, void* dy, void* dz, DType zt,
-                          float* dw, float* part, hipStream_t st);
+                          int64_t dz_ld, float* dw, float* part, hipStream_t st);
 
 // dt = softplus(raw + bias[h]) over rows x H, in `dt` (f32 or bf16)
 int dt_nparts(int64_t rows);

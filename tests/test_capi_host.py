@@ -178,9 +178,12 @@ def test_shell_argument_checks(lib):
     assert lib.mamba2_rmsnorm_gated_fwd(4, 64, 1e-5, 0, f, None, f, f, f, None) == -1
     need = lib.mamba2_rmsnorm_gated_bwd_workspace_bytes(100, 64)
     assert need > 0
-    assert lib.mamba2_rmsnorm_gated_bwd(100, 64, 0, 0, 0, 0, f, f, f, f, f, f, f, f, f, need - 1, None) == -4
-    assert lib.mamba2_rmsnorm_gated_bwd(100, 64, 0, 0, 7, 0, f, f, f, f, f, f, f, f, f, need, None) == -3
-    assert lib.mamba2_rmsnorm_gated_bwd(100, 64, 0, 0, 0, 7, f, f, f, f, f, f, f, f, f, need, None) == -3
+    assert lib.mamba2_rmsnorm_gated_bwd(100, 64, 0, 0, 0, 0, f, f, f, f, f, f, f, 0, f, f, need - 1, None) == -4
+    assert lib.mamba2_rmsnorm_gated_bwd(100, 64, 0, 0, 7, 0, f, f, f, f, f, f, f, 0, f, f, need, None) == -3
+    assert lib.mamba2_rmsnorm_gated_bwd(100, 64, 0, 0, 0, 7, f, f, f, f, f, f, f, 0, f, f, need, None) == -3
+    # dz_ld below width, or above it but not a multiple of 8
+    assert lib.mamba2_rmsnorm_gated_bwd(100, 64, 0, 0, 0, 0, f, f, f, f, f, f, f, 60, f, f, need, None) == -1
+    assert lib.mamba2_rmsnorm_gated_bwd(100, 64, 0, 0, 0, 0, f, f, f, f, f, f, f, 68, f, f, need, None) == -1
     cneed = lib.mamba2_conv1d_silu_bwd_workspace_bytes(2, 300, 64, 1, 16, 4)
     assert cneed > 0
     assert lib.mamba2_conv1d_silu_bwd(2, 300, 64, 1, 16, 4, 0, f, f, f, f, f, f, 7, f, 0, f, f, f, cneed, None) == -3

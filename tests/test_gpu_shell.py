@@ -124,10 +124,17 @@ def test_rmsnorm_gated_bwd_bf16_dz_is_the_cast(rows, width, dtype, gdtype):
     dy32, dz32, dw32 = ssd.rmsnorm_gated_bwd(*args)
     dy16, dz16, dw16 = ssd.rmsnorm_gated_bwd(*args, dz_dtype=torch.bfloat16)
     ref = ssd.cast_bf16(dz32.reshape(-1)).view(dz16.shape)
+    # the same bf16 dz written as the first column block of a wider matrix
+    n = int(np.prod(rows))
+    ld = -(-(width + 64) // 8) * 8  # a wider row stride must be a multiple of 8
+    wide = torch.full((n, ld), float("nan"), dtype=torch.bfloat16, device=dz16.device)
+    ssd.rmsnorm_gated_bwd(*args, dz_dtype=torch.bfloat16, dz_out=wide[:, :width].view(rows + (width,)))
     torch.cuda.synchronize()
     assert dz16.dtype == torch.bfloat16
     assert torch.equal(dz16.view(torch.int16), ref.view(torch.int16))
     assert torch.equal(dy16, dy32) and torch.equal(dw16, dw32)
+    assert torch.equal(wide[:, :width].reshape(dz16.shape).view(torch.int16), dz16.view(torch.int16))
+    assert torch.isnan(wide[:, width:]).all()
 
 
 @pytest.mark.parametrize("b,T,d_inner,G,N,K,H", [
